@@ -1,0 +1,73 @@
+"""Adapted linear layer, forward and backward, in float64 (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.
+
+Notation follows "QLoRA (low-rank adapters on a quantized model)", section
+"How it works": the weight is stored (in, out); A is (in x r), B is (r x out);
+the layer's weight is W = Wq + A B; the dense weight gradient gives
+dA = dW B^T and dB = A^T dW.  In row form the layer is y = X W, so with
+dY = dL/dy:
+
+  forward   XA = X A,          y  = X Wq + XA B
+  backward  G  = dY B^T,       dX = dY Wq^T + G A^T,
+            dA = X^T G,        dB = XA^T dY
+
+The factored dA, dB equal dW B^T and A^T dW with dW = X^T dY (matrix
+products are associative); ``backward_via_dense_dw`` computes them the way
+the chain rule is written, for tiny shapes.  "LoRA & QLoRA",
+"Mathematical Formulation", gives the same layer in column form,
+h = W0 x + B (A x).  There is no alpha/r factor, bias or dropout (the guide's
+own code has none).
+
+Every operand is widened to float64 first; the caller passes exactly the
+values the GPU receives (bf16 inputs already rounded), so the only error left
+in a comparison is the GPU's.
+"""
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def forward(X, W_hat, A=None, B=None):
+    """Returns (XA, y).  ``W_hat`` is the dequantized (in, out) weight.
+
+    With rank 0 (A or B is None) XA is an (M, 0) array and y = X W_hat.
+    """
+    X = _f64(X)
+    y = X @ _f64(W_hat)
+    if A is None or B is None or _f64(A).shape[1] == 0:
+        return np.zeros((X.shape[0], 0)), y
+    XA = X @ _f64(A)
+    return XA, y + XA @ _f64(B)
+
+
+def backward(X, dY, W_hat, A=None, B=None, XA=None):
+    """Returns dict with G, dX, dA, dB (factored; dW never formed)."""
+    X = _f64(X)
+    dY = _f64(dY)
+    dX = dY @ _f64(W_hat).T
+    if A is None or B is None or _f64(A).shape[1] == 0:
+        r = 0
+        return {"G": np.zeros((X.shape[0], r)), "dX": dX,
+                "dA": np.zeros((X.shape[1], r)), "dB": np.zeros((r, dY.shape[1]))}
+    A = _f64(A)
+    B = _f64(B)
+    if XA is None:
+        XA = X @ A
+    G = dY @ B.T
+    dX = dX + G @ A.T
+    dA = X.T @ G
+    dB = _f64(XA).T @ dY
+    return {"G": G, "dX": dX, "dA": dA, "dB": dB}
+
+
+def backward_via_dense_dw(X, dY, W_hat, A, B):
+    """Chain rule through the merged weight W = W_hat + A B, as written:
+    dW = X^T dY, dA = dW B^T, dB = A^T dW, dX = dY W^T.  Tiny shapes only."""
+    X, dY, A, B = _f64(X), _f64(dY), _f64(A), _f64(B)
+    W = _f64(W_hat) + A @ B
+    dW = X.T @ dY
+    return {"dW": dW, "dX": dY @ W.T, "dA": dW @ B.T, "dB": A.T @ dW}

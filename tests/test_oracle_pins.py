@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``check_*`` function takes the implementation under test as arguments,
+so that ``test_planted_mistakes.py`` can hand it a deliberately broken copy
+of an oracle function and show that the pin catches it.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import linear as olin
+from oracle import nf4 as onf4
+from quantized_rank_fine_amd import synth, workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split("|"))
+    return rows
+
+
+# --------------------------------------------------------------------------
+# level table
+
+
+def check_level_table(L):
+    L = np.asarray(L, np.float32)
+    assert L.shape == (16,)
+    assert L[0] == np.float32(-1.0) and L[15] == np.float32(1.0)
+    assert np.all(np.diff(L.astype(np.float64)) > 0.07)
+    assert np.array_equal(L[::-1], -L)                  # exact symmetry
+    # Each level is Phi^-1(p_i)/Phi^-1(0.98): check through the forward CDF
+    # (erfc), a different function from the inverse used to build the table.
+    qmax = None
+    for i, v in enumerate(L):
+        p = (0.02 * (15 - i) + 0.98 * i) / 15
+        # solve scale: L_i * q98 = Phi^-1(p_i)  ->  Phi(L_i * q98) ~= p_i
+        if qmax is None:
+            # bisection for Phi^-1(0.98) on the CDF
+            lo, hi = 0.0, 5.0
+            for _ in range(200):
+                mid = 0.5 * (lo + hi)
+                if 0.5 * math.erfc(-mid / math.sqrt(2)) < 0.98:
+                    lo = mid
+                else:
+                    hi = mid
+            qmax = 0.5 * (lo + hi)
+        x = float(v) * qmax
+        pdf = math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+        # |Phi(x) - p| bounded by the fp32 rounding of L_i (half ulp)
+        half_ulp = float(np.spacing(np.float32(abs(v)))) * 0.5 * qmax
+        assert abs(0.5 * math.erfc(-x / math.sqrt(2)) - p) <= pdf * half_ulp * 1.01 + 1e-15
+
+
+def test_nf4_level_table():
+    check_level_table(oracle.nf4_levels())
+
+
+def test_nf4_levels_agree_with_second_inverse_cdf():
+    from scipy.special import ndtri
+    p = np.array([(0.02 * (15 - i) + 0.98 * i) / 15 for i in range(16)])
+    q = ndtri(p)
+    L2 = (q / np.abs(q).max()).astype(np.float32)
+    assert np.array_equal(L2, oracle.nf4_levels())
+
+
+def test_nf4_levels_close_to_listing_pipeline():
+    """The page's float32 pipeline (linspace fp32 -> ppf -> fp32 -> divide)
+    differs from the exact table by a few units of 2^-24 only (reading of the
+    level construction; the listing calls itself an approximation)."""
+    from scipy.stats import norm
+    p = np.linspace(0.02, 0.98, 16, dtype=np.float32)
+    q = np.asarray(norm.ppf(p.astype(np.float64)), dtype=np.float32)
+    L2 = q / np.abs(q).max()
+    L = oracle.nf4_levels()
+    diff = np.abs(L2.astype(np.float64) - L)
+    assert np.all(diff <= 4 * 2.0 ** -24) and np.any(diff > 0)
+
+
+def test_uniform_grid():
+    U = oracle.uniform4_levels()
+    assert U[0] == -1 and U[15] == 1
+    assert np.allclose(np.diff(U.astype(np.float64)), 2 / 15, atol=1e-7)
+    assert np.array_equal(U[::-1], -U)
+
+
+# --------------------------------------------------------------------------
+# the page's worked example
+
+
+def check_p2_example(encode, levels_nf4, levels_u4):
+    w = synth.p2_sample()
+    want = {r[0]: (r[1], r[2]) for r in _golden("p2_reconstruction.txt")}
+    for name, L in (("uniform 4-bit", levels_u4), ("NF4-style", levels_nf4)):
+        c = onf4.block_absmax(w)
+        codes = encode(w, c, L)
+        deq = (np.asarray(L, np.float64)[codes].reshape(-1, 64) * c[:, None]).reshape(-1)
+        mae = np.abs(deq - w.astype(np.float64)).mean()
+        use = np.bincount(codes, minlength=16)
+        got = (f"{mae:.2e}", f"{use.min() / use.sum():.2%}")
+        assert got == want[name], (name, got, want[name])
+
+
+def test_p2_worked_example():
+    check_p2_example(oracle.encode, oracle.nf4_levels(), oracle.uniform4_levels())
+
+
+# --------------------------------------------------------------------------
+# encoding rules
+
+
+def check_encode_rules(encode):
+    L = oracle.nf4_levels()
+    # (i) exact levels in a block of scale 2^k come back as their own index
+    for k in (-7, -3, 0, 2):
+        s = np.float32(2.0 ** k)
+        idx = np.arange(64) % 16
+        w = (L[idx] * s).astype(np.float32)
+        w[0] = s                                          # absmax = 2^k
+        idx[0] = 15
+        c = onf4.block_absmax(w)
+        assert c[0] == s
+        assert np.array_equal(encode(w, c, L), idx)
+    # (ii) away from the decision midpoints the code is the nearest level in
+    # exact arithmetic: #{midpoints below x}
+    g = np.random.default_rng(7)
+    x = g.uniform(-1, 1, 64 * 2000).astype(np.float32)
+    x[::64] = 1.0                                         # absmax 1 -> w = x
+    L64 = L.astype(np.float64)
+    mids = 0.5 * (L64[1:] + L64[:-1])
+    far = np.min(np.abs(x.astype(np.float64)[:, None] - mids[None, :]), axis=1) > 1e-6
+    c = onf4.block_absmax(x)
+    codes = encode(x, c, L)
+    want = np.searchsorted(mids, x.astype(np.float64), side="right")
+    assert np.array_equal(codes[far], want[far])
+    # (iii) ties and the zero block: x = 0 is equidistant from L7 and L8 and
+    # the first minimum wins; tiny x rounds onto the same tie.
+    w = np.zeros(64, np.float32)
+    w[0] = 1.0
+    w[1] = 0.0
+    w[2] = -0.0
+    w[3] = 1e-10
+    w[4] = 1e-6
+    w[5] = -1e-6
+    codes = encode(w, onf4.block_absmax(w), L)
+    assert codes[1] == 7 and codes[2] == 7 and codes[3] == 7
+    assert codes[4] == 8 and codes[5] == 7
+    z = np.zeros(64, np.float32)
+    assert np.all(encode(z, onf4.block_absmax(z), L) == 7)
+    # (iv) the extremes of every block
+    w = g.standard_normal(64 * 50).astype(np.float32)
+    c = onf4.block_absmax(w)
+    codes = encode(w, c, L).reshape(-1, 64)
+    amax = np.abs(w.reshape(-1, 64)).argmax(axis=1)
+    ext = codes[np.arange(codes.shape[0]), amax]
+    sign = np.sign(w.reshape(-1, 64)[np.arange(codes.shape[0]), amax])
+    assert np.all(ext == np.where(sign > 0, 15, 0))
+
+
+def test_encode_rules():
+    check_encode_rules(oracle.encode)
+
+
+def test_pack_nibble_order():
+    codes = np.array([1, 2, 15, 0, 7, 8], np.uint8)
+    packed = oracle.pack_codes(codes)
+    assert packed.tolist() == [0x21, 0x0F, 0x87]
+    assert np.array_equal(oracle.unpack_codes(packed), codes)
+
+
+# --------------------------------------------------------------------------
+# double quantization and storage
+
+
+def check_double_quant(dq):
+    g = np.random.default_rng(3)
+    c = np.abs(g.standard_normal(256 * 5 + 17)).astype(np.float32) * 0.05
+    c[256:512] = 0.0                                    # an all-zero group
+    q8, s2 = dq(c)
+    assert q8.dtype == np.int8 and s2.dtype == np.float32
+    assert s2.size == 6 and s2[1] == 0 and np.all(q8[256:512] == 0)
+    for gi in range(s2.size):
+        cg = c[gi * 256:(gi + 1) * 256].astype(np.float64)
+        qg = q8[gi * 256:(gi + 1) * 256].astype(np.float64)
+        if s2[gi] == 0:
+            continue
+        assert qg[cg.argmax()] == 127                    # largest scale -> 127
+        assert np.all((qg >= 0) & (qg <= 127))
+        err = np.abs(qg * float(s2[gi]) - cg)
+        assert np.all(err <= 0.5 * float(s2[gi]) * (1 + 1e-6))
+        assert abs(float(s2[gi]) - cg.max() / 127) <= 1e-7 * cg.max() / 127
+
+
+def test_double_quant():
+    check_double_quant(oracle.double_quantize)
+
+
+def test_storage_figures():
+    rows = _golden("memory_figures.txt")
+    bits = oracle.storage_bits_per_weight()
+    assert abs(bits - 4.127) < 1e-3
+    for r in rows:
+        if r[0] == "7e9":
+            gb = 7e9 * int(r[1]) / 8 / 1e9
+            assert f"{gb:5.1f}".strip() == r[2]
+        elif r[0] == "dq_saving_bits":
+            # one fp32 absmax per 64 weights replaced by int8 + fp32 per 256
+            saving = 32 / 64 - (bits - 4.0)
+            assert f"{saving:.2f}" == r[1]
+        elif r[0] == "adapter":
+            assert oracle.adapter_params(int(r[1]), int(r[2]), int(r[3])) == int(r[4])
+        elif r[0] == "adapter12":
+            assert 12 * oracle.adapter_params(int(r[1]), int(r[2]), int(r[3])) == int(r[4])
+    # the 65B workload: 80 layers of 4x8192^2 + 3x8192x22016 in 4-bit with
+    # double-quantized scales is "about 33 GB"
+    tot = 80 * sum(workloads.nf4_bytes(i, o) for _, i, o in workloads.LLAMA65B_LINEARS)
+    assert 33.0e9 < tot < 34.0e9
+    n = 80 * sum(i * o for _, i, o in workloads.LLAMA65B_LINEARS)
+    assert abs(tot - n * bits / 8) < 80 * 7 * 8
+
+
+def test_quantize_bytes_formula():
+    n_in, n_out = 4096, 4096
+    n = n_in * n_out
+    assert workloads.quantize_bytes(n_in, n_out) == 4 * n + n // 2 + n // 64 + 4 * (n // 16384)
+
+
+# --------------------------------------------------------------------------
+# dequantization layout
+
+
+def check_dequant_layout(dequantize):
+    L = oracle.nf4_levels().astype(np.float64)
+    n_in, n_out = 3, 128                    # 6 blocks, one group
+    codes = np.arange(n_in * n_out, dtype=np.int64) % 16
+    codes = codes.astype(np.uint8)
+    packed = oracle.pack_codes(codes)
+    q8 = np.array([1, 2, 3, 4, 5, 6], np.int8)
+    s2 = np.array([0.5], np.float32)
+    W = dequantize(packed, q8, s2, n_in, n_out)
+    assert W.shape == (n_in, n_out)
+    for k in range(n_in):
+        for n in range(n_out):
+            flat = k * n_out + n
+            assert W[k, n] == L[flat % 16] * (flat // 64 + 1) * 0.5
+
+
+def test_dequant_layout():
+    check_dequant_layout(oracle.dequantize)
+
+
+def test_quantize_dequantize_error_bound():
+    """|w - w_hat| <= half the largest level gap * c_b + the DQ rounding."""
+    w0 = synth.weights(64, 512, workload=0)
+    qd = oracle.quantize(w0)
+    W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], 64, 512)
+    c = np.repeat(qd["absmax"].astype(np.float64), 64).reshape(64, 512)
+    L = oracle.nf4_levels().astype(np.float64)
+    half_gap = 0.5 * np.max(np.diff(L))
+    s2 = float(qd["s2"].max())
+    assert np.all(np.abs(W - w0) <= half_gap * c + 0.5 * s2 + 1e-9)
+
+
+# --------------------------------------------------------------------------
+# forward / backward
+
+
+def _tiny(seed=0, M=3, n_in=64, n_out=64, r=2, b_zero=False):
+    g = np.random.default_rng(seed)
+    X = g.standard_normal((M, n_in))
+    W = g.standard_normal((n_in, n_out)) * 0.02
+    A = g.standard_normal((n_in, r)) / np.sqrt(n_in)
+    B = np.zeros((r, n_out)) if b_zero else g.standard_normal((r, n_out)) * 0.01
+    dY = g.standard_normal((M, n_out))
+    return X, W, A, B, dY
+
+
+def check_forward(forward):
+    X, W, A, B, _ = _tiny(b_zero=True)
+    XA, y = forward(X, W, A, B)
+    assert np.array_equal(y, X @ W)                  # B = 0: quantized base only
+    # X = I: the layer returns its merged weight W + A B
+    X, W, A, B, _ = _tiny(M=64, n_in=64, n_out=128, r=4)
+    _, y = forward(np.eye(64), W, A, B)
+    merged = W + np.einsum("kr,rn->kn", A, B)
+    assert np.allclose(y, merged, rtol=0, atol=1e-14)
+
+
+def test_forward_pins():
+    check_forward(oracle.forward)
+
+
+def _loss(forward, X, W, A, B, dY):
+    return float(np.sum(dY * forward(X, W, A, B)[1]))
+
+
+def check_backward_fd(forward, backward):
+    X, W, A, B, dY = _tiny(seed=11, M=3, n_in=64, n_out=64, r=2)
+    g = backward(X, dY, W, A, B)
+    h = 1e-3                       # L is linear in each argument: exact FD
+    for name, T in (("dX", X), ("dA", A), ("dB", B)):
+        num = np.zeros_like(T)
+        for idx in np.ndindex(*T.shape):
+            old = T[idx]
+            T[idx] = old + h
+            lp = _loss(forward, X, W, A, B, dY)
+            T[idx] = old - h
+            lm = _loss(forward, X, W, A, B, dY)
+            T[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(g[name], num, rtol=1e-7, atol=1e-9), name
+
+
+def test_backward_finite_differences():
+    check_backward_fd(oracle.forward, oracle.backward)
+
+
+def test_backward_factored_equals_chain_rule():
+    X, W, A, B, dY = _tiny(seed=5, M=7, n_in=128, n_out=64, r=3)
+    f = oracle.backward(X, dY, W, A, B)
+    d = oracle.backward_via_dense_dw(X, dY, W, A, B)
+    for k in ("dX", "dA", "dB"):
+        assert np.allclose(f[k], d[k], rtol=1e-12, atol=1e-13), k
+
+
+def test_first_step_dA_is_zero():
+    """B = 0 at the start, so dL/dA = dL/dW B^T is exactly zero and only B moves."""
+    X, W, A, B, dY = _tiny(seed=9, M=5, n_in=64, n_out=128, r=4, b_zero=True)
+    g = oracle.backward(X, dY, W, A, B)
+    assert np.all(g["dA"] == 0)
+    assert np.any(g["dB"] != 0)
+    assert np.array_equal(g["dX"], dY @ W.T)
+
+
+def test_rank_zero_is_plain_linear():
+    X, W, A, B, dY = _tiny(seed=2)
+    XA, y = oracle.forward(X, W, None, None)
+    assert XA.shape == (3, 0) and np.array_equal(y, X @ W)
+    g = oracle.backward(X, dY, W, None, None)
+    assert np.array_equal(g["dX"], dY @ W.T)

@@ -1,0 +1,122 @@
+"""The oracle's pins have teeth: each test plants one plausible mistake in a
+copy of an oracle function (on the CPU, never in the HIP path) and shows
+that the corresponding pin rejects it."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import nf4 as onf4
+
+import test_oracle_pins as pins
+
+
+def _encode_ties_high(w_flat, c, levels=None):
+    """Mistake: ties resolved to the higher index."""
+    L = oracle.nf4_levels() if levels is None else np.asarray(levels, np.float32)
+    w = np.asarray(w_flat, np.float32).reshape(-1, 64)
+    cc = np.asarray(c, np.float32).reshape(-1, 1)
+    safe = np.where(cc == 0, np.float32(1), cc)
+    x = np.where(cc == 0, np.float32(0), (w / safe).astype(np.float32))
+    d = np.abs(x[..., None] - L)
+    return (15 - np.argmin(d[..., ::-1], axis=-1)).astype(np.uint8).reshape(-1)
+
+
+def _encode_no_fp32(w_flat, c, levels=None):
+    """Mistake: nearest level chosen in float64 and against the midpoint only
+    (drops the fp32 tie behaviour around x = 0)."""
+    L = (oracle.nf4_levels() if levels is None else np.asarray(levels, np.float32)).astype(np.float64)
+    w = np.asarray(w_flat, np.float64).reshape(-1, 64)
+    cc = np.asarray(c, np.float64).reshape(-1, 1)
+    x = np.where(cc == 0, 0.0, w / np.where(cc == 0, 1.0, cc))
+    mids = 0.5 * (L[1:] + L[:-1])
+    return np.searchsorted(mids, x.reshape(-1), side="left").astype(np.uint8)
+
+
+def _unnormalised_levels():
+    """Mistake: quantiles not divided by the largest magnitude."""
+    from statistics import NormalDist
+    p = [(0.02 * (15 - i) + 0.98 * i) / 15 for i in range(16)]
+    return np.array([NormalDist().inv_cdf(v) for v in p], np.float32)
+
+
+def _dq_wrong_qmax(c):
+    """Mistake: scales quantized against 255 instead of the symmetric 127."""
+    c = np.asarray(c, np.float32)
+    ng = (c.size + 255) // 256
+    q8 = np.zeros(c.size, np.int8)
+    s2 = np.zeros(ng, np.float32)
+    for g in range(ng):
+        cg = c[g * 256:(g + 1) * 256]
+        s = np.float32(cg.max()) / np.float32(255)
+        s2[g] = s
+        if s:
+            q8[g * 256:(g + 1) * 256] = np.clip(np.rint(cg / s), -127, 127).astype(np.int8)
+    return q8, s2
+
+
+def _dequant_transposed(packed, q8, s2, n_in, n_out):
+    """Mistake: the flat code order read back as (out, in)."""
+    W = oracle.dequantize(packed, q8, s2, n_in, n_out)
+    return W.reshape(-1).reshape(n_out, n_in).T
+
+
+def _forward_no_adapter(X, W, A=None, B=None):
+    XA, y = oracle.forward(X, W, A, B)
+    return XA, np.asarray(X, np.float64) @ np.asarray(W, np.float64)
+
+
+def _backward_wrong_sign(X, dY, W, A=None, B=None, XA=None):
+    g = oracle.backward(X, dY, W, A, B, XA)
+    g["dX"] = g["dX"] - 2 * g["G"] @ np.asarray(A, np.float64).T
+    return g
+
+
+def _backward_dB_from_A(X, dY, W, A=None, B=None, XA=None):
+    """Mistake: dB = A^T dY-shaped product built from the wrong operand."""
+    g = oracle.backward(X, dY, W, A, B, XA)
+    Xf = np.asarray(X, np.float64)
+    g["dB"] = (Xf @ np.asarray(A, np.float64)[:, ::-1]).T @ np.asarray(dY, np.float64)
+    return g
+
+
+def test_ties_high_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_encode_rules(_encode_ties_high)
+
+
+def test_float64_midpoint_rule_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_encode_rules(_encode_no_fp32)
+
+
+def test_unnormalised_levels_are_caught():
+    with pytest.raises(AssertionError):
+        pins.check_level_table(_unnormalised_levels())
+    with pytest.raises(AssertionError):
+        pins.check_p2_example(oracle.encode, _unnormalised_levels(), oracle.uniform4_levels())
+
+
+def test_wrong_dq_range_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_double_quant(_dq_wrong_qmax)
+
+
+def test_transposed_dequant_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_dequant_layout(_dequant_transposed)
+
+
+def test_dropped_adapter_term_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_forward(_forward_no_adapter)
+
+
+def test_wrong_sign_in_dX_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_backward_fd(oracle.forward, _backward_wrong_sign)
+
+
+def test_wrong_operand_in_dB_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_backward_fd(oracle.forward, _backward_dB_from_A)
