@@ -1,0 +1,198 @@
+/*
+ * qlora.h -- C ABI of libqlora, the MI355X (gfx950) QLoRA adapted linear layer.
+ *
+ * Three calls carry the hot path:
+ *   qlora_quantize    W0 (fp32, frozen)  -> Wq = (4-bit codes, int8 block
+ *                                            scales, fp32 group scales)
+ *   qlora_linear_fwd  y  = X.deq(Wq) + (X.A).B
+ *   qlora_linear_bwd  dX = dY.deq(Wq)^T + (dY.B^T).A^T,
+ *                     dA = X^T.(dY.B^T),  dB = (X.A)^T.dY
+ *
+ * Sources (page titles; sections):
+ *   "QLoRA (low-rank adapters on a quantized model)", "How it works": the
+ *     weight is stored (in, out); quantize once, Wq = Q(W0), and freeze it;
+ *     A is (in x r), B is (r x out); W = Wq + A B; update only A and B with
+ *     dA = dW B^T, dB = A^T dW.  "What QLoRA adds": blocks of 64 weights with
+ *     an absmax scale each, 16 normal-quantile levels, block scales quantized
+ *     again to 8 bits, weights expanded to bf16 for every matmul and never
+ *     updated.
+ *   "LLMs · QLoRA", NormalFloat paragraph and code listing: level table
+ *     (normal quantiles at 16 evenly spaced probabilities in [0.02, 0.98],
+ *     divided by the largest magnitude), absmax per block of 64, nearest
+ *     level by argmin of |w/absmax - level|.
+ *   "LoRA & QLoRA", "Mathematical Formulation": h = W0 x + B(A x), the same
+ *     layer in column form.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     16-byte aligned, owned by the caller, and must not overlap one another.
+ *     Matrices are row-major and dense (no strides).
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     any error nothing is enqueued and no output byte is written.
+ *     QLORA_OK means the work was enqueued on `stream` (stream-ordered; the
+ *     caller synchronizes).  A launch failure reported by the runtime maps to
+ *     QLORA_ERR_DEVICE; device faults surface at the caller's next sync.
+ *   - Outputs are overwritten, never accumulated.  Wq, X, A, B, dY and XA
+ *     (in the backward) are only read.
+ *   - The library keeps no state between calls except the constant tables
+ *     it derives once from the level definition, and allocates no device
+ *     memory: scratch space is the caller's `ws` buffer.  Calls are
+ *     reentrant; calls on different streams may run concurrently.
+ *   - Same inputs give the same output bits (no order-dependent atomics).
+ *   - Finite inputs are assumed; NaN/Inf inputs give unspecified outputs.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,      /* a required pointer is NULL                    */
+  QLORA_ERR_SHAPE = 2,     /* in/out not positive multiples of 64, M < 0,
+                              r outside [0, QLORA_MAX_RANK]                 */
+  QLORA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned              */
+  QLORA_ERR_DTYPE = 4,     /* unknown qlora_dtype                           */
+  QLORA_ERR_WORKSPACE = 5, /* ws too small (see qlora_bwd_workspace_bytes)  */
+  QLORA_ERR_DEVICE = 6     /* the HIP runtime reported an error             */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+#define QLORA_BLOCK 64      /* weights per absmax block                      */
+#define QLORA_GROUP 256     /* block scales per double-quantization group    */
+#define QLORA_MAX_RANK 256  /* largest adapter rank r accepted               */
+
+/*
+ * Frozen quantized weight.  For W0 of shape (in, out), n = in*out, flattened
+ * row-major:
+ *   codes  [n/2]  uint8   byte j holds the 4-bit code of element 2j in its
+ *                         low nibble and of element 2j+1 in its high nibble;
+ *                         code i selects level L_i of the 16-entry table.
+ *   qscale [n/64] int8    block b (elements 64b..64b+63) scale q_b in
+ *                         [0, 127].
+ *   gscale [ceil(n/64/256)] fp32  group g (blocks 256g..256g+255) scale s2_g.
+ * Dequantized weight: w_hat = L[code] * (q_b * s2_g).
+ * Requires in % 64 == 0 and out % 64 == 0, so blocks never straddle rows.
+ */
+typedef struct {
+  int64_t in;
+  int64_t out;
+  uint8_t *codes;
+  int8_t *qscale;
+  float *gscale;
+} qlora_nf4;
+
+/* Number of bytes of each part of a qlora_nf4 of shape (in, out). */
+static inline size_t qlora_codes_bytes(int64_t in, int64_t out) {
+  return (size_t)(in * out / 2);
+}
+static inline size_t qlora_qscale_bytes(int64_t in, int64_t out) {
+  return (size_t)(in * out / QLORA_BLOCK);
+}
+static inline size_t qlora_gscale_count(int64_t in, int64_t out) {
+  return (size_t)((in * out / QLORA_BLOCK + QLORA_GROUP - 1) / QLORA_GROUP);
+}
+
+/*
+ * qlora_quantize: Wq = Q(W0).
+ *   W0  [in, out] fp32, device.  wq: host struct whose in/out give the shape
+ *   and whose three device buffers are overwritten.
+ * Encoding ("LLMs · QLoRA" listing): c_b = max |w| over the block (exact);
+ * x = w / c_b rounded to fp32 (IEEE, round to nearest even); code = the
+ * index i minimising fp32(|x - L_i|), the lower index on a tie; a block with
+ * c_b = 0 encodes as x = 0 (code 7).  Double quantization ("What QLoRA
+ * adds"): s2_g = fp32(max_b c_b) / 127, q_b = round_half_even(c_b / s2_g) in
+ * fp32; an all-zero group has s2_g = 0 and q_b = 0.  Codes use the exact c_b.
+ */
+qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t stream);
+
+/*
+ * qlora_linear_fwd: y = X.deq(Wq) + XA.B with XA = X.A
+ *   ("How it works" step 2; "Mathematical Formulation" forward pass).
+ *   X   [M, in]  act dtype         Y  [M, out] act dtype (output)
+ *   A   [in, r]  adt dtype         B  [r, out] adt dtype
+ *   XA  [M, r]   fp32 (output; the saved activation the backward reads).
+ * The base weight is expanded to bf16 in registers, w = bf16(L[code] *
+ * (q_b * s2_g)) computed in fp32; X (and XA, B) enter the bf16 matrix cores
+ * rounded to bf16; accumulation is fp32.  ws must hold
+ * qlora_fwd_workspace_bytes(M, in, out, r) bytes of device memory.  r = 0
+ * gives a plain NF4 linear (A, B, XA, ws may be NULL).  M = 0 is a no-op.
+ */
+qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M,
+                              qlora_dtype act, const void *A, const void *B,
+                              int32_t r, qlora_dtype adt, void *Y, float *XA,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes qlora_linear_fwd needs for this shape (host-only); 0 when
+ * r == 0 or M == 0 (ws may then be NULL). */
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r);
+
+/*
+ * qlora_linear_bwd: with G = dY.B^T,
+ *   dX = dY.deq(Wq)^T + G.A^T   (act dtype, [M, in]; NULL skips dX)
+ *   dA = X^T.G                  (fp32, [in, r])
+ *   dB = XA^T.dY                (fp32, [r, out])
+ * ("How it works" steps 3-4: dA = dW B^T and dB = A^T dW with dW = X^T dY,
+ * evaluated in factored form so dW is never formed; the base weight gets no
+ * gradient.)  XA is the forward's saved X.A (fp32 [M, r]); NULL recomputes it
+ * into the workspace.  ws must hold qlora_bwd_workspace_bytes(M, in, out, r)
+ * bytes of device memory.  r = 0 computes dX only (A, B, dA, dB, XA may be
+ * NULL).  M = 0 writes zeros to dA and dB.
+ */
+qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY,
+                              int64_t M, qlora_dtype act, const void *A,
+                              const void *B, int32_t r, qlora_dtype adt,
+                              const float *XA, void *dX, float *dA, float *dB,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes qlora_linear_bwd needs for this shape (host-only). */
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r);
+
+/* Human-readable name of a status code (host-only, static string). */
+const char *qlora_status_string(qlora_status s);
+
+/* The library's own fp32 level table L[0..15], ascending, derived from the
+ * level definition ("LLMs · QLoRA") in double precision (host-only). */
+void qlora_levels(float out[16]);
+
+/* Decision thresholds of the encoder (host-only): code = #{j in 1..15 :
+ * x >= T[j]} reproduces the fp32 argmin rule exactly; out[j-1] = T[j]. */
+void qlora_thresholds(float out[15]);
+
+/*
+ * Kernel-level event timing (instrumentation; off by default).  While
+ * enabled, every kernel the library launches is bracketed by a pair of HIP
+ * events recorded on the call's stream.  qlora_timing_read synchronizes those
+ * events and returns the summed duration (ms) and the number of launches of
+ * one kernel kind since the last reset.  Not thread-safe.
+ */
+typedef enum {
+  QLORA_KERNEL_QUANTIZE = 0,
+  QLORA_KERNEL_XA = 1,          /* XA = X.A (forward; backward recompute) */
+  QLORA_KERNEL_FWD_GEMM = 2,    /* fused y = X.deq(Wq) + XA.B             */
+  QLORA_KERNEL_DY_PASS = 3,     /* G = dY.B^T and dB partials             */
+  QLORA_KERNEL_DX_GEMM = 4,     /* fused dX = dY.deq(Wq)^T + G.A^T        */
+  QLORA_KERNEL_DA_PASS = 5,     /* dA partials = X^T.G                    */
+  QLORA_KERNEL_REDUCE = 6,      /* deterministic reduction of partials    */
+  QLORA_KERNEL_FWD_SMALLM = 7,  /* small-M forward                        */
+  QLORA_KERNEL_COUNT = 8
+} qlora_kernel_kind;
+
+int qlora_timing_enable(int on);
+int qlora_timing_read(int kind, double *total_ms, int64_t *launches);
+void qlora_timing_reset(void);
+const char *qlora_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,365 @@
+// C-ABI boundary of libqlora: argument validation, workspace planning,
+// kernel sequencing on the caller's stream and optional kernel timing.
+//
+// The three calls follow "QLoRA (low-rank adapters on a quantized model)",
+// "How it works": quantize once (Wq = Q(W0)), forward through W = Wq + A B,
+// backward giving dA = dW B^T and dB = A^T dW (here in factored form,
+// dA = X^T (dY B^T) and dB = (X A)^T dY, so dW is never formed).
+
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+#include "qlora.h"
+
+using namespace qlora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(qlora_dtype d) { return d == QLORA_F32 || d == QLORA_BF16; }
+
+bool shape_ok(int64_t in, int64_t out) {
+  const int64_t lim = int64_t(1) << 24;  // keeps every index product in int64
+  return in > 0 && out > 0 && in % 64 == 0 && out % 64 == 0 && in <= lim && out <= lim;
+}
+
+// ---------------------------------------------------------------- timing
+struct TimingState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[QLORA_KERNEL_COUNT];
+  double total_ms[QLORA_KERNEL_COUNT] = {};
+  int64_t launches[QLORA_KERNEL_COUNT] = {};
+};
+TimingState g_timing;
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F &&launch) {
+  if (!g_timing.on) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
+  (void)hipEventRecord(a, s);
+  hipError_t e = launch();
+  (void)hipEventRecord(b, s);
+  g_timing.pending[kind].emplace_back(a, b);
+  return e;
+}
+
+qlora_status dev(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE; }
+
+// ---------------------------------------------------------------- plans
+struct FwdPlan {
+  int64_t ks = 0;
+  size_t off_at = 0, off_bt = 0, off_part = 0, total = 0;
+};
+
+FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r) {
+  FwdPlan p;
+  if (r == 0 || M == 0) return p;
+  p.ks = rowdot_splits(M, in, r);
+  size_t o = 0;
+  p.off_at = o;
+  o = align_up(o + size_t(r) * in * 2);
+  p.off_bt = o;
+  o = align_up(o + size_t(out) * rank_pad32(r) * 2);
+  p.off_part = o;
+  o = align_up(o + size_t(p.ks) * M * r * 4);
+  p.total = o;
+  return p;
+}
+
+struct BwdPlan {
+  int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0;
+  size_t off_bq = 0, off_gpart = 0, off_g16 = 0, off_gt16 = 0;
+  size_t off_at = 0, off_xapart = 0, off_xa = 0, off_xat16 = 0;
+  size_t off_dbpart = 0, off_dapart = 0, total = 0;
+};
+
+BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r) {
+  BwdPlan p;
+  if (r == 0 || M == 0) return p;
+  p.ks_g = rowdot_splits(M, out, r);
+  p.ks_x = rowdot_splits(M, in, r);
+  p.ks_b = coldot_splits(M, out, r);
+  p.ks_a = coldot_splits(M, in, r);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  p.off_bq = take(size_t(r) * out * 2);
+  p.off_gpart = take(size_t(p.ks_g) * M * r * 4);
+  p.off_g16 = take(size_t(M) * rank_pad32(r) * 2);
+  p.off_gt16 = take(size_t(pad8(M)) * r * 2);
+  p.off_at = take(size_t(r) * in * 2);
+  p.off_xapart = take(size_t(p.ks_x) * M * r * 4);
+  p.off_xa = take(size_t(M) * r * 4);
+  p.off_xat16 = take(size_t(pad8(M)) * r * 2);
+  p.off_dbpart = take(size_t(p.ks_b) * out * r * 4);
+  p.off_dapart = take(size_t(p.ks_a) * in * r * 4);
+  p.total = o;
+  return p;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+qlora_status check_nf4(const qlora_nf4 *wq) {
+  if (!wq) return QLORA_ERR_NULL;
+  if (!shape_ok(wq->in, wq->out)) return QLORA_ERR_SHAPE;
+  if (!wq->codes || !wq->qscale || !wq->gscale) return QLORA_ERR_NULL;
+  if (!aligned16(wq->codes) || !aligned16(wq->qscale) || !aligned16(wq->gscale))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qlora_status_string(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "null pointer";
+    case QLORA_ERR_SHAPE: return "invalid shape";
+    case QLORA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QLORA_ERR_DTYPE: return "invalid dtype";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r) {
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out)) return 0;
+  return plan_fwd(M, in, out, r).total;
+}
+
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r) {
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out)) return 0;
+  return plan_bwd(M, in, out, r).total;
+}
+
+qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t stream) {
+  qlora_status st = check_nf4(wq);
+  if (st != QLORA_OK) return st;
+  if (!W0) return QLORA_ERR_NULL;
+  if (!aligned16(W0)) return QLORA_ERR_ALIGN;
+  const int64_t nblocks = wq->in * wq->out / 64;
+  return dev(timed(QLORA_KERNEL_QUANTIZE, stream, [&] {
+    return launch_quantize(W0, wq->codes, wq->qscale, wq->gscale, nblocks, stream);
+  }));
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlora_dtype act,
+                              const void *A, const void *B, int32_t r, qlora_dtype adt,
+                              void *Y, float *XA, void *ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  qlora_status st = check_nf4(wq);
+  if (st != QLORA_OK) return st;
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
+  if (M == 0) return QLORA_OK;
+  if (!X || !Y) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Y)) return QLORA_ERR_ALIGN;
+  const FwdPlan p = plan_fwd(M, wq->in, wq->out, r);
+  if (r > 0) {
+    if (!A || !B || !XA || !ws) return QLORA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(XA) || !aligned16(ws))
+      return QLORA_ERR_ALIGN;
+    if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  }
+  const int64_t in = wq->in, out = wq->out;
+  const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
+  hipError_t e = hipSuccess;
+  uint16_t *Bt = nullptr;
+  if (r > 0) {
+    uint16_t *At = at<uint16_t>(ws, p.off_at);
+    Bt = at<uint16_t>(ws, p.off_bt);
+    float *part = at<float>(ws, p.off_part);
+    e = timed(QLORA_KERNEL_REDUCE, stream,
+              [&] { return launch_transpose_to_bf16(A, ab, in, r, At, in, stream); });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
+      return launch_transpose_to_bf16(B, ab, r, out, Bt, rank_pad32(r), stream);
+    });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    e = timed(QLORA_KERNEL_XA, stream,
+              [&] { return launch_rowdot(X, xb, At, M, in, r, part, stream); });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
+      return launch_reduce(part, p.ks, M, r, XA, false, nullptr, 0, nullptr, 0, stream);
+    });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+  }
+  e = timed(QLORA_KERNEL_FWD_GEMM, stream, [&] {
+    return launch_fwd_gemm(wq->codes, wq->qscale, wq->gscale, in, out, X, xb, M, XA, Bt, r, Y,
+                           stream);
+  });
+  return dev(e);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int64_t M,
+                              qlora_dtype act, const void *A, const void *B, int32_t r,
+                              qlora_dtype adt, const float *XA, void *dX, float *dA, float *dB,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  qlora_status st = check_nf4(wq);
+  if (st != QLORA_OK) return st;
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
+  const int64_t in = wq->in, out = wq->out;
+  if (r > 0) {
+    if (!A || !B || !dA || !dB) return QLORA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB))
+      return QLORA_ERR_ALIGN;
+    if (XA && !aligned16(XA)) return QLORA_ERR_ALIGN;
+  }
+  if (M > 0) {
+    if (!dY) return QLORA_ERR_NULL;
+    if (!aligned16(dY)) return QLORA_ERR_ALIGN;
+    if (r > 0 && !X) return QLORA_ERR_NULL;
+    if (X && !aligned16(X)) return QLORA_ERR_ALIGN;
+    if (dX && !aligned16(dX)) return QLORA_ERR_ALIGN;
+  }
+  const BwdPlan p = plan_bwd(M, in, out, r);
+  if (p.total > 0) {
+    if (!ws) return QLORA_ERR_NULL;
+    if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+    if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  }
+  hipError_t e = hipSuccess;
+  if (M == 0) {
+    if (r > 0) {
+      e = launch_fill_zero(dA, in * r, stream);
+      if (e == hipSuccess) e = launch_fill_zero(dB, int64_t(r) * out, stream);
+    }
+    return dev(e);
+  }
+  const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
+  uint16_t *G16 = nullptr;
+  if (r > 0) {
+    // G = dY . B^T  (rowdot with Qt = B as bf16, contraction over out)
+    const uint16_t *Bq = static_cast<const uint16_t *>(B);
+    if (!ab) {
+      uint16_t *bq = at<uint16_t>(ws, p.off_bq);
+      e = timed(QLORA_KERNEL_REDUCE, stream,
+                [&] { return launch_convert_to_bf16(B, false, int64_t(r) * out, bq, stream); });
+      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+      Bq = bq;
+    }
+    float *gpart = at<float>(ws, p.off_gpart);
+    G16 = at<uint16_t>(ws, p.off_g16);
+    uint16_t *Gt16 = at<uint16_t>(ws, p.off_gt16);
+    e = timed(QLORA_KERNEL_DY_PASS, stream,
+              [&] { return launch_rowdot(dY, xb, Bq, M, out, r, gpart, stream); });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    const int64_t ldM = pad8(M);
+    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
+      return launch_reduce(gpart, p.ks_g, M, r, nullptr, false, G16, rank_pad32(r), Gt16, ldM,
+                           stream);
+    });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+
+    // XA^T in bf16 (from the saved XA, or recomputed)
+    uint16_t *XAt16 = at<uint16_t>(ws, p.off_xat16);
+    if (!XA) {
+      uint16_t *At = at<uint16_t>(ws, p.off_at);
+      float *xpart = at<float>(ws, p.off_xapart);
+      float *xaw = at<float>(ws, p.off_xa);
+      e = timed(QLORA_KERNEL_REDUCE, stream,
+                [&] { return launch_transpose_to_bf16(A, ab, in, r, At, in, stream); });
+      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+      e = timed(QLORA_KERNEL_XA, stream,
+                [&] { return launch_rowdot(X, xb, At, M, in, r, xpart, stream); });
+      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+      e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
+        return launch_reduce(xpart, p.ks_x, M, r, xaw, false, nullptr, 0, XAt16, ldM, stream);
+      });
+      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    } else {
+      e = timed(QLORA_KERNEL_REDUCE, stream,
+                [&] { return launch_transpose_to_bf16(XA, false, M, r, XAt16, ldM, stream); });
+      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    }
+
+    // dB = XA^T . dY : coldot over M of dY with XA^T, stored transposed
+    float *dbpart = at<float>(ws, p.off_dbpart);
+    e = timed(QLORA_KERNEL_DY_PASS, stream,
+              [&] { return launch_coldot(dY, xb, XAt16, ldM, M, out, r, dbpart, stream); });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
+      return launch_reduce(dbpart, p.ks_b, out, r, dB, true, nullptr, 0, nullptr, 0, stream);
+    });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+
+    // dA = X^T . G : coldot over M of X with G^T
+    float *dapart = at<float>(ws, p.off_dapart);
+    e = timed(QLORA_KERNEL_DA_PASS, stream,
+              [&] { return launch_coldot(X, xb, Gt16, ldM, M, in, r, dapart, stream); });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
+      return launch_reduce(dapart, p.ks_a, in, r, dA, false, nullptr, 0, nullptr, 0, stream);
+    });
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+  }
+  if (dX) {
+    e = timed(QLORA_KERNEL_DX_GEMM, stream, [&] {
+      return launch_dx_gemm(wq->codes, wq->qscale, wq->gscale, in, out, dY, xb, M, G16, A, ab, r,
+                            dX, stream);
+    });
+  }
+  return dev(e);
+}
+
+int qlora_timing_enable(int on) {
+  g_timing.on = on != 0;
+  return 0;
+}
+
+int qlora_timing_read(int kind, double *total_ms, int64_t *launches) {
+  if (kind < 0 || kind >= QLORA_KERNEL_COUNT) return -1;
+  for (auto &pr : g_timing.pending[kind]) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(pr.second) != hipSuccess) return -2;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return -2;
+    g_timing.total_ms[kind] += ms;
+    g_timing.launches[kind] += 1;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  g_timing.pending[kind].clear();
+  if (total_ms) *total_ms = g_timing.total_ms[kind];
+  if (launches) *launches = g_timing.launches[kind];
+  return 0;
+}
+
+void qlora_timing_reset(void) {
+  for (int k = 0; k < QLORA_KERNEL_COUNT; ++k) {
+    for (auto &pr : g_timing.pending[k]) {
+      (void)hipEventSynchronize(pr.second);
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+    g_timing.pending[k].clear();
+    g_timing.total_ms[k] = 0.0;
+    g_timing.launches[k] = 0;
+  }
+}
+
+const char *qlora_kernel_name(int kind) {
+  static const char *names[QLORA_KERNEL_COUNT] = {
+      "quantize", "xa_rowdot", "fwd_gemm", "dy_pass", "dx_gemm", "da_pass", "reduce", "fwd_smallm"};
+  if (kind < 0 || kind >= QLORA_KERNEL_COUNT) return "unknown";
+  return names[kind];
+}
+
+}  // extern "C"

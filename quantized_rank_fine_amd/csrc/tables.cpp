@@ -1,0 +1,147 @@
+// Host-side constant tables of libqlora, derived once from the definition of
+// the level set.
+//
+// Level set ("LLMs · QLoRA", NormalFloat paragraph and its code listing):
+// 16 normal quantiles at evenly spaced probabilities in [0.02, 0.98], divided
+// by the largest magnitude.  Here each quantile is found in double precision
+// by bisection on the normal CDF Phi(x) = erfc(-x/sqrt 2)/2, and the
+// normalised value is rounded to fp32 once.
+//
+// Encoder thresholds: the listing picks the level nearest to x = w/absmax by
+// an argmin of |x - L_i| in fp32, the first minimum winning.  For x between
+// L_i and L_{i+1} only those two levels can win (every other level is at
+// least one level gap, > 0.07, farther), and "L_{i+1} wins" is a monotone
+// predicate of x, so the whole rule is code = #{j : x >= T_j} for 15 fp32
+// thresholds T_1..T_15.  Each T_j is found exactly by bisection over the
+// ordered fp32 values between L_{j-1} and L_j with the same fp32 arithmetic.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+
+namespace qlora {
+namespace {
+
+double normal_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+// Phi^-1(p) by bisection to the resolution of double.
+double normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 4000; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (normal_cdf(mid) < p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  double dlo = std::fabs(normal_cdf(lo) - p), dhi = std::fabs(normal_cdf(hi) - p);
+  return dlo <= dhi ? lo : hi;
+}
+
+uint32_t f2u(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+float u2f(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Monotone map fp32 -> uint32 (total order on finite values, -0 < +0).
+uint32_t order_key(float f) {
+  uint32_t u = f2u(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+float from_key(uint32_t k) { return u2f((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+// true if the upper level of the pair wins at x (strictly smaller fp32 distance)
+bool upper_wins(float x, float lo, float hi) {
+  volatile float dlo = x - lo;   // fp32 subtraction, round to nearest even
+  volatile float dhi = hi - x;
+  return dhi < dlo;
+}
+
+uint16_t bf16_rne(float f) {
+  uint32_t u = f2u(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+Tables build_tables() {
+  Tables t;
+  double q[16];
+  double qmax = 0.0;
+  for (int i = 0; i < 16; ++i) {
+    double p = (0.02 * (15 - i) + 0.98 * i) / 15.0;
+    q[i] = normal_quantile(p);
+    qmax = std::fmax(qmax, std::fabs(q[i]));
+  }
+  for (int i = 0; i < 16; ++i) t.L[i] = (float)(q[i] / qmax);
+
+  t.T[0] = -INFINITY;
+  for (int j = 1; j < 16; ++j) {
+    float lo = t.L[j - 1], hi = t.L[j];
+    uint32_t a = order_key(lo), b = order_key(hi);   // pred(a) false, pred(b) true
+    while (b - a > 1) {
+      uint32_t m = a + (b - a) / 2;
+      if (upper_wins(from_key(m), lo, hi))
+        b = m;
+      else
+        a = m;
+    }
+    t.T[j] = from_key(b);
+  }
+
+  // Byte planes of the 8 magnitudes |L|_m = L[8+m] (m = 0..7): plane p holds
+  // byte p of each fp32 pattern; word 0 covers m = 0..3, word 1 m = 4..7.
+  for (int p = 0; p < 4; ++p) {
+    for (int w = 0; w < 2; ++w) {
+      uint32_t v = 0;
+      for (int b = 0; b < 4; ++b) {
+        uint32_t bits = f2u(t.L[8 + 4 * w + b]);
+        v |= ((bits >> (8 * p)) & 0xffu) << (8 * b);
+      }
+      t.expand.plane[p][w] = v;
+    }
+  }
+  // Same for the bf16-rounded magnitudes (bytes 2 and 3 of the fp32 pattern).
+  for (int p = 0; p < 2; ++p) {
+    for (int w = 0; w < 2; ++w) {
+      uint32_t v = 0;
+      for (int b = 0; b < 4; ++b) {
+        uint32_t bits = (uint32_t)bf16_rne(t.L[8 + 4 * w + b]) << 16;
+        v |= ((bits >> (8 * (p + 2))) & 0xffu) << (8 * b);
+      }
+      t.expand16.plane[p][w] = v;
+    }
+  }
+  for (int i = 0; i < 16; ++i) t.quant.T[i] = t.T[i];
+  return t;
+}
+
+}  // namespace
+
+const Tables &tables() {
+  static Tables t;
+  static std::once_flag once;
+  std::call_once(once, [] { t = build_tables(); });
+  return t;
+}
+
+}  // namespace qlora
+
+extern "C" void qlora_levels(float out[16]) {
+  const qlora::Tables &t = qlora::tables();
+  for (int i = 0; i < 16; ++i) out[i] = t.L[i];
+}
+
+extern "C" void qlora_thresholds(float out[15]) {
+  const qlora::Tables &t = qlora::tables();
+  for (int j = 1; j < 16; ++j) out[j - 1] = t.T[j];
+}

@@ -1,0 +1,198 @@
+"""Thin Python binding of libqlora (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it turns torch tensors into device pointers, takes the
+current HIP stream, calls the library and raises on a non-OK status.  Every
+step of the hot path runs in the HIP kernels of ``libqlora.so``; if the
+library is missing the import fails loudly.
+"""
+
+import ctypes
+import os
+import re
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "qlora.h")
+
+F32, BF16 = 0, 1
+STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "pointer not 16-byte aligned",
+          4: "invalid dtype", 5: "workspace too small", 6: "HIP runtime error"}
+KERNELS = ("quantize", "xa_rowdot", "fwd_gemm", "dy_pass", "dx_gemm", "da_pass", "reduce",
+           "fwd_smallm")
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} (status {status})")
+
+
+class qlora_nf4(ctypes.Structure):
+    _fields_ = [("in_", ctypes.c_int64), ("out", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqlora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(or python quantized_rank_fine_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    pnf4 = ctypes.POINTER(qlora_nf4)
+    L.qlora_quantize.argtypes = [vp, pnf4, vp]
+    L.qlora_linear_fwd.argtypes = [pnf4, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp, vp,
+                                   vp, sz, vp]
+    L.qlora_linear_bwd.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp,
+                                   vp, vp, vp, vp, sz, vp]
+    for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd):
+        f.restype = ctypes.c_int
+    for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
+        f.argtypes = [i64, i64, i64, i32]
+        f.restype = sz
+    L.qlora_status_string.argtypes = [ctypes.c_int]
+    L.qlora_status_string.restype = ctypes.c_char_p
+    L.qlora_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.qlora_levels.restype = None
+    L.qlora_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.qlora_thresholds.restype = None
+    L.qlora_timing_enable.argtypes = [ctypes.c_int]
+    L.qlora_timing_enable.restype = ctypes.c_int
+    L.qlora_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]
+    L.qlora_timing_read.restype = ctypes.c_int
+    L.qlora_timing_reset.argtypes = []
+    L.qlora_timing_reset.restype = None
+    L.qlora_kernel_name.argtypes = [ctypes.c_int]
+    L.qlora_kernel_name.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def header_functions():
+    """Names of the functions include/qlora.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(qlora_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    inline = set(re.findall(r"static\s+inline\s+\w+\s+(qlora_[a-z0-9_]+)\s*\(", text))
+    return sorted(set(names) - inline)
+
+
+# ------------------------------------------------------------------ helpers
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status, where):
+    if status != 0:
+        raise QloraError(status, where)
+
+
+def nf4_struct(n_in, n_out, codes, qscale, gscale):
+    """qlora_nf4 describing caller-owned buffers (tensors or raw pointers)."""
+    return qlora_nf4(int(n_in), int(n_out), _ptr(codes), _ptr(qscale), _ptr(gscale))
+
+
+class NF4Weight:
+    """Caller-owned device buffers of one quantized (in, out) weight."""
+
+    def __init__(self, n_in, n_out, device="cuda"):
+        import torch
+        n = n_in * n_out
+        self.n_in, self.n_out = n_in, n_out
+        self.codes = torch.empty(n // 2, dtype=torch.uint8, device=device)
+        self.qscale = torch.empty(n // 64, dtype=torch.int8, device=device)
+        self.gscale = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=device)
+
+    def struct(self):
+        return nf4_struct(self.n_in, self.n_out, self.codes, self.qscale, self.gscale)
+
+
+# ------------------------------------------------------------- entry points
+
+def qlora_quantize(W0, wq, stream=None):
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    _check(lib().qlora_quantize(_ptr(W0), ctypes.byref(s), _stream(stream)), "qlora_quantize")
+
+
+def qlora_fwd_workspace_bytes(M, n_in, n_out, r):
+    return int(lib().qlora_fwd_workspace_bytes(M, n_in, n_out, r))
+
+
+def qlora_bwd_workspace_bytes(M, n_in, n_out, r):
+    return int(lib().qlora_bwd_workspace_bytes(M, n_in, n_out, r))
+
+
+def qlora_linear_fwd(wq, X, M, act, A, B, r, adt, Y, XA, ws, ws_bytes, stream=None):
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    _check(lib().qlora_linear_fwd(ctypes.byref(s), _ptr(X), int(M), int(act), _ptr(A), _ptr(B),
+                                  int(r), int(adt), _ptr(Y), _ptr(XA), _ptr(ws), int(ws_bytes),
+                                  _stream(stream)), "qlora_linear_fwd")
+
+
+def qlora_linear_bwd(wq, X, dY, M, act, A, B, r, adt, XA, dX, dA, dB, ws, ws_bytes,
+                     stream=None):
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    _check(lib().qlora_linear_bwd(ctypes.byref(s), _ptr(X), _ptr(dY), int(M), int(act), _ptr(A),
+                                  _ptr(B), int(r), int(adt), _ptr(XA), _ptr(dX), _ptr(dA),
+                                  _ptr(dB), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "qlora_linear_bwd")
+
+
+def qlora_levels():
+    buf = (ctypes.c_float * 16)()
+    lib().qlora_levels(buf)
+    return list(buf)
+
+
+def qlora_thresholds():
+    buf = (ctypes.c_float * 15)()
+    lib().qlora_thresholds(buf)
+    return list(buf)
+
+
+def qlora_status_string(status):
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def qlora_timing_enable(on=True):
+    return lib().qlora_timing_enable(1 if on else 0)
+
+
+def qlora_timing_read(kind):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    rc = lib().qlora_timing_read(int(kind), ctypes.byref(ms), ctypes.byref(n))
+    if rc != 0:
+        raise RuntimeError(f"qlora_timing_read failed ({rc})")
+    return ms.value, n.value
+
+
+def qlora_timing_reset():
+    lib().qlora_timing_reset()
+
+
+def qlora_kernel_name(kind):
+    return lib().qlora_kernel_name(int(kind)).decode()

@@ -1,0 +1,157 @@
+"""Shared helpers of the GPU parity tests: run the library through its C ABI
+on seeded synthetic inputs and compute what the oracle says about them."""
+
+import sys
+
+import numpy as np
+
+import oracle
+from quantized_rank_fine_amd import qlora as q
+from quantized_rank_fine_amd import synth
+
+TOL = 1e-2          # max|gpu - ref| / max|ref| for float outputs (bf16 compute)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dev():
+    import torch
+    return torch, torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    torch, dev = torch_dev()
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(dev)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.abs(ref).max()
+    if den == 0:
+        return float(np.abs(got).max())
+    return float(np.abs(got - ref).max() / den)
+
+
+def bf16_to_f64(t):
+    """device bf16 tensor (torch) -> numpy float64."""
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).__lshift__(16) \
+        .view(np.float32).astype(np.float64)
+
+
+def out_to_f64(t, dtype):
+    import torch
+    if dtype == "bf16":
+        return bf16_to_f64(t)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def quantize_gpu(w0):
+    """Quantize an fp32 (in, out) numpy matrix on the GPU; returns the
+    NF4Weight and host copies of its three buffers."""
+    torch, dev = torch_dev()
+    n_in, n_out = w0.shape
+    wq = q.NF4Weight(n_in, n_out, dev)
+    tw = to_dev(w0)
+    q.qlora_quantize(tw, wq)
+    torch.cuda.synchronize()
+    del tw
+    return wq
+
+
+class Layer:
+    """Seeded inputs of one adapted linear, on host and device."""
+
+    def __init__(self, workload, M, n_in, n_out, r, act="bf16", adt="bf16", b_zero=False,
+                 layer=0, linear=0, w0=None):
+        torch, dev = torch_dev()
+        self.M, self.n_in, self.n_out, self.r = M, n_in, n_out, r
+        self.act, self.adt = act, adt
+        self.w0 = synth.weights(n_in, n_out, workload, layer, linear) if w0 is None else w0
+        self.X = synth.activations(M, n_in, workload, act, layer, linear)
+        self.dY = synth.activations(M, n_out, workload, act, layer, linear, tensor=synth.T_DY)
+        if r > 0:
+            self.A, self.B = synth.adapters(n_in, n_out, r, workload, adt, b_zero, layer, linear)
+        else:
+            self.A = self.B = None
+        self.tdt = torch.bfloat16 if act == "bf16" else torch.float32
+        self.adt_t = torch.bfloat16 if adt == "bf16" else torch.float32
+        self.qact = q.BF16 if act == "bf16" else q.F32
+        self.qadt = q.BF16 if adt == "bf16" else q.F32
+
+        def dv(tensor, dt):
+            if tensor is None:
+                return None
+            if tensor.dtype == "bf16":
+                return to_dev(tensor.raw.view(np.int16)).view(torch.bfloat16)
+            return to_dev(tensor.raw)
+
+        self.tX = dv(self.X, self.tdt)
+        self.tdY = dv(self.dY, self.tdt)
+        self.tA = dv(self.A, self.adt_t)
+        self.tB = dv(self.B, self.adt_t)
+        self.wq = quantize_gpu(self.w0)
+
+    # ---------------------------------------------------------------- runs
+    def fwd(self):
+        torch, dev = torch_dev()
+        M, r = self.M, self.r
+        Y = torch.empty(M, self.n_out, dtype=self.tdt, device=dev)
+        XA = torch.empty(M, max(r, 1), dtype=torch.float32, device=dev) if r else None
+        wsb = q.qlora_fwd_workspace_bytes(M, self.n_in, self.n_out, r)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+        q.qlora_linear_fwd(self.wq, self.tX, M, self.qact, self.tA, self.tB, r, self.qadt, Y, XA,
+                           ws, wsb)
+        torch.cuda.synchronize()
+        return Y, XA
+
+    def bwd(self, XA=None, want_dx=True):
+        torch, dev = torch_dev()
+        M, r = self.M, self.r
+        dX = torch.empty(M, self.n_in, dtype=self.tdt, device=dev) if want_dx else None
+        dA = torch.empty(self.n_in, max(r, 1), dtype=torch.float32, device=dev) if r else None
+        dB = torch.empty(max(r, 1), self.n_out, dtype=torch.float32, device=dev) if r else None
+        wsb = q.qlora_bwd_workspace_bytes(M, self.n_in, self.n_out, r)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+        q.qlora_linear_bwd(self.wq, self.tX, self.tdY, M, self.qact, self.tA, self.tB, r,
+                           self.qadt, XA, dX, dA, dB, ws, wsb)
+        torch.cuda.synchronize()
+        return dX, dA, dB
+
+    # -------------------------------------------------------------- oracle
+    def w_hat(self):
+        c = self.wq.codes.cpu().numpy()
+        q8 = self.wq.qscale.cpu().numpy()
+        s2 = self.wq.gscale.cpu().numpy()
+        return oracle.dequantize(c, q8, s2, self.n_in, self.n_out)
+
+    def ref(self, rows=None):
+        """Oracle forward/backward (float64) on the GPU's own quantized
+        weight (its codes are checked bit-exactly elsewhere).  With `rows`,
+        y and dX only for those rows."""
+        W = self.w_hat()
+        X = self.X.values.astype(np.float64)
+        dY = self.dY.values.astype(np.float64)
+        A = None if self.A is None else self.A.values
+        B = None if self.B is None else self.B.values
+        out = {}
+        if A is not None:
+            XA = X @ A.astype(np.float64)
+            out["XA"] = XA
+        sel = slice(None) if rows is None else rows
+        _, y = oracle.forward(X[sel], W, A, B)
+        out["y"] = y
+        g = oracle.backward(X[sel], dY[sel], W, A, B)
+        out["dX"] = g["dX"]
+        if A is not None:
+            G = dY @ B.astype(np.float64).T
+            out["dA"] = X.T @ G
+            out["dB"] = XA.T @ dY
+        return out

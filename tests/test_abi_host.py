@@ -1,0 +1,160 @@
+"""Host-side checks of libqlora (no GPU): the library loads and exports every
+function its header declares, its own constant tables agree with the oracle,
+and argument validation returns the documented status before anything is
+enqueued."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import nf4 as onf4
+from quantized_rank_fine_amd import qlora as q
+from quantized_rank_fine_amd import workloads
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = q.header_functions()
+    assert {"qlora_quantize", "qlora_linear_fwd", "qlora_linear_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_level_table_matches_oracle(L):
+    lv = np.array(q.qlora_levels(), dtype=np.float32)
+    assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def _x_sweep():
+    """fp32 values in [-1, 1]: a strided sweep of bit patterns, the
+    neighbourhood of every threshold and level, and the special values."""
+    pos = np.arange(0, 0x3F800001, 4099, dtype=np.uint32).view(np.float32)
+    xs = [pos, -pos]
+    T = np.array(q.qlora_thresholds(), np.float32)
+    L = oracle.nf4_levels()
+    for v in np.concatenate([T, L]):
+        b = np.array([v], np.float32).view(np.int32)[0]
+        nb = np.arange(b - 300, b + 301, dtype=np.int64)
+        if v >= 0:
+            nb = nb[(nb >= 0) & (nb <= 0x3F800000)]
+        else:
+            nb = nb[(nb >= np.int64(np.int32(-0x7FFFFFFF) - 1)) & (nb < 0)]
+        xs.append(nb.astype(np.int32).view(np.float32))
+    xs.append(np.array([0.0, -0.0, 1.0, -1.0, 1e-30, -1e-30, 1.4e-45], np.float32))
+    x = np.concatenate(xs).astype(np.float32)
+    return x[(x >= -1) & (x <= 1)]
+
+
+def test_thresholds_reproduce_oracle_argmin(L):
+    """code = #{j : x >= T_j} equals the oracle's fp32 argmin for every x."""
+    T = np.array(q.qlora_thresholds(), np.float32)
+    x = _x_sweep()
+    pad = (-x.size) % 63
+    x = np.concatenate([x, np.zeros(pad, np.float32)])
+    blocks = x.reshape(-1, 63)
+    w = np.concatenate([np.ones((blocks.shape[0], 1), np.float32), blocks], axis=1).reshape(-1)
+    c = onf4.block_absmax(w)
+    assert np.all(c == 1.0)
+    codes = oracle.encode(w, c).reshape(-1, 64)[:, 1:].reshape(-1)
+    mine = np.searchsorted(T, x, side="right")
+    assert np.array_equal(codes, mine)
+
+
+def test_workspace_sizes(L):
+    for (M, i, o, r) in [(2048, 4096, 4096, 16), (1, 4096, 11008, 16), (8192, 22016, 8192, 64),
+                         (64, 256, 256, 8)]:
+        f = q.qlora_fwd_workspace_bytes(M, i, o, r)
+        b = q.qlora_bwd_workspace_bytes(M, i, o, r)
+        assert f >= r * i * 2 + o * r * 2 + M * r * 4
+        assert b >= M * r * 4
+        assert f % 256 == 0 and b % 256 == 0
+    assert q.qlora_fwd_workspace_bytes(2048, 4096, 4096, 0) == 0
+    assert q.qlora_fwd_workspace_bytes(0, 4096, 4096, 16) == 0
+    assert q.qlora_bwd_workspace_bytes(64, 100, 256, 8) == 0     # invalid shape
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert q.qlora_status_string(s) == q.STATUS[s]
+
+
+# ------------------------------------------------------------ validation
+# Fake device addresses: validation fails before any pointer is touched or
+# any HIP call is made, so these never reach the runtime.
+P = 0x10000          # 16-byte aligned
+U = 0x10004          # misaligned
+
+
+def _nf4(i=256, o=256, codes=P, qs=P, gs=P):
+    return q.nf4_struct(i, o, codes, qs, gs)
+
+
+def _st(f, *a):
+    return f(*a)
+
+
+def test_quantize_validation(L):
+    s = _nf4()
+    assert L.qlora_quantize(None, ctypes.byref(s), None) == 1
+    assert L.qlora_quantize(U, ctypes.byref(s), None) == 3
+    assert L.qlora_quantize(P, None, None) == 1
+    for (i, o) in [(100, 256), (256, 100), (0, 256), (-64, 64)]:
+        s2 = _nf4(i, o)
+        assert L.qlora_quantize(P, ctypes.byref(s2), None) == 2
+    assert L.qlora_quantize(P, ctypes.byref(_nf4(codes=None)), None) == 1
+    assert L.qlora_quantize(P, ctypes.byref(_nf4(qs=U)), None) == 3
+
+
+def test_fwd_validation(L):
+    s = _nf4()
+    f = L.qlora_linear_fwd
+    ws = q.qlora_fwd_workspace_bytes(64, 256, 256, 8)
+    # M = 0 is a no-op that succeeds without touching the device
+    assert f(ctypes.byref(s), P, 0, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 0
+    assert f(ctypes.byref(s), P, -1, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 2
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 300, q.BF16, P, P, P, ws, None) == 2
+    assert f(ctypes.byref(s), P, 64, 7, P, P, 8, q.BF16, P, P, P, ws, None) == 4
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, 9, P, P, P, ws, None) == 4
+    assert f(ctypes.byref(s), None, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 1
+    assert f(ctypes.byref(s), P, 64, q.BF16, None, P, 8, q.BF16, P, P, P, ws, None) == 1
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, None, P, ws, None) == 1
+    assert f(ctypes.byref(s), U, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 3
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, U, P, P, ws, None) == 3
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws - 1, None) == 5
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, P, None, ws, None) == 1
+    bad = _nf4(256, 96)
+    assert f(ctypes.byref(bad), P, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 2
+
+
+def test_bwd_validation(L):
+    s = _nf4()
+    f = L.qlora_linear_bwd
+    ws = q.qlora_bwd_workspace_bytes(64, 256, 256, 8)
+    args = lambda **k: [ctypes.byref(k.get("s", s)), k.get("X", P), k.get("dY", P), k.get("M", 64),
+                        k.get("act", q.BF16), k.get("A", P), k.get("B", P), k.get("r", 8),
+                        k.get("adt", q.BF16), k.get("XA", P), k.get("dX", P), k.get("dA", P),
+                        k.get("dB", P), k.get("ws", P), k.get("wsb", ws), None]
+    assert f(*args(M=-5)) == 2
+    assert f(*args(r=-1)) == 2
+    assert f(*args(act=3)) == 4
+    assert f(*args(dY=None)) == 1
+    assert f(*args(X=None)) == 1
+    assert f(*args(dA=None)) == 1
+    assert f(*args(dB=U)) == 3
+    assert f(*args(XA=U)) == 3
+    assert f(*args(wsb=ws - 256)) == 5
+    assert f(*args(ws=None)) == 1
+    assert f(*args(s=_nf4(192, 100))) == 2
+
+
+def test_algorithmic_work_formulas():
+    # fwd+bwd FLOP at 4096^2, r = 16, M = 2048 (without the dense dW)
+    f = workloads.fwd_flops(2048, 4096, 4096, 16) + workloads.bwd_flops(2048, 4096, 4096, 16)
+    assert f == 2 * 2048 * (2 * 4096 * 4096 + 3 * 16 * (4096 + 4096))
+    assert workloads.quantize_bytes(4096, 4096) == 75763712

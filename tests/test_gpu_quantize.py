@@ -1,0 +1,114 @@
+"""GPU parity of qlora_quantize against the oracle: codes, packed bytes and
+int8 block scales bit-exact, group scales bit-exact (same fp32 division),
+dequantized weights within 1e-6 relative."""
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_rank_fine_amd import synth, workloads
+
+from gpu_harness import quantize_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(w0, tag):
+    say(f"[quantize] {tag} shape={w0.shape}")
+    wq = quantize_gpu(w0)
+    ref = oracle.quantize(w0)
+    codes = wq.codes.cpu().numpy()
+    q8 = wq.qscale.cpu().numpy()
+    s2 = wq.gscale.cpu().numpy()
+    bad = np.flatnonzero(codes != ref["packed"])
+    assert bad.size == 0, f"{tag}: {bad.size} packed bytes differ, first at {bad[:5]}"
+    assert np.array_equal(q8, ref["q8"]), f"{tag}: q8 differs"
+    assert np.array_equal(s2.view(np.uint32), ref["s2"].view(np.uint32)), f"{tag}: s2 differs"
+    n_in, n_out = w0.shape
+    Wg = oracle.dequantize(codes, q8, s2, n_in, n_out)
+    Wr = oracle.dequantize(ref["packed"], ref["q8"], ref["s2"], n_in, n_out)
+    assert np.abs(Wg - Wr).max() <= 1e-6 * np.abs(Wr).max()
+    return wq
+
+
+def test_quantize_small_config():
+    _check_full(synth.weights(256, 256, workload=0), "256x256")
+
+
+def test_quantize_4096_square():
+    _check_full(synth.weights(4096, 4096, workload=1), "4096x4096")
+
+
+@pytest.mark.parametrize("shape", [(64, 192), (320, 640), (64, 64), (128, 704)])
+def test_quantize_ragged_groups(shape):
+    # n/64 not a multiple of 256: the last double-quantization group is short
+    _check_full(synth.weights(*shape, workload=7), f"ragged {shape}")
+
+
+def test_quantize_edge_values():
+    g = np.random.default_rng(11)
+    w = (g.standard_normal((256, 512)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.0                                   # zero block
+    w[1, :] = 0.0                                     # two zero blocks...
+    w[2:66, :] = 0.0                                  # ...and a whole zero group
+    w[70, 64:128] = -0.0                              # negative zeros
+    w[71, :64] = np.float32(1e-40) * g.standard_normal(64).astype(np.float32)   # denormals
+    w[72, 64:128] = np.float32(3e-39)                 # denormal absmax, constant block
+    w[73, :64] = np.float32(1e30) * g.standard_normal(64).astype(np.float32)    # huge
+    L = oracle.nf4_levels()
+    w[74, :64] = L[np.arange(64) % 16] * np.float32(0.125)                       # exact levels
+    w[75, :64] = -w[74, :64]
+    _check_full(w, "edge values")
+
+
+def test_quantize_near_thresholds():
+    """Weights whose quotient w / absmax lands within a few ulp of every
+    decision threshold, for many random block scales: exercises the exact
+    fp32 division of the kernel."""
+    from quantized_rank_fine_amd import qlora as q
+    T = np.array(q.qlora_thresholds(), np.float32)
+    g = np.random.default_rng(5)
+    nblk = 4096
+    c = (np.abs(g.standard_normal(nblk)) * 0.05 + 1e-3).astype(np.float32)
+    w = np.empty((nblk, 64), np.float32)
+    w[:, 0] = c * np.where(g.random(nblk) < 0.5, 1, -1)
+    for b in range(nblk):
+        t = T[g.integers(0, 15, 63)]
+        x = (t.astype(np.float64) * c[b]).astype(np.float32)
+        ulp = g.integers(-3, 4, 63).astype(np.int32)
+        x = (x.view(np.int32) + ulp * np.sign(x).astype(np.int32)).view(np.float32)
+        w[b, 1:] = np.clip(x, -c[b], c[b])
+    _check_full(w.reshape(1024, 256), "near thresholds")
+
+
+def test_quantize_deterministic():
+    w0 = synth.weights(512, 1024, workload=3)
+    a = quantize_gpu(w0)
+    b = quantize_gpu(w0)
+    assert np.array_equal(a.codes.cpu().numpy(), b.codes.cpu().numpy())
+    assert np.array_equal(a.qscale.cpu().numpy(), b.qscale.cpu().numpy())
+
+
+@pytest.mark.parametrize("name,n_in,n_out", [l for l in workloads.LLAMA7B_LINEARS if l[0] in ("up", "down")])
+def test_quantize_7b_shapes(name, n_in, n_out):
+    _check_full(synth.weights(n_in, n_out, workload=3, linear=5), f"7b {name}")
+
+
+@pytest.mark.parametrize("name,n_in,n_out", [("q", 8192, 8192), ("down", 22016, 8192)])
+def test_quantize_65b_shapes_sampled(name, n_in, n_out):
+    """Full-size 65B-style linears: compare 64 sampled double-quantization
+    groups (each group depends on its own 16384 weights only)."""
+    say(f"[quantize] 65b {name} {n_in}x{n_out}")
+    w0 = synth.weights(n_in, n_out, workload=4, layer=79, linear=6 if name == "down" else 0)
+    wq = quantize_gpu(w0)
+    codes = wq.codes.cpu().numpy()
+    q8 = wq.qscale.cpu().numpy()
+    s2 = wq.gscale.cpu().numpy()
+    flat = w0.reshape(-1)
+    ngroups = flat.size // 16384
+    g = np.random.default_rng(0)
+    for gi in np.concatenate([[0, ngroups - 1], g.integers(0, ngroups, 62)]):
+        ref = oracle.quantize(flat[gi * 16384:(gi + 1) * 16384].reshape(64, 256))
+        assert np.array_equal(codes[gi * 8192:(gi + 1) * 8192], ref["packed"]), gi
+        assert np.array_equal(q8[gi * 256:(gi + 1) * 256], ref["q8"]), gi
+        assert s2[gi] == ref["s2"][0], gi
