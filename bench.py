@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA adapted linear on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input:
+  qlora_quantize (fp32 W0 -> NF4 codes + int8/fp32 scales)
+  qlora_linear_fwd  y = X.deq(Wq) + (X.A).B
+  qlora_linear_bwd  dX, dA, dB (factored; dW never formed)
+on the 4096 x 4096 projection, r = 16, M = 2048 tokens, bf16 activations and
+adapters.  Inputs are resident in HBM before the timed region; five distinct
+W0 buffers (335 MB, more than the 256 MB Infinity Cache) are cycled so every
+quantize reads its weights from HBM.
+
+Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s (the dense dW
+is not formed and not counted), timed with HIP events around the forward and
+backward calls of every timed step; quantize GB/s is reported beside it.
+`roofline` covers the dominant kernel (a fused dequantizing GEMM), timed with
+HIP events around each of its launches on the stream it runs on.
+`cpu_baseline` times the CPU oracle on the same workload (bounded to a few
+repetitions of the full step, about 10 s of CPU work).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s & quantize GB/s (% roofline), 4096² r=16"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+N_W0 = 5                      # distinct W0 buffers cycled by the quantize step
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time of the oracle baseline")
+    p.add_argument("--copy-calibrate", action="store_true",
+                   help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device.h"):
+        with open(os.path.join(ROOT, "quantized_rank_fine_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, launches_flops_key):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_4096x4096_r16_M2048_hbm.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibrate():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def cpu_baseline(w0, X, dY, A, B, min_seconds):
+    """The oracle, as it stands, on the same workload: full quantize of W0
+    (fp32 numpy, one thread) and full forward+backward of all tokens
+    (dequantize + float64 BLAS matmuls), repeated until `min_seconds` of CPU
+    work have been timed (at most 5 repetitions)."""
+    import oracle
+    from quantized_rank_fine_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = os.cpu_count()
+    n_in, n_out = w0.shape
+    M, r = X.shape[0], A.shape[1]
+    tq = tf = 0.0
+    reps = 0
+    while (tq + tf) < min_seconds and reps < 5:
+        t0 = time.perf_counter()
+        qd = oracle.quantize(w0)
+        t1 = time.perf_counter()
+        W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], n_in, n_out)
+        XA, y = oracle.forward(X, W, A, B)
+        g = oracle.backward(X, dY, W, A, B, XA)
+        t2 = time.perf_counter()
+        del W, XA, y, g, qd
+        tq += t1 - t0
+        tf += t2 - t1
+        reps += 1
+    flops = workloads.fwd_flops(M, n_in, n_out, r) + workloads.bwd_flops(M, n_in, n_out, r)
+    qbytes = workloads.quantize_bytes(n_in, n_out)
+    return {
+        "value": round(reps * flops / tf / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(blas),
+        "kind": "oracle",
+        "sample": (f"the full step {reps} time(s): quantize of the 4096x4096 W0 in fp32 numpy "
+                   f"(1 thread, {tq / reps:.2f} s each) and fwd+bwd of all {M} tokens "
+                   f"(dequantize + float64 BLAS on {blas} threads, {tf / reps:.2f} s each)"),
+        "quantize_GBps": round(reps * qbytes / tq / 1e9, 4),
+        "host_cpu_count": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibrate:
+        copy_calibrate()
+        return
+
+    import numpy as np
+    import torch
+
+    from quantized_rank_fine_amd import qlora as q
+    from quantized_rank_fine_amd import synth, workloads
+
+    wl = workloads.WORKLOADS[1]
+    _, n_in, n_out = wl["linears"][0]
+    r, M = wl["rank"], wl["tokens"][0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16_dev(t):
+        return torch.from_numpy(t.raw.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    w0_host = [synth.weights(n_in, n_out, 1, layer=i) for i in range(N_W0)]
+    W0s = [torch.from_numpy(w).to(dev) for w in w0_host]
+    Xs = synth.activations(M, n_in, 1, "bf16")
+    dYs = synth.activations(M, n_out, 1, "bf16", tensor=synth.T_DY)
+    As, Bs = synth.adapters(n_in, n_out, r, 1, "bf16")
+    X, dY, A, B = bf16_dev(Xs), bf16_dev(dYs), bf16_dev(As), bf16_dev(Bs)
+    wq = q.NF4Weight(n_in, n_out, dev)
+    Y = torch.empty(M, n_out, dtype=torch.bfloat16, device=dev)
+    XA = torch.empty(M, r, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, n_in, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(n_in, r, dtype=torch.float32, device=dev)
+    dB = torch.empty(r, n_out, dtype=torch.float32, device=dev)
+    fwb = q.qlora_fwd_workspace_bytes(M, n_in, n_out, r, q.BF16)
+    bwb = q.qlora_bwd_workspace_bytes(M, n_in, n_out, r, q.BF16)
+    wsf = torch.empty(fwb, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bwb, dtype=torch.uint8, device=dev)
+
+    def quantize(i):
+        q.qlora_quantize(W0s[i % N_W0], wq)
+
+    def fwd_bwd():
+        q.qlora_linear_fwd(wq, X, M, q.BF16, A, B, r, q.BF16, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd(wq, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
+
+    for i in range(args.warmup):
+        quantize(i)
+        fwd_bwd()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    q.qlora_timing_reset()
+    q.qlora_timing_enable(["quantize", "fwd_gemm", "dx_gemm"])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        quantize(i)
+        ev[i][1].record()
+        fwd_bwd()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    q.qlora_timing_disable()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
+    fb_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
+    flops = workloads.fwd_flops(M, n_in, n_out, r) + workloads.bwd_flops(M, n_in, n_out, r)
+    qbytes = workloads.quantize_bytes(n_in, n_out)
+    value = K * flops / (fb_ms * 1e-3) / 1e12
+    q_gbps = K * qbytes / (q_ms * 1e-3) / 1e9
+
+    kernels = {}
+    per_launch_flops = {"fwd_gemm": 2 * M * n_out * (n_in + r),
+                        "dx_gemm": 2 * M * n_in * (n_out + r)}
+    for name in ("fwd_gemm", "dx_gemm"):
+        tot, n = q.qlora_timing_read(q.KERNELS.index(name))
+        avg = tot / max(n, 1)
+        ach = per_launch_flops[name] / (avg * 1e-3) / 1e12
+        kernels[name] = {"launches": n, "avg_us": round(avg * 1e3, 2),
+                         "algorithmic_flop": per_launch_flops[name],
+                         "TFLOPs": round(ach, 2), "frac_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
+    tot, n = q.qlora_timing_read(q.KERNELS.index("quantize"))
+    qavg = tot / max(n, 1)
+    kernels["quantize"] = {"launches": n, "avg_us": round(qavg * 1e3, 2),
+                           "algorithmic_bytes": qbytes,
+                           "GBps": round(qbytes / (qavg * 1e-3) / 1e9, 1),
+                           "frac_hbm_peak": round(qbytes / (qavg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    dom = max(("fwd_gemm", "dx_gemm"), key=lambda k: kernels[k]["avg_us"])
+    roof = {"bound": "mfma", "kernel": dom,
+            "achieved": kernels[dom]["TFLOPs"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": kernels[dom]["frac_bf16_peak"],
+            "traffic": read_traffic(dom, "flops")}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) bf16 activations)",
+        "config": {"workload": wl["name"], "in": n_in, "out": n_out, "rank": r, "tokens": M,
+                   "step": "quantize+fwd+bwd", "w0_buffers_cycled": N_W0},
+        "quantize_GBps": round(q_gbps, 2),
+        "quantize_frac_hbm": round(q_gbps / PEAK_HBM_GBPS, 4),
+        "fwd_bwd_ms_per_step": round(fb_ms / K, 4),
+        "quantize_ms_per_step": round(q_ms / K, 4),
+        "fwd_bwd_frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w0_host[0], Xs.values, dYs.values, As.values,
+                                           Bs.values, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -123,17 +123,19 @@ qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t st
  * The base weight is expanded to bf16 in registers, w = bf16(L[code] *
  * (q_b * s2_g)) computed in fp32; X (and XA, B) enter the bf16 matrix cores
  * rounded to bf16; accumulation is fp32.  ws must hold
- * qlora_fwd_workspace_bytes(M, in, out, r) bytes of device memory.  r = 0
- * gives a plain NF4 linear (A, B, XA, ws may be NULL).  M = 0 is a no-op.
+ * qlora_fwd_workspace_bytes(M, in, out, r, act) bytes of device memory.
+ * r = 0 gives a plain NF4 linear (A, B, XA may be NULL).  M = 0 is a no-op
+ * (ws may be NULL).
  */
 qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M,
                               qlora_dtype act, const void *A, const void *B,
                               int32_t r, qlora_dtype adt, void *Y, float *XA,
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes qlora_linear_fwd needs for this shape (host-only); 0 when
- * r == 0 or M == 0 (ws may then be NULL). */
-size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r);
+/* Workspace bytes qlora_linear_fwd needs for this shape and activation dtype
+ * (host-only); 0 when M == 0 or the arguments are invalid. */
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
+                                 qlora_dtype act);
 
 /*
  * qlora_linear_bwd: with G = dY.B^T,
@@ -143,9 +145,9 @@ size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r);
  * ("How it works" steps 3-4: dA = dW B^T and dB = A^T dW with dW = X^T dY,
  * evaluated in factored form so dW is never formed; the base weight gets no
  * gradient.)  XA is the forward's saved X.A (fp32 [M, r]); NULL recomputes it
- * into the workspace.  ws must hold qlora_bwd_workspace_bytes(M, in, out, r)
- * bytes of device memory.  r = 0 computes dX only (A, B, dA, dB, XA may be
- * NULL).  M = 0 writes zeros to dA and dB.
+ * into the workspace.  ws must hold qlora_bwd_workspace_bytes(M, in, out, r,
+ * act) bytes of device memory.  r = 0 computes dX only (A, B, dA, dB, XA may
+ * be NULL).  M = 0 writes zeros to dA and dB (ws may be NULL).
  */
 qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY,
                               int64_t M, qlora_dtype act, const void *A,
@@ -153,8 +155,10 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
                               const float *XA, void *dX, float *dA, float *dB,
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes qlora_linear_bwd needs for this shape (host-only). */
-size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r);
+/* Workspace bytes qlora_linear_bwd needs for this shape and activation dtype
+ * (host-only); 0 when M == 0 or the arguments are invalid. */
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
+                                 qlora_dtype act);
 
 /* Human-readable name of a status code (host-only, static string). */
 const char *qlora_status_string(qlora_status s);
@@ -168,11 +172,12 @@ void qlora_levels(float out[16]);
 void qlora_thresholds(float out[15]);
 
 /*
- * Kernel-level event timing (instrumentation; off by default).  While
- * enabled, every kernel the library launches is bracketed by a pair of HIP
- * events recorded on the call's stream.  qlora_timing_read synchronizes those
- * events and returns the summed duration (ms) and the number of launches of
- * one kernel kind since the last reset.  Not thread-safe.
+ * Kernel-level event timing (instrumentation; off by default).
+ * qlora_timing_enable(mask): bit k of mask selects kernel kind k; every
+ * launch of a selected kind is bracketed by a pair of HIP events recorded on
+ * the call's stream (mask 0 turns timing off).  qlora_timing_read
+ * synchronizes those events and returns the summed duration (ms) and the
+ * number of launches of one kind since the last reset.  Not thread-safe.
  */
 typedef enum {
   QLORA_KERNEL_QUANTIZE = 0,
@@ -186,7 +191,7 @@ typedef enum {
   QLORA_KERNEL_COUNT = 8
 } qlora_kernel_kind;
 
-int qlora_timing_enable(int on);
+int qlora_timing_enable(int kind_mask);
 int qlora_timing_read(int kind, double *total_ms, int64_t *launches);
 void qlora_timing_reset(void);
 const char *qlora_kernel_name(int kind);

@@ -31,6 +31,9 @@ DEVICE = [
     f"--offload-arch={ARCH}",
     # keep packed fp32 ALU ops out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in the VGPR file: avoids AGPR<->VGPR copies of the
+    # loop-carried accumulators
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -32,7 +32,7 @@ bool shape_ok(int64_t in, int64_t out) {
 
 // ---------------------------------------------------------------- timing
 struct TimingState {
-  bool on = false;
+  int mask = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[QLORA_KERNEL_COUNT];
   double total_ms[QLORA_KERNEL_COUNT] = {};
   int64_t launches[QLORA_KERNEL_COUNT] = {};
@@ -41,7 +41,7 @@ TimingState g_timing;
 
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F &&launch) {
-  if (!g_timing.on) return launch();
+  if (!(g_timing.mask & (1 << kind))) return launch();
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
   (void)hipEventRecord(a, s);
@@ -54,57 +54,78 @@ hipError_t timed(int kind, hipStream_t s, F &&launch) {
 qlora_status dev(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE; }
 
 // ---------------------------------------------------------------- plans
-struct FwdPlan {
-  int64_t ks = 0;
-  size_t off_at = 0, off_bt = 0, off_part = 0, total = 0;
+// Workspace layouts.  Every region starts on a 256-byte boundary.
+
+#ifndef QLORA_EXACT_EXPAND
+#define QLORA_EXACT_EXPAND 1
+#endif
+constexpr bool kExact = QLORA_EXACT_EXPAND != 0;
+
+struct Layout {
+  size_t o = 0;
+  size_t take(size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  }
 };
 
-FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r) {
+struct FwdPlan {
+  int64_t ks = 0, rp = 0;
+  size_t off_x16 = 0, off_cs = 0, off_at = 0, off_bt = 0, off_part = 0, off_xa16 = 0, total = 0;
+};
+
+FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   FwdPlan p;
-  if (r == 0 || M == 0) return p;
-  p.ks = rowdot_splits(M, in, r);
-  size_t o = 0;
-  p.off_at = o;
-  o = align_up(o + size_t(r) * in * 2);
-  p.off_bt = o;
-  o = align_up(o + size_t(out) * rank_pad32(r) * 2);
-  p.off_part = o;
-  o = align_up(o + size_t(p.ks) * M * r * 4);
-  p.total = o;
+  if (M == 0) return p;
+  Layout L;
+  p.off_x16 = act_bf16 ? 0 : L.take(size_t(M) * in * 2);
+  p.off_cs = L.take(size_t(in) * (out / 64) * 4);
+  if (r > 0) {
+    p.rp = rank_pad32(r);
+    p.ks = rowdot_splits(M, in, r);
+    p.off_at = L.take(size_t(r) * in * 2);
+    p.off_bt = L.take(size_t(out) * p.rp * 2);
+    p.off_part = L.take(size_t(p.ks) * M * r * 4);
+    p.off_xa16 = L.take(size_t(M) * p.rp * 2);
+  }
+  p.total = L.o;
   return p;
 }
 
 struct BwdPlan {
-  int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0;
-  size_t off_bq = 0, off_gpart = 0, off_g16 = 0, off_gt16 = 0;
+  int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0, rp = 0, ldM = 0;
+  size_t off_dy16 = 0, off_cs = 0, off_bq = 0, off_gpart = 0, off_g16 = 0, off_gt16 = 0;
   size_t off_at = 0, off_xapart = 0, off_xa = 0, off_xat16 = 0;
-  size_t off_dbpart = 0, off_dapart = 0, total = 0;
+  size_t off_dbpart = 0, off_dapart = 0, off_a16 = 0, total = 0;
 };
 
-BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r) {
+BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   BwdPlan p;
-  if (r == 0 || M == 0) return p;
-  p.ks_g = rowdot_splits(M, out, r);
-  p.ks_x = rowdot_splits(M, in, r);
-  p.ks_b = coldot_splits(M, out, r);
-  p.ks_a = coldot_splits(M, in, r);
-  size_t o = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = o;
-    o = align_up(o + bytes);
-    return at;
-  };
-  p.off_bq = take(size_t(r) * out * 2);
-  p.off_gpart = take(size_t(p.ks_g) * M * r * 4);
-  p.off_g16 = take(size_t(M) * rank_pad32(r) * 2);
-  p.off_gt16 = take(size_t(pad8(M)) * r * 2);
-  p.off_at = take(size_t(r) * in * 2);
-  p.off_xapart = take(size_t(p.ks_x) * M * r * 4);
-  p.off_xa = take(size_t(M) * r * 4);
-  p.off_xat16 = take(size_t(pad8(M)) * r * 2);
-  p.off_dbpart = take(size_t(p.ks_b) * out * r * 4);
-  p.off_dapart = take(size_t(p.ks_a) * in * r * 4);
-  p.total = o;
+  if (M == 0) return p;
+  Layout L;
+  p.off_dy16 = act_bf16 ? 0 : L.take(size_t(M) * out * 2);
+  p.off_cs = L.take(size_t(in) * (out / 64) * 4);
+  if (r > 0) {
+    p.rp = rank_pad32(r);
+    p.ldM = pad8(M);
+    p.ks_g = rowdot_splits(M, out, r);
+    p.ks_x = rowdot_splits(M, in, r);
+    p.ks_b = coldot_splits(M, out, r);
+    p.ks_a = coldot_splits(M, in, r);
+    p.off_bq = L.take(size_t(r) * out * 2);
+    p.off_gpart = L.take(size_t(p.ks_g) * M * r * 4);
+    p.off_g16 = L.take(size_t(M) * p.rp * 2);
+    p.off_gt16 = L.take(size_t(p.ldM) * r * 2);
+    p.off_at = L.take(size_t(r) * in * 2);
+    p.off_xapart = L.take(size_t(p.ks_x) * M * r * 4);
+    p.off_xa = L.take(size_t(M) * r * 4);
+    p.off_xat16 = L.take(size_t(p.ldM) * r * 2);
+    p.off_dbpart = L.take(size_t(p.ks_b) * out * r * 4);
+    p.off_dapart = L.take(size_t(p.ks_a) * in * r * 4);
+    p.off_a16 = L.take(size_t(in) * p.rp * 2);
+  }
+  p.total = L.o;
   return p;
 }
 
@@ -139,14 +160,16 @@ const char *qlora_status_string(qlora_status s) {
   return "unknown status";
 }
 
-size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r) {
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out)) return 0;
-  return plan_fwd(M, in, out, r).total;
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
+                                 qlora_dtype act) {
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out) || !dtype_ok(act)) return 0;
+  return plan_fwd(M, in, out, r, act == QLORA_BF16).total;
 }
 
-size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r) {
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out)) return 0;
-  return plan_bwd(M, in, out, r).total;
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
+                                 qlora_dtype act) {
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out) || !dtype_ok(act)) return 0;
+  return plan_bwd(M, in, out, r, act == QLORA_BF16).total;
 }
 
 qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t stream) {
@@ -169,43 +192,45 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
   if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
   if (M == 0) return QLORA_OK;
-  if (!X || !Y) return QLORA_ERR_NULL;
-  if (!aligned16(X) || !aligned16(Y)) return QLORA_ERR_ALIGN;
-  const FwdPlan p = plan_fwd(M, wq->in, wq->out, r);
+  if (!X || !Y || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (r > 0) {
-    if (!A || !B || !XA || !ws) return QLORA_ERR_NULL;
-    if (!aligned16(A) || !aligned16(B) || !aligned16(XA) || !aligned16(ws))
-      return QLORA_ERR_ALIGN;
-    if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+    if (!A || !B || !XA) return QLORA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(XA)) return QLORA_ERR_ALIGN;
   }
-  const int64_t in = wq->in, out = wq->out;
   const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
+  const int64_t in = wq->in, out = wq->out;
+  const FwdPlan p = plan_fwd(M, in, out, r, xb);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
   hipError_t e = hipSuccess;
-  uint16_t *Bt = nullptr;
+#define QLORA_RUN(KIND, CALL)                              \
+  do {                                                     \
+    e = timed(KIND, stream, [&] { return CALL; });         \
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;          \
+  } while (0)
+  const uint16_t *X16 = static_cast<const uint16_t *>(X);
+  if (!xb) {
+    uint16_t *x16 = at<uint16_t>(ws, p.off_x16);
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(X, false, M * in, x16, stream));
+    X16 = x16;
+  }
+  float *cs = at<float>(ws, p.off_cs);
+  QLORA_RUN(QLORA_KERNEL_REDUCE, launch_scales(wq->qscale, wq->gscale, in, out, cs, stream));
+  uint16_t *Bt = nullptr, *XA16 = nullptr;
   if (r > 0) {
     uint16_t *At = at<uint16_t>(ws, p.off_at);
     Bt = at<uint16_t>(ws, p.off_bt);
+    XA16 = at<uint16_t>(ws, p.off_xa16);
     float *part = at<float>(ws, p.off_part);
-    e = timed(QLORA_KERNEL_REDUCE, stream,
-              [&] { return launch_transpose_to_bf16(A, ab, in, r, At, in, stream); });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
-      return launch_transpose_to_bf16(B, ab, r, out, Bt, rank_pad32(r), stream);
-    });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-    e = timed(QLORA_KERNEL_XA, stream,
-              [&] { return launch_rowdot(X, xb, At, M, in, r, part, stream); });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
-      return launch_reduce(part, p.ks, M, r, XA, false, nullptr, 0, nullptr, 0, stream);
-    });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_transpose_to_bf16(A, ab, in, r, At, in, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_transpose_to_bf16(B, ab, r, out, Bt, p.rp, stream));
+    QLORA_RUN(QLORA_KERNEL_XA, launch_rowdot(X16, true, At, M, in, r, part, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE,
+              launch_reduce(part, p.ks, M, r, XA, false, XA16, p.rp, nullptr, 0, stream));
   }
-  e = timed(QLORA_KERNEL_FWD_GEMM, stream, [&] {
-    return launch_fwd_gemm(wq->codes, wq->qscale, wq->gscale, in, out, X, xb, M, XA, Bt, r, Y,
-                           stream);
-  });
-  return dev(e);
+  QLORA_RUN(QLORA_KERNEL_FWD_GEMM, launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, Bt,
+                                                   int32_t(p.rp), Y, xb, kExact, stream));
+  return QLORA_OK;
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int64_t M,
@@ -223,105 +248,86 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
       return QLORA_ERR_ALIGN;
     if (XA && !aligned16(XA)) return QLORA_ERR_ALIGN;
   }
-  if (M > 0) {
-    if (!dY) return QLORA_ERR_NULL;
-    if (!aligned16(dY)) return QLORA_ERR_ALIGN;
-    if (r > 0 && !X) return QLORA_ERR_NULL;
-    if (X && !aligned16(X)) return QLORA_ERR_ALIGN;
-    if (dX && !aligned16(dX)) return QLORA_ERR_ALIGN;
-  }
-  const BwdPlan p = plan_bwd(M, in, out, r);
-  if (p.total > 0) {
-    if (!ws) return QLORA_ERR_NULL;
-    if (!aligned16(ws)) return QLORA_ERR_ALIGN;
-    if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
-  }
+  const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
   hipError_t e = hipSuccess;
   if (M == 0) {
     if (r > 0) {
-      e = launch_fill_zero(dA, in * r, stream);
-      if (e == hipSuccess) e = launch_fill_zero(dB, int64_t(r) * out, stream);
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fill_zero(dA, in * r, stream));
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fill_zero(dB, int64_t(r) * out, stream));
     }
-    return dev(e);
+    return QLORA_OK;
   }
-  const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
-  uint16_t *G16 = nullptr;
+  if (!dY || !ws) return QLORA_ERR_NULL;
+  if (r > 0 && !X) return QLORA_ERR_NULL;
+  if (!aligned16(dY) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (X && !aligned16(X)) return QLORA_ERR_ALIGN;
+  if (dX && !aligned16(dX)) return QLORA_ERR_ALIGN;
+  const BwdPlan p = plan_bwd(M, in, out, r, xb);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+
+  const uint16_t *dY16 = static_cast<const uint16_t *>(dY);
+  if (!xb && dX) {
+    uint16_t *d16 = at<uint16_t>(ws, p.off_dy16);
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(dY, false, M * out, d16, stream));
+    dY16 = d16;
+  }
+  uint16_t *G16 = nullptr, *A16 = nullptr;
   if (r > 0) {
-    // G = dY . B^T  (rowdot with Qt = B as bf16, contraction over out)
+    // G = dY . B^T  (rowdot with Qt = B in bf16, contraction over out)
     const uint16_t *Bq = static_cast<const uint16_t *>(B);
     if (!ab) {
       uint16_t *bq = at<uint16_t>(ws, p.off_bq);
-      e = timed(QLORA_KERNEL_REDUCE, stream,
-                [&] { return launch_convert_to_bf16(B, false, int64_t(r) * out, bq, stream); });
-      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(B, false, int64_t(r) * out, bq, stream));
       Bq = bq;
     }
     float *gpart = at<float>(ws, p.off_gpart);
     G16 = at<uint16_t>(ws, p.off_g16);
     uint16_t *Gt16 = at<uint16_t>(ws, p.off_gt16);
-    e = timed(QLORA_KERNEL_DY_PASS, stream,
-              [&] { return launch_rowdot(dY, xb, Bq, M, out, r, gpart, stream); });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-    const int64_t ldM = pad8(M);
-    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
-      return launch_reduce(gpart, p.ks_g, M, r, nullptr, false, G16, rank_pad32(r), Gt16, ldM,
-                           stream);
-    });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-
-    // XA^T in bf16 (from the saved XA, or recomputed)
+    QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_rowdot(dY, xb, Bq, M, out, r, gpart, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp,
+                                                 Gt16, p.ldM, stream));
+    // XA^T in bf16, from the saved XA or recomputed
     uint16_t *XAt16 = at<uint16_t>(ws, p.off_xat16);
     if (!XA) {
       uint16_t *At = at<uint16_t>(ws, p.off_at);
       float *xpart = at<float>(ws, p.off_xapart);
       float *xaw = at<float>(ws, p.off_xa);
-      e = timed(QLORA_KERNEL_REDUCE, stream,
-                [&] { return launch_transpose_to_bf16(A, ab, in, r, At, in, stream); });
-      if (e != hipSuccess) return QLORA_ERR_DEVICE;
-      e = timed(QLORA_KERNEL_XA, stream,
-                [&] { return launch_rowdot(X, xb, At, M, in, r, xpart, stream); });
-      if (e != hipSuccess) return QLORA_ERR_DEVICE;
-      e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
-        return launch_reduce(xpart, p.ks_x, M, r, xaw, false, nullptr, 0, XAt16, ldM, stream);
-      });
-      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_transpose_to_bf16(A, ab, in, r, At, in, stream));
+      QLORA_RUN(QLORA_KERNEL_XA, launch_rowdot(X, xb, At, M, in, r, xpart, stream));
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
+                                                   XAt16, p.ldM, stream));
     } else {
-      e = timed(QLORA_KERNEL_REDUCE, stream,
-                [&] { return launch_transpose_to_bf16(XA, false, M, r, XAt16, ldM, stream); });
-      if (e != hipSuccess) return QLORA_ERR_DEVICE;
+      QLORA_RUN(QLORA_KERNEL_REDUCE,
+                launch_transpose_to_bf16(XA, false, M, r, XAt16, p.ldM, stream));
     }
-
-    // dB = XA^T . dY : coldot over M of dY with XA^T, stored transposed
+    // dB = XA^T . dY : coldot over tokens of dY with XA^T, stored transposed
     float *dbpart = at<float>(ws, p.off_dbpart);
-    e = timed(QLORA_KERNEL_DY_PASS, stream,
-              [&] { return launch_coldot(dY, xb, XAt16, ldM, M, out, r, dbpart, stream); });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
-      return launch_reduce(dbpart, p.ks_b, out, r, dB, true, nullptr, 0, nullptr, 0, stream);
-    });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-
-    // dA = X^T . G : coldot over M of X with G^T
+    QLORA_RUN(QLORA_KERNEL_DY_PASS,
+              launch_coldot(dY, xb, XAt16, p.ldM, M, out, r, dbpart, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(dbpart, p.ks_b, out, r, dB, true, nullptr, 0,
+                                                 nullptr, 0, stream));
+    // dA = X^T . G : coldot over tokens of X with G^T
     float *dapart = at<float>(ws, p.off_dapart);
-    e = timed(QLORA_KERNEL_DA_PASS, stream,
-              [&] { return launch_coldot(X, xb, Gt16, ldM, M, in, r, dapart, stream); });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
-    e = timed(QLORA_KERNEL_REDUCE, stream, [&] {
-      return launch_reduce(dapart, p.ks_a, in, r, dA, false, nullptr, 0, nullptr, 0, stream);
-    });
-    if (e != hipSuccess) return QLORA_ERR_DEVICE;
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_coldot(X, xb, Gt16, p.ldM, M, in, r, dapart, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
+                                                 nullptr, 0, stream));
+    if (dX) {
+      A16 = at<uint16_t>(ws, p.off_a16);
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_pad_to_bf16(A, ab, in, r, A16, p.rp, stream));
+    }
   }
   if (dX) {
-    e = timed(QLORA_KERNEL_DX_GEMM, stream, [&] {
-      return launch_dx_gemm(wq->codes, wq->qscale, wq->gscale, in, out, dY, xb, M, G16, A, ab, r,
-                            dX, stream);
-    });
+    float *cs = at<float>(ws, p.off_cs);
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_scales(wq->qscale, wq->gscale, in, out, cs, stream));
+    QLORA_RUN(QLORA_KERNEL_DX_GEMM, launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, A16,
+                                                   int32_t(p.rp), dX, xb, kExact, stream));
   }
-  return dev(e);
+  return QLORA_OK;
+#undef QLORA_RUN
 }
 
-int qlora_timing_enable(int on) {
-  g_timing.on = on != 0;
+int qlora_timing_enable(int kind_mask) {
+  g_timing.mask = kind_mask & ((1 << QLORA_KERNEL_COUNT) - 1);
   return 0;
 }
 

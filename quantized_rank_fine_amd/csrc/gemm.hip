@@ -5,27 +5,34 @@
 //
 // "QLoRA (low-rank adapters on a quantized model)", "What QLoRA adds": the
 // frozen 4-bit weights are expanded to bf16 on the fly for each matmul and
-// never updated; "How it works": W = Wq + A B with the rank-r term added as
-// "one small extra matmul".  Here that extra matmul runs on the same
-// accumulators after the main K loop.
+// never updated; "How it works": W = Wq + A B, the rank-r term being "one
+// small extra matmul" -- here it runs on the same accumulators after the
+// main K loop.
 //
-// Tiling (both kernels): workgroup 256 threads = 4 wavefronts in 2 x 2, tile
-// 256 (M) x 128 (N) x 64 (K); each wavefront owns 128 x 64 of the output as
-// 8 x 4 tiles of v_mfma_f32_16x16x32_bf16.  X / dY tiles are staged in LDS
-// (16-B chunks XOR-swizzled, double-buffered); the weight tile is staged as
-// raw packed codes (1/4 of the bf16 bytes) and expanded in registers:
-//   w = bf16(L[code] * (q_b * s2_g)), L looked up with v_perm byte planes.
+// Workgroup: 256 threads = 4 wavefronts side by side along N; tile 256 (M) x
+// 128 (N) x 64 (K); each wavefront owns all 256 rows x 32 columns as 16 x 2
+// tiles of v_mfma_f32_16x16x32_bf16, so every weight of the tile is expanded
+// exactly once per workgroup.  Tiles stream through a 3-stage LDS ring filled
+// by buffer_load ... lds (the K offset is a scalar; rows past M read as 0).
+// Activation tiles are row-major with 16-B chunks XOR-swizzled by row; the
+// weight tile is raw packed codes (1/4 of its bf16 size) and the per-block
+// scales c_b = q_b * s2_g come from a small fp32 array laid out [block][row].
 // K slots are permuted inside each 64-wide K tile: lane group h of the MFMA
-// owns k = 16h .. 16h+15 (8 per substep), for both operands.
+// owns k = 16h .. 16h+15 (8 per substep), identically for both operands.
 //
-// Forward: the code tile is (64 k-rows) x (128 n-cols) nibbles, n-contiguous;
-// ds_read_b64_tr_b4 hands lane i of a 16-lane group column i of the 16 rows
-// the group points at, i.e. 16 consecutive k of one column, in one read.
-// Every wavefront's 64 columns form one 64-wide scale block, so its scales
-// depend on k only (16 per lane per K tile).
-// Backward dX: the code tile is (128 W-rows) x (64 W-cols); the contraction
-// runs along a W row, so a plain 8-byte read gives 16 consecutive k, and the
-// K tile is one scale block, so each W row has a single scale per tile.
+// Forward: the code tile is 64 k-rows x 128 n-cols, n-contiguous;
+// ds_read_b64_tr_b4 gives lane i of a 16-lane group column i of the 16 rows
+// the group points at (16 consecutive k of one column) in one read.  The
+// scale of a weight depends on its k row (and the wavefront's block column).
+// Backward dX: the code tile is 128 W-rows x 64 W-cols and the contraction
+// runs along a W row: a plain 8-byte read gives 16 consecutive k, all under
+// one scale (the K tile is one 64-wide block).
+//
+// Expansion: w = bf16(level * scale) with level = L[code] from a 16-entry
+// table held as v_perm byte planes (sign-symmetric: 8 magnitudes).  kExact
+// selects the fp32 table (w rounded once from the fp32 product); otherwise
+// the level is rounded to bf16 first (fewer VALU operations, w within one
+// bf16 ulp of the fp32 product).
 #include "device.h"
 
 namespace qlora {
@@ -37,18 +44,98 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kFwdCodePitch = 72;   // bytes per k-row of the forward code tile
-constexpr int kDxCodePitch = 40;    // bytes per W-row of the dX code tile
+constexpr int kStages = 3;
+constexpr int kXBytes = BM * BK * 2;     // 32 KiB activation tile
+constexpr int kCBytes = 4096;            // code tile
+constexpr int kSBytes = 1024;            // scales (512 B used)
+constexpr int kStageBytes = kXBytes + kCBytes + kSBytes;
+constexpr int kLdsBytes = kStages * kStageBytes;   // 120 KiB
+constexpr uint32_t kBufFlags = 0x00020000u;
+constexpr int kLoadsPerTile = 10;        // per wavefront: 8 X + 1 code + 1 scale
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// 8 codes (nibble t = k slot t) times per-slot scales -> MFMA bf16 operand.
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0) over [base, base + bytes); loads past the
+// end return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : int32_t(bytes));
+  rsrc_t r = {int32_t(uint32_t(b)), int32_t(uint32_t(b >> 32) & 0xffffu), n, int32_t(kBufFlags)};
+  r[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  r[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_char *)(p)));
+}
+
+// buffer_load ... lds: each lane's 16 (or 4) bytes land at M0 + 16*lane (4*lane).
+// Issued from inline assembly so that the compiler does not fold its own
+// conservative wait for these LDS writes into the pipeline's vmcnt waits; the
+// ring protocol below waits and synchronizes explicitly.  No register is
+// written by these loads.
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
+__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
+
+// ------------------------------------------------------------- expansion
+// Four codes (bytes of v, values 0..15) -> four levels as fp32.
+template <bool kExact>
+__device__ __forceinline__ void levels4(uint32_t v, const ExpandConsts &t, float out[4]) {
+  const uint32_t u = v ^ 0x08080808u;            // c>=8 -> c-8 ; c<8 -> c+8
+  const uint32_t b3 = u & 0x08080808u;           // 8 where the level is negative
+  const uint32_t m7 = b3 - (b3 >> 3);            // 7 where negative
+  const uint32_t m = (u ^ m7) & 0x07070707u;     // magnitude index 0..7
+  const uint32_t p2 = perm_b32(t.plane[2][1], t.plane[2][0], m);
+  const uint32_t p3 = perm_b32(t.plane[3][1], t.plane[3][0], m) | (b3 << 4);
+  if constexpr (kExact) {
+    const uint32_t p0 = perm_b32(t.plane[0][1], t.plane[0][0], m);
+    const uint32_t p1 = perm_b32(t.plane[1][1], t.plane[1][0], m);
+    const uint32_t a = perm_b32(p1, p0, 0x05010400u);
+    const uint32_t b = perm_b32(p1, p0, 0x07030602u);
+    const uint32_t c = perm_b32(p3, p2, 0x05010400u);
+    const uint32_t d = perm_b32(p3, p2, 0x07030602u);
+    out[0] = __uint_as_float(perm_b32(c, a, 0x05040100u));
+    out[1] = __uint_as_float(perm_b32(c, a, 0x07060302u));
+    out[2] = __uint_as_float(perm_b32(d, b, 0x05040100u));
+    out[3] = __uint_as_float(perm_b32(d, b, 0x07060302u));
+  } else {
+    // bf16 levels: bytes 2 and 3 of the fp32 pattern, low half zero
+    out[0] = __uint_as_float(perm_b32(p3, p2, 0x04000c0cu));
+    out[1] = __uint_as_float(perm_b32(p3, p2, 0x05010c0cu));
+    out[2] = __uint_as_float(perm_b32(p3, p2, 0x06020c0cu));
+    out[3] = __uint_as_float(perm_b32(p3, p2, 0x07030c0cu));
+  }
+}
+
+// 8 codes (nibble t = k slot t) x per-slot scales -> MFMA bf16 operand.
+template <bool kExact>
 __device__ __forceinline__ u32x4_t expand8(uint32_t d, const float *s, const ExpandConsts &tb) {
   float le[4], lo[4];
-  lookup4(d & 0x0F0F0F0Fu, tb, le);
-  lookup4((d >> 4) & 0x0F0F0F0Fu, tb, lo);
+  levels4<kExact>(d & 0x0F0F0F0Fu, tb, le);
+  levels4<kExact>((d >> 4) & 0x0F0F0F0Fu, tb, lo);
   u32x4_t r;
   r[0] = pack_bf16x2(le[0] * s[0], lo[0] * s[1]);
   r[1] = pack_bf16x2(le[1] * s[2], lo[1] * s[3]);
@@ -57,11 +144,11 @@ __device__ __forceinline__ u32x4_t expand8(uint32_t d, const float *s, const Exp
   return r;
 }
 
-// Same with one scale for all 8 slots.
+template <bool kExact>
 __device__ __forceinline__ u32x4_t expand8u(uint32_t d, float s, const ExpandConsts &tb) {
   float le[4], lo[4];
-  lookup4(d & 0x0F0F0F0Fu, tb, le);
-  lookup4((d >> 4) & 0x0F0F0F0Fu, tb, lo);
+  levels4<kExact>(d & 0x0F0F0F0Fu, tb, le);
+  levels4<kExact>((d >> 4) & 0x0F0F0F0Fu, tb, lo);
   u32x4_t r;
   r[0] = pack_bf16x2(le[0] * s, lo[0] * s);
   r[1] = pack_bf16x2(le[1] * s, lo[1] * s);
@@ -70,22 +157,10 @@ __device__ __forceinline__ u32x4_t expand8u(uint32_t d, float s, const ExpandCon
   return r;
 }
 
-template <bool kBf16>
-__device__ __forceinline__ u32x4_t load8(const void *base, int64_t idx) {
-  if constexpr (kBf16) {
-    return *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(base) + idx);
-  } else {
-    const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
-    float4 a = q[0], b = q[1];
-    return u32x4_t{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                   pack_bf16x2(b.z, b.w)};
-  }
-}
-
-// Map the linear workgroup id to a (m-tile, n-tile): workgroups are dealt to
-// the 8 XCDs round-robin, so tile index T = (id % 8) * (n / 8) + id / 8 gives
-// each XCD a contiguous run of tiles sharing m-tiles (and their X rows in the
-// XCD's L2).
+// Map the linear workgroup id to a (m-tile, n-tile).  Workgroups are dealt
+// to the 8 XCDs round-robin; T = (id % 8) * (n / 8) + id / 8 gives each XCD a
+// contiguous run of tiles, which share m-tiles (their activation rows stay in
+// that XCD's L2).
 __device__ __forceinline__ void tile_of(int nt_count, int &mt, int &nt) {
   const int n = gridDim.x, id = blockIdx.x;
   const int T = (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
@@ -93,354 +168,351 @@ __device__ __forceinline__ void tile_of(int nt_count, int &mt, int &nt) {
   nt = T % nt_count;
 }
 
-// ---------------------------------------------------------------- A staging
-// BM x BK tile of a row-major [M x K] activation into LDS, bf16, 16-B chunks
-// at position (c ^ (row & 7)).  Thread t loads rows t/8 + 32j, chunk t%8.
-template <bool kBf16>
-__device__ __forceinline__ void load_a_tile(const void *Av, int64_t M, int64_t K, int64_t m0,
-                                            int64_t k0, u32x4_t (&reg)[8]) {
-  const int t = threadIdx.x;
-  const int c = t & 7;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = (t >> 3) + 32 * j;
-    const int64_t gm = m0 + row;
-    reg[j] = (gm < M) ? load8<kBf16>(Av, gm * K + k0 + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-}
+// LDS address (bytes) of the 16-B chunk `c` of activation row `row`.
+__device__ __forceinline__ uint32_t xoff(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 
-__device__ __forceinline__ void store_a_tile(uint16_t *sA, const u32x4_t (&reg)[8]) {
-  const int t = threadIdx.x;
-  const int c = t & 7;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = (t >> 3) + 32 * j;
-    *reinterpret_cast<u32x4_t *>(sA + row * BK + ((c ^ (row & 7)) * 8)) = reg[j];
-  }
-}
-
-__device__ __forceinline__ u32x4_t read_a_frag(const uint16_t *sA, int row, int chunk) {
-  return *reinterpret_cast<const u32x4_t *>(sA + row * BK + ((chunk ^ (row & 7)) * 8));
-}
-
-template <bool kBf16>
+template <bool kOutBf16>
 __device__ __forceinline__ void store_out(void *Yv, int64_t M, int64_t N, int64_t m, int64_t n,
                                           float v) {
   if (m < M && n < N) {
-    if constexpr (kBf16)
+    if constexpr (kOutBf16)
       static_cast<uint16_t *>(Yv)[m * N + n] = bf16_bits(v);
     else
       static_cast<float *>(Yv)[m * N + n] = v;
   }
 }
 
-// ================================================================ forward
-template <bool kXbf16>
-__global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
-    const uint8_t *__restrict__ codes, const int8_t *__restrict__ q8,
-    const float *__restrict__ s2, int64_t K, int64_t N, const void *__restrict__ X, int64_t M,
-    const float *__restrict__ XA, const uint16_t *__restrict__ Bt, int r, int rp,
-    void *__restrict__ Y, ExpandConsts tb, int nt_count) {
-  __shared__ __align__(16) uint16_t sX[2][BM * BK];
-  __shared__ __align__(16) uint8_t sC[2][BK * kFwdCodePitch];
-  __shared__ __align__(16) float sS[2][2 * BK];
+// ------------------------------------------------------- shared main loop
+//
+// kFwd selects the weight-tile layout and expansion; everything else is
+// common.  Arguments (bytes are byte offsets):
+//   A16: activations bf16 [M x K]; codes; cs: scales fp32 [blocks][rows].
+//   Forward: weight rows = K (k), columns = N; cs row count = K.
+//   dX:      weight rows = N (i), columns = K; cs row count = N.
+template <bool kFwd, bool kExact>
+__device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, int64_t M, int64_t K,
+                                              int64_t N, const uint8_t *__restrict__ codes,
+                                              const float *__restrict__ cs, int64_t m0, int64_t n0,
+                                              const ExpandConsts &tb, char *smem,
+                                              f32x4_t (&acc)[16][2]) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets go to M0
+  const int i16 = lane & 15, h = lane >> 4;
+  const int KT = int(K / BK);
 
+  // ---- buffer descriptors (per workgroup) and per-lane constant offsets
+  const rsrc_t rX = make_rsrc(A16 + m0 * K, (M - m0) * K * 2);
+  uint32_t vx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = (8 * wave + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7);
+    vx[j] = uint32_t(row) * uint32_t(K) * 2u + uint32_t(c) * 16u;
+  }
+  rsrc_t rC, rS;
+  uint32_t vc, vs;
+  {
+    const int s = 64 * wave + lane;               // 16-B slot of the code tile
+    if constexpr (kFwd) {
+      // 64 k-rows x 4 pieces; slot s -> row 8*(s>>5) + (s&7), piece (s>>3)&3
+      const int row = 8 * (s >> 5) + (s & 7);
+      int q = (s >> 3) & 3;
+      // A ragged last tile (N % 128 == 64) has only pieces 0 and 1 inside the
+      // row; pieces 2 and 3 re-read them (their columns are never stored).
+      // The range check of a raw buffer covers the per-lane offset only, so
+      // every address must stay inside the row by construction.
+      if (n0 / 2 + 16 * q + 16 > N / 2) q -= 2;
+      rC = make_rsrc(codes + n0 / 2, K * (N / 2) - n0 / 2);
+      vc = uint32_t(row) * uint32_t(N / 2) + 16u * q;
+      // scales: block column nb0 + (wave & 1), 64 k per tile
+      const int64_t nb = n0 / 64 + (wave & 1);
+      rS = make_rsrc(cs, (N / 64) * K * 4);
+      vs = uint32_t(nb * K + lane) * 4u;
+    } else {
+      // 128 W-rows x 2 pieces; slot s -> row 8*(s>>4) + (s&7), piece (s>>3)&1
+      const int row = 8 * (s >> 4) + (s & 7), q = (s >> 3) & 1;
+      rC = make_rsrc(codes + n0 * (K / 2), (N - n0) * (K / 2));
+      vc = uint32_t(row) * uint32_t(K / 2) + 16u * q;
+      rS = make_rsrc(cs, (K / 64) * N * 4);
+      // the K offset is scalar (outside the range check): clamp the row
+      const int64_t srow = n0 + 64 * (wave & 1) + lane;
+      vs = uint32_t(srow < N ? srow : N - 1) * 4u;
+    }
+  }
+
+  const uint32_t lds0 = lds_addr(smem);
+  // Range checks of these raw buffers apply to the per-lane offset only; the
+  // scalar K offset never moves an address out of its row (or array).
+  auto issue = [&](int kt, int stage) {
+    const uint32_t base = lds0 + uint32_t(stage * kStageBytes);
+    const uint32_t sx = uint32_t(kt) * BK * 2u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds_load16(rX, base + (8 * wave + j) * 1024, vx[j], sx);
+    uint32_t sc, ss;
+    if constexpr (kFwd) {
+      sc = uint32_t(kt) * BK * uint32_t(N / 2);
+      ss = uint32_t(kt) * BK * 4u;
+    } else {
+      sc = uint32_t(kt) * (BK / 2);
+      ss = uint32_t(kt) * uint32_t(N) * 4u;
+    }
+    lds_load16(rC, base + kXBytes + wave * 1024, vc, sc);
+    lds_load4(rS, base + kXBytes + kCBytes + wave * 256, vs, ss);
+  };
+
+  issue(0, 0);
+  issue(KT > 1 ? 1 : 0, 1);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % kStages;
+    wait_vmcnt<kLoadsPerTile>();          // tile kt landed (tile kt+1 may be in flight)
+    __syncthreads();                      // visible to all; stage (kt+2)%3 is free
+    {
+      const int nk = kt + 2 < KT ? kt + 2 : KT - 1;
+      issue(nk, (kt + 2) % kStages);
+    }
+    const char *base = smem + st * kStageBytes;
+    const uint16_t *sX = reinterpret_cast<const uint16_t *>(base);
+    const char *sC = base + kXBytes;
+    const float *sS = reinterpret_cast<const float *>(base + kXBytes + kCBytes);
+
+    uint32_t nib[2][2];
+    if constexpr (kFwd) {
+      const int r = 16 * h + i16;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int slot = (r >> 3) * 32 + wave * 8 + (r & 7);
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+            (lds_i32x2 *)(lds_char *)(sC + slot * 16 + 8 * s));
+        nib[s][0] = uint32_t(v[0]);
+        nib[s][1] = uint32_t(v[1]);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int r = 32 * wave + 16 * s + i16;
+        const int slot = (r >> 3) * 16 + (h >> 1) * 8 + (r & 7);
+        const u32x2_t v = *reinterpret_cast<const u32x2_t *>(sC + slot * 16 + 8 * (h & 1));
+        nib[s][0] = v[0];
+        nib[s][1] = v[1];
+      }
+    }
+    float sc[16];
+    float scu[2];
+    if constexpr (kFwd) {
+      const f32x4_t *sp = reinterpret_cast<const f32x4_t *>(sS + (wave >> 1) * 64 + 16 * h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = sp[q];
+        sc[4 * q + 0] = v[0];
+        sc[4 * q + 1] = v[1];
+        sc[4 * q + 2] = v[2];
+        sc[4 * q + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) scu[s] = sS[32 * wave + 16 * s + i16];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4_t b0, b1;
+      if constexpr (kFwd) {
+        b0 = expand8<kExact>(nib[0][u], sc + 8 * u, tb);
+        b1 = expand8<kExact>(nib[1][u], sc + 8 * u, tb);
+      } else {
+        b0 = expand8u<kExact>(nib[0][u], scu[0], tb);
+        b1 = expand8u<kExact>(nib[1][u], scu[1], tb);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const char *>(sX) +
+                                               xoff(16 * i + i16, 2 * h + u));
+        acc[i][0] = mfma16x16x32(a, b0, acc[i][0]);
+        acc[i][1] = mfma16x16x32(a, b1, acc[i][1]);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+}
+
+// ================================================================ forward
+template <bool kOutBf16, bool kExact>
+__global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
+    const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t K, int64_t N,
+    const uint16_t *__restrict__ X16, int64_t M, const uint16_t *__restrict__ XA16,
+    const uint16_t *__restrict__ Bt, int rp, void *__restrict__ Y, ExpandConsts tb,
+    int nt_count) {
+  extern __shared__ __align__(16) char smem[];
   int mt, nt;
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, h = lane >> 4;
-  const int64_t N2 = N / 2, NB = N / 64;
-  const int KT = int(K / BK);
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[16][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc[i][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // staging registers
-  u32x4_t ra[8];
-  u32x4_t rc;
-  float rs = 0.f;
-  const int c_row = t >> 2, c_piece = t & 3;          // code tile: 64 rows x 4 x 16 B
-  const bool c_ok = n0 + 32 * (c_piece + 1) <= N;
-  const int s_kk = t & 63, s_j = (t >> 6) & 1;        // scales: threads 0..127
-  const bool s_ok = (t < 128) && (n0 / 64 + s_j < NB);
-
-  auto load_tile = [&](int kt) {
-    const int64_t k0 = int64_t(kt) * BK;
-    load_a_tile<kXbf16>(X, M, K, m0, k0, ra);
-    rc = c_ok ? *reinterpret_cast<const u32x4_t *>(codes + (k0 + c_row) * N2 + n0 / 2 +
-                                                   16 * c_piece)
-              : u32x4_t{0u, 0u, 0u, 0u};
-    if (s_ok) {
-      const int64_t b = (k0 + s_kk) * NB + n0 / 64 + s_j;
-      rs = float(q8[b]) * s2[b >> 8];
-    } else {
-      rs = 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    store_a_tile(sX[buf], ra);
-    uint8_t *cdst = sC[buf] + c_row * kFwdCodePitch + 16 * c_piece;
-    *reinterpret_cast<u32x2_t *>(cdst) = u32x2_t{rc[0], rc[1]};
-    *reinterpret_cast<u32x2_t *>(cdst + 8) = u32x2_t{rc[2], rc[3]};
-    if (t < 128) sS[buf][s_j * BK + s_kk] = rs;
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
-
-    // weight operands: 4 column groups of 16, 16 consecutive k each
-    uint32_t nib[4][2];
-    lds_char *cbase = (lds_char *)(sC[buf]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(
-          cbase + (16 * h + i16) * kFwdCodePitch + 32 * wn + 8 * s));
-      nib[s][0] = uint32_t(v[0]);
-      nib[s][1] = uint32_t(v[1]);
-    }
-    float sc[16];
-    {
-      const float4 *sp = reinterpret_cast<const float4 *>(&sS[buf][wn * BK + 16 * h]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float4 v = sp[q];
-        sc[4 * q + 0] = v.x;
-        sc[4 * q + 1] = v.y;
-        sc[4 * q + 2] = v.z;
-        sc[4 * q + 3] = v.w;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      u32x4_t bop[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bop[s] = expand8(nib[s][u], sc + 8 * u, tb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t a = read_a_frag(sX[buf], 128 * wm + 16 * i + i16, 2 * h + u);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[i][s] = mfma16x16x32(a, bop[s], acc[i][s]);
-      }
-    }
-    if (kt + 1 < KT) store_tile(buf ^ 1);
-    __syncthreads();
+  for (int i = 0; i < 16; ++i) {
+    acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  gemm_mainloop<true, kExact>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
 
-  // rank-r term: acc += bf16(XA) . bf16(B), B read transposed (Bt [N x rp])
+  // rank-r term: acc += XA16 . Bt^T (both bf16, zero-padded to rp columns)
   for (int r0 = 0; r0 < rp; r0 += 32) {
-    u32x4_t bop[4];
+    u32x4_t b[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t n = n0 + 64 * wn + 16 * s + i16;
-      bop[s] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Bt + n * rp + r0 + 8 * h)
-                       : u32x4_t{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 2; ++s) {
+      const int64_t n = n0 + 32 * wave + 16 * s + i16;
+      b[s] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Bt + n * rp + r0 + 8 * h)
+                     : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + 128 * wm + 16 * i + i16;
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = r0 + 8 * h + q;
-        v[q] = (m < M && j < r) ? XA[m * r + j] : 0.f;
-      }
-      const u32x4_t a = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc[i][s] = mfma16x16x32(a, bop[s], acc[i][s]);
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = m0 + 16 * i + i16;
+      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(XA16 + m * rp + r0 + 8 * h)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+      acc[i][0] = mfma16x16x32(a, b[0], acc[i][0]);
+      acc[i][1] = mfma16x16x32(a, b[1], acc[i][1]);
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        store_out<kXbf16>(Y, M, N, m0 + 128 * wm + 16 * i + 4 * h + q,
-                          n0 + 64 * wn + 16 * s + i16, acc[i][s][q]);
+        store_out<kOutBf16>(Y, M, N, m0 + 16 * i + 4 * h + q, n0 + 32 * wave + 16 * s + i16,
+                            acc[i][s][q]);
 }
 
 // ================================================================ dX
-template <bool kYbf16, bool kAbf16>
+template <bool kOutBf16, bool kExact>
 __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
-    const uint8_t *__restrict__ codes, const int8_t *__restrict__ q8,
-    const float *__restrict__ s2, int64_t IN, int64_t OUT, const void *__restrict__ dY,
-    int64_t M, const uint16_t *__restrict__ G16, int rp, const void *__restrict__ A, int r,
-    void *__restrict__ dX, ExpandConsts tb, int nt_count) {
-  __shared__ __align__(16) uint16_t sY[2][BM * BK];
-  __shared__ __align__(16) uint8_t sC[2][BN * kDxCodePitch];
-  __shared__ __align__(16) float sS[2][BN];
-
+    const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t IN, int64_t OUT,
+    const uint16_t *__restrict__ dY16, int64_t M, const uint16_t *__restrict__ G16,
+    const uint16_t *__restrict__ A16, int rp, void *__restrict__ dX, ExpandConsts tb,
+    int nt_count) {
+  extern __shared__ __align__(16) char smem[];
   int mt, nt;
   tile_of(nt_count, mt, nt);
-  const int64_t m0 = int64_t(mt) * BM, i0 = int64_t(nt) * BN;   // i: W row = dX column
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t m0 = int64_t(mt) * BM, i0 = int64_t(nt) * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, h = lane >> 4;
-  const int64_t OUT2 = OUT / 2, OB = OUT / 64;
-  const int KT = int(OUT / BK);
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[16][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc[i][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4_t ra[8];
-  u32x4_t rc;
-  float rs = 0.f;
-  const int c_row = t >> 1, c_piece = t & 1;          // code tile: 128 rows x 2 x 16 B
-  const bool c_ok = i0 + c_row < IN;
-  const bool s_ok = (t < 128) && (i0 + t < IN);
-
-  auto load_tile = [&](int kt) {
-    const int64_t k0 = int64_t(kt) * BK;
-    load_a_tile<kYbf16>(dY, M, OUT, m0, k0, ra);
-    rc = c_ok ? *reinterpret_cast<const u32x4_t *>(codes + (i0 + c_row) * OUT2 + k0 / 2 +
-                                                   16 * c_piece)
-              : u32x4_t{0u, 0u, 0u, 0u};
-    if (s_ok) {
-      const int64_t b = (i0 + t) * OB + k0 / 64;
-      rs = float(q8[b]) * s2[b >> 8];
-    } else {
-      rs = 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    store_a_tile(sY[buf], ra);
-    uint8_t *cdst = sC[buf] + c_row * kDxCodePitch + 16 * c_piece;
-    *reinterpret_cast<u32x2_t *>(cdst) = u32x2_t{rc[0], rc[1]};
-    *reinterpret_cast<u32x2_t *>(cdst + 8) = u32x2_t{rc[2], rc[3]};
-    if (t < 128) sS[buf][t] = rs;
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
-
-    uint32_t nib[4][2];
-    float sc[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int wr = 64 * wn + 16 * s + i16;
-      const u32x2_t v = *reinterpret_cast<const u32x2_t *>(sC[buf] + wr * kDxCodePitch + 8 * h);
-      nib[s][0] = v[0];
-      nib[s][1] = v[1];
-      sc[s] = sS[buf][wr];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      u32x4_t bop[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bop[s] = expand8u(nib[s][u], sc[s], tb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t a = read_a_frag(sY[buf], 128 * wm + 16 * i + i16, 2 * h + u);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[i][s] = mfma16x16x32(a, bop[s], acc[i][s]);
-      }
-    }
-    if (kt + 1 < KT) store_tile(buf ^ 1);
-    __syncthreads();
+  for (int i = 0; i < 16; ++i) {
+    acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  gemm_mainloop<false, kExact>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
 
-  // rank-r term: acc += G . A^T, G bf16 [M x rp] (zero padded), A [IN x r]
+  // rank-r term: acc += G16 . A16^T (G16 [M x rp], A16 [IN x rp], zero-padded)
   for (int r0 = 0; r0 < rp; r0 += 32) {
-    u32x4_t bop[4];
+    u32x4_t b[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t i = i0 + 64 * wn + 16 * s + i16;
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = r0 + 8 * h + q;
-        float x = 0.f;
-        if (i < IN && j < r) {
-          if constexpr (kAbf16)
-            x = __uint_as_float(uint32_t(static_cast<const uint16_t *>(A)[i * r + j]) << 16);
-          else
-            x = static_cast<const float *>(A)[i * r + j];
-        }
-        v[q] = x;
-      }
-      bop[s] = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    for (int s = 0; s < 2; ++s) {
+      const int64_t i = i0 + 32 * wave + 16 * s + i16;
+      b[s] = (i < IN) ? *reinterpret_cast<const u32x4_t *>(A16 + i * rp + r0 + 8 * h)
+                      : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + 128 * wm + 16 * i + i16;
+    for (int ii = 0; ii < 16; ++ii) {
+      const int64_t m = m0 + 16 * ii + i16;
       const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(G16 + m * rp + r0 + 8 * h)
                                 : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc[i][s] = mfma16x16x32(a, bop[s], acc[i][s]);
+      acc[ii][0] = mfma16x16x32(a, b[0], acc[ii][0]);
+      acc[ii][1] = mfma16x16x32(a, b[1], acc[ii][1]);
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int ii = 0; ii < 16; ++ii)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        store_out<kYbf16>(dX, M, IN, m0 + 128 * wm + 16 * i + 4 * h + q,
-                          i0 + 64 * wn + 16 * s + i16, acc[i][s][q]);
+        store_out<kOutBf16>(dX, M, IN, m0 + 16 * ii + 4 * h + q, i0 + 32 * wave + 16 * s + i16,
+                            acc[ii][s][q]);
+}
+
+// ----------------------------------------------------------- scale prep
+// cs[b][row] = q8[row * NB + b] * s2[(row * NB + b) >> 8]  (fp32 product)
+__global__ __launch_bounds__(256) void scales_kernel(const int8_t *__restrict__ q8,
+                                                     const float *__restrict__ s2, int64_t rows,
+                                                     int64_t NB, float *__restrict__ cs) {
+  const int64_t n = rows * NB;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t b = i / rows, row = i - b * rows;
+    const int64_t src = row * NB + b;
+    cs[i] = float(q8[src]) * s2[src >> 8];
+  }
+}
+
+bool set_lds(const void *fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) ==
+         hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_gemm(const uint8_t *codes, const int8_t *qscale, const float *gscale,
-                           int64_t K, int64_t N, const void *X, bool x_bf16, int64_t M,
-                           const float *XA, const uint16_t *Bt, int32_t r, void *Y,
-                           hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  const int mtc = int((M + BM - 1) / BM), ntc = int((N + BN - 1) / BN);
-  const int rp = r > 0 ? int((r + 31) / 32 * 32) : 0;
-  dim3 grid(unsigned(mtc * ntc));
-  const ExpandConsts tb = tables().expand;
-  if (x_bf16)
-    hipLaunchKernelGGL(fwd_gemm_kernel<true>, grid, dim3(kThreads), 0, s, codes, qscale, gscale,
-                       K, N, X, M, XA, Bt, int(r), rp, Y, tb, ntc);
-  else
-    hipLaunchKernelGGL(fwd_gemm_kernel<false>, grid, dim3(kThreads), 0, s, codes, qscale,
-                       gscale, K, N, X, M, XA, Bt, int(r), rp, Y, tb, ntc);
+hipError_t launch_scales(const int8_t *qscale, const float *gscale, int64_t rows, int64_t cols,
+                         float *cs, hipStream_t s) {
+  const int64_t nb = cols / 64, n = rows * nb;
+  if (n == 0) return hipSuccess;
+  int64_t g = (n + 255) / 256;
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(scales_kernel, dim3(unsigned(g)), dim3(256), 0, s, qscale, gscale, rows, nb,
+                     cs);
   return hipGetLastError();
 }
 
-hipError_t launch_dx_gemm(const uint8_t *codes, const int8_t *qscale, const float *gscale,
-                          int64_t in, int64_t out, const void *dY, bool dy_bf16, int64_t M,
-                          const uint16_t *G16, const void *A, bool a_bf16, int32_t r, void *dX,
+hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int64_t N,
+                           const uint16_t *X16, int64_t M, const uint16_t *XA16,
+                           const uint16_t *Bt, int32_t rp, void *Y, bool y_bf16, bool exact,
+                           hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int mtc = int((M + BM - 1) / BM), ntc = int((N + BN - 1) / BN);
+  dim3 grid(unsigned(mtc * ntc));
+  const ExpandConsts tb = tables().expand;
+#define QLORA_FWD(OB, EX)                                                                      \
+  do {                                                                                         \
+    static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB, EX>));        \
+    if (!ok) return hipErrorInvalidValue;                                                      \
+    hipLaunchKernelGGL((fwd_gemm_kernel<OB, EX>), grid, dim3(kThreads), kLdsBytes, s, codes,  \
+                       cs, K, N, X16, M, XA16, Bt, int(rp), Y, tb, ntc);                       \
+  } while (0)
+  if (y_bf16) {
+    if (exact) QLORA_FWD(true, true); else QLORA_FWD(true, false);
+  } else {
+    if (exact) QLORA_FWD(false, true); else QLORA_FWD(false, false);
+  }
+#undef QLORA_FWD
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int64_t out,
+                          const uint16_t *dY16, int64_t M, const uint16_t *G16,
+                          const uint16_t *A16, int32_t rp, void *dX, bool dx_bf16, bool exact,
                           hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int mtc = int((M + BM - 1) / BM), ntc = int((in + BN - 1) / BN);
-  const int rp = r > 0 ? int((r + 31) / 32 * 32) : 0;
   dim3 grid(unsigned(mtc * ntc));
   const ExpandConsts tb = tables().expand;
-#define QLORA_DX(YB, AB)                                                                       \
-  hipLaunchKernelGGL((dx_gemm_kernel<YB, AB>), grid, dim3(kThreads), 0, s, codes, qscale,     \
-                     gscale, in, out, dY, M, G16, rp, A, int(r), dX, tb, ntc)
-  if (dy_bf16 && a_bf16)
-    QLORA_DX(true, true);
-  else if (dy_bf16)
-    QLORA_DX(true, false);
-  else if (a_bf16)
-    QLORA_DX(false, true);
-  else
-    QLORA_DX(false, false);
+#define QLORA_DX(OB, EX)                                                                       \
+  do {                                                                                         \
+    static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB, EX>));         \
+    if (!ok) return hipErrorInvalidValue;                                                      \
+    hipLaunchKernelGGL((dx_gemm_kernel<OB, EX>), grid, dim3(kThreads), kLdsBytes, s, codes,   \
+                       cs, in, out, dY16, M, G16, A16, int(rp), dX, tb, ntc);                  \
+  } while (0)
+  if (dx_bf16) {
+    if (exact) QLORA_DX(true, true); else QLORA_DX(true, false);
+  } else {
+    if (exact) QLORA_DX(false, true); else QLORA_DX(false, false);
+  }
 #undef QLORA_DX
   return hipGetLastError();
 }

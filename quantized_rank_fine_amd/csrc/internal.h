@@ -72,20 +72,30 @@ hipError_t launch_reduce(const float *part, int64_t ks, int64_t rows, int64_t R,
                          int64_t ld_bf16, uint16_t *outT_bf16, int64_t ldT,
                          hipStream_t s);
 
-// y = X . deq(Wq) + bf16(XA) . Bt^T; Bt [N x rp] bf16 zero-padded, rp =
-// round_up(r, 32).
-hipError_t launch_fwd_gemm(const uint8_t *codes, const int8_t *qscale,
-                           const float *gscale, int64_t K, int64_t N,
-                           const void *X, bool x_bf16, int64_t M,
-                           const float *XA, const uint16_t *Bt, int32_t r,
-                           void *Y, hipStream_t s);
+// cs[b][row] = q8[row][b] * s2[group] (fp32) for a quantized [rows x cols]
+// weight: the block scales, one row per 64-wide block column.
+hipError_t launch_scales(const int8_t *qscale, const float *gscale, int64_t rows,
+                         int64_t cols, float *cs, hipStream_t s);
 
-// dX = dY . deq(Wq)^T + G16 . A^T; G16 [M x rp] bf16 zero-padded.
-hipError_t launch_dx_gemm(const uint8_t *codes, const int8_t *qscale,
-                          const float *gscale, int64_t in, int64_t out,
-                          const void *dY, bool dy_bf16, int64_t M,
-                          const uint16_t *G16, const void *A, bool a_bf16,
-                          int32_t r, void *dX, hipStream_t s);
+// dst[i][j] = src[i][j] as bf16 for j < cols, 0 for cols <= j < ldd.
+hipError_t launch_pad_to_bf16(const void *src, bool src_bf16, int64_t rows,
+                              int64_t cols, uint16_t *dst, int64_t ldd,
+                              hipStream_t s);
+
+// y = X16 . deq(Wq) + XA16 . Bt^T (K = in, N = out).  X16 [M x K] bf16;
+// XA16 [M x rp], Bt [N x rp] bf16 zero-padded (rp = round_up(r, 32), 0 for
+// no adapter); cs from launch_scales(rows = K, cols = N).
+hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K,
+                           int64_t N, const uint16_t *X16, int64_t M,
+                           const uint16_t *XA16, const uint16_t *Bt, int32_t rp,
+                           void *Y, bool y_bf16, bool exact, hipStream_t s);
+
+// dX = dY16 . deq(Wq)^T + G16 . A16^T.  dY16 [M x out] bf16; G16 [M x rp],
+// A16 [in x rp] bf16 zero-padded; cs from launch_scales(rows = in, cols = out).
+hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
+                          int64_t out, const uint16_t *dY16, int64_t M,
+                          const uint16_t *G16, const uint16_t *A16, int32_t rp,
+                          void *dX, bool dx_bf16, bool exact, hipStream_t s);
 
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }

@@ -72,6 +72,21 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const void *__restr
   }
 }
 
+__global__ __launch_bounds__(256) void pad_bf16_kernel(const void *__restrict__ src,
+                                                       bool src_bf16, int64_t rows, int64_t cols,
+                                                       uint16_t *__restrict__ dst, int64_t ldd) {
+  const int64_t n = rows * ldd;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / ldd, j = i - r * ldd;
+    uint16_t v = 0;
+    if (j < cols) {
+      v = src_bf16 ? static_cast<const uint16_t *>(src)[r * cols + j]
+                   : f32_to_bf16_bits(static_cast<const float *>(src)[r * cols + j]);
+    }
+    dst[i] = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void convert_bf16_kernel(const void *__restrict__ src,
                                                            bool src_bf16, int64_t n,
                                                            uint16_t *__restrict__ dst) {
@@ -326,6 +341,14 @@ hipError_t launch_convert_to_bf16(const void *src, bool src_bf16, int64_t n, uin
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(convert_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, s, src, src_bf16, n,
                      dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_to_bf16(const void *src, bool src_bf16, int64_t rows, int64_t cols,
+                              uint16_t *dst, int64_t ldd, hipStream_t s) {
+  if (rows == 0 || ldd == 0) return hipSuccess;
+  hipLaunchKernelGGL(pad_bf16_kernel, dim3(grid_for(rows * ldd)), dim3(256), 0, s, src, src_bf16,
+                     rows, cols, dst, ldd);
   return hipGetLastError();
 }
 

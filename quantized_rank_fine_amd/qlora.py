@@ -56,7 +56,7 @@ def lib():
     for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd):
         f.restype = ctypes.c_int
     for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
-        f.argtypes = [i64, i64, i64, i32]
+        f.argtypes = [i64, i64, i64, i32, ctypes.c_int]
         f.restype = sz
     L.qlora_status_string.argtypes = [ctypes.c_int]
     L.qlora_status_string.restype = ctypes.c_char_p
@@ -137,12 +137,12 @@ def qlora_quantize(W0, wq, stream=None):
     _check(lib().qlora_quantize(_ptr(W0), ctypes.byref(s), _stream(stream)), "qlora_quantize")
 
 
-def qlora_fwd_workspace_bytes(M, n_in, n_out, r):
-    return int(lib().qlora_fwd_workspace_bytes(M, n_in, n_out, r))
+def qlora_fwd_workspace_bytes(M, n_in, n_out, r, act=BF16):
+    return int(lib().qlora_fwd_workspace_bytes(M, n_in, n_out, r, int(act)))
 
 
-def qlora_bwd_workspace_bytes(M, n_in, n_out, r):
-    return int(lib().qlora_bwd_workspace_bytes(M, n_in, n_out, r))
+def qlora_bwd_workspace_bytes(M, n_in, n_out, r, act=BF16):
+    return int(lib().qlora_bwd_workspace_bytes(M, n_in, n_out, r, int(act)))
 
 
 def qlora_linear_fwd(wq, X, M, act, A, B, r, adt, Y, XA, ws, ws_bytes, stream=None):
@@ -177,8 +177,19 @@ def qlora_status_string(status):
     return lib().qlora_status_string(int(status)).decode()
 
 
-def qlora_timing_enable(on=True):
-    return lib().qlora_timing_enable(1 if on else 0)
+def qlora_timing_enable(kinds=None):
+    """Time the given kernel kinds (indices into KERNELS); None = all."""
+    if kinds is None:
+        mask = (1 << len(KERNELS)) - 1
+    else:
+        mask = 0
+        for k in kinds:
+            mask |= 1 << (KERNELS.index(k) if isinstance(k, str) else int(k))
+    return lib().qlora_timing_enable(mask)
+
+
+def qlora_timing_disable():
+    return lib().qlora_timing_enable(0)
 
 
 def qlora_timing_read(kind):

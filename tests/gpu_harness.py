@@ -105,7 +105,7 @@ class Layer:
         M, r = self.M, self.r
         Y = torch.empty(M, self.n_out, dtype=self.tdt, device=dev)
         XA = torch.empty(M, max(r, 1), dtype=torch.float32, device=dev) if r else None
-        wsb = q.qlora_fwd_workspace_bytes(M, self.n_in, self.n_out, r)
+        wsb = q.qlora_fwd_workspace_bytes(M, self.n_in, self.n_out, r, self.qact)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
         q.qlora_linear_fwd(self.wq, self.tX, M, self.qact, self.tA, self.tB, r, self.qadt, Y, XA,
                            ws, wsb)
@@ -118,7 +118,7 @@ class Layer:
         dX = torch.empty(M, self.n_in, dtype=self.tdt, device=dev) if want_dx else None
         dA = torch.empty(self.n_in, max(r, 1), dtype=torch.float32, device=dev) if r else None
         dB = torch.empty(max(r, 1), self.n_out, dtype=torch.float32, device=dev) if r else None
-        wsb = q.qlora_bwd_workspace_bytes(M, self.n_in, self.n_out, r)
+        wsb = q.qlora_bwd_workspace_bytes(M, self.n_in, self.n_out, r, self.qact)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
         q.qlora_linear_bwd(self.wq, self.tX, self.tdY, M, self.qact, self.tA, self.tB, r,
                            self.qadt, XA, dX, dA, dB, ws, wsb)

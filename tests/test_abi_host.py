@@ -69,14 +69,18 @@ def test_thresholds_reproduce_oracle_argmin(L):
 def test_workspace_sizes(L):
     for (M, i, o, r) in [(2048, 4096, 4096, 16), (1, 4096, 11008, 16), (8192, 22016, 8192, 64),
                          (64, 256, 256, 8)]:
-        f = q.qlora_fwd_workspace_bytes(M, i, o, r)
-        b = q.qlora_bwd_workspace_bytes(M, i, o, r)
-        assert f >= r * i * 2 + o * r * 2 + M * r * 4
-        assert b >= M * r * 4
-        assert f % 256 == 0 and b % 256 == 0
-    assert q.qlora_fwd_workspace_bytes(2048, 4096, 4096, 0) == 0
-    assert q.qlora_fwd_workspace_bytes(0, 4096, 4096, 16) == 0
-    assert q.qlora_bwd_workspace_bytes(64, 100, 256, 8) == 0     # invalid shape
+        for act in (q.BF16, q.F32):
+            f = q.qlora_fwd_workspace_bytes(M, i, o, r, act)
+            b = q.qlora_bwd_workspace_bytes(M, i, o, r, act)
+            assert f >= r * i * 2 + o * r * 2 + M * r * 4 + i * o // 16
+            assert b >= M * r * 4 + i * o // 16
+            assert f % 256 == 0 and b % 256 == 0
+            if act == q.F32:
+                assert f >= M * i * 2 and b >= M * o * 2
+    assert q.qlora_fwd_workspace_bytes(2048, 4096, 4096, 0, q.BF16) == 4096 * 64 * 4
+    assert q.qlora_fwd_workspace_bytes(0, 4096, 4096, 16, q.BF16) == 0
+    assert q.qlora_bwd_workspace_bytes(64, 100, 256, 8, q.BF16) == 0     # invalid shape
+    assert q.qlora_bwd_workspace_bytes(64, 256, 256, 8, 5) == 0          # invalid dtype
 
 
 def test_status_strings(L):
@@ -114,7 +118,7 @@ def test_quantize_validation(L):
 def test_fwd_validation(L):
     s = _nf4()
     f = L.qlora_linear_fwd
-    ws = q.qlora_fwd_workspace_bytes(64, 256, 256, 8)
+    ws = q.qlora_fwd_workspace_bytes(64, 256, 256, 8, q.BF16)
     # M = 0 is a no-op that succeeds without touching the device
     assert f(ctypes.byref(s), P, 0, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 0
     assert f(ctypes.byref(s), P, -1, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 2
@@ -135,7 +139,7 @@ def test_fwd_validation(L):
 def test_bwd_validation(L):
     s = _nf4()
     f = L.qlora_linear_bwd
-    ws = q.qlora_bwd_workspace_bytes(64, 256, 256, 8)
+    ws = q.qlora_bwd_workspace_bytes(64, 256, 256, 8, q.BF16)
     args = lambda **k: [ctypes.byref(k.get("s", s)), k.get("X", P), k.get("dY", P), k.get("M", 64),
                         k.get("act", q.BF16), k.get("A", P), k.get("B", P), k.get("r", 8),
                         k.get("adt", q.BF16), k.get("XA", P), k.get("dX", P), k.get("dA", P),
