@@ -10,23 +10,24 @@
 // main K loop.
 //
 // Workgroup: 256 threads = 4 wavefronts side by side along N; tile 256 (M) x
-// 128 (N) x 64 (K); each wavefront owns all 256 rows x 32 columns as 16 x 2
-// tiles of v_mfma_f32_16x16x32_bf16, so every weight of the tile is expanded
+// 128 (N) x 64 (K); each wavefront owns all 256 rows x 32 columns as 8 tiles
+// of v_mfma_f32_32x32x16_bf16, so every weight of the tile is expanded
 // exactly once per workgroup.  Tiles stream through a 3-stage LDS ring filled
 // by buffer_load ... lds (the K offset is a scalar; rows past M read as 0).
 // Activation tiles are row-major with 16-B chunks XOR-swizzled by row; the
 // weight tile is raw packed codes (1/4 of its bf16 size) and the per-block
 // scales c_b = q_b * s2_g come from a small fp32 array laid out [block][row].
-// K slots are permuted inside each 64-wide K tile: lane group h of the MFMA
-// owns k = 16h .. 16h+15 (8 per substep), identically for both operands.
+// K slots are permuted inside each 64-wide K tile: lane half h (lanes 32h..)
+// of the MFMA owns k = 32h .. 32h+31 (8 per substep), for both operands.
 //
 // Forward: the code tile is 64 k-rows x 128 n-cols, n-contiguous;
 // ds_read_b64_tr_b4 gives lane i of a 16-lane group column i of the 16 rows
-// the group points at (16 consecutive k of one column) in one read.  The
-// scale of a weight depends on its k row (and the wavefront's block column).
+// the group points at (16 consecutive k of one column) in one read; two such
+// reads give a lane its 32 k.  The scale of a weight depends on its k row
+// (and the wavefront's block column).
 // Backward dX: the code tile is 128 W-rows x 64 W-cols and the contraction
-// runs along a W row: a plain 8-byte read gives 16 consecutive k, all under
-// one scale (the K tile is one 64-wide block).
+// runs along a W row: one 16-byte read gives a lane its 32 consecutive k,
+// all under one scale (the K tile is one 64-wide block).
 //
 // Expansion: w = bf16(level * scale) with level = L[code] from a 16-entry
 // table held as v_perm byte planes (sign-symmetric: 8 magnitudes).  kExact
@@ -194,10 +195,10 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
                                               int64_t N, const uint8_t *__restrict__ codes,
                                               const float *__restrict__ cs, int64_t m0, int64_t n0,
                                               const ExpandConsts &tb, char *smem,
-                                              f32x4_t (&acc)[16][2]) {
+                                              f32x16_t (&acc)[8]) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets go to M0
-  const int i16 = lane & 15, h = lane >> 4;
+  const int l32 = lane & 31, h2 = lane >> 5;
   const int KT = int(K / BK);
 
   // ---- buffer descriptors (per workgroup) and per-lane constant offsets
@@ -272,64 +273,52 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       issue(nk, (kt + 2) % kStages);
     }
     const char *base = smem + st * kStageBytes;
-    const uint16_t *sX = reinterpret_cast<const uint16_t *>(base);
+    const char *sXb = base;
     const char *sC = base + kXBytes;
     const float *sS = reinterpret_cast<const float *>(base + kXBytes + kCBytes);
 
-    uint32_t nib[2][2];
+    // weight codes of this lane: 32 consecutive k (k = 32*h2 + 0..31) of one
+    // column (forward) or one W row (dX), as four 8-nibble words
+    uint32_t nib[4];
     if constexpr (kFwd) {
-      const int r = 16 * h + i16;
+      const int c16 = (lane >> 4) & 1, t16 = lane & 15;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int j = 0; j < 2; ++j) {
+        const int r = 32 * h2 + 16 * j + t16;
         const int slot = (r >> 3) * 32 + wave * 8 + (r & 7);
         const i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-            (lds_i32x2 *)(lds_char *)(sC + slot * 16 + 8 * s));
-        nib[s][0] = uint32_t(v[0]);
-        nib[s][1] = uint32_t(v[1]);
+            (lds_i32x2 *)(lds_char *)(sC + slot * 16 + 8 * c16));
+        nib[2 * j] = uint32_t(v[0]);
+        nib[2 * j + 1] = uint32_t(v[1]);
       }
     } else {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int r = 32 * wave + 16 * s + i16;
-        const int slot = (r >> 3) * 16 + (h >> 1) * 8 + (r & 7);
-        const u32x2_t v = *reinterpret_cast<const u32x2_t *>(sC + slot * 16 + 8 * (h & 1));
-        nib[s][0] = v[0];
-        nib[s][1] = v[1];
-      }
+      const int r = 32 * wave + l32;
+      const int slot = (r >> 3) * 16 + h2 * 8 + (r & 7);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(sC + slot * 16);
+      nib[0] = v[0];
+      nib[1] = v[1];
+      nib[2] = v[2];
+      nib[3] = v[3];
     }
-    float sc[16];
-    float scu[2];
-    if constexpr (kFwd) {
-      const f32x4_t *sp = reinterpret_cast<const f32x4_t *>(sS + (wave >> 1) * 64 + 16 * h);
+    float scu = 0.f;
+    if constexpr (!kFwd) scu = sS[32 * wave + l32];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t v = sp[q];
-        sc[4 * q + 0] = v[0];
-        sc[4 * q + 1] = v[1];
-        sc[4 * q + 2] = v[2];
-        sc[4 * q + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) scu[s] = sS[32 * wave + 16 * s + i16];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      u32x4_t b0, b1;
+    for (int u = 0; u < 4; ++u) {
+      u32x4_t b;
       if constexpr (kFwd) {
-        b0 = expand8<kExact>(nib[0][u], sc + 8 * u, tb);
-        b1 = expand8<kExact>(nib[1][u], sc + 8 * u, tb);
+        const f32x4_t *sp =
+            reinterpret_cast<const f32x4_t *>(sS + (wave >> 1) * 64 + 32 * h2 + 8 * u);
+        const f32x4_t s0 = sp[0], s1 = sp[1];
+        const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        b = expand8<kExact>(nib[u], sc, tb);
       } else {
-        b0 = expand8u<kExact>(nib[0][u], scu[0], tb);
-        b1 = expand8u<kExact>(nib[1][u], scu[1], tb);
+        b = expand8u<kExact>(nib[u], scu, tb);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const u32x4_t a =
-            *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const char *>(sX) +
-                                               xoff(16 * i + i16, 2 * h + u));
-        acc[i][0] = mfma16x16x32(a, b0, acc[i][0]);
-        acc[i][1] = mfma16x16x32(a, b1, acc[i][1]);
+            *reinterpret_cast<const u32x4_t *>(sXb + xoff(32 * i + l32, 4 * h2 + u));
+        acc[i] = mfma32x32x16(a, b, acc[i]);
       }
     }
   }
@@ -348,43 +337,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, h = lane >> 4;
+  const int l32 = lane & 31, h2 = lane >> 5;
 
-  f32x4_t acc[16][2];
+  f32x16_t acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   gemm_mainloop<true, kExact>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
 
   // rank-r term: acc += XA16 . Bt^T (both bf16, zero-padded to rp columns)
-  for (int r0 = 0; r0 < rp; r0 += 32) {
-    u32x4_t b[2];
+  const int64_t n = n0 + 32 * wave + l32;
+  for (int r0 = 0; r0 < rp; r0 += 16) {
+    const u32x4_t b = (n < N) ? *reinterpret_cast<const u32x4_t *>(Bt + n * rp + r0 + 8 * h2)
+                              : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t n = n0 + 32 * wave + 16 * s + i16;
-      b[s] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Bt + n * rp + r0 + 8 * h)
-                     : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t m = m0 + 16 * i + i16;
-      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(XA16 + m * rp + r0 + 8 * h)
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + 32 * i + l32;
+      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(XA16 + m * rp + r0 + 8 * h2)
                                 : u32x4_t{0u, 0u, 0u, 0u};
-      acc[i][0] = mfma16x16x32(a, b[0], acc[i][0]);
-      acc[i][1] = mfma16x16x32(a, b[1], acc[i][1]);
+      acc[i] = mfma32x32x16(a, b, acc[i]);
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store_out<kOutBf16>(Y, M, N, m0 + 16 * i + 4 * h + q, n0 + 32 * wave + 16 * s + i16,
-                            acc[i][s][q]);
+    for (int r = 0; r < 16; ++r)
+      store_out<kOutBf16>(Y, M, N, m0 + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3), n, acc[i][r]);
 }
 
 // ================================================================ dX
@@ -399,43 +379,35 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, i0 = int64_t(nt) * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, h = lane >> 4;
+  const int l32 = lane & 31, h2 = lane >> 5;
 
-  f32x4_t acc[16][2];
+  f32x16_t acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   gemm_mainloop<false, kExact>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
 
   // rank-r term: acc += G16 . A16^T (G16 [M x rp], A16 [IN x rp], zero-padded)
-  for (int r0 = 0; r0 < rp; r0 += 32) {
-    u32x4_t b[2];
+  const int64_t col = i0 + 32 * wave + l32;
+  for (int r0 = 0; r0 < rp; r0 += 16) {
+    const u32x4_t b = (col < IN) ? *reinterpret_cast<const u32x4_t *>(A16 + col * rp + r0 + 8 * h2)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t i = i0 + 32 * wave + 16 * s + i16;
-      b[s] = (i < IN) ? *reinterpret_cast<const u32x4_t *>(A16 + i * rp + r0 + 8 * h)
-                      : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-      const int64_t m = m0 + 16 * ii + i16;
-      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(G16 + m * rp + r0 + 8 * h)
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + 32 * i + l32;
+      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(G16 + m * rp + r0 + 8 * h2)
                                 : u32x4_t{0u, 0u, 0u, 0u};
-      acc[ii][0] = mfma16x16x32(a, b[0], acc[ii][0]);
-      acc[ii][1] = mfma16x16x32(a, b[1], acc[ii][1]);
+      acc[i] = mfma32x32x16(a, b, acc[i]);
     }
   }
 
 #pragma unroll
-  for (int ii = 0; ii < 16; ++ii)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store_out<kOutBf16>(dX, M, IN, m0 + 16 * ii + 4 * h + q, i0 + 32 * wave + 16 * s + i16,
-                            acc[ii][s][q]);
+    for (int r = 0; r < 16; ++r)
+      store_out<kOutBf16>(dX, M, IN, m0 + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3), col,
+                          acc[i][r]);
 }
 
 // ----------------------------------------------------------- scale prep
