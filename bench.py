@@ -95,7 +95,7 @@ def cpu_baseline(w0, X, dY, A, B, min_seconds):
     """The oracle, as it stands, on the same workload: full quantize of W0
     (fp32 numpy, one thread) and full forward+backward of all tokens
     (dequantize + float64 BLAS matmuls), repeated until `min_seconds` of CPU
-    work have been timed (at most 5 repetitions)."""
+    work have been timed (at most 50 repetitions)."""
     import oracle
     from quantized_rank_fine_amd import workloads
     try:
@@ -107,7 +107,7 @@ def cpu_baseline(w0, X, dY, A, B, min_seconds):
     M, r = X.shape[0], A.shape[1]
     tq = tf = 0.0
     reps = 0
-    while (tq + tf) < min_seconds and reps < 5:
+    while (tq + tf) < min_seconds and reps < 50:
         t0 = time.perf_counter()
         qd = oracle.quantize(w0)
         t1 = time.perf_counter()
