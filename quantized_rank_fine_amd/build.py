@@ -31,10 +31,15 @@ DEVICE = [
     f"--offload-arch={ARCH}",
     # keep packed fp32 ALU ops out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in the VGPR file: avoids AGPR<->VGPR copies of the
-    # loop-carried accumulators
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# Per-source device flags.  The skinny kernels keep their few MFMA
+# accumulators in the VGPR file (no AGPR<->VGPR copies of loop-carried
+# accumulators); the fused GEMMs hold 256 accumulator registers per lane and
+# need the AGPR file for them.
+DEVICE_EXTRA = {
+    "skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc():
@@ -49,7 +54,7 @@ def _compile(src):
     path = os.path.join(CSRC, src)
     cmd = [hipcc()] + COMMON
     if src.endswith(".hip"):
-        cmd += ["-x", "hip"] + DEVICE
+        cmd += ["-x", "hip"] + DEVICE + DEVICE_EXTRA.get(src, [])
     else:
         cmd += ["-D__HIP_PLATFORM_AMD__"]
     cmd += ["-c", path, "-o", obj]

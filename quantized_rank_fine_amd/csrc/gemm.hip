@@ -185,8 +185,20 @@ __device__ __forceinline__ void store_out(void *Yv, int64_t M, int64_t N, int64_
 
 // ------------------------------------------------------- shared main loop
 //
+// Wavefront roles: column half ch = wave & 1 owns 64 columns of the tile (two
+// 32-wide MFMA column blocks b), and k half kh = wave >> 1 owns two of the
+// four k16 substeps of every K tile (u = 2 kh + j, j = 0, 1).  Each wavefront
+// therefore accumulates a 256 x 64 partial over half of K (acc[b][i]); the two
+// k halves are summed once, after the loop.  Per K tile a wavefront reads 16
+// activation fragments from LDS and expands 4 weight fragments for 32 MFMAs.
+//
+// The loop is software-pipelined by one substep: while the MFMAs of substep j
+// run, the operands of the next substep are read and expanded.  The workgroup
+// barrier sits between the two substeps of a tile, so the operands of the
+// next tile are prepared while the second substep's MFMAs run.
+//
 // kFwd selects the weight-tile layout and expansion; everything else is
-// common.  Arguments (bytes are byte offsets):
+// common.  Arguments:
 //   A16: activations bf16 [M x K]; codes; cs: scales fp32 [blocks][rows].
 //   Forward: weight rows = K (k), columns = N; cs row count = K.
 //   dX:      weight rows = N (i), columns = K; cs row count = N.
@@ -195,9 +207,10 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
                                               int64_t N, const uint8_t *__restrict__ codes,
                                               const float *__restrict__ cs, int64_t m0, int64_t n0,
                                               const ExpandConsts &tb, char *smem,
-                                              f32x16_t (&acc)[8]) {
+                                              f32x16_t (&acc)[2][8]) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets go to M0
+  const int ch = wave & 1, kh = wave >> 1;
   const int l32 = lane & 31, h2 = lane >> 5;
   const int KT = int(K / BK);
 
@@ -261,68 +274,210 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
     lds_load4(rS, base + kXBytes + kCBytes + wave * 256, vs, ss);
   };
 
-  issue(0, 0);
-  issue(KT > 1 ? 1 : 0, 1);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt % kStages;
-    wait_vmcnt<kLoadsPerTile>();          // tile kt landed (tile kt+1 may be in flight)
-    __syncthreads();                      // visible to all; stage (kt+2)%3 is free
-    {
-      const int nk = kt + 2 < KT ? kt + 2 : KT - 1;
-      issue(nk, (kt + 2) % kStages);
-    }
-    const char *base = smem + st * kStageBytes;
-    const char *sXb = base;
-    const char *sC = base + kXBytes;
-    const float *sS = reinterpret_cast<const float *>(base + kXBytes + kCBytes);
-
-    // weight codes of this lane: 32 consecutive k (k = 32*h2 + 0..31) of one
-    // column (forward) or one W row (dX), as four 8-nibble words
-    uint32_t nib[4];
-    if constexpr (kFwd) {
-      const int c16 = (lane >> 4) & 1, t16 = lane & 15;
+  // ---- per-lane LDS read offsets inside a stage
+  // activation fragment (i, j): row 32 i + l32, 16-B chunk 4 h2 + 2 kh + j
+  uint32_t xo[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = 32 * h2 + 16 * j + t16;
-        const int slot = (r >> 3) * 32 + wave * 8 + (r & 7);
-        const i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-            (lds_i32x2 *)(lds_char *)(sC + slot * 16 + 8 * c16));
-        nib[2 * j] = uint32_t(v[0]);
-        nib[2 * j + 1] = uint32_t(v[1]);
+  for (int j = 0; j < 2; ++j) xo[j] = xoff(l32, 4 * h2 + 2 * kh + j);   // + 32 i rows = 4096 i B
+  uint32_t co[2];                                  // code read offset per column block b
+  if constexpr (kFwd) {
+    const int c16 = (lane >> 4) & 1, t16 = lane & 15;
+    const int r = 32 * h2 + 16 * kh + t16;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      co[b] = uint32_t(((r >> 3) * 32 + (2 * ch + b) * 8 + (r & 7)) * 16 + 8 * c16);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int row = 64 * ch + 32 * b + l32;
+      co[b] = uint32_t(((row >> 3) * 16 + h2 * 8 + (row & 7)) * 16 + 8 * kh);
+    }
+  }
+  // scale read offset (bytes into the scale area of a stage)
+  const uint32_t so = kFwd ? uint32_t((ch * 64 + 32 * h2 + 16 * kh) * 4) : uint32_t((ch * 64 + l32) * 4);
+
+  // Per tile and lane: nib[b][j] = 8 codes (k slots 32 h2 + 8 (2 kh + j) +
+  // 0..7) of column block b; sc = the scales they need (forward: one per k
+  // slot, 16 for both substeps; dX: one per column block).
+  constexpr int kNS = kFwd ? 16 : 2;
+  auto read_tile = [&](const char *st, uint32_t (&nib)[2][2], float (&sc)[kNS]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      i32x2_t v;
+      if constexpr (kFwd)
+        v = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(lds_char *)(st + kXBytes + co[b]));
+      else
+        v = *reinterpret_cast<const i32x2_t *>(st + kXBytes + co[b]);
+      nib[b][0] = uint32_t(v[0]);
+      nib[b][1] = uint32_t(v[1]);
+    }
+    const char *sp = st + kXBytes + kCBytes + so;
+    if constexpr (kFwd) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sp + 16 * q);
+        sc[4 * q] = v[0]; sc[4 * q + 1] = v[1]; sc[4 * q + 2] = v[2]; sc[4 * q + 3] = v[3];
       }
     } else {
-      const int r = 32 * wave + l32;
-      const int slot = (r >> 3) * 16 + h2 * 8 + (r & 7);
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(sC + slot * 16);
-      nib[0] = v[0];
-      nib[1] = v[1];
-      nib[2] = v[2];
-      nib[3] = v[3];
+      sc[0] = *reinterpret_cast<const float *>(sp);
+      sc[1] = *reinterpret_cast<const float *>(sp + 128);
     }
-    float scu = 0.f;
-    if constexpr (!kFwd) scu = sS[32 * wave + l32];
+  };
+  auto read_a = [&](const char *st, int j, u32x4_t (&a)[8]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      u32x4_t b;
-      if constexpr (kFwd) {
-        const f32x4_t *sp =
-            reinterpret_cast<const f32x4_t *>(sS + (wave >> 1) * 64 + 32 * h2 + 8 * u);
-        const f32x4_t s0 = sp[0], s1 = sp[1];
-        const float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-        b = expand8<kExact>(nib[u], sc, tb);
-      } else {
-        b = expand8u<kExact>(nib[u], scu, tb);
-      }
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const u32x4_t *>(st + xo[j] + 4096 * i);
+  };
+  auto make_b = [&](const uint32_t (&nib)[2][2], const float (&sc)[kNS], int j, u32x4_t (&bb)[2]) {
+    if constexpr (kFwd) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t *>(sXb + xoff(32 * i + l32, 4 * h2 + u));
-        acc[i] = mfma32x32x16(a, b, acc[i]);
-      }
+      for (int b = 0; b < 2; ++b) bb[b] = expand8<kExact>(nib[b][j], sc + 8 * j, tb);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bb[b] = expand8u<kExact>(nib[b][j], sc[b], tb);
+    }
+  };
+  auto mfmas = [&](const u32x4_t (&a)[8], const u32x4_t (&bb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(a[i], bb[b], acc[b][i]);
+  };
+
+  // ---- prologue: tiles 0..2 in flight (clamped to the last tile), operands
+  // of tile 0 substep 0 ready
+  issue(0, 0);
+  issue(KT > 1 ? 1 : KT - 1, 1);
+  issue(KT > 2 ? 2 : KT - 1, 2);
+  wait_vmcnt<2 * kLoadsPerTile>();
+  __syncthreads();
+  uint32_t nib[2][2];
+  float sc[kNS];
+  u32x4_t a0[8], a1[8], b0[2], b1[2];
+  read_tile(smem, nib, sc);
+  read_a(smem, 0, a0);
+  make_b(nib, sc, 0, b0);
+
+  // Every iteration issues one tile group (past the end: a harmless re-load
+  // of the last tile into the stage just freed), so one constant vmcnt wait
+  // always means "tile kt+1 has landed".
+  for (int kt = 0; kt < KT; ++kt) {
+    const char *st = smem + (kt % kStages) * kStageBytes;
+    const char *sn = smem + ((kt + 1) % kStages) * kStageBytes;
+    // substep 0 of tile kt; prepare substep 1
+    read_a(st, 1, a1);
+    make_b(nib, sc, 1, b1);
+    mfmas(a0, b0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+      if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);           // VALU
+    }
+    // tile kt+1 landed and visible; the stage of tile kt is free
+    wait_vmcnt<kLoadsPerTile>();
+    __syncthreads();
+    issue(kt + 3 < KT ? kt + 3 : KT - 1, kt % kStages);
+    // substep 1 of tile kt; prepare substep 0 of tile kt+1 (past the end:
+    // reads of a stage that is never used)
+    read_tile(sn, nib, sc);
+    read_a(sn, 0, a0);
+    make_b(nib, sc, 0, b0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kFwd ? 6 : 4, 0);    // codes + scales
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+      if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+      if (q >= 3) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0); // VALU
     }
   }
   wait_vmcnt<0>();
+}
+
+// Epilogue.  The two k halves of a column half are summed through LDS: the
+// wavefront with k half kh stores row blocks i = 4 kh .. 4 kh + 3 and gives
+// the other four to its partner.  The rank-r term (P16 . Q16^T, bf16,
+// zero-padded to rp columns) is added on the given blocks, so it enters every
+// output once.  Row-block indices are compile-time constants under uniform
+// guards, so the accumulators never leave their registers.
+template <bool kOutBf16>
+__device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
+                                         const uint16_t *__restrict__ P16,
+                                         const uint16_t *__restrict__ Q16, int rp, int64_t M,
+                                         int64_t N, int64_t m0, int64_t n0, void *__restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ch = wave & 1, kh = wave >> 1;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int64_t nw = n0 + 64 * ch;
+
+  for (int r0 = 0; r0 < rp; r0 += 16) {
+    u32x4_t q[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = nw + 32 * b + l32;
+      q[b] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Q16 + n * rp + r0 + 8 * h2)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i >> 2) == kh) continue;
+      const int64_t m = m0 + 32 * i + l32;
+      const u32x4_t p = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * rp + r0 + 8 * h2)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(p, q[b], acc[b][i]);
+    }
+  }
+
+  const bool full = (m0 + 32 * (4 * kh + 4) <= M) && (nw + 64 <= N);
+  char *wr = smem + (ch * 2 + kh) * 16384 + lane * 16;
+  const char *rd = smem + (ch * 2 + (kh ^ 1)) * 16384 + lane * 16;
+  __syncthreads();
+#pragma unroll
+  for (int rnd = 0; rnd < 2; ++rnd) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i >> 2) == kh || ((i >> 1) & 1) != rnd) continue;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<f32x4_t *>(wr + ((i & 1) * 2 + b) * 4096 + c * 1024) =
+              f32x4_t{acc[b][i][4 * c], acc[b][i][4 * c + 1], acc[b][i][4 * c + 2], acc[b][i][4 * c + 3]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i >> 2) != kh || ((i >> 1) & 1) != rnd) continue;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float v[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4_t p = *reinterpret_cast<const f32x4_t *>(rd + ((i & 1) * 2 + b) * 4096 + c * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * c + e] = acc[b][i][4 * c + e] + p[e];
+        }
+        const int64_t mr = m0 + 32 * i + 4 * h2, n = nw + 32 * b + l32;
+        if (full) {
+          const int64_t e0 = mr * N + n;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t e = e0 + int64_t(8 * (r >> 2) + (r & 3)) * N;
+            if constexpr (kOutBf16)
+              static_cast<uint16_t *>(Y)[e] = bf16_bits(v[r]);
+            else
+              static_cast<float *>(Y)[e] = v[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) store_out<kOutBf16>(Y, M, N, mr + 8 * (r >> 2) + (r & 3), n, v[r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // ================================================================ forward
@@ -336,35 +491,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
   int mt, nt;
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h2 = lane >> 5;
-
-  f32x16_t acc[8];
+  f32x16_t acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<true, kExact>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
-
-  // rank-r term: acc += XA16 . Bt^T (both bf16, zero-padded to rp columns)
-  const int64_t n = n0 + 32 * wave + l32;
-  for (int r0 = 0; r0 < rp; r0 += 16) {
-    const u32x4_t b = (n < N) ? *reinterpret_cast<const u32x4_t *>(Bt + n * rp + r0 + 8 * h2)
-                              : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + 32 * i + l32;
-      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(XA16 + m * rp + r0 + 8 * h2)
-                                : u32x4_t{0u, 0u, 0u, 0u};
-      acc[i] = mfma32x32x16(a, b, acc[i]);
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      store_out<kOutBf16>(Y, M, N, m0 + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3), n, acc[i][r]);
+  // rank-r term: y += XA16 . Bt^T (both bf16, zero-padded to rp columns)
+  epilogue<kOutBf16>(acc, smem, XA16, Bt, rp, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
@@ -378,36 +514,16 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
   int mt, nt;
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, i0 = int64_t(nt) * BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h2 = lane >> 5;
-
-  f32x16_t acc[8];
+  f32x16_t acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<false, kExact>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
-
-  // rank-r term: acc += G16 . A16^T (G16 [M x rp], A16 [IN x rp], zero-padded)
-  const int64_t col = i0 + 32 * wave + l32;
-  for (int r0 = 0; r0 < rp; r0 += 16) {
-    const u32x4_t b = (col < IN) ? *reinterpret_cast<const u32x4_t *>(A16 + col * rp + r0 + 8 * h2)
-                                 : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + 32 * i + l32;
-      const u32x4_t a = (m < M) ? *reinterpret_cast<const u32x4_t *>(G16 + m * rp + r0 + 8 * h2)
-                                : u32x4_t{0u, 0u, 0u, 0u};
-      acc[i] = mfma32x32x16(a, b, acc[i]);
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      store_out<kOutBf16>(dX, M, IN, m0 + 32 * i + 8 * (r >> 2) + 4 * h2 + (r & 3), col,
-                          acc[i][r]);
+  // rank-r term: dX += G16 . A16^T (G16 [M x rp], A16 [IN x rp], zero-padded)
+  epilogue<kOutBf16>(acc, smem, G16, A16, rp, M, IN, m0, i0, dX);
 }
 
 // ----------------------------------------------------------- scale prep
