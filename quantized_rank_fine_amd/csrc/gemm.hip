@@ -9,25 +9,30 @@
 // small extra matmul" -- here it runs on the same accumulators after the
 // main K loop.
 //
-// Workgroup: 256 threads = 4 wavefronts side by side along N; tile 256 (M) x
-// 128 (N) x 64 (K); each wavefront owns all 256 rows x 32 columns as 8 tiles
-// of v_mfma_f32_32x32x16_bf16, so every weight of the tile is expanded
-// exactly once per workgroup.  Tiles stream through a 3-stage LDS ring filled
-// by buffer_load ... lds (the K offset is a scalar; rows past M read as 0).
-// Activation tiles are row-major with 16-B chunks XOR-swizzled by row; the
-// weight tile is raw packed codes (1/4 of its bf16 size) and the per-block
-// scales c_b = q_b * s2_g come from a small fp32 array laid out [block][row].
+// Workgroup: 256 threads = 4 wavefronts; tile 256 (M) x 128 (N) x 64 (K).
+// Wavefront w owns columns 64 (w & 1) .. +63 and half of every K tile
+// (k half w >> 1), as 8 x 2 tiles of v_mfma_f32_32x32x16_bf16; every weight of
+// the tile is expanded exactly once per workgroup and every activation
+// fragment read from LDS feeds two MFMAs.  The two k halves are summed in the
+// epilogue.  Tiles stream through a 4-stage LDS ring filled by
+// buffer_load ... lds (the K offset is a scalar; rows past M read as 0).
+// Activation tiles are row-major (128 B per row) with the 16-B chunks of a row
+// XOR-swizzled by (row >> 1) & 7: the 16 rows one MFMA fragment read touches
+// per 16-lane group then fall on 16 distinct 16-B bank groups of the 256-B
+// LDS bank window.  The weight tile is raw packed codes (1/4 of its bf16
+// size) and the per-block scales c_b = q_b * s2_g come from a small fp32
+// array laid out [block][row].
 // K slots are permuted inside each 64-wide K tile: lane half h (lanes 32h..)
 // of the MFMA owns k = 32h .. 32h+31 (8 per substep), for both operands.
 //
 // Forward: the code tile is 64 k-rows x 128 n-cols, n-contiguous;
 // ds_read_b64_tr_b4 gives lane i of a 16-lane group column i of the 16 rows
-// the group points at (16 consecutive k of one column) in one read; two such
-// reads give a lane its 32 k.  The scale of a weight depends on its k row
+// the group points at (16 consecutive k of one column) in one read: the 16 k
+// of the wavefront's k half.  The scale of a weight depends on its k row
 // (and the wavefront's block column).
 // Backward dX: the code tile is 128 W-rows x 64 W-cols and the contraction
-// runs along a W row: one 16-byte read gives a lane its 32 consecutive k,
-// all under one scale (the K tile is one 64-wide block).
+// runs along a W row: one 8-byte read gives a lane the 16 consecutive k of
+// its k half, all under one scale (the K tile is one 64-wide block).
 //
 // Expansion: w = bf16(level * scale) with level = L[code] from a 16-entry
 // table held as v_perm byte planes (sign-symmetric: 8 magnitudes).  kExact
@@ -45,12 +50,12 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kXBytes = BM * BK * 2;     // 32 KiB activation tile
 constexpr int kCBytes = 4096;            // code tile
 constexpr int kSBytes = 1024;            // scales (512 B used)
 constexpr int kStageBytes = kXBytes + kCBytes + kSBytes;
-constexpr int kLdsBytes = kStages * kStageBytes;   // 120 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;   // 148 KiB
 constexpr uint32_t kBufFlags = 0x00020000u;
 constexpr int kLoadsPerTile = 10;        // per wavefront: 8 X + 1 code + 1 scale
 
@@ -92,13 +97,13 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds, uint32_t voff
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // ------------------------------------------------------------- expansion
@@ -170,7 +175,7 @@ __device__ __forceinline__ void tile_of(int nt_count, int &mt, int &nt) {
 }
 
 // LDS address (bytes) of the 16-B chunk `c` of activation row `row`.
-__device__ __forceinline__ uint32_t xoff(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+__device__ __forceinline__ uint32_t xoff(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 template <bool kOutBf16>
 __device__ __forceinline__ void store_out(void *Yv, int64_t M, int64_t N, int64_t m, int64_t n,
@@ -220,7 +225,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int row = (8 * wave + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (row & 7);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
     vx[j] = uint32_t(row) * uint32_t(K) * 2u + uint32_t(c) * 16u;
   }
   rsrc_t rC, rS;
@@ -343,12 +348,11 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(a[i], bb[b], acc[b][i]);
   };
 
-  // ---- prologue: tiles 0..2 in flight (clamped to the last tile), operands
-  // of tile 0 substep 0 ready
-  issue(0, 0);
-  issue(KT > 1 ? 1 : KT - 1, 1);
-  issue(KT > 2 ? 2 : KT - 1, 2);
-  wait_vmcnt<2 * kLoadsPerTile>();
+  // ---- prologue: tiles 0..kStages-1 in flight (clamped to the last tile),
+  // operands of tile 0 substep 0 ready
+#pragma unroll
+  for (int p = 0; p < kStages; ++p) issue(p < KT ? p : KT - 1, p);
+  wait_vmcnt<(kStages - 1) * kLoadsPerTile>();
   __syncthreads();
   uint32_t nib[2][2];
   float sc[kNS];
@@ -374,9 +378,9 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);           // VALU
     }
     // tile kt+1 landed and visible; the stage of tile kt is free
-    wait_vmcnt<kLoadsPerTile>();
+    wait_vmcnt<(kStages - 2) * kLoadsPerTile>();
     __syncthreads();
-    issue(kt + 3 < KT ? kt + 3 : KT - 1, kt % kStages);
+    issue(kt + kStages < KT ? kt + kStages : KT - 1, kt % kStages);
     // substep 1 of tile kt; prepare substep 0 of tile kt+1 (past the end:
     // reads of a stage that is never used)
     read_tile(sn, nib, sc);
@@ -394,12 +398,15 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   wait_vmcnt<0>();
 }
 
-// Epilogue.  The two k halves of a column half are summed through LDS: the
-// wavefront with k half kh stores row blocks i = 4 kh .. 4 kh + 3 and gives
-// the other four to its partner.  The rank-r term (P16 . Q16^T, bf16,
-// zero-padded to rp columns) is added on the given blocks, so it enters every
-// output once.  Row-block indices are compile-time constants under uniform
-// guards, so the accumulators never leave their registers.
+// Epilogue.  The rank-r term (P16 . Q16^T, bf16, zero-padded to rp columns)
+// is added by the k-half-0 wavefronts only, so it enters every output once.
+// The two k halves of a column half are then summed through LDS in four
+// rounds of two row blocks: every wavefront writes its partials of row blocks
+// 2 rnd, 2 rnd + 1 (64 KiB in all), and reads back both halves of column
+// block b = kh, sums them and stores.  No register index depends on kh, so
+// the accumulators stay in their registers and are read straight into the
+// LDS writes.  LDS layout per fragment: 4 chunks of 1 KiB, chunk c = registers
+// 4c..4c+3 of every lane (16 B per lane, contiguous across lanes).
 template <bool kOutBf16>
 __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
                                          const uint16_t *__restrict__ P16,
@@ -411,72 +418,72 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
   const int l32 = lane & 31, h2 = lane >> 5;
   const int64_t nw = n0 + 64 * ch;
 
-  for (int r0 = 0; r0 < rp; r0 += 16) {
-    u32x4_t q[2];
+  if (kh == 0) {
+    for (int r0 = 0; r0 < rp; r0 += 16) {
+      u32x4_t q[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t n = nw + 32 * b + l32;
-      q[b] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Q16 + n * rp + r0 + 8 * h2)
-                     : u32x4_t{0u, 0u, 0u, 0u};
-    }
+      for (int b = 0; b < 2; ++b) {
+        const int64_t n = nw + 32 * b + l32;
+        q[b] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Q16 + n * rp + r0 + 8 * h2)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if ((i >> 2) == kh) continue;
-      const int64_t m = m0 + 32 * i + l32;
-      const u32x4_t p = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * rp + r0 + 8 * h2)
-                                : u32x4_t{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + 32 * i + l32;
+        const u32x4_t p = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * rp + r0 + 8 * h2)
+                                  : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(p, q[b], acc[b][i]);
+        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(p, q[b], acc[b][i]);
+      }
     }
   }
 
-  const bool full = (m0 + 32 * (4 * kh + 4) <= M) && (nw + 64 <= N);
+  const int64_t n = nw + 32 * kh + l32;               // this lane's output column
+  const bool ncol = (nw + 64 <= N);
   char *wr = smem + (ch * 2 + kh) * 16384 + lane * 16;
-  const char *rd = smem + (ch * 2 + (kh ^ 1)) * 16384 + lane * 16;
-  __syncthreads();
+  const char *rd0 = smem + (ch * 2) * 16384 + kh * 4096 + lane * 16;   // k half 0, block b = kh
+  const char *rd1 = rd0 + 16384;                                         // k half 1
 #pragma unroll
-  for (int rnd = 0; rnd < 2; ++rnd) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if ((i >> 2) == kh || ((i >> 1) & 1) != rnd) continue;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<f32x4_t *>(wr + ((i & 1) * 2 + b) * 4096 + c * 1024) =
-              f32x4_t{acc[b][i][4 * c], acc[b][i][4 * c + 1], acc[b][i][4 * c + 2], acc[b][i][4 * c + 3]};
-    }
+  for (int rnd = 0; rnd < 4; ++rnd) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if ((i >> 2) != kh || ((i >> 1) & 1) != rnd) continue;
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        float v[16];
+        const f32x16_t v = acc[b][2 * rnd + ii];
+        char *w = wr + ii * 8192 + b * 4096;
+        *reinterpret_cast<f32x4_t *>(w) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        *reinterpret_cast<f32x4_t *>(w + 1024) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+        *reinterpret_cast<f32x4_t *>(w + 2048) = __builtin_shufflevector(v, v, 8, 9, 10, 11);
+        *reinterpret_cast<f32x4_t *>(w + 3072) = __builtin_shufflevector(v, v, 12, 13, 14, 15);
+      }
+    __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4_t p = *reinterpret_cast<const f32x4_t *>(rd + ((i & 1) * 2 + b) * 4096 + c * 1024);
+    for (int ii = 0; ii < 2; ++ii) {
+      float v[16];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * c + e] = acc[b][i][4 * c + e] + p[e];
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(rd0 + ii * 8192 + c * 1024);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(rd1 + ii * 8192 + c * 1024);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * c + e] = x0[e] + x1[e];
+      }
+      const int64_t mr = m0 + 32 * (2 * rnd + ii) + 4 * h2;
+      if (ncol && mr + 28 < M) {
+        const int64_t e0 = mr * N + n;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t e = e0 + int64_t(8 * (r >> 2) + (r & 3)) * N;
+          if constexpr (kOutBf16)
+            static_cast<uint16_t *>(Y)[e] = bf16_bits(v[r]);
+          else
+            static_cast<float *>(Y)[e] = v[r];
         }
-        const int64_t mr = m0 + 32 * i + 4 * h2, n = nw + 32 * b + l32;
-        if (full) {
-          const int64_t e0 = mr * N + n;
+      } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t e = e0 + int64_t(8 * (r >> 2) + (r & 3)) * N;
-            if constexpr (kOutBf16)
-              static_cast<uint16_t *>(Y)[e] = bf16_bits(v[r]);
-            else
-              static_cast<float *>(Y)[e] = v[r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) store_out<kOutBf16>(Y, M, N, mr + 8 * (r >> 2) + (r & 3), n, v[r]);
-        }
+        for (int r = 0; r < 16; ++r) store_out<kOutBf16>(Y, M, N, mr + 8 * (r >> 2) + (r & 3), n, v[r]);
       }
     }
-    __syncthreads();
   }
 }
 
