@@ -72,7 +72,7 @@ struct Layout {
 
 struct FwdPlan {
   int64_t ks = 0, rp = 0;
-  size_t off_x16 = 0, off_cs = 0, off_at = 0, off_bt = 0, off_part = 0, off_xa16 = 0, total = 0;
+  size_t off_x16 = 0, off_cs = 0, off_part = 0, off_xa16 = 0, total = 0;
 };
 
 FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
@@ -84,8 +84,6 @@ FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   if (r > 0) {
     p.rp = rank_pad32(r);
     p.ks = rowdot_splits(M, in, r);
-    p.off_at = L.take(size_t(r) * in * 2);
-    p.off_bt = L.take(size_t(out) * p.rp * 2);
     p.off_part = L.take(size_t(p.ks) * M * r * 4);
     p.off_xa16 = L.take(size_t(M) * p.rp * 2);
   }
@@ -94,10 +92,9 @@ FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
 }
 
 struct BwdPlan {
-  int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0, rp = 0, ldM = 0;
-  size_t off_dy16 = 0, off_cs = 0, off_bq = 0, off_gpart = 0, off_g16 = 0, off_gt16 = 0;
-  size_t off_at = 0, off_xapart = 0, off_xa = 0, off_xat16 = 0;
-  size_t off_dbpart = 0, off_dapart = 0, off_a16 = 0, total = 0;
+  int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0, rp = 0;
+  size_t off_dy16 = 0, off_cs = 0, off_gpart = 0, off_g16 = 0;
+  size_t off_xapart = 0, off_xa = 0, off_dbpart = 0, off_dapart = 0, total = 0;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
@@ -108,22 +105,16 @@ BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   p.off_cs = L.take(size_t(in) * (out / 64) * 4);
   if (r > 0) {
     p.rp = rank_pad32(r);
-    p.ldM = pad8(M);
     p.ks_g = rowdot_splits(M, out, r);
     p.ks_x = rowdot_splits(M, in, r);
     p.ks_b = coldot_splits(M, out, r);
     p.ks_a = coldot_splits(M, in, r);
-    p.off_bq = L.take(size_t(r) * out * 2);
     p.off_gpart = L.take(size_t(p.ks_g) * M * r * 4);
     p.off_g16 = L.take(size_t(M) * p.rp * 2);
-    p.off_gt16 = L.take(size_t(p.ldM) * r * 2);
-    p.off_at = L.take(size_t(r) * in * 2);
     p.off_xapart = L.take(size_t(p.ks_x) * M * r * 4);
     p.off_xa = L.take(size_t(M) * r * 4);
-    p.off_xat16 = L.take(size_t(p.ldM) * r * 2);
     p.off_dbpart = L.take(size_t(p.ks_b) * out * r * 4);
     p.off_dapart = L.take(size_t(p.ks_a) * in * r * 4);
-    p.off_a16 = L.take(size_t(in) * p.rp * 2);
   }
   p.total = L.o;
   return p;
@@ -214,22 +205,21 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(X, false, M * in, x16, stream));
     X16 = x16;
   }
+  // one launch: XA partials (X . A) and the GEMM's block scales
   float *cs = at<float>(ws, p.off_cs);
-  QLORA_RUN(QLORA_KERNEL_REDUCE, launch_scales(wq->qscale, wq->gscale, in, out, cs, stream));
-  uint16_t *Bt = nullptr, *XA16 = nullptr;
+  float *part = r > 0 ? at<float>(ws, p.off_part) : nullptr;
+  QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, part, wq->qscale,
+                                             wq->gscale, out, cs, stream));
+  uint16_t *XA16 = nullptr;
   if (r > 0) {
-    uint16_t *At = at<uint16_t>(ws, p.off_at);
-    Bt = at<uint16_t>(ws, p.off_bt);
     XA16 = at<uint16_t>(ws, p.off_xa16);
-    float *part = at<float>(ws, p.off_part);
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_transpose_to_bf16(A, ab, in, r, At, in, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_transpose_to_bf16(B, ab, r, out, Bt, p.rp, stream));
-    QLORA_RUN(QLORA_KERNEL_XA, launch_rowdot(X16, true, At, M, in, r, part, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE,
-              launch_reduce(part, p.ks, M, r, XA, false, XA16, p.rp, nullptr, 0, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(part, p.ks, M, r, XA, false, XA16, p.rp,
+                                                  nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                  stream));
   }
-  QLORA_RUN(QLORA_KERNEL_FWD_GEMM, launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, Bt,
-                                                   int32_t(p.rp), Y, xb, kExact, stream));
+  QLORA_RUN(QLORA_KERNEL_FWD_GEMM,
+            launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, int32_t(p.rp), B, ab, r, Y, xb,
+                            kExact, stream));
   return QLORA_OK;
 }
 
@@ -271,56 +261,41 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(dY, false, M * out, d16, stream));
     dY16 = d16;
   }
-  uint16_t *G16 = nullptr, *A16 = nullptr;
+  float *cs = dX ? at<float>(ws, p.off_cs) : nullptr;
+  uint16_t *G16 = nullptr;
+  if (r > 0 && !XA) {
+    // recompute XA = X . A into the workspace
+    float *xpart = at<float>(ws, p.off_xapart);
+    float *xaw = at<float>(ws, p.off_xa);
+    QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, xpart, nullptr, nullptr,
+                                               out, nullptr, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
+                                                  nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                  stream));
+    XA = xaw;
+  }
+  // one pass over dY: G = dY . B^T and dB = XA^T . dY partials, block scales
+  float *gpart = r > 0 ? at<float>(ws, p.off_gpart) : nullptr;
+  float *dbpart = r > 0 ? at<float>(ws, p.off_dbpart) : nullptr;
+  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XA, M, out, r, gpart, dbpart,
+                                                wq->qscale, wq->gscale, in, cs, stream));
   if (r > 0) {
-    // G = dY . B^T  (rowdot with Qt = B in bf16, contraction over out)
-    const uint16_t *Bq = static_cast<const uint16_t *>(B);
-    if (!ab) {
-      uint16_t *bq = at<uint16_t>(ws, p.off_bq);
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(B, false, int64_t(r) * out, bq, stream));
-      Bq = bq;
-    }
-    float *gpart = at<float>(ws, p.off_gpart);
     G16 = at<uint16_t>(ws, p.off_g16);
-    uint16_t *Gt16 = at<uint16_t>(ws, p.off_gt16);
-    QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_rowdot(dY, xb, Bq, M, out, r, gpart, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp,
-                                                 Gt16, p.ldM, stream));
-    // XA^T in bf16, from the saved XA or recomputed
-    uint16_t *XAt16 = at<uint16_t>(ws, p.off_xat16);
-    if (!XA) {
-      uint16_t *At = at<uint16_t>(ws, p.off_at);
-      float *xpart = at<float>(ws, p.off_xapart);
-      float *xaw = at<float>(ws, p.off_xa);
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_transpose_to_bf16(A, ab, in, r, At, in, stream));
-      QLORA_RUN(QLORA_KERNEL_XA, launch_rowdot(X, xb, At, M, in, r, xpart, stream));
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
-                                                   XAt16, p.ldM, stream));
-    } else {
-      QLORA_RUN(QLORA_KERNEL_REDUCE,
-                launch_transpose_to_bf16(XA, false, M, r, XAt16, p.ldM, stream));
-    }
-    // dB = XA^T . dY : coldot over tokens of dY with XA^T, stored transposed
-    float *dbpart = at<float>(ws, p.off_dbpart);
-    QLORA_RUN(QLORA_KERNEL_DY_PASS,
-              launch_coldot(dY, xb, XAt16, p.ldM, M, out, r, dbpart, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(dbpart, p.ks_b, out, r, dB, true, nullptr, 0,
-                                                 nullptr, 0, stream));
-    // dA = X^T . G : coldot over tokens of X with G^T
+    // G (bf16, zero-padded) and dB (stored [r x out]) in one launch
+    QLORA_RUN(QLORA_KERNEL_REDUCE,
+              launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b, out,
+                             dB, true, nullptr, 0, stream));
+    // dA = X^T . G
     float *dapart = at<float>(ws, p.off_dapart);
-    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_coldot(X, xb, Gt16, p.ldM, M, in, r, dapart, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
-                                                 nullptr, 0, stream));
-    if (dX) {
-      A16 = at<uint16_t>(ws, p.off_a16);
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_pad_to_bf16(A, ab, in, r, A16, p.rp, stream));
-    }
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
+                                                  nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                  stream));
   }
   if (dX) {
-    float *cs = at<float>(ws, p.off_cs);
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_scales(wq->qscale, wq->gscale, in, out, cs, stream));
-    QLORA_RUN(QLORA_KERNEL_DX_GEMM, launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, A16,
-                                                   int32_t(p.rp), dX, xb, kExact, stream));
+    QLORA_RUN(QLORA_KERNEL_DX_GEMM,
+              launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
+                             xb, kExact, stream));
   }
   return QLORA_OK;
 #undef QLORA_RUN

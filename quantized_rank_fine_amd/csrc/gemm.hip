@@ -348,57 +348,93 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(a[i], bb[b], acc[b][i]);
   };
 
-  // ---- prologue: tiles 0..kStages-1 in flight (clamped to the last tile),
-  // operands of tile 0 substep 0 ready
+  // ---- prologue: tiles 0..kStages-1 in flight (clamped to the last tile);
+  // tiles 0 and 1 landed and visible; operands of tile 0 substep 0 ready.
+  static_assert(kStages >= 4, "the pipeline keeps two tiles visible ahead of the issue");
 #pragma unroll
   for (int p = 0; p < kStages; ++p) issue(p < KT ? p : KT - 1, p);
-  wait_vmcnt<(kStages - 1) * kLoadsPerTile>();
+  wait_vmcnt<(kStages - 2) * kLoadsPerTile>();
   __syncthreads();
-  uint32_t nib[2][2];
-  float sc[kNS];
+  uint32_t nib[2][2], nibn[2][2];
+  float sc[kNS], scn[kNS];
   u32x4_t a0[8], a1[8], b0[2], b1[2];
   read_tile(smem, nib, sc);
   read_a(smem, 0, a0);
   make_b(nib, sc, 0, b0);
 
-  // Every iteration issues one tile group (past the end: a harmless re-load
-  // of the last tile into the stage just freed), so one constant vmcnt wait
-  // always means "tile kt+1 has landed".
+  // Invariant at the top of iteration kt: tiles kt and kt+1 are visible;
+  // a0/b0 hold substep 0 of tile kt and nib/sc its codes and scales.  Every
+  // iteration issues one tile group (past the end: a harmless re-load of the
+  // last tile into the stage just freed), so one constant vmcnt wait always
+  // means "tile kt+2 has landed".  Codes and scales are read one half-step
+  // before they are expanded, so no expansion waits on LDS.
   for (int kt = 0; kt < KT; ++kt) {
     const char *st = smem + (kt % kStages) * kStageBytes;
     const char *sn = smem + ((kt + 1) % kStages) * kStageBytes;
-    // substep 0 of tile kt; prepare substep 1
+    // substep 0 of tile kt; prepare substep 1 and fetch tile kt+1's codes
+    read_tile(sn, nibn, scn);
     read_a(st, 1, a1);
     make_b(nib, sc, 1, b1);
     mfmas(a0, b0);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-      if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);           // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+      if (q < (kFwd ? 14 : 12)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);            // VALU
     }
-    // tile kt+1 landed and visible; the stage of tile kt is free
-    wait_vmcnt<(kStages - 2) * kLoadsPerTile>();
+    // tile kt+2 landed and visible; the stage of tile kt is free
+    wait_vmcnt<(kStages - 3) * kLoadsPerTile>();
     __syncthreads();
     issue(kt + kStages < KT ? kt + kStages : KT - 1, kt % kStages);
     // substep 1 of tile kt; prepare substep 0 of tile kt+1 (past the end:
     // reads of a stage that is never used)
-    read_tile(sn, nib, sc);
     read_a(sn, 0, a0);
-    make_b(nib, sc, 0, b0);
+    make_b(nibn, scn, 0, b0);
     mfmas(a1, b1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kFwd ? 6 : 4, 0);    // codes + scales
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-      if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-      if (q >= 3) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0); // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+      if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);            // VALU
     }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      nib[b][0] = nibn[b][0];
+      nib[b][1] = nibn[b][1];
+    }
+#pragma unroll
+    for (int q = 0; q < kNS; ++q) sc[q] = scn[q];
   }
   wait_vmcnt<0>();
 }
 
-// Epilogue.  The rank-r term (P16 . Q16^T, bf16, zero-padded to rp columns)
+// The adapter factor of the rank-r term, read in the caller's layout and
+// dtype: element (n, j) = Q[n * sn + j * sj] for j < r, 0 beyond.
+struct AdapterRef {
+  const void *Q;
+  bool bf16;
+  int64_t sn, sj;
+  int r;
+};
+
+// 8 consecutive rank indices j0..j0+7 of row n as a bf16x8 MFMA operand.
+__device__ __forceinline__ u32x4_t load_adapter8(const AdapterRef &q, int64_t n, int j0) {
+  uint32_t e[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int j = j0 + t;
+    uint32_t v = 0;
+    if (j < q.r) {
+      const int64_t i = n * q.sn + int64_t(j) * q.sj;
+      v = q.bf16 ? static_cast<const uint16_t *>(q.Q)[i] : bf16_bits(static_cast<const float *>(q.Q)[i]);
+    }
+    e[t] = v;
+  }
+  return u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
+// Epilogue.  The rank-r term P16 . Q^T (P16 bf16 [M x ldp], zero-padded
+// columns r..ldp-1; Q the adapter factor, rows indexed by the output column)
 // is added by the k-half-0 wavefronts only, so it enters every output once.
 // The two k halves of a column half are then summed through LDS in four
 // rounds of two row blocks: every wavefront writes its partials of row blocks
@@ -409,8 +445,8 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
 // 4c..4c+3 of every lane (16 B per lane, contiguous across lanes).
 template <bool kOutBf16>
 __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
-                                         const uint16_t *__restrict__ P16,
-                                         const uint16_t *__restrict__ Q16, int rp, int64_t M,
+                                         const uint16_t *__restrict__ P16, int ldp,
+                                         const AdapterRef q, int64_t M,
                                          int64_t N, int64_t m0, int64_t n0, void *__restrict__ Y) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -419,21 +455,20 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
   const int64_t nw = n0 + 64 * ch;
 
   if (kh == 0) {
-    for (int r0 = 0; r0 < rp; r0 += 16) {
-      u32x4_t q[2];
+    for (int r0 = 0; r0 < q.r; r0 += 16) {
+      u32x4_t qb[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int64_t n = nw + 32 * b + l32;
-        q[b] = (n < N) ? *reinterpret_cast<const u32x4_t *>(Q16 + n * rp + r0 + 8 * h2)
-                       : u32x4_t{0u, 0u, 0u, 0u};
+        qb[b] = (n < N) ? load_adapter8(q, n, r0 + 8 * h2) : u32x4_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t m = m0 + 32 * i + l32;
-        const u32x4_t p = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * rp + r0 + 8 * h2)
+        const u32x4_t p = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * ldp + r0 + 8 * h2)
                                   : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(p, q[b], acc[b][i]);
+        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(p, qb[b], acc[b][i]);
       }
     }
   }
@@ -492,7 +527,7 @@ template <bool kOutBf16, bool kExact>
 __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t K, int64_t N,
     const uint16_t *__restrict__ X16, int64_t M, const uint16_t *__restrict__ XA16,
-    const uint16_t *__restrict__ Bt, int rp, void *__restrict__ Y, ExpandConsts tb,
+    int ldp, AdapterRef bq, void *__restrict__ Y, ExpandConsts tb,
     int nt_count) {
   extern __shared__ __align__(16) char smem[];
   int mt, nt;
@@ -506,8 +541,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<true, kExact>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
-  // rank-r term: y += XA16 . Bt^T (both bf16, zero-padded to rp columns)
-  epilogue<kOutBf16>(acc, smem, XA16, Bt, rp, M, N, m0, n0, Y);
+  // rank-r term: y += XA16 . B (B read as rows n of B^T)
+  epilogue<kOutBf16>(acc, smem, XA16, ldp, bq, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
@@ -515,7 +550,7 @@ template <bool kOutBf16, bool kExact>
 __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t IN, int64_t OUT,
     const uint16_t *__restrict__ dY16, int64_t M, const uint16_t *__restrict__ G16,
-    const uint16_t *__restrict__ A16, int rp, void *__restrict__ dX, ExpandConsts tb,
+    int ldp, AdapterRef aq, void *__restrict__ dX, ExpandConsts tb,
     int nt_count) {
   extern __shared__ __align__(16) char smem[];
   int mt, nt;
@@ -529,21 +564,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<false, kExact>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
-  // rank-r term: dX += G16 . A16^T (G16 [M x rp], A16 [IN x rp], zero-padded)
-  epilogue<kOutBf16>(acc, smem, G16, A16, rp, M, IN, m0, i0, dX);
-}
-
-// ----------------------------------------------------------- scale prep
-// cs[b][row] = q8[row * NB + b] * s2[(row * NB + b) >> 8]  (fp32 product)
-__global__ __launch_bounds__(256) void scales_kernel(const int8_t *__restrict__ q8,
-                                                     const float *__restrict__ s2, int64_t rows,
-                                                     int64_t NB, float *__restrict__ cs) {
-  const int64_t n = rows * NB;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
-    const int64_t b = i / rows, row = i - b * rows;
-    const int64_t src = row * NB + b;
-    cs[i] = float(q8[src]) * s2[src >> 8];
-  }
+  // rank-r term: dX += G16 . A^T (A read as rows i of A)
+  epilogue<kOutBf16>(acc, smem, G16, ldp, aq, M, IN, m0, i0, dX);
 }
 
 bool set_lds(const void *fn) {
@@ -553,22 +575,12 @@ bool set_lds(const void *fn) {
 
 }  // namespace
 
-hipError_t launch_scales(const int8_t *qscale, const float *gscale, int64_t rows, int64_t cols,
-                         float *cs, hipStream_t s) {
-  const int64_t nb = cols / 64, n = rows * nb;
-  if (n == 0) return hipSuccess;
-  int64_t g = (n + 255) / 256;
-  if (g > 8192) g = 8192;
-  hipLaunchKernelGGL(scales_kernel, dim3(unsigned(g)), dim3(256), 0, s, qscale, gscale, rows, nb,
-                     cs);
-  return hipGetLastError();
-}
-
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int64_t N,
-                           const uint16_t *X16, int64_t M, const uint16_t *XA16,
-                           const uint16_t *Bt, int32_t rp, void *Y, bool y_bf16, bool exact,
-                           hipStream_t s) {
+                           const uint16_t *X16, int64_t M, const uint16_t *XA16, int32_t ldp,
+                           const void *B, bool b_bf16, int32_t r, void *Y, bool y_bf16,
+                           bool exact, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  const AdapterRef bq{B, b_bf16, 1, N, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((N + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
   const ExpandConsts tb = tables().expand;
@@ -577,7 +589,7 @@ hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int
     static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB, EX>));        \
     if (!ok) return hipErrorInvalidValue;                                                      \
     hipLaunchKernelGGL((fwd_gemm_kernel<OB, EX>), grid, dim3(kThreads), kLdsBytes, s, codes,  \
-                       cs, K, N, X16, M, XA16, Bt, int(rp), Y, tb, ntc);                       \
+                       cs, K, N, X16, M, XA16, int(ldp), bq, Y, tb, ntc);                      \
   } while (0)
   if (y_bf16) {
     if (exact) QLORA_FWD(true, true); else QLORA_FWD(true, false);
@@ -589,10 +601,11 @@ hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int
 }
 
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int64_t out,
-                          const uint16_t *dY16, int64_t M, const uint16_t *G16,
-                          const uint16_t *A16, int32_t rp, void *dX, bool dx_bf16, bool exact,
-                          hipStream_t s) {
+                          const uint16_t *dY16, int64_t M, const uint16_t *G16, int32_t ldp,
+                          const void *A, bool a_bf16, int32_t r, void *dX, bool dx_bf16,
+                          bool exact, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  const AdapterRef aq{A, a_bf16, int64_t(r), 1, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((in + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
   const ExpandConsts tb = tables().expand;
@@ -601,7 +614,7 @@ hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int
     static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB, EX>));         \
     if (!ok) return hipErrorInvalidValue;                                                      \
     hipLaunchKernelGGL((dx_gemm_kernel<OB, EX>), grid, dim3(kThreads), kLdsBytes, s, codes,   \
-                       cs, in, out, dY16, M, G16, A16, int(rp), dX, tb, ntc);                  \
+                       cs, in, out, dY16, M, G16, int(ldp), aq, dX, tb, ntc);                  \
   } while (0)
   if (dx_bf16) {
     if (exact) QLORA_DX(true, true); else QLORA_DX(true, false);

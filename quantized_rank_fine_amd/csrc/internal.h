@@ -38,64 +38,63 @@ const Tables &tables();
 hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale,
                            float *gscale, int64_t nblocks, hipStream_t s);
 
-// dst[j][k] = src[k][j] as bf16 for src [K x R] (f32 or bf16); dst rows have
-// length ldd >= K and are zero-padded in [K, ldd).
-hipError_t launch_transpose_to_bf16(const void *src, bool src_bf16, int64_t K,
-                                    int64_t R, uint16_t *dst, int64_t ldd,
-                                    hipStream_t s);
 // dst[n] (bf16) = src[n] (f32 or bf16)
 hipError_t launch_convert_to_bf16(const void *src, bool src_bf16, int64_t n,
                                   uint16_t *dst, hipStream_t s);
 
-// part[ks][M][R] = sum over k in split ks of P[m][k] * Qt[j][k]
-//   P: [M x K] (f32 or bf16), Qt: [R x K] bf16.  rowdot_splits gives the
-//   number of splits (host-only planning).
+// Number of split-K partials the rank-r passes write (host-only planning).
+//   rowdot: C[M x R] = P[M x K] . Q, split over K;
+//   coldot: C[K x R] = P[M x K]^T . Q[M x R], split over the tokens M.
 int64_t rowdot_splits(int64_t M, int64_t K, int64_t R);
-hipError_t launch_rowdot(const void *P, bool p_bf16, const uint16_t *Qt,
-                         int64_t M, int64_t K, int64_t R, float *part,
-                         hipStream_t s);
-
-// part[ks][K][R] = sum over m in split ks of P[m][k] * Qt[j][m]
-//   P: [M x K] (f32 or bf16), Qt: [R x ldq] bf16 (the transposed skinny
-//   factor, ldq % 8 == 0)
 int64_t coldot_splits(int64_t M, int64_t K, int64_t R);
-hipError_t launch_coldot(const void *P, bool p_bf16, const uint16_t *Qt,
-                         int64_t ldq, int64_t M, int64_t K, int64_t R,
-                         float *part, hipStream_t s);
 
-// out[i] = sum_ks part[ks][i] in ks order (fp32) for a [rows x R] result,
-// with optional extra outputs: out (fp32; [R x rows] if transpose_out),
-// out_bf16 ([rows x ld_bf16], zero-padded columns) and outT_bf16
-// ([R x ldT]).
-hipError_t launch_reduce(const float *part, int64_t ks, int64_t rows, int64_t R,
-                         float *out, bool transpose_out, uint16_t *out_bf16,
-                         int64_t ld_bf16, uint16_t *outT_bf16, int64_t ldT,
-                         hipStream_t s);
+// Forward prep, one launch: xa_part[ks][M][r] = partial X . A (X [M x in],
+// A [in x r], each f32 or bf16) and, if cs != nullptr, the block scales
+// cs[b][row] = q8[row][b] * s2[group] of the [in x out] weight.
+hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf16,
+                           int64_t M, int64_t in, int64_t r, float *xa_part,
+                           const int8_t *qscale, const float *gscale, int64_t out,
+                           float *cs, hipStream_t s);
 
-// cs[b][row] = q8[row][b] * s2[group] (fp32) for a quantized [rows x cols]
-// weight: the block scales, one row per 64-wide block column.
-hipError_t launch_scales(const int8_t *qscale, const float *gscale, int64_t rows,
-                         int64_t cols, float *cs, hipStream_t s);
+// Backward pass over dY, one launch: g_part[ks][M][r] = partial dY . B^T
+// (B [r x out]); db_part[ks][out][r] = partial dY^T . XA (XA fp32 [M x r]);
+// and, if cs != nullptr, the block scales as in launch_fwd_prep.
+hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf16,
+                         const float *XA, int64_t M, int64_t out, int64_t r,
+                         float *g_part, float *db_part, const int8_t *qscale,
+                         const float *gscale, int64_t in, float *cs, hipStream_t s);
 
-// dst[i][j] = src[i][j] as bf16 for j < cols, 0 for cols <= j < ldd.
-hipError_t launch_pad_to_bf16(const void *src, bool src_bf16, int64_t rows,
-                              int64_t cols, uint16_t *dst, int64_t ldd,
-                              hipStream_t s);
+// Backward pass over X: da_part[ks][in][r] = partial X^T . G with G given as
+// G16 bf16 [M x ldg].
+hipError_t launch_bwd_x(const void *X, bool x_bf16, const uint16_t *G16, int64_t ldg,
+                        int64_t M, int64_t in, int64_t r, float *da_part,
+                        hipStream_t s);
 
-// y = X16 . deq(Wq) + XA16 . Bt^T (K = in, N = out).  X16 [M x K] bf16;
-// XA16 [M x rp], Bt [N x rp] bf16 zero-padded (rp = round_up(r, 32), 0 for
-// no adapter); cs from launch_scales(rows = K, cols = N).
+// Two fixed-order split sums in one launch.  For each of a, b (skipped when
+// its part is nullptr): out[i] = sum_k part[k][i] over a [rows x R] result;
+// outputs (each optional) fp32 ([R x rows] if transpose) and bf16
+// [rows x ld] with zero padding columns R..ld-1.
+hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int64_t R,
+                          float *out_a, bool transpose_a, uint16_t *bf16_a, int64_t ld_a,
+                          const float *part_b, int64_t ks_b, int64_t rows_b, float *out_b,
+                          bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s);
+
+// y = X16 . deq(Wq) + XA16 . B (K = in, N = out).  X16 [M x K] bf16; XA16
+// [M x ldp] bf16 with zero padding columns r..ldp-1; B [r x N] (f32 or bf16)
+// as given by the caller; cs from the prep pass (rows = K).
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K,
                            int64_t N, const uint16_t *X16, int64_t M,
-                           const uint16_t *XA16, const uint16_t *Bt, int32_t rp,
-                           void *Y, bool y_bf16, bool exact, hipStream_t s);
+                           const uint16_t *XA16, int32_t ldp, const void *B,
+                           bool b_bf16, int32_t r, void *Y, bool y_bf16, bool exact,
+                           hipStream_t s);
 
-// dX = dY16 . deq(Wq)^T + G16 . A16^T.  dY16 [M x out] bf16; G16 [M x rp],
-// A16 [in x rp] bf16 zero-padded; cs from launch_scales(rows = in, cols = out).
+// dX = dY16 . deq(Wq)^T + G16 . A^T.  dY16 [M x out] bf16; G16 [M x ldp] bf16
+// zero-padded; A [in x r] (f32 or bf16) as given; cs as in the forward.
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
                           int64_t out, const uint16_t *dY16, int64_t M,
-                          const uint16_t *G16, const uint16_t *A16, int32_t rp,
-                          void *dX, bool dx_bf16, bool exact, hipStream_t s);
+                          const uint16_t *G16, int32_t ldp, const void *A,
+                          bool a_bf16, int32_t r, void *dX, bool dx_bf16, bool exact,
+                          hipStream_t s);
 
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }

@@ -72,7 +72,8 @@ def test_workspace_sizes(L):
         for act in (q.BF16, q.F32):
             f = q.qlora_fwd_workspace_bytes(M, i, o, r, act)
             b = q.qlora_bwd_workspace_bytes(M, i, o, r, act)
-            assert f >= r * i * 2 + o * r * 2 + M * r * 4 + i * o // 16
+            # block scales (fp32 per 64 weights), XA split partials, XA in bf16
+            assert f >= i * o // 16 + M * r * 4 + M * r * 2
             assert b >= M * r * 4 + i * o // 16
             assert f % 256 == 0 and b % 256 == 0
             if act == q.F32:
