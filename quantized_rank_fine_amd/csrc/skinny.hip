@@ -64,15 +64,21 @@ __device__ __forceinline__ uint32_t load1_bf16(const void *p, int64_t i) {
     return f32_to_bf16_bits(static_cast<const float *>(p)[i]);
 }
 
-// 8 elements p[i0 + q*stride], q = 0..7, as bf16x8 (elements with
-// (q < nvalid) only; the rest are 0).
-template <bool kBf16>
-__device__ __forceinline__ u32x4_t gather8_bf16(const void *p, int64_t i0, int64_t stride,
-                                               int nvalid) {
-  uint32_t e[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) e[q] = (q < nvalid) ? load1_bf16<kBf16>(p, i0 + q * stride) : 0u;
-  return u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+// Transposed read of a row-major bf16 LDS tile T (pitch PP elements): lane
+// (i16 = lane & 15, h = (lane >> 4) & 3) receives column cb + i16, rows
+// rb + 8h .. rb + 8h + 7 -- the k-run of one MFMA 16x16x32 operand lane --
+// from two ds_read_b64_tr_b16 (each: 16 lanes x 4 rows -> 4 columns).
+__device__ __forceinline__ u32x4_t lds_col8(const uint16_t *T, int PP, int rb, int cb) {
+  const int lane = threadIdx.x & 63, i16 = lane & 15, h = (lane >> 4) & 3;
+  const int q = i16 & 3, tq = i16 >> 2;
+  const int rr = rb + 8 * h + tq;
+  lds_char *base = (lds_char *)(T);
+  i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(base + (rr * PP + cb + 4 * q) * 2));
+  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(base + ((rr + 4) * PP + cb + 4 * q) * 2));
+  u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
 }
 
 // ------------------------------------------------------------ conversions
@@ -94,8 +100,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 // ------------------------------------------------------------ block scales
 // cs[b][row] = q8[row * NB + b] * s2[(row * NB + b) >> 8]  (fp32 product), the
 // per-block scales of a quantized [rows x 64 NB] weight laid out one row per
-// 64-wide block column (the layout the fused GEMMs stream).  Role of a merged
-// launch: workgroups wg = 0 .. nwg-1 of it.
+// 64-wide block column (the layout the fused GEMMs stream).  A thread owns one
+// row and 16 consecutive blocks of it: one 16-B read of q8, 16 stores that are
+// coalesced across the wavefront (consecutive rows).  Role of a merged launch:
+// workgroups wg = 0 .. nwg-1 of it, nwg = scales_workgroups(rows, NB).
 struct ScalesArgs {
   const int8_t *q8;
   const float *s2;
@@ -103,38 +111,74 @@ struct ScalesArgs {
   float *cs;
 };
 
+constexpr int kScaleSpan = 16;   // blocks per thread
+
+__host__ __device__ inline int64_t scales_workgroups(int64_t rows, int64_t NB) {
+  return ((rows + 255) / 256) * ((NB + kScaleSpan - 1) / kScaleSpan);
+}
+
 __device__ __forceinline__ void scales_role(const ScalesArgs &a, int64_t wg, int64_t nwg) {
-  const int64_t n = a.rows * a.NB;
-  for (int64_t i = wg * 256 + threadIdx.x; i < n; i += nwg * 256) {
-    const int64_t b = i / a.rows, row = i - b * a.rows;
-    const int64_t src = row * a.NB + b;
-    a.cs[i] = float(a.q8[src]) * a.s2[src >> 8];
+  (void)nwg;
+  const int64_t nspan = (a.NB + kScaleSpan - 1) / kScaleSpan;
+  const int64_t row = (wg / nspan) * 256 + threadIdx.x;
+  const int64_t b0 = (wg % nspan) * kScaleSpan;
+  if (row >= a.rows) return;
+  const int8_t *q = a.q8 + row * a.NB + b0;
+  int8_t v[kScaleSpan];
+  if (b0 + kScaleSpan <= a.NB && ((reinterpret_cast<uintptr_t>(q) & 15u) == 0)) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(q);
+#pragma unroll
+    for (int e = 0; e < kScaleSpan; ++e) v[e] = int8_t(w[e >> 2] >> (8 * (e & 3)));
+  } else {
+#pragma unroll
+    for (int e = 0; e < kScaleSpan; ++e) v[e] = (b0 + e < a.NB) ? q[e] : int8_t(0);
+  }
+#pragma unroll
+  for (int e = 0; e < kScaleSpan; ++e) {
+    const int64_t b = b0 + e;
+    if (b < a.NB) a.cs[b * a.rows + row] = float(v[e]) * a.s2[(row * a.NB + b) >> 8];
   }
 }
 
 // ------------------------------------------------------------------ rowdot
 //
 // Workgroup: 4 wavefronts x 16 rows = 64 rows of P, all R columns, one
-// contiguous K range.  Q is staged per 64-wide K slice in LDS as [RP][64]
-// (rows of 128 B, 16-B chunks XOR-swizzled by row) and shared by the 4
-// wavefronts; P rows go straight from global memory into the MFMA A operand.
+// contiguous K range walked in slices of kTK (256 for R <= 64, else 64).  Per
+// slice, Q is staged in LDS as [RP][kTK] (16-B chunks XOR-swizzled by row) and
+// shared by the 4 wavefronts; P rows go straight from global memory into the
+// MFMA A operand.  Small register and LDS footprints keep several workgroups
+// resident per CU, which hides the load latency of a slice; at the usual
+// shapes one slice is the whole K range of a workgroup.
 
 constexpr int kRowdotRows = 64;
-constexpr int kSliceK = 64;
+
+__host__ __device__ inline int rank_pad16(int R) { return (R + 15) / 16 * 16; }
+__host__ __device__ inline bool skinny_wide(int R) { return rank_pad16(R) <= 64; }
 
 struct RowdotArgs {
   const void *P;      // [M x K]
   const void *Q;      // Qt [R x K] (kQt) or Q [K x R]
   int64_t M, K;
   int R;
-  int64_t kchunk;     // K range per split (multiple of 64)
+  int64_t kchunk;     // K range per split (multiple of the slice width)
   int64_t mt;         // row tiles
   float *part;        // [ks][M][R]
 };
 
-template <bool kPbf16, bool kQt, bool kQbf16>
+// Q modes: kQRows -- Qt [R x K], rows contiguous along k (B for G);
+// kQFast -- Q [K x R] with R % 8 == 0, staged row-major [kTK][RP] with 16-B
+// copies and read transposed; kQGeneric -- Q [K x R], any R, staged
+// transposed element by element.
+constexpr int kQRows = 0, kQFast = 1, kQGeneric = 2;
+
+template <bool kPbf16, int kQMode, bool kQbf16, bool kWide>
 __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, unsigned char *smem) {
-  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem);   // [RP][64]
+  constexpr int kTK = kWide ? 256 : 64;      // slice width
+  constexpr int kCPR = kTK / 8;              // 16-B chunks per staged Q row
+  constexpr int kNS = kTK / 32;              // MFMA k substeps per slice
+  constexpr int kMaxRT = kWide ? 4 : 16;     // 16-wide column tiles of R
+  constexpr int kMask = (kCPR < 16 ? kCPR : 16) - 1;
+  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem);   // [RP][kTK], or [kTK][RP] (kQFast)
   const int R = a.R;
   const int RT = (R + 15) / 16;
   const int RP = RT * 16;
@@ -149,56 +193,91 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
   const size_t esz = kPbf16 ? 2 : 4;
   const char *prow = static_cast<const char *>(a.P) + (row_ok ? row : 0) * a.K * esz;
 
-  f32x4_t acc[16];
+  f32x4_t acc[kMaxRT];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kMaxRT; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = kb; k0 < ke; k0 += kSliceK) {
-    // A operands of this slice: substep u covers k0 + 32u + 8h .. +8
-    u32x4_t av[2];
+  for (int64_t k0 = kb; k0 < ke; k0 += kTK) {
+    // A operands of this slice: substep s covers k0 + 32 s + 8 h .. +8
+    u32x4_t pv[kNS];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      av[u] = row_ok ? load8_bf16<kPbf16>(prow + (k0 + 32 * u + 8 * h) * esz)
-                     : u32x4_t{0u, 0u, 0u, 0u};
+    for (int s = 0; s < kNS; ++s) {
+      const int64_t k = k0 + 32 * s + 8 * h;
+      pv[s] = (row_ok && k < ke) ? load8_bf16<kPbf16>(prow + k * esz) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
-    // stage Q for k0..k0+63 as [RP][64]: RP rows x 8 chunks of 8 k
-    for (int c = t; c < RP * 8; c += 256) {
-      const int j = c >> 3, ch = c & 7;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (j < R) {
+    __syncthreads();                         // previous slice's readers are done
+    if constexpr (kQMode == kQRows) {
+      // rows of Qt are contiguous along k: one 16-B chunk = 8 k of one j
+      for (int cid = t; cid < RP * kCPR; cid += 256) {
+        const int j = cid / kCPR, ch = cid % kCPR;
         const int64_t k = k0 + 8 * ch;
-        if constexpr (kQt)
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (j < R && k < ke)
           v = load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (int64_t(j) * a.K + k) * (kQbf16 ? 2 : 4));
-        else
-          v = gather8_bf16<kQbf16>(a.Q, k * R + j, R, 8);
+        *reinterpret_cast<u32x4_t *>(sQ + j * kTK + ((ch ^ (j & kMask)) * 8)) = v;
       }
-      *reinterpret_cast<u32x4_t *>(sQ + j * 64 + ((ch ^ (j & 7)) * 8)) = v;
+    } else if constexpr (kQMode == kQFast) {
+      // Q [K x R], R % 8 == 0: rows k0..k0+kTK-1 copied as 16-B chunks into
+      // [kTK][RP] (columns R..RP-1 zero)
+      const int C8 = RP / 8, R8 = R / 8;
+      for (int cid = t; cid < kTK * C8; cid += 256) {
+        const int kk = cid / C8, c = cid - kk * C8;
+        const int64_t k = k0 + kk;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (c < R8 && k < ke)
+          v = load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (k * R + 8 * c) * (kQbf16 ? 2 : 4));
+        *reinterpret_cast<u32x4_t *>(sQ + kk * RP + 8 * c) = v;
+      }
+    } else {
+      // Q [K x R] row-major: coalesced element reads (16 in flight per
+      // thread), transposed LDS writes
+      for (int e0 = 0; e0 < kTK * RP; e0 += 256 * 16) {
+        uint16_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          const int kk = e / RP, j = e - kk * RP;
+          const int64_t k = k0 + kk;
+          v[u] = (e < kTK * RP && j < R && k < ke) ? uint16_t(load1_bf16<kQbf16>(a.Q, k * R + j))
+                                                   : uint16_t(0);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          const int kk = e / RP, j = e - kk * RP;
+          if (e < kTK * RP) sQ[j * kTK + (((kk >> 3) ^ (j & kMask)) << 3) + (kk & 7)] = v[u];
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int s = 0; s < kNS; ++s) {
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if (s < RT) {
-          const int j = 16 * s + i16;
-          const int ch = 4 * u + h;
-          u32x4_t b = *reinterpret_cast<const u32x4_t *>(sQ + j * 64 + ((ch ^ (j & 7)) * 8));
-          acc[s] = mfma16x16x32(av[u], b, acc[s]);
+      for (int st = 0; st < kMaxRT; ++st) {
+        if (st < RT) {
+          u32x4_t b;
+          if constexpr (kQMode == kQFast) {
+            b = lds_col8(sQ, RP, 32 * s, 16 * st);
+          } else {
+            const int j = 16 * st + i16;
+            const int c = 4 * s + h;
+            b = *reinterpret_cast<const u32x4_t *>(sQ + j * kTK + ((c ^ (j & kMask)) * 8));
+          }
+          acc[st] = mfma16x16x32(pv[s], b, acc[st]);
         }
       }
     }
   }
-  // C layout: lane holds rows 4h..4h+3 of the wave's 16, column i16 of subtile s
+  // C layout: lane holds rows 4h..4h+3 of the wave's 16, column i16 of subtile st
   float *out = a.part + int64_t(ks) * a.M * R;
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s < RT) {
-      const int j = 16 * s + i16;
+  for (int st = 0; st < kMaxRT; ++st) {
+    if (st < RT) {
+      const int j = 16 * st + i16;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t m = m0 + wave * 16 + 4 * h + q;
-        if (m < a.M && j < R) out[m * R + j] = acc[s][q];
+        if (m < a.M && j < R) out[m * R + j] = acc[st][q];
       }
     }
   }
@@ -206,13 +285,14 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
 
 // ------------------------------------------------------------------ coldot
 //
-// Workgroup: 4 wavefronts x 16 columns of P = 64 columns, all R, one
-// contiguous range of tokens.  Per 64-token slice the P tile (64 x 64 bf16)
-// is stored row-major in LDS with a 160-byte row pitch (conflict-free for the
-// transposed reads) and Q^T (R x 64) with swizzled 16-B chunks.
+// Workgroup: 4 wavefronts, kTN columns of P (256 for R <= 64, else 64; a
+// wavefront owns kTN/4 of them as 16-wide MFMA tiles), all R, one contiguous
+// token range walked in 64-token slices.  Per slice the P tile (64 x kTN
+// bf16) is stored row-major in LDS with a row pitch that keeps the transposed
+// reads conflict-free, and Q^T (R x 64) with swizzled 16-B chunks.
 
-constexpr int kColdotCols = 64;
-constexpr int kPPitch = 80;   // bf16 elements per P row in LDS (160 bytes)
+__host__ __device__ inline int coldot_tn(int R) { return skinny_wide(R) ? 256 : 64; }
+__host__ __device__ inline int coldot_pitch(int TN) { return TN == 256 ? 272 : 80; }
 
 struct ColdotArgs {
   const void *P;      // [M x K]
@@ -225,16 +305,26 @@ struct ColdotArgs {
   float *part;        // [ks][K][R]
 };
 
-template <bool kPbf16, bool kQbf16>
+// kQFastC: Q rows hold a multiple of 8 columns and are 16-B aligned (R % 8
+// == 0 or a zero-padded bf16 Q), so Q[mm..mm+63][0..RP) is copied row-major
+// with 16-B chunks and read transposed; otherwise Q^T is staged element by
+// element.
+template <bool kPbf16, bool kQbf16, bool kWide, bool kQFastC>
 __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, unsigned char *smem) {
-  uint16_t *sP = reinterpret_cast<uint16_t *>(smem);               // [64][kPPitch]
-  uint16_t *sQ = sP + 64 * kPPitch;                                // [RP][64]
+  constexpr int kTN = kWide ? 256 : 64;
+  constexpr int kPP = kTN == 256 ? 272 : 80;  // LDS row pitch of the P tile (elements)
+  constexpr int kCPR = kTN / 8;               // 16-B chunks per P row
+  constexpr int kNP = 64 * kCPR / 256;        // P chunks per thread: 8 or 2
+  constexpr int kNCT = kTN / 64;              // 16-wide column tiles per wavefront
+  constexpr int kMaxRT = kWide ? 4 : 16;
   const int R = a.R;
   const int RT = (R + 15) / 16;
   const int RP = RT * 16;
+  uint16_t *sP = reinterpret_cast<uint16_t *>(smem);               // [64][kPP]
+  uint16_t *sQ = sP + 64 * kPP;                        // [RP][64], or [64][RP] (kQFastC)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i16 = lane & 15, h = lane >> 4;
-  const int64_t c0 = (wg % a.ct) * kColdotCols;
+  const int64_t c0 = (wg % a.ct) * kTN;
   const int ks = int(wg / a.ct);
   const int64_t mb = int64_t(ks) * a.mchunk;
   const int64_t me = min64(a.M, mb + a.mchunk);
@@ -242,76 +332,110 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
   const size_t esz = kPbf16 ? 2 : 4;
   const char *P = static_cast<const char *>(a.P);
 
-  f32x4_t acc[16];
+  f32x4_t acc[kNCT][kMaxRT];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c4 = 0; c4 < kNCT; ++c4)
+#pragma unroll
+    for (int s = 0; s < kMaxRT; ++s) acc[c4][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t mm = mb; mm < me; mm += 64) {
-    // P tile rows mm..mm+63, columns c0..c0+63: 64 rows x 8 chunks of 16 B
-    u32x4_t pv[2];
+    u32x4_t pv[kNP];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = t + 256 * it;
-      const int rr = c >> 3, ch = c & 7;
+    for (int q = 0; q < kNP; ++q) {
+      const int cid = t + 256 * q;
+      const int rr = cid / kCPR, ch = cid % kCPR;
       const int64_t m = mm + rr, col = c0 + 8 * ch;
-      pv[it] = (m < me && col < K) ? load8_bf16<kPbf16>(P + (m * K + col) * esz)
-                                   : u32x4_t{0u, 0u, 0u, 0u};
+      pv[q] = (m < me && col < K) ? load8_bf16<kPbf16>(P + (m * K + col) * esz)
+                                  : u32x4_t{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
+    __syncthreads();                         // previous slice's readers are done
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = t + 256 * it;
-      const int rr = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4_t *>(sP + rr * kPPitch + 8 * ch) = pv[it];
+    for (int q = 0; q < kNP; ++q) {
+      const int cid = t + 256 * q;
+      const int rr = cid / kCPR, ch = cid % kCPR;
+      *reinterpret_cast<u32x4_t *>(sP + rr * kPP + 8 * ch) = pv[q];
     }
-    // Q^T for tokens mm..mm+63: RP rows x 8 chunks of 8 tokens
-    for (int c = t; c < RP * 8; c += 256) {
-      const int j = c >> 3, ch = c & 7;
-      const int64_t m = mm + 8 * ch;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (j < R && m < me) {
-        const int64_t left = me - m;
-        v = gather8_bf16<kQbf16>(a.Q, m * a.ldq + j, a.ldq, left < 8 ? int(left) : 8);
+    if constexpr (kQFastC) {
+      // Q rows mm..mm+63, columns 0..RP-1, as 16-B chunks into [64][RP]
+      const int C8 = RP / 8;
+      for (int cid = t; cid < 64 * C8; cid += 256) {
+        const int mi = cid / C8, c = cid - mi * C8;
+        const int64_t m = mm + mi;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (m < me && 8 * c < a.ldq)
+          v = load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (m * a.ldq + 8 * c) * (kQbf16 ? 2 : 4));
+        *reinterpret_cast<u32x4_t *>(sQ + mi * RP + 8 * c) = v;
       }
-      *reinterpret_cast<u32x4_t *>(sQ + j * 64 + ((ch ^ (j & 7)) * 8)) = v;
+    } else {
+      // Q^T for tokens mm..mm+63: coalesced element reads of Q rows,
+      // transposed LDS writes (16-B chunks of 8 tokens, swizzled by j)
+      for (int e0 = 0; e0 < 64 * RP; e0 += 256 * 16) {
+        uint16_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          const int mi = e / RP, j = e - mi * RP;
+          const int64_t m = mm + mi;
+          v[u] = (e < 64 * RP && j < R && m < me) ? uint16_t(load1_bf16<kQbf16>(a.Q, m * a.ldq + j))
+                                                  : uint16_t(0);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 256 * u + t;
+          const int mi = e / RP, j = e - mi * RP;
+          if (e < 64 * RP) sQ[j * 64 + (((mi >> 3) ^ (j & 7)) << 3) + (mi & 7)] = v[u];
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      // A operand: column (16*wave + i16) of P, tokens 32u + 8h .. +8, via two
-      // transposed reads of 4 rows x 4 columns per 16-lane group.
-      u32x4_t av;
-      {
-        const int q = i16 & 3, tq = i16 >> 2;
-        const int rr = 32 * u + 8 * h + tq;
-        lds_char *base = (lds_char *)(sP);
-        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(base + (rr * kPPitch + 16 * wave + 4 * q) * 2));
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(base + ((rr + 4) * kPPitch + 16 * wave + 4 * q) * 2));
-        u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        av = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-      }
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if (s < RT) {
-          const int j = 16 * s + i16;
-          const int ch = 4 * u + h;
-          u32x4_t b = *reinterpret_cast<const u32x4_t *>(sQ + j * 64 + ((ch ^ (j & 7)) * 8));
-          acc[s] = mfma16x16x32(av, b, acc[s]);
+      for (int c4 = 0; c4 < kNCT; ++c4) {
+        // A operand: column cb + i16 of P, tokens 32u + 8h .. +8, via two
+        // transposed reads of 4 rows x 4 columns per 16-lane group.
+        const int cb = wave * (kTN / 4) + 16 * c4;
+        u32x4_t av;
+        {
+          const int q = i16 & 3, tq = i16 >> 2;
+          const int rr = 32 * u + 8 * h + tq;
+          lds_char *base = (lds_char *)(sP);
+          i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4 *)(base + (rr * kPP + cb + 4 * q) * 2));
+          i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4 *)(base + ((rr + 4) * kPP + cb + 4 * q) * 2));
+          u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+          av = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+        }
+#pragma unroll
+        for (int st = 0; st < kMaxRT; ++st) {
+          if (st < RT) {
+            u32x4_t b;
+            if constexpr (kQFastC) {
+              b = lds_col8(sQ, RP, 32 * u, 16 * st);
+            } else {
+              const int j = 16 * st + i16;
+              const int ch = 4 * u + h;
+              b = *reinterpret_cast<const u32x4_t *>(sQ + j * 64 + ((ch ^ (j & 7)) * 8));
+            }
+            acc[c4][st] = mfma16x16x32(av, b, acc[c4][st]);
+          }
         }
       }
     }
   }
   float *out = a.part + int64_t(ks) * K * R;
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s < RT) {
-      const int j = 16 * s + i16;
+  for (int c4 = 0; c4 < kNCT; ++c4) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = c0 + 16 * wave + 4 * h + q;
-        if (col < K && j < R) out[col * R + j] = acc[s][q];
+    for (int st = 0; st < kMaxRT; ++st) {
+      if (st < RT) {
+        const int j = 16 * st + i16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = c0 + wave * (kTN / 4) + 16 * c4 + 4 * h + q;
+          if (col < K && j < R) out[col * R + j] = acc[c4][st][q];
+        }
       }
     }
   }
@@ -333,8 +457,18 @@ struct ReduceArgs {
 __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int64_t nwg) {
   const int64_t n = a.rows * a.R;
   for (int64_t i = wg * 256 + threadIdx.x; i < n; i += nwg * 256) {
+    // partials are loaded 8 at a time (independent loads in flight) and
+    // summed in k order
     float s = 0.0f;
-    for (int64_t k = 0; k < a.ks; ++k) s += a.part[k * n + i];
+    int64_t k = 0;
+    for (; k + 8 <= a.ks; k += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.part[(k + u) * n + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < a.ks; ++k) s += a.part[k * n + i];
     const int64_t rr = i / a.R, j = i - rr * a.R;
     if (a.out) a.out[a.transpose_out ? j * a.rows + rr : i] = s;
     if (a.out_bf16) a.out_bf16[rr * a.ld_bf16 + j] = f32_to_bf16_bits(s);
@@ -352,13 +486,13 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
 
 // XA partials (rowdot with Q = A [in x r]) on workgroups [0, n_row), block
 // scales on [n_row, grid).  Either role may be empty.
-template <bool kXbf16, bool kAbf16>
+template <bool kXbf16, bool kAbf16, bool kWide, int kQMode>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(RowdotArgs ra, int64_t n_row,
                                                        ScalesArgs sa) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t wg = blockIdx.x;
   if (wg < n_row)
-    rowdot_role<kXbf16, false, kAbf16>(ra, wg, smem);
+    rowdot_role<kXbf16, kQMode, kAbf16, kWide>(ra, wg, smem);
   else
     scales_role(sa, wg - n_row, int64_t(gridDim.x) - n_row);
 }
@@ -366,24 +500,24 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(RowdotArgs ra, int64_t n_
 // One pass over dY: G partials (rowdot with Qt = B [r x out]) on [0, n_row),
 // dB partials (coldot with Q = XA fp32 [M x r]) on [n_row, n_row + n_col),
 // block scales on the rest.
-template <bool kDYbf16, bool kBbf16>
+template <bool kDYbf16, bool kBbf16, bool kWide, bool kQFastC>
 __global__ __launch_bounds__(256) void bwd_dy_kernel(RowdotArgs ra, int64_t n_row, ColdotArgs ca,
                                                      int64_t n_col, ScalesArgs sa) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t wg = blockIdx.x;
   if (wg < n_row)
-    rowdot_role<kDYbf16, true, kBbf16>(ra, wg, smem);
+    rowdot_role<kDYbf16, kQRows, kBbf16, kWide>(ra, wg, smem);
   else if (wg < n_row + n_col)
-    coldot_role<kDYbf16, false>(ca, wg - n_row, smem);
+    coldot_role<kDYbf16, false, kWide, kQFastC>(ca, wg - n_row, smem);
   else
     scales_role(sa, wg - n_row - n_col, int64_t(gridDim.x) - n_row - n_col);
 }
 
-// One pass over X: dA partials (coldot with Q = G16 bf16 [M x rp]).
-template <bool kXbf16>
+// One pass over X: dA partials (coldot with Q = G16 bf16 [M x rp], zero-padded).
+template <bool kXbf16, bool kWide>
 __global__ __launch_bounds__(256) void bwd_x_kernel(ColdotArgs ca) {
   extern __shared__ __align__(16) unsigned char smem[];
-  coldot_role<kXbf16, true>(ca, blockIdx.x, smem);
+  coldot_role<kXbf16, true, kWide, true>(ca, blockIdx.x, smem);
 }
 
 // Two independent reductions in one launch: a on [0, n_a), b on the rest.
@@ -402,18 +536,19 @@ int64_t grid_for(int64_t n) {
   return g;
 }
 
-int64_t rowdot_chunk(int64_t M, int64_t K) {
+int64_t rowdot_chunk(int64_t M, int64_t K, int64_t R) {
+  const int64_t TK = skinny_wide(int(R)) ? 256 : 64;
   const int64_t rt = (M + kRowdotRows - 1) / kRowdotRows;
-  const int64_t slices = K / kSliceK;
+  const int64_t slices = (K + TK - 1) / TK;
   int64_t ks = (512 + rt - 1) / rt;
   if (ks < 1) ks = 1;
   if (ks > slices) ks = slices;
   const int64_t per = (slices + ks - 1) / ks;   // slices per split
-  return per * kSliceK;
+  return per * TK;
 }
 
-int64_t coldot_chunk(int64_t M, int64_t K) {
-  const int64_t ct = (K + kColdotCols - 1) / kColdotCols;
+int64_t coldot_chunk(int64_t M, int64_t K, int64_t R) {
+  const int64_t ct = (K + coldot_tn(int(R)) - 1) / coldot_tn(int(R));
   const int64_t mt = (M + 63) / 64;
   int64_t ks = (512 + ct - 1) / ct;
   if (ks < 1) ks = 1;
@@ -426,7 +561,7 @@ RowdotArgs rowdot_args(const void *P, const void *Q, int64_t M, int64_t K, int64
                        float *part, int64_t &nwg) {
   RowdotArgs a;
   a.P = P; a.Q = Q; a.M = M; a.K = K; a.R = int(R);
-  a.kchunk = rowdot_chunk(M, K);
+  a.kchunk = rowdot_chunk(M, K, R);
   a.mt = (M + kRowdotRows - 1) / kRowdotRows;
   a.part = part;
   nwg = (M == 0 || R == 0) ? 0 : a.mt * ((K + a.kchunk - 1) / a.kchunk);
@@ -437,29 +572,29 @@ ColdotArgs coldot_args(const void *P, const void *Q, int64_t ldq, int64_t M, int
                        float *part, int64_t &nwg) {
   ColdotArgs a;
   a.P = P; a.Q = Q; a.ldq = ldq; a.M = M; a.K = K; a.R = int(R);
-  a.mchunk = coldot_chunk(M, K);
-  a.ct = (K + kColdotCols - 1) / kColdotCols;
+  a.mchunk = coldot_chunk(M, K, R);
+  a.ct = (K + coldot_tn(int(R)) - 1) / coldot_tn(int(R));
   a.part = part;
   nwg = (M == 0 || R == 0) ? 0 : a.ct * ((M + a.mchunk - 1) / a.mchunk);
   return a;
 }
 
-size_t rowdot_lds(int64_t R) { return size_t((R + 15) / 16 * 16) * 64 * 2; }
-size_t coldot_lds(int64_t R) { return size_t(64) * kPPitch * 2 + rowdot_lds(R); }
+size_t rowdot_lds(int64_t R) { return size_t(rank_pad16(int(R))) * (skinny_wide(int(R)) ? 256 : 64) * 2; }
+size_t coldot_lds(int64_t R) {
+  return size_t(64) * coldot_pitch(coldot_tn(int(R))) * 2 + size_t(rank_pad16(int(R))) * 64 * 2;
+}
 
 }  // namespace
 
 int64_t rowdot_splits(int64_t M, int64_t K, int64_t R) {
-  (void)R;
   if (M == 0) return 0;
-  const int64_t kc = rowdot_chunk(M, K);
+  const int64_t kc = rowdot_chunk(M, K, R);
   return (K + kc - 1) / kc;
 }
 
 int64_t coldot_splits(int64_t M, int64_t K, int64_t R) {
-  (void)R;
   if (M == 0) return 0;
-  const int64_t mc = coldot_chunk(M, K);
+  const int64_t mc = coldot_chunk(M, K, R);
   return (M + mc - 1) / mc;
 }
 
@@ -483,17 +618,27 @@ hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf1
   int64_t n_row = 0;
   const RowdotArgs ra = rowdot_args(X, A, M, in, r, xa_part, n_row);
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
-  const int64_t n_sc = cs ? grid_for(in * (out / 64)) : 0;
+  const int64_t n_sc = cs ? scales_workgroups(in, out / 64) : 0;
   if (n_row + n_sc == 0) return hipSuccess;
   const size_t lds = n_row ? rowdot_lds(r) : 0;
   const dim3 grid = dim3(unsigned(n_row + n_sc));
-#define QLORA_PREP(XB, AB) \
-  hipLaunchKernelGGL((fwd_prep_kernel<XB, AB>), grid, dim3(256), lds, s, ra, n_row, sa)
+#define QLORA_PREP2(XB, AB, W)                                                              \
+  do {                                                                                      \
+    if (r % 8 == 0)                                                                         \
+      hipLaunchKernelGGL((fwd_prep_kernel<XB, AB, W, kQFast>), grid, dim3(256), lds, s, ra, n_row, sa); \
+    else                                                                                    \
+      hipLaunchKernelGGL((fwd_prep_kernel<XB, AB, W, kQGeneric>), grid, dim3(256), lds, s, ra, n_row, sa); \
+  } while (0)
+#define QLORA_PREP(XB, AB)                                                                  \
+  do {                                                                                      \
+    if (skinny_wide(int(r))) QLORA_PREP2(XB, AB, true); else QLORA_PREP2(XB, AB, false);    \
+  } while (0)
   if (x_bf16) {
     if (a_bf16) QLORA_PREP(true, true); else QLORA_PREP(true, false);
   } else {
     if (a_bf16) QLORA_PREP(false, true); else QLORA_PREP(false, false);
   }
+#undef QLORA_PREP2
 #undef QLORA_PREP
   return hipGetLastError();
 }
@@ -506,17 +651,27 @@ hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf1
   const RowdotArgs ra = rowdot_args(dY, B, M, out, r, g_part, n_row);
   const ColdotArgs ca = coldot_args(dY, XA, r, M, out, r, db_part, n_col);
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
-  const int64_t n_sc = cs ? grid_for(in * (out / 64)) : 0;
+  const int64_t n_sc = cs ? scales_workgroups(in, out / 64) : 0;
   if (n_row + n_col + n_sc == 0) return hipSuccess;
-  const size_t lds = (n_row + n_col) ? coldot_lds(r) : 0;
+  const size_t lds = (n_row + n_col) ? (coldot_lds(r) > rowdot_lds(r) ? coldot_lds(r) : rowdot_lds(r)) : 0;
   const dim3 grid = dim3(unsigned(n_row + n_col + n_sc));
-#define QLORA_DY(DB, BB) \
-  hipLaunchKernelGGL((bwd_dy_kernel<DB, BB>), grid, dim3(256), lds, s, ra, n_row, ca, n_col, sa)
+#define QLORA_DY2(DB, BB, W)                                                                \
+  do {                                                                                      \
+    if (r % 8 == 0)                                                                         \
+      hipLaunchKernelGGL((bwd_dy_kernel<DB, BB, W, true>), grid, dim3(256), lds, s, ra, n_row, ca, n_col, sa); \
+    else                                                                                    \
+      hipLaunchKernelGGL((bwd_dy_kernel<DB, BB, W, false>), grid, dim3(256), lds, s, ra, n_row, ca, n_col, sa); \
+  } while (0)
+#define QLORA_DY(DB, BB)                                                                    \
+  do {                                                                                      \
+    if (skinny_wide(int(r))) QLORA_DY2(DB, BB, true); else QLORA_DY2(DB, BB, false);        \
+  } while (0)
   if (dy_bf16) {
     if (b_bf16) QLORA_DY(true, true); else QLORA_DY(true, false);
   } else {
     if (b_bf16) QLORA_DY(false, true); else QLORA_DY(false, false);
   }
+#undef QLORA_DY2
 #undef QLORA_DY
   return hipGetLastError();
 }
@@ -527,10 +682,14 @@ hipError_t launch_bwd_x(const void *X, bool x_bf16, const uint16_t *G16, int64_t
   const ColdotArgs ca = coldot_args(X, G16, ldg, M, in, r, da_part, n_col);
   if (n_col == 0) return hipSuccess;
   const dim3 grid = dim3(unsigned(n_col));
-  if (x_bf16)
-    hipLaunchKernelGGL((bwd_x_kernel<true>), grid, dim3(256), coldot_lds(r), s, ca);
-  else
-    hipLaunchKernelGGL((bwd_x_kernel<false>), grid, dim3(256), coldot_lds(r), s, ca);
+  const bool wide = skinny_wide(int(r));
+  if (x_bf16) {
+    if (wide) hipLaunchKernelGGL((bwd_x_kernel<true, true>), grid, dim3(256), coldot_lds(r), s, ca);
+    else hipLaunchKernelGGL((bwd_x_kernel<true, false>), grid, dim3(256), coldot_lds(r), s, ca);
+  } else {
+    if (wide) hipLaunchKernelGGL((bwd_x_kernel<false, true>), grid, dim3(256), coldot_lds(r), s, ca);
+    else hipLaunchKernelGGL((bwd_x_kernel<false, false>), grid, dim3(256), coldot_lds(r), s, ca);
+  }
   return hipGetLastError();
 }
 

@@ -58,6 +58,10 @@ def test_small_config_fp32(b_zero):
     (17, 384, 256, 40, "f32", "bf16"),      # r not a multiple of 16
     (1, 256, 384, 16, "bf16", "bf16"),      # single token
     (260, 320, 192, 0, "bf16", "bf16"),     # rank 0: plain NF4 linear
+    (130, 320, 448, 12, "bf16", "f32"),     # r % 8 != 0: element-wise staging of A, XA
+    (70, 256, 320, 5, "f32", "bf16"),       # r % 8 != 0, fp32 activations
+    (96, 576, 320, 80, "bf16", "bf16"),     # r > 64: narrow skinny tiles
+    (65, 384, 256, 100, "bf16", "f32"),     # r > 64 and r % 8 != 0
 ])
 def test_ragged_full(M, n_in, n_out, r, act, adt):
     L = Layer(9, M, n_in, n_out, r, act=act, adt=adt)
