@@ -163,6 +163,52 @@ __device__ __forceinline__ u32x4_t expand8u(uint32_t d, float s, const ExpandCon
   return r;
 }
 
+// Per-scale level table for a uniform scale s: the 8 magnitudes
+// bf16(|L|_m * s) (fp32 product, one rounding) as two v_perm byte planes --
+// lo[w] holds the low bytes of m = 4w..4w+3, hi[w] the high bytes.  A weight
+// with code c is then +-table[m] (sign-symmetric levels), bit-identical to
+// bf16(L[c] * s).
+struct ScaledTable {
+  uint32_t lo[2], hi[2];
+};
+
+__device__ __forceinline__ ScaledTable scaled_table(float s, const ExpandConsts &t) {
+  uint32_t p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) p[q] = pack_bf16x2(t.mag[2 * q] * s, t.mag[2 * q + 1] * s);
+  ScaledTable r;
+  r.lo[0] = perm_b32(p[1], p[0], 0x06040200u);
+  r.lo[1] = perm_b32(p[3], p[2], 0x06040200u);
+  r.hi[0] = perm_b32(p[1], p[0], 0x07050301u);
+  r.hi[1] = perm_b32(p[3], p[2], 0x07050301u);
+  return r;
+}
+
+// 8 codes (nibble t of d = k slot t) -> the bf16x8 MFMA operand (k pairs).
+__device__ __forceinline__ u32x4_t expand8_table(uint32_t d, const ScaledTable &T) {
+  // magnitude index m = c - 8 (c >= 8) or 7 - c (c < 8), per byte; nt has
+  // 0x08 in the bytes of negative levels
+  const uint32_t nl = ~d & 0x08080808u;                     // even k slots
+  const uint32_t ml = (d ^ (nl - (nl >> 3))) & 0x07070707u;
+  const uint32_t dh = d >> 4;                               // odd k slots
+  const uint32_t nh = ~dh & 0x08080808u;
+  const uint32_t mh = (dh ^ (nh - (nh >> 3))) & 0x07070707u;
+  const uint32_t LL = perm_b32(T.lo[1], T.lo[0], ml);       // low bytes, k = 0,2,4,6
+  const uint32_t HL = perm_b32(T.hi[1], T.hi[0], ml) | (nl << 4);
+  const uint32_t LH = perm_b32(T.lo[1], T.lo[0], mh);       // k = 1,3,5,7
+  const uint32_t HH = perm_b32(T.hi[1], T.hi[0], mh) | (nh << 4);
+  const uint32_t A0 = perm_b32(HL, LL, 0x05010400u);        // bf16 k0, k2
+  const uint32_t B0 = perm_b32(HH, LH, 0x05010400u);        // bf16 k1, k3
+  const uint32_t A1 = perm_b32(HL, LL, 0x07030602u);        // k4, k6
+  const uint32_t B1 = perm_b32(HH, LH, 0x07030602u);        // k5, k7
+  u32x4_t r;
+  r[0] = perm_b32(B0, A0, 0x05040100u);
+  r[1] = perm_b32(B0, A0, 0x07060302u);
+  r[2] = perm_b32(B1, A1, 0x05040100u);
+  r[3] = perm_b32(B1, A1, 0x07060302u);
+  return r;
+}
+
 // Map the linear workgroup id to a (m-tile, n-tile).  Workgroups are dealt
 // to the 8 XCDs round-robin; T = (id % 8) * (n / 8) + id / 8 gives each XCD a
 // contiguous run of tiles, which share m-tiles (their activation rows stay in
@@ -332,13 +378,20 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const u32x4_t *>(st + xo[j] + 4096 * i);
   };
+  // dX: one scale per column block and tile, so the expansion goes through a
+  // per-scale table built at substep 0 and reused at substep 1.
+  ScaledTable tbl[2];
   auto make_b = [&](const uint32_t (&nib)[2][2], const float (&sc)[kNS], int j, u32x4_t (&bb)[2]) {
     if constexpr (kFwd) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) bb[b] = expand8<kExact>(nib[b][j], sc + 8 * j, tb);
     } else {
+      if (j == 0) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bb[b] = expand8u<kExact>(nib[b][j], sc[b], tb);
+        for (int b = 0; b < 2; ++b) tbl[b] = scaled_table(sc[b], tb);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bb[b] = expand8_table(nib[b][j], tbl[b]);
     }
   };
   auto mfmas = [&](const u32x4_t (&a)[8], const u32x4_t (&bb)[2]) {

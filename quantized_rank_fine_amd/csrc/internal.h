@@ -17,6 +17,7 @@ struct QuantConsts {
 // plane[p][0] holds byte p of |L|_0..|L|_3, plane[p][1] of |L|_4..|L|_7.
 struct ExpandConsts {
   uint32_t plane[4][2];
+  float mag[8];          // |L|_m = L[8+m] as fp32 (for per-scale tables)
 };
 struct ExpandConsts16 {
   uint32_t plane[2][2];  // bytes 2 and 3 of the bf16-rounded magnitudes

@@ -110,6 +110,7 @@ Tables build_tables() {
       t.expand.plane[p][w] = v;
     }
   }
+  for (int m = 0; m < 8; ++m) t.expand.mag[m] = t.L[8 + m];
   // Same for the bf16-rounded magnitudes (bytes 2 and 3 of the fp32 pattern).
   for (int p = 0; p < 2; ++p) {
     for (int w = 0; w < 2; ++w) {
