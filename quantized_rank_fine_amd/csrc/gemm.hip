@@ -55,7 +55,12 @@ constexpr int kXBytes = BM * BK * 2;     // 32 KiB activation tile
 constexpr int kCBytes = 4096;            // code tile
 constexpr int kSBytes = 1024;            // scales (512 B used)
 constexpr int kStageBytes = kXBytes + kCBytes + kSBytes;
-constexpr int kLdsBytes = kStages * kStageBytes;   // 148 KiB
+constexpr int kRingBytes = kStages * kStageBytes;  // 148 KiB
+// Forward: per-wavefront expansion scratch after the ring, 16 k rows x 64
+// columns of bf16 with a 160-B row pitch (conflict-free transposed reads).
+constexpr int kXPitch = 80;                          // elements
+constexpr int kScratchBytes = 16 * kXPitch * 2;      // 2560 B per wavefront
+constexpr int kLdsBytes = kRingBytes + 4 * kScratchBytes;   // 158 KiB
 constexpr uint32_t kBufFlags = 0x00020000u;
 constexpr int kLoadsPerTile = 10;        // per wavefront: 8 X + 1 code + 1 scale
 
@@ -209,6 +214,36 @@ __device__ __forceinline__ u32x4_t expand8_table(uint32_t d, const ScaledTable &
   return r;
 }
 
+// Transposed read of a row-major bf16 LDS tile T (pitch kXPitch): lane l
+// receives column cb + (l & 31), rows 8 (l >> 5) .. +7 -- one lane of a
+// v_mfma_f32_32x32x16 B operand -- from two ds_read_b64_tr_b16 (each: 16
+// lanes x 4 rows -> 4 columns).
+__device__ __forceinline__ u32x4_t lds_col8_32(const char *T, int cb) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
+  const int q = i16 & 3, tq = i16 >> 2;
+  const int rr = 8 * (g >> 1) + tq;
+  const int col = cb + 16 * (g & 1) + 4 * q;
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  lds_char *base = (lds_char *)(T);
+  i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (rr * kXPitch + col) * 2));
+  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + ((rr + 4) * kXPitch + col) * 2));
+  const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Scheduling hint for one half-step: 16 MFMAs, each followed by one LDS read
+// (for the first kNDS) and kNV VALU instructions.
+template <int kNDS, int kNV>
+__device__ __forceinline__ void sched_pattern() {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    if (q < kNDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, kNV, 0);                  // VALU
+  }
+}
+
 // Map the linear workgroup id to a (m-tile, n-tile).  Workgroups are dealt
 // to the 8 XCDs round-robin; T = (id % 8) * (n / 8) + id / 8 gives each XCD a
 // contiguous run of tiles, which share m-tiles (their activation rows stay in
@@ -223,16 +258,6 @@ __device__ __forceinline__ void tile_of(int nt_count, int &mt, int &nt) {
 // LDS address (bytes) of the 16-B chunk `c` of activation row `row`.
 __device__ __forceinline__ uint32_t xoff(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-template <bool kOutBf16>
-__device__ __forceinline__ void store_out(void *Yv, int64_t M, int64_t N, int64_t m, int64_t n,
-                                          float v) {
-  if (m < M && n < N) {
-    if constexpr (kOutBf16)
-      static_cast<uint16_t *>(Yv)[m * N + n] = bf16_bits(v);
-    else
-      static_cast<float *>(Yv)[m * N + n] = v;
-  }
-}
 
 // ------------------------------------------------------- shared main loop
 //
@@ -330,13 +355,21 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   uint32_t xo[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) xo[j] = xoff(l32, 4 * h2 + 2 * kh + j);   // + 32 i rows = 4096 i B
-  uint32_t co[2];                                  // code read offset per column block b
+  uint32_t co[2];                   // code read offset per column block b (dX) or substep j (fwd)
+  // Forward expansion layout: lane (er = lane >> 2, seg = lane & 3) expands
+  // 16 consecutive columns 16 seg .. of the wavefront's 64 for k row
+  // kr(j) = 32 (er >> 3) + 8 (2 kh + j) + (er & 7) of substep j; scratch row
+  // er, so that scratch rows 8 h2 .. 8 h2 + 7 are the k slots of lane half h2.
+  const int er = lane >> 2, seg = lane & 3;
+  uint32_t sco = 0;                 // fwd: scale offset (floats) of k row kr(0)
   if constexpr (kFwd) {
-    const int c16 = (lane >> 4) & 1, t16 = lane & 15;
-    const int r = 32 * h2 + 16 * kh + t16;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-      co[b] = uint32_t(((r >> 3) * 32 + (2 * ch + b) * 8 + (r & 7)) * 16 + 8 * c16);
+    for (int j = 0; j < 2; ++j) {
+      const int kr = 32 * (er >> 3) + 8 * (2 * kh + j) + (er & 7);
+      const int piece = 2 * ch + (seg >> 1);
+      co[j] = uint32_t(((kr >> 3) * 32 + piece * 8 + (kr & 7)) * 16 + 8 * (seg & 1));
+    }
+    sco = uint32_t(ch * 64 + 32 * (er >> 3) + 16 * kh + (er & 7));
   } else {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -345,30 +378,28 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
     }
   }
   // scale read offset (bytes into the scale area of a stage)
-  const uint32_t so = kFwd ? uint32_t((ch * 64 + 32 * h2 + 16 * kh) * 4) : uint32_t((ch * 64 + l32) * 4);
+  const uint32_t so = kFwd ? sco * 4u : uint32_t((ch * 64 + l32) * 4);
+  char *scr = smem + kRingBytes + wave * kScratchBytes;              // fwd expansion scratch
+  const uint32_t swo = uint32_t((er * kXPitch + 16 * seg) * 2);      // this lane's scratch bytes
 
   // Per tile and lane: nib[b][j] = 8 codes (k slots 32 h2 + 8 (2 kh + j) +
   // 0..7) of column block b; sc = the scales they need (forward: one per k
   // slot, 16 for both substeps; dX: one per column block).
-  constexpr int kNS = kFwd ? 16 : 2;
+  // Per tile and lane: dX -- nib[b][j] = 8 codes (k slots 32 h2 + 8 (2 kh +
+  // j) + 0..7) of column block b and sc[b] its scale; forward -- nib[j][w] =
+  // codes of columns 16 seg + 8 w .. +7 of k row kr(j) and sc[j] its scale.
+  constexpr int kNS = 2;
   auto read_tile = [&](const char *st, uint32_t (&nib)[2][2], float (&sc)[kNS]) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      i32x2_t v;
-      if constexpr (kFwd)
-        v = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(lds_char *)(st + kXBytes + co[b]));
-      else
-        v = *reinterpret_cast<const i32x2_t *>(st + kXBytes + co[b]);
+      const i32x2_t v = *reinterpret_cast<const i32x2_t *>(st + kXBytes + co[b]);
       nib[b][0] = uint32_t(v[0]);
       nib[b][1] = uint32_t(v[1]);
     }
     const char *sp = st + kXBytes + kCBytes + so;
     if constexpr (kFwd) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sp + 16 * q);
-        sc[4 * q] = v[0]; sc[4 * q + 1] = v[1]; sc[4 * q + 2] = v[2]; sc[4 * q + 3] = v[3];
-      }
+      sc[0] = *reinterpret_cast<const float *>(sp);
+      sc[1] = *reinterpret_cast<const float *>(sp + 32);     // k row kr(1) = kr(0) + 8
     } else {
       sc[0] = *reinterpret_cast<const float *>(sp);
       sc[1] = *reinterpret_cast<const float *>(sp + 128);
@@ -381,18 +412,28 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   // dX: one scale per column block and tile, so the expansion goes through a
   // per-scale table built at substep 0 and reused at substep 1.
   ScaledTable tbl[2];
+  // dX: the expansion of substep j of a tile, in registers (per-scale
+  // tables built at substep 0 and reused at substep 1).
   auto make_b = [&](const uint32_t (&nib)[2][2], const float (&sc)[kNS], int j, u32x4_t (&bb)[2]) {
-    if constexpr (kFwd) {
+    if (j == 0) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bb[b] = expand8<kExact>(nib[b][j], sc + 8 * j, tb);
-    } else {
-      if (j == 0) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) tbl[b] = scaled_table(sc[b], tb);
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b) bb[b] = expand8_table(nib[b][j], tbl[b]);
+      for (int b = 0; b < 2; ++b) tbl[b] = scaled_table(sc[b], tb);
     }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bb[b] = expand8_table(nib[b][j], tbl[b]);
+  };
+  // Forward: this lane's 16 weights of one k row (one scale) of substep j,
+  // expanded into the wavefront's scratch ...
+  auto expand_write = [&](const uint32_t (&nib)[2][2], const float (&sc)[kNS], int j) {
+    const ScaledTable T = scaled_table(sc[j], tb);
+    const u32x4_t w0 = expand8_table(nib[j][0], T), w1 = expand8_table(nib[j][1], T);
+    *reinterpret_cast<u32x4_t *>(scr + swo) = w0;
+    *reinterpret_cast<u32x4_t *>(scr + swo + 16) = w1;
+  };
+  // ... and read back transposed as the two B fragments.
+  auto read_b = [&](u32x4_t (&bb)[2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32(scr, 32 * b);
   };
   auto mfmas = [&](const u32x4_t (&a)[8], const u32x4_t (&bb)[2]) {
 #pragma unroll
@@ -402,7 +443,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   };
 
   // ---- prologue: tiles 0..kStages-1 in flight (clamped to the last tile);
-  // tiles 0 and 1 landed and visible; operands of tile 0 substep 0 ready.
+  // tiles 0 and 1 landed and visible.
   static_assert(kStages >= 4, "the pipeline keeps two tiles visible ahead of the issue");
 #pragma unroll
   for (int p = 0; p < kStages; ++p) issue(p < KT ? p : KT - 1, p);
@@ -411,52 +452,87 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   uint32_t nib[2][2], nibn[2][2];
   float sc[kNS], scn[kNS];
   u32x4_t a0[8], a1[8], b0[2], b1[2];
-  read_tile(smem, nib, sc);
-  read_a(smem, 0, a0);
-  make_b(nib, sc, 0, b0);
 
-  // Invariant at the top of iteration kt: tiles kt and kt+1 are visible;
-  // a0/b0 hold substep 0 of tile kt and nib/sc its codes and scales.  Every
-  // iteration issues one tile group (past the end: a harmless re-load of the
-  // last tile into the stage just freed), so one constant vmcnt wait always
-  // means "tile kt+2 has landed".  Codes and scales are read one half-step
-  // before they are expanded, so no expansion waits on LDS.
-  for (int kt = 0; kt < KT; ++kt) {
-    const char *st = smem + (kt % kStages) * kStageBytes;
-    const char *sn = smem + ((kt + 1) % kStages) * kStageBytes;
-    // substep 0 of tile kt; prepare substep 1 and fetch tile kt+1's codes
-    read_tile(sn, nibn, scn);
-    read_a(st, 1, a1);
-    make_b(nib, sc, 1, b1);
-    mfmas(a0, b0);
+  if constexpr (kFwd) {
+    // Forward pipeline.  The scratch holds one substep at a time: in every
+    // half-step the B fragments of the next half-step are read from it first,
+    // then the substep after that is expanded into it (same wavefront, LDS
+    // in order: the reads see the old contents).  Codes of tile kt+2 are read
+    // in the second half of iteration kt, one half-step before their first
+    // expansion.  Invariant at the top of iteration kt: tiles kt, kt+1
+    // visible; a0/b0 = substep 0 of tile kt; scratch = substep 1 of tile kt;
+    // nib/sc = codes and scales of tile kt+1.
+    read_tile(smem, nib, sc);
+    expand_write(nib, sc, 0);
+    read_b(b0);
+    expand_write(nib, sc, 1);
+    read_tile(smem + kStageBytes, nib, sc);
+    read_a(smem, 0, a0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const char *st = smem + (kt % kStages) * kStageBytes;
+      const char *sn = smem + ((kt + 1) % kStages) * kStageBytes;
+      const char *s2 = smem + ((kt + 2) % kStages) * kStageBytes;
+      // substep 0 of tile kt; prepare substep 1 of kt, expand substep 0 of kt+1
+      read_a(st, 1, a1);
+      read_b(b1);
+      expand_write(nib, sc, 0);
+      mfmas(a0, b0);
+      sched_pattern<10, 4>();
+      // tile kt+2 landed and visible; the stage of tile kt is free
+      wait_vmcnt<(kStages - 3) * kLoadsPerTile>();
+      __syncthreads();
+      issue(kt + kStages < KT ? kt + kStages : KT - 1, kt % kStages);
+      // substep 1 of tile kt; prepare substep 0 of kt+1, expand substep 1 of
+      // kt+1, fetch the codes of kt+2 (past the end: stages never used)
+      read_tile(s2, nibn, scn);
+      read_a(sn, 0, a0);
+      read_b(b0);
+      expand_write(nib, sc, 1);
+      mfmas(a1, b1);
+      sched_pattern<14, 4>();
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-      if (q < (kFwd ? 14 : 12)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);            // VALU
+      for (int b = 0; b < 2; ++b) {
+        nib[b][0] = nibn[b][0];
+        nib[b][1] = nibn[b][1];
+      }
+#pragma unroll
+      for (int q = 0; q < kNS; ++q) sc[q] = scn[q];
     }
-    // tile kt+2 landed and visible; the stage of tile kt is free
-    wait_vmcnt<(kStages - 3) * kLoadsPerTile>();
-    __syncthreads();
-    issue(kt + kStages < KT ? kt + kStages : KT - 1, kt % kStages);
-    // substep 1 of tile kt; prepare substep 0 of tile kt+1 (past the end:
-    // reads of a stage that is never used)
-    read_a(sn, 0, a0);
-    make_b(nibn, scn, 0, b0);
-    mfmas(a1, b1);
+  } else {
+    // dX pipeline.  Invariant at the top of iteration kt: tiles kt and kt+1
+    // are visible; a0/b0 hold substep 0 of tile kt and nib/sc its codes and
+    // scales.  Codes and scales are read one half-step before they are
+    // expanded, so no expansion waits on LDS.
+    read_tile(smem, nib, sc);
+    read_a(smem, 0, a0);
+    make_b(nib, sc, 0, b0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const char *st = smem + (kt % kStages) * kStageBytes;
+      const char *sn = smem + ((kt + 1) % kStages) * kStageBytes;
+      // substep 0 of tile kt; prepare substep 1 and fetch tile kt+1's codes
+      read_tile(sn, nibn, scn);
+      read_a(st, 1, a1);
+      make_b(nib, sc, 1, b1);
+      mfmas(a0, b0);
+      sched_pattern<12, 6>();
+      // tile kt+2 landed and visible; the stage of tile kt is free
+      wait_vmcnt<(kStages - 3) * kLoadsPerTile>();
+      __syncthreads();
+      issue(kt + kStages < KT ? kt + kStages : KT - 1, kt % kStages);
+      // substep 1 of tile kt; prepare substep 0 of tile kt+1 (past the end:
+      // reads of a stage that is never used)
+      read_a(sn, 0, a0);
+      make_b(nibn, scn, 0, b0);
+      mfmas(a1, b1);
+      sched_pattern<8, 6>();
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-      if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);            // VALU
+      for (int b = 0; b < 2; ++b) {
+        nib[b][0] = nibn[b][0];
+        nib[b][1] = nibn[b][1];
+      }
+#pragma unroll
+      for (int q = 0; q < kNS; ++q) sc[q] = scn[q];
     }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      nib[b][0] = nibn[b][0];
-      nib[b][1] = nibn[b][1];
-    }
-#pragma unroll
-    for (int q = 0; q < kNS; ++q) sc[q] = scn[q];
   }
   wait_vmcnt<0>();
 }
@@ -491,11 +567,12 @@ __device__ __forceinline__ u32x4_t load_adapter8(const AdapterRef &q, int64_t n,
 // is added by the k-half-0 wavefronts only, so it enters every output once.
 // The two k halves of a column half are then summed through LDS in four
 // rounds of two row blocks: every wavefront writes its partials of row blocks
-// 2 rnd, 2 rnd + 1 (64 KiB in all), and reads back both halves of column
-// block b = kh, sums them and stores.  No register index depends on kh, so
-// the accumulators stay in their registers and are read straight into the
-// LDS writes.  LDS layout per fragment: 4 chunks of 1 KiB, chunk c = registers
-// 4c..4c+3 of every lane (16 B per lane, contiguous across lanes).
+// 2 rnd, 2 rnd + 1 (64 KiB in all), reads back both halves of column block
+// b = kh, sums them into a row-major staging tile, and after a barrier stores
+// half of the staged rows as whole row segments.  No register index depends
+// on kh, so the accumulators stay in their registers and are read straight
+// into the LDS writes.  LDS layout per fragment: 4 chunks of 1 KiB, chunk c =
+// registers 4c..4c+3 of every lane (16 B per lane, contiguous across lanes).
 template <bool kOutBf16>
 __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
                                          const uint16_t *__restrict__ P16, int ldp,
@@ -526,11 +603,16 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
     }
   }
 
-  const int64_t n = nw + 32 * kh + l32;               // this lane's output column
-  const bool ncol = (nw + 64 <= N);
+  // Output staging after the 64-KiB exchange area: per column half ch, a
+  // 64-row x 64-column tile of the output dtype, so that the stores are whole
+  // 128-B (bf16) or 256-B (fp32) row segments written with 16-B stores.
+  constexpr int kOE = kOutBf16 ? 2 : 4;                       // output element bytes
+  constexpr int kOPitch = kOutBf16 ? 144 : 272;               // staging row pitch (bytes)
+  char *stg = smem + 65536 + ch * 64 * kOPitch;
   char *wr = smem + (ch * 2 + kh) * 16384 + lane * 16;
   const char *rd0 = smem + (ch * 2) * 16384 + kh * 4096 + lane * 16;   // k half 0, block b = kh
   const char *rd1 = rd0 + 16384;                                         // k half 1
+  const bool ncol = nw < N;                                              // N % 64 == 0
 #pragma unroll
   for (int rnd = 0; rnd < 4; ++rnd) {
     __syncthreads();
@@ -546,31 +628,35 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
         *reinterpret_cast<f32x4_t *>(w + 3072) = __builtin_shufflevector(v, v, 12, 13, 14, 15);
       }
     __syncthreads();
+    // sum the two k halves of column block b = kh and stage them row-major
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      float v[16];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(rd0 + ii * 8192 + c * 1024);
         const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(rd1 + ii * 8192 + c * 1024);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * c + e] = x0[e] + x1[e];
-      }
-      const int64_t mr = m0 + 32 * (2 * rnd + ii) + 4 * h2;
-      if (ncol && mr + 28 < M) {
-        const int64_t e0 = mr * N + n;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t e = e0 + int64_t(8 * (r >> 2) + (r & 3)) * N;
+        for (int e = 0; e < 4; ++e) {
+          const int row = 32 * ii + 8 * c + 4 * h2 + e;       // register 4c + e
+          char *d = stg + row * kOPitch + (32 * kh + l32) * kOE;
           if constexpr (kOutBf16)
-            static_cast<uint16_t *>(Y)[e] = bf16_bits(v[r]);
+            *reinterpret_cast<uint16_t *>(d) = bf16_bits(x0[e] + x1[e]);
           else
-            static_cast<float *>(Y)[e] = v[r];
+            *reinterpret_cast<float *>(d) = x0[e] + x1[e];
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) store_out<kOutBf16>(Y, M, N, mr + 8 * (r >> 2) + (r & 3), n, v[r]);
       }
+    }
+    __syncthreads();
+    // wavefront kh stores staged rows 32 kh .. 32 kh + 31 of this 64-row block
+    constexpr int kChunks = 64 * kOE / 16;                    // 16-B chunks per row
+#pragma unroll
+    for (int q = 0; q < 32 * kChunks / 64; ++q) {
+      const int cid = lane + 64 * q;
+      const int row = 32 * kh + cid / kChunks, c = cid % kChunks;
+      const int64_t m = m0 + 64 * rnd + row;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + row * kOPitch + 16 * c);
+      if (ncol && m < M)
+        *reinterpret_cast<u32x4_t *>(static_cast<char *>(Y) + (m * N + nw) * kOE + 16 * c) = v;
     }
   }
 }
