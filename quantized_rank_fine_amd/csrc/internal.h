@@ -9,8 +9,19 @@
 namespace qlora {
 
 // Encoder thresholds, passed by value as a kernel argument.
+// Encoder bucket table: x = w/absmax in [-1, 1] is bucketed by the top 7
+// bits of the fp32 pattern of u = x + 3 past its exponent (u in [2, 4]):
+// bucket i covers x in [-1 + i/32, -1 + (i+1)/32), bucket 64 is x = 1.  Every
+// bucket holds at most one threshold, so code = base + (x >= T) with the
+// bucket's entry (entries 65..127 are never addressed by finite x).
+constexpr int kBuckets = 128;
+struct BucketEntry {
+  float T;              // the threshold inside the bucket, +inf if none
+  uint32_t base;        // number of thresholds below the bucket
+};
 struct QuantConsts {
-  float T[16];          // T[1..15]: code = #{j : x >= T[j]}; T[0] unused
+  BucketEntry bucket[kBuckets];
+  int ok;               // 1 if the bucket scheme is exact for these thresholds
 };
 
 // Byte planes of the 8 level magnitudes |L|_m = L[8+m], m = 0..7.

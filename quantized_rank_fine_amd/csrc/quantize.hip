@@ -7,13 +7,32 @@
 // to 8 bits (here: symmetric int8, one fp32 scale per 256 block scales).
 //
 // One workgroup (4 wavefronts) per double-quantization group of 256 blocks
-// (64 KiB of fp32).  Each lane owns 16 consecutive weights (one quarter of a
-// block), so a wavefront covers 16 blocks = 4 KiB per step and the absmax of
-// a block is a 4-lane reduction.  x = w / c_b is the IEEE fp32 quotient,
-// obtained from the correctly rounded reciprocal y = 1/c_b (one division per
-// lane and block) and two Markstein corrections q <- q + (w - q*c)*y, which
-// return the correctly rounded quotient; the code is then a 4-step binary
-// search over the 15 exact fp32 decision thresholds held in LDS.
+// (64 KiB of fp32); wavefront w owns blocks 64 w .. 64 w + 63.  Load step j
+// (0..7) covers 8 blocks: the 8 lanes of a block each take weights
+// 4k .. 4k+3 and 32+4k .. 32+4k+3 (k = lane % 8), so each of the two load
+// instructions of a step reads 8 whole 128-B lines, and the block absmax is an
+// 8-lane DPP reduction.  All 16 loads are issued before the first is used;
+// the buffer descriptors end at the last block, so a ragged last group loads
+// zeros and drops its stores without a branch.
+//
+// The quotient x = w / c_b is the fp32 rounding of w * y in fp64, where
+// y = 1/c_b is the correctly rounded fp64 reciprocal (one fp64 division per
+// lane and block).  That equals the IEEE fp32 quotient: the fp64 product is
+// within 2^-52 (relative) of w / c_b, while a quotient of two fp32 numbers in
+// the fp32 normal range is never an fp32 rounding midpoint and never within
+// 2^-49 (relative) of one, so both round to the same fp32 value.  (Below the
+// normal range x may differ, but every |x| < 2^-9 gets the same code.)
+//
+// Code lookup: code = #{j : x >= T_j} for the 15 exact fp32 decision
+// thresholds.  The bucket of x is read off u = x + 3 in fp32 (u in [2, 4], so
+// the top mantissa bits of u are a uniform grid of width 1/32 in x); the
+// threshold gap (> 0.078) exceeds the bucket width, so a bucket holds at most
+// one threshold and code = base + (x >= T_bucket), the compare on x itself.
+// Rounding in x + 3 can move x at most 2^-23 up into the next bucket, which
+// is harmless while no threshold lies that close below a bucket boundary (the
+// nearest is 2^-10.7 away; the host checks this when it builds the table).
+// The table {T_bucket, base} is built on the host and copied into LDS by
+// each workgroup.
 #include "device.h"
 
 namespace qlora {
@@ -21,98 +40,95 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBlocksPerGroup = 256;
+constexpr int kSteps = 8;                 // load steps per wavefront, 8 blocks each
+constexpr int32_t kBufFlags = 0x00020000;
 
-__device__ __forceinline__ uint32_t encode_one(float w, float y, float cs, float sc,
-                                               const float *sT) {
-  float x;
-  if (y == 0.0f) {
-    x = 0.0f;                                   // zero block
-  } else {
-    float ws = w * sc;                          // exact power-of-two scaling
-    float q = ws * y;
-    float r = fmaf(-q, cs, ws);
-    q = fmaf(r, y, q);
-    r = fmaf(-q, cs, ws);
-    x = fmaf(r, y, q);
-  }
-  uint32_t k = (x >= sT[8]) ? 8u : 0u;
-  k += (x >= sT[k + 4]) ? 4u : 0u;
-  k += (x >= sT[k + 2]) ? 2u : 0u;
-  k += (x >= sT[k + 1]) ? 1u : 0u;
-  return k;
+__device__ __forceinline__ uint32_t bucket_of(float x) {
+  return (__float_as_uint(x + 3.0f) >> 17) & uint32_t(kBuckets - 1);
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, const BucketEntry *lut) {
+  const BucketEntry e = lut[bucket_of(x)];
+  return e.base + ((x >= e.T) ? 1u : 0u);
+}
+
+// x = w / c as described above; y = 1/c in fp64 (y = 1 for a zero block, x = 0)
+__device__ __forceinline__ uint32_t code4(f32x4_t w, double y, const BucketEntry *lut) {
+  const uint32_t c0 = code_of(float(double(w.x) * y), lut);
+  const uint32_t c1 = code_of(float(double(w.y) * y), lut);
+  const uint32_t c2 = code_of(float(double(w.z) * y), lut);
+  const uint32_t c3 = code_of(float(double(w.w) * y), lut);
+  // element 2i -> low nibble of byte i, 2i+1 -> high nibble
+  return c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
+}
+
+// max over the 8 lanes of a DPP half-row of non-negative fp32 bit patterns
+// (0 is the identity, so each DPP move folds into its max)
+__device__ __forceinline__ uint32_t row8_max(uint32_t m) {
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+  return m;
+}
+
+// max |w| over the 8 weights of a lane (v_max3 with source modifiers; the
+// library's fmaxf would first canonicalize every operand)
+__device__ __forceinline__ float absmax8(f32x4_t a, f32x4_t b) {
+  float m;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\t"
+      "v_max3_f32 %0, %0, |%4|, |%5|\n\t"
+      "v_max3_f32 %0, %0, |%6|, |%7|\n\t"
+      "v_max_f32_e64 %0, %0, |%8|\n\t"
+      "s_nop 1"                     // VALU write -> DPP read of the result
+      : "=&v"(m)
+      : "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w), "v"(b.x), "v"(b.y), "v"(b.z), "v"(b.w));
+  return m;
 }
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const float *__restrict__ W0, uint8_t *__restrict__ codes, int8_t *__restrict__ qscale,
     float *__restrict__ gscale, int64_t nblocks, QuantConsts qc) {
-  __shared__ float sT[16];
+  __shared__ BucketEntry lut[kBuckets];
   __shared__ float sc_blk[kBlocksPerGroup];
   __shared__ float sred[kThreads / 64];
 
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t g = blockIdx.x;
+  const int64_t rem = nblocks - g * kBlocksPerGroup;
+  const int nb = rem < kBlocksPerGroup ? int(rem) : kBlocksPerGroup;   // blocks in this group
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(W0 + g * kBlocksPerGroup * 64), (short)0, nb * 256, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(codes + g * kBlocksPerGroup * 32), (short)0, nb * 32, kBufFlags);
 
-  if (t < 16) sT[t] = qc.T[t];
+  const int k = lane & 7;
+  const int bl0 = wave * 64 + (lane >> 3);      // block (within the group) of step 0
+  const uint32_t vw = uint32_t(bl0 * 256 + 16 * k);
+  const uint32_t vc = uint32_t(bl0 * 32 + 2 * k);
+  BucketEntry own = {0.0f, 0u};
+  if (t < kBuckets) own = qc.bucket[t];
+  __builtin_amdgcn_sched_barrier(0);            // table read ahead of the weight loads
+  f32x4_t v[kSteps][2];
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    v[j][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rW, vw + j * 2048, 0, 0));
+    v[j][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rW, vw + j * 2048 + 128, 0, 0));
+  }
+  if (t < kBuckets) lut[t] = own;
   __syncthreads();
 
-#pragma unroll 1
-  for (int it = 0; it < 4; ++it) {
-    const int bl = wave * 64 + it * 16 + (lane >> 2);     // block within group
-    const int64_t b = g * kBlocksPerGroup + bl;
-    const bool valid = b < nblocks;
-    f32x4_t v[4];
-    if (valid) {
-      const f32x4_t *src = reinterpret_cast<const f32x4_t *>(W0 + b * 64 + (lane & 3) * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m = fmaxf(m, fabsf(v[j].x));
-      m = fmaxf(m, fabsf(v[j].y));
-      m = fmaxf(m, fabsf(v[j].z));
-      m = fmaxf(m, fabsf(v[j].w));
-    }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-
-    // reciprocal of the (power-of-two rescaled) absmax; y = 0 marks c = 0
-    float sc = 1.0f;
-    if (m < 0x1p-100f) sc = 0x1p64f;
-    if (m > 0x1p100f) sc = 0x1p-64f;
-    const float cs = m * sc;
-    const float y = (m == 0.0f) ? 0.0f : 1.0f / cs;
-
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lo |= encode_one(v[j].x, y, cs, sc, sT) << (16 * j + 0);
-      lo |= encode_one(v[j].y, y, cs, sc, sT) << (16 * j + 4);
-      lo |= encode_one(v[j].z, y, cs, sc, sT) << (16 * j + 8);
-      lo |= encode_one(v[j].w, y, cs, sc, sT) << (16 * j + 12);
-    }
-#pragma unroll
-    for (int j = 2; j < 4; ++j) {
-      hi |= encode_one(v[j].x, y, cs, sc, sT) << (16 * (j - 2) + 0);
-      hi |= encode_one(v[j].y, y, cs, sc, sT) << (16 * (j - 2) + 4);
-      hi |= encode_one(v[j].z, y, cs, sc, sT) << (16 * (j - 2) + 8);
-      hi |= encode_one(v[j].w, y, cs, sc, sT) << (16 * (j - 2) + 12);
-    }
-    if (valid) {
-      u32x2_t packed = {lo, hi};
-      *reinterpret_cast<u32x2_t *>(codes + b * 32 + (lane & 3) * 8) = packed;
-    }
-    if ((lane & 3) == 0) sc_blk[bl] = m;                 // 0 for padding blocks
+  for (int j = 0; j < kSteps; ++j) {
+    const f32x4_t a = v[j][0], b = v[j][1];
+    const float m = __uint_as_float(row8_max(__float_as_uint(absmax8(a, b))));
+    sc_blk[bl0 + 8 * j] = m;                    // the 8 lanes of the block agree
+    const double y = 1.0 / double(m == 0.0f ? 1.0f : m);
+    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(code4(a, y, lut)), rC, vc + j * 256, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(code4(b, y, lut)), rC, vc + j * 256 + 16, 0, 0);
   }
   __syncthreads();
 
-  // double quantization of this group's 256 block scales
+  // double quantization of this group's 256 block scales (0 for padding blocks)
   const float c = sc_blk[t];
   float gm = c;
 #pragma unroll
@@ -121,14 +137,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   __syncthreads();
   gm = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
   const float s2 = gm / 127.0f;
-  const int64_t b = g * kBlocksPerGroup + t;
-  if (b < nblocks) {
+  if (t < nb) {
     int q = 0;
     if (s2 != 0.0f) {
       q = (int)rintf(c / s2);
       q = q > 127 ? 127 : (q < -127 ? -127 : q);
     }
-    qscale[b] = (int8_t)q;
+    qscale[g * kBlocksPerGroup + t] = (int8_t)q;
   }
   if (t == 0) gscale[g] = s2;
 }
@@ -139,6 +154,7 @@ hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale, floa
                            int64_t nblocks, hipStream_t s) {
   const int64_t groups = (nblocks + kBlocksPerGroup - 1) / kBlocksPerGroup;
   if (groups == 0) return hipSuccess;
+  if (!tables().quant.ok) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W0, codes,
                      qscale, gscale, nblocks, tables().quant);
   return hipGetLastError();

@@ -122,7 +122,28 @@ Tables build_tables() {
       t.expand16.plane[p][w] = v;
     }
   }
-  for (int i = 0; i < 16; ++i) t.quant.T[i] = t.T[i];
+  // Bucket table of the encoder.  The bucket of x is computed from
+  // u = RN(x + 3), which lies at most 2^-23 above x + 3 and never below the
+  // bucket of x, so it is exact if no threshold lies within 2^-23 below a
+  // bucket boundary; that and "one threshold per bucket" are checked here.
+  t.quant.ok = 1;
+  for (int i = 0; i < kBuckets; ++i) {
+    const double a = -1.0 + i / 32.0, b = (i < 64) ? a + 1.0 / 32.0 : INFINITY;
+    BucketEntry &en = t.quant.bucket[i];
+    en.T = INFINITY;
+    en.base = 0;
+    int inside = 0;
+    for (int j = 1; j < 16; ++j) {
+      const double tj = t.T[j];
+      if (tj < a) ++en.base;
+      else if (tj < b) {
+        en.T = t.T[j];
+        ++inside;
+      }
+      if (i > 0 && tj < a && tj >= a - 0x1p-23) t.quant.ok = 0;
+    }
+    if (inside > 1) t.quant.ok = 0;
+  }
   return t;
 }
 

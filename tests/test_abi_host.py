@@ -163,3 +163,66 @@ def test_algorithmic_work_formulas():
     f = workloads.fwd_flops(2048, 4096, 4096, 16) + workloads.bwd_flops(2048, 4096, 4096, 16)
     assert f == 2 * 2048 * (2 * 4096 * 4096 + 3 * 16 * (4096 + 4096))
     assert workloads.quantize_bytes(4096, 4096) == 75763712
+
+
+def _bucket_lut(T):
+    """The encoder's bucket table, built from its definition: bucket i holds
+    x in [-1 + i/32, -1 + (i+1)/32) (bucket 64: x = 1); base = number of
+    thresholds below the bucket, T = the one threshold inside (+inf if none)."""
+    T = np.asarray(T, np.float64)
+    T = T[np.isfinite(T)]
+    lut = []
+    for i in range(128):
+        a = -1.0 + i / 32.0
+        b = a + 1.0 / 32.0 if i < 64 else np.inf
+        inside = T[(T >= a) & (T < b)]
+        assert inside.size <= 1, (i, inside)
+        lut.append((np.float32(inside[0]) if inside.size else np.float32(np.inf), int(np.sum(T < a))))
+    return lut
+
+
+def test_bucket_lookup_reproduces_oracle_argmin(L):
+    """code = base + (x >= T_bucket), with the bucket read off the fp32 bits of
+    x + 3, equals the oracle's fp32 argmin on the threshold sweep and around
+    every bucket boundary (where x + 3 rounds up into the next bucket)."""
+    T = np.array(q.qlora_thresholds(), np.float32)
+    lut = _bucket_lut(T)
+    edges = []
+    for i in range(65):
+        b = np.array([-1.0 + i / 32.0], np.float32).view(np.int32)[0]
+        nb = np.arange(b - 4000, b + 4001, dtype=np.int64)
+        nb = nb[(nb >= np.int64(np.int32(-0x7FFFFFFF) - 1)) & (nb <= 0x7FFFFFFF)]
+        edges.append(nb.astype(np.int32).view(np.float32))
+        edges.append(-edges[-1])
+    x = np.concatenate([_x_sweep()] + edges)
+    x = x[(x >= -1) & (x <= 1)]
+    key = ((x + np.float32(3.0)).astype(np.float32).view(np.uint32) >> 17) & 127
+    Tb = np.array([e[0] for e in lut], np.float32)[key]
+    base = np.array([e[1] for e in lut], np.int64)[key]
+    mine = base + (x >= Tb)
+    pad = (-x.size) % 63
+    xx = np.concatenate([x, np.zeros(pad, np.float32)])
+    w = np.concatenate([np.ones((xx.size // 63, 1), np.float32), xx.reshape(-1, 63)], axis=1).reshape(-1)
+    codes = oracle.encode(w, onf4.block_absmax(w)).reshape(-1, 64)[:, 1:].reshape(-1)[: x.size]
+    assert np.array_equal(codes, mine)
+
+
+def test_fp64_reciprocal_product_rounds_like_fp32_division():
+    """The encoder forms x = RN32(w * RN64(1/c)) in fp64.  For fp32 w, c this
+    equals the IEEE fp32 quotient w / c: random pairs over many binades, and
+    pairs whose quotient sits next to an fp32 rounding midpoint."""
+    rng = np.random.default_rng(7)
+    n = 1 << 20
+    c = (rng.random(n) * 2.0 ** rng.integers(-60, 60, n)).astype(np.float32)
+    c = c[c > 0]
+    w = (c * (rng.random(c.size) * 2 - 1)).astype(np.float32)
+    # quotients near midpoints: w = RN32(c * mid) for a random fp32 midpoint
+    mid_base = (rng.random(c.size) * 0.999 + 0.001).astype(np.float32)
+    up = np.nextafter(mid_base, np.float32(2.0))
+    mid = (mid_base.astype(np.float64) + up.astype(np.float64)) / 2
+    w2 = (c.astype(np.float64) * mid).astype(np.float32)
+    for ww in (w, w2, -w2):
+        exact = (ww / c).astype(np.float32)
+        y = 1.0 / c.astype(np.float64)
+        mine = (ww.astype(np.float64) * y).astype(np.float32)
+        assert np.array_equal(exact.view(np.uint32), mine.view(np.uint32))
