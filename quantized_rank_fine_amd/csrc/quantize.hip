@@ -42,6 +42,8 @@ constexpr int kThreads = 256;
 constexpr int kBlocksPerGroup = 256;
 constexpr int kSteps = 8;                 // load steps per wavefront, 8 blocks each
 constexpr int32_t kBufFlags = 0x00020000;
+constexpr int kNT = 2;                     // cache policy of the weight loads: non-temporal
+constexpr int64_t kStreamGrid = 1 << 30;  // above this many groups, walk them with a fixed grid
 
 __device__ __forceinline__ uint32_t bucket_of(float x) {
   return (__float_as_uint(x + 3.0f) >> 17) & uint32_t(kBuckets - 1);
@@ -85,50 +87,61 @@ __device__ __forceinline__ float absmax8(f32x4_t a, f32x4_t b) {
   return m;
 }
 
-__global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const float *__restrict__ W0, uint8_t *__restrict__ codes, int8_t *__restrict__ qscale,
-    float *__restrict__ gscale, int64_t nblocks, QuantConsts qc) {
-  __shared__ BucketEntry lut[kBuckets];
-  __shared__ float sc_blk[kBlocksPerGroup];
-  __shared__ float sred[kThreads / 64];
+struct GroupRefs {
+  __amdgpu_buffer_rsrc_t w, c;   // this group's weights and codes, ending at the last block
+  int nb;                        // blocks in this group
+};
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t g = blockIdx.x;
+__device__ __forceinline__ GroupRefs group_refs(const float *W0, uint8_t *codes, int64_t nblocks,
+                                                int64_t g) {
   const int64_t rem = nblocks - g * kBlocksPerGroup;
-  const int nb = rem < kBlocksPerGroup ? int(rem) : kBlocksPerGroup;   // blocks in this group
-  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(W0 + g * kBlocksPerGroup * 64), (short)0, nb * 256, kBufFlags);
-  const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(codes + g * kBlocksPerGroup * 32), (short)0, nb * 32, kBufFlags);
+  GroupRefs r;
+  r.nb = rem < kBlocksPerGroup ? int(rem) : kBlocksPerGroup;
+  r.w = __builtin_amdgcn_make_buffer_rsrc((void *)(W0 + g * kBlocksPerGroup * 64), (short)0,
+                                          r.nb * 256, kBufFlags);
+  r.c = __builtin_amdgcn_make_buffer_rsrc((void *)(codes + g * kBlocksPerGroup * 32), (short)0,
+                                          r.nb * 32, kBufFlags);
+  return r;
+}
 
-  const int k = lane & 7;
-  const int bl0 = wave * 64 + (lane >> 3);      // block (within the group) of step 0
-  const uint32_t vw = uint32_t(bl0 * 256 + 16 * k);
-  const uint32_t vc = uint32_t(bl0 * 32 + 2 * k);
-  BucketEntry own = {0.0f, 0u};
-  if (t < kBuckets) own = qc.bucket[t];
-  __builtin_amdgcn_sched_barrier(0);            // table read ahead of the weight loads
-  f32x4_t v[kSteps][2];
+__device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t rW, uint32_t vw,
+                                           f32x4_t (&v)[kSteps][2]) {
 #pragma unroll
   for (int j = 0; j < kSteps; ++j) {
-    v[j][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rW, vw + j * 2048, 0, 0));
-    v[j][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rW, vw + j * 2048 + 128, 0, 0));
+    v[j][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rW, vw + j * 2048, 0, kNT));
+    v[j][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rW, vw + j * 2048 + 128, 0, kNT));
   }
-  if (t < kBuckets) lut[t] = own;
-  __syncthreads();
+}
 
+// codes of this wavefront's 64 blocks: block absmax to sc_blk, the 16-bit
+// code groups to the wavefront's 2-KiB staging area, which then leaves in two
+// 1-KiB contiguous stores
+__device__ __forceinline__ void encode_group(const f32x4_t (&v)[kSteps][2], const BucketEntry *lut,
+                                             float *sc_blk, uint16_t *stage, int bl0,
+                                             __amdgpu_buffer_rsrc_t rC) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, k = lane & 7;
+  uint16_t *st = stage + (lane >> 3) * 16 + k;   // block bl0 - 64 wave, halfword k
 #pragma unroll
   for (int j = 0; j < kSteps; ++j) {
     const f32x4_t a = v[j][0], b = v[j][1];
     const float m = __uint_as_float(row8_max(__float_as_uint(absmax8(a, b))));
     sc_blk[bl0 + 8 * j] = m;                    // the 8 lanes of the block agree
     const double y = 1.0 / double(m == 0.0f ? 1.0f : m);
-    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(code4(a, y, lut)), rC, vc + j * 256, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(code4(b, y, lut)), rC, vc + j * 256 + 16, 0, 0);
+    st[j * 128] = uint16_t(code4(a, y, lut));
+    st[j * 128 + 8] = uint16_t(code4(b, y, lut));
   }
-  __syncthreads();
+  // LDS operations of one wavefront complete in order: the reads see all writes
+  const u32x4_t *s4 = reinterpret_cast<const u32x4_t *>(stage);
+  __builtin_amdgcn_raw_buffer_store_b128(s4[lane], rC, wave * 2048 + lane * 16, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(s4[64 + lane], rC, wave * 2048 + 1024 + lane * 16, 0, 0);
+}
 
-  // double quantization of this group's 256 block scales (0 for padding blocks)
+// double quantization of group g's 256 block scales (0 for padding blocks);
+// sc_blk must be complete (barrier before), and is free again on return
+__device__ __forceinline__ void double_quantize(const float *sc_blk, float *sred, int nb, int64_t g,
+                                                int8_t *__restrict__ qscale,
+                                                float *__restrict__ gscale) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float c = sc_blk[t];
   float gm = c;
 #pragma unroll
@@ -146,6 +159,56 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     qscale[g * kBlocksPerGroup + t] = (int8_t)q;
   }
   if (t == 0) gscale[g] = s2;
+  __syncthreads();
+}
+
+// kStream: the workgroup walks groups blockIdx.x, + gridDim.x, ... and loads
+// the next group while it encodes the current one.
+template <bool kStream>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const float *__restrict__ W0, uint8_t *__restrict__ codes, int8_t *__restrict__ qscale,
+    float *__restrict__ gscale, int64_t nblocks, int64_t ngroups, QuantConsts qc) {
+  __shared__ BucketEntry lut[kBuckets];
+  __shared__ float sc_blk[kBlocksPerGroup];
+  __shared__ float sred[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kThreads / 64][1024];   // 2 KiB per wavefront
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int k = lane & 7;
+  const int bl0 = wave * 64 + (lane >> 3);      // block (within the group) of step 0
+  const uint32_t vw = uint32_t(bl0 * 256 + 16 * k);
+
+  int64_t g = blockIdx.x;
+  GroupRefs cur = group_refs(W0, codes, nblocks, g);
+  BucketEntry own = {0.0f, 0u};
+  if (t < kBuckets) own = qc.bucket[t];
+  __builtin_amdgcn_sched_barrier(0);            // table read ahead of the weight loads
+  f32x4_t v[kSteps][2];
+  load_group(cur.w, vw, v);
+  if (t < kBuckets) lut[t] = own;
+  __syncthreads();
+
+  for (;;) {
+    const int64_t gn = g + gridDim.x;
+    const bool more = kStream && gn < ngroups;
+    GroupRefs nxt = cur;
+    f32x4_t vn[kSteps][2];
+    if (more) {
+      nxt = group_refs(W0, codes, nblocks, gn);
+      load_group(nxt.w, vw, vn);
+    }
+    encode_group(v, lut, sc_blk, stage[wave], bl0, cur.c);
+    __syncthreads();
+    double_quantize(sc_blk, sred, cur.nb, g, qscale, gscale);
+    if (!more) break;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      v[j][0] = vn[j][0];
+      v[j][1] = vn[j][1];
+    }
+    cur = nxt;
+    g = gn;
+  }
 }
 
 }  // namespace
@@ -155,8 +218,13 @@ hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale, floa
   const int64_t groups = (nblocks + kBlocksPerGroup - 1) / kBlocksPerGroup;
   if (groups == 0) return hipSuccess;
   if (!tables().quant.ok) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W0, codes,
-                     qscale, gscale, nblocks, tables().quant);
+  if (groups > kStreamGrid) {
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)kStreamGrid), dim3(kThreads), 0, s, W0,
+                       codes, qscale, gscale, nblocks, groups, tables().quant);
+  } else {
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)groups), dim3(kThreads), 0, s, W0,
+                       codes, qscale, gscale, nblocks, groups, tables().quant);
+  }
   return hipGetLastError();
 }
 
