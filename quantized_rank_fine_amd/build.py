@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
 
-SOURCES = ["api.cpp", "tables.cpp", "quantize.hip", "skinny.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "tables.cpp", "quantize.hip", "skinny.hip", "gemm.hip", "smallm.hip"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -39,6 +39,7 @@ DEVICE = [
 DEVICE_EXTRA = {
     "skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "smallm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -71,14 +71,24 @@ struct Layout {
 };
 
 struct FwdPlan {
-  int64_t ks = 0, rp = 0;
-  size_t off_x16 = 0, off_cs = 0, off_part = 0, off_xa16 = 0, total = 0;
+  bool small = false;          // few-token path: split-K partials + fixed-order reduction
+  int64_t ks = 0, rp = 0, kc = 0;
+  size_t off_x16 = 0, off_cs = 0, off_part = 0, off_xa16 = 0, off_p = 0, off_pxa = 0, total = 0;
 };
 
 FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   FwdPlan p;
   if (M == 0) return p;
   Layout L;
+  if (M <= kSmallMaxM && r <= kSmallMaxR) {
+    p.small = true;
+    p.kc = small_fwd_chunk_rows(M, in, out);
+    p.ks = (in + p.kc - 1) / p.kc;
+    p.off_p = L.take(size_t(p.ks) * M * out * 4);
+    if (r > 0) p.off_pxa = L.take(size_t(p.ks) * M * r * 4);
+    p.total = L.o;
+    return p;
+  }
   p.off_x16 = act_bf16 ? 0 : L.take(size_t(M) * in * 2);
   p.off_cs = L.take(size_t(in) * (out / 64) * 4);
   if (r > 0) {
@@ -199,6 +209,16 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
     e = timed(KIND, stream, [&] { return CALL; });         \
     if (e != hipSuccess) return QLORA_ERR_DEVICE;          \
   } while (0)
+  if (p.small) {
+    float *P = at<float>(ws, p.off_p);
+    float *PXA = r > 0 ? at<float>(ws, p.off_pxa) : nullptr;
+    QLORA_RUN(QLORA_KERNEL_FWD_SMALLM,
+              launch_fwd_small_partial(wq->codes, wq->qscale, wq->gscale, in, out, X, xb, M, A,
+                                       ab, r, p.kc, P, PXA, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fwd_small_reduce(P, PXA, p.ks, M, out, r, B, ab, XA,
+                                                           Y, xb, stream));
+    return QLORA_OK;
+  }
   const uint16_t *X16 = static_cast<const uint16_t *>(X);
   if (!xb) {
     uint16_t *x16 = at<uint16_t>(ws, p.off_x16);

@@ -108,6 +108,23 @@ hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
                           bool a_bf16, int32_t r, void *dX, bool dx_bf16, bool exact,
                           hipStream_t s);
 
+// Small-M forward (M <= kSmallMaxM tokens, r <= kSmallMaxR), two launches:
+// partials over K chunks of small_fwd_chunk_rows(M, K, N) rows,
+//   P[ks][M][N] = X . deq(Wq) over the chunk, PXA[ks][M][r] = X . A over the
+//   chunk (ks = number of chunks);
+// then XA = sum_ks PXA (fp32 [M x r], optional when r == 0) and
+//   Y = sum_ks P + XA . B (act dtype), both sums in a fixed order.
+constexpr int kSmallMaxM = 16;
+constexpr int kSmallMaxR = 64;
+int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N);
+hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
+                                    const float *gscale, int64_t K, int64_t N, const void *X,
+                                    bool x_bf16, int64_t M, const void *A, bool a_bf16, int64_t r,
+                                    int64_t Kc, float *P, float *PXA, hipStream_t s);
+hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS, int64_t M,
+                                   int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
+                                   void *Y, bool y_bf16, hipStream_t s);
+
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
 

@@ -72,12 +72,18 @@ def test_workspace_sizes(L):
         for act in (q.BF16, q.F32):
             f = q.qlora_fwd_workspace_bytes(M, i, o, r, act)
             b = q.qlora_bwd_workspace_bytes(M, i, o, r, act)
-            # block scales (fp32 per 64 weights), XA split partials, XA in bf16
-            assert f >= i * o // 16 + M * r * 4 + M * r * 2
+            if M <= 16 and r <= 64:
+                # few tokens: split-K partials of y and of XA (at least one chunk)
+                assert f >= M * o * 4 + M * r * 4
+            else:
+                # block scales (fp32 per 64 weights), XA split partials, XA in bf16
+                assert f >= i * o // 16 + M * r * 4 + M * r * 2
+                if act == q.F32:
+                    assert f >= M * i * 2
             assert b >= M * r * 4 + i * o // 16
             assert f % 256 == 0 and b % 256 == 0
             if act == q.F32:
-                assert f >= M * i * 2 and b >= M * o * 2
+                assert b >= M * o * 2
     assert q.qlora_fwd_workspace_bytes(2048, 4096, 4096, 0, q.BF16) == 4096 * 64 * 4
     assert q.qlora_fwd_workspace_bytes(0, 4096, 4096, 16, q.BF16) == 0
     assert q.qlora_bwd_workspace_bytes(64, 100, 256, 8, q.BF16) == 0     # invalid shape

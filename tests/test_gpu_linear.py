@@ -69,6 +69,31 @@ def test_ragged_full(M, n_in, n_out, r, act, adt):
     _check(L, tag="ragged")
 
 
+@pytest.mark.parametrize("M,n_in,n_out,r,act,adt", [
+    (1, 320, 448, 16, "bf16", "bf16"),      # N not a multiple of the 256-column slice
+    (3, 192, 320, 5, "f32", "f32"),         # fp32 everywhere, r % 8 != 0
+    (16, 640, 704, 64, "bf16", "f32"),      # largest M and r of the few-token path
+    (7, 1088, 192, 40, "f32", "bf16"),      # several K chunks, ragged last chunk
+    (2, 256, 256, 0, "bf16", "bf16"),       # rank 0
+    (16, 320, 256, 65, "bf16", "bf16"),     # r above the few-token limit: GEMM path
+])
+def test_few_tokens(M, n_in, n_out, r, act, adt):
+    L = Layer(14, M, n_in, n_out, r, act=act, adt=adt)
+    _codes_match_oracle(L)
+    _check(L, tag="few tokens")
+
+
+def test_few_tokens_b_zero_equals_rank_zero_and_deterministic():
+    L = Layer(15, 5, 576, 448, 16, b_zero=True)
+    Y, XA = L.fwd()
+    Y2, XA2 = L.fwd()
+    assert np.array_equal(out_to_f64(Y, "bf16"), out_to_f64(Y2, "bf16"))
+    assert np.array_equal(XA.cpu().numpy(), XA2.cpu().numpy())
+    L0 = Layer(15, 5, 576, 448, 0)
+    Y0, _ = L0.fwd()
+    assert np.array_equal(out_to_f64(Y, "bf16"), out_to_f64(Y0, "bf16"))
+
+
 def test_b_zero_equals_rank_zero():
     """B = 0: the output is exactly the quantized base output (the r = 0
     path), up to the sign of zero."""
