@@ -16,9 +16,11 @@
 // 16-lane group column i of 16 consecutive k rows: the k run of one MFMA
 // operand lane.  Codes expand to bf16 levels through two v_perm byte planes
 // (sign-symmetric level set: 8 magnitudes).  v_mfma_f32_16x16x32_bf16 runs
-// with the tokens as its 16 rows (rows >= M are zero).  Workgroups of slice 0
-// also accumulate the chunk's X . A (unscaled X, A staged in LDS and read
-// transposed).  Partials: P[chunk][m][n] and PXA[chunk][m][j], fp32.
+// with the tokens as its 16 rows (rows >= M are zero).  A chunk of K is
+// walked in sub-chunks of 128 rows; the loads of the next sub-chunk are in
+// flight while the current one is multiplied.  One extra column of
+// workgroups accumulates each chunk's X . A (unscaled X, A staged in LDS and
+// read transposed).  Partials: P[chunk][m][n] and PXA[chunk][m][j], fp32.
 // Pass 2: XA = sum over chunks of PXA (written out), y = sum of P + XA . B.
 #include "device.h"
 
@@ -31,10 +33,12 @@ typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;           // reduction pass
+constexpr int kThreads1 = 512;          // partial pass: 8 wavefronts
 constexpr int kSliceN = 256;            // columns per workgroup (4 block columns)
 constexpr int kSub = 128;               // k rows per LDS sub-chunk
 constexpr int kCodePitch = 40;          // bytes per k row of a wavefront's code tile
+constexpr int kRegion = kSub * kCodePitch + 32;   // bytes per wavefront code tile (bank shift 8)
 constexpr int kXPitchS = kSub + 4;      // fp32 per X row in LDS
 constexpr int kAPitch = kSmallMaxR + 8; // bf16 per A row in LDS
 constexpr int32_t kBufFlags = 0x00020000;
@@ -52,9 +56,8 @@ struct SmallArgs {
   float *PXA;            // [KS][M][r]
 };
 
-__device__ __forceinline__ float load_act(const void *p, int64_t i, bool bf16) {
-  if (bf16) return __uint_as_float(uint32_t(static_cast<const uint16_t *>(p)[i]) << 16);
-  return static_cast<const float *>(p)[i];
+__device__ __forceinline__ int32_t clamp_records(int64_t bytes) {
+  return bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : int32_t(bytes));
 }
 
 // 8 codes (nibble t of d = k row t of the lane's run) -> four bf16 pairs of
@@ -77,93 +80,200 @@ __device__ __forceinline__ u32x4_t expand_levels(uint32_t d, const ExpandConsts1
   return r;
 }
 
+// One sub-chunk of loads in registers (prefetched while the previous
+// sub-chunk is multiplied).
+struct Stage {
+  u32x4_t cv[kSub / 64];   // codes: 16-B chunk t & 7 of row (t >> 3) + 64 it
+  f32x4_t xv;              // X[t >> 5][4 (t & 31) .. +3]
+  float sc;                // block scale of k row 64 (wave >> 2) + lane
+};
+
+// X[16 x kSub] of rows kb.. to registers: thread t -> row t >> 5, k run
+// 4 (t & 31) .. +3 (rows >= M read as zero through the descriptor range).
+template <bool kX16>
+__device__ __forceinline__ f32x4_t load_x4(__amdgpu_buffer_rsrc_t rX, int64_t K, int64_t kb) {
+  const int t = threadIdx.x;
+  constexpr int esx = kX16 ? 2 : 4;
+  const uint32_t off = uint32_t((int64_t(t >> 5) * K + kb + 4 * (t & 31)) * esx);
+  if constexpr (kX16) {
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rX, off, 0, 0));
+    return f32x4_t{bf16_lo_to_f32(v[0]), bf16_hi_to_f32(v[0]), bf16_lo_to_f32(v[1]), bf16_hi_to_f32(v[1])};
+  } else {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void store_x4(float (*xs)[kXPitchS], f32x4_t v, int64_t kb, int64_t kend) {
+  const int t = threadIdx.x;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  *reinterpret_cast<f32x4_t *>(&xs[t >> 5][4 * (t & 31)]) = (kb + 4 * (t & 31) < kend) ? v : zero4;
+}
+
+// The X . A workgroups (slice index == number of code slices): X[16 x kSub]
+// times A[kSub x r] for the chunk, wavefront w -> columns 16 w .. 16 w + 15.
 template <bool kX16, bool kA16>
-__global__ __launch_bounds__(kThreads) void fwd_small_kernel(SmallArgs a, ExpandConsts16 t16) {
+__device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int64_t kend,
+                                          float (*xs)[kXPitchS], uint16_t (*as)[kAPitch]) {
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  constexpr int esx = kX16 ? 2 : 4, esa = kA16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.X, (short)0, clamp_records(a.M * a.K * esx), kBufFlags);   // rows >= M: zero
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.A, (short)0, clamp_records(a.K * a.r * esa), kBufFlags);
+  const bool active = wave < 4 && 16 * wave < a.r;
+  f32x4_t xacc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t kb = kbeg; kb < kend; kb += kSub) {
+    const int rows = int(min64(kSub, kend - kb));
+    const f32x4_t xv = load_x4<kX16>(rX, a.K, kb);
+    float av[kSub / 8];      // A rows (t >> 6) + 8 u, column lane
+#pragma unroll
+    for (int u = 0; u < kSub / 8; ++u) {
+      const uint32_t off = uint32_t(((kb + (t >> 6) + 8 * u) * a.r + lane) * esa);
+      if constexpr (kA16)
+        av[u] = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rA, off, 0, 0)) << 16);
+      else
+        av[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA, off, 0, 0));
+    }
+    store_x4(xs, xv, kb, kend);
+#pragma unroll
+    for (int u = 0; u < kSub / 8; ++u) {
+      const int kk = (t >> 6) + 8 * u;
+      const float v = (lane < a.r && kk < rows) ? av[u] : 0.0f;
+      as[kk][lane] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+    __syncthreads();
+    if (active) {
+      for (int rb = 0; rb < rows; rb += 64) {
+        // natural k order: lane (g, i) <- X[i][rb + 16 g + 0..15]
+        u32x4_t U1, U2;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(&xs[i][rb + 16 * g + 8 * q]);
+          const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(&xs[i][rb + 16 * g + 8 * q + 4]);
+          u32x4_t &U = q ? U2 : U1;
+          U[0] = pack_bf16x2(x0.x, x0.y);
+          U[1] = pack_bf16x2(x0.z, x0.w);
+          U[2] = pack_bf16x2(x1.x, x1.y);
+          U[3] = pack_bf16x2(x1.z, x1.w);
+        }
+        // A^T operand: two ds_read_b64_tr_b16 per 8 k rows (16 lanes x 4 rows
+        // -> lane i gets column i of the 4 rows)
+        const int tq = i >> 2, qq = i & 3;
+        const lds_char *ab = (const lds_char *)(&as[0][0]);
+        const int col = 16 * wave + 4 * qq;
+        u32x2_t w[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          w[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (lds_i16x4 *)(ab + ((rb + 16 * g + 4 * h + tq) * kAPitch + col) * 2)));
+        xacc = mfma16x16x32(U1, u32x4_t{w[0][0], w[0][1], w[1][0], w[1][1]}, xacc);
+        xacc = mfma16x16x32(U2, u32x4_t{w[2][0], w[2][1], w[3][0], w[3][1]}, xacc);
+      }
+    }
+    __syncthreads();
+  }
+  const int j = 16 * wave + i;
+  if (active && j < a.r) {
+    float *PX = a.PXA + int64_t(blockIdx.y) * a.M * a.r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * g + e;
+      if (m < a.M) PX[int64_t(m) * a.r + j] = xacc[e];
+    }
+  }
+}
+
+template <bool kX16, bool kA16>
+__global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, ExpandConsts16 t16) {
   __shared__ __attribute__((aligned(16))) float xs[16][kXPitchS];
   __shared__ __attribute__((aligned(16))) float cs[4][kSub];
-  __shared__ __attribute__((aligned(16))) uint8_t ct[4][kSub * kCodePitch];
-  __shared__ __attribute__((aligned(16))) uint16_t as[kSub][kAPitch];
+  // codes of the 4 block columns, or (X . A workgroups) the adapter rows;
+  // after the K loop, the k-half partial sums
+  __shared__ __attribute__((aligned(16))) uint8_t ct[4 * kRegion];
+  static_assert(kSub * kAPitch * 2 <= 4 * kRegion, "A tile fits the code tiles");
+  static_assert(4 * 16 * 64 * 4 <= 4 * kRegion, "k-half sums fit the code tiles");
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4, i = lane & 15;
-  const int64_t n0 = int64_t(blockIdx.x) * kSliceN;
   const int c = blockIdx.y;
   const int64_t kbeg = int64_t(c) * a.Kc;
   const int64_t kend = min64(kbeg + a.Kc, a.K);
-  const int64_t nblk = a.N / 64, blk = n0 / 64 + wave;   // this wavefront's block column
+  const int64_t slices = (a.N + kSliceN - 1) / kSliceN;
+  if (blockIdx.x == slices) {
+    xa_worker<kX16, kA16>(a, kbeg, kend, xs, reinterpret_cast<uint16_t (*)[kAPitch]>(ct));
+    return;
+  }
+
+  // wavefront w: block column bc = w & 3 (64 columns), k half kh = w >> 2
+  // (rows 64 kh .. 64 kh + 63 of every sub-chunk)
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: buffer descriptors
+  const int bc = wave & 3, kh = wave >> 2;
+  const int64_t n0 = int64_t(blockIdx.x) * kSliceN;
+  const int64_t nblk = a.N / 64, blk = n0 / 64 + bc;
   const bool blk_ok = blk < nblk;
   const int64_t half_n = a.N / 2;
-  const bool xa_tile = blockIdx.x == 0 && 16 * wave < a.r;   // X . A column tile `wave`
+  constexpr int esx = kX16 ? 2 : 4;
+  uint8_t *myct = ct + bc * kRegion;
 
-  f32x4_t acc[4], xacc;
+  // Every global read goes through a buffer descriptor whose range ends at
+  // the last valid byte: reads past it return zero, so no load is predicated.
+  const int64_t cbase = kbeg * half_n + n0 / 2;
+  const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.codes + cbase), (short)0, clamp_records((kend - kbeg) * half_n - n0 / 2),
+      kBufFlags);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.X, (short)0, clamp_records(a.M * a.K * esx), kBufFlags);   // rows >= M: zero
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.qscale, (short)0, clamp_records(a.K * nblk), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.gscale, (short)0, clamp_records((a.K * nblk + 255) / 256 * 4), kBufFlags);
+
+  auto load_stage = [&](int64_t kb, Stage &S) {
+    // the workgroup's 128-B segment of 8 rows per load instruction (whole
+    // lines); rows past the chunk read as zero
+#pragma unroll
+    for (int it = 0; it < kSub / 64; ++it) {
+      const int row = (t >> 3) + 64 * it;
+      const uint32_t off = uint32_t((kb - kbeg + row) * half_n) + 16u * uint32_t(t & 7);
+      S.cv[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 2));
+    }
+    S.xv = load_x4<kX16>(rX, a.K, kb);
+    const uint32_t b = uint32_t((kb + 64 * kh + lane) * nblk + blk);
+    const int8_t qv = int8_t(__builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0));
+    const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, (b >> 8) * 4u, 0, 0));
+    S.sc = float(qv) * s2;
+  };
+
+  f32x4_t acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  xacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // codes of this wavefront's block column, rows kbeg .. kend
-  const int64_t cbase = kbeg * half_n + n0 / 2 + 32 * wave;
-  const int64_t cbytes = (kend - kbeg) * half_n - (n0 / 2 + 32 * wave);
-  const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.codes + cbase), (short)0, int32_t(cbytes > 0x7fffffff ? 0x7fffffff : cbytes),
-      kBufFlags);
-
+  Stage S;
+  load_stage(kbeg, S);
   for (int64_t kb = kbeg; kb < kend; kb += kSub) {
-    const int rows = int(min64(kSub, kend - kb));        // multiple of 64
-    // ---- issue the code loads: 2 lanes per row, 32 rows per instruction
-    u32x4_t cv[kSub / 32];
+    const int rows = int(min64(kSub, kend - kb));        // 64 or 128
+    // ---- this sub-chunk to LDS
 #pragma unroll
-    for (int it = 0; it < kSub / 32; ++it) {
-      const int row = (lane >> 1) + 32 * it;
-      const uint32_t off = uint32_t((kb - kbeg + row) * half_n) + 16u * uint32_t(lane & 1);
-      cv[it] = row < rows ? __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 2))
-                          : u32x4_t{0u, 0u, 0u, 0u};
+    for (int it = 0; it < kSub / 64; ++it) {
+      const int row = (t >> 3) + 64 * it, ch = t & 7;   // chunk ch -> block column ch / 2
+      uint8_t *dst = ct + (ch >> 1) * kRegion + row * kCodePitch + 16 * (ch & 1);
+      *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{S.cv[it][0], S.cv[it][1]};
+      *reinterpret_cast<u32x2_t *>(dst + 8) = u32x2_t{S.cv[it][2], S.cv[it][3]};
     }
-    // ---- activations [16][kSub] fp32 (rows >= M and k >= kend are zero)
-    {
-      const int m = t >> 4, k8 = (t & 15) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t k = kb + k8 + e;
-        xs[m][k8 + e] = (m < a.M && k < kend) ? load_act(a.X, int64_t(m) * a.K + k, kX16) : 0.0f;
-      }
-    }
-    // ---- block scales of this wavefront's block column
-#pragma unroll
-    for (int e = 0; e < kSub / 64; ++e) {
-      const int kk = lane + 64 * e;
-      const int64_t k = kb + kk;
-      float s = 0.0f;
-      if (blk_ok && kk < rows) {
-        const int64_t b = k * nblk + blk;
-        s = float(a.qscale[b]) * a.gscale[b >> 8];
-      }
-      cs[wave][kk] = s;
-    }
-    // ---- adapter A rows of this sub-chunk (slice 0 only), as bf16
-    if (blockIdx.x == 0 && a.r > 0) {
-      for (int e = t; e < kSub * a.r; e += kThreads) {
-        const int kk = e / int(a.r), j = e % int(a.r);
-        const int64_t k = kb + kk;
-        const float v = (kk < rows) ? load_act(a.A, k * a.r + j, kA16) : 0.0f;
-        as[kk][j] = __builtin_bit_cast(uint16_t, (__bf16)v);
-      }
-    }
-    // ---- codes to this wavefront's LDS tile (read back only by this wavefront)
-#pragma unroll
-    for (int it = 0; it < kSub / 32; ++it) {
-      const int row = (lane >> 1) + 32 * it;
-      uint8_t *dst = &ct[wave][row * kCodePitch + 16 * (lane & 1)];
-      *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{cv[it][0], cv[it][1]};
-      *reinterpret_cast<u32x2_t *>(dst + 8) = u32x2_t{cv[it][2], cv[it][3]};
-    }
+    store_x4(xs, S.xv, kb, kend);
+    cs[bc][64 * kh + lane] = (blk_ok && 64 * kh + lane < rows) ? S.sc : 0.0f;
     __syncthreads();
+    // ---- the next sub-chunk's loads fly while this one is multiplied
+    if (kb + kSub < kend) load_stage(kb + kSub, S);
 
-    for (int rb = 0; rb < rows; rb += 64) {
+    const int rb = 64 * kh;
+    if (rb < rows) {
       // activation operand: X[m = i][rb + 16 g + 0..15] times the row scales
       float xv[16], sv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4_t x4 = *reinterpret_cast<const f32x4_t *>(&xs[i][rb + 16 * g + 4 * q]);
-        const f32x4_t s4 = *reinterpret_cast<const f32x4_t *>(&cs[wave][rb + 16 * g + 4 * q]);
+        const f32x4_t s4 = *reinterpret_cast<const f32x4_t *>(&cs[bc][rb + 16 * g + 4 * q]);
         xv[4 * q] = x4.x; xv[4 * q + 1] = x4.y; xv[4 * q + 2] = x4.z; xv[4 * q + 3] = x4.w;
         sv[4 * q] = s4.x; sv[4 * q + 1] = s4.y; sv[4 * q + 2] = s4.z; sv[4 * q + 3] = s4.w;
       }
@@ -177,96 +287,122 @@ __global__ __launch_bounds__(kThreads) void fwd_small_kernel(SmallArgs a, Expand
       A2[2] = pack_bf16x2(xv[9] * sv[9], xv[11] * sv[11]);
       A2[3] = pack_bf16x2(xv[13] * sv[13], xv[15] * sv[15]);
       // weight operand: lane (g, i) <- column 16 q + i, rows rb + 16 g + 0..15
-      const lds_char *crow = (const lds_char *)(&ct[wave][(rb + 16 * g + i) * kCodePitch]);
+      const lds_char *crow = (const lds_char *)(myct + (rb + 16 * g + i) * kCodePitch);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const i32x2_t d = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(crow + 8 * q));
         acc[q] = mfma16x16x32(A1, expand_levels(uint32_t(d[0]), t16), acc[q]);
         acc[q] = mfma16x16x32(A2, expand_levels(uint32_t(d[1]), t16), acc[q]);
       }
-      if (xa_tile) {
-        // X . A for columns 16 wave .. +15, natural k order
-        u32x4_t U1, U2, B1, B2;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          U1[p] = pack_bf16x2(xv[2 * p], xv[2 * p + 1]);
-          U2[p] = pack_bf16x2(xv[8 + 2 * p], xv[9 + 2 * p]);
-        }
-        const int tq = i >> 2, qq = i & 3;
-        const lds_char *ab = (const lds_char *)(&as[0][0]);
-        const int col = 16 * wave + 4 * qq;
-        const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(ab + ((rb + 16 * g + tq) * kAPitch + col) * 2));
-        const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(ab + ((rb + 16 * g + 4 + tq) * kAPitch + col) * 2));
-        const i16x4_t r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(ab + ((rb + 16 * g + 8 + tq) * kAPitch + col) * 2));
-        const i16x4_t r3 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(ab + ((rb + 16 * g + 12 + tq) * kAPitch + col) * 2));
-        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, r0), w1 = __builtin_bit_cast(u32x2_t, r1);
-        const u32x2_t w2 = __builtin_bit_cast(u32x2_t, r2), w3 = __builtin_bit_cast(u32x2_t, r3);
-        B1 = u32x4_t{w0[0], w0[1], w1[0], w1[1]};
-        B2 = u32x4_t{w2[0], w2[1], w3[0], w3[1]};
-        xacc = mfma16x16x32(U1, B1, xacc);
-        xacc = mfma16x16x32(U2, B2, xacc);
-      }
     }
     __syncthreads();   // LDS tiles are rewritten by the next sub-chunk
   }
 
+  // ---- k half 1 hands its sums to k half 0 (fixed order: half 0 + half 1)
+  float *red = reinterpret_cast<float *>(ct) + bc * (16 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(4 * q + e) * 64 + lane] = acc[q][e];
+  }
+  __syncthreads();
+  if (kh == 1) return;
   // ---- partials: lane (g, i) holds rows 4 g .. 4 g + 3 of column 16 q + i
   float *P = a.P + int64_t(c) * a.M * a.N;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int64_t n = n0 + 64 * wave + 16 * q + i;
-    if (!blk_ok || n >= a.N) continue;
+    const int64_t n = n0 + 64 * bc + 16 * q + i;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      const float v = acc[q][e] + red[(4 * q + e) * 64 + lane];
       const int m = 4 * g + e;
-      if (m < a.M) P[int64_t(m) * a.N + n] = acc[q][e];
-    }
-  }
-  if (xa_tile) {
-    float *PX = a.PXA + int64_t(c) * a.M * a.r;
-    const int j = 16 * wave + i;
-    if (j < a.r) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * g + e;
-        if (m < a.M) PX[int64_t(m) * a.r + j] = xacc[e];
-      }
+      if (blk_ok && n < a.N && m < a.M) P[int64_t(m) * a.N + n] = v;
     }
   }
 }
 
-// Pass 2: 64 columns per workgroup, thread (m-group, column).
+// Pass 2: a workgroup covers `cols` = 256 / Mp columns of all M rows (Mp =
+// M rounded up to a power of two); thread -> (row, column).  The partials of
+// up to 32 chunks, 16 rows of B and the XA partials are all requested before
+// any is used (range-checked buffer loads: zero past the end), so the pass
+// waits for memory about once; sums run in chunk order.
 template <bool kY16, bool kB16>
 __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
     const float *__restrict__ P, const float *__restrict__ PXA, int64_t KS, int64_t M, int64_t N,
-    int64_t r, const void *B, float *XA, void *Y) {
+    int64_t r, int cols, const void *B, float *XA, void *Y) {
   __shared__ float xa[16][kSmallMaxR];
   const int t = threadIdx.x;
-  // XA = sum over chunks of PXA, fixed order
-  for (int e = t; e < M * r; e += kThreads) {
-    float s = 0.0f;
-    for (int64_t k = 0; k < KS; ++k) s += PXA[k * M * r + e];
-    xa[e / r][e % r] = s;
-    if (blockIdx.x == 0) XA[e] = s;
+  const int64_t ER = M * r;
+  constexpr int esb = kB16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P, (short)0, clamp_records(KS * M * N * 4), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rPX = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)PXA, (short)0, clamp_records(KS * ER * 4), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)B, (short)0, clamp_records(r * N * esb), kBufFlags);
+  const int m = t / cols;
+  const int64_t n = int64_t(blockIdx.x) * cols + (t % cols);
+  const bool ok = m < M && n < N;
+  auto load_b = [&](int j) -> float {
+    const uint32_t off = uint32_t((int64_t(j) * N + n) * esb);
+    if constexpr (kB16)
+      return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rB, off, 0, 0)) << 16);
+    else
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rB, off, 0, 0));
+  };
+  // ---- requests: partials of chunks 0..31, rows 0..15 of B
+  float pv[32], bv[16];
+#pragma unroll
+  for (int u = 0; u < 32; ++u)
+    pv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          rP, uint32_t(((u * M + m) * N + n) * 4), 0, 0));
+#pragma unroll
+  for (int q = 0; q < 16; ++q) bv[q] = load_b(q);
+  // ---- XA = sum over chunks of PXA
+  for (int e = t; e < ER; e += kThreads) {
+    float xv[32];
+    float sx = 0.0f;
+    for (int64_t c0 = 0; c0 < KS; c0 += 32) {
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        xv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              rPX, uint32_t(((c0 + u) * ER + e) * 4), 0, 0));
+#pragma unroll
+      for (int u = 0; u < 32; ++u) sx += xv[u];
+    }
+    xa[e / r][e % r] = sx;
+    if (blockIdx.x == 0) XA[e] = sx;
   }
   __syncthreads();
-  const int64_t n = int64_t(blockIdx.x) * 64 + (t & 63);
-  if (n >= N) return;
-  for (int m = t >> 6; m < M; m += 4) {
-    float s = 0.0f;
-    for (int64_t k = 0; k < KS; ++k) s += P[(k * M + m) * N + n];
-    float u = 0.0f;
-    for (int j = 0; j < r; ++j) u += xa[m][j] * load_act(B, int64_t(j) * N + n, kB16);
-    const float y = s + u;
-    if (kY16)
-      static_cast<uint16_t *>(Y)[int64_t(m) * N + n] = __builtin_bit_cast(uint16_t, (__bf16)y);
-    else
-      static_cast<float *>(Y)[int64_t(m) * N + n] = y;
+  if (!ok) return;
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) sum += pv[u];
+  for (int64_t c0 = 32; c0 < KS; c0 += 32) {
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      pv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            rP, uint32_t((((c0 + u) * M + m) * N + n) * 4), 0, 0));
+#pragma unroll
+    for (int u = 0; u < 32; ++u) sum += pv[u];
   }
+  float ua = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (q < r) ua += xa[m][q] * bv[q];
+  for (int j0 = 16; j0 < r; j0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) bv[q] = load_b(j0 + q);
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (j0 + q < r) ua += xa[m][j0 + q] * bv[q];
+  }
+  const float y = sum + ua;
+  if (kY16)
+    static_cast<uint16_t *>(Y)[int64_t(m) * N + n] = __builtin_bit_cast(uint16_t, (__bf16)y);
+  else
+    static_cast<float *>(Y)[int64_t(m) * N + n] = y;
 }
 
 }  // namespace
@@ -287,13 +423,14 @@ hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
   const int64_t slices = (N + kSliceN - 1) / kSliceN;
   SmallArgs a{codes, qscale, gscale, K, N, X, A, M, r, Kc, P, PXA};
   const ExpandConsts16 &t16 = tables().expand16;
-  const dim3 grid = dim3(unsigned(slices), unsigned(KS));
+  // one extra column of workgroups computes the X . A partials
+  const dim3 grid = dim3(unsigned(slices + (r > 0 ? 1 : 0)), unsigned(KS));
   if (x_bf16) {
-    if (a_bf16) hipLaunchKernelGGL((fwd_small_kernel<true, true>), grid, dim3(kThreads), 0, s, a, t16);
-    else hipLaunchKernelGGL((fwd_small_kernel<true, false>), grid, dim3(kThreads), 0, s, a, t16);
+    if (a_bf16) hipLaunchKernelGGL((fwd_small_kernel<true, true>), grid, dim3(kThreads1), 0, s, a, t16);
+    else hipLaunchKernelGGL((fwd_small_kernel<true, false>), grid, dim3(kThreads1), 0, s, a, t16);
   } else {
-    if (a_bf16) hipLaunchKernelGGL((fwd_small_kernel<false, true>), grid, dim3(kThreads), 0, s, a, t16);
-    else hipLaunchKernelGGL((fwd_small_kernel<false, false>), grid, dim3(kThreads), 0, s, a, t16);
+    if (a_bf16) hipLaunchKernelGGL((fwd_small_kernel<false, true>), grid, dim3(kThreads1), 0, s, a, t16);
+    else hipLaunchKernelGGL((fwd_small_kernel<false, false>), grid, dim3(kThreads1), 0, s, a, t16);
   }
   return hipGetLastError();
 }
@@ -301,13 +438,16 @@ hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
 hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS, int64_t M,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
                                    void *Y, bool y_bf16, hipStream_t s) {
-  const dim3 grid = dim3(unsigned((N + 63) / 64));
+  int mp = 1;
+  while (mp < M) mp *= 2;
+  const int cols = kThreads / mp;
+  const dim3 grid = dim3(unsigned((N + cols - 1) / cols));
   if (y_bf16) {
-    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<true, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, B, XA, Y);
-    else hipLaunchKernelGGL((fwd_small_reduce_kernel<true, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, B, XA, Y);
+    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<true, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
+    else hipLaunchKernelGGL((fwd_small_reduce_kernel<true, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
   } else {
-    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<false, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, B, XA, Y);
-    else hipLaunchKernelGGL((fwd_small_reduce_kernel<false, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, B, XA, Y);
+    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<false, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
+    else hipLaunchKernelGGL((fwd_small_reduce_kernel<false, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
   }
   return hipGetLastError();
 }
