@@ -16,7 +16,8 @@ backward calls of every timed step; quantize GB/s is reported beside it.
 `roofline` covers the dominant kernel (a fused dequantizing GEMM), timed with
 HIP events around each of its launches on the stream it runs on.
 `cpu_baseline` times the CPU oracle on the same workload (bounded to a few
-repetitions of the full step, about 10 s of CPU work).
+repetitions of the full step, about 10 s of CPU work).  `decode` reports the
+few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
 """
 
 import argparse
@@ -45,6 +46,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time of the oracle baseline")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the few-token (decode) forward measurement")
+    p.add_argument("--decode-sets", type=int, default=32,
+                   help="distinct 7B layer sets cycled by the decode measurement")
     p.add_argument("--copy-calibrate", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -132,6 +137,82 @@ def cpu_baseline(w0, X, dY, A, B, min_seconds):
         "quantize_GBps": round(reps * qbytes / tq / 1e9, 4),
         "host_cpu_count": os.cpu_count(),
     }
+
+
+def decode_report(sets, reps=5):
+    """Few-token forward of 7B-style layer sets (q, k, v, o 4096x4096; gate,
+    up 4096x11008; down 11008x4096), r = 16, M in {1, 4, 16}, bf16.  `sets`
+    distinct layer sets (each its own NF4 weights, quantized here from seeded
+    N(0, 0.02^2) fp32 weights drawn on the device) are run back to back so the
+    weights stream from HBM; the whole sequence is captured once in a HIP
+    graph and replayed.  Bytes per linear: codes + int8 block scales + fp32
+    group scales + X + A + B + y."""
+    import math
+    import torch
+    from quantized_rank_fine_amd import qlora as q, workloads
+
+    dev = torch.device("cuda:0")
+    R = 16
+    lins = workloads.LLAMA7B_LINEARS
+    g = torch.Generator(device=dev)
+    layers = []
+    for s in range(sets):
+        row = []
+        for li, (_, n_in, n_out) in enumerate(lins):
+            g.manual_seed(1000003 * s + li)
+            w0 = torch.randn(n_in, n_out, device=dev, generator=g) * 0.02
+            wq = q.NF4Weight(n_in, n_out, dev)
+            q.qlora_quantize(w0, wq)
+            del w0
+            A = (torch.randn(n_in, R, device=dev, generator=g) / math.sqrt(n_in)).to(torch.bfloat16)
+            B = (torch.randn(R, n_out, device=dev, generator=g) * 0.01).to(torch.bfloat16)
+            row.append((wq, A, B))
+        layers.append(row)
+    torch.cuda.synchronize()
+    res = {}
+    for M in (1, 4, 16):
+        g.manual_seed(77 + M)
+        X = {n_in: torch.randn(M, n_in, device=dev, generator=g).to(torch.bfloat16)
+             for (_, n_in, _) in lins}
+        Y = {n_out: torch.empty(M, n_out, dtype=torch.bfloat16, device=dev) for (_, _, n_out) in lins}
+        XA = torch.empty(M, R, dtype=torch.float32, device=dev)
+        wsb = max(q.qlora_fwd_workspace_bytes(M, n_in, n_out, R) for (_, n_in, n_out) in lins)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def seq():
+            for s in range(sets):
+                for li, (_, n_in, n_out) in enumerate(lins):
+                    wq, A, B = layers[s][li]
+                    q.qlora_linear_fwd(wq, X[n_in], M, q.BF16, A, B, R, q.BF16, Y[n_out], XA, ws, wsb)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            seq()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            seq()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = sets * sum(workloads.nf4_bytes(n_in, n_out) + M * n_in * 2 + (n_in * R + R * n_out) * 2
+                            + M * n_out * 2 for (_, n_in, n_out) in lins)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        res[f"M{M}"] = {"us_per_layer_set": round(us / sets, 2), "GBps": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        del graph
+    return {"workload": "7b-layer-decode-r16-bf16", "layer_sets": sets,
+            "bytes_per_set_M1": sum(workloads.nf4_bytes(i, o) + i * 2 + (i * R + R * o) * 2 + o * 2
+                                    for (_, i, o) in lins),
+            "timing": "HIP graph of the whole sequence, replayed", **res}
 
 
 def main():
@@ -258,6 +339,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if not args.no_decode:
+        out["decode"] = decode_report(args.decode_sets)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w0_host[0], Xs.values, dYs.values, As.values,
                                            Bs.values, args.cpu_seconds)
