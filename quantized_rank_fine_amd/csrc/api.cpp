@@ -56,11 +56,6 @@ qlora_status dev(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_D
 // ---------------------------------------------------------------- plans
 // Workspace layouts.  Every region starts on a 256-byte boundary.
 
-#ifndef QLORA_EXACT_EXPAND
-#define QLORA_EXACT_EXPAND 1
-#endif
-constexpr bool kExact = QLORA_EXACT_EXPAND != 0;
-
 struct Layout {
   size_t o = 0;
   size_t take(size_t bytes) {
@@ -239,7 +234,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
   }
   QLORA_RUN(QLORA_KERNEL_FWD_GEMM,
             launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, int32_t(p.rp), B, ab, r, Y, xb,
-                            kExact, stream));
+                            stream));
   return QLORA_OK;
 }
 
@@ -315,7 +310,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
   if (dX) {
     QLORA_RUN(QLORA_KERNEL_DX_GEMM,
               launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
-                             xb, kExact, stream));
+                             xb, stream));
   }
   return QLORA_OK;
 #undef QLORA_RUN

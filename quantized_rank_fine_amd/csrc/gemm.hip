@@ -25,20 +25,20 @@
 // K slots are permuted inside each 64-wide K tile: lane half h (lanes 32h..)
 // of the MFMA owns k = 32h .. 32h+31 (8 per substep), for both operands.
 //
-// Forward: the code tile is 64 k-rows x 128 n-cols, n-contiguous;
-// ds_read_b64_tr_b4 gives lane i of a 16-lane group column i of the 16 rows
-// the group points at (16 consecutive k of one column) in one read: the 16 k
-// of the wavefront's k half.  The scale of a weight depends on its k row
-// (and the wavefront's block column).
+// Forward: the code tile is 64 k-rows x 128 n-cols, n-contiguous, and the
+// scale of a weight depends on its k row (and the wavefront's block column).
+// A lane reads 8 bytes of one k row (16 consecutive columns, one scale),
+// expands them through that row's per-scale table and writes the bf16 values
+// to a per-wavefront LDS scratch, which is read back transposed with
+// ds_read_b64_tr_b16 as the MFMA B fragments.
 // Backward dX: the code tile is 128 W-rows x 64 W-cols and the contraction
 // runs along a W row: one 8-byte read gives a lane the 16 consecutive k of
 // its k half, all under one scale (the K tile is one 64-wide block).
 //
-// Expansion: w = bf16(level * scale) with level = L[code] from a 16-entry
-// table held as v_perm byte planes (sign-symmetric: 8 magnitudes).  kExact
-// selects the fp32 table (w rounded once from the fp32 product); otherwise
-// the level is rounded to bf16 first (fewer VALU operations, w within one
-// bf16 ulp of the fp32 product).
+// Expansion: w = bf16(L[code] * scale), the fp32 product rounded once.  For
+// each scale a per-scale table holds the 8 magnitudes bf16(|L|_m * scale) as
+// two v_perm byte planes (the level set is sign-symmetric), so a code becomes
+// its bf16 weight by table lookup and a sign bit.
 #include "device.h"
 
 namespace qlora {
@@ -112,62 +112,6 @@ __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t lds, uint32_t voff,
 }
 
 // ------------------------------------------------------------- expansion
-// Four codes (bytes of v, values 0..15) -> four levels as fp32.
-template <bool kExact>
-__device__ __forceinline__ void levels4(uint32_t v, const ExpandConsts &t, float out[4]) {
-  const uint32_t u = v ^ 0x08080808u;            // c>=8 -> c-8 ; c<8 -> c+8
-  const uint32_t b3 = u & 0x08080808u;           // 8 where the level is negative
-  const uint32_t m7 = b3 - (b3 >> 3);            // 7 where negative
-  const uint32_t m = (u ^ m7) & 0x07070707u;     // magnitude index 0..7
-  const uint32_t p2 = perm_b32(t.plane[2][1], t.plane[2][0], m);
-  const uint32_t p3 = perm_b32(t.plane[3][1], t.plane[3][0], m) | (b3 << 4);
-  if constexpr (kExact) {
-    const uint32_t p0 = perm_b32(t.plane[0][1], t.plane[0][0], m);
-    const uint32_t p1 = perm_b32(t.plane[1][1], t.plane[1][0], m);
-    const uint32_t a = perm_b32(p1, p0, 0x05010400u);
-    const uint32_t b = perm_b32(p1, p0, 0x07030602u);
-    const uint32_t c = perm_b32(p3, p2, 0x05010400u);
-    const uint32_t d = perm_b32(p3, p2, 0x07030602u);
-    out[0] = __uint_as_float(perm_b32(c, a, 0x05040100u));
-    out[1] = __uint_as_float(perm_b32(c, a, 0x07060302u));
-    out[2] = __uint_as_float(perm_b32(d, b, 0x05040100u));
-    out[3] = __uint_as_float(perm_b32(d, b, 0x07060302u));
-  } else {
-    // bf16 levels: bytes 2 and 3 of the fp32 pattern, low half zero
-    out[0] = __uint_as_float(perm_b32(p3, p2, 0x04000c0cu));
-    out[1] = __uint_as_float(perm_b32(p3, p2, 0x05010c0cu));
-    out[2] = __uint_as_float(perm_b32(p3, p2, 0x06020c0cu));
-    out[3] = __uint_as_float(perm_b32(p3, p2, 0x07030c0cu));
-  }
-}
-
-// 8 codes (nibble t = k slot t) x per-slot scales -> MFMA bf16 operand.
-template <bool kExact>
-__device__ __forceinline__ u32x4_t expand8(uint32_t d, const float *s, const ExpandConsts &tb) {
-  float le[4], lo[4];
-  levels4<kExact>(d & 0x0F0F0F0Fu, tb, le);
-  levels4<kExact>((d >> 4) & 0x0F0F0F0Fu, tb, lo);
-  u32x4_t r;
-  r[0] = pack_bf16x2(le[0] * s[0], lo[0] * s[1]);
-  r[1] = pack_bf16x2(le[1] * s[2], lo[1] * s[3]);
-  r[2] = pack_bf16x2(le[2] * s[4], lo[2] * s[5]);
-  r[3] = pack_bf16x2(le[3] * s[6], lo[3] * s[7]);
-  return r;
-}
-
-template <bool kExact>
-__device__ __forceinline__ u32x4_t expand8u(uint32_t d, float s, const ExpandConsts &tb) {
-  float le[4], lo[4];
-  levels4<kExact>(d & 0x0F0F0F0Fu, tb, le);
-  levels4<kExact>((d >> 4) & 0x0F0F0F0Fu, tb, lo);
-  u32x4_t r;
-  r[0] = pack_bf16x2(le[0] * s, lo[0] * s);
-  r[1] = pack_bf16x2(le[1] * s, lo[1] * s);
-  r[2] = pack_bf16x2(le[2] * s, lo[2] * s);
-  r[3] = pack_bf16x2(le[3] * s, lo[3] * s);
-  return r;
-}
-
 // Per-scale level table for a uniform scale s: the 8 magnitudes
 // bf16(|L|_m * s) (fp32 product, one rounding) as two v_perm byte planes --
 // lo[w] holds the low bytes of m = 4w..4w+3, hi[w] the high bytes.  A weight
@@ -278,7 +222,7 @@ __device__ __forceinline__ uint32_t xoff(int row, int c) { return row * 128 + ((
 //   A16: activations bf16 [M x K]; codes; cs: scales fp32 [blocks][rows].
 //   Forward: weight rows = K (k), columns = N; cs row count = K.
 //   dX:      weight rows = N (i), columns = K; cs row count = N.
-template <bool kFwd, bool kExact>
+template <bool kFwd>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, int64_t M, int64_t K,
                                               int64_t N, const uint8_t *__restrict__ codes,
                                               const float *__restrict__ cs, int64_t m0, int64_t n0,
@@ -662,7 +606,7 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
 }
 
 // ================================================================ forward
-template <bool kOutBf16, bool kExact>
+template <bool kOutBf16>
 __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t K, int64_t N,
     const uint16_t *__restrict__ X16, int64_t M, const uint16_t *__restrict__ XA16,
@@ -679,13 +623,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
-  gemm_mainloop<true, kExact>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
+  gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
   // rank-r term: y += XA16 . B (B read as rows n of B^T)
   epilogue<kOutBf16>(acc, smem, XA16, ldp, bq, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
-template <bool kOutBf16, bool kExact>
+template <bool kOutBf16>
 __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t IN, int64_t OUT,
     const uint16_t *__restrict__ dY16, int64_t M, const uint16_t *__restrict__ G16,
@@ -702,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
-  gemm_mainloop<false, kExact>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
+  gemm_mainloop<false>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
   // rank-r term: dX += G16 . A^T (A read as rows i of A)
   epilogue<kOutBf16>(acc, smem, G16, ldp, aq, M, IN, m0, i0, dX);
 }
@@ -717,24 +661,23 @@ bool set_lds(const void *fn) {
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int64_t N,
                            const uint16_t *X16, int64_t M, const uint16_t *XA16, int32_t ldp,
                            const void *B, bool b_bf16, int32_t r, void *Y, bool y_bf16,
-                           bool exact, hipStream_t s) {
+                           hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef bq{B, b_bf16, 1, N, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((N + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
   const ExpandConsts tb = tables().expand;
-#define QLORA_FWD(OB, EX)                                                                      \
+#define QLORA_FWD(OB)                                                                          \
   do {                                                                                         \
-    static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB, EX>));        \
+    static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB>));            \
     if (!ok) return hipErrorInvalidValue;                                                      \
-    hipLaunchKernelGGL((fwd_gemm_kernel<OB, EX>), grid, dim3(kThreads), kLdsBytes, s, codes,  \
-                       cs, K, N, X16, M, XA16, int(ldp), bq, Y, tb, ntc);                      \
+    hipLaunchKernelGGL((fwd_gemm_kernel<OB>), grid, dim3(kThreads), kLdsBytes, s, codes, cs,  \
+                       K, N, X16, M, XA16, int(ldp), bq, Y, tb, ntc);                          \
   } while (0)
-  if (y_bf16) {
-    if (exact) QLORA_FWD(true, true); else QLORA_FWD(true, false);
-  } else {
-    if (exact) QLORA_FWD(false, true); else QLORA_FWD(false, false);
-  }
+  if (y_bf16)
+    QLORA_FWD(true);
+  else
+    QLORA_FWD(false);
 #undef QLORA_FWD
   return hipGetLastError();
 }
@@ -742,24 +685,23 @@ hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int64_t out,
                           const uint16_t *dY16, int64_t M, const uint16_t *G16, int32_t ldp,
                           const void *A, bool a_bf16, int32_t r, void *dX, bool dx_bf16,
-                          bool exact, hipStream_t s) {
+                          hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef aq{A, a_bf16, int64_t(r), 1, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((in + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
   const ExpandConsts tb = tables().expand;
-#define QLORA_DX(OB, EX)                                                                       \
+#define QLORA_DX(OB)                                                                           \
   do {                                                                                         \
-    static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB, EX>));         \
+    static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB>));             \
     if (!ok) return hipErrorInvalidValue;                                                      \
-    hipLaunchKernelGGL((dx_gemm_kernel<OB, EX>), grid, dim3(kThreads), kLdsBytes, s, codes,   \
-                       cs, in, out, dY16, M, G16, int(ldp), aq, dX, tb, ntc);                  \
+    hipLaunchKernelGGL((dx_gemm_kernel<OB>), grid, dim3(kThreads), kLdsBytes, s, codes, cs,   \
+                       in, out, dY16, M, G16, int(ldp), aq, dX, tb, ntc);                      \
   } while (0)
-  if (dx_bf16) {
-    if (exact) QLORA_DX(true, true); else QLORA_DX(true, false);
-  } else {
-    if (exact) QLORA_DX(false, true); else QLORA_DX(false, false);
-  }
+  if (dx_bf16)
+    QLORA_DX(true);
+  else
+    QLORA_DX(false);
 #undef QLORA_DX
   return hipGetLastError();
 }

@@ -24,11 +24,10 @@ struct QuantConsts {
   int ok;               // 1 if the bucket scheme is exact for these thresholds
 };
 
-// Byte planes of the 8 level magnitudes |L|_m = L[8+m], m = 0..7.
-// plane[p][0] holds byte p of |L|_0..|L|_3, plane[p][1] of |L|_4..|L|_7.
+// The 8 level magnitudes |L|_m = L[8+m] (m = 0..7) as fp32; the fused GEMMs
+// build their per-scale tables from them.
 struct ExpandConsts {
-  uint32_t plane[4][2];
-  float mag[8];          // |L|_m = L[8+m] as fp32 (for per-scale tables)
+  float mag[8];
 };
 struct ExpandConsts16 {
   uint32_t plane[2][2];  // bytes 2 and 3 of the bf16-rounded magnitudes
@@ -97,16 +96,14 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K,
                            int64_t N, const uint16_t *X16, int64_t M,
                            const uint16_t *XA16, int32_t ldp, const void *B,
-                           bool b_bf16, int32_t r, void *Y, bool y_bf16, bool exact,
-                           hipStream_t s);
+                           bool b_bf16, int32_t r, void *Y, bool y_bf16, hipStream_t s);
 
 // dX = dY16 . deq(Wq)^T + G16 . A^T.  dY16 [M x out] bf16; G16 [M x ldp] bf16
 // zero-padded; A [in x r] (f32 or bf16) as given; cs as in the forward.
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
                           int64_t out, const uint16_t *dY16, int64_t M,
                           const uint16_t *G16, int32_t ldp, const void *A,
-                          bool a_bf16, int32_t r, void *dX, bool dx_bf16, bool exact,
-                          hipStream_t s);
+                          bool a_bf16, int32_t r, void *dX, bool dx_bf16, hipStream_t s);
 
 // Small-M forward (M <= kSmallMaxM tokens, r <= kSmallMaxR), two launches:
 // partials over K chunks of small_fwd_chunk_rows(M, K, N) rows,

@@ -98,20 +98,9 @@ Tables build_tables() {
     t.T[j] = from_key(b);
   }
 
-  // Byte planes of the 8 magnitudes |L|_m = L[8+m] (m = 0..7): plane p holds
-  // byte p of each fp32 pattern; word 0 covers m = 0..3, word 1 m = 4..7.
-  for (int p = 0; p < 4; ++p) {
-    for (int w = 0; w < 2; ++w) {
-      uint32_t v = 0;
-      for (int b = 0; b < 4; ++b) {
-        uint32_t bits = f2u(t.L[8 + 4 * w + b]);
-        v |= ((bits >> (8 * p)) & 0xffu) << (8 * b);
-      }
-      t.expand.plane[p][w] = v;
-    }
-  }
   for (int m = 0; m < 8; ++m) t.expand.mag[m] = t.L[8 + m];
-  // Same for the bf16-rounded magnitudes (bytes 2 and 3 of the fp32 pattern).
+  // Byte planes of the bf16-rounded magnitudes (bytes 2 and 3 of the fp32
+  // pattern): plane[p][w] holds byte p + 2 of m = 4w .. 4w + 3.
   for (int p = 0; p < 2; ++p) {
     for (int w = 0; w < 2; ++w) {
       uint32_t v = 0;
