@@ -82,31 +82,41 @@ __device__ __forceinline__ u32x4_t expand_levels(uint32_t d, const ExpandConsts1
 
 // One sub-chunk of loads in registers (prefetched while the previous
 // sub-chunk is multiplied).
+// Raw loads of one sub-chunk, kept unconverted so that prefetching them does
+// not wait for them: converted when they are written to LDS.
+template <bool kX16>
 struct Stage {
   u32x4_t cv[kSub / 64];   // codes: 16-B chunk t & 7 of row (t >> 3) + 64 it
-  f32x4_t xv;              // X[t >> 5][4 (t & 31) .. +3]
-  float sc;                // block scale of k row 64 (wave >> 2) + lane
+  u32x4_t xr;              // X[t >> 5][4 (t & 31) .. +3] (bf16: first 8 bytes)
+  int qv;                  // int8 block scale of k row 64 (wave >> 2) + lane
+  float s2;                // its group scale
 };
 
 // X[16 x kSub] of rows kb.. to registers: thread t -> row t >> 5, k run
 // 4 (t & 31) .. +3 (rows >= M read as zero through the descriptor range).
 template <bool kX16>
-__device__ __forceinline__ f32x4_t load_x4(__amdgpu_buffer_rsrc_t rX, int64_t K, int64_t kb) {
+__device__ __forceinline__ u32x4_t load_x4(__amdgpu_buffer_rsrc_t rX, int64_t K, int64_t kb) {
   const int t = threadIdx.x;
   constexpr int esx = kX16 ? 2 : 4;
   const uint32_t off = uint32_t((int64_t(t >> 5) * K + kb + 4 * (t & 31)) * esx);
   if constexpr (kX16) {
     const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rX, off, 0, 0));
-    return f32x4_t{bf16_lo_to_f32(v[0]), bf16_hi_to_f32(v[0]), bf16_lo_to_f32(v[1]), bf16_hi_to_f32(v[1])};
+    return u32x4_t{v[0], v[1], 0u, 0u};
   } else {
-    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
   }
 }
 
-__device__ __forceinline__ void store_x4(float (*xs)[kXPitchS], f32x4_t v, int64_t kb, int64_t kend) {
+template <bool kX16>
+__device__ __forceinline__ void store_x4(float (*xs)[kXPitchS], u32x4_t v, int64_t kb, int64_t kend) {
   const int t = threadIdx.x;
+  f32x4_t f;
+  if constexpr (kX16)
+    f = f32x4_t{bf16_lo_to_f32(v[0]), bf16_hi_to_f32(v[0]), bf16_lo_to_f32(v[1]), bf16_hi_to_f32(v[1])};
+  else
+    f = __builtin_bit_cast(f32x4_t, v);
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  *reinterpret_cast<f32x4_t *>(&xs[t >> 5][4 * (t & 31)]) = (kb + 4 * (t & 31) < kend) ? v : zero4;
+  *reinterpret_cast<f32x4_t *>(&xs[t >> 5][4 * (t & 31)]) = (kb + 4 * (t & 31) < kend) ? f : zero4;
 }
 
 // The X . A workgroups (slice index == number of code slices): X[16 x kSub]
@@ -125,7 +135,7 @@ __device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int6
   f32x4_t xacc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t kb = kbeg; kb < kend; kb += kSub) {
     const int rows = int(min64(kSub, kend - kb));
-    const f32x4_t xv = load_x4<kX16>(rX, a.K, kb);
+    const u32x4_t xv = load_x4<kX16>(rX, a.K, kb);
     float av[kSub / 8];      // A rows (t >> 6) + 8 u, column lane
 #pragma unroll
     for (int u = 0; u < kSub / 8; ++u) {
@@ -135,7 +145,7 @@ __device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int6
       else
         av[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA, off, 0, 0));
     }
-    store_x4(xs, xv, kb, kend);
+    store_x4<kX16>(xs, xv, kb, kend);
 #pragma unroll
     for (int u = 0; u < kSub / 8; ++u) {
       const int kk = (t >> 6) + 8 * u;
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
   const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
       (void *)a.gscale, (short)0, clamp_records((a.K * nblk + 255) / 256 * 4), kBufFlags);
 
-  auto load_stage = [&](int64_t kb, Stage &S) {
+  auto load_stage = [&](int64_t kb, Stage<kX16> &S) {
     // the workgroup's 128-B segment of 8 rows per load instruction (whole
     // lines); rows past the chunk read as zero
 #pragma unroll
@@ -237,18 +247,17 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
       const uint32_t off = uint32_t((kb - kbeg + row) * half_n) + 16u * uint32_t(t & 7);
       S.cv[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 2));
     }
-    S.xv = load_x4<kX16>(rX, a.K, kb);
+    S.xr = load_x4<kX16>(rX, a.K, kb);
     const uint32_t b = uint32_t((kb + 64 * kh + lane) * nblk + blk);
-    const int8_t qv = int8_t(__builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0));
-    const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, (b >> 8) * 4u, 0, 0));
-    S.sc = float(qv) * s2;
+    S.qv = int(__builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0));
+    S.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, (b >> 8) * 4u, 0, 0));
   };
 
   f32x4_t acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  Stage S;
+  Stage<kX16> S;
   load_stage(kbeg, S);
   for (int64_t kb = kbeg; kb < kend; kb += kSub) {
     const int rows = int(min64(kSub, kend - kb));        // 64 or 128
@@ -260,8 +269,8 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
       *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{S.cv[it][0], S.cv[it][1]};
       *reinterpret_cast<u32x2_t *>(dst + 8) = u32x2_t{S.cv[it][2], S.cv[it][3]};
     }
-    store_x4(xs, S.xv, kb, kend);
-    cs[bc][64 * kh + lane] = (blk_ok && 64 * kh + lane < rows) ? S.sc : 0.0f;
+    store_x4<kX16>(xs, S.xr, kb, kend);
+    cs[bc][64 * kh + lane] = (blk_ok && 64 * kh + lane < rows) ? float(int8_t(S.qv)) * S.s2 : 0.0f;
     __syncthreads();
     // ---- the next sub-chunk's loads fly while this one is multiplied
     if (kb + kSub < kend) load_stage(kb + kSub, S);
