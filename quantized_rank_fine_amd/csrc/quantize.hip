@@ -43,7 +43,6 @@ constexpr int kBlocksPerGroup = 256;
 constexpr int kSteps = 8;                 // load steps per wavefront, 8 blocks each
 constexpr int32_t kBufFlags = 0x00020000;
 constexpr int kNT = 2;                     // cache policy of the weight loads: non-temporal
-constexpr int64_t kStreamGrid = 1 << 30;  // above this many groups, walk them with a fixed grid
 
 __device__ __forceinline__ uint32_t bucket_of(float x) {
   return (__float_as_uint(x + 3.0f) >> 17) & uint32_t(kBuckets - 1);
@@ -137,7 +136,7 @@ __device__ __forceinline__ void encode_group(const f32x4_t (&v)[kSteps][2], cons
 }
 
 // double quantization of group g's 256 block scales (0 for padding blocks);
-// sc_blk must be complete (barrier before), and is free again on return
+// sc_blk must be complete (barrier before)
 __device__ __forceinline__ void double_quantize(const float *sc_blk, float *sred, int nb, int64_t g,
                                                 int8_t *__restrict__ qscale,
                                                 float *__restrict__ gscale) {
@@ -159,27 +158,24 @@ __device__ __forceinline__ void double_quantize(const float *sc_blk, float *sred
     qscale[g * kBlocksPerGroup + t] = (int8_t)q;
   }
   if (t == 0) gscale[g] = s2;
-  __syncthreads();
 }
 
-// kStream: the workgroup walks groups blockIdx.x, + gridDim.x, ... and loads
-// the next group while it encodes the current one.
-template <bool kStream>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const float *__restrict__ W0, uint8_t *__restrict__ codes, int8_t *__restrict__ qscale,
-    float *__restrict__ gscale, int64_t nblocks, int64_t ngroups, QuantConsts qc) {
+    float *__restrict__ gscale, int64_t nblocks, QuantConsts qc) {
   __shared__ BucketEntry lut[kBuckets];
   __shared__ float sc_blk[kBlocksPerGroup];
   __shared__ float sred[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint16_t stage[kThreads / 64][1024];   // 2 KiB per wavefront
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int k = lane & 7;
   const int bl0 = wave * 64 + (lane >> 3);      // block (within the group) of step 0
   const uint32_t vw = uint32_t(bl0 * 256 + 16 * k);
 
-  int64_t g = blockIdx.x;
-  GroupRefs cur = group_refs(W0, codes, nblocks, g);
+  const int64_t g = blockIdx.x;
+  const GroupRefs cur = group_refs(W0, codes, nblocks, g);
   BucketEntry own = {0.0f, 0u};
   if (t < kBuckets) own = qc.bucket[t];
   __builtin_amdgcn_sched_barrier(0);            // table read ahead of the weight loads
@@ -187,28 +183,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   load_group(cur.w, vw, v);
   if (t < kBuckets) lut[t] = own;
   __syncthreads();
-
-  for (;;) {
-    const int64_t gn = g + gridDim.x;
-    const bool more = kStream && gn < ngroups;
-    GroupRefs nxt = cur;
-    f32x4_t vn[kSteps][2];
-    if (more) {
-      nxt = group_refs(W0, codes, nblocks, gn);
-      load_group(nxt.w, vw, vn);
-    }
-    encode_group(v, lut, sc_blk, stage[wave], bl0, cur.c);
-    __syncthreads();
-    double_quantize(sc_blk, sred, cur.nb, g, qscale, gscale);
-    if (!more) break;
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      v[j][0] = vn[j][0];
-      v[j][1] = vn[j][1];
-    }
-    cur = nxt;
-    g = gn;
-  }
+  encode_group(v, lut, sc_blk, stage[wave], bl0, cur.c);
+  __syncthreads();
+  double_quantize(sc_blk, sred, cur.nb, g, qscale, gscale);
 }
 
 }  // namespace
@@ -218,13 +195,8 @@ hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale, floa
   const int64_t groups = (nblocks + kBlocksPerGroup - 1) / kBlocksPerGroup;
   if (groups == 0) return hipSuccess;
   if (!tables().quant.ok) return hipErrorInvalidValue;
-  if (groups > kStreamGrid) {
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)kStreamGrid), dim3(kThreads), 0, s, W0,
-                       codes, qscale, gscale, nblocks, groups, tables().quant);
-  } else {
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)groups), dim3(kThreads), 0, s, W0,
-                       codes, qscale, gscale, nblocks, groups, tables().quant);
-  }
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W0, codes,
+                     qscale, gscale, nblocks, tables().quant);
   return hipGetLastError();
 }
 
