@@ -57,10 +57,13 @@ constexpr int kSBytes = 1024;            // scales (512 B used)
 constexpr int kStageBytes = kXBytes + kCBytes + kSBytes;
 constexpr int kRingBytes = kStages * kStageBytes;  // 148 KiB
 // Forward: per-wavefront expansion scratch after the ring, 16 k rows x 64
-// columns of bf16 with a 160-B row pitch (conflict-free transposed reads).
-constexpr int kXPitch = 80;                          // elements
-constexpr int kScratchBytes = 16 * kXPitch * 2;      // 2560 B per wavefront
-constexpr int kLdsBytes = kRingBytes + 4 * kScratchBytes;   // 158 KiB
+// columns of bf16 with a 176-B (44-dword) row pitch: the expansion's 16-B
+// writes hit every LDS bank exactly 4 times per instruction (the minimum) and
+// the transposed reads at most 3 times (minimum 2).
+constexpr int kXPitch = 88;                          // elements
+constexpr int kScratchBytes = 16 * kXPitch * 2;      // 2816 B per wavefront
+constexpr int kLdsBytes = kRingBytes + 4 * kScratchBytes;   // 159 KiB
+static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 constexpr uint32_t kBufFlags = 0x00020000u;
 constexpr int kLoadsPerTile = 10;        // per wavefront: 8 X + 1 code + 1 scale
 
