@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
 
 int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N) {
   const int64_t slices = (N + kSliceN - 1) / kSliceN;
-  const int64_t target = M <= 4 ? 512 : (M <= 8 ? 256 : 128);
+  const int64_t target = M <= 4 ? 512 : 256;
   int64_t ks = (target + slices - 1) / slices;
   ks = ks < 1 ? 1 : (ks > K / 64 ? K / 64 : ks);
   return ((K + ks - 1) / ks + 63) / 64 * 64;
