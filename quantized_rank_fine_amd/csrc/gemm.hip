@@ -509,9 +509,35 @@ __device__ __forceinline__ u32x4_t load_adapter8(const AdapterRef &q, int64_t n,
   return u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
 }
 
+// Operands of the first 16 rank indices of the rank-r term, loaded when the
+// kernel starts (independent of the K loop) so that the epilogue does not
+// wait for them: p[i] = P16 rows m0 + 32 i + l32, ranks r0 + 8 h2 .. +7;
+// qb[b] = adapter rows nw + 32 b + l32, the same ranks.
+struct RankOps {
+  u32x4_t p[8], qb[2];
+};
+
+__device__ __forceinline__ void load_rank_ops(RankOps &o, const uint16_t *__restrict__ P16, int ldp,
+                                              const AdapterRef &q, int r0, int64_t M, int64_t N,
+                                              int64_t m0, int64_t nw) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t n = nw + 32 * b + l32;
+    o.qb[b] = (n < N) ? load_adapter8(q, n, r0 + 8 * h2) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + 32 * i + l32;
+    o.p[i] = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * ldp + r0 + 8 * h2)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
 // Epilogue.  The rank-r term P16 . Q^T (P16 bf16 [M x ldp], zero-padded
 // columns r..ldp-1; Q the adapter factor, rows indexed by the output column)
-// is added by the k-half-0 wavefronts only, so it enters every output once.
+// is added by the k-half-0 wavefronts only, so it enters every output once
+// (ranks 0..15 from operands loaded at kernel start).
 // The two k halves of a column half are then summed through LDS in four
 // rounds of two row blocks: every wavefront writes its partials of row blocks
 // 2 rnd, 2 rnd + 1 (64 KiB in all), reads back both halves of column block
@@ -521,7 +547,7 @@ __device__ __forceinline__ u32x4_t load_adapter8(const AdapterRef &q, int64_t n,
 // into the LDS writes.  LDS layout per fragment: 4 chunks of 1 KiB, chunk c =
 // registers 4c..4c+3 of every lane (16 B per lane, contiguous across lanes).
 template <bool kOutBf16>
-__device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
+__device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem, const RankOps &ro,
                                          const uint16_t *__restrict__ P16, int ldp,
                                          const AdapterRef q, int64_t M,
                                          int64_t N, int64_t m0, int64_t n0, void *__restrict__ Y) {
@@ -531,22 +557,19 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem,
   const int l32 = lane & 31, h2 = lane >> 5;
   const int64_t nw = n0 + 64 * ch;
 
-  if (kh == 0) {
-    for (int r0 = 0; r0 < q.r; r0 += 16) {
-      u32x4_t qb[2];
+  if (kh == 0 && q.r > 0) {
+    // ranks 0..15 from the operands loaded at kernel start, the rest here
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int64_t n = nw + 32 * b + l32;
-        qb[b] = (n < N) ? load_adapter8(q, n, r0 + 8 * h2) : u32x4_t{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + 32 * i + l32;
-        const u32x4_t p = (m < M) ? *reinterpret_cast<const u32x4_t *>(P16 + m * ldp + r0 + 8 * h2)
-                                  : u32x4_t{0u, 0u, 0u, 0u};
+      for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(ro.p[i], ro.qb[b], acc[b][i]);
+    for (int r0 = 16; r0 < q.r; r0 += 16) {
+      RankOps o;
+      load_rank_ops(o, P16, ldp, q, r0, M, N, m0, nw);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(p, qb[b], acc[b][i]);
-      }
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(o.p[i], o.qb[b], acc[b][i]);
     }
   }
 
@@ -619,6 +642,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
   int mt, nt;
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
+  RankOps ro;
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 2 && bq.r > 0)  // k-half-0 wavefronts
+    load_rank_ops(ro, XA16, ldp, bq, 0, M, N, m0, n0 + 64 * ((threadIdx.x >> 6) & 1));
   f32x16_t acc[2][8];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -628,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
   // rank-r term: y += XA16 . B (B read as rows n of B^T)
-  epilogue<kOutBf16>(acc, smem, XA16, ldp, bq, M, N, m0, n0, Y);
+  epilogue<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
@@ -642,6 +668,9 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
   int mt, nt;
   tile_of(nt_count, mt, nt);
   const int64_t m0 = int64_t(mt) * BM, i0 = int64_t(nt) * BN;
+  RankOps ro;
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 2 && aq.r > 0)
+    load_rank_ops(ro, G16, ldp, aq, 0, M, IN, m0, i0 + 64 * ((threadIdx.x >> 6) & 1));
   f32x16_t acc[2][8];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -651,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<false>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
   // rank-r term: dX += G16 . A^T (A read as rows i of A)
-  epilogue<kOutBf16>(acc, smem, G16, ldp, aq, M, IN, m0, i0, dX);
+  epilogue<kOutBf16>(acc, smem, ro, G16, ldp, aq, M, IN, m0, i0, dX);
 }
 
 bool set_lds(const void *fn) {
