@@ -88,8 +88,8 @@ FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   p.off_cs = L.take(size_t(in) * (out / 64) * 4);
   if (r > 0) {
     p.rp = rank_pad32(r);
-    p.ks = rowdot_splits(M, in, r);
-    p.off_part = L.take(size_t(p.ks) * M * r * 4);
+    p.ks = xa_complete(M, in, r) ? 0 : rowdot_splits(M, in, r);
+    if (p.ks) p.off_part = L.take(size_t(p.ks) * M * r * 4);
     p.off_xa16 = L.take(size_t(M) * p.rp * 2);
   }
   p.total = L.o;
@@ -110,13 +110,13 @@ BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   p.off_cs = L.take(size_t(in) * (out / 64) * 4);
   if (r > 0) {
     p.rp = rank_pad32(r);
-    p.ks_g = rowdot_splits(M, out, r);
-    p.ks_x = rowdot_splits(M, in, r);
+    p.ks_g = g_complete(M, out, r) ? 0 : rowdot_splits(M, out, r);
+    p.ks_x = xa_complete(M, in, r) ? 0 : rowdot_splits(M, in, r);
     p.ks_b = coldot_splits(M, out, r);
     p.ks_a = coldot_splits(M, in, r);
-    p.off_gpart = L.take(size_t(p.ks_g) * M * r * 4);
+    if (p.ks_g) p.off_gpart = L.take(size_t(p.ks_g) * M * r * 4);
     p.off_g16 = L.take(size_t(M) * p.rp * 2);
-    p.off_xapart = L.take(size_t(p.ks_x) * M * r * 4);
+    if (p.ks_x) p.off_xapart = L.take(size_t(p.ks_x) * M * r * 4);
     p.off_xa = L.take(size_t(M) * r * 4);
     p.off_dbpart = L.take(size_t(p.ks_b) * out * r * 4);
     p.off_dapart = L.take(size_t(p.ks_a) * in * r * 4);
@@ -220,14 +220,13 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(X, false, M * in, x16, stream));
     X16 = x16;
   }
-  // one launch: XA partials (X . A) and the GEMM's block scales
+  // one launch: X . A (complete, or split-K partials) and the GEMM's block scales
   float *cs = at<float>(ws, p.off_cs);
-  float *part = r > 0 ? at<float>(ws, p.off_part) : nullptr;
-  QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, part, wq->qscale,
-                                             wq->gscale, out, cs, stream));
-  uint16_t *XA16 = nullptr;
-  if (r > 0) {
-    XA16 = at<uint16_t>(ws, p.off_xa16);
+  float *part = p.ks > 0 ? at<float>(ws, p.off_part) : nullptr;
+  uint16_t *XA16 = r > 0 ? at<uint16_t>(ws, p.off_xa16) : nullptr;
+  QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, part, XA, XA16, p.rp,
+                                             wq->qscale, wq->gscale, out, cs, stream));
+  if (p.ks > 0) {
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(part, p.ks, M, r, XA, false, XA16, p.rp,
                                                   nullptr, 0, 0, nullptr, false, nullptr, 0,
                                                   stream));
@@ -280,32 +279,43 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
   uint16_t *G16 = nullptr;
   if (r > 0 && !XA) {
     // recompute XA = X . A into the workspace
-    float *xpart = at<float>(ws, p.off_xapart);
+    float *xpart = p.ks_x > 0 ? at<float>(ws, p.off_xapart) : nullptr;
     float *xaw = at<float>(ws, p.off_xa);
-    QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, xpart, nullptr, nullptr,
-                                               out, nullptr, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
-                                                  nullptr, 0, 0, nullptr, false, nullptr, 0,
-                                                  stream));
+    QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, xpart, xaw, nullptr, 0,
+                                               nullptr, nullptr, out, nullptr, stream));
+    if (p.ks_x > 0) {
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
+                                                    nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                    stream));
+    }
     XA = xaw;
   }
-  // one pass over dY: G = dY . B^T and dB = XA^T . dY partials, block scales
-  float *gpart = r > 0 ? at<float>(ws, p.off_gpart) : nullptr;
+  // one pass over dY: G = dY . B^T (complete, or partials), dB = XA^T . dY
+  // partials, block scales
+  float *gpart = p.ks_g > 0 ? at<float>(ws, p.off_gpart) : nullptr;
   float *dbpart = r > 0 ? at<float>(ws, p.off_dbpart) : nullptr;
-  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XA, M, out, r, gpart, dbpart,
-                                                wq->qscale, wq->gscale, in, cs, stream));
+  if (r > 0) G16 = at<uint16_t>(ws, p.off_g16);
+  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XA, M, out, r, gpart, G16, p.rp,
+                                                dbpart, wq->qscale, wq->gscale, in, cs, stream));
   if (r > 0) {
-    G16 = at<uint16_t>(ws, p.off_g16);
-    // G (bf16, zero-padded) and dB (stored [r x out]) in one launch
-    QLORA_RUN(QLORA_KERNEL_REDUCE,
-              launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b, out,
-                             dB, true, nullptr, 0, stream));
-    // dA = X^T . G
     float *dapart = at<float>(ws, p.off_dapart);
-    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
-                                                  nullptr, 0, 0, nullptr, false, nullptr, 0,
-                                                  stream));
+    if (p.ks_g > 0) {
+      // G (bf16, zero-padded) and dB (stored [r x out]) in one launch
+      QLORA_RUN(QLORA_KERNEL_REDUCE,
+                launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b,
+                               out, dB, true, nullptr, 0, stream));
+      // dA = X^T . G
+      QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
+                                                    nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                    stream));
+    } else {
+      // G is complete: dA = X^T . G, then dA and dB (stored [r x out]) in one launch
+      QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+      QLORA_RUN(QLORA_KERNEL_REDUCE,
+                launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_b, out,
+                               dB, true, nullptr, 0, stream));
+    }
   }
   if (dX) {
     QLORA_RUN(QLORA_KERNEL_DX_GEMM,

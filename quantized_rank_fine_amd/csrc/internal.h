@@ -59,21 +59,27 @@ hipError_t launch_convert_to_bf16(const void *src, bool src_bf16, int64_t n,
 int64_t rowdot_splits(int64_t M, int64_t K, int64_t R);
 int64_t coldot_splits(int64_t M, int64_t K, int64_t R);
 
-// Forward prep, one launch: xa_part[ks][M][r] = partial X . A (X [M x in],
-// A [in x r], each f32 or bf16) and, if cs != nullptr, the block scales
-// cs[b][row] = q8[row][b] * s2[group] of the [in x out] weight.
+// Forward prep, one launch: the block scales cs[b][row] = q8[row][b] *
+// s2[group] of the [in x out] weight (if cs != nullptr) and X . A (X [M x in],
+// A [in x r], each f32 or bf16) -- complete into XA (fp32 [M x r]) and XA16
+// (bf16 [M x ld16], zero-padded), each optional, when xa_complete(M, in, r),
+// else as split-K partials xa_part[ks][M][r] for launch_reduce2.
+bool xa_complete(int64_t M, int64_t in, int64_t r);
 hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf16,
-                           int64_t M, int64_t in, int64_t r, float *xa_part,
-                           const int8_t *qscale, const float *gscale, int64_t out,
-                           float *cs, hipStream_t s);
+                           int64_t M, int64_t in, int64_t r, float *xa_part, float *XA,
+                           uint16_t *XA16, int64_t ld16, const int8_t *qscale,
+                           const float *gscale, int64_t out, float *cs, hipStream_t s);
 
-// Backward pass over dY, one launch: g_part[ks][M][r] = partial dY . B^T
-// (B [r x out]); db_part[ks][out][r] = partial dY^T . XA (XA fp32 [M x r]);
-// and, if cs != nullptr, the block scales as in launch_fwd_prep.
+// Backward pass over dY, one launch: G = dY . B^T (B [r x out]) -- complete
+// into G16 (bf16 [M x ldg], zero-padded) when g_complete(M, out, r), else as
+// partials g_part[ks][M][r]; db_part[ks][out][r] = partial dY^T . XA (XA fp32
+// [M x r]); and, if cs != nullptr, the block scales as in launch_fwd_prep.
+bool g_complete(int64_t M, int64_t out, int64_t r);
 hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf16,
                          const float *XA, int64_t M, int64_t out, int64_t r,
-                         float *g_part, float *db_part, const int8_t *qscale,
-                         const float *gscale, int64_t in, float *cs, hipStream_t s);
+                         float *g_part, uint16_t *G16, int64_t ldg, float *db_part,
+                         const int8_t *qscale, const float *gscale, int64_t in, float *cs,
+                         hipStream_t s);
 
 // Backward pass over X: da_part[ks][in][r] = partial X^T . G with G given as
 // G16 bf16 [M x ldg].

@@ -32,6 +32,7 @@ namespace {
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+constexpr int32_t kBufFlags = 0x00020000;   // raw buffer descriptor word 3
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
@@ -101,9 +102,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 // cs[b][row] = q8[row * NB + b] * s2[(row * NB + b) >> 8]  (fp32 product), the
 // per-block scales of a quantized [rows x 64 NB] weight laid out one row per
 // 64-wide block column (the layout the fused GEMMs stream).  A thread owns one
-// row and 16 consecutive blocks of it: one 16-B read of q8, 16 stores that are
-// coalesced across the wavefront (consecutive rows).  Role of a merged launch:
-// workgroups wg = 0 .. nwg-1 of it, nwg = scales_workgroups(rows, NB).
+// row and 16 consecutive blocks of it: one 16-B read of q8, the (at most two)
+// second-level scales those 16 blocks use, 16 stores that are coalesced across
+// the wavefront (consecutive rows).  Role of a merged launch: workgroups
+// wg = 0 .. scales_workgroups(rows, NB) - 1, placed first in the grid so that
+// their short dependent chain starts with the launch.
 struct ScalesArgs {
   const int8_t *q8;
   const float *s2;
@@ -117,27 +120,32 @@ __host__ __device__ inline int64_t scales_workgroups(int64_t rows, int64_t NB) {
   return ((rows + 255) / 256) * ((NB + kScaleSpan - 1) / kScaleSpan);
 }
 
-__device__ __forceinline__ void scales_role(const ScalesArgs &a, int64_t wg, int64_t nwg) {
-  (void)nwg;
+__device__ __forceinline__ void scales_role(const ScalesArgs &a, int64_t wg) {
   const int64_t nspan = (a.NB + kScaleSpan - 1) / kScaleSpan;
   const int64_t row = (wg / nspan) * 256 + threadIdx.x;
   const int64_t b0 = (wg % nspan) * kScaleSpan;
   if (row >= a.rows) return;
-  const int8_t *q = a.q8 + row * a.NB + b0;
+  const int64_t f0 = row * a.NB + b0;                          // flat block index of b0
+  const int nb = int(min64(kScaleSpan, a.NB - b0));            // blocks of this thread
+  const float s2a = a.s2[f0 >> 8], s2b = a.s2[(f0 + nb - 1) >> 8];   // at most two groups
   int8_t v[kScaleSpan];
-  if (b0 + kScaleSpan <= a.NB && ((reinterpret_cast<uintptr_t>(q) & 15u) == 0)) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(q);
+  if (a.NB % kScaleSpan == 0) {
+    // every span is whole and 16-B aligned (q8 is)
+    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(a.q8 + f0);
 #pragma unroll
     for (int e = 0; e < kScaleSpan; ++e) v[e] = int8_t(w[e >> 2] >> (8 * (e & 3)));
   } else {
+    // byte loads, all issued (indices past the span repeat its last block)
 #pragma unroll
-    for (int e = 0; e < kScaleSpan; ++e) v[e] = (b0 + e < a.NB) ? q[e] : int8_t(0);
+    for (int e = 0; e < kScaleSpan; ++e) v[e] = a.q8[f0 + (e < nb ? e : nb - 1)];
   }
+  float c[kScaleSpan];
 #pragma unroll
-  for (int e = 0; e < kScaleSpan; ++e) {
-    const int64_t b = b0 + e;
-    if (b < a.NB) a.cs[b * a.rows + row] = float(v[e]) * a.s2[(row * a.NB + b) >> 8];
-  }
+  for (int e = 0; e < kScaleSpan; ++e)
+    c[e] = float(v[e]) * (((f0 + e) >> 8) == (f0 >> 8) ? s2a : s2b);
+#pragma unroll
+  for (int e = 0; e < kScaleSpan; ++e)
+    if (e < nb) a.cs[(b0 + e) * a.rows + row] = c[e];
 }
 
 // ------------------------------------------------------------------ rowdot
@@ -279,6 +287,208 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
         const int64_t m = m0 + wave * 16 + 4 * h + q;
         if (m < a.M && j < R) out[m * R + j] = acc[st][q];
       }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- rowfull
+//
+// C[M x R] = P[M x K] . Q for R <= 32 at large M, without split-K partials:
+// a workgroup owns kRows (8 or 16) rows of P and the whole K range, cut into
+// four contiguous runs of 32-wide k steps, one per wavefront.  A wavefront
+// keeps the loads of its next batch of kFullSteps steps in flight while it
+// multiplies the current one: P rows go straight into the MFMA A operand
+// (kept raw until use), Q either straight into the B operand (Qt [R x K],
+// rows contiguous along k) or, for Q [K x R], through the wavefront's own LDS
+// area (loaded as whole rows), read back transposed.  The four partial products are then summed in
+// wavefront order through LDS and written as fp32 and/or zero-padded bf16.
+// Rows past M, lanes past kRows and steps past a wavefront's run read zero
+// through the range check of raw buffer loads (no branches around loads).
+
+constexpr int kFullSteps = 8;                 // 32-wide k steps per batch
+constexpr int kFullMinM = 1024;               // below this, split-K partials
+
+struct RowfullArgs {
+  const void *P;      // [M x K]
+  const void *Q;      // Qt [R x K] (kQRows) or Q [K x R], R % 8 == 0 (kQFast)
+  int64_t M, K;
+  int R;
+  int rows;           // rows per workgroup: 8 or 16
+  float *out;         // fp32 [M x R], optional
+  uint16_t *out16;    // bf16 [M x ld16], zero padding columns R..ld16-1, optional
+  int64_t ld16;
+};
+
+__host__ __device__ inline int32_t clamp_records(int64_t bytes) {
+  return bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : int32_t(bytes));
+}
+
+// 8 consecutive elements as loaded (bf16: one 16-B piece; fp32: two), and
+// their conversion to the bf16x8 MFMA operand at the point of use.
+template <bool kBf16>
+struct Raw8 {
+  u32x4_t v[kBf16 ? 1 : 2];
+};
+
+template <bool kBf16>
+__device__ __forceinline__ Raw8<kBf16> buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  Raw8<kBf16> x;
+  x.v[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  if constexpr (!kBf16)
+    x.v[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+  return x;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ u32x4_t as_bf16x8_op(const Raw8<kBf16> &x) {
+  if constexpr (kBf16) {
+    return x.v[0];
+  } else {
+    const f32x4_t a = __builtin_bit_cast(f32x4_t, x.v[0]), b = __builtin_bit_cast(f32x4_t, x.v[1]);
+    return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                   pack_bf16x2(b[2], b[3])};
+  }
+}
+
+// Per-wavefront Q staging of one batch (kQFast only): [kFullSteps * 32][RP],
+// read transposed.
+template <int kQMode, int kRT>
+__host__ __device__ constexpr size_t rowfull_stage_bytes() {
+  return kQMode == kQFast ? size_t(kFullSteps) * 32 * (16 * kRT) * 2 : 0;
+}
+
+template <int kQMode, int kRT>
+__host__ __device__ constexpr size_t rowfull_lds_bytes() {
+  return 4 * rowfull_stage_bytes<kQMode, kRT>() + size_t(4) * kRT * 16 * 16 * 4;
+}
+
+template <bool kPbf16, int kQMode, bool kQbf16, int kRT>
+__device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, unsigned char *smem) {
+  constexpr int kRP = 16 * kRT;
+  constexpr int pes = kPbf16 ? 2 : 4, qes = kQbf16 ? 2 : 4;
+  constexpr int kCPR = kRP / 8;                                  // 16-B chunks per staged Q row
+  // 16-B Q chunks per lane and batch: kQFast -- staging chunks; kQRows --
+  // the B operands of every step and rank tile
+  constexpr int kQN = kQMode == kQFast ? kFullSteps * 32 * kCPR / 64 : kFullSteps * kRT;
+  constexpr size_t kStageBytes = rowfull_stage_bytes<kQMode, kRT>();   // per wavefront
+  static_assert(kQMode == kQRows || kQMode == kQFast, "rowfull Q form");
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int i16 = lane & 15, h = lane >> 4;
+  const int64_t K = a.K;
+  const int R = a.R;
+  const int64_t m0 = wg * a.rows;
+  const int nrows = int(min64(a.rows, a.M - m0));
+
+  // P rows m0 .. m0 + nrows - 1; lanes past them address the first byte
+  // past the range (every later k offset stays out of range too)
+  const uint32_t p_rec = uint32_t(clamp_records(int64_t(nrows) * K * pes));
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(static_cast<const char *>(a.P) + m0 * K * pes), (short)0, int32_t(p_rec), kBufFlags);
+  const uint32_t prow = i16 < nrows ? uint32_t(i16 * K * pes) : p_rec;
+  const uint32_t q_rec = uint32_t(clamp_records(int64_t(R) * K * qes));
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void *)a.Q, (short)0,
+                                                                      int32_t(q_rec), kBufFlags);
+  uint32_t qrow[kRT];                          // kQRows: row j = 16 st + i16 of Qt
+#pragma unroll
+  for (int st = 0; st < kRT; ++st) {
+    const int j = 16 * st + i16;
+    qrow[st] = j < R ? uint32_t(j * K * qes) : q_rec;
+  }
+
+  const int ns = int(K / 32);
+  const int s0 = wave * ns / 4, s1 = (wave + 1) * ns / 4;
+  const int nb = (s1 - s0 + kFullSteps - 1) / kFullSteps;
+  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + wave * kStageBytes);
+
+  Raw8<kPbf16> xb[2][kFullSteps];
+  Raw8<kQbf16> qb[2][kQN];
+  auto load_batch = [&](int b, Raw8<kPbf16> (&xv)[kFullSteps], Raw8<kQbf16> (&qv)[kQN]) {
+#pragma unroll
+    for (int u = 0; u < kFullSteps; ++u) {
+      const int st = s0 + kFullSteps * b + u;
+      const bool in = st < s1;
+      xv[u] = buf_load8<kPbf16>(rP, in ? prow + uint32_t((32 * st + 8 * h) * pes) : p_rec);
+      if constexpr (kQMode == kQRows) {
+        // the B operand straight from the rows of Qt
+#pragma unroll
+        for (int r = 0; r < kRT; ++r)
+          qv[u * kRT + r] = buf_load8<kQbf16>(rQ, in ? qrow[r] + uint32_t((32 * st + 8 * h) * qes) : q_rec);
+      }
+    }
+    if constexpr (kQMode == kQFast) {
+      // rows kb .. kb + 255 of Q [K x R], 16-B chunks in row order
+      const int64_t kb = int64_t(32) * (s0 + kFullSteps * b), ke = int64_t(32) * s1;
+#pragma unroll
+      for (int u = 0; u < kQN; ++u) {
+        const int cid = lane + 64 * u, kk = cid / kCPR, c = cid % kCPR;
+        const int64_t k = kb + kk;
+        qv[u] = buf_load8<kQbf16>(rQ, (k < ke && 8 * c < R) ? uint32_t((k * R + 8 * c) * qes) : q_rec);
+      }
+    }
+  };
+
+  f32x4_t acc[kRT];
+#pragma unroll
+  for (int r = 0; r < kRT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute_batch = [&](const Raw8<kPbf16> (&xv)[kFullSteps], const Raw8<kQbf16> (&qv)[kQN]) {
+    if constexpr (kQMode == kQFast) {
+      // stage Q rows [kFullSteps * 32][kRP] in this wavefront's area (LDS
+      // operations of one wavefront complete in order, so the transposed
+      // reads below see these writes and the next batch's writes follow them)
+#pragma unroll
+      for (int u = 0; u < kQN; ++u) {
+        const int cid = lane + 64 * u, kk = cid / kCPR, c = cid % kCPR;
+        *reinterpret_cast<u32x4_t *>(sQ + kk * kRP + 8 * c) = as_bf16x8_op<kQbf16>(qv[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFullSteps; ++u) {
+      const u32x4_t av = as_bf16x8_op<kPbf16>(xv[u]);
+#pragma unroll
+      for (int r = 0; r < kRT; ++r) {
+        u32x4_t bv;
+        if constexpr (kQMode == kQFast)
+          bv = lds_col8(sQ, kRP, 32 * u, 16 * r);
+        else
+          bv = as_bf16x8_op<kQbf16>(qv[u * kRT + r]);
+        acc[r] = mfma16x16x32(av, bv, acc[r]);
+      }
+    }
+  };
+
+  // two register sets, alternating; the loads of batch b + 1 are issued
+  // before batch b is multiplied (batches past nb read zero)
+  load_batch(0, xb[0], qb[0]);
+  for (int b = 0; b < nb; b += 2) {
+    load_batch(b + 1, xb[1], qb[1]);
+    compute_batch(xb[0], qb[0]);
+    if (b + 1 >= nb) break;
+    load_batch(b + 2, xb[0], qb[0]);
+    compute_batch(xb[1], qb[1]);
+  }
+
+  // fixed-order sum of the four wavefronts' products
+  float *red = reinterpret_cast<float *>(smem + 4 * kStageBytes);
+#pragma unroll
+  for (int r = 0; r < kRT; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[((wave * kRT + r) * 16 + 4 * h + e) * 16 + i16] = acc[r][e];
+  __syncthreads();
+  const int L = a.out16 ? int(a.ld16) : R;
+  for (int e = t; e < nrows * L; e += 256) {
+    const int row = e / L, j = e - row * L;
+    const int64_t m = m0 + row;
+    if (j < R) {
+      const int r = j >> 4, jj = j & 15;
+      float v = red[((0 * kRT + r) * 16 + row) * 16 + jj];
+      v += red[((1 * kRT + r) * 16 + row) * 16 + jj];
+      v += red[((2 * kRT + r) * 16 + row) * 16 + jj];
+      v += red[((3 * kRT + r) * 16 + row) * 16 + jj];
+      if (a.out) a.out[m * R + j] = v;
+      if (a.out16) a.out16[m * a.ld16 + j] = f32_to_bf16_bits(v);
+    } else {
+      a.out16[m * a.ld16 + j] = 0;
     }
   }
 }
@@ -454,24 +664,61 @@ struct ReduceArgs {
   int64_t ld_bf16;
 };
 
+// Vector form (R % 4 == 0): a thread owns 4 consecutive elements of one row
+// and keeps up to kRedBatch 16-B partial loads in flight, so that a pass over
+// ks partials costs ceil(ks / kRedBatch) load round trips.
+constexpr int kRedBatch = 16;
+
 __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int64_t nwg) {
   const int64_t n = a.rows * a.R;
-  for (int64_t i = wg * 256 + threadIdx.x; i < n; i += nwg * 256) {
-    // partials are loaded 8 at a time (independent loads in flight) and
-    // summed in k order
-    float s = 0.0f;
-    int64_t k = 0;
-    for (; k + 8 <= a.ks; k += 8) {
-      float v[8];
+  if (a.R % 4 == 0) {
+    const int64_t n4 = n / 4;
+    for (int64_t i4 = wg * 256 + threadIdx.x; i4 < n4; i4 += nwg * 256) {
+      const f32x4_t *p = reinterpret_cast<const f32x4_t *>(a.part) + i4;
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+      for (int64_t k = 0; k < a.ks; k += kRedBatch) {
+        f32x4_t v[kRedBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.part[(k + u) * n + i];
+        for (int u = 0; u < kRedBatch; ++u)
+          v[u] = (k + u < a.ks) ? p[(k + u) * n4] : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < kRedBatch; ++u)
+          if (k + u < a.ks) s += v[u];     // k order
+      }
+      const int64_t i = 4 * i4, rr = i / a.R, j = i - rr * a.R;
+      if (a.out) {
+        if (a.transpose_out) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a.out[(j + e) * a.rows + rr] = s[e];
+        } else {
+          *reinterpret_cast<f32x4_t *>(a.out + i) = s;
+        }
+      }
+      if (a.out_bf16) {
+        uint16_t *d = a.out_bf16 + rr * a.ld_bf16 + j;
+        const uint32_t lo = uint32_t(f32_to_bf16_bits(s[0])) | (uint32_t(f32_to_bf16_bits(s[1])) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_bits(s[2])) | (uint32_t(f32_to_bf16_bits(s[3])) << 16);
+        *reinterpret_cast<u32x2_t *>(d) = u32x2_t{lo, hi};
+      }
     }
-    for (; k < a.ks; ++k) s += a.part[k * n + i];
-    const int64_t rr = i / a.R, j = i - rr * a.R;
-    if (a.out) a.out[a.transpose_out ? j * a.rows + rr : i] = s;
-    if (a.out_bf16) a.out_bf16[rr * a.ld_bf16 + j] = f32_to_bf16_bits(s);
+  } else {
+    for (int64_t i = wg * 256 + threadIdx.x; i < n; i += nwg * 256) {
+      // partials are loaded 8 at a time (independent loads in flight) and
+      // summed in k order
+      float s = 0.0f;
+      int64_t k = 0;
+      for (; k + 8 <= a.ks; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = a.part[(k + u) * n + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      for (; k < a.ks; ++k) s += a.part[k * n + i];
+      const int64_t rr = i / a.R, j = i - rr * a.R;
+      if (a.out) a.out[a.transpose_out ? j * a.rows + rr : i] = s;
+      if (a.out_bf16) a.out_bf16[rr * a.ld_bf16 + j] = f32_to_bf16_bits(s);
+    }
   }
   if (a.out_bf16 && a.ld_bf16 > a.R) {   // zero padding columns R..ld_bf16-1
     const int64_t pad = a.ld_bf16 - a.R, np = a.rows * pad;
@@ -484,33 +731,61 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
 
 // ------------------------------------------------------------------ kernels
 
-// XA partials (rowdot with Q = A [in x r]) on workgroups [0, n_row), block
-// scales on [n_row, grid).  Either role may be empty.
+// Block scales on workgroups [0, n_sc), XA partials (rowdot with Q = A
+// [in x r]) on [n_sc, grid).  Either role may be empty.
 template <bool kXbf16, bool kAbf16, bool kWide, int kQMode>
-__global__ __launch_bounds__(256) void fwd_prep_kernel(RowdotArgs ra, int64_t n_row,
+__global__ __launch_bounds__(256) void fwd_prep_kernel(RowdotArgs ra, int64_t n_sc,
                                                        ScalesArgs sa) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t wg = blockIdx.x;
-  if (wg < n_row)
-    rowdot_role<kXbf16, kQMode, kAbf16, kWide>(ra, wg, smem);
+  if (wg < n_sc)
+    scales_role(sa, wg);
   else
-    scales_role(sa, wg - n_row, int64_t(gridDim.x) - n_row);
+    rowdot_role<kXbf16, kQMode, kAbf16, kWide>(ra, wg - n_sc, smem);
 }
 
-// One pass over dY: G partials (rowdot with Qt = B [r x out]) on [0, n_row),
-// dB partials (coldot with Q = XA fp32 [M x r]) on [n_row, n_row + n_col),
-// block scales on the rest.
-template <bool kDYbf16, bool kBbf16, bool kWide, bool kQFastC>
-__global__ __launch_bounds__(256) void bwd_dy_kernel(RowdotArgs ra, int64_t n_row, ColdotArgs ca,
-                                                     int64_t n_col, ScalesArgs sa) {
+// Block scales on [0, n_sc), XA = X . A complete (rowfull with Q = A
+// [in x r], r % 8 == 0) on the rest.
+template <bool kXbf16, bool kAbf16, int kRT>
+__global__ __launch_bounds__(256) void fwd_full_kernel(RowfullArgs ra, int64_t n_sc, ScalesArgs sa) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t wg = blockIdx.x;
-  if (wg < n_row)
-    rowdot_role<kDYbf16, kQRows, kBbf16, kWide>(ra, wg, smem);
-  else if (wg < n_row + n_col)
-    coldot_role<kDYbf16, false, kWide, kQFastC>(ca, wg - n_row, smem);
+  if (wg < n_sc)
+    scales_role(sa, wg);
   else
-    scales_role(sa, wg - n_row - n_col, int64_t(gridDim.x) - n_row - n_col);
+    rowfull_role<kXbf16, kQFast, kAbf16, kRT>(ra, wg - n_sc, smem);
+}
+
+// One pass over dY with G complete: block scales on [0, n_sc), G = dY . B^T
+// (rowfull with Qt = B [r x out]) on [n_sc, n_sc + n_row), dB partials
+// (coldot with Q = XA fp32 [M x r]) on the rest.
+template <bool kDYbf16, bool kBbf16, int kRT, bool kQFastC>
+__global__ __launch_bounds__(256) void dy_full_kernel(RowfullArgs ra, int64_t n_row, ColdotArgs ca,
+                                                      int64_t n_sc, ScalesArgs sa) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t wg = blockIdx.x;
+  if (wg < n_sc)
+    scales_role(sa, wg);
+  else if (wg < n_sc + n_row)
+    rowfull_role<kDYbf16, kQRows, kBbf16, kRT>(ra, wg - n_sc, smem);
+  else
+    coldot_role<kDYbf16, false, true, kQFastC>(ca, wg - n_sc - n_row, smem);
+}
+
+// One pass over dY: block scales on [0, n_sc), G partials (rowdot with
+// Qt = B [r x out]) on [n_sc, n_sc + n_row), dB partials (coldot with Q = XA
+// fp32 [M x r]) on the rest.
+template <bool kDYbf16, bool kBbf16, bool kWide, bool kQFastC>
+__global__ __launch_bounds__(256) void bwd_dy_kernel(RowdotArgs ra, int64_t n_row, ColdotArgs ca,
+                                                     int64_t n_sc, ScalesArgs sa) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t wg = blockIdx.x;
+  if (wg < n_sc)
+    scales_role(sa, wg);
+  else if (wg < n_sc + n_row)
+    rowdot_role<kDYbf16, kQRows, kBbf16, kWide>(ra, wg - n_sc, smem);
+  else
+    coldot_role<kDYbf16, false, kWide, kQFastC>(ca, wg - n_sc - n_row, smem);
 }
 
 // One pass over X: dA partials (coldot with Q = G16 bf16 [M x rp], zero-padded).
@@ -550,7 +825,7 @@ int64_t rowdot_chunk(int64_t M, int64_t K, int64_t R) {
 int64_t coldot_chunk(int64_t M, int64_t K, int64_t R) {
   const int64_t ct = (K + coldot_tn(int(R)) - 1) / coldot_tn(int(R));
   const int64_t mt = (M + 63) / 64;
-  int64_t ks = (512 + ct - 1) / ct;
+  int64_t ks = (256 + ct - 1) / ct;
   if (ks < 1) ks = 1;
   if (ks > mt) ks = mt;
   const int64_t per = (mt + ks - 1) / ks;
@@ -584,7 +859,29 @@ size_t coldot_lds(int64_t R) {
   return size_t(64) * coldot_pitch(coldot_tn(int(R))) * 2 + size_t(rank_pad16(int(R))) * 64 * 2;
 }
 
+int rowfull_rows(int64_t M) { return M >= 4096 ? 16 : 8; }
+
+// rowfull applies: enough rows for a full grid, R <= 32, and every buffer
+// offset of a workgroup inside the 31-bit range of a raw buffer.
+bool rowfull_fits(int64_t M, int64_t K, int64_t R) {
+  return M >= kFullMinM && R > 0 && R <= 32 && int64_t(16) * K * 4 <= 0x7fffffff &&
+         R * K * 4 <= 0x7fffffff;
+}
+
+RowfullArgs rowfull_args(const void *P, const void *Q, int64_t M, int64_t K, int64_t R, float *out,
+                         uint16_t *out16, int64_t ld16, int64_t &nwg) {
+  RowfullArgs a;
+  a.P = P; a.Q = Q; a.M = M; a.K = K; a.R = int(R);
+  a.rows = rowfull_rows(M);
+  a.out = out; a.out16 = out16; a.ld16 = ld16;
+  nwg = (M + a.rows - 1) / a.rows;
+  return a;
+}
+
 }  // namespace
+
+bool xa_complete(int64_t M, int64_t in, int64_t r) { return r % 8 == 0 && rowfull_fits(M, in, r); }
+bool g_complete(int64_t M, int64_t out, int64_t r) { return rowfull_fits(M, out, r); }
 
 int64_t rowdot_splits(int64_t M, int64_t K, int64_t R) {
   if (M == 0) return 0;
@@ -613,21 +910,42 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf16, int64_t M,
-                           int64_t in, int64_t r, float *xa_part, const int8_t *qscale,
-                           const float *gscale, int64_t out, float *cs, hipStream_t s) {
-  int64_t n_row = 0;
-  const RowdotArgs ra = rowdot_args(X, A, M, in, r, xa_part, n_row);
+                           int64_t in, int64_t r, float *xa_part, float *XA, uint16_t *XA16,
+                           int64_t ld16, const int8_t *qscale, const float *gscale, int64_t out,
+                           float *cs, hipStream_t s) {
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
   const int64_t n_sc = cs ? scales_workgroups(in, out / 64) : 0;
+  if (r > 0 && xa_complete(M, in, r)) {
+    int64_t n_full = 0;
+    const RowfullArgs fa = rowfull_args(X, A, M, in, r, XA, XA16, ld16, n_full);
+    const dim3 grid = dim3(unsigned(n_full + n_sc));
+    const size_t lds1 = rowfull_lds_bytes<kQFast, 1>(), lds2 = rowfull_lds_bytes<kQFast, 2>();
+#define QLORA_FULL(XB, AB)                                                                      \
+  do {                                                                                          \
+    if (r <= 16)                                                                                \
+      hipLaunchKernelGGL((fwd_full_kernel<XB, AB, 1>), grid, dim3(256), lds1, s, fa, n_sc, sa);  \
+    else                                                                                        \
+      hipLaunchKernelGGL((fwd_full_kernel<XB, AB, 2>), grid, dim3(256), lds2, s, fa, n_sc, sa);  \
+  } while (0)
+    if (x_bf16) {
+      if (a_bf16) QLORA_FULL(true, true); else QLORA_FULL(true, false);
+    } else {
+      if (a_bf16) QLORA_FULL(false, true); else QLORA_FULL(false, false);
+    }
+#undef QLORA_FULL
+    return hipGetLastError();
+  }
+  int64_t n_row = 0;
+  const RowdotArgs ra = rowdot_args(X, A, M, in, r, xa_part, n_row);
   if (n_row + n_sc == 0) return hipSuccess;
   const size_t lds = n_row ? rowdot_lds(r) : 0;
   const dim3 grid = dim3(unsigned(n_row + n_sc));
 #define QLORA_PREP2(XB, AB, W)                                                              \
   do {                                                                                      \
     if (r % 8 == 0)                                                                         \
-      hipLaunchKernelGGL((fwd_prep_kernel<XB, AB, W, kQFast>), grid, dim3(256), lds, s, ra, n_row, sa); \
+      hipLaunchKernelGGL((fwd_prep_kernel<XB, AB, W, kQFast>), grid, dim3(256), lds, s, ra, n_sc, sa); \
     else                                                                                    \
-      hipLaunchKernelGGL((fwd_prep_kernel<XB, AB, W, kQGeneric>), grid, dim3(256), lds, s, ra, n_row, sa); \
+      hipLaunchKernelGGL((fwd_prep_kernel<XB, AB, W, kQGeneric>), grid, dim3(256), lds, s, ra, n_sc, sa); \
   } while (0)
 #define QLORA_PREP(XB, AB)                                                                  \
   do {                                                                                      \
@@ -645,22 +963,51 @@ hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf1
 
 hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf16,
                          const float *XA, int64_t M, int64_t out, int64_t r, float *g_part,
-                         float *db_part, const int8_t *qscale, const float *gscale, int64_t in,
-                         float *cs, hipStream_t s) {
-  int64_t n_row = 0, n_col = 0;
-  const RowdotArgs ra = rowdot_args(dY, B, M, out, r, g_part, n_row);
+                         uint16_t *G16, int64_t ldg, float *db_part, const int8_t *qscale,
+                         const float *gscale, int64_t in, float *cs, hipStream_t s) {
+  int64_t n_col = 0;
   const ColdotArgs ca = coldot_args(dY, XA, r, M, out, r, db_part, n_col);
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
   const int64_t n_sc = cs ? scales_workgroups(in, out / 64) : 0;
+  if (r > 0 && g_complete(M, out, r)) {
+    int64_t n_full = 0;
+    const RowfullArgs fa = rowfull_args(dY, B, M, out, r, nullptr, G16, ldg, n_full);
+    const dim3 grid = dim3(unsigned(n_sc + n_full + n_col));
+    const size_t lds_full = rowfull_lds_bytes<kQRows, 2>();
+    const size_t lds = coldot_lds(r) > lds_full ? coldot_lds(r) : lds_full;
+#define QLORA_DYF2(DB, BB, RT)                                                                  \
+  do {                                                                                          \
+    if (r % 8 == 0)                                                                             \
+      hipLaunchKernelGGL((dy_full_kernel<DB, BB, RT, true>), grid, dim3(256), lds, s, fa, n_full, \
+                         ca, n_sc, sa);                                                         \
+    else                                                                                        \
+      hipLaunchKernelGGL((dy_full_kernel<DB, BB, RT, false>), grid, dim3(256), lds, s, fa,       \
+                         n_full, ca, n_sc, sa);                                                 \
+  } while (0)
+#define QLORA_DYF(DB, BB)                                                                       \
+  do {                                                                                          \
+    if (r <= 16) QLORA_DYF2(DB, BB, 1); else QLORA_DYF2(DB, BB, 2);                             \
+  } while (0)
+    if (dy_bf16) {
+      if (b_bf16) QLORA_DYF(true, true); else QLORA_DYF(true, false);
+    } else {
+      if (b_bf16) QLORA_DYF(false, true); else QLORA_DYF(false, false);
+    }
+#undef QLORA_DYF2
+#undef QLORA_DYF
+    return hipGetLastError();
+  }
+  int64_t n_row = 0;
+  const RowdotArgs ra = rowdot_args(dY, B, M, out, r, g_part, n_row);
   if (n_row + n_col + n_sc == 0) return hipSuccess;
   const size_t lds = (n_row + n_col) ? (coldot_lds(r) > rowdot_lds(r) ? coldot_lds(r) : rowdot_lds(r)) : 0;
   const dim3 grid = dim3(unsigned(n_row + n_col + n_sc));
 #define QLORA_DY2(DB, BB, W)                                                                \
   do {                                                                                      \
     if (r % 8 == 0)                                                                         \
-      hipLaunchKernelGGL((bwd_dy_kernel<DB, BB, W, true>), grid, dim3(256), lds, s, ra, n_row, ca, n_col, sa); \
+      hipLaunchKernelGGL((bwd_dy_kernel<DB, BB, W, true>), grid, dim3(256), lds, s, ra, n_row, ca, n_sc, sa); \
     else                                                                                    \
-      hipLaunchKernelGGL((bwd_dy_kernel<DB, BB, W, false>), grid, dim3(256), lds, s, ra, n_row, ca, n_col, sa); \
+      hipLaunchKernelGGL((bwd_dy_kernel<DB, BB, W, false>), grid, dim3(256), lds, s, ra, n_row, ca, n_sc, sa); \
   } while (0)
 #define QLORA_DY(DB, BB)                                                                    \
   do {                                                                                      \
@@ -699,8 +1046,10 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
                           bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s) {
   ReduceArgs ra{part_a, ks_a, rows_a, R, out_a, transpose_a, bf16_a, ld_a};
   ReduceArgs rb{part_b, ks_b, rows_b, R, out_b, transpose_b, bf16_b, ld_b};
-  const int64_t n_a = part_a ? grid_for(rows_a * (ld_a > R ? ld_a : R)) : 0;
-  const int64_t n_b = part_b ? grid_for(rows_b * (ld_b > R ? ld_b : R)) : 0;
+  // one thread per 4 elements (vector form), else per element
+  const int64_t per = R % 4 == 0 ? 4 : 1;
+  const int64_t n_a = part_a ? grid_for(rows_a * (ld_a > R ? ld_a : R) / per) : 0;
+  const int64_t n_b = part_b ? grid_for(rows_b * (ld_b > R ? ld_b : R) / per) : 0;
   if (n_a + n_b == 0) return hipSuccess;
   hipLaunchKernelGGL(reduce2_kernel, dim3(unsigned(n_a + n_b)), dim3(256), 0, s, ra, n_a, rb);
   return hipGetLastError();

@@ -83,6 +83,19 @@ def test_few_tokens(M, n_in, n_out, r, act, adt):
     _check(L, tag="few tokens")
 
 
+@pytest.mark.parametrize("M,n_in,n_out,r,act,adt", [
+    (1030, 320, 448, 16, "bf16", "bf16"),   # 8-row workgroups, ragged M, uneven k runs
+    (1100, 1088, 320, 24, "f32", "f32"),    # fp32 operands, rank tile pair, two batches
+    (1024, 640, 704, 12, "bf16", "bf16"),   # r % 8 != 0: G complete, XA split-K
+    (4100, 128, 192, 32, "bf16", "f32"),    # 16-row workgroups, one k step per wavefront
+])
+def test_complete_rank_products(M, n_in, n_out, r, act, adt):
+    """Token counts where X . A and dY . B^T are formed whole per workgroup
+    (no split-K partials)."""
+    L = Layer(16, M, n_in, n_out, r, act=act, adt=adt)
+    _check(L, tag="complete rank products")
+
+
 def test_few_tokens_b_zero_equals_rank_zero_and_deterministic():
     L = Layer(15, 5, 576, 448, 16, b_zero=True)
     Y, XA = L.fwd()
@@ -126,8 +139,9 @@ def test_identity_probe():
     assert np.all(np.abs(got - W) <= ulp)
 
 
-def test_xa_recompute_and_dx_skip():
-    L = Layer(12, 130, 256, 320, 16)
+@pytest.mark.parametrize("M", [130, 1030])
+def test_xa_recompute_and_dx_skip(M):
+    L = Layer(12, M, 256, 320, 16)
     Y, XA = L.fwd()
     dX1, dA1, dB1 = L.bwd(XA=XA)
     dX2, dA2, dB2 = L.bwd(XA=None)
