@@ -14,7 +14,9 @@ Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s (the dense dW
 is not formed and not counted), timed with HIP events around the forward and
 backward calls of every timed step; quantize GB/s is reported beside it.
 `roofline` covers the dominant kernel (a fused dequantizing GEMM), timed with
-HIP events around each of its launches on the stream it runs on.
+HIP events around each of its launches on the stream it runs on, in a second
+pass over the same K steps (per-launch events would lengthen the steps that
+`value` times).
 `cpu_baseline` times the CPU oracle on the same workload (bounded to a few
 repetitions of the full step, about 10 s of CPU work).  `decode` reports the
 few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
@@ -271,8 +273,6 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    q.qlora_timing_reset()
-    q.qlora_timing_enable(["quantize", "fwd_gemm", "dx_gemm"])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -284,6 +284,16 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    # Per-launch kernel times for the roofline: the same K steps once more,
+    # with the library's HIP events around each launch of the timed kernels
+    # (kept out of the loop above, whose step time they would lengthen).
+    q.qlora_timing_reset()
+    q.qlora_timing_enable(["quantize", "fwd_gemm", "dx_gemm"])
+    for i in range(K):
+        quantize(i)
+        fwd_bwd()
+    torch.cuda.synchronize()
     q.qlora_timing_disable()
 
     ms_per_step = (t1 - t0) * 1e3 / K
