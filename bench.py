@@ -20,6 +20,7 @@ pass over the same K steps (per-launch events would lengthen the steps that
 `cpu_baseline` times the CPU oracle on the same workload (bounded to a few
 repetitions of the full step, about 10 s of CPU work).  `decode` reports the
 few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
+`uniform4` repeats the timed steps with the uniform 4-bit codebook.
 """
 
 import argparse
@@ -296,6 +297,21 @@ def main():
     torch.cuda.synchronize()
     q.qlora_timing_disable()
 
+    # The uniform 4-bit codebook on the same kernels: the same K steps with a
+    # weight quantized to that grid (quantize GB/s and fwd+bwd TFLOP/s).
+    wq_u = q.NF4Weight(n_in, n_out, dev, q.CB_UNIFORM4)
+    for i in range(args.warmup):
+        q.qlora_quantize(W0s[i % N_W0], wq_u)
+    evu = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        evu[i][0].record()
+        q.qlora_quantize(W0s[i % N_W0], wq_u)
+        evu[i][1].record()
+        q.qlora_linear_fwd(wq_u, X, M, q.BF16, A, B, r, q.BF16, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd(wq_u, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
+        evu[i][2].record()
+    torch.cuda.synchronize()
+
     ms_per_step = (t1 - t0) * 1e3 / K
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
     fb_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
@@ -303,6 +319,13 @@ def main():
     qbytes = workloads.quantize_bytes(n_in, n_out)
     value = K * flops / (fb_ms * 1e-3) / 1e12
     q_gbps = K * qbytes / (q_ms * 1e-3) / 1e9
+    uq_ms = sum(e[0].elapsed_time(e[1]) for e in evu)
+    ufb_ms = sum(e[1].elapsed_time(e[2]) for e in evu)
+    uniform4 = {"codebook": "uniform 4-bit grid (16 evenly spaced levels in [-1, 1])",
+                "fwd_bwd_TFLOPs": round(K * flops / (ufb_ms * 1e-3) / 1e12, 2),
+                "quantize_GBps": round(K * qbytes / (uq_ms * 1e-3) / 1e9, 1),
+                "fwd_bwd_ms_per_step": round(ufb_ms / K, 4),
+                "quantize_ms_per_step": round(uq_ms / K, 4)}
 
     kernels = {}
     per_launch_flops = {"fwd_gemm": 2 * M * n_out * (n_in + r),
@@ -348,6 +371,7 @@ def main():
         "fwd_bwd_frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "kernels": kernels,
+        "uniform4": uniform4,
     }
     if not args.no_decode:
         out["decode"] = decode_report(args.decode_sets)

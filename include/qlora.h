@@ -59,12 +59,24 @@ typedef enum {
   QLORA_ERR_SHAPE = 2,     /* in/out not positive multiples of 64, M < 0,
                               r outside [0, QLORA_MAX_RANK]                 */
   QLORA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned              */
-  QLORA_ERR_DTYPE = 4,     /* unknown qlora_dtype                           */
+  QLORA_ERR_DTYPE = 4,     /* unknown qlora_dtype or qlora_codebook         */
   QLORA_ERR_WORKSPACE = 5, /* ws too small (see qlora_bwd_workspace_bytes)  */
   QLORA_ERR_DEVICE = 6     /* the HIP runtime reported an error             */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+/*
+ * Level set of the 4-bit codes ("LLMs · QLoRA", NormalFloat paragraph and its
+ * listing, which builds both and compares them):
+ *   QLORA_CB_NF4       normal quantiles at 16 evenly spaced probabilities in
+ *                      [0.02, 0.98], scaled so the largest magnitude is 1;
+ *   QLORA_CB_UNIFORM4  16 evenly spaced values from -1 to 1.
+ * Each level is computed in double and rounded to fp32 once
+ * (qlora_codebook_levels returns the table).  A weight quantized with one
+ * codebook must be used with the same codebook.
+ */
+typedef enum { QLORA_CB_NF4 = 0, QLORA_CB_UNIFORM4 = 1 } qlora_codebook;
 
 #define QLORA_BLOCK 64      /* weights per absmax block                      */
 #define QLORA_GROUP 256     /* block scales per double-quantization group    */
@@ -79,6 +91,8 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
  *   qscale [n/64] int8    block b (elements 64b..64b+63) scale q_b in
  *                         [0, 127].
  *   gscale [ceil(n/64/256)] fp32  group g (blocks 256g..256g+255) scale s2_g.
+ *   codebook              a qlora_codebook value: the level table L (zero,
+ *                         as in a zero-initialised struct, is NF4).
  * Dequantized weight: w_hat = L[code] * (q_b * s2_g).
  * Requires in % 64 == 0 and out % 64 == 0, so blocks never straddle rows.
  */
@@ -88,6 +102,7 @@ typedef struct {
   uint8_t *codes;
   int8_t *qscale;
   float *gscale;
+  int32_t codebook;
 } qlora_nf4;
 
 /* Number of bytes of each part of a qlora_nf4 of shape (in, out). */
@@ -170,6 +185,11 @@ void qlora_levels(float out[16]);
 /* Decision thresholds of the encoder (host-only): code = #{j in 1..15 :
  * x >= T[j]} reproduces the fp32 argmin rule exactly; out[j-1] = T[j]. */
 void qlora_thresholds(float out[15]);
+
+/* The same two tables for any codebook (host-only); return 0, or -1 for an
+ * unknown codebook or a NULL out (nothing written). */
+int qlora_codebook_levels(int codebook, float out[16]);
+int qlora_codebook_thresholds(int codebook, float out[15]);
 
 /*
  * Kernel-level event timing (instrumentation; off by default).

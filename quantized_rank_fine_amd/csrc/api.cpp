@@ -133,6 +133,7 @@ T *at(void *ws, size_t off) {
 qlora_status check_nf4(const qlora_nf4 *wq) {
   if (!wq) return QLORA_ERR_NULL;
   if (!shape_ok(wq->in, wq->out)) return QLORA_ERR_SHAPE;
+  if (wq->codebook < 0 || wq->codebook >= kCodebooks) return QLORA_ERR_DTYPE;
   if (!wq->codes || !wq->qscale || !wq->gscale) return QLORA_ERR_NULL;
   if (!aligned16(wq->codes) || !aligned16(wq->qscale) || !aligned16(wq->gscale))
     return QLORA_ERR_ALIGN;
@@ -175,7 +176,7 @@ qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t st
   if (!aligned16(W0)) return QLORA_ERR_ALIGN;
   const int64_t nblocks = wq->in * wq->out / 64;
   return dev(timed(QLORA_KERNEL_QUANTIZE, stream, [&] {
-    return launch_quantize(W0, wq->codes, wq->qscale, wq->gscale, nblocks, stream);
+    return launch_quantize(W0, wq->codes, wq->qscale, wq->gscale, nblocks, wq->codebook, stream);
   }));
 }
 
@@ -209,7 +210,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
     float *PXA = r > 0 ? at<float>(ws, p.off_pxa) : nullptr;
     QLORA_RUN(QLORA_KERNEL_FWD_SMALLM,
               launch_fwd_small_partial(wq->codes, wq->qscale, wq->gscale, in, out, X, xb, M, A,
-                                       ab, r, p.kc, P, PXA, stream));
+                                       ab, r, p.kc, P, PXA, wq->codebook, stream));
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fwd_small_reduce(P, PXA, p.ks, M, out, r, B, ab, XA,
                                                            Y, xb, stream));
     return QLORA_OK;
@@ -233,7 +234,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
   }
   QLORA_RUN(QLORA_KERNEL_FWD_GEMM,
             launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, int32_t(p.rp), B, ab, r, Y, xb,
-                            stream));
+                            wq->codebook, stream));
   return QLORA_OK;
 }
 
@@ -320,7 +321,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
   if (dX) {
     QLORA_RUN(QLORA_KERNEL_DX_GEMM,
               launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
-                             xb, stream));
+                             xb, wq->codebook, stream));
   }
   return QLORA_OK;
 #undef QLORA_RUN

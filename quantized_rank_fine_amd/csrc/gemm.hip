@@ -693,12 +693,13 @@ bool set_lds(const void *fn) {
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int64_t N,
                            const uint16_t *X16, int64_t M, const uint16_t *XA16, int32_t ldp,
                            const void *B, bool b_bf16, int32_t r, void *Y, bool y_bf16,
-                           hipStream_t s) {
+                           int codebook, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef bq{B, b_bf16, 1, N, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((N + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
-  const ExpandConsts tb = tables().expand;
+  if (!tables(codebook).symmetric) return hipErrorInvalidValue;
+  const ExpandConsts tb = tables(codebook).expand;
 #define QLORA_FWD(OB)                                                                          \
   do {                                                                                         \
     static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB>));            \
@@ -717,12 +718,13 @@ hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int64_t out,
                           const uint16_t *dY16, int64_t M, const uint16_t *G16, int32_t ldp,
                           const void *A, bool a_bf16, int32_t r, void *dX, bool dx_bf16,
-                          hipStream_t s) {
+                          int codebook, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef aq{A, a_bf16, int64_t(r), 1, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((in + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
-  const ExpandConsts tb = tables().expand;
+  if (!tables(codebook).symmetric) return hipErrorInvalidValue;
+  const ExpandConsts tb = tables(codebook).expand;
 #define QLORA_DX(OB)                                                                           \
   do {                                                                                         \
     static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB>));             \

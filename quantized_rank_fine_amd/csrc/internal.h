@@ -36,18 +36,25 @@ struct ExpandConsts16 {
 struct Tables {
   float L[16];
   float T[16];
+  int symmetric;        // 1 if L[15 - i] == -L[i] for every i (the expansions need it)
   QuantConsts quant;
   ExpandConsts expand;
   ExpandConsts16 expand16;
 };
 
-const Tables &tables();
+// Codebooks (values of qlora_nf4.codebook): the level set of the 4-bit codes.
+constexpr int kCodebookNF4 = 0;
+constexpr int kCodebookUniform4 = 1;
+constexpr int kCodebooks = 2;
+
+// The tables of one codebook (built once, on first use).
+const Tables &tables(int codebook);
 
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `s` and returns hipGetLastError() of the launch.
 
 hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale,
-                           float *gscale, int64_t nblocks, hipStream_t s);
+                           float *gscale, int64_t nblocks, int codebook, hipStream_t s);
 
 // dst[n] (bf16) = src[n] (f32 or bf16)
 hipError_t launch_convert_to_bf16(const void *src, bool src_bf16, int64_t n,
@@ -102,14 +109,16 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K,
                            int64_t N, const uint16_t *X16, int64_t M,
                            const uint16_t *XA16, int32_t ldp, const void *B,
-                           bool b_bf16, int32_t r, void *Y, bool y_bf16, hipStream_t s);
+                           bool b_bf16, int32_t r, void *Y, bool y_bf16, int codebook,
+                           hipStream_t s);
 
 // dX = dY16 . deq(Wq)^T + G16 . A^T.  dY16 [M x out] bf16; G16 [M x ldp] bf16
 // zero-padded; A [in x r] (f32 or bf16) as given; cs as in the forward.
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
                           int64_t out, const uint16_t *dY16, int64_t M,
                           const uint16_t *G16, int32_t ldp, const void *A,
-                          bool a_bf16, int32_t r, void *dX, bool dx_bf16, hipStream_t s);
+                          bool a_bf16, int32_t r, void *dX, bool dx_bf16, int codebook,
+                          hipStream_t s);
 
 // Small-M forward (M <= kSmallMaxM tokens, r <= kSmallMaxR), two launches:
 // partials over K chunks of small_fwd_chunk_rows(M, K, N) rows,
@@ -123,7 +132,7 @@ int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N);
 hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
                                     const float *gscale, int64_t K, int64_t N, const void *X,
                                     bool x_bf16, int64_t M, const void *A, bool a_bf16, int64_t r,
-                                    int64_t Kc, float *P, float *PXA, hipStream_t s);
+                                    int64_t Kc, float *P, float *PXA, int codebook, hipStream_t s);
 hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS, int64_t M,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
                                    void *Y, bool y_bf16, hipStream_t s);

@@ -191,12 +191,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 }  // namespace
 
 hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale, float *gscale,
-                           int64_t nblocks, hipStream_t s) {
+                           int64_t nblocks, int codebook, hipStream_t s) {
   const int64_t groups = (nblocks + kBlocksPerGroup - 1) / kBlocksPerGroup;
   if (groups == 0) return hipSuccess;
-  if (!tables().quant.ok) return hipErrorInvalidValue;
+  const Tables &t = tables(codebook);
+  if (!t.quant.ok) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W0, codes,
-                     qscale, gscale, nblocks, tables().quant);
+                     qscale, gscale, nblocks, t.quant);
   return hipGetLastError();
 }
 

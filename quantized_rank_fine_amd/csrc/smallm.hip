@@ -427,11 +427,12 @@ int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N) {
 hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
                                     const float *gscale, int64_t K, int64_t N, const void *X,
                                     bool x_bf16, int64_t M, const void *A, bool a_bf16, int64_t r,
-                                    int64_t Kc, float *P, float *PXA, hipStream_t s) {
+                                    int64_t Kc, float *P, float *PXA, int codebook, hipStream_t s) {
   const int64_t KS = (K + Kc - 1) / Kc;
   const int64_t slices = (N + kSliceN - 1) / kSliceN;
   SmallArgs a{codes, qscale, gscale, K, N, X, A, M, r, Kc, P, PXA};
-  const ExpandConsts16 &t16 = tables().expand16;
+  if (!tables(codebook).symmetric) return hipErrorInvalidValue;
+  const ExpandConsts16 &t16 = tables(codebook).expand16;
   // one extra column of workgroups computes the X . A partials
   const dim3 grid = dim3(unsigned(slices + (r > 0 ? 1 : 0)), unsigned(KS));
   if (x_bf16) {

@@ -1,11 +1,14 @@
-// Host-side constant tables of libqlora, derived once from the definition of
-// the level set.
+// Host-side constant tables of libqlora, derived once per codebook from the
+// definition of its level set.
 //
-// Level set ("LLMs · QLoRA", NormalFloat paragraph and its code listing):
-// 16 normal quantiles at evenly spaced probabilities in [0.02, 0.98], divided
-// by the largest magnitude.  Here each quantile is found in double precision
-// by bisection on the normal CDF Phi(x) = erfc(-x/sqrt 2)/2, and the
-// normalised value is rounded to fp32 once.
+// Level sets ("LLMs · QLoRA", NormalFloat paragraph and its code listing):
+// * NF4: 16 normal quantiles at evenly spaced probabilities in [0.02, 0.98],
+//   divided by the largest magnitude.  Each quantile is found in double
+//   precision by bisection on the normal CDF Phi(x) = erfc(-x/sqrt 2)/2, and
+//   the normalised value is rounded to fp32 once.
+// * uniform 4-bit (the comparison grid of the same write-up): 16 evenly
+//   spaced values from -1 to 1, each computed in double and rounded to fp32
+//   once.
 //
 // Encoder thresholds: the listing picks the level nearest to x = w/absmax by
 // an argmin of |x - L_i| in fp32, the first minimum winning.  For x between
@@ -73,16 +76,25 @@ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-Tables build_tables() {
+Tables build_tables(int codebook) {
   Tables t;
-  double q[16];
-  double qmax = 0.0;
-  for (int i = 0; i < 16; ++i) {
-    double p = (0.02 * (15 - i) + 0.98 * i) / 15.0;
-    q[i] = normal_quantile(p);
-    qmax = std::fmax(qmax, std::fabs(q[i]));
+  if (codebook == kCodebookUniform4) {
+    for (int i = 0; i < 16; ++i) t.L[i] = (float)(-1.0 + 2.0 * i / 15.0);
+  } else {
+    double q[16];
+    double qmax = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      double p = (0.02 * (15 - i) + 0.98 * i) / 15.0;
+      q[i] = normal_quantile(p);
+      qmax = std::fmax(qmax, std::fabs(q[i]));
+    }
+    for (int i = 0; i < 16; ++i) t.L[i] = (float)(q[i] / qmax);
   }
-  for (int i = 0; i < 16; ++i) t.L[i] = (float)(q[i] / qmax);
+  // The fused expansions use the magnitudes L[8..15] and a sign bit: the
+  // table must be sign-symmetric, L[15 - i] = -L[i] exactly.
+  t.symmetric = 1;
+  for (int i = 0; i < 16; ++i)
+    if (t.L[15 - i] != -t.L[i]) t.symmetric = 0;
 
   t.T[0] = -INFINITY;
   for (int j = 1; j < 16; ++j) {
@@ -138,21 +150,36 @@ Tables build_tables() {
 
 }  // namespace
 
-const Tables &tables() {
-  static Tables t;
-  static std::once_flag once;
-  std::call_once(once, [] { t = build_tables(); });
-  return t;
+const Tables &tables(int codebook) {
+  static Tables t[kCodebooks];
+  static std::once_flag once[kCodebooks];
+  const int cb = (codebook >= 0 && codebook < kCodebooks) ? codebook : 0;
+  std::call_once(once[cb], [cb] { t[cb] = build_tables(cb); });
+  return t[cb];
 }
 
 }  // namespace qlora
 
 extern "C" void qlora_levels(float out[16]) {
-  const qlora::Tables &t = qlora::tables();
+  const qlora::Tables &t = qlora::tables(qlora::kCodebookNF4);
   for (int i = 0; i < 16; ++i) out[i] = t.L[i];
 }
 
 extern "C" void qlora_thresholds(float out[15]) {
-  const qlora::Tables &t = qlora::tables();
+  const qlora::Tables &t = qlora::tables(qlora::kCodebookNF4);
   for (int j = 1; j < 16; ++j) out[j - 1] = t.T[j];
+}
+
+extern "C" int qlora_codebook_levels(int codebook, float out[16]) {
+  if (codebook < 0 || codebook >= qlora::kCodebooks || !out) return -1;
+  const qlora::Tables &t = qlora::tables(codebook);
+  for (int i = 0; i < 16; ++i) out[i] = t.L[i];
+  return 0;
+}
+
+extern "C" int qlora_codebook_thresholds(int codebook, float out[15]) {
+  if (codebook < 0 || codebook >= qlora::kCodebooks || !out) return -1;
+  const qlora::Tables &t = qlora::tables(codebook);
+  for (int j = 1; j < 16; ++j) out[j - 1] = t.T[j];
+  return 0;
 }

@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "qlora.h")
 
 F32, BF16 = 0, 1
+CB_NF4, CB_UNIFORM4 = 0, 1          # qlora_codebook
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "pointer not 16-byte aligned",
           4: "invalid dtype", 5: "workspace too small", 6: "HIP runtime error"}
 KERNELS = ("quantize", "xa_rowdot", "fwd_gemm", "dy_pass", "dx_gemm", "da_pass", "reduce",
@@ -31,7 +32,7 @@ class QloraError(RuntimeError):
 class qlora_nf4(ctypes.Structure):
     _fields_ = [("in_", ctypes.c_int64), ("out", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
-                ("gscale", ctypes.c_void_p)]
+                ("gscale", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
 
 
 _lib = None
@@ -64,6 +65,9 @@ def lib():
     L.qlora_levels.restype = None
     L.qlora_thresholds.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.qlora_thresholds.restype = None
+    for f in (L.qlora_codebook_levels, L.qlora_codebook_thresholds):
+        f.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+        f.restype = ctypes.c_int
     L.qlora_timing_enable.argtypes = [ctypes.c_int]
     L.qlora_timing_enable.restype = ctypes.c_int
     L.qlora_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -110,24 +114,28 @@ def _check(status, where):
         raise QloraError(status, where)
 
 
-def nf4_struct(n_in, n_out, codes, qscale, gscale):
+def nf4_struct(n_in, n_out, codes, qscale, gscale, codebook=CB_NF4):
     """qlora_nf4 describing caller-owned buffers (tensors or raw pointers)."""
-    return qlora_nf4(int(n_in), int(n_out), _ptr(codes), _ptr(qscale), _ptr(gscale))
+    return qlora_nf4(int(n_in), int(n_out), _ptr(codes), _ptr(qscale), _ptr(gscale),
+                     int(codebook))
 
 
 class NF4Weight:
-    """Caller-owned device buffers of one quantized (in, out) weight."""
+    """Caller-owned device buffers of one quantized (in, out) weight and the
+    codebook its codes index."""
 
-    def __init__(self, n_in, n_out, device="cuda"):
+    def __init__(self, n_in, n_out, device="cuda", codebook=CB_NF4):
         import torch
         n = n_in * n_out
         self.n_in, self.n_out = n_in, n_out
+        self.codebook = codebook
         self.codes = torch.empty(n // 2, dtype=torch.uint8, device=device)
         self.qscale = torch.empty(n // 64, dtype=torch.int8, device=device)
         self.gscale = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=device)
 
     def struct(self):
-        return nf4_struct(self.n_in, self.n_out, self.codes, self.qscale, self.gscale)
+        return nf4_struct(self.n_in, self.n_out, self.codes, self.qscale, self.gscale,
+                          self.codebook)
 
 
 # ------------------------------------------------------------- entry points
@@ -170,6 +178,20 @@ def qlora_levels():
 def qlora_thresholds():
     buf = (ctypes.c_float * 15)()
     lib().qlora_thresholds(buf)
+    return list(buf)
+
+
+def qlora_codebook_levels(codebook):
+    buf = (ctypes.c_float * 16)()
+    _check(0 if lib().qlora_codebook_levels(int(codebook), buf) == 0 else 4,
+           "qlora_codebook_levels")
+    return list(buf)
+
+
+def qlora_codebook_thresholds(codebook):
+    buf = (ctypes.c_float * 15)()
+    _check(0 if lib().qlora_codebook_thresholds(int(codebook), buf) == 0 else 4,
+           "qlora_codebook_thresholds")
     return list(buf)
 
 

@@ -53,12 +53,17 @@ def out_to_f64(t, dtype):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def quantize_gpu(w0):
+def levels_of(codebook):
+    """The oracle's level table of a codebook."""
+    return oracle.uniform4_levels() if codebook == q.CB_UNIFORM4 else oracle.nf4_levels()
+
+
+def quantize_gpu(w0, codebook=q.CB_NF4):
     """Quantize an fp32 (in, out) numpy matrix on the GPU; returns the
-    NF4Weight and host copies of its three buffers."""
+    NF4Weight (device buffers)."""
     torch, dev = torch_dev()
     n_in, n_out = w0.shape
-    wq = q.NF4Weight(n_in, n_out, dev)
+    wq = q.NF4Weight(n_in, n_out, dev, codebook)
     tw = to_dev(w0)
     q.qlora_quantize(tw, wq)
     torch.cuda.synchronize()
@@ -70,9 +75,10 @@ class Layer:
     """Seeded inputs of one adapted linear, on host and device."""
 
     def __init__(self, workload, M, n_in, n_out, r, act="bf16", adt="bf16", b_zero=False,
-                 layer=0, linear=0, w0=None):
+                 layer=0, linear=0, w0=None, codebook=q.CB_NF4):
         torch, dev = torch_dev()
         self.M, self.n_in, self.n_out, self.r = M, n_in, n_out, r
+        self.codebook = codebook
         self.act, self.adt = act, adt
         self.w0 = synth.weights(n_in, n_out, workload, layer, linear) if w0 is None else w0
         self.X = synth.activations(M, n_in, workload, act, layer, linear)
@@ -97,7 +103,7 @@ class Layer:
         self.tdY = dv(self.dY, self.tdt)
         self.tA = dv(self.A, self.adt_t)
         self.tB = dv(self.B, self.adt_t)
-        self.wq = quantize_gpu(self.w0)
+        self.wq = quantize_gpu(self.w0, codebook)
 
     # ---------------------------------------------------------------- runs
     def fwd(self):
@@ -130,7 +136,7 @@ class Layer:
         c = self.wq.codes.cpu().numpy()
         q8 = self.wq.qscale.cpu().numpy()
         s2 = self.wq.gscale.cpu().numpy()
-        return oracle.dequantize(c, q8, s2, self.n_in, self.n_out)
+        return oracle.dequantize(c, q8, s2, self.n_in, self.n_out, levels_of(self.codebook))
 
     def ref(self, rows=None):
         """Oracle forward/backward (float64) on the GPU's own quantized

@@ -31,13 +31,30 @@ def test_level_table_matches_oracle(L):
     assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels().view(np.uint32))
 
 
-def _x_sweep():
+CODEBOOKS = [(q.CB_NF4, oracle.nf4_levels), (q.CB_UNIFORM4, oracle.uniform4_levels)]
+
+
+def test_codebook_tables(L):
+    """Each codebook's level table equals the oracle's bit for bit; the NF4
+    entry points agree with codebook 0; an unknown codebook is rejected."""
+    for cb, levels in CODEBOOKS:
+        lv = np.array(q.qlora_codebook_levels(cb), np.float32)
+        assert np.array_equal(lv.view(np.uint32), levels().view(np.uint32))
+        assert np.array_equal(lv, -lv[::-1])              # sign-symmetric
+    assert q.qlora_codebook_levels(q.CB_NF4) == q.qlora_levels()
+    assert q.qlora_codebook_thresholds(q.CB_NF4) == q.qlora_thresholds()
+    buf = (ctypes.c_float * 16)()
+    assert L.qlora_codebook_levels(2, buf) == -1
+    assert L.qlora_codebook_thresholds(-1, buf) == -1
+
+
+def _x_sweep(T=None, levels=None):
     """fp32 values in [-1, 1]: a strided sweep of bit patterns, the
     neighbourhood of every threshold and level, and the special values."""
     pos = np.arange(0, 0x3F800001, 4099, dtype=np.uint32).view(np.float32)
     xs = [pos, -pos]
-    T = np.array(q.qlora_thresholds(), np.float32)
-    L = oracle.nf4_levels()
+    T = np.array(q.qlora_thresholds() if T is None else T, np.float32)
+    L = oracle.nf4_levels() if levels is None else levels
     for v in np.concatenate([T, L]):
         b = np.array([v], np.float32).view(np.int32)[0]
         nb = np.arange(b - 300, b + 301, dtype=np.int64)
@@ -51,17 +68,18 @@ def _x_sweep():
     return x[(x >= -1) & (x <= 1)]
 
 
-def test_thresholds_reproduce_oracle_argmin(L):
+@pytest.mark.parametrize("cb,levels", CODEBOOKS)
+def test_thresholds_reproduce_oracle_argmin(L, cb, levels):
     """code = #{j : x >= T_j} equals the oracle's fp32 argmin for every x."""
-    T = np.array(q.qlora_thresholds(), np.float32)
-    x = _x_sweep()
+    T = np.array(q.qlora_codebook_thresholds(cb), np.float32)
+    x = _x_sweep(T, levels())
     pad = (-x.size) % 63
     x = np.concatenate([x, np.zeros(pad, np.float32)])
     blocks = x.reshape(-1, 63)
     w = np.concatenate([np.ones((blocks.shape[0], 1), np.float32), blocks], axis=1).reshape(-1)
     c = onf4.block_absmax(w)
     assert np.all(c == 1.0)
-    codes = oracle.encode(w, c).reshape(-1, 64)[:, 1:].reshape(-1)
+    codes = oracle.encode(w, c, levels()).reshape(-1, 64)[:, 1:].reshape(-1)
     mine = np.searchsorted(T, x, side="right")
     assert np.array_equal(codes, mine)
 
@@ -105,8 +123,8 @@ P = 0x10000          # 16-byte aligned
 U = 0x10004          # misaligned
 
 
-def _nf4(i=256, o=256, codes=P, qs=P, gs=P):
-    return q.nf4_struct(i, o, codes, qs, gs)
+def _nf4(i=256, o=256, codes=P, qs=P, gs=P, cb=0):
+    return q.nf4_struct(i, o, codes, qs, gs, cb)
 
 
 def _st(f, *a):
@@ -123,6 +141,8 @@ def test_quantize_validation(L):
         assert L.qlora_quantize(P, ctypes.byref(s2), None) == 2
     assert L.qlora_quantize(P, ctypes.byref(_nf4(codes=None)), None) == 1
     assert L.qlora_quantize(P, ctypes.byref(_nf4(qs=U)), None) == 3
+    for cb in (2, -1):                                 # unknown codebook
+        assert L.qlora_quantize(P, ctypes.byref(_nf4(cb=cb)), None) == 4
 
 
 def test_fwd_validation(L):
@@ -144,6 +164,7 @@ def test_fwd_validation(L):
     assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, P, None, ws, None) == 1
     bad = _nf4(256, 96)
     assert f(ctypes.byref(bad), P, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 2
+    assert f(ctypes.byref(_nf4(cb=5)), P, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 4
 
 
 def test_bwd_validation(L):
@@ -190,11 +211,12 @@ def _bucket_lut(T):
     return lut
 
 
-def test_bucket_lookup_reproduces_oracle_argmin(L):
+@pytest.mark.parametrize("cb,levels", CODEBOOKS)
+def test_bucket_lookup_reproduces_oracle_argmin(L, cb, levels):
     """code = base + (x >= T_bucket), with the bucket read off the fp32 bits of
     x + 3, equals the oracle's fp32 argmin on the threshold sweep and around
     every bucket boundary (where x + 3 rounds up into the next bucket)."""
-    T = np.array(q.qlora_thresholds(), np.float32)
+    T = np.array(q.qlora_codebook_thresholds(cb), np.float32)
     lut = _bucket_lut(T)
     edges = []
     for i in range(65):
@@ -203,7 +225,7 @@ def test_bucket_lookup_reproduces_oracle_argmin(L):
         nb = nb[(nb >= np.int64(np.int32(-0x7FFFFFFF) - 1)) & (nb <= 0x7FFFFFFF)]
         edges.append(nb.astype(np.int32).view(np.float32))
         edges.append(-edges[-1])
-    x = np.concatenate([_x_sweep()] + edges)
+    x = np.concatenate([_x_sweep(T, levels())] + edges)
     x = x[(x >= -1) & (x <= 1)]
     key = ((x + np.float32(3.0)).astype(np.float32).view(np.uint32) >> 17) & 127
     Tb = np.array([e[0] for e in lut], np.float32)[key]
@@ -212,7 +234,7 @@ def test_bucket_lookup_reproduces_oracle_argmin(L):
     pad = (-x.size) % 63
     xx = np.concatenate([x, np.zeros(pad, np.float32)])
     w = np.concatenate([np.ones((xx.size // 63, 1), np.float32), xx.reshape(-1, 63)], axis=1).reshape(-1)
-    codes = oracle.encode(w, onf4.block_absmax(w)).reshape(-1, 64)[:, 1:].reshape(-1)[: x.size]
+    codes = oracle.encode(w, onf4.block_absmax(w), levels()).reshape(-1, 64)[:, 1:].reshape(-1)[: x.size]
     assert np.array_equal(codes, mine)
 
 

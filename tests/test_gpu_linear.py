@@ -10,15 +10,16 @@ import numpy as np
 import pytest
 
 import oracle
+from quantized_rank_fine_amd import qlora as q
 from quantized_rank_fine_amd import workloads
 
-from gpu_harness import TOL, Layer, out_to_f64, rel_err, say
+from gpu_harness import TOL, Layer, levels_of, out_to_f64, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
 
 def _codes_match_oracle(L):
-    ref = oracle.quantize(L.w0)
+    ref = oracle.quantize(L.w0, levels_of(L.codebook))
     assert np.array_equal(L.wq.codes.cpu().numpy(), ref["packed"])
     assert np.array_equal(L.wq.qscale.cpu().numpy(), ref["q8"])
 
@@ -94,6 +95,19 @@ def test_complete_rank_products(M, n_in, n_out, r, act, adt):
     (no split-K partials)."""
     L = Layer(16, M, n_in, n_out, r, act=act, adt=adt)
     _check(L, tag="complete rank products")
+
+
+@pytest.mark.parametrize("M,n_in,n_out,r,act,adt", [
+    (300, 640, 704, 16, "bf16", "bf16"),    # fused GEMMs, split-K rank-r passes
+    (1030, 320, 448, 16, "bf16", "f32"),    # whole-K rank-r passes
+    (5, 576, 448, 16, "f32", "bf16"),       # few-token forward
+])
+def test_uniform4_codebook(M, n_in, n_out, r, act, adt):
+    """The uniform 4-bit grid through every path: same kernels, its own
+    level table."""
+    L = Layer(17, M, n_in, n_out, r, act=act, adt=adt, codebook=q.CB_UNIFORM4)
+    _codes_match_oracle(L)
+    _check(L, tag="uniform4")
 
 
 def test_few_tokens_b_zero_equals_rank_zero_and_deterministic():

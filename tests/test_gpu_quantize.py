@@ -8,15 +8,18 @@ import pytest
 import oracle
 from quantized_rank_fine_amd import synth, workloads
 
-from gpu_harness import quantize_gpu, say
+from quantized_rank_fine_amd import qlora as q
+
+from gpu_harness import levels_of, quantize_gpu, say
 
 pytestmark = pytest.mark.gpu
 
 
-def _check_full(w0, tag):
-    say(f"[quantize] {tag} shape={w0.shape}")
-    wq = quantize_gpu(w0)
-    ref = oracle.quantize(w0)
+def _check_full(w0, tag, codebook=q.CB_NF4):
+    say(f"[quantize] {tag} shape={w0.shape} codebook={codebook}")
+    wq = quantize_gpu(w0, codebook)
+    L = levels_of(codebook)
+    ref = oracle.quantize(w0, L)
     codes = wq.codes.cpu().numpy()
     q8 = wq.qscale.cpu().numpy()
     s2 = wq.gscale.cpu().numpy()
@@ -25,8 +28,8 @@ def _check_full(w0, tag):
     assert np.array_equal(q8, ref["q8"]), f"{tag}: q8 differs"
     assert np.array_equal(s2.view(np.uint32), ref["s2"].view(np.uint32)), f"{tag}: s2 differs"
     n_in, n_out = w0.shape
-    Wg = oracle.dequantize(codes, q8, s2, n_in, n_out)
-    Wr = oracle.dequantize(ref["packed"], ref["q8"], ref["s2"], n_in, n_out)
+    Wg = oracle.dequantize(codes, q8, s2, n_in, n_out, L)
+    Wr = oracle.dequantize(ref["packed"], ref["q8"], ref["s2"], n_in, n_out, L)
     assert np.abs(Wg - Wr).max() <= 1e-6 * np.abs(Wr).max()
     return wq
 
@@ -37,6 +40,13 @@ def test_quantize_small_config():
 
 def test_quantize_4096_square():
     _check_full(synth.weights(4096, 4096, workload=1), "4096x4096")
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096), (320, 640), (128, 704)])
+def test_quantize_uniform4(shape):
+    """The uniform 4-bit codebook on the same kernel: codes, q8 and s2 bit-exact
+    against the oracle's argmin over the uniform grid."""
+    _check_full(synth.weights(*shape, workload=1), f"uniform4 {shape}", q.CB_UNIFORM4)
 
 
 @pytest.mark.parametrize("shape", [(64, 192), (320, 640), (64, 64), (128, 704)])
