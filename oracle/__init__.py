@@ -18,7 +18,8 @@ What it computes (plain, slow, obviously correct):
   dequantization is exact in float64.
 * ``linear``  -- forward y = X.deq(Wq) + (X.A).B and the backward
   dX, dA, dB in float64, both in factored form and (for tiny shapes) through
-  the dense weight gradient dW = X^T.dY exactly as the chain rule is written.
+  the dense weight gradient dW = X^T.dY exactly as the chain rule is written;
+  the merged dense weight deq(Wq) + A.B.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against values the pages print or against closed forms; no function is
@@ -39,7 +40,7 @@ from .nf4 import (
     dequantize,
     storage_bits_per_weight,
 )
-from .linear import forward, backward, backward_via_dense_dw
+from .linear import forward, backward, backward_via_dense_dw, merge
 
 __all__ = [
     "nf4_levels",
@@ -58,5 +59,6 @@ __all__ = [
     "storage_bits_per_weight",
     "forward",
     "backward",
+    "merge",
     "backward_via_dense_dw",
 ]

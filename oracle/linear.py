@@ -71,3 +71,19 @@ def backward_via_dense_dw(X, dY, W_hat, A, B):
     W = _f64(W_hat) + A @ B
     dW = X.T @ dY
     return {"dW": dW, "dX": dY @ W.T, "dA": dW @ B.T, "dB": A.T @ dW}
+
+
+def merge(W_hat, A=None, B=None):
+    """The merged dense weight W = W_hat + A B (float64, shape (in, out)).
+
+    "QLoRA (low-rank adapters on a quantized model)", "How it works", step 5:
+    after training the adapters may be folded into the base weight, which
+    is then a dense float matrix, off the quantization grid ("What the
+    simulations show"); re-quantizing it (``nf4.quantize``) gives the
+    4-bit storage back at some loss ("When it breaks").  Rank 0 (A or B is
+    None) returns W_hat.
+    """
+    W = _f64(W_hat).copy()
+    if A is None or B is None or _f64(A).shape[1] == 0:
+        return W
+    return W + _f64(A) @ _f64(B)

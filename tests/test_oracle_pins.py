@@ -348,3 +348,63 @@ def test_rank_zero_is_plain_linear():
     assert XA.shape == (3, 0) and np.array_equal(y, X @ W)
     g = oracle.backward(X, dY, W, None, None)
     assert np.array_equal(g["dX"], dY @ W.T)
+
+
+# --------------------------------------------------------------------------
+# merge (after training) and re-quantization
+
+
+def check_merge(merge):
+    """merge(W_hat, A, B) = W_hat + A B: entry by entry on a tiny shape (plain
+    loops), the layer's own forward with X = I returns it, X times it is the
+    forward output for any X, and B = 0 or rank 0 give W_hat exactly."""
+    X, W, A, B, _ = _tiny(seed=21, M=5, n_in=64, n_out=64, r=3)
+    Wm = np.asarray(merge(W, A, B), np.float64)
+    for k in range(0, 64, 7):
+        for n in range(0, 64, 5):
+            s = W[k, n]
+            for j in range(3):
+                s += A[k, j] * B[j, n]
+            assert abs(Wm[k, n] - s) <= 1e-15 * max(1.0, abs(s))
+    _, y_eye = oracle.forward(np.eye(64), W, A, B)
+    assert np.allclose(Wm, y_eye, rtol=0, atol=1e-14)
+    _, y = oracle.forward(X, W, A, B)
+    assert np.allclose(X @ Wm, y, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(np.asarray(merge(W, A, np.zeros_like(B))), W)
+    assert np.array_equal(np.asarray(merge(W, None, None)), W)
+
+
+def test_merge_pins():
+    check_merge(oracle.merge)
+
+
+def test_requantize_unmodified_weight_reproduces_it():
+    """Re-quantizing a dequantized weight that no adapter changed gives back
+    its codes and block scales (every level is a fixed point of the encoder;
+    each block's absmax element sits at level +-1)."""
+    w0 = synth.weights(256, 512, workload=7)
+    for levels in (oracle.nf4_levels(), oracle.uniform4_levels()):
+        q1 = oracle.quantize(w0, levels)
+        W = oracle.dequantize(q1["packed"], q1["q8"], q1["s2"], 256, 512, levels).astype(np.float32)
+        q2 = oracle.quantize(W, levels)
+        assert np.array_equal(q2["codes"], q1["codes"])
+        assert np.array_equal(q2["q8"], q1["q8"])
+        assert np.allclose(q2["s2"], q1["s2"], rtol=2.0 ** -22, atol=0)
+
+
+def test_requantize_drops_sub_step_corrections():
+    """Merging then re-quantizing keeps an adapter correction only where it
+    moves a weight across a decision threshold: corrections far below one
+    quantization step leave almost every code unchanged, corrections of a
+    few steps change most of them."""
+    w0 = synth.weights(256, 512, workload=7)
+    q1 = oracle.quantize(w0)
+    W = oracle.dequantize(q1["packed"], q1["q8"], q1["s2"], 256, 512)
+    step = float(np.median(q1["absmax"])) * 0.08      # about the smallest level gap
+    g = np.random.default_rng(3)
+    A = g.standard_normal((256, 4)) / 2.0                # rank-4 adapter pair, |A B| ~ 1
+    B = g.standard_normal((4, 512))
+    for frac, lo, hi in ((1e-3, 0.99, 1.0), (3.0, 0.0, 0.5)):
+        q2 = oracle.quantize(oracle.merge(W, A, frac * step * B).astype(np.float32))
+        same = np.mean(q2["codes"] == q1["codes"])
+        assert lo <= same <= hi, (frac, same)

@@ -120,3 +120,16 @@ def test_wrong_sign_in_dX_is_caught():
 def test_wrong_operand_in_dB_is_caught():
     with pytest.raises(AssertionError):
         pins.check_backward_fd(oracle.forward, _backward_dB_from_A)
+
+
+def _merge_wrong_sign(W, A=None, B=None):
+    """Mistake: the adapter product subtracted from the base weight."""
+    W = np.asarray(W, np.float64)
+    if A is None or B is None:
+        return W.copy()
+    return W - np.asarray(A, np.float64) @ np.asarray(B, np.float64)
+
+
+def test_wrong_sign_in_merge_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_merge(_merge_wrong_sign)
