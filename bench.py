@@ -20,7 +20,8 @@ pass over the same K steps (per-launch events would lengthen the steps that
 `cpu_baseline` times the CPU oracle on the same workload (bounded to a few
 repetitions of the full step, about 10 s of CPU work).  `decode` reports the
 few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
-`uniform4` repeats the timed steps with the uniform 4-bit codebook.
+`uniform4` repeats the timed steps with the uniform 4-bit codebook; `merge`
+times folding the adapters into a dense bf16 weight (HBM-bound).
 """
 
 import argparse
@@ -312,6 +313,25 @@ def main():
         evu[i][2].record()
     torch.cuda.synchronize()
 
+    # Merge (fold the adapters into a dense bf16 weight), K launches.
+    Wm = torch.empty(n_in, n_out, dtype=torch.bfloat16, device=dev)
+    q.qlora_merge(wq, A, B, r, q.BF16, Wm, q.BF16)
+    em0, em1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    em0.record()
+    for i in range(K):
+        q.qlora_merge(wq, A, B, r, q.BF16, Wm, q.BF16)
+    em1.record()
+    torch.cuda.synchronize()
+    merge_us = em0.elapsed_time(em1) * 1e3 / K
+    nw = n_in * n_out
+    merge_bytes = nw // 2 + nw // 64 + 4 * ((nw // 64 + 255) // 256) + 2 * r * (n_in + n_out) + 2 * nw
+    merge = {"us": round(merge_us, 2), "algorithmic_bytes": merge_bytes,
+             "GBps": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1),
+             "frac_hbm_peak": round(merge_bytes / (merge_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+             "what": "W = deq(Wq) + A.B written as dense bf16, r = 16"}
+    del Wm
+
     ms_per_step = (t1 - t0) * 1e3 / K
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
     fb_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
@@ -372,6 +392,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "uniform4": uniform4,
+        "merge": merge,
     }
     if not args.no_decode:
         out["decode"] = decode_report(args.decode_sets)

@@ -175,6 +175,21 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
                                  qlora_dtype act);
 
+/*
+ * qlora_merge: the merged dense weight W = deq(Wq) + A.B
+ *   ("How it works" step 5: fold the trained adapters into the base weight;
+ *   "What the simulations show": the result is a dense float matrix, off the
+ *   quantization grid).
+ *   A [in, r], B [r, out] in adt; W [in, out] in wdt (output, caller-owned).
+ * Per element in fp32: L[code] * (q_b * s2_g), plus the rank-r sum
+ * accumulated in rank order with fp32 fused multiply-adds, rounded once to
+ * wdt.  r = 0 writes deq(Wq) (A, B may be NULL).  To store the merged weight
+ * in 4 bits again, merge with wdt = QLORA_F32 and pass W to qlora_quantize
+ * ("When it breaks": corrections smaller than a quantization step are lost).
+ */
+qlora_status qlora_merge(const qlora_nf4 *wq, const void *A, const void *B, int32_t r,
+                         qlora_dtype adt, void *W, qlora_dtype wdt, hipStream_t stream);
+
 /* Human-readable name of a status code (host-only, static string). */
 const char *qlora_status_string(qlora_status s);
 

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
 
-SOURCES = ["api.cpp", "tables.cpp", "quantize.hip", "skinny.hip", "gemm.hip", "smallm.hip"]
+SOURCES = ["api.cpp", "tables.cpp", "quantize.hip", "skinny.hip", "gemm.hip", "smallm.hip",
+           "merge.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -327,6 +327,22 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
 #undef QLORA_RUN
 }
 
+qlora_status qlora_merge(const qlora_nf4 *wq, const void *A, const void *B, int32_t r,
+                         qlora_dtype adt, void *W, qlora_dtype wdt, hipStream_t stream) {
+  qlora_status st = check_nf4(wq);
+  if (st != QLORA_OK) return st;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!dtype_ok(adt) || !dtype_ok(wdt)) return QLORA_ERR_DTYPE;
+  if (!W) return QLORA_ERR_NULL;
+  if (!aligned16(W)) return QLORA_ERR_ALIGN;
+  if (r > 0) {
+    if (!A || !B) return QLORA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B)) return QLORA_ERR_ALIGN;
+  }
+  return dev(launch_merge(wq->codes, wq->qscale, wq->gscale, wq->in, wq->out, A, B,
+                          adt == QLORA_BF16, r, W, wdt == QLORA_BF16, wq->codebook, stream));
+}
+
 int qlora_timing_enable(int kind_mask) {
   g_timing.mask = kind_mask & ((1 << QLORA_KERNEL_COUNT) - 1);
   return 0;

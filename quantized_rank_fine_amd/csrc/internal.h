@@ -137,6 +137,12 @@ hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
                                    void *Y, bool y_bf16, hipStream_t s);
 
+// W = deq(Wq) + A . B (W [in x out] fp32 or bf16; A [in x r], B [r x out]
+// in the adapter dtype), per element in fp32, one rounding at the end.
+hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2, int64_t in,
+                        int64_t out, const void *A, const void *B, bool a_bf16, int32_t r,
+                        void *W, bool w_bf16, int codebook, hipStream_t s);
+
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
 

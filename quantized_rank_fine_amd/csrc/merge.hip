@@ -1,0 +1,143 @@
+// Merged dense weight W = deq(Wq) + A . B.
+//
+// "QLoRA (low-rank adapters on a quantized model)", "How it works", step 5:
+// after training the adapters can be folded into the base weight; the result
+// is a dense float matrix, off the quantization grid ("What the simulations
+// show"), which qlora_quantize can take back to 4 bits at some loss.
+//
+// Per element, in fp32: w = L[code] * (q_b * s2_g) (the two products the
+// fused GEMMs form before their bf16 rounding), plus sum_j A[k][j] * B[j][n]
+// accumulated in rank order with fp32 fused multiply-adds, then one rounding
+// to the output dtype.
+//
+// Workgroup: 256 threads, a 64-row x 128-column tile of W.  Thread t owns rows
+// 4 (t >> 4) .. +3 and columns 8 (t & 15) .. +7: four 4-byte code words (one
+// 64-block each, so one scale per row) and a 4 x 8 fp32 accumulator of the
+// rank-r term.  The rank runs in chunks of 32: the A chunk is staged
+// transposed ([j][row], 68-float pitch) and the B chunk as is ([j][col]), so
+// a thread reads one 16-B A quad and two 16-B B quads per rank index for 32
+// multiply-adds.  The kernel is bound by HBM (the output write) for small r
+// and by the fp32 multiply-adds (8 r per weight) as r grows.
+#include "device.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kRows = 64, kCols = 128, kRC = 32, kAPitch = 68;
+
+struct MergeArgs {
+  const uint8_t *codes;
+  const int8_t *q8;
+  const float *s2;
+  int64_t in, out;
+  const void *A;      // [in x r]
+  const void *B;      // [r x out]
+  int r;
+  void *W;            // [in x out]
+};
+
+struct Levels {
+  float L[16];
+};
+
+template <bool kAbf16>
+__device__ __forceinline__ float load_adapter(const void *p, int64_t i) {
+  if constexpr (kAbf16)
+    return __uint_as_float(uint32_t(static_cast<const uint16_t *>(p)[i]) << 16);
+  else
+    return static_cast<const float *>(p)[i];
+}
+
+template <bool kAbf16, bool kWbf16>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, Levels lv) {
+  __shared__ __align__(16) float sA[kRC][kAPitch];
+  __shared__ __align__(16) float sB[kRC][kCols];
+  __shared__ float sL[16];
+  const int t = threadIdx.x, cg = t & 15, rg = t >> 4;
+  const int64_t k0 = int64_t(blockIdx.y) * kRows, n0 = int64_t(blockIdx.x) * kCols;
+  const int64_t ncols = min64(kCols, a.out - n0);          // 64 or 128
+  if (t < 16) sL[t] = lv.L[t];
+
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+
+  for (int j0 = 0; j0 < a.r; j0 += kRC) {
+    __syncthreads();                                       // previous chunk consumed
+#pragma unroll
+    for (int u = 0; u < kRows * kRC / 256; ++u) {          // A rows k0.., ranks j0..
+      const int e = t + 256 * u, row = e / kRC, j = e % kRC;
+      sA[j][row] = (j0 + j < a.r) ? load_adapter<kAbf16>(a.A, (k0 + row) * a.r + j0 + j) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kRC * kCols / 256; ++u) {          // B ranks j0.., columns n0..
+      const int e = t + 256 * u, j = e / kCols, col = e % kCols;
+      sB[j][col] = (j0 + j < a.r && col < ncols)
+                       ? load_adapter<kAbf16>(a.B, int64_t(j0 + j) * a.out + n0 + col) : 0.0f;
+    }
+    __syncthreads();
+    const int jn = a.r - j0 < kRC ? a.r - j0 : kRC;
+    for (int j = 0; j < jn; ++j) {
+      const f32x4_t av = *reinterpret_cast<const f32x4_t *>(&sA[j][4 * rg]);
+      const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(&sB[j][8 * cg]);
+      const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(&sB[j][8 * cg + 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[i][e] = __builtin_fmaf(av[i], b0[e], acc[i][e]);
+          acc[i][4 + e] = __builtin_fmaf(av[i], b1[e], acc[i][4 + e]);
+        }
+      }
+    }
+  }
+  __syncthreads();                                         // sL visible (r = 0 too)
+
+  if (8 * cg >= ncols) return;
+  const int64_t NB = a.out / 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = k0 + 4 * rg + i, col = n0 + 8 * cg;
+    const int64_t flat = row * a.out + col;
+    const uint32_t word = *reinterpret_cast<const uint32_t *>(a.codes + flat / 2);
+    const int64_t blk = row * NB + col / 64;
+    const float c = float(a.q8[blk]) * a.s2[blk >> 8];
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = sL[(word >> (4 * e)) & 15u] * c + acc[i][e];
+    if constexpr (kWbf16) {
+      u32x4_t o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+      *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.W) + flat) = o;
+    } else {
+      float *d = static_cast<float *>(a.W) + flat;
+      *reinterpret_cast<f32x4_t *>(d) = f32x4_t{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4_t *>(d + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2, int64_t in,
+                        int64_t out, const void *A, const void *B, bool a_bf16, int32_t r,
+                        void *W, bool w_bf16, int codebook, hipStream_t s) {
+  MergeArgs a{codes, q8, s2, in, out, A, B, int(r), W};
+  Levels lv;
+  const Tables &t = tables(codebook);
+  for (int i = 0; i < 16; ++i) lv.L[i] = t.L[i];
+  const dim3 grid(unsigned((out + kCols - 1) / kCols), unsigned(in / kRows));
+  if (a_bf16) {
+    if (w_bf16) hipLaunchKernelGGL((merge_kernel<true, true>), grid, dim3(256), 0, s, a, lv);
+    else hipLaunchKernelGGL((merge_kernel<true, false>), grid, dim3(256), 0, s, a, lv);
+  } else {
+    if (w_bf16) hipLaunchKernelGGL((merge_kernel<false, true>), grid, dim3(256), 0, s, a, lv);
+    else hipLaunchKernelGGL((merge_kernel<false, false>), grid, dim3(256), 0, s, a, lv);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qlora

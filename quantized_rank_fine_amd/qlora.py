@@ -54,7 +54,8 @@ def lib():
                                    vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp,
                                    vp, vp, vp, vp, sz, vp]
-    for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd):
+    L.qlora_merge.argtypes = [pnf4, vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
+    for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd, L.qlora_merge):
         f.restype = ctypes.c_int
     for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
         f.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -143,6 +144,12 @@ class NF4Weight:
 def qlora_quantize(W0, wq, stream=None):
     s = wq.struct() if isinstance(wq, NF4Weight) else wq
     _check(lib().qlora_quantize(_ptr(W0), ctypes.byref(s), _stream(stream)), "qlora_quantize")
+
+
+def qlora_merge(wq, A, B, r, adt, W, wdt, stream=None):
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    _check(lib().qlora_merge(ctypes.byref(s), _ptr(A), _ptr(B), int(r), int(adt), _ptr(W),
+                             int(wdt), _stream(stream)), "qlora_merge")
 
 
 def qlora_fwd_workspace_bytes(M, n_in, n_out, r, act=BF16):

@@ -188,6 +188,22 @@ def test_bwd_validation(L):
     assert f(*args(s=_nf4(192, 100))) == 2
 
 
+def test_merge_validation(L):
+    s = _nf4()
+    f = L.qlora_merge
+    assert f(ctypes.byref(s), P, P, 8, q.BF16, None, q.F32, None) == 1
+    assert f(ctypes.byref(s), P, P, 8, q.BF16, U, q.F32, None) == 3
+    assert f(ctypes.byref(s), None, P, 8, q.BF16, P, q.F32, None) == 1
+    assert f(ctypes.byref(s), P, U, 8, q.BF16, P, q.F32, None) == 3
+    assert f(ctypes.byref(s), P, P, -1, q.BF16, P, q.F32, None) == 2
+    assert f(ctypes.byref(s), P, P, 300, q.BF16, P, q.F32, None) == 2
+    assert f(ctypes.byref(s), P, P, 8, 3, P, q.F32, None) == 4
+    assert f(ctypes.byref(s), P, P, 8, q.BF16, P, 7, None) == 4
+    assert f(ctypes.byref(_nf4(256, 100)), P, P, 8, q.BF16, P, q.F32, None) == 2
+    assert f(ctypes.byref(_nf4(cb=3)), P, P, 8, q.BF16, P, q.F32, None) == 4
+    assert f(None, P, P, 8, q.BF16, P, q.F32, None) == 1
+
+
 def test_algorithmic_work_formulas():
     # fwd+bwd FLOP at 4096^2, r = 16, M = 2048 (without the dense dW)
     f = workloads.fwd_flops(2048, 4096, 4096, 16) + workloads.bwd_flops(2048, 4096, 4096, 16)

@@ -1,0 +1,95 @@
+"""GPU parity of qlora_merge (W = deq(Wq) + A.B) against the float64 oracle,
+the merged weight against the forward path, and re-quantization of the
+merged weight through qlora_quantize."""
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_rank_fine_amd import qlora as q
+
+from gpu_harness import Layer, bf16_to_f64, levels_of, out_to_f64, rel_err, say, torch_dev, TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _merge(L, wdt):
+    torch, dev = torch_dev()
+    W = torch.empty(L.n_in, L.n_out, dtype=torch.bfloat16 if wdt == "bf16" else torch.float32,
+                    device=dev)
+    q.qlora_merge(L.wq, L.tA, L.tB, L.r, L.qadt, W, q.BF16 if wdt == "bf16" else q.F32)
+    torch.cuda.synchronize()
+    return W
+
+
+def _ref(L):
+    A = None if L.A is None else L.A.values
+    B = None if L.B is None else L.B.values
+    return oracle.merge(L.w_hat(), A, B)
+
+
+@pytest.mark.parametrize("n_in,n_out,r,adt,wdt", [
+    (256, 256, 8, "f32", "f32"),          # small config shape, fp32 throughout
+    (640, 704, 16, "bf16", "bf16"),       # ragged last column tile (704 = 5.5 x 128)
+    (320, 448, 40, "f32", "bf16"),        # rank not a multiple of the 32-rank chunk
+    (192, 256, 100, "bf16", "f32"),       # several rank chunks
+    (256, 320, 0, "bf16", "f32"),         # rank 0: the dequantized weight
+])
+def test_merge_parity(n_in, n_out, r, adt, wdt):
+    say(f"[merge] {n_in}x{n_out} r={r} adt={adt} wdt={wdt}")
+    L = Layer(18, 64, n_in, n_out, r, act="bf16", adt=adt)
+    W = _merge(L, wdt)
+    ref = _ref(L)
+    if wdt == "f32":
+        # fp32 products and sums: a few fp32 ulps of the largest entries
+        err = rel_err(W.cpu().numpy(), ref)
+        assert err <= 1e-6, err
+    else:
+        got = bf16_to_f64(W)
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) * 2.0 ** 16
+        assert np.all(np.abs(got - ref) <= ulp), np.abs(got - ref).max()
+
+
+def test_merge_rank_zero_equals_dequantized_and_b_zero():
+    """r = 0 and B = 0 both give deq(Wq) exactly (as fp32 products)."""
+    L0 = Layer(19, 64, 256, 384, 0)
+    Lb = Layer(19, 64, 256, 384, 16, b_zero=True)
+    W0 = _merge(L0, "f32").cpu().numpy()
+    Wb = _merge(Lb, "f32").cpu().numpy()
+    assert np.array_equal(W0, Wb)
+    assert rel_err(W0, L0.w_hat()) <= 1e-6
+
+
+def test_merged_weight_reproduces_the_forward():
+    """X . W_merged equals the adapted layer's forward output y."""
+    L = Layer(20, 96, 384, 320, 16)
+    Y, _ = L.fwd()
+    W = _merge(L, "f32").cpu().numpy().astype(np.float64)
+    y_merged = L.X.values.astype(np.float64) @ W
+    assert rel_err(out_to_f64(Y, "bf16"), y_merged) <= TOL
+
+
+@pytest.mark.parametrize("codebook", [q.CB_NF4, q.CB_UNIFORM4])
+def test_requantize_merged_weight(codebook):
+    """The fp32 merged weight goes back through qlora_quantize: codes and
+    scales bit-exact against the oracle's quantizer on the same matrix; with
+    B = 0 the codes and block scales come back unchanged."""
+    torch, dev = torch_dev()
+    for b_zero in (False, True):
+        L = Layer(21, 64, 256, 512, 16, b_zero=b_zero, codebook=codebook)
+        W = _merge(L, "f32")
+        wq2 = q.NF4Weight(256, 512, dev, codebook)
+        q.qlora_quantize(W, wq2)
+        torch.cuda.synchronize()
+        ref = oracle.quantize(W.cpu().numpy(), levels_of(codebook))
+        assert np.array_equal(wq2.codes.cpu().numpy(), ref["packed"])
+        assert np.array_equal(wq2.qscale.cpu().numpy(), ref["q8"])
+        if b_zero:
+            assert np.array_equal(wq2.codes.cpu().numpy(), L.wq.codes.cpu().numpy())
+            assert np.array_equal(wq2.qscale.cpu().numpy(), L.wq.qscale.cpu().numpy())
+
+
+def test_merge_uniform4():
+    L = Layer(22, 64, 320, 448, 16, codebook=q.CB_UNIFORM4)
+    W = _merge(L, "f32")
+    assert rel_err(W.cpu().numpy(), _ref(L)) <= 1e-6
