@@ -10,6 +10,10 @@ adapters.  Inputs are resident in HBM before the timed region; five distinct
 W0 buffers (335 MB, more than the 256 MB Infinity Cache) are cycled so every
 quantize reads its weights from HBM.
 
+Warm-up runs at least W untimed steps and at least 0.3 s of them (the
+chip's clocks ramp over the first tens of milliseconds of load); the steps
+actually run are reported as `warmup_steps_run`.
+
 Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s (the dense dW
 is not formed and not counted), timed with HIP events around the forward and
 backward calls of every timed step; quantize GB/s is reported beside it.
@@ -39,6 +43,7 @@ METRIC = "QLoRA linear fwd+bwd TFLOP/s & quantize GB/s (% roofline), 4096² r=16
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 N_W0 = 5                      # distinct W0 buffers cycled by the quantize step
+SETTLE_S = 0.3                # minimum untimed warm-up time (clock settling)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -269,9 +274,17 @@ def main():
         q.qlora_linear_fwd(wq, X, M, q.BF16, A, B, r, q.BF16, Y, XA, wsf, fwb)
         q.qlora_linear_bwd(wq, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
 
-    for i in range(args.warmup):
-        quantize(i)
+    # Untimed warm-up: at least W steps and at least SETTLE_S seconds of them,
+    # so the timed steps run at the clocks the chip holds under this load (a
+    # cold start ramps over the first tens of milliseconds).
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < SETTLE_S:
+        quantize(n_warm)
         fwd_bwd()
+        n_warm += 1
+        if n_warm % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -376,6 +389,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
