@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="minimum seconds of untimed warm-up steps (clock settling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time of the oracle baseline")
@@ -274,12 +276,12 @@ def main():
         q.qlora_linear_fwd(wq, X, M, q.BF16, A, B, r, q.BF16, Y, XA, wsf, fwb)
         q.qlora_linear_bwd(wq, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
 
-    # Untimed warm-up: at least W steps and at least SETTLE_S seconds of them,
+    # Untimed warm-up: at least W steps and at least --settle seconds of them,
     # so the timed steps run at the clocks the chip holds under this load (a
     # cold start ramps over the first tens of milliseconds).
     t_w = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_w < SETTLE_S:
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.settle:
         quantize(n_warm)
         fwd_bwd()
         n_warm += 1
