@@ -20,6 +20,7 @@ What it computes (plain, slow, obviously correct):
   dX, dA, dB in float64, both in factored form and (for tiny shapes) through
   the dense weight gradient dW = X^T.dY exactly as the chain rule is written;
   the merged dense weight deq(Wq) + A.B.
+* ``optim``   -- one Adam (AdamW) step of an adapter matrix, in float64.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against values the pages print or against closed forms; no function is
@@ -41,6 +42,7 @@ from .nf4 import (
     storage_bits_per_weight,
 )
 from .linear import forward, backward, backward_via_dense_dw, merge
+from .optim import adam_step
 
 __all__ = [
     "nf4_levels",
@@ -60,5 +62,6 @@ __all__ = [
     "forward",
     "backward",
     "merge",
+    "adam_step",
     "backward_via_dense_dw",
 ]

@@ -408,3 +408,37 @@ def test_requantize_drops_sub_step_corrections():
         q2 = oracle.quantize(oracle.merge(W, A, frac * step * B).astype(np.float32))
         same = np.mean(q2["codes"] == q1["codes"])
         assert lo <= same <= hi, (frac, same)
+
+
+# --------------------------------------------------------------------------
+# Adam step of the adapters
+
+
+def check_adam(adam_step):
+    """Closed forms of the Adam step: the first step moves every coordinate by
+    lr * g / (|g| + eps) (bias correction makes m_hat = g, v_hat = g^2); a zero
+    gradient leaves theta unchanged without weight decay and shrinks it by
+    lr * wd with it; a constant gradient keeps the step at lr * g/(|g| + eps)
+    for every t; the moments follow their recurrences."""
+    g = np.array([0.5, -2.0, 1e-3, 0.0, 3.0])
+    th = np.array([1.0, -1.0, 0.25, 2.0, 0.0])
+    lr, eps = 1e-2, 1e-8
+    th1, m1, v1 = adam_step(th, g, np.zeros(5), np.zeros(5), 1, lr, eps=eps)
+    assert np.allclose(th - th1, lr * g / (np.abs(g) + eps), rtol=1e-12, atol=0)
+    assert np.allclose(m1, 0.1 * g, rtol=1e-15) and np.allclose(v1, 0.001 * g * g, rtol=1e-15)
+    th2, _, _ = adam_step(th, np.zeros(5), np.zeros(5), np.zeros(5), 1, lr)
+    assert np.array_equal(th2, th)
+    th3, _, _ = adam_step(th, np.zeros(5), np.zeros(5), np.zeros(5), 1, lr, weight_decay=0.1)
+    assert np.allclose(th3, th * (1 - lr * 0.1), rtol=1e-15)
+    gn = g[g != 0]
+    thc, m, v = th[g != 0].copy(), np.zeros(gn.size), np.zeros(gn.size)
+    for t in range(1, 6):
+        prev = thc
+        thc, m, v = adam_step(thc, gn, m, v, t, lr, eps=0.0)
+        assert np.allclose(prev - thc, lr * np.sign(gn), rtol=1e-12, atol=0)
+    assert np.allclose(m, (1 - 0.9 ** 5) * gn, rtol=1e-12)
+    assert np.allclose(v, (1 - 0.999 ** 5) * gn * gn, rtol=1e-12)
+
+
+def test_adam_pins():
+    check_adam(oracle.adam_step)

@@ -133,3 +133,17 @@ def _merge_wrong_sign(W, A=None, B=None):
 def test_wrong_sign_in_merge_is_caught():
     with pytest.raises(AssertionError):
         pins.check_merge(_merge_wrong_sign)
+
+
+def _adam_no_bias_correction(theta, g, m, v, t, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                             weight_decay=0.0):
+    """Mistake: the moments used without bias correction."""
+    theta, g = np.asarray(theta, np.float64), np.asarray(g, np.float64)
+    m = beta1 * np.asarray(m, np.float64) + (1 - beta1) * g
+    v = beta2 * np.asarray(v, np.float64) + (1 - beta2) * g * g
+    return theta - lr * (m / (np.sqrt(v) + eps) + weight_decay * theta), m, v
+
+
+def test_adam_without_bias_correction_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_adam(_adam_no_bias_correction)
