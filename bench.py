@@ -25,7 +25,8 @@ pass over the same K steps (per-launch events would lengthen the steps that
 repetitions of the full step, about 10 s of CPU work).  `decode` reports the
 few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
 `uniform4` repeats the timed steps with the uniform 4-bit codebook; `merge`
-times folding the adapters into a dense bf16 weight (HBM-bound).
+times folding the adapters into a dense bf16 weight (HBM-bound); `adam`
+times one optimizer step of A and B.
 """
 
 import argparse
@@ -347,6 +348,44 @@ def main():
              "what": "W = deq(Wq) + A.B written as dense bf16, r = 16"}
     del Wm
 
+    # Adam step of both adapter matrices (fp32 master copies, bf16 copies for
+    # the forward), K times.
+    na, nb = n_in * r, r * n_out
+    opt = {nm: [torch.zeros(nn, dtype=torch.float32, device=dev) for _ in range(4)]
+           for nm, nn in (("A", na), ("B", nb))}
+    for nm, (th, gr, _, _) in opt.items():
+        th.normal_(0.0, 0.02)
+        gr.normal_(0.0, 1e-3)
+    a16 = torch.empty(na, dtype=torch.bfloat16, device=dev)
+    b16 = torch.empty(nb, dtype=torch.bfloat16, device=dev)
+    # The K steps are captured in one HIP graph and replayed, so the time is
+    # the kernels' and not the Python launch path's (2 x 3.9 MB per step).
+    sgr = torch.cuda.Stream()
+    sgr.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(sgr):
+        q.qlora_adam_step(*opt["A"], 1, 1e-3, theta_bf16=a16)        # warm (uncaptured)
+        q.qlora_adam_step(*opt["B"], 1, 1e-3, theta_bf16=b16)
+    torch.cuda.current_stream().wait_stream(sgr)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(K):
+            q.qlora_adam_step(*opt["A"], i + 1, 1e-3, theta_bf16=a16)
+            q.qlora_adam_step(*opt["B"], i + 1, 1e-3, theta_bf16=b16)
+    ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ea0.record()
+    graph.replay()
+    ea1.record()
+    torch.cuda.synchronize()
+    adam_us = ea0.elapsed_time(ea1) * 1e3 / K
+    del graph
+    adam_bytes = (na + nb) * (16 + 12 + 2)
+    adam = {"us_per_step": round(adam_us, 2), "params": na + nb, "algorithmic_bytes": adam_bytes,
+            "GBps": round(adam_bytes / (adam_us * 1e-6) / 1e9, 1),
+            "what": "Adam step of A and B (fp32, two launches, bf16 copies written; HIP graph)"}
+    del opt
+
     ms_per_step = (t1 - t0) * 1e3 / K
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
     fb_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
@@ -409,6 +448,7 @@ def main():
         "kernels": kernels,
         "uniform4": uniform4,
         "merge": merge,
+        "adam": adam,
     }
     if not args.no_decode:
         out["decode"] = decode_report(args.decode_sets)

@@ -61,7 +61,8 @@ typedef enum {
   QLORA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned              */
   QLORA_ERR_DTYPE = 4,     /* unknown qlora_dtype or qlora_codebook         */
   QLORA_ERR_WORKSPACE = 5, /* ws too small (see qlora_bwd_workspace_bytes)  */
-  QLORA_ERR_DEVICE = 6     /* the HIP runtime reported an error             */
+  QLORA_ERR_DEVICE = 6,    /* the HIP runtime reported an error             */
+  QLORA_ERR_VALUE = 7      /* a hyperparameter out of its range             */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -189,6 +190,25 @@ size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
  */
 qlora_status qlora_merge(const qlora_nf4 *wq, const void *A, const void *B, int32_t r,
                          qlora_dtype adt, void *W, qlora_dtype wdt, hipStream_t stream);
+
+/*
+ * qlora_adam_step: one Adam step of an adapter matrix (A or B), in place.
+ * ("The code, line by line": the optimizer is handed only A and B.)  The
+ * pages do not print the update; this is the published Adam algorithm
+ * (Kingma & Ba) with decoupled weight decay (AdamW), per element in fp32:
+ *   m <- beta1*m + (1-beta1)*g;  v <- beta2*v + (1-beta2)*g*g;
+ *   theta <- theta - lr*((m*c1) / (sqrt(v*c2) + eps) + weight_decay*theta),
+ *   c1 = 1/(1 - beta1^step), c2 = 1/(1 - beta2^step) (double on the host,
+ *   rounded to fp32).  weight_decay = 0 is plain Adam.
+ *   theta, grad, m, v: n fp32 elements each (device, 16-B aligned; the
+ *   moments start at zero before step 1).  theta_bf16 (nullable): also
+ *   receives the updated theta in bf16, for a bf16 forward.
+ * n = 0 is a no-op.  step >= 1, 0 <= beta < 1, eps >= 0, weight_decay >= 0
+ * and finite lr, else QLORA_ERR_VALUE (n < 0 or step < 1: QLORA_ERR_SHAPE).
+ */
+qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v, int64_t n,
+                             int64_t step, float lr, float beta1, float beta2, float eps,
+                             float weight_decay, uint16_t *theta_bf16, hipStream_t stream);
 
 /* Human-readable name of a status code (host-only, static string). */
 const char *qlora_status_string(qlora_status s);

@@ -6,6 +6,7 @@
 // backward giving dA = dW B^T and dB = A^T dW (here in factored form,
 // dA = X^T (dY B^T) and dB = (X A)^T dY, so dW is never formed).
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -153,6 +154,7 @@ const char *qlora_status_string(qlora_status s) {
     case QLORA_ERR_DTYPE: return "invalid dtype";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_DEVICE: return "HIP runtime error";
+    case QLORA_ERR_VALUE: return "invalid value";
   }
   return "unknown status";
 }
@@ -341,6 +343,23 @@ qlora_status qlora_merge(const qlora_nf4 *wq, const void *A, const void *B, int3
   }
   return dev(launch_merge(wq->codes, wq->qscale, wq->gscale, wq->in, wq->out, A, B,
                           adt == QLORA_BF16, r, W, wdt == QLORA_BF16, wq->codebook, stream));
+}
+
+qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v, int64_t n,
+                             int64_t step, float lr, float beta1, float beta2, float eps,
+                             float weight_decay, uint16_t *theta_bf16, hipStream_t stream) {
+  if (n < 0 || step < 1) return QLORA_ERR_SHAPE;
+  const bool ok = std::isfinite(lr) && std::isfinite(eps) && std::isfinite(weight_decay) &&
+                  beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f &&
+                  eps >= 0.0f && weight_decay >= 0.0f;
+  if (!ok) return QLORA_ERR_VALUE;
+  if (n == 0) return QLORA_OK;
+  if (!theta || !grad || !m || !v) return QLORA_ERR_NULL;
+  if (!aligned16(theta) || !aligned16(grad) || !aligned16(m) || !aligned16(v) ||
+      (theta_bf16 && !aligned16(theta_bf16)))
+    return QLORA_ERR_ALIGN;
+  return dev(launch_adam(theta, grad, m, v, n, step, lr, beta1, beta2, eps, weight_decay,
+                         theta_bf16, stream));
 }
 
 int qlora_timing_enable(int kind_mask) {

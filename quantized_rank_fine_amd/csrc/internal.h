@@ -143,6 +143,12 @@ hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2,
                         int64_t out, const void *A, const void *B, bool a_bf16, int32_t r,
                         void *W, bool w_bf16, int codebook, hipStream_t s);
 
+// One Adam (AdamW) step over n fp32 elements in place (bias corrections for
+// step t >= 1); theta16, if not null, receives the updated theta as bf16.
+hipError_t launch_adam(float *theta, const float *g, float *m, float *v, int64_t n, int64_t step,
+                       float lr, float beta1, float beta2, float eps, float weight_decay,
+                       uint16_t *theta16, hipStream_t s);
+
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
 

@@ -18,7 +18,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 F32, BF16 = 0, 1
 CB_NF4, CB_UNIFORM4 = 0, 1          # qlora_codebook
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "pointer not 16-byte aligned",
-          4: "invalid dtype", 5: "workspace too small", 6: "HIP runtime error"}
+          4: "invalid dtype", 5: "workspace too small", 6: "HIP runtime error",
+          7: "invalid value"}
 KERNELS = ("quantize", "xa_rowdot", "fwd_gemm", "dy_pass", "dx_gemm", "da_pass", "reduce",
            "fwd_smallm")
 
@@ -55,7 +56,10 @@ def lib():
     L.qlora_linear_bwd.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp,
                                    vp, vp, vp, vp, sz, vp]
     L.qlora_merge.argtypes = [pnf4, vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
-    for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd, L.qlora_merge):
+    f32 = ctypes.c_float
+    L.qlora_adam_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
+    for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd, L.qlora_merge,
+              L.qlora_adam_step):
         f.restype = ctypes.c_int
     for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
         f.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -150,6 +154,15 @@ def qlora_merge(wq, A, B, r, adt, W, wdt, stream=None):
     s = wq.struct() if isinstance(wq, NF4Weight) else wq
     _check(lib().qlora_merge(ctypes.byref(s), _ptr(A), _ptr(B), int(r), int(adt), _ptr(W),
                              int(wdt), _stream(stream)), "qlora_merge")
+
+
+def qlora_adam_step(theta, grad, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                    weight_decay=0.0, theta_bf16=None, n=None, stream=None):
+    n = theta.numel() if n is None else int(n)
+    _check(lib().qlora_adam_step(_ptr(theta), _ptr(grad), _ptr(m), _ptr(v), n, int(step),
+                                 float(lr), float(beta1), float(beta2), float(eps),
+                                 float(weight_decay), _ptr(theta_bf16), _stream(stream)),
+           "qlora_adam_step")
 
 
 def qlora_fwd_workspace_bytes(M, n_in, n_out, r, act=BF16):

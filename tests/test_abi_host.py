@@ -112,7 +112,7 @@ def test_workspace_sizes(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert q.qlora_status_string(s) == q.STATUS[s]
 
 
@@ -202,6 +202,24 @@ def test_merge_validation(L):
     assert f(ctypes.byref(_nf4(256, 100)), P, P, 8, q.BF16, P, q.F32, None) == 2
     assert f(ctypes.byref(_nf4(cb=3)), P, P, 8, q.BF16, P, q.F32, None) == 4
     assert f(None, P, P, 8, q.BF16, P, q.F32, None) == 1
+
+
+def test_adam_validation(L):
+    f = L.qlora_adam_step
+    F = ctypes.c_float
+    ok = (P, P, P, P, 64, 1, F(1e-3), F(0.9), F(0.999), F(1e-8), F(0.0), None, None)
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[["th", "g", "m", "v", "n", "step", "lr", "b1", "b2", "eps", "wd", "t16", "s"].index(k)] = v
+        return f(*a)
+    assert call(n=0, th=None) == 0                     # no-op before any pointer check
+    assert call(th=None) == 1 and call(v=None) == 1
+    assert call(g=U) == 3 and call(t16=U) == 3
+    assert call(n=-1) == 2 and call(step=0) == 2
+    assert call(b1=F(1.0)) == 7 and call(b2=F(-0.1)) == 7
+    assert call(eps=F(-1.0)) == 7 and call(wd=F(-1e-3)) == 7
+    assert call(lr=F(float("inf"))) == 7
 
 
 def test_algorithmic_work_formulas():
