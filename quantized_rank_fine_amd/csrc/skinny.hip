@@ -6,22 +6,23 @@
 //   XA = X.A (forward),  G = dY.B^T,  dA = X^T.G,  dB = XA^T.dY (backward),
 // which are memory-bound passes over X or dY (r <= 256 << in, out).
 //
-// rowdot: C[M x R] = P[M x K] . Q, contraction along rows of P (P = X or dY,
-//         read once, coalesced).  Q is given either as Qt [R x K] (B for G)
-//         or as [K x R] (A for XA); a 64-wide K slice of it is staged in LDS
-//         in the [R][64] form the MFMA B operand reads.
-// coldot: C[K x R] = P[M x K]^T . Q[M x R], contraction over the token axis
-//         (P = X or dY, Q = G or XA given row-major).  P tiles are staged
-//         row-major in LDS and read transposed with ds_read_b64_tr_b16
-//         (16 lanes x 4 rows -> 4 columns).
-// Both split the contraction over workgroups and write fp32 partials that a
-// reduce pass sums in a fixed order (deterministic, no atomics).
+// rowfull: C[M x R] = P[M x K] . Q whole, R <= 32 and M >= 1024: a
+//          workgroup owns a few rows of P and all of K (no partials).
+// rowdot:  the same product split over K (any shape): a slice of Q is staged
+//          in LDS in the form the MFMA B operand reads; fp32 partials.
+// coldot:  C[K x R] = P[M x K]^T . Q[M x R], contraction over the token axis
+//          (P = X or dY, Q = G or XA given row-major).  P tiles are staged
+//          row-major in LDS and read transposed with ds_read_b64_tr_b16
+//          (16 lanes x 4 rows -> 4 columns); fp32 partials over token chunks.
+// Partials are summed by a reduce pass in a fixed order (deterministic, no
+// atomics).
 //
-// Launches are merged where the data allow it: the forward runs one prep
-// launch (XA partials + the GEMM's block scales) and one reduce; the backward
-// runs one pass over dY (G partials, dB partials, block scales), one reduce
-// of G and dB, one pass over X (dA partials) and one reduce of dA.  A merged
-// launch gives each role a contiguous range of workgroup ids.
+// Launches are merged where the data allow it, each role on a contiguous
+// range of workgroup ids (the block-scale table for the GEMMs first).  At
+// M >= 1024 and r <= 32 the forward runs one launch (XA whole + scales) and
+// the backward one pass over dY (G whole, dB partials, scales), one pass over
+// X (dA partials) and one reduce of dA and dB; otherwise X.A and G come as
+// split-K partials with a reduce after each pass.
 //
 // All matrix-core work is v_mfma_f32_16x16x32_bf16: operands rounded to bf16,
 // fp32 accumulation.
