@@ -33,6 +33,7 @@ def _ref(L):
     (640, 704, 16, "bf16", "bf16"),       # ragged last column tile (704 = 5.5 x 128)
     (320, 448, 40, "f32", "bf16"),        # rank not a multiple of the 32-rank chunk
     (192, 256, 100, "bf16", "f32"),       # several rank chunks
+    (128, 256, 256, "bf16", "bf16"),      # the largest rank accepted
     (256, 320, 0, "bf16", "f32"),         # rank 0: the dequantized weight
 ])
 def test_merge_parity(n_in, n_out, r, adt, wdt):
