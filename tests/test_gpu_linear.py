@@ -223,3 +223,48 @@ def test_65b_layer_r64_M8192_sampled(name, n_in, n_out, li):
     rows = np.random.default_rng(li).choice(8192, 48, replace=False)
     rows.sort()
     _check(L, rows=rows, tag=f"65b {name} r64 M8192")
+
+
+def test_two_streams_concurrently():
+    """Two layers on two non-default streams at once, each with its own
+    workspace: every output equals the same call alone on the default stream
+    (the library keeps no state between calls and launches only on the
+    caller's stream)."""
+    import torch
+    from quantized_rank_fine_amd import qlora as q
+    La = Layer(23, 300, 640, 704, 16)
+    Lb = Layer(24, 1030, 320, 448, 16, codebook=q.CB_UNIFORM4)
+    ref = {}
+    for name, L in (("a", La), ("b", Lb)):
+        Y, XA = L.fwd()
+        dX, dA, dB = L.bwd(XA=XA)
+        ref[name] = [t.float().cpu().numpy() for t in (Y, XA, dX, dA, dB)]
+    dev = torch.device("cuda:0")
+    outs = {}
+    streams = {"a": torch.cuda.Stream(), "b": torch.cuda.Stream()}
+    bufs = {}
+    for name, L in (("a", La), ("b", Lb)):
+        M, r = L.M, L.r
+        bufs[name] = dict(
+            Y=torch.empty(M, L.n_out, dtype=L.tdt, device=dev),
+            XA=torch.empty(M, r, dtype=torch.float32, device=dev),
+            dX=torch.empty(M, L.n_in, dtype=L.tdt, device=dev),
+            dA=torch.empty(L.n_in, r, dtype=torch.float32, device=dev),
+            dB=torch.empty(r, L.n_out, dtype=torch.float32, device=dev),
+            wf=torch.empty(q.qlora_fwd_workspace_bytes(M, L.n_in, L.n_out, r, L.qact), dtype=torch.uint8, device=dev),
+            wb=torch.empty(q.qlora_bwd_workspace_bytes(M, L.n_in, L.n_out, r, L.qact), dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    for _ in range(3):                       # interleave the two streams' launches
+        for name, L in (("a", La), ("b", Lb)):
+            b = bufs[name]
+            s = streams[name]
+            q.qlora_linear_fwd(L.wq, L.tX, L.M, L.qact, L.tA, L.tB, L.r, L.qadt, b["Y"], b["XA"],
+                               b["wf"], b["wf"].numel(), stream=s)
+            q.qlora_linear_bwd(L.wq, L.tX, L.tdY, L.M, L.qact, L.tA, L.tB, L.r, L.qadt, b["XA"],
+                               b["dX"], b["dA"], b["dB"], b["wb"], b["wb"].numel(), stream=s)
+    torch.cuda.synchronize()
+    for name in ("a", "b"):
+        b = bufs[name]
+        got = [b[k].float().cpu().numpy() for k in ("Y", "XA", "dX", "dA", "dB")]
+        for g, r_ in zip(got, ref[name]):
+            assert np.array_equal(g, r_), name
