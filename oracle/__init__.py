@@ -19,7 +19,8 @@ What it computes (plain, slow, obviously correct):
 * ``linear``  -- forward y = X.deq(Wq) + (X.A).B and the backward
   dX, dA, dB in float64, both in factored form and (for tiny shapes) through
   the dense weight gradient dW = X^T.dY exactly as the chain rule is written;
-  the merged dense weight deq(Wq) + A.B.
+  the merged dense weight deq(Wq) + A.B; adapters initialised from the
+  best rank-r approximation of the quantization residual W0 - deq(Q(W0)).
 * ``optim``   -- one Adam (AdamW) step of an adapter matrix, in float64.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
@@ -41,7 +42,7 @@ from .nf4 import (
     dequantize,
     storage_bits_per_weight,
 )
-from .linear import forward, backward, backward_via_dense_dw, merge
+from .linear import forward, backward, backward_via_dense_dw, merge, residual, loftq_init
 from .optim import adam_step
 
 __all__ = [
@@ -62,6 +63,8 @@ __all__ = [
     "forward",
     "backward",
     "merge",
+    "residual",
+    "loftq_init",
     "adam_step",
     "backward_via_dense_dw",
 ]

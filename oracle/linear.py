@@ -87,3 +87,24 @@ def merge(W_hat, A=None, B=None):
     if A is None or B is None or _f64(A).shape[1] == 0:
         return W
     return W + _f64(A) @ _f64(B)
+
+
+def residual(W0, W_hat):
+    """R = W0 - deq(Q(W0)) in float64: what the quantizer lost."""
+    return _f64(W0) - _f64(W_hat)
+
+
+def loftq_init(W0, W_hat, r):
+    """Adapters that start from the residual instead of zero.
+
+    "QLoRA (low-rank adapters on a quantized model)", "What QLoRA adds" (the
+    paragraph on running it and its relatives): LoftQ-style methods start A
+    and B from an SVD of W0 - Q(W0), so training begins closer to the
+    original model.  Reading taken: the best rank-r approximation of the
+    residual (truncated SVD, numpy's LAPACK routine as the step), split
+    evenly, A = U_r sqrt(S_r), B = sqrt(S_r) V_r^T.  Returns (A, B) float64.
+    """
+    R = residual(W0, W_hat)
+    U, S, Vt = np.linalg.svd(R, full_matrices=False)
+    s = np.sqrt(S[:r])
+    return U[:, :r] * s, s[:, None] * Vt[:r]

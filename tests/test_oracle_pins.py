@@ -442,3 +442,44 @@ def check_adam(adam_step):
 
 def test_adam_pins():
     check_adam(oracle.adam_step)
+
+
+# --------------------------------------------------------------------------
+# adapters started from the quantization residual
+
+
+def check_loftq(loftq_init):
+    """A residual of rank <= r is recovered exactly (A B = R); in general
+    |R - A B|_F^2 = |R|_F^2 - (sum of the r largest squared singular values)
+    (Eckart-Young), so the start is closer to W0 than B = 0 is; the factors
+    are balanced (A^T A = B B^T = diag(S_r))."""
+    g = np.random.default_rng(41)
+    W_hat = g.standard_normal((64, 96))
+    low = g.standard_normal((64, 3)) @ g.standard_normal((3, 96))
+    A, B = loftq_init(W_hat + low, W_hat, 4)
+    assert np.allclose(A @ B, low, rtol=0, atol=1e-10)
+    R = g.standard_normal((64, 96))
+    A, B = loftq_init(W_hat + R, W_hat, 5)
+    S = np.linalg.svd(R, compute_uv=False)
+    err = np.sum((R - A @ B) ** 2)
+    assert abs(err - (np.sum(R ** 2) - np.sum(S[:5] ** 2))) <= 1e-9 * np.sum(R ** 2)
+    assert err < np.sum(R ** 2)
+    assert np.allclose(A.T @ A, np.diag(S[:5]), atol=1e-10)
+    assert np.allclose(B @ B.T, np.diag(S[:5]), atol=1e-10)
+
+
+def test_loftq_pins():
+    check_loftq(oracle.loftq_init)
+
+
+def test_loftq_start_is_closer_than_zero():
+    """On a real quantization residual: the adapted layer at the start is
+    closer to the unquantized layer than the B = 0 start."""
+    w0 = synth.weights(256, 512, workload=7)
+    qd = oracle.quantize(w0)
+    W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], 256, 512)
+    A, B = oracle.loftq_init(w0, W, 16)
+    X = np.random.default_rng(5).standard_normal((32, 256))
+    e0 = np.linalg.norm(X @ w0.astype(np.float64) - X @ W)
+    e1 = np.linalg.norm(X @ w0.astype(np.float64) - oracle.forward(X, W, A, B)[1])
+    assert e1 < e0

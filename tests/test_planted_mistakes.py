@@ -147,3 +147,16 @@ def _adam_no_bias_correction(theta, g, m, v, t, lr, beta1=0.9, beta2=0.999, eps=
 def test_adam_without_bias_correction_is_caught():
     with pytest.raises(AssertionError):
         pins.check_adam(_adam_no_bias_correction)
+
+
+def _loftq_smallest(W0, W_hat, r):
+    """Mistake: the r smallest singular directions taken."""
+    R = np.asarray(W0, np.float64) - np.asarray(W_hat, np.float64)
+    U, S, Vt = np.linalg.svd(R, full_matrices=False)
+    s = np.sqrt(S[-r:])
+    return U[:, -r:] * s, s[:, None] * Vt[-r:]
+
+
+def test_loftq_smallest_directions_are_caught():
+    with pytest.raises(AssertionError):
+        pins.check_loftq(_loftq_smallest)
