@@ -26,7 +26,8 @@ repetitions of the full step, about 10 s of CPU work).  `decode` reports the
 few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
 `uniform4` repeats the timed steps with the uniform 4-bit codebook; `merge`
 times folding the adapters into a dense bf16 weight (HBM-bound); `adam`
-times one optimizer step of A and B.
+times one optimizer step of A and B; `loftq_init` times the start of A and B
+from the quantization residual.
 """
 
 import argparse
@@ -386,6 +387,26 @@ def main():
             "what": "Adam step of A and B (fp32, two launches, bf16 copies written; HIP graph)"}
     del opt
 
+    # LoftQ-style start of A and B (rank 16, 24 probe columns, 2 power
+    # iterations): a synchronous call, timed on the host clock.
+    kq = 24
+    gq = torch.Generator(device="cpu").manual_seed(7)
+    omega = torch.randn(n_out, kq, generator=gq).to(dev)
+    Aq = torch.empty(n_in, r, dtype=torch.bfloat16, device=dev)
+    Bq = torch.empty(r, n_out, dtype=torch.bfloat16, device=dev)
+    wsq_b = q.qlora_loftq_workspace_bytes(n_in, n_out, kq)
+    wsq = torch.empty(wsq_b, dtype=torch.uint8, device=dev)
+    q.qlora_quantize(W0s[0], wq)
+    q.qlora_loftq_init(W0s[0], wq, omega, kq, r, 2, Aq, Bq, q.BF16, wsq, wsq_b)
+    torch.cuda.synchronize()
+    tq0 = time.perf_counter()
+    for _ in range(3):
+        q.qlora_loftq_init(W0s[0], wq, omega, kq, r, 2, Aq, Bq, q.BF16, wsq, wsq_b)
+    loftq = {"ms": round((time.perf_counter() - tq0) * 1e3 / 3, 2), "rank": r, "probe_columns": kq,
+             "power_iterations": 2,
+             "what": "A, B from a rank-16 SVD of W0 - deq(Wq) (6 GPU residual products + host k x k work)"}
+    del wsq
+
     ms_per_step = (t1 - t0) * 1e3 / K
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
     fb_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
@@ -449,6 +470,7 @@ def main():
         "uniform4": uniform4,
         "merge": merge,
         "adam": adam,
+        "loftq_init": loftq,
     }
     if not args.no_decode:
         out["decode"] = decode_report(args.decode_sets)

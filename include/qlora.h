@@ -210,6 +210,30 @@ qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v
                              int64_t step, float lr, float beta1, float beta2, float eps,
                              float weight_decay, uint16_t *theta_bf16, hipStream_t stream);
 
+/*
+ * qlora_loftq_init: adapters started from the quantization residual instead
+ * of B = 0 ("What QLoRA adds", the paragraph on running it: LoftQ-style
+ * methods start A and B from an SVD of W0 - Q(W0)).
+ *   W0 [in, out] fp32 (the weight wq was quantized from), omega [out, k]
+ *   fp32: the caller's random test matrix (e.g. standard normal), k >= r
+ *   columns (r plus some oversampling, k <= 128 and k <= in, out).
+ *   Output A [in, r], B [r, out] in adt: the rank-r truncated SVD
+ *   U_r S_r V_r^T of R = W0 - deq(Wq), split as A = U_r sqrt(S_r),
+ *   B = sqrt(S_r) V_r^T, found by randomized subspace iteration with
+ *   `iters` power iterations (0..16; 2 is usual).  R is formed on the fly in
+ *   fp32 by the GPU products R.M and R^T.M; the small orthonormalisations and
+ *   the k x k SVD run on the host in double.  ws: qlora_loftq_workspace_bytes
+ *   (in, out, k) bytes of device memory.  The call is synchronous (it waits
+ *   for the stream) and cannot be captured in a graph.
+ */
+qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, const float *omega,
+                              int32_t k, int32_t r, int32_t iters, void *A, void *B,
+                              qlora_dtype adt, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes qlora_loftq_init needs (host-only); 0 for invalid
+ * arguments. */
+size_t qlora_loftq_workspace_bytes(int64_t in, int64_t out, int32_t k);
+
 /* Human-readable name of a status code (host-only, static string). */
 const char *qlora_status_string(qlora_status s);
 

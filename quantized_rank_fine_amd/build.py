@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
 
 SOURCES = ["api.cpp", "tables.cpp", "quantize.hip", "skinny.hip", "gemm.hip", "smallm.hip",
-           "merge.hip", "optim.hip"]
+           "merge.hip", "optim.hip", "loftq.hip", "loftq.cpp"]
 
 ARCH = "gfx950"
 COMMON = [

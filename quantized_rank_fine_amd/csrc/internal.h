@@ -149,6 +149,18 @@ hipError_t launch_adam(float *theta, const float *g, float *m, float *v, int64_t
                        float lr, float beta1, float beta2, float eps, float weight_decay,
                        uint16_t *theta16, hipStream_t s);
 
+// The 16 fp32 levels of a codebook, passed by value to a kernel.
+struct Levels16 {
+  float L[16];
+};
+
+// Products with the quantization residual R = W0 - deq(Wq) (formed on the
+// fly in fp32): transpose = false: Y [in x k] = R . M (M [out x k]);
+// transpose = true: Y [out x k] = R^T . M (M [in x k]); 1 <= k <= 128.
+hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8_t *q8,
+                               const float *s2, int64_t in, int64_t out, const float *M, int k,
+                               float *Y, bool transpose, int codebook, hipStream_t s);
+
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
 

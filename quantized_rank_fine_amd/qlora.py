@@ -58,8 +58,11 @@ def lib():
     L.qlora_merge.argtypes = [pnf4, vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
     f32 = ctypes.c_float
     L.qlora_adam_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
+    L.qlora_loftq_init.argtypes = [vp, pnf4, vp, i32, i32, i32, vp, vp, ctypes.c_int, vp, sz, vp]
+    L.qlora_loftq_workspace_bytes.argtypes = [i64, i64, i32]
+    L.qlora_loftq_workspace_bytes.restype = sz
     for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd, L.qlora_merge,
-              L.qlora_adam_step):
+              L.qlora_adam_step, L.qlora_loftq_init):
         f.restype = ctypes.c_int
     for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
         f.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -163,6 +166,17 @@ def qlora_adam_step(theta, grad, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-
                                  float(lr), float(beta1), float(beta2), float(eps),
                                  float(weight_decay), _ptr(theta_bf16), _stream(stream)),
            "qlora_adam_step")
+
+
+def qlora_loftq_workspace_bytes(n_in, n_out, k):
+    return int(lib().qlora_loftq_workspace_bytes(int(n_in), int(n_out), int(k)))
+
+
+def qlora_loftq_init(W0, wq, omega, k, r, iters, A, B, adt, ws, ws_bytes, stream=None):
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    _check(lib().qlora_loftq_init(_ptr(W0), ctypes.byref(s), _ptr(omega), int(k), int(r),
+                                  int(iters), _ptr(A), _ptr(B), int(adt), _ptr(ws),
+                                  int(ws_bytes), _stream(stream)), "qlora_loftq_init")
 
 
 def qlora_fwd_workspace_bytes(M, n_in, n_out, r, act=BF16):

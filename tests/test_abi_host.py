@@ -222,6 +222,24 @@ def test_adam_validation(L):
     assert call(lr=F(float("inf"))) == 7
 
 
+def test_loftq_validation(L):
+    f = L.qlora_loftq_init
+    s = _nf4(256, 256)
+    ws = q.qlora_loftq_workspace_bytes(256, 256, 24)
+    assert ws > 0 and q.qlora_loftq_workspace_bytes(256, 256, 0) == 0
+    ok = [P, ctypes.byref(s), P, 24, 16, 2, P, P, q.F32, P, ws, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == 1 and call(2, None) == 1 and call(9, None) == 1
+    assert call(3, 129) == 2 and call(4, 25) == 2 and call(4, 0) == 2 and call(5, -1) == 2
+    assert call(8, 5) == 4
+    assert call(6, U) == 3
+    assert call(10, ws - 1) == 5
+    assert call(1, ctypes.byref(_nf4(256, 100))) == 2
+
+
 def test_algorithmic_work_formulas():
     # fwd+bwd FLOP at 4096^2, r = 16, M = 2048 (without the dense dW)
     f = workloads.fwd_flops(2048, 4096, 4096, 16) + workloads.bwd_flops(2048, 4096, 4096, 16)
