@@ -6,6 +6,7 @@
 // backward giving dA = dW B^T and dB = A^T dW (here in factored form,
 // dA = X^T (dY B^T) and dB = (X A)^T dY, so dW is never formed).
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -97,10 +98,19 @@ FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   return p;
 }
 
+// dB folded into the dX GEMM (bf16 activations, r <= 16 and a multiple of 4,
+// G formed whole, at most a few dY tiles per GEMM workgroup): its partials
+// are per 256-token block, and the dY pass writes XA^T in bf16.
+bool db_in_dx(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
+  return act_bf16 && r > 0 && r <= 16 && r % 4 == 0 && g_complete(M, out, r) &&
+         dx_fold_fits(M, in, out);
+}
+
 struct BwdPlan {
   int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0, rp = 0;
+  int64_t ks_bx = 0, ldm = 0;   // dB folded into the dX GEMM: partials, XA^T row length
   size_t off_dy16 = 0, off_cs = 0, off_gpart = 0, off_g16 = 0;
-  size_t off_xapart = 0, off_xa = 0, off_dbpart = 0, off_dapart = 0, total = 0;
+  size_t off_xapart = 0, off_xa = 0, off_dbpart = 0, off_dapart = 0, off_xat = 0, total = 0;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
@@ -119,7 +129,12 @@ BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
     p.off_g16 = L.take(size_t(M) * p.rp * 2);
     if (p.ks_x) p.off_xapart = L.take(size_t(p.ks_x) * M * r * 4);
     p.off_xa = L.take(size_t(M) * r * 4);
-    p.off_dbpart = L.take(size_t(p.ks_b) * out * r * 4);
+    if (db_in_dx(M, in, out, r, act_bf16)) {
+      p.ks_bx = (M + 255) / 256;
+      p.ldm = p.ks_bx * 256;
+      p.off_xat = L.take(size_t(16) * p.ldm * 2);
+    }
+    p.off_dbpart = L.take(size_t(std::max(p.ks_b, p.ks_bx)) * out * r * 4);
     p.off_dapart = L.take(size_t(p.ks_a) * in * r * 4);
   }
   p.total = L.o;
@@ -294,12 +309,28 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
     XA = xaw;
   }
   // one pass over dY: G = dY . B^T (complete, or partials), dB = XA^T . dY
-  // partials, block scales
+  // partials (or, when the dX GEMM forms them, XA^T in bf16), block scales
   float *gpart = p.ks_g > 0 ? at<float>(ws, p.off_gpart) : nullptr;
   float *dbpart = r > 0 ? at<float>(ws, p.off_dbpart) : nullptr;
   if (r > 0) G16 = at<uint16_t>(ws, p.off_g16);
+  const bool fold = dX && p.ks_bx > 0;
+  uint16_t *xat = fold ? at<uint16_t>(ws, p.off_xat) : nullptr;
   QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XA, M, out, r, gpart, G16, p.rp,
-                                                dbpart, wq->qscale, wq->gscale, in, cs, stream));
+                                                dbpart, xat, p.ldm, wq->qscale, wq->gscale, in,
+                                                cs, stream));
+  if (fold) {
+    // dA = X^T . G; dX and the dB partials in the GEMM; dA and dB (stored
+    // [r x out]) in one reduction launch
+    float *dapart = at<float>(ws, p.off_dapart);
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+    QLORA_RUN(QLORA_KERNEL_DX_GEMM,
+              launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
+                             xb, wq->codebook, xat, p.ldm, dbpart, stream));
+    QLORA_RUN(QLORA_KERNEL_REDUCE,
+              launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_bx, out,
+                             dB, true, nullptr, 0, stream));
+    return QLORA_OK;
+  }
   if (r > 0) {
     float *dapart = at<float>(ws, p.off_dapart);
     if (p.ks_g > 0) {
@@ -323,7 +354,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
   if (dX) {
     QLORA_RUN(QLORA_KERNEL_DX_GEMM,
               launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
-                             xb, wq->codebook, stream));
+                             xb, wq->codebook, nullptr, 0, nullptr, stream));
   }
   return QLORA_OK;
 #undef QLORA_RUN

@@ -101,16 +101,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // conservative wait for these LDS writes into the pipeline's vmcnt waits; the
 // ring protocol below waits and synchronizes explicitly.  No register is
 // written by these loads.
+// The LDS address and the scalar offset are wavefront-uniform by construction;
+// readfirstlane keeps them in SGPRs wherever the compiler cannot prove it.
 __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory", "m0");
 }
 
@@ -225,12 +229,65 @@ __device__ __forceinline__ uint32_t xoff(int row, int c) { return row * 128 + ((
 //   A16: activations bf16 [M x K]; codes; cs: scales fp32 [blocks][rows].
 //   Forward: weight rows = K (k), columns = N; cs row count = K.
 //   dX:      weight rows = N (i), columns = K; cs row count = N.
+// dB = XA^T . dY taken over by the dX GEMM (ranks r <= 16).  The workgroup of
+// token block tb = m0 / 256 and output-column block cw = n0 / 128 multiplies
+// the dY tiles kt = cw, cw + ncw, ... of its LDS ring by XA^T over its 256
+// tokens: wavefront w owns the 16 dB columns 64 kt + 16 w .. + 15, eight
+// v_mfma_f32_16x16x32_bf16 with XA^T (rows = ranks) as the A operand, held in
+// registers from the start, and dY read transposed out of the swizzled tile
+// with ds_read_b64_tr_b16.  Every column of dB is formed once per token block,
+// as part[tb][n][j] (fp32), which a fixed-order reduction sums over tb.
+struct DbFold {
+  const uint16_t *xat;   // XA^T bf16 [16 x ldm], zero for ranks >= r, tokens >= M
+  int64_t ldm;
+  float *part;           // [ceil(M / 256)][K][r]; nullptr: no dB here
+  int r;
+  int ncw;               // output-column blocks of the launch
+};
+constexpr int kMaxDbTiles = 4;               // dB tiles per workgroup, at most
+constexpr uint32_t kNoStore = 0xffffffffu;   // no dB results for this lane
+
+// 4 consecutive rows of one column of a bf16 tile, transposed across a
+// 16-lane group (see lds_col8_32).
+__device__ __forceinline__ u32x2_t lds_tr4(const char *p) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((lds_char *)(p)));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// The eight dB products of one tile as one chain on VGPR accumulators.  Every
+// AGPR holds a GEMM accumulator, and the builtin form would take four of them
+// (the compiler then moves an accumulator block through VGPRs on every
+// iteration).  The products accumulate back to back on the same registers
+// (srcC = vdst, the form the hardware forwards); the leading s_nop covers a
+// VALU write of an operand just before, the trailing ones the wait states
+// before any VALU or memory instruction reads the result.
+__device__ __forceinline__ f32x4_t db_chain(const u32x4_t (&a)[8], const u32x4_t (&b)[8]) {
+  f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %1, %9, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %10, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %11, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %14, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %7, %15, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %8, %16, %0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(d)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
+  return d;
+}
+
 template <bool kFwd>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, int64_t M, int64_t K,
                                               int64_t N, const uint8_t *__restrict__ codes,
                                               const float *__restrict__ cs, int64_t m0, int64_t n0,
                                               const ExpandConsts &tb, char *smem,
-                                              f32x16_t (&acc)[2][8]) {
+                                              f32x16_t (&acc)[2][8], const DbFold &dbf) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets go to M0
   const int ch = wave & 1, kh = wave >> 1;
@@ -389,6 +446,54 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(a[i], bb[b], acc[b][i]);
   };
 
+  // dB fold.  XA^T of the workgroup's 256 tokens (8 KiB bf16) goes to the
+  // LDS area the forward uses as expansion scratch, by direct-to-LDS loads
+  // issued before the prologue's (so its first wait covers them): row j =
+  // rank j (512 B), 16-B token chunk t stored in slot t ^ j so that the 16
+  // ranks of one chunk read from distinct banks.  A operand of the
+  // 16 x 16 x 32 products: lane = rank j (lane & 15), tokens 32 s + 8 g ..
+  // + 7 (g = lane >> 4), i.e. chunk 4 s + g.  B operand: lane i16 = 4 tq + q
+  // of group g points at dY row 32 s + 8 g + tq (+ 4), columns 16 w + 4 q ..
+  // + 3 (16-B chunk 2 w + (q >> 1), half q & 1); the row swizzle does not
+  // depend on s, so the eight steps are fixed offsets 4096 s from two
+  // per-lane offsets.  Lane results: ranks 4 g .. 4 g + 3 of dB column
+  // 64 kt + 16 w + i16.
+  int db_first = KT;                // first tile whose dB columns this workgroup forms
+  uint32_t db_lo = 0, db_hi = 0, db_a = 0;
+  uint32_t db_off = kNoStore;       // byte offset of this lane's results for tile 0
+  f32x4_t db_res[kMaxDbTiles];
+  char *const sxat = smem + kRingBytes;
+  if constexpr (!kFwd) {
+    if (dbf.part) {
+      const rsrc_t rA = make_rsrc(dbf.xat, 16 * dbf.ldm * 2);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int j = 2 * (2 * wave + p) + (lane >> 5), t = (lane & 31) ^ j;
+        lds_load16(rA, lds_addr(sxat) + (2 * wave + p) * 1024,
+                   uint32_t((j * dbf.ldm + m0 + 8 * t) * 2), 0u);
+      }
+      const int i16 = lane & 15, g = lane >> 4, q = i16 & 3, tq = i16 >> 2;
+      db_first = __builtin_amdgcn_readfirstlane(int(n0 / BN) < KT ? int(n0 / BN) : KT);
+      db_a = uint32_t(i16 * 512 + 16 * (g ^ i16));    // + 64 s: chunk (4 s + g) ^ i16
+      const int c = 2 * wave + (q >> 1);
+      db_lo = xoff(8 * g + tq, c) + 8 * (q & 1);
+      db_hi = xoff(8 * g + tq + 4, c) + 8 * (q & 1);
+      if (4 * g < dbf.r)                              // ranks past r: nothing to store
+        db_off = uint32_t((((m0 / BM) * K + 16 * wave + i16) * dbf.r + 4 * g) * 4);
+    }
+  }
+  auto db_tile = [&](const char *st) {
+    u32x4_t xa[8], bt[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      xa[s] = *reinterpret_cast<const u32x4_t *>(sxat + (db_a ^ uint32_t(64 * s)));
+      const u32x2_t lo = lds_tr4(st + db_lo + 4096 * s);
+      const u32x2_t hi = lds_tr4(st + db_hi + 4096 * s);
+      bt[s] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+    return db_chain(xa, bt);
+  };
+
   // ---- prologue: tiles 0..kStages-1 in flight (clamped to the last tile);
   // tiles 0 and 1 landed and visible.
   static_assert(kStages >= 4, "the pipeline keeps two tiles visible ahead of the issue");
@@ -450,10 +555,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
     // are visible; a0/b0 hold substep 0 of tile kt and nib/sc its codes and
     // scales.  Codes and scales are read one half-step before they are
     // expanded, so no expansion waits on LDS.
-    read_tile(smem, nib, sc);
-    read_a(smem, 0, a0);
-    make_b(nib, sc, 0, b0);
-    for (int kt = 0; kt < KT; ++kt) {
+    auto body = [&](int kt) {
       const char *st = smem + (kt % kStages) * kStageBytes;
       const char *sn = smem + ((kt + 1) % kStages) * kStageBytes;
       // substep 0 of tile kt; prepare substep 1 and fetch tile kt+1's codes
@@ -479,9 +581,40 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       }
 #pragma unroll
       for (int q = 0; q < kNS; ++q) sc[q] = scn[q];
+    };
+    read_tile(smem, nib, sc);
+    read_a(smem, 0, a0);
+    make_b(nib, sc, 0, b0);
+    // The K loop runs in segments that end at the workgroup's dB tiles: the
+    // dB columns of tile d are formed at the top of iteration d (its stage
+    // visible, freed only by that iteration's barrier), between two runs of
+    // the unbranched loop body, and held in registers until the loop is over,
+    // so that no store enters the loop's vmcnt waits.
+    // (kt and the segment ends are uniform; readfirstlane keeps them scalar)
+    int kt = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxDbTiles; ++i) {
+      const int d = __builtin_amdgcn_readfirstlane(db_first + i * dbf.ncw);
+      const int e = d < KT ? d : KT;
+      for (; kt < e; ++kt) body(kt);
+      kt = __builtin_amdgcn_readfirstlane(kt);
+      db_res[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (d < KT) db_res[i] = db_tile(smem + (d % kStages) * kStageBytes);
     }
+    for (; kt < KT; ++kt) body(kt);
   }
   wait_vmcnt<0>();
+  if constexpr (!kFwd) {
+    if (db_off != kNoStore) {
+#pragma unroll
+      for (int i = 0; i < kMaxDbTiles; ++i) {
+        const int d = db_first + i * dbf.ncw;
+        if (d < KT)
+          *reinterpret_cast<f32x4_t *>(reinterpret_cast<char *>(dbf.part) + db_off +
+                                       int64_t(d) * BK * dbf.r * 4) = db_res[i];
+      }
+    }
+  }
 }
 
 // The adapter factor of the rank-r term, read in the caller's layout and
@@ -652,7 +785,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
-  gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc);
+  gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc, DbFold{});
   // rank-r term: y += XA16 . B (B read as rows n of B^T)
   epilogue<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
 }
@@ -663,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t IN, int64_t OUT,
     const uint16_t *__restrict__ dY16, int64_t M, const uint16_t *__restrict__ G16,
     int ldp, AdapterRef aq, void *__restrict__ dX, ExpandConsts tb,
-    int nt_count) {
+    int nt_count, DbFold dbf) {
   extern __shared__ __align__(16) char smem[];
   int mt, nt;
   tile_of(nt_count, mt, nt);
@@ -678,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
-  gemm_mainloop<false>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc);
+  gemm_mainloop<false>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc, dbf);
   // rank-r term: dX += G16 . A^T (A read as rows i of A)
   epilogue<kOutBf16>(acc, smem, ro, G16, ldp, aq, M, IN, m0, i0, dX);
 }
@@ -715,13 +848,25 @@ hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int
   return hipGetLastError();
 }
 
+bool dx_fold_fits(int64_t M, int64_t in, int64_t out) {
+  const int64_t ncw = (in + BN - 1) / BN, kt = out / BK;
+  return M > 0 && (kt + ncw - 1) / ncw <= kMaxDbTiles;
+}
+
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int64_t out,
                           const uint16_t *dY16, int64_t M, const uint16_t *G16, int32_t ldp,
                           const void *A, bool a_bf16, int32_t r, void *dX, bool dx_bf16,
-                          int codebook, hipStream_t s) {
+                          int codebook, const uint16_t *xat, int64_t ldm, float *db_part,
+                          hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef aq{A, a_bf16, int64_t(r), 1, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((in + BN - 1) / BN);
+  // the XA^T fragments of the last token block reach token mtc * 256 - 1
+  if (db_part && (!xat || r < 1 || r > 16 || r % 4 != 0 || ldm < int64_t(mtc) * BM))
+    return hipErrorInvalidValue;
+  const DbFold dbf{xat, ldm, db_part, int(r), ntc};
+  if (db_part && (!dx_fold_fits(M, in, out) || int64_t(mtc) * out * r * 4 > 0x7fffffff))
+    return hipErrorInvalidValue;
   dim3 grid(unsigned(mtc * ntc));
   if (!tables(codebook).symmetric) return hipErrorInvalidValue;
   const ExpandConsts tb = tables(codebook).expand;
@@ -730,7 +875,7 @@ hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int
     static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB>));             \
     if (!ok) return hipErrorInvalidValue;                                                      \
     hipLaunchKernelGGL((dx_gemm_kernel<OB>), grid, dim3(kThreads), kLdsBytes, s, codes, cs,   \
-                       in, out, dY16, M, G16, int(ldp), aq, dX, tb, ntc);                      \
+                       in, out, dY16, M, G16, int(ldp), aq, dX, tb, ntc, dbf);                 \
   } while (0)
   if (dx_bf16)
     QLORA_DX(true);

@@ -81,12 +81,15 @@ hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf1
 // into G16 (bf16 [M x ldg], zero-padded) when g_complete(M, out, r), else as
 // partials g_part[ks][M][r]; db_part[ks][out][r] = partial dY^T . XA (XA fp32
 // [M x r]); and, if cs != nullptr, the block scales as in launch_fwd_prep.
+// With xat != nullptr (only when r <= 16 and g_complete; ldm a multiple of
+// 256, >= M) the dB partials are left to launch_dx_gemm and the launch
+// instead writes xat [16 x ldm] = XA^T in bf16, zero-padded.
 bool g_complete(int64_t M, int64_t out, int64_t r);
 hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf16,
                          const float *XA, int64_t M, int64_t out, int64_t r,
                          float *g_part, uint16_t *G16, int64_t ldg, float *db_part,
-                         const int8_t *qscale, const float *gscale, int64_t in, float *cs,
-                         hipStream_t s);
+                         uint16_t *xat, int64_t ldm, const int8_t *qscale,
+                         const float *gscale, int64_t in, float *cs, hipStream_t s);
 
 // Backward pass over X: da_part[ks][in][r] = partial X^T . G with G given as
 // G16 bf16 [M x ldg].
@@ -114,10 +117,15 @@ hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K,
 
 // dX = dY16 . deq(Wq)^T + G16 . A^T.  dY16 [M x out] bf16; G16 [M x ldp] bf16
 // zero-padded; A [in x r] (f32 or bf16) as given; cs as in the forward.
+// With db_part != nullptr (r <= 16, r % 4 == 0, dx_fold_fits; xat from
+// launch_bwd_dy) also db_part[ceil(M / 256)][out][r] = XA^T . dY over each
+// 256-token block.
+bool dx_fold_fits(int64_t M, int64_t in, int64_t out);
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
                           int64_t out, const uint16_t *dY16, int64_t M,
                           const uint16_t *G16, int32_t ldp, const void *A,
                           bool a_bf16, int32_t r, void *dX, bool dx_bf16, int codebook,
+                          const uint16_t *xat, int64_t ldm, float *db_part,
                           hipStream_t s);
 
 // Small-M forward (M <= kSmallMaxM tokens, r <= kSmallMaxR), two launches:

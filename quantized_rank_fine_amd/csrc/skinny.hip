@@ -149,6 +149,35 @@ __device__ __forceinline__ void scales_role(const ScalesArgs &a, int64_t wg) {
     if (e < nb) a.cs[(b0 + e) * a.rows + row] = c[e];
 }
 
+// ------------------------------------------------------- XA^T for the dX GEMM
+// xat[j][m] = bf16(XA[m][j]) for j < 16, m < ldm (ldm a multiple of 256), zero
+// for j >= r or m >= M: the A operand of the dB products that the dX GEMM
+// takes from the dY tiles in its LDS ring.  A thread owns 8 consecutive
+// tokens of one rank index (one 16-B store).  Role of a merged launch.
+struct XatArgs {
+  const float *XA;    // [M x r]
+  int64_t M;
+  int r;
+  uint16_t *xat;      // [16 x ldm]
+  int64_t ldm;
+};
+
+__host__ __device__ inline int64_t xat_workgroups(int64_t ldm) { return ldm * 16 / 2048; }
+
+__device__ __forceinline__ void xat_role(const XatArgs &a, int64_t wg) {
+  const int64_t e0 = (wg * 256 + threadIdx.x) * 8;    // first element, row-major [16][ldm]
+  const int j = int(e0 / a.ldm);
+  const int64_t m0 = e0 % a.ldm;
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t m = m0 + e;
+    h[e] = (j < a.r && m < a.M) ? uint32_t(f32_to_bf16_bits(a.XA[m * a.r + j])) : 0u;
+  }
+  *reinterpret_cast<u32x4_t *>(a.xat + e0) =
+      u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
 // ------------------------------------------------------------------ rowdot
 //
 // Workgroup: 4 wavefronts x 16 rows = 64 rows of P, all R columns, one
@@ -757,20 +786,30 @@ __global__ __launch_bounds__(256) void fwd_full_kernel(RowfullArgs ra, int64_t n
     rowfull_role<kXbf16, kQFast, kAbf16, kRT>(ra, wg - n_sc, smem);
 }
 
-// One pass over dY with G complete: block scales on [0, n_sc), G = dY . B^T
-// (rowfull with Qt = B [r x out]) on [n_sc, n_sc + n_row), dB partials
-// (coldot with Q = XA fp32 [M x r]) on the rest.
+// One pass over dY with G complete: block scales on [0, n_sc), XA^T bf16 on
+// [n_sc, n_sc + n_xat) (only when the dX GEMM takes dB over), G = dY . B^T
+// (rowfull with Qt = B [r x out]) on the next n_row, and otherwise dB
+// partials (coldot with Q = XA fp32 [M x r]) on the rest.
 template <bool kDYbf16, bool kBbf16, int kRT, bool kQFastC>
 __global__ __launch_bounds__(256) void dy_full_kernel(RowfullArgs ra, int64_t n_row, ColdotArgs ca,
-                                                      int64_t n_sc, ScalesArgs sa) {
+                                                      int64_t n_sc, ScalesArgs sa, int64_t n_xat,
+                                                      XatArgs xa) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int64_t wg = blockIdx.x;
-  if (wg < n_sc)
+  int64_t wg = blockIdx.x;
+  if (wg < n_sc) {
     scales_role(sa, wg);
-  else if (wg < n_sc + n_row)
-    rowfull_role<kDYbf16, kQRows, kBbf16, kRT>(ra, wg - n_sc, smem);
+    return;
+  }
+  wg -= n_sc;
+  if (wg < n_xat) {
+    xat_role(xa, wg);
+    return;
+  }
+  wg -= n_xat;
+  if (wg < n_row)
+    rowfull_role<kDYbf16, kQRows, kBbf16, kRT>(ra, wg, smem);
   else
-    coldot_role<kDYbf16, false, true, kQFastC>(ca, wg - n_sc - n_row, smem);
+    coldot_role<kDYbf16, false, true, kQFastC>(ca, wg - n_row, smem);
 }
 
 // One pass over dY: block scales on [0, n_sc), G partials (rowdot with
@@ -964,26 +1003,32 @@ hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf1
 
 hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf16,
                          const float *XA, int64_t M, int64_t out, int64_t r, float *g_part,
-                         uint16_t *G16, int64_t ldg, float *db_part, const int8_t *qscale,
-                         const float *gscale, int64_t in, float *cs, hipStream_t s) {
+                         uint16_t *G16, int64_t ldg, float *db_part, uint16_t *xat,
+                         int64_t ldm, const int8_t *qscale, const float *gscale, int64_t in,
+                         float *cs, hipStream_t s) {
   int64_t n_col = 0;
   const ColdotArgs ca = coldot_args(dY, XA, r, M, out, r, db_part, n_col);
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
   const int64_t n_sc = cs ? scales_workgroups(in, out / 64) : 0;
+  if (xat && !(r > 0 && r <= 16 && g_complete(M, out, r) && ldm % 256 == 0 && ldm >= M))
+    return hipErrorInvalidValue;
   if (r > 0 && g_complete(M, out, r)) {
     int64_t n_full = 0;
     const RowfullArgs fa = rowfull_args(dY, B, M, out, r, nullptr, G16, ldg, n_full);
-    const dim3 grid = dim3(unsigned(n_sc + n_full + n_col));
+    const XatArgs xa{XA, M, int(r), xat, ldm};
+    const int64_t n_xat = xat ? xat_workgroups(ldm) : 0;
+    if (xat) n_col = 0;    // dB is formed by the dX GEMM
+    const dim3 grid = dim3(unsigned(n_sc + n_xat + n_full + n_col));
     const size_t lds_full = rowfull_lds_bytes<kQRows, 2>();
     const size_t lds = coldot_lds(r) > lds_full ? coldot_lds(r) : lds_full;
 #define QLORA_DYF2(DB, BB, RT)                                                                  \
   do {                                                                                          \
     if (r % 8 == 0)                                                                             \
       hipLaunchKernelGGL((dy_full_kernel<DB, BB, RT, true>), grid, dim3(256), lds, s, fa, n_full, \
-                         ca, n_sc, sa);                                                         \
+                         ca, n_sc, sa, n_xat, xa);                                              \
     else                                                                                        \
       hipLaunchKernelGGL((dy_full_kernel<DB, BB, RT, false>), grid, dim3(256), lds, s, fa,       \
-                         n_full, ca, n_sc, sa);                                                 \
+                         n_full, ca, n_sc, sa, n_xat, xa);                                      \
   } while (0)
 #define QLORA_DYF(DB, BB)                                                                       \
   do {                                                                                          \
@@ -998,6 +1043,7 @@ hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf1
 #undef QLORA_DYF
     return hipGetLastError();
   }
+  if (xat) return hipErrorInvalidValue;
   int64_t n_row = 0;
   const RowdotArgs ra = rowdot_args(dY, B, M, out, r, g_part, n_row);
   if (n_row + n_col + n_sc == 0) return hipSuccess;

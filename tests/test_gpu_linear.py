@@ -91,6 +91,9 @@ def test_few_tokens(M, n_in, n_out, r, act, adt):
     (1100, 1088, 320, 24, "f32", "f32"),    # fp32 operands, rank tile pair, two batches
     (1024, 640, 704, 12, "bf16", "bf16"),   # r % 8 != 0: G complete, XA split-K
     (4100, 128, 192, 32, "bf16", "f32"),    # 16-row workgroups, one k step per wavefront
+    (1300, 384, 320, 12, "bf16", "bf16"),   # dB in the dX GEMM, ragged last token block
+    (1100, 1088, 192, 8, "bf16", "f32"),    # dB in the dX GEMM: more column blocks than dY tiles
+    (1300, 384, 320, 10, "bf16", "bf16"),   # r % 4 != 0: dB stays in the dY pass
 ])
 def test_complete_rank_products(M, n_in, n_out, r, act, adt):
     """Token counts where X . A and dY . B^T are formed whole per workgroup
