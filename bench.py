@@ -423,8 +423,9 @@ def main():
                 "quantize_ms_per_step": round(uq_ms / K, 4)}
 
     kernels = {}
+    # at this workload the dX GEMM also forms dB = XA^T dY (2 M r out flops)
     per_launch_flops = {"fwd_gemm": 2 * M * n_out * (n_in + r),
-                        "dx_gemm": 2 * M * n_in * (n_out + r)}
+                        "dx_gemm": 2 * M * n_in * (n_out + r) + 2 * M * r * n_out}
     for name in ("fwd_gemm", "dx_gemm"):
         tot, n = q.qlora_timing_read(q.KERNELS.index(name))
         avg = tot / max(n, 1)
