@@ -24,7 +24,9 @@ pass over the same K steps (per-launch events would lengthen the steps that
 `cpu_baseline` times the CPU oracle on the same workload (bounded to a few
 repetitions of the full step, about 10 s of CPU work).  `decode` reports the
 few-token forward (7B-style layer sets, M = 1, 4, 16) in GB/s against HBM.
-`uniform4` repeats the timed steps with the uniform 4-bit codebook; `merge`
+`uniform4` repeats the timed steps with the uniform 4-bit codebook;
+`lora_options` repeats the fwd+bwd steps with the alpha/r factor and dropout
+on X.A; `merge`
 times folding the adapters into a dense bf16 weight (HBM-bound); `adam`
 times one optimizer step of A and B; `loftq_init` times the start of A and B
 from the quantization residual.
@@ -330,6 +332,27 @@ def main():
         evu[i][2].record()
     torch.cuda.synchronize()
 
+    # The adapter options (alpha/r = 2, dropout p = 0.05 on X.A with a fixed
+    # seeded keep mask): the same K fwd+bwd steps through the options entry
+    # points.
+    keep = (torch.rand(M, r, generator=torch.Generator(device="cpu").manual_seed(11)) >= 0.05)
+    keep = keep.to(torch.uint8).to(dev)
+    lopt = (2.0, 0.05, keep)
+    for _ in range(args.warmup):
+        q.qlora_linear_fwd_lora(wq, X, M, q.BF16, A, B, r, q.BF16, *lopt, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd_lora(wq, X, dY, M, q.BF16, A, B, r, q.BF16, *lopt, XA, dX, dA, dB,
+                                wsb, bwb)
+    el0, el1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    el0.record()
+    for i in range(K):
+        q.qlora_linear_fwd_lora(wq, X, M, q.BF16, A, B, r, q.BF16, *lopt, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd_lora(wq, X, dY, M, q.BF16, A, B, r, q.BF16, *lopt, XA, dX, dA, dB,
+                                wsb, bwb)
+    el1.record()
+    torch.cuda.synchronize()
+    lora_ms = el0.elapsed_time(el1) / K
+
     # Merge (fold the adapters into a dense bf16 weight), K launches.
     Wm = torch.empty(n_in, n_out, dtype=torch.bfloat16, device=dev)
     q.qlora_merge(wq, A, B, r, q.BF16, Wm, q.BF16)
@@ -422,6 +445,10 @@ def main():
                 "fwd_bwd_ms_per_step": round(ufb_ms / K, 4),
                 "quantize_ms_per_step": round(uq_ms / K, 4)}
 
+    lora = {"what": "fwd+bwd with alpha/r = 2 and dropout p = 0.05 on X.A (keep mask given)",
+            "fwd_bwd_TFLOPs": round(flops / (lora_ms * 1e-3) / 1e12, 2),
+            "fwd_bwd_ms_per_step": round(lora_ms, 4)}
+
     kernels = {}
     # at this workload the dX GEMM also forms dB = XA^T dY (2 M r out flops)
     per_launch_flops = {"fwd_gemm": 2 * M * n_out * (n_in + r),
@@ -469,6 +496,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "uniform4": uniform4,
+        "lora_options": lora,
         "merge": merge,
         "adam": adam,
         "loftq_init": loftq,

@@ -177,6 +177,44 @@ size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
                                  qlora_dtype act);
 
 /*
+ * Adapter options ("LoRA & QLoRA", sections Scaling Factor alpha and
+ * Dropout): the rank-r path becomes alpha/r . B(dropout(A x)), in row form
+ *   U = c * (keep o XA),  c = scale / (1 - dropout_p),
+ *   y = X.deq(Wq) + U.B,
+ * with keep the caller's dropout draw (the library draws no random numbers).
+ *   scale      alpha / r; any finite value (1 = no scaling).
+ *   dropout_p  the dropout probability, 0 <= p < 1; kept elements are scaled
+ *              by 1 / (1 - p) (inverted dropout).
+ *   keep       [M, r] uint8 row-major, device, nonzero = kept; NULL = no
+ *              dropout (then dropout_p must be 0).  The same mask must be
+ *              passed to the forward and the backward of one step.
+ * c is computed in double and rounded to fp32 once.  The backward follows
+ * the chain rule: G' = c * (keep o dY.B^T) takes G's place in dX and dA, and
+ * dB = U^T.dY.  XA (the saved activation) is always the plain X.A.  Invalid
+ * options give QLORA_ERR_VALUE.
+ */
+typedef struct {
+  float scale;
+  float dropout_p;
+  const uint8_t *keep;
+} qlora_lora;
+
+/* qlora_linear_fwd with adapter options (lora == NULL: qlora_linear_fwd). */
+qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M,
+                                   qlora_dtype act, const void *A, const void *B,
+                                   int32_t r, qlora_dtype adt, const qlora_lora *lora,
+                                   void *Y, float *XA, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* qlora_linear_bwd with adapter options (lora == NULL: qlora_linear_bwd). */
+qlora_status qlora_linear_bwd_lora(const qlora_nf4 *wq, const void *X, const void *dY,
+                                   int64_t M, qlora_dtype act, const void *A,
+                                   const void *B, int32_t r, qlora_dtype adt,
+                                   const qlora_lora *lora, const float *XA, void *dX,
+                                   float *dA, float *dB, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
  * qlora_merge: the merged dense weight W = deq(Wq) + A.B
  *   ("How it works" step 5: fold the trained adapters into the base weight;
  *   "What the simulations show": the result is a dense float matrix, off the

@@ -19,6 +19,7 @@ What it computes (plain, slow, obviously correct):
 * ``linear``  -- forward y = X.deq(Wq) + (X.A).B and the backward
   dX, dA, dB in float64, both in factored form and (for tiny shapes) through
   the dense weight gradient dW = X^T.dY exactly as the chain rule is written;
+  the same with the alpha/r factor and dropout on X.A (mask given);
   the merged dense weight deq(Wq) + A.B; adapters initialised from the
   best rank-r approximation of the quantization residual W0 - deq(Q(W0)).
 * ``optim``   -- one Adam (AdamW) step of an adapter matrix, in float64.
@@ -42,7 +43,17 @@ from .nf4 import (
     dequantize,
     storage_bits_per_weight,
 )
-from .linear import forward, backward, backward_via_dense_dw, merge, residual, loftq_init
+from .linear import (
+    forward,
+    backward,
+    backward_via_dense_dw,
+    forward_lora,
+    backward_lora,
+    lora_factor,
+    merge,
+    residual,
+    loftq_init,
+)
 from .optim import adam_step
 
 __all__ = [
@@ -67,4 +78,7 @@ __all__ = [
     "loftq_init",
     "adam_step",
     "backward_via_dense_dw",
+    "forward_lora",
+    "backward_lora",
+    "lora_factor",
 ]

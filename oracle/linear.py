@@ -16,8 +16,9 @@ The factored dA, dB equal dW B^T and A^T dW with dW = X^T dY (matrix
 products are associative); ``backward_via_dense_dw`` computes them the way
 the chain rule is written, for tiny shapes.  "LoRA & QLoRA",
 "Mathematical Formulation", gives the same layer in column form,
-h = W0 x + B (A x).  There is no alpha/r factor, bias or dropout (the guide's
-own code has none).
+h = W0 x + B (A x).  ``forward_lora`` / ``backward_lora`` add the alpha/r
+factor and the dropout on A x of that page's Scaling Factor alpha and Dropout
+sections (the mask is an input); there is no bias.
 
 Every operand is widened to float64 first; the caller passes exactly the
 values the GPU receives (bf16 inputs already rounded), so the only error left
@@ -62,6 +63,46 @@ def backward(X, dY, W_hat, A=None, B=None, XA=None):
     dA = X.T @ G
     dB = _f64(XA).T @ dY
     return {"G": G, "dX": dX, "dA": dA, "dB": dB}
+
+
+def lora_factor(scale, dropout_p):
+    """c = scale / (1 - p) computed in double and rounded to fp32 once (the
+    multiplier the library applies to kept elements)."""
+    return float(np.float32(float(scale) / (1.0 - float(dropout_p))))
+
+
+def forward_lora(X, W_hat, A, B, scale, dropout_p=0.0, keep=None):
+    """Returns (XA, U, y) with the alpha/r factor and dropout on X A.
+
+    "LoRA & QLoRA", sections Scaling Factor alpha and Dropout: the adapter
+    path is scaled by alpha/r and dropout is applied to A x, the rank-r
+    intermediate.  In row form, with the caller's keep mask K (nonzero =
+    kept) and inverted dropout (kept elements scaled by 1/(1 - p)):
+      U = c * (K o XA),  c = scale / (1 - p),   y = X W_hat + U B.
+    ``keep`` None means no dropout (every element kept).  XA is the plain
+    X A (what the layer saves for the backward).
+    """
+    X = _f64(X)
+    XA = X @ _f64(A)
+    c = lora_factor(scale, dropout_p)
+    K = np.ones_like(XA) if keep is None else (np.asarray(keep) != 0).astype(np.float64)
+    U = c * (K * XA)
+    return XA, U, X @ _f64(W_hat) + U @ _f64(B)
+
+
+def backward_lora(X, dY, W_hat, A, B, scale, dropout_p=0.0, keep=None):
+    """Gradients of ``forward_lora`` by the chain rule:
+      G = dY B^T,  G' = c * (K o G)   (dL/dXA),
+      dX = dY W_hat^T + G' A^T,  dA = X^T G',  dB = U^T dY.
+    """
+    X, dY, A, B = _f64(X), _f64(dY), _f64(A), _f64(B)
+    XA = X @ A
+    c = lora_factor(scale, dropout_p)
+    K = np.ones_like(XA) if keep is None else (np.asarray(keep) != 0).astype(np.float64)
+    U = c * (K * XA)
+    G = dY @ B.T
+    Gp = c * (K * G)
+    return {"G": Gp, "dX": dY @ _f64(W_hat).T + Gp @ A.T, "dA": X.T @ Gp, "dB": U.T @ dY}
 
 
 def backward_via_dense_dw(X, dY, W_hat, A, B):

@@ -110,7 +110,8 @@ struct BwdPlan {
   int64_t ks_g = 0, ks_x = 0, ks_b = 0, ks_a = 0, rp = 0;
   int64_t ks_bx = 0, ldm = 0;   // dB folded into the dX GEMM: partials, XA^T row length
   size_t off_dy16 = 0, off_cs = 0, off_gpart = 0, off_g16 = 0;
-  size_t off_xapart = 0, off_xa = 0, off_dbpart = 0, off_dapart = 0, off_xat = 0, total = 0;
+  size_t off_xapart = 0, off_xa = 0, off_u = 0, off_dbpart = 0, off_dapart = 0, off_xat = 0;
+  size_t total = 0;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
@@ -129,6 +130,7 @@ BwdPlan plan_bwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
     p.off_g16 = L.take(size_t(M) * p.rp * 2);
     if (p.ks_x) p.off_xapart = L.take(size_t(p.ks_x) * M * r * 4);
     p.off_xa = L.take(size_t(M) * r * 4);
+    p.off_u = L.take(size_t(M) * r * 4);
     if (db_in_dx(M, in, out, r, act_bf16)) {
       p.ks_bx = (M + 255) / 256;
       p.ldm = p.ks_bx * 256;
@@ -154,6 +156,19 @@ qlora_status check_nf4(const qlora_nf4 *wq) {
   if (!aligned16(wq->codes) || !aligned16(wq->qscale) || !aligned16(wq->gscale))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
+}
+
+// The multiplier of the rank-r intermediates from the caller's options:
+// c = alpha/r / (1 - p) (double, rounded to fp32 once) on kept elements.
+bool lora_mul(const qlora_lora *lora, RankMul &mul) {
+  mul = RankMul();
+  if (!lora) return true;
+  const double sc = lora->scale, pd = lora->dropout_p;
+  if (!std::isfinite(sc) || !std::isfinite(pd) || pd < 0.0 || pd >= 1.0) return false;
+  if (!lora->keep && pd != 0.0) return false;
+  mul.keep = lora->keep;
+  mul.c = float(sc / (1.0 - pd));
+  return std::isfinite(mul.c);
 }
 
 }  // namespace
@@ -201,6 +216,23 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
                               const void *A, const void *B, int32_t r, qlora_dtype adt,
                               void *Y, float *XA, void *ws, size_t ws_bytes,
                               hipStream_t stream) {
+  return qlora_linear_fwd_lora(wq, X, M, act, A, B, r, adt, nullptr, Y, XA, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int64_t M,
+                              qlora_dtype act, const void *A, const void *B, int32_t r,
+                              qlora_dtype adt, const float *XA, void *dX, float *dA, float *dB,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  return qlora_linear_bwd_lora(wq, X, dY, M, act, A, B, r, adt, nullptr, XA, dX, dA, dB, ws,
+                               ws_bytes, stream);
+}
+
+qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M,
+                                   qlora_dtype act, const void *A, const void *B, int32_t r,
+                                   qlora_dtype adt, const qlora_lora *lora, void *Y, float *XA,
+                                   void *ws, size_t ws_bytes, hipStream_t stream) {
+  RankMul mul;
+  if (!lora_mul(lora, mul)) return QLORA_ERR_VALUE;
   qlora_status st = check_nf4(wq);
   if (st != QLORA_OK) return st;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -229,7 +261,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
               launch_fwd_small_partial(wq->codes, wq->qscale, wq->gscale, in, out, X, xb, M, A,
                                        ab, r, p.kc, P, PXA, wq->codebook, stream));
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fwd_small_reduce(P, PXA, p.ks, M, out, r, B, ab, XA,
-                                                           Y, xb, stream));
+                                                           Y, xb, stream, mul));
     return QLORA_OK;
   }
   const uint16_t *X16 = static_cast<const uint16_t *>(X);
@@ -243,11 +275,11 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
   float *part = p.ks > 0 ? at<float>(ws, p.off_part) : nullptr;
   uint16_t *XA16 = r > 0 ? at<uint16_t>(ws, p.off_xa16) : nullptr;
   QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, part, XA, XA16, p.rp,
-                                             wq->qscale, wq->gscale, out, cs, stream));
+                                             wq->qscale, wq->gscale, out, cs, stream, mul));
   if (p.ks > 0) {
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(part, p.ks, M, r, XA, false, XA16, p.rp,
                                                   nullptr, 0, 0, nullptr, false, nullptr, 0,
-                                                  stream));
+                                                  stream, mul));
   }
   QLORA_RUN(QLORA_KERNEL_FWD_GEMM,
             launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, int32_t(p.rp), B, ab, r, Y, xb,
@@ -255,10 +287,13 @@ qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M, qlo
   return QLORA_OK;
 }
 
-qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int64_t M,
-                              qlora_dtype act, const void *A, const void *B, int32_t r,
-                              qlora_dtype adt, const float *XA, void *dX, float *dA, float *dB,
-                              void *ws, size_t ws_bytes, hipStream_t stream) {
+qlora_status qlora_linear_bwd_lora(const qlora_nf4 *wq, const void *X, const void *dY,
+                                   int64_t M, qlora_dtype act, const void *A, const void *B,
+                                   int32_t r, qlora_dtype adt, const qlora_lora *lora,
+                                   const float *XA, void *dX, float *dA, float *dB, void *ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  RankMul mul;
+  if (!lora_mul(lora, mul)) return QLORA_ERR_VALUE;
   qlora_status st = check_nf4(wq);
   if (st != QLORA_OK) return st;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -315,9 +350,17 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
   if (r > 0) G16 = at<uint16_t>(ws, p.off_g16);
   const bool fold = dX && p.ks_bx > 0;
   uint16_t *xat = fold ? at<uint16_t>(ws, p.off_xat) : nullptr;
-  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XA, M, out, r, gpart, G16, p.rp,
+  // the dY pass's dB operand: XA after its multiplier (the dX GEMM's XA^T
+  // copy applies it itself)
+  const float *XAd = XA;
+  if (r > 0 && !fold && (mul.keep || mul.c != 1.0f)) {
+    float *U = at<float>(ws, p.off_u);
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_rank_mul(XA, M, r, mul, U, stream));
+    XAd = U;
+  }
+  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XAd, M, out, r, gpart, G16, p.rp,
                                                 dbpart, xat, p.ldm, wq->qscale, wq->gscale, in,
-                                                cs, stream));
+                                                cs, stream, mul));
   if (fold) {
     // dA = X^T . G; dX and the dB partials in the GEMM; dA and dB (stored
     // [r x out]) in one reduction launch
@@ -337,7 +380,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY
       // G (bf16, zero-padded) and dB (stored [r x out]) in one launch
       QLORA_RUN(QLORA_KERNEL_REDUCE,
                 launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b,
-                               out, dB, true, nullptr, 0, stream));
+                               out, dB, true, nullptr, 0, stream, mul));
       // dA = X^T . G
       QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
       QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,

@@ -46,4 +46,11 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
+// Element (m, j) of an [M x R] rank-r intermediate after its multiplier (a
+// dropped element is 0 whatever v is).
+__device__ __forceinline__ float rank_mul(const RankMul &k, int64_t m, int64_t j, int64_t R,
+                                          float v) {
+  return (k.keep && k.keep[m * R + j] == 0) ? 0.0f : k.c * v;
+}
+
 }  // namespace qlora

@@ -8,6 +8,16 @@
 
 namespace qlora {
 
+// Multiplier of a rank-r intermediate (XA in the forward, G = dY B^T in the
+// backward) on its way into the next product: the alpha / r factor and the
+// dropout on A x ("LoRA & QLoRA", sections Scaling Factor alpha and Dropout).
+// Element (m, j) of an [M x R] intermediate becomes c * v where keep is null
+// or keep[m * R + j] != 0, and 0 elsewhere; c = 1 with no mask leaves v as is.
+struct RankMul {
+  const uint8_t *keep = nullptr;
+  float c = 1.0f;
+};
+
 // Encoder thresholds, passed by value as a kernel argument.
 // Encoder bucket table: x = w/absmax in [-1, 1] is bucketed by the top 7
 // bits of the fp32 pattern of u = x + 3 past its exponent (u in [2, 4]):
@@ -75,7 +85,8 @@ bool xa_complete(int64_t M, int64_t in, int64_t r);
 hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf16,
                            int64_t M, int64_t in, int64_t r, float *xa_part, float *XA,
                            uint16_t *XA16, int64_t ld16, const int8_t *qscale,
-                           const float *gscale, int64_t out, float *cs, hipStream_t s);
+                           const float *gscale, int64_t out, float *cs, hipStream_t s,
+                          RankMul mul = RankMul());
 
 // Backward pass over dY, one launch: G = dY . B^T (B [r x out]) -- complete
 // into G16 (bf16 [M x ldg], zero-padded) when g_complete(M, out, r), else as
@@ -89,7 +100,8 @@ hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf1
                          const float *XA, int64_t M, int64_t out, int64_t r,
                          float *g_part, uint16_t *G16, int64_t ldg, float *db_part,
                          uint16_t *xat, int64_t ldm, const int8_t *qscale,
-                         const float *gscale, int64_t in, float *cs, hipStream_t s);
+                         const float *gscale, int64_t in, float *cs, hipStream_t s,
+                          RankMul mul = RankMul());
 
 // Backward pass over X: da_part[ks][in][r] = partial X^T . G with G given as
 // G16 bf16 [M x ldg].
@@ -101,10 +113,16 @@ hipError_t launch_bwd_x(const void *X, bool x_bf16, const uint16_t *G16, int64_t
 // its part is nullptr): out[i] = sum_k part[k][i] over a [rows x R] result;
 // outputs (each optional) fp32 ([R x rows] if transpose) and bf16
 // [rows x ld] with zero padding columns R..ld-1.
+// U = mul(XA) in fp32 ([M x R]), the dB operand of the dY pass when XA
+// carries a multiplier.
+hipError_t launch_rank_mul(const float *XA, int64_t M, int64_t R, RankMul mul, float *U,
+                           hipStream_t s);
+
 hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int64_t R,
                           float *out_a, bool transpose_a, uint16_t *bf16_a, int64_t ld_a,
                           const float *part_b, int64_t ks_b, int64_t rows_b, float *out_b,
-                          bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s);
+                          bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s,
+                          RankMul mul = RankMul());
 
 // y = X16 . deq(Wq) + XA16 . B (K = in, N = out).  X16 [M x K] bf16; XA16
 // [M x ldp] bf16 with zero padding columns r..ldp-1; B [r x N] (f32 or bf16)
@@ -143,7 +161,8 @@ hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
                                     int64_t Kc, float *P, float *PXA, int codebook, hipStream_t s);
 hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS, int64_t M,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
-                                   void *Y, bool y_bf16, hipStream_t s);
+                                   void *Y, bool y_bf16, hipStream_t s,
+                          RankMul mul = RankMul());
 
 // W = deq(Wq) + A . B (W [in x out] fp32 or bf16; A [in x r], B [r x out]
 // in the adapter dtype), per element in fp32, one rounding at the end.

@@ -150,7 +150,7 @@ __device__ __forceinline__ void scales_role(const ScalesArgs &a, int64_t wg) {
 }
 
 // ------------------------------------------------------- XA^T for the dX GEMM
-// xat[j][m] = bf16(XA[m][j]) for j < 16, m < ldm (ldm a multiple of 256), zero
+// xat[j][m] = bf16(mul(XA)[m][j]) for j < 16, m < ldm (ldm a multiple of 256), zero
 // for j >= r or m >= M: the A operand of the dB products that the dX GEMM
 // takes from the dY tiles in its LDS ring.  A thread owns 8 consecutive
 // tokens of one rank index (one 16-B store).  Role of a merged launch.
@@ -160,6 +160,7 @@ struct XatArgs {
   int r;
   uint16_t *xat;      // [16 x ldm]
   int64_t ldm;
+  RankMul mul;        // applied before the rounding to bf16
 };
 
 __host__ __device__ inline int64_t xat_workgroups(int64_t ldm) { return ldm * 16 / 2048; }
@@ -172,7 +173,9 @@ __device__ __forceinline__ void xat_role(const XatArgs &a, int64_t wg) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int64_t m = m0 + e;
-    h[e] = (j < a.r && m < a.M) ? uint32_t(f32_to_bf16_bits(a.XA[m * a.r + j])) : 0u;
+    h[e] = (j < a.r && m < a.M)
+               ? uint32_t(f32_to_bf16_bits(rank_mul(a.mul, m, j, a.r, a.XA[m * a.r + j])))
+               : 0u;
   }
   *reinterpret_cast<u32x4_t *>(a.xat + e0) =
       u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
@@ -347,6 +350,7 @@ struct RowfullArgs {
   float *out;         // fp32 [M x R], optional
   uint16_t *out16;    // bf16 [M x ld16], zero padding columns R..ld16-1, optional
   int64_t ld16;
+  RankMul mul;        // applied to the bf16 copy only
 };
 
 __host__ __device__ inline int32_t clamp_records(int64_t bytes) {
@@ -516,7 +520,7 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
       v += red[((2 * kRT + r) * 16 + row) * 16 + jj];
       v += red[((3 * kRT + r) * 16 + row) * 16 + jj];
       if (a.out) a.out[m * R + j] = v;
-      if (a.out16) a.out16[m * a.ld16 + j] = f32_to_bf16_bits(v);
+      if (a.out16) a.out16[m * a.ld16 + j] = f32_to_bf16_bits(rank_mul(a.mul, m, j, R, v));
     } else {
       a.out16[m * a.ld16 + j] = 0;
     }
@@ -692,6 +696,7 @@ struct ReduceArgs {
   bool transpose_out;
   uint16_t *out_bf16;
   int64_t ld_bf16;
+  RankMul mul;        // applied to the bf16 copy only
 };
 
 // Vector form (R % 4 == 0): a thread owns 4 consecutive elements of one row
@@ -726,8 +731,11 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
       }
       if (a.out_bf16) {
         uint16_t *d = a.out_bf16 + rr * a.ld_bf16 + j;
-        const uint32_t lo = uint32_t(f32_to_bf16_bits(s[0])) | (uint32_t(f32_to_bf16_bits(s[1])) << 16);
-        const uint32_t hi = uint32_t(f32_to_bf16_bits(s[2])) | (uint32_t(f32_to_bf16_bits(s[3])) << 16);
+        f32x4_t u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = rank_mul(a.mul, rr, j + e, a.R, s[e]);
+        const uint32_t lo = uint32_t(f32_to_bf16_bits(u[0])) | (uint32_t(f32_to_bf16_bits(u[1])) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_bits(u[2])) | (uint32_t(f32_to_bf16_bits(u[3])) << 16);
         *reinterpret_cast<u32x2_t *>(d) = u32x2_t{lo, hi};
       }
     }
@@ -747,7 +755,7 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
       for (; k < a.ks; ++k) s += a.part[k * n + i];
       const int64_t rr = i / a.R, j = i - rr * a.R;
       if (a.out) a.out[a.transpose_out ? j * a.rows + rr : i] = s;
-      if (a.out_bf16) a.out_bf16[rr * a.ld_bf16 + j] = f32_to_bf16_bits(s);
+      if (a.out_bf16) a.out_bf16[rr * a.ld_bf16 + j] = f32_to_bf16_bits(rank_mul(a.mul, rr, j, a.R, s));
     }
   }
   if (a.out_bf16 && a.ld_bf16 > a.R) {   // zero padding columns R..ld_bf16-1
@@ -833,6 +841,14 @@ template <bool kXbf16, bool kWide>
 __global__ __launch_bounds__(256) void bwd_x_kernel(ColdotArgs ca) {
   extern __shared__ __align__(16) unsigned char smem[];
   coldot_role<kXbf16, true, kWide, true>(ca, blockIdx.x, smem);
+}
+
+// U = mul(XA), element by element.
+__global__ __launch_bounds__(256) void rank_mul_kernel(const float *__restrict__ XA, int64_t M,
+                                                       int64_t R, RankMul mul,
+                                                       float *__restrict__ U) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < M * R; i += int64_t(gridDim.x) * 256)
+    U[i] = rank_mul(mul, i / R, i % R, R, XA[i]);
 }
 
 // Two independent reductions in one launch: a on [0, n_a), b on the rest.
@@ -952,12 +968,14 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
 hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf16, int64_t M,
                            int64_t in, int64_t r, float *xa_part, float *XA, uint16_t *XA16,
                            int64_t ld16, const int8_t *qscale, const float *gscale, int64_t out,
-                           float *cs, hipStream_t s) {
+                           float *cs, hipStream_t s,
+                         RankMul mul) {
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
   const int64_t n_sc = cs ? scales_workgroups(in, out / 64) : 0;
   if (r > 0 && xa_complete(M, in, r)) {
     int64_t n_full = 0;
-    const RowfullArgs fa = rowfull_args(X, A, M, in, r, XA, XA16, ld16, n_full);
+    RowfullArgs fa = rowfull_args(X, A, M, in, r, XA, XA16, ld16, n_full);
+    fa.mul = mul;
     const dim3 grid = dim3(unsigned(n_full + n_sc));
     const size_t lds1 = rowfull_lds_bytes<kQFast, 1>(), lds2 = rowfull_lds_bytes<kQFast, 2>();
 #define QLORA_FULL(XB, AB)                                                                      \
@@ -1005,7 +1023,8 @@ hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf1
                          const float *XA, int64_t M, int64_t out, int64_t r, float *g_part,
                          uint16_t *G16, int64_t ldg, float *db_part, uint16_t *xat,
                          int64_t ldm, const int8_t *qscale, const float *gscale, int64_t in,
-                         float *cs, hipStream_t s) {
+                         float *cs, hipStream_t s,
+                         RankMul mul) {
   int64_t n_col = 0;
   const ColdotArgs ca = coldot_args(dY, XA, r, M, out, r, db_part, n_col);
   ScalesArgs sa{qscale, gscale, in, out / 64, cs};
@@ -1014,8 +1033,9 @@ hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf1
     return hipErrorInvalidValue;
   if (r > 0 && g_complete(M, out, r)) {
     int64_t n_full = 0;
-    const RowfullArgs fa = rowfull_args(dY, B, M, out, r, nullptr, G16, ldg, n_full);
-    const XatArgs xa{XA, M, int(r), xat, ldm};
+    RowfullArgs fa = rowfull_args(dY, B, M, out, r, nullptr, G16, ldg, n_full);
+    fa.mul = mul;
+    const XatArgs xa{XA, M, int(r), xat, ldm, mul};
     const int64_t n_xat = xat ? xat_workgroups(ldm) : 0;
     if (xat) n_col = 0;    // dB is formed by the dX GEMM
     const dim3 grid = dim3(unsigned(n_sc + n_xat + n_full + n_col));
@@ -1087,12 +1107,21 @@ hipError_t launch_bwd_x(const void *X, bool x_bf16, const uint16_t *G16, int64_t
   return hipGetLastError();
 }
 
+hipError_t launch_rank_mul(const float *XA, int64_t M, int64_t R, RankMul mul, float *U,
+                           hipStream_t s) {
+  if (M * R == 0) return hipSuccess;
+  hipLaunchKernelGGL(rank_mul_kernel, dim3(unsigned(grid_for(M * R))), dim3(256), 0, s, XA, M, R,
+                     mul, U);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int64_t R,
                           float *out_a, bool transpose_a, uint16_t *bf16_a, int64_t ld_a,
                           const float *part_b, int64_t ks_b, int64_t rows_b, float *out_b,
-                          bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s) {
-  ReduceArgs ra{part_a, ks_a, rows_a, R, out_a, transpose_a, bf16_a, ld_a};
-  ReduceArgs rb{part_b, ks_b, rows_b, R, out_b, transpose_b, bf16_b, ld_b};
+                          bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s,
+                         RankMul mul) {
+  ReduceArgs ra{part_a, ks_a, rows_a, R, out_a, transpose_a, bf16_a, ld_a, mul};
+  ReduceArgs rb{part_b, ks_b, rows_b, R, out_b, transpose_b, bf16_b, ld_b, RankMul()};
   // one thread per 4 elements (vector form), else per element
   const int64_t per = R % 4 == 0 ? 4 : 1;
   const int64_t n_a = part_a ? grid_for(rows_a * (ld_a > R ? ld_a : R) / per) : 0;

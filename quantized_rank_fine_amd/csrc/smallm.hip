@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
 template <bool kY16, bool kB16>
 __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
     const float *__restrict__ P, const float *__restrict__ PXA, int64_t KS, int64_t M, int64_t N,
-    int64_t r, int cols, const void *B, float *XA, void *Y) {
+    int64_t r, int cols, const void *B, float *XA, void *Y, RankMul mul) {
   __shared__ float xa[16][kSmallMaxR];
   const int t = threadIdx.x;
   const int64_t ER = M * r;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
 #pragma unroll
       for (int u = 0; u < 32; ++u) sx += xv[u];
     }
-    xa[e / r][e % r] = sx;
+    xa[e / r][e % r] = rank_mul(mul, e / r, e % r, r, sx);
     if (blockIdx.x == 0) XA[e] = sx;
   }
   __syncthreads();
@@ -447,17 +447,18 @@ hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
 
 hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS, int64_t M,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
-                                   void *Y, bool y_bf16, hipStream_t s) {
+                                   void *Y, bool y_bf16, hipStream_t s,
+                         RankMul mul) {
   int mp = 1;
   while (mp < M) mp *= 2;
   const int cols = kThreads / mp;
   const dim3 grid = dim3(unsigned((N + cols - 1) / cols));
   if (y_bf16) {
-    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<true, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
-    else hipLaunchKernelGGL((fwd_small_reduce_kernel<true, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
+    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<true, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
+    else hipLaunchKernelGGL((fwd_small_reduce_kernel<true, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
   } else {
-    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<false, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
-    else hipLaunchKernelGGL((fwd_small_reduce_kernel<false, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y);
+    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<false, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
+    else hipLaunchKernelGGL((fwd_small_reduce_kernel<false, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
   }
   return hipGetLastError();
 }

@@ -36,6 +36,11 @@ class qlora_nf4(ctypes.Structure):
                 ("gscale", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
 
 
+class qlora_lora(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("dropout_p", ctypes.c_float),
+                ("keep", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -55,6 +60,11 @@ def lib():
                                    vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp,
                                    vp, vp, vp, vp, sz, vp]
+    plora = ctypes.POINTER(qlora_lora)
+    L.qlora_linear_fwd_lora.argtypes = [pnf4, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int,
+                                        plora, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd_lora.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32,
+                                        ctypes.c_int, plora, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_merge.argtypes = [pnf4, vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
     f32 = ctypes.c_float
     L.qlora_adam_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
@@ -62,7 +72,8 @@ def lib():
     L.qlora_loftq_workspace_bytes.argtypes = [i64, i64, i32]
     L.qlora_loftq_workspace_bytes.restype = sz
     for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd, L.qlora_merge,
-              L.qlora_adam_step, L.qlora_loftq_init):
+              L.qlora_adam_step, L.qlora_loftq_init, L.qlora_linear_fwd_lora,
+              L.qlora_linear_bwd_lora):
         f.restype = ctypes.c_int
     for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
         f.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -201,6 +212,34 @@ def qlora_linear_bwd(wq, X, dY, M, act, A, B, r, adt, XA, dX, dA, dB, ws, ws_byt
                                   _ptr(B), int(r), int(adt), _ptr(XA), _ptr(dX), _ptr(dA),
                                   _ptr(dB), _ptr(ws), int(ws_bytes), _stream(stream)),
            "qlora_linear_bwd")
+
+
+def _lora(scale, dropout_p, keep):
+    return qlora_lora(float(scale), float(dropout_p), _ptr(keep))
+
+
+def qlora_linear_fwd_lora(wq, X, M, act, A, B, r, adt, scale, dropout_p, keep, Y, XA, ws,
+                          ws_bytes, stream=None):
+    """qlora_linear_fwd with the alpha/r factor `scale` and dropout on X.A
+    (`keep`: [M, r] uint8 device mask or None, `dropout_p` its probability)."""
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    o = _lora(scale, dropout_p, keep)
+    _check(lib().qlora_linear_fwd_lora(ctypes.byref(s), _ptr(X), int(M), int(act), _ptr(A),
+                                       _ptr(B), int(r), int(adt), ctypes.byref(o), _ptr(Y),
+                                       _ptr(XA), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "qlora_linear_fwd_lora")
+
+
+def qlora_linear_bwd_lora(wq, X, dY, M, act, A, B, r, adt, scale, dropout_p, keep, XA, dX, dA,
+                          dB, ws, ws_bytes, stream=None):
+    """qlora_linear_bwd with the same adapter options as the forward."""
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    o = _lora(scale, dropout_p, keep)
+    _check(lib().qlora_linear_bwd_lora(ctypes.byref(s), _ptr(X), _ptr(dY), int(M), int(act),
+                                       _ptr(A), _ptr(B), int(r), int(adt), ctypes.byref(o),
+                                       _ptr(XA), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                       int(ws_bytes), _stream(stream)),
+           "qlora_linear_bwd_lora")
 
 
 def qlora_levels():

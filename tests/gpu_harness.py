@@ -106,19 +106,26 @@ class Layer:
         self.wq = quantize_gpu(self.w0, codebook)
 
     # ---------------------------------------------------------------- runs
-    def fwd(self):
+    def fwd(self, lora=None):
+        """lora: None, or (scale, dropout_p, keep) with keep a device uint8
+        [M, r] tensor or None -- then the call goes through the options entry
+        point."""
         torch, dev = torch_dev()
         M, r = self.M, self.r
         Y = torch.empty(M, self.n_out, dtype=self.tdt, device=dev)
         XA = torch.empty(M, max(r, 1), dtype=torch.float32, device=dev) if r else None
         wsb = q.qlora_fwd_workspace_bytes(M, self.n_in, self.n_out, r, self.qact)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
-        q.qlora_linear_fwd(self.wq, self.tX, M, self.qact, self.tA, self.tB, r, self.qadt, Y, XA,
-                           ws, wsb)
+        if lora is None:
+            q.qlora_linear_fwd(self.wq, self.tX, M, self.qact, self.tA, self.tB, r, self.qadt,
+                               Y, XA, ws, wsb)
+        else:
+            q.qlora_linear_fwd_lora(self.wq, self.tX, M, self.qact, self.tA, self.tB, r,
+                                    self.qadt, *lora, Y, XA, ws, wsb)
         torch.cuda.synchronize()
         return Y, XA
 
-    def bwd(self, XA=None, want_dx=True):
+    def bwd(self, XA=None, want_dx=True, lora=None):
         torch, dev = torch_dev()
         M, r = self.M, self.r
         dX = torch.empty(M, self.n_in, dtype=self.tdt, device=dev) if want_dx else None
@@ -126,8 +133,12 @@ class Layer:
         dB = torch.empty(max(r, 1), self.n_out, dtype=torch.float32, device=dev) if r else None
         wsb = q.qlora_bwd_workspace_bytes(M, self.n_in, self.n_out, r, self.qact)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
-        q.qlora_linear_bwd(self.wq, self.tX, self.tdY, M, self.qact, self.tA, self.tB, r,
-                           self.qadt, XA, dX, dA, dB, ws, wsb)
+        if lora is None:
+            q.qlora_linear_bwd(self.wq, self.tX, self.tdY, M, self.qact, self.tA, self.tB, r,
+                               self.qadt, XA, dX, dA, dB, ws, wsb)
+        else:
+            q.qlora_linear_bwd_lora(self.wq, self.tX, self.tdY, M, self.qact, self.tA, self.tB,
+                                    r, self.qadt, *lora, XA, dX, dA, dB, ws, wsb)
         torch.cuda.synchronize()
         return dX, dA, dB
 

@@ -188,6 +188,33 @@ def test_bwd_validation(L):
     assert f(*args(s=_nf4(192, 100))) == 2
 
 
+def test_lora_validation(L):
+    """Adapter options are checked before anything else; valid ones fall
+    through to the usual checks (here M = 0 or a NULL workspace)."""
+    s = _nf4()
+    ws = q.qlora_fwd_workspace_bytes(64, 256, 256, 8, q.BF16)
+    def fwd(o, M=64):
+        return L.qlora_linear_fwd_lora(ctypes.byref(s), P, M, q.BF16, P, P, 8, q.BF16,
+                                       ctypes.byref(o) if o is not None else None,
+                                       P, P, None, ws, None)
+    def bwd(o):
+        return L.qlora_linear_bwd_lora(ctypes.byref(s), P, P, 64, q.BF16, P, P, 8, q.BF16,
+                                       ctypes.byref(o), P, P, P, P, None, ws, None)
+    for bad in (q.qlora_lora(1.0, 0.5, None),          # dropout without a mask
+                q.qlora_lora(1.0, 1.0, P),             # p = 1
+                q.qlora_lora(1.0, -0.1, P),
+                q.qlora_lora(1.0, float("nan"), P),
+                q.qlora_lora(float("inf"), 0.0, None),
+                q.qlora_lora(3e38, 0.9, P)):           # c = scale / (1 - p) overflows fp32
+        assert fwd(bad) == 7 and bwd(bad) == 7
+        assert fwd(bad, M=0) == 7
+    for good in (None, q.qlora_lora(2.0, 0.0, None), q.qlora_lora(0.5, 0.1, P),
+                 q.qlora_lora(-1.0, 0.0, P)):
+        assert fwd(good) == 1                          # passes to the NULL workspace check
+        assert fwd(good, M=0) == 0
+    assert bwd(q.qlora_lora(2.0, 0.25, P)) == 1
+
+
 def test_merge_validation(L):
     s = _nf4()
     f = L.qlora_merge

@@ -354,6 +354,56 @@ def test_rank_zero_is_plain_linear():
 # merge (after training) and re-quantization
 
 
+def check_lora(forward_lora, backward_lora):
+    """alpha/r and dropout on X A ("LoRA & QLoRA", Scaling Factor alpha and
+    Dropout) against what fixes them: no scaling and no mask is the plain
+    layer; a mask of zeros leaves only the base; two complementary masks at
+    p = 1/2 average to scale * X A (inverted dropout is unbiased); the
+    gradients are those of the forward (finite differences)."""
+    X, W, A, B, dY = _tiny(seed=21, M=4, n_in=64, n_out=64, r=3)
+    XA, U, y = forward_lora(X, W, A, B, 1.0)
+    _, y0 = oracle.forward(X, W, A, B)
+    assert np.array_equal(y, y0) and np.array_equal(U, XA)
+    g, g0 = backward_lora(X, dY, W, A, B, 1.0), oracle.backward(X, dY, W, A, B)
+    for k in ("dX", "dA", "dB"):
+        assert np.array_equal(g[k], g0[k]), k
+    zero = np.zeros((4, 3), np.uint8)
+    _, U, y = forward_lora(X, W, A, B, 2.0, 0.3, zero)
+    assert np.array_equal(y, X @ W) and not U.any()
+    g = backward_lora(X, dY, W, A, B, 2.0, 0.3, zero)
+    assert not g["dA"].any() and not g["dB"].any() and np.array_equal(g["dX"], dY @ W.T)
+    rng = np.random.default_rng(3)
+    K = (rng.random((4, 3)) < 0.5).astype(np.uint8)
+    _, U1, _ = forward_lora(X, W, A, B, 1.5, 0.5, K)
+    _, U2, _ = forward_lora(X, W, A, B, 1.5, 0.5, 1 - K)
+    assert np.allclose((U1 + U2) / 2, 1.5 * (X @ A), rtol=1e-14, atol=0)
+    # scale enters the adapter term linearly
+    _, _, y3 = forward_lora(X, W, A, B, 3.0)
+    assert np.allclose(y3 - X @ W, 3.0 * (y0 - X @ W), rtol=1e-13, atol=1e-16)
+    # finite differences with a mask and p > 0
+    scale, p = 2.0, 0.25
+    loss = lambda: float(np.sum(dY * forward_lora(X, W, A, B, scale, p, K)[2]))
+    g = backward_lora(X, dY, W, A, B, scale, p, K)
+    h = 1e-3                       # the loss is linear in each argument: exact FD
+    for name, T in (("dX", X), ("dA", A), ("dB", B)):
+        num = np.zeros_like(T)
+        for idx in np.ndindex(*T.shape):
+            old = T[idx]
+            T[idx] = old + h
+            lp = loss()
+            T[idx] = old - h
+            lm = loss()
+            T[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(g[name], num, rtol=1e-7, atol=1e-9), name
+
+
+def test_lora_pins():
+    check_lora(oracle.forward_lora, oracle.backward_lora)
+    assert oracle.lora_factor(2.0, 0.5) == 4.0
+    assert oracle.lora_factor(1.0, 0.1) == float(np.float32(1 / 0.9))
+
+
 def check_merge(merge):
     """merge(W_hat, A, B) = W_hat + A B: entry by entry on a tiny shape (plain
     loops), the layer's own forward with X = I returns it, X times it is the

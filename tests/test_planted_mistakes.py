@@ -160,3 +160,25 @@ def _loftq_smallest(W0, W_hat, r):
 def test_loftq_smallest_directions_are_caught():
     with pytest.raises(AssertionError):
         pins.check_loftq(_loftq_smallest)
+
+
+def _backward_lora_unmasked_G(X, dY, W, A, B, scale, dropout_p=0.0, keep=None):
+    """Mistake: the dropout mask is left out of the gradient of X A."""
+    g = oracle.backward_lora(X, dY, W, A, B, scale, dropout_p, None)
+    ref = oracle.backward_lora(X, dY, W, A, B, scale, dropout_p, keep)
+    return {**g, "dB": ref["dB"]}
+
+
+def test_unmasked_lora_gradient_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_lora(oracle.forward_lora, _backward_lora_unmasked_G)
+
+
+def _forward_lora_no_rescale(X, W, A, B, scale, dropout_p=0.0, keep=None):
+    """Mistake: kept elements are not scaled by 1 / (1 - p)."""
+    return oracle.forward_lora(X, W, A, B, scale * (1.0 - dropout_p), dropout_p, keep)
+
+
+def test_dropout_without_rescale_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_lora(_forward_lora_no_rescale, oracle.backward_lora)
