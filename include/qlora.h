@@ -73,11 +73,26 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
  *   QLORA_CB_NF4       normal quantiles at 16 evenly spaced probabilities in
  *                      [0.02, 0.98], scaled so the largest magnitude is 1;
  *   QLORA_CB_UNIFORM4  16 evenly spaced values from -1 to 1.
+ * and the symmetric integer grids of "QLoRA (low-rank adapters on a
+ * quantized model)" ("The code, line by line", "What the simulations show":
+ * symmetric uniform integers; "2-bit" is ternary), on the same 64-weight
+ * absmax blocks and double-quantized scales:
+ *   QLORA_CB_INT4      k / 7, k = -7..7      (4-bit)
+ *   QLORA_CB_INT3      k / 3, k = -3..3      (3-bit)
+ *   QLORA_CB_TERNARY   -1, 0, 1              (2-bit)
+ * stored as 4-bit codes in sign-magnitude order (code 8 + m = +m/h, code
+ * 7 - m = -m/h; zero twice, magnitudes above 1 never chosen).
  * Each level is computed in double and rounded to fp32 once
  * (qlora_codebook_levels returns the table).  A weight quantized with one
  * codebook must be used with the same codebook.
  */
-typedef enum { QLORA_CB_NF4 = 0, QLORA_CB_UNIFORM4 = 1 } qlora_codebook;
+typedef enum {
+  QLORA_CB_NF4 = 0,
+  QLORA_CB_UNIFORM4 = 1,
+  QLORA_CB_INT4 = 2,
+  QLORA_CB_INT3 = 3,
+  QLORA_CB_TERNARY = 4
+} qlora_codebook;
 
 #define QLORA_BLOCK 64      /* weights per absmax block                      */
 #define QLORA_GROUP 256     /* block scales per double-quantization group    */

@@ -10,7 +10,8 @@ What it computes (plain, slow, obviously correct):
 
 * ``levels``  -- the 16 NormalFloat-style levels (normal quantiles at 16 evenly
   spaced probabilities in [0.02, 0.98], divided by the largest magnitude), and
-  the uniform 4-bit grid used as the comparison in the same write-up.
+  the uniform 4-bit grid used as the comparison in the same write-up, and
+  the symmetric integer grids (4, 3 bits and ternary) of the QLoRA lab.
 * ``nf4``     -- blockwise absmax (64 weights per block), nearest-level
   encoding, two-codes-per-byte packing, double quantization of the block
   scales to int8 with one fp32 scale per 256 blocks, and dequantization.
@@ -29,7 +30,7 @@ against values the pages print or against closed forms; no function is
 "parity unpinned".
 """
 
-from .levels import nf4_levels, uniform4_levels, adapter_params
+from .levels import nf4_levels, uniform4_levels, int_levels, adapter_params
 from .nf4 import (
     BLOCK,
     GROUP,
@@ -59,6 +60,7 @@ from .optim import adam_step
 __all__ = [
     "nf4_levels",
     "uniform4_levels",
+    "int_levels",
     "adapter_params",
     "BLOCK",
     "GROUP",

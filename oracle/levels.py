@@ -49,6 +49,21 @@ def uniform4_levels():
                     dtype=np.float64).astype(np.float32)
 
 
+def int_levels(h):
+    """Symmetric integer grid k / h (|k| <= h) as a 16-entry level table, fp32.
+
+    "QLoRA (low-rank adapters on a quantized model)", "The code, line by
+    line" and "What the simulations show": the lab quantizes to symmetric
+    uniform integers, "2-bit" being ternary {-s, 0, s}.  h = 7, 3, 1 for 4,
+    3 and 2 bits.  Entry 8 + m is +m/h and entry 7 - m is -m/h (m = 0..7):
+    zero appears twice (-0.0, +0.0) and magnitudes m > h lie beyond 1, where
+    x = w / absmax never reaches them; each entry is m/h in double rounded
+    to fp32 once.
+    """
+    mag = np.array([m / h for m in range(8)], dtype=np.float64).astype(np.float32)
+    return np.concatenate([-mag[::-1], mag]).astype(np.float32)
+
+
 def adapter_params(n_in, n_out, rank):
     """Trainable parameters of one adapter pair A (in x r), B (r x out)."""
     return rank * (n_in + n_out)

@@ -45,6 +45,10 @@ def encode(w_flat, c, levels=None):
     """4-bit codes: argmin_i fp32(|fp32(w / c_b) - L_i|), first minimum wins.
 
     ``w_flat`` fp32 [n], ``c`` fp32 [n/64]; returns uint8 [n] in 0..15.
+    A table in sign-magnitude order (the integer grids) holds zero twice,
+    -0 then +0, one value: there the tie goes by the sign of x (x > 0 takes
+    +0), so that the codes rise with x.  The NF4 and uniform tables have no
+    zero entry.
     """
     L = nf4_levels() if levels is None else np.asarray(levels, np.float32)
     w = np.asarray(w_flat, dtype=np.float32).reshape(-1, BLOCK)
@@ -58,7 +62,11 @@ def encode(w_flat, c, levels=None):
         x = (wb / safe).astype(np.float32)           # IEEE fp32 division
         x = np.where(cb == 0, np.float32(0), x)       # zero block -> x = 0
         d = np.abs(x[..., None] - L)                  # fp32 distances
-        out[r0:r0 + rows_per_chunk] = np.argmin(d, axis=-1)
+        idx = np.argmin(d, axis=-1)
+        nxt = np.minimum(idx + 1, L.size - 1)
+        zero_pair = ((L[idx] == 0) & np.signbit(L[idx]) & (L[nxt] == 0) & ~np.signbit(L[nxt])
+                     & (nxt == idx + 1))
+        out[r0:r0 + rows_per_chunk] = np.where(zero_pair & (x > 0), nxt, idx)
     return out.reshape(-1)
 
 

@@ -55,7 +55,10 @@ struct Tables {
 // Codebooks (values of qlora_nf4.codebook): the level set of the 4-bit codes.
 constexpr int kCodebookNF4 = 0;
 constexpr int kCodebookUniform4 = 1;
-constexpr int kCodebooks = 2;
+constexpr int kCodebookInt4 = 2;      // symmetric integers -7..7 (/7)
+constexpr int kCodebookInt3 = 3;      // -3..3 (/3)
+constexpr int kCodebookTernary = 4;   // -1, 0, 1
+constexpr int kCodebooks = 5;
 
 // The tables of one codebook (built once, on first use).
 const Tables &tables(int codebook);

@@ -80,6 +80,17 @@ Tables build_tables(int codebook) {
   Tables t;
   if (codebook == kCodebookUniform4) {
     for (int i = 0; i < 16; ++i) t.L[i] = (float)(-1.0 + 2.0 * i / 15.0);
+  } else if (codebook == kCodebookInt4 || codebook == kCodebookInt3 ||
+             codebook == kCodebookTernary) {
+    // Symmetric integers k / h, |k| <= h, in sign-magnitude form: code 8 + m
+    // is +m / h and code 7 - m is -m / h (m = 0..7), so zero appears twice
+    // (-0, +0) and magnitudes m > h lie beyond +-1, where x = w / c_b never
+    // reaches them.
+    const int h = codebook == kCodebookInt4 ? 7 : (codebook == kCodebookInt3 ? 3 : 1);
+    for (int m = 0; m < 8; ++m) {
+      t.L[8 + m] = (float)((double)m / h);
+      t.L[7 - m] = -t.L[8 + m];
+    }
   } else {
     double q[16];
     double qmax = 0.0;
@@ -107,6 +118,9 @@ Tables build_tables(int codebook) {
       else
         a = m;
     }
+    // hi itself loses when it ties with lo (-0 and +0): the threshold is the
+    // next value up
+    while (!upper_wins(from_key(b), lo, hi)) ++b;
     t.T[j] = from_key(b);
   }
 
@@ -136,6 +150,7 @@ Tables build_tables(int codebook) {
     int inside = 0;
     for (int j = 1; j < 16; ++j) {
       const double tj = t.T[j];
+      if (tj > 1.0) continue;              // beyond the largest x = w / c_b
       if (tj < a) ++en.base;
       else if (tj < b) {
         en.T = t.T[j];

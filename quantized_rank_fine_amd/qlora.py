@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "qlora.h")
 
 F32, BF16 = 0, 1
-CB_NF4, CB_UNIFORM4 = 0, 1          # qlora_codebook
+CB_NF4, CB_UNIFORM4, CB_INT4, CB_INT3, CB_TERNARY = 0, 1, 2, 3, 4   # qlora_codebook
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "pointer not 16-byte aligned",
           4: "invalid dtype", 5: "workspace too small", 6: "HIP runtime error",
           7: "invalid value"}

@@ -55,7 +55,9 @@ def out_to_f64(t, dtype):
 
 def levels_of(codebook):
     """The oracle's level table of a codebook."""
-    return oracle.uniform4_levels() if codebook == q.CB_UNIFORM4 else oracle.nf4_levels()
+    return {q.CB_NF4: oracle.nf4_levels, q.CB_UNIFORM4: oracle.uniform4_levels,
+            q.CB_INT4: lambda: oracle.int_levels(7), q.CB_INT3: lambda: oracle.int_levels(3),
+            q.CB_TERNARY: lambda: oracle.int_levels(1)}[codebook]()
 
 
 def quantize_gpu(w0, codebook=q.CB_NF4):

@@ -31,7 +31,9 @@ def test_level_table_matches_oracle(L):
     assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels().view(np.uint32))
 
 
-CODEBOOKS = [(q.CB_NF4, oracle.nf4_levels), (q.CB_UNIFORM4, oracle.uniform4_levels)]
+CODEBOOKS = [(q.CB_NF4, oracle.nf4_levels), (q.CB_UNIFORM4, oracle.uniform4_levels),
+             (q.CB_INT4, lambda: oracle.int_levels(7)), (q.CB_INT3, lambda: oracle.int_levels(3)),
+             (q.CB_TERNARY, lambda: oracle.int_levels(1))]
 
 
 def test_codebook_tables(L):
@@ -44,7 +46,7 @@ def test_codebook_tables(L):
     assert q.qlora_codebook_levels(q.CB_NF4) == q.qlora_levels()
     assert q.qlora_codebook_thresholds(q.CB_NF4) == q.qlora_thresholds()
     buf = (ctypes.c_float * 16)()
-    assert L.qlora_codebook_levels(2, buf) == -1
+    assert L.qlora_codebook_levels(5, buf) == -1
     assert L.qlora_codebook_thresholds(-1, buf) == -1
 
 
@@ -56,7 +58,7 @@ def _x_sweep(T=None, levels=None):
     T = np.array(q.qlora_thresholds() if T is None else T, np.float32)
     L = oracle.nf4_levels() if levels is None else levels
     for v in np.concatenate([T, L]):
-        b = np.array([v], np.float32).view(np.int32)[0]
+        b = int(np.array([v], np.float32).view(np.int32)[0])
         nb = np.arange(b - 300, b + 301, dtype=np.int64)
         if v >= 0:
             nb = nb[(nb >= 0) & (nb <= 0x3F800000)]
@@ -141,7 +143,7 @@ def test_quantize_validation(L):
         assert L.qlora_quantize(P, ctypes.byref(s2), None) == 2
     assert L.qlora_quantize(P, ctypes.byref(_nf4(codes=None)), None) == 1
     assert L.qlora_quantize(P, ctypes.byref(_nf4(qs=U)), None) == 3
-    for cb in (2, -1):                                 # unknown codebook
+    for cb in (5, -1):                                 # unknown codebook
         assert L.qlora_quantize(P, ctypes.byref(_nf4(cb=cb)), None) == 4
 
 
@@ -227,7 +229,7 @@ def test_merge_validation(L):
     assert f(ctypes.byref(s), P, P, 8, 3, P, q.F32, None) == 4
     assert f(ctypes.byref(s), P, P, 8, q.BF16, P, 7, None) == 4
     assert f(ctypes.byref(_nf4(256, 100)), P, P, 8, q.BF16, P, q.F32, None) == 2
-    assert f(ctypes.byref(_nf4(cb=3)), P, P, 8, q.BF16, P, q.F32, None) == 4
+    assert f(ctypes.byref(_nf4(cb=7)), P, P, 8, q.BF16, P, q.F32, None) == 4
     assert f(None, P, P, 8, q.BF16, P, q.F32, None) == 1
 
 
@@ -279,7 +281,7 @@ def _bucket_lut(T):
     x in [-1 + i/32, -1 + (i+1)/32) (bucket 64: x = 1); base = number of
     thresholds below the bucket, T = the one threshold inside (+inf if none)."""
     T = np.asarray(T, np.float64)
-    T = T[np.isfinite(T)]
+    T = T[np.isfinite(T) & (T <= 1.0)]     # x = w / absmax never exceeds 1
     lut = []
     for i in range(128):
         a = -1.0 + i / 32.0

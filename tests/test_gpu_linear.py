@@ -115,6 +115,20 @@ def test_uniform4_codebook(M, n_in, n_out, r, act, adt):
     _check(L, tag="uniform4")
 
 
+@pytest.mark.parametrize("codebook", [q.CB_INT4, q.CB_INT3, q.CB_TERNARY])
+@pytest.mark.parametrize("M,n_in,n_out,r,act,adt", [
+    (300, 640, 704, 16, "bf16", "bf16"),    # fused GEMMs, split-K rank-r passes
+    (1030, 320, 448, 16, "bf16", "bf16"),   # whole-K rank-r passes, dB in the dX GEMM
+    (5, 576, 448, 16, "f32", "bf16"),       # few-token forward
+])
+def test_integer_grid_codebooks(codebook, M, n_in, n_out, r, act, adt):
+    """The symmetric integer grids through every path: same kernels, their
+    own level tables (zero twice, magnitudes past 1 never used)."""
+    L = Layer(18, M, n_in, n_out, r, act=act, adt=adt, codebook=codebook)
+    _codes_match_oracle(L)
+    _check(L, tag=f"int grid {codebook}")
+
+
 def test_few_tokens_b_zero_equals_rank_zero_and_deterministic():
     L = Layer(15, 5, 576, 448, 16, b_zero=True)
     Y, XA = L.fwd()

@@ -49,6 +49,22 @@ def test_quantize_uniform4(shape):
     _check_full(synth.weights(*shape, workload=1), f"uniform4 {shape}", q.CB_UNIFORM4)
 
 
+@pytest.mark.parametrize("codebook", [q.CB_INT4, q.CB_INT3, q.CB_TERNARY])
+@pytest.mark.parametrize("shape", [(1024, 1024), (320, 640)])
+def test_quantize_integer_grids(codebook, shape):
+    """The symmetric integer grids (4, 3 bits, ternary) on the same kernel:
+    codes bit-exact against the oracle (nearest level, +0 for x > 0), also on
+    weights that sit exactly on the grid and between its points."""
+    _check_full(synth.weights(*shape, workload=1), f"int grid {codebook} {shape}", codebook)
+    h = {q.CB_INT4: 7, q.CB_INT3: 3, q.CB_TERNARY: 1}[codebook]
+    g = np.random.default_rng(codebook)
+    k = g.integers(-h, h + 1, size=(128, 256)).astype(np.float32)
+    k[:, ::64] = h                                     # absmax 1 per block: x = k / h
+    w = (k / np.float32(h)).astype(np.float32)
+    w[1::2] += np.float32(0.25 / h) * g.choice([-1, 1], size=w[1::2].shape).astype(np.float32)
+    _check_full(w, f"int grid {codebook} on/between grid points", codebook)
+
+
 @pytest.mark.parametrize("shape", [(64, 192), (320, 640), (64, 64), (128, 704)])
 def test_quantize_ragged_groups(shape):
     # n/64 not a multiple of 256: the last double-quantization group is short

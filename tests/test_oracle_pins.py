@@ -87,6 +87,36 @@ def test_nf4_levels_close_to_listing_pipeline():
     assert np.all(diff <= 4 * 2.0 ** -24) and np.any(diff > 0)
 
 
+def test_integer_grids():
+    """The symmetric integer grids (4, 3 bits and ternary): entries are m/h in
+    sign-magnitude order, and quantizing with them is rounding h x to the
+    nearest integer (the lab's symmetric uniform integers), checked against
+    that definition on a sweep, with x > 0 going to +0 and the ternary dead
+    zone |x| <= 1/2."""
+    for h in (7, 3, 1):
+        L = oracle.int_levels(h)
+        assert L.dtype == np.float32 and L.size == 16
+        for m in range(8):
+            assert L[8 + m] == np.float32(m / h) and L[7 - m] == -np.float32(m / h)
+        assert np.signbit(L[7]) and not np.signbit(L[8])
+        assert np.all(np.diff(L) >= 0)
+        # every block holds a 1 so that c_b = 1 and x = w exactly
+        g = np.random.default_rng(h)
+        x = np.concatenate([g.uniform(-1, 1, 63 * 400), np.linspace(-1, 1, 63 * 9)]).astype(np.float32)
+        x = x[np.abs(np.abs(x * h) - np.floor(np.abs(x * h)) - 0.5) > 1e-5]   # no ties
+        x = x[: (x.size // 63) * 63]
+        w = np.concatenate([np.ones((x.size // 63, 1), np.float32), x.reshape(-1, 63)], 1).reshape(-1)
+        codes = oracle.encode(w, onf4.block_absmax(w), L).reshape(-1, 64)[:, 1:].reshape(-1)
+        k = np.rint(h * x.astype(np.float64)).astype(np.int64)
+        want = np.where((k > 0) | ((k == 0) & (x > 0)), 8 + k, 7 + k)
+        assert np.array_equal(codes.astype(np.int64), want), h
+        assert np.array_equal(L[codes], (k / h).astype(np.float32))
+    T = oracle.int_levels(1)
+    t = oracle.encode(np.array([1.0, 0.49, 0.51, -0.49, -0.51, 0.0, -1.0, 0.3] * 8, np.float32),
+                      np.ones(1, np.float32), T)
+    assert list(T[t[:8]]) == [1.0, 0.0, 1.0, -0.0, -1.0, -0.0, -1.0, 0.0]
+
+
 def test_uniform_grid():
     U = oracle.uniform4_levels()
     assert U[0] == -1 and U[15] == 1
