@@ -404,10 +404,34 @@ def main():
     torch.cuda.synchronize()
     adam_us = ea0.elapsed_time(ea1) * 1e3 / K
     del graph
+    # The same Adam step fused into the backward's last launch, against the
+    # backward followed by the two Adam launches (K steps each, eager).
+    stA = [opt["A"][0], opt["A"][2], opt["A"][3], a16]
+    stB = [opt["B"][0], opt["B"][2], opt["B"][3], b16]
+    def bwd_then_adam(i):
+        q.qlora_linear_bwd(wq, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
+        q.qlora_adam_step(stA[0], dA.view(-1), stA[1], stA[2], i + 1, 1e-3, theta_bf16=a16)
+        q.qlora_adam_step(stB[0], dB.view(-1), stB[1], stB[2], i + 1, 1e-3, theta_bf16=b16)
+    def bwd_adam(i):
+        q.qlora_linear_bwd_adam(wq, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, stA, stB, i + 1,
+                                1e-3, wsb, bwb)
+    adam_fused = {}
+    for name, fn in (("bwd_then_adam_us", bwd_then_adam), ("bwd_adam_fused_us", bwd_adam)):
+        for i in range(3):
+            fn(i)
+        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        eb0.record()
+        for i in range(K):
+            fn(i)
+        eb1.record()
+        torch.cuda.synchronize()
+        adam_fused[name] = round(eb0.elapsed_time(eb1) * 1e3 / K, 2)
     adam_bytes = (na + nb) * (16 + 12 + 2)
     adam = {"us_per_step": round(adam_us, 2), "params": na + nb, "algorithmic_bytes": adam_bytes,
             "GBps": round(adam_bytes / (adam_us * 1e-6) / 1e9, 1),
-            "what": "Adam step of A and B (fp32, two launches, bf16 copies written; HIP graph)"}
+            "what": "Adam step of A and B (fp32, two launches, bf16 copies written; HIP graph)",
+            "fused_into_backward": adam_fused}
     del opt
 
     # LoftQ-style start of A and B (rank 16, 24 probe columns, 2 power

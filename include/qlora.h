@@ -230,6 +230,47 @@ qlora_status qlora_linear_bwd_lora(const qlora_nf4 *wq, const void *X, const voi
                                    hipStream_t stream);
 
 /*
+ * The backward with one Adam (AdamW) step of A and B fused into its final
+ * reduction launch (the adapter update of "The code, line by line": the
+ * optimizer holds only A and B), the same arithmetic as qlora_adam_step:
+ * given the same gradients, the same bits.
+ *   state_A / state_B: the fp32 master copy theta ([in, r] / [r, out]), the
+ *     moments m, v (same layout, zero before step 1) and an optional bf16
+ *     copy of the updated theta.  theta may be the A (B) the call reads when
+ *     adt = QLORA_F32, and theta_bf16 the one it reads when adt = QLORA_BF16:
+ *     every read of A and B comes before the update.
+ *   hparams: step >= 1, 0 <= beta < 1, eps >= 0, weight_decay >= 0, finite
+ *     lr (else QLORA_ERR_VALUE).
+ *   dA, dB: NULL, or also receive the gradients.
+ * Otherwise as qlora_linear_bwd_lora (lora may be NULL); M must be >= 1.
+ */
+typedef struct {
+  float *theta;
+  float *m;
+  float *v;
+  uint16_t *theta_bf16;
+} qlora_adam_state;
+
+typedef struct {
+  int64_t step;
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} qlora_adam_hparams;
+
+qlora_status qlora_linear_bwd_adam(const qlora_nf4 *wq, const void *X, const void *dY,
+                                   int64_t M, qlora_dtype act, const void *A,
+                                   const void *B, int32_t r, qlora_dtype adt,
+                                   const qlora_lora *lora, const float *XA, void *dX,
+                                   const qlora_adam_state *state_A,
+                                   const qlora_adam_state *state_B,
+                                   const qlora_adam_hparams *hparams, float *dA,
+                                   float *dB, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
  * qlora_merge: the merged dense weight W = deq(Wq) + A.B
  *   ("How it works" step 5: fold the trained adapters into the base weight;
  *   "What the simulations show": the result is a dense float matrix, off the

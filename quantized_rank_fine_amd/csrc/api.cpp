@@ -171,6 +171,153 @@ bool lora_mul(const qlora_lora *lora, RankMul &mul) {
   return std::isfinite(mul.c);
 }
 
+// The backward, with optional Adam steps of A and B fused into the final
+// reductions (ta/tb.theta != nullptr; dA/dB may then be null).  Every read of
+// A and B comes before those reductions, so the updated adapters may alias
+// the ones the call reads.
+qlora_status linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int64_t M,
+                        qlora_dtype act, const void *A, const void *B, int32_t r,
+                        qlora_dtype adt, const RankMul &mul, const float *XA, void *dX,
+                        float *dA, float *dB, const AdamTarget &ta, const AdamTarget &tb,
+                        void *ws, size_t ws_bytes, hipStream_t stream) {
+  const bool adam = ta.theta != nullptr;
+  qlora_status st = check_nf4(wq);
+  if (st != QLORA_OK) return st;
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
+  const int64_t in = wq->in, out = wq->out;
+  if (r > 0) {
+    if (!A || !B || (!adam && (!dA || !dB))) return QLORA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || (dA && !aligned16(dA)) || (dB && !aligned16(dB)))
+      return QLORA_ERR_ALIGN;
+    if (XA && !aligned16(XA)) return QLORA_ERR_ALIGN;
+  }
+  const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
+  hipError_t e = hipSuccess;
+#define QLORA_RUN(KIND, CALL)                              \
+  do {                                                     \
+    e = timed(KIND, stream, [&] { return CALL; });         \
+    if (e != hipSuccess) return QLORA_ERR_DEVICE;          \
+  } while (0)
+  if (M == 0) {
+    if (adam) return QLORA_ERR_SHAPE;
+    if (r > 0) {
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fill_zero(dA, in * r, stream));
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fill_zero(dB, int64_t(r) * out, stream));
+    }
+    return QLORA_OK;
+  }
+  if (!dY || !ws) return QLORA_ERR_NULL;
+  if (r > 0 && !X) return QLORA_ERR_NULL;
+  if (!aligned16(dY) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (X && !aligned16(X)) return QLORA_ERR_ALIGN;
+  if (dX && !aligned16(dX)) return QLORA_ERR_ALIGN;
+  const BwdPlan p = plan_bwd(M, in, out, r, xb);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+
+  const uint16_t *dY16 = static_cast<const uint16_t *>(dY);
+  if (!xb && dX) {
+    uint16_t *d16 = at<uint16_t>(ws, p.off_dy16);
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(dY, false, M * out, d16, stream));
+    dY16 = d16;
+  }
+  float *cs = dX ? at<float>(ws, p.off_cs) : nullptr;
+  uint16_t *G16 = nullptr;
+  if (r > 0 && !XA) {
+    // recompute XA = X . A into the workspace
+    float *xpart = p.ks_x > 0 ? at<float>(ws, p.off_xapart) : nullptr;
+    float *xaw = at<float>(ws, p.off_xa);
+    QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, xpart, xaw, nullptr, 0,
+                                               nullptr, nullptr, out, nullptr, stream));
+    if (p.ks_x > 0) {
+      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
+                                                    nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                    stream));
+    }
+    XA = xaw;
+  }
+  // one pass over dY: G = dY . B^T (complete, or partials), dB = XA^T . dY
+  // partials (or, when the dX GEMM forms them, XA^T in bf16), block scales
+  float *gpart = p.ks_g > 0 ? at<float>(ws, p.off_gpart) : nullptr;
+  float *dbpart = r > 0 ? at<float>(ws, p.off_dbpart) : nullptr;
+  if (r > 0) G16 = at<uint16_t>(ws, p.off_g16);
+  const bool fold = dX && p.ks_bx > 0;
+  uint16_t *xat = fold ? at<uint16_t>(ws, p.off_xat) : nullptr;
+  // the dY pass's dB operand: XA after its multiplier (the dX GEMM's XA^T
+  // copy applies it itself)
+  const float *XAd = XA;
+  if (r > 0 && !fold && (mul.keep || mul.c != 1.0f)) {
+    float *U = at<float>(ws, p.off_u);
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_rank_mul(XA, M, r, mul, U, stream));
+    XAd = U;
+  }
+  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XAd, M, out, r, gpart, G16, p.rp,
+                                                dbpart, xat, p.ldm, wq->qscale, wq->gscale, in,
+                                                cs, stream, mul));
+  auto dx_gemm = [&](const uint16_t *xt, float *dbp) {
+    return launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX, xb,
+                          wq->codebook, xt, p.ldm, dbp, stream);
+  };
+  if (r == 0) {
+    if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
+    return QLORA_OK;
+  }
+  float *dapart = at<float>(ws, p.off_dapart);
+  if (fold) {
+    // dA = X^T . G; dX and the dB partials in the GEMM; dA and dB (stored
+    // [r x out]) in one reduction launch
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+    QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(xat, dbpart));
+    QLORA_RUN(QLORA_KERNEL_REDUCE,
+              launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_bx, out,
+                             dB, true, nullptr, 0, stream, RankMul(), ta, tb));
+    return QLORA_OK;
+  }
+  if (p.ks_g > 0) {
+    // G (bf16, zero-padded) and dB (stored [r x out]) in one launch; B is
+    // not read after the dY pass
+    QLORA_RUN(QLORA_KERNEL_REDUCE,
+              launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b, out,
+                             dB, true, nullptr, 0, stream, mul, AdamTarget(), tb));
+    // dA = X^T . G; dX (the last reader of A); dA
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+    if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
+    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
+                                                  nullptr, 0, 0, nullptr, false, nullptr, 0,
+                                                  stream, RankMul(), ta));
+  } else {
+    // G is complete: dA = X^T . G, dX, then dA and dB (stored [r x out]) in
+    // one launch
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+    if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
+    QLORA_RUN(QLORA_KERNEL_REDUCE,
+              launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_b, out,
+                             dB, true, nullptr, 0, stream, RankMul(), ta, tb));
+  }
+  return QLORA_OK;
+#undef QLORA_RUN
+}
+
+bool adam_hparams_ok(const qlora_adam_hparams *h) {
+  return h && h->step >= 1 && std::isfinite(h->lr) && std::isfinite(h->eps) &&
+         std::isfinite(h->weight_decay) && h->beta1 >= 0.0f && h->beta1 < 1.0f &&
+         h->beta2 >= 0.0f && h->beta2 < 1.0f && h->eps >= 0.0f && h->weight_decay >= 0.0f;
+}
+
+qlora_status adam_target(const qlora_adam_state *s, const qlora_adam_hparams *h,
+                         AdamTarget &t) {
+  if (!s || !s->theta || !s->m || !s->v) return QLORA_ERR_NULL;
+  if (!aligned16(s->theta) || !aligned16(s->m) || !aligned16(s->v) ||
+      (s->theta_bf16 && !aligned16(s->theta_bf16)))
+    return QLORA_ERR_ALIGN;
+  t.theta = s->theta;
+  t.m = s->m;
+  t.v = s->v;
+  t.theta16 = s->theta_bf16;
+  t.p = make_adam_params(h->step, h->lr, h->beta1, h->beta2, h->eps, h->weight_decay);
+  return QLORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -285,6 +432,7 @@ qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M
             launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, int32_t(p.rp), B, ab, r, Y, xb,
                             wq->codebook, stream));
   return QLORA_OK;
+#undef QLORA_RUN
 }
 
 qlora_status qlora_linear_bwd_lora(const qlora_nf4 *wq, const void *X, const void *dY,
@@ -294,113 +442,28 @@ qlora_status qlora_linear_bwd_lora(const qlora_nf4 *wq, const void *X, const voi
                                    size_t ws_bytes, hipStream_t stream) {
   RankMul mul;
   if (!lora_mul(lora, mul)) return QLORA_ERR_VALUE;
-  qlora_status st = check_nf4(wq);
-  if (st != QLORA_OK) return st;
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
-  if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
-  const int64_t in = wq->in, out = wq->out;
-  if (r > 0) {
-    if (!A || !B || !dA || !dB) return QLORA_ERR_NULL;
-    if (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB))
-      return QLORA_ERR_ALIGN;
-    if (XA && !aligned16(XA)) return QLORA_ERR_ALIGN;
-  }
-  const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
-  hipError_t e = hipSuccess;
-  if (M == 0) {
-    if (r > 0) {
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fill_zero(dA, in * r, stream));
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fill_zero(dB, int64_t(r) * out, stream));
-    }
-    return QLORA_OK;
-  }
-  if (!dY || !ws) return QLORA_ERR_NULL;
-  if (r > 0 && !X) return QLORA_ERR_NULL;
-  if (!aligned16(dY) || !aligned16(ws)) return QLORA_ERR_ALIGN;
-  if (X && !aligned16(X)) return QLORA_ERR_ALIGN;
-  if (dX && !aligned16(dX)) return QLORA_ERR_ALIGN;
-  const BwdPlan p = plan_bwd(M, in, out, r, xb);
-  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  return linear_bwd(wq, X, dY, M, act, A, B, r, adt, mul, XA, dX, dA, dB, AdamTarget(),
+                    AdamTarget(), ws, ws_bytes, stream);
+}
 
-  const uint16_t *dY16 = static_cast<const uint16_t *>(dY);
-  if (!xb && dX) {
-    uint16_t *d16 = at<uint16_t>(ws, p.off_dy16);
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_convert_to_bf16(dY, false, M * out, d16, stream));
-    dY16 = d16;
-  }
-  float *cs = dX ? at<float>(ws, p.off_cs) : nullptr;
-  uint16_t *G16 = nullptr;
-  if (r > 0 && !XA) {
-    // recompute XA = X . A into the workspace
-    float *xpart = p.ks_x > 0 ? at<float>(ws, p.off_xapart) : nullptr;
-    float *xaw = at<float>(ws, p.off_xa);
-    QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, xpart, xaw, nullptr, 0,
-                                               nullptr, nullptr, out, nullptr, stream));
-    if (p.ks_x > 0) {
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(xpart, p.ks_x, M, r, xaw, false, nullptr, 0,
-                                                    nullptr, 0, 0, nullptr, false, nullptr, 0,
-                                                    stream));
-    }
-    XA = xaw;
-  }
-  // one pass over dY: G = dY . B^T (complete, or partials), dB = XA^T . dY
-  // partials (or, when the dX GEMM forms them, XA^T in bf16), block scales
-  float *gpart = p.ks_g > 0 ? at<float>(ws, p.off_gpart) : nullptr;
-  float *dbpart = r > 0 ? at<float>(ws, p.off_dbpart) : nullptr;
-  if (r > 0) G16 = at<uint16_t>(ws, p.off_g16);
-  const bool fold = dX && p.ks_bx > 0;
-  uint16_t *xat = fold ? at<uint16_t>(ws, p.off_xat) : nullptr;
-  // the dY pass's dB operand: XA after its multiplier (the dX GEMM's XA^T
-  // copy applies it itself)
-  const float *XAd = XA;
-  if (r > 0 && !fold && (mul.keep || mul.c != 1.0f)) {
-    float *U = at<float>(ws, p.off_u);
-    QLORA_RUN(QLORA_KERNEL_REDUCE, launch_rank_mul(XA, M, r, mul, U, stream));
-    XAd = U;
-  }
-  QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XAd, M, out, r, gpart, G16, p.rp,
-                                                dbpart, xat, p.ldm, wq->qscale, wq->gscale, in,
-                                                cs, stream, mul));
-  if (fold) {
-    // dA = X^T . G; dX and the dB partials in the GEMM; dA and dB (stored
-    // [r x out]) in one reduction launch
-    float *dapart = at<float>(ws, p.off_dapart);
-    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
-    QLORA_RUN(QLORA_KERNEL_DX_GEMM,
-              launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
-                             xb, wq->codebook, xat, p.ldm, dbpart, stream));
-    QLORA_RUN(QLORA_KERNEL_REDUCE,
-              launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_bx, out,
-                             dB, true, nullptr, 0, stream));
-    return QLORA_OK;
-  }
+qlora_status qlora_linear_bwd_adam(const qlora_nf4 *wq, const void *X, const void *dY,
+                                   int64_t M, qlora_dtype act, const void *A, const void *B,
+                                   int32_t r, qlora_dtype adt, const qlora_lora *lora,
+                                   const float *XA, void *dX, const qlora_adam_state *state_A,
+                                   const qlora_adam_state *state_B,
+                                   const qlora_adam_hparams *hparams, float *dA, float *dB,
+                                   void *ws, size_t ws_bytes, hipStream_t stream) {
+  RankMul mul;
+  if (!lora_mul(lora, mul) || !adam_hparams_ok(hparams)) return QLORA_ERR_VALUE;
+  if (M < 1) return QLORA_ERR_SHAPE;
+  AdamTarget ta, tb;
   if (r > 0) {
-    float *dapart = at<float>(ws, p.off_dapart);
-    if (p.ks_g > 0) {
-      // G (bf16, zero-padded) and dB (stored [r x out]) in one launch
-      QLORA_RUN(QLORA_KERNEL_REDUCE,
-                launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b,
-                               out, dB, true, nullptr, 0, stream, mul));
-      // dA = X^T . G
-      QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
-      QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
-                                                    nullptr, 0, 0, nullptr, false, nullptr, 0,
-                                                    stream));
-    } else {
-      // G is complete: dA = X^T . G, then dA and dB (stored [r x out]) in one launch
-      QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
-      QLORA_RUN(QLORA_KERNEL_REDUCE,
-                launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_b, out,
-                               dB, true, nullptr, 0, stream));
-    }
+    qlora_status st = adam_target(state_A, hparams, ta);
+    if (st == QLORA_OK) st = adam_target(state_B, hparams, tb);
+    if (st != QLORA_OK) return st;
   }
-  if (dX) {
-    QLORA_RUN(QLORA_KERNEL_DX_GEMM,
-              launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX,
-                             xb, wq->codebook, nullptr, 0, nullptr, stream));
-  }
-  return QLORA_OK;
-#undef QLORA_RUN
+  return linear_bwd(wq, X, dY, M, act, A, B, r, adt, mul, XA, dX, dA, dB, ta, tb, ws, ws_bytes,
+                    stream);
 }
 
 qlora_status qlora_merge(const qlora_nf4 *wq, const void *A, const void *B, int32_t r,

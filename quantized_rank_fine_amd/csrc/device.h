@@ -46,6 +46,20 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
+// One Adam (AdamW) step of one element, fp32 (Kingma & Ba, Algorithm 1, with
+// decoupled weight decay):
+//   m <- b1 m + (1 - b1) g,   v <- b2 v + (1 - b2) g g,
+//   theta <- theta - lr ( (m c1) / (sqrt(v c2) + eps) + wd theta ).
+// Shared by the Adam kernel and the backward's fused update, so the two give
+// the same bits.
+__device__ __forceinline__ void adam1(const AdamParams &a, float &th, float g, float &m,
+                                      float &v) {
+  m = a.b1 * m + a.omb1 * g;
+  v = a.b2 * v + a.omb2 * (g * g);
+  const float den = sqrtf(v * a.c2) + a.eps;
+  th = th - a.lr * ((m * a.c1) / den + a.wd * th);
+}
+
 // Element (m, j) of an [M x R] rank-r intermediate after its multiplier (a
 // dropped element is 0 whatever v is).
 __device__ __forceinline__ float rank_mul(const RankMul &k, int64_t m, int64_t j, int64_t R,

@@ -18,6 +18,24 @@ struct RankMul {
   float c = 1.0f;
 };
 
+// One Adam (AdamW) step's constants, fp32 (the bias corrections and 1 - beta
+// formed in double on the host, rounded once).
+struct AdamParams {
+  float lr, b1, omb1, b2, omb2, eps, wd, c1, c2;
+};
+AdamParams make_adam_params(int64_t step, float lr, float beta1, float beta2, float eps,
+                            float weight_decay);
+
+// An adapter matrix updated in place by one Adam step from a gradient that
+// a reduction has just formed (theta == nullptr: none).  Same layout as the
+// gradient the reduction writes.
+struct AdamTarget {
+  float *theta = nullptr;
+  float *m = nullptr, *v = nullptr;
+  uint16_t *theta16 = nullptr;    // optional bf16 copy of the updated theta
+  AdamParams p{};
+};
+
 // Encoder thresholds, passed by value as a kernel argument.
 // Encoder bucket table: x = w/absmax in [-1, 1] is bucketed by the top 7
 // bits of the fp32 pattern of u = x + 3 past its exponent (u in [2, 4]):
@@ -125,7 +143,9 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
                           float *out_a, bool transpose_a, uint16_t *bf16_a, int64_t ld_a,
                           const float *part_b, int64_t ks_b, int64_t rows_b, float *out_b,
                           bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s,
-                          RankMul mul = RankMul());
+                          RankMul mul = RankMul(),
+                          const AdamTarget &adam_a = AdamTarget(),
+                          const AdamTarget &adam_b = AdamTarget());
 
 // y = X16 . deq(Wq) + XA16 . B (K = in, N = out).  X16 [M x K] bf16; XA16
 // [M x ldp] bf16 with zero padding columns r..ldp-1; B [r x N] (f32 or bf16)

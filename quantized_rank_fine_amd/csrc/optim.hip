@@ -22,16 +22,9 @@ struct AdamArgs {
   const float *g;
   float *m, *v;
   int64_t n;
-  float lr, b1, omb1, b2, omb2, eps, wd, c1, c2;
+  AdamParams p;
   uint16_t *theta16;
 };
-
-__device__ __forceinline__ void adam1(const AdamArgs &a, float &th, float g, float &m, float &v) {
-  m = a.b1 * m + a.omb1 * g;
-  v = a.b2 * v + a.omb2 * (g * g);
-  const float den = sqrtf(v * a.c2) + a.eps;
-  th = th - a.lr * ((m * a.c1) / den + a.wd * th);
-}
 
 __global__ __launch_bounds__(256) void adam_kernel(AdamArgs a) {
   const int64_t n4 = a.n / 4;
@@ -44,7 +37,7 @@ __global__ __launch_bounds__(256) void adam_kernel(AdamArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float t = th[e], mm = m[e], vv = v[e];
-      adam1(a, t, g[e], mm, vv);
+      adam1(a.p, t, g[e], mm, vv);
       th[e] = t; m[e] = mm; v[e] = vv;
     }
     reinterpret_cast<f32x4_t *>(a.theta)[i] = th;
@@ -58,7 +51,7 @@ __global__ __launch_bounds__(256) void adam_kernel(AdamArgs a) {
   const int64_t i = 4 * n4 + int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (blockIdx.x == 0 && i < a.n) {
     float t = a.theta[i], mm = a.m[i], vv = a.v[i];
-    adam1(a, t, a.g[i], mm, vv);
+    adam1(a.p, t, a.g[i], mm, vv);
     a.theta[i] = t; a.m[i] = mm; a.v[i] = vv;
     if (a.theta16) a.theta16[i] = __builtin_bit_cast(uint16_t, (__bf16)t);
   }
@@ -66,17 +59,24 @@ __global__ __launch_bounds__(256) void adam_kernel(AdamArgs a) {
 
 }  // namespace
 
+AdamParams make_adam_params(int64_t step, float lr, float beta1, float beta2, float eps,
+                            float weight_decay) {
+  AdamParams a;
+  a.lr = lr; a.b1 = beta1; a.b2 = beta2; a.eps = eps; a.wd = weight_decay;
+  a.omb1 = float(1.0 - double(beta1));
+  a.omb2 = float(1.0 - double(beta2));
+  a.c1 = float(1.0 / (1.0 - std::pow(double(beta1), double(step))));
+  a.c2 = float(1.0 / (1.0 - std::pow(double(beta2), double(step))));
+  return a;
+}
+
 hipError_t launch_adam(float *theta, const float *g, float *m, float *v, int64_t n, int64_t step,
                        float lr, float beta1, float beta2, float eps, float weight_decay,
                        uint16_t *theta16, hipStream_t s) {
   if (n == 0) return hipSuccess;
   AdamArgs a;
   a.theta = theta; a.g = g; a.m = m; a.v = v; a.n = n; a.theta16 = theta16;
-  a.lr = lr; a.b1 = beta1; a.b2 = beta2; a.eps = eps; a.wd = weight_decay;
-  a.omb1 = float(1.0 - double(beta1));
-  a.omb2 = float(1.0 - double(beta2));
-  a.c1 = float(1.0 / (1.0 - std::pow(double(beta1), double(step))));
-  a.c2 = float(1.0 / (1.0 - std::pow(double(beta2), double(step))));
+  a.p = make_adam_params(step, lr, beta1, beta2, eps, weight_decay);
   int64_t blocks = (n / 4 + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 2048) blocks = 2048;

@@ -697,7 +697,18 @@ struct ReduceArgs {
   uint16_t *out_bf16;
   int64_t ld_bf16;
   RankMul mul;        // applied to the bf16 copy only
+  AdamTarget adam;    // one Adam step from the sums, in the layout of out
 };
+
+// The Adam step of element i of the result (index in out's layout).
+__device__ __forceinline__ void reduce_adam(const AdamTarget &t, int64_t i, float g) {
+  float th = t.theta[i], m = t.m[i], v = t.v[i];
+  adam1(t.p, th, g, m, v);
+  t.theta[i] = th;
+  t.m[i] = m;
+  t.v[i] = v;
+  if (t.theta16) t.theta16[i] = f32_to_bf16_bits(th);
+}
 
 // Vector form (R % 4 == 0): a thread owns 4 consecutive elements of one row
 // and keeps up to kRedBatch 16-B partial loads in flight, so that a pass over
@@ -729,6 +740,11 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
           *reinterpret_cast<f32x4_t *>(a.out + i) = s;
         }
       }
+      if (a.adam.theta) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          reduce_adam(a.adam, a.transpose_out ? (j + e) * a.rows + rr : i + e, s[e]);
+      }
       if (a.out_bf16) {
         uint16_t *d = a.out_bf16 + rr * a.ld_bf16 + j;
         f32x4_t u;
@@ -755,6 +771,7 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
       for (; k < a.ks; ++k) s += a.part[k * n + i];
       const int64_t rr = i / a.R, j = i - rr * a.R;
       if (a.out) a.out[a.transpose_out ? j * a.rows + rr : i] = s;
+      if (a.adam.theta) reduce_adam(a.adam, a.transpose_out ? j * a.rows + rr : i, s);
       if (a.out_bf16) a.out_bf16[rr * a.ld_bf16 + j] = f32_to_bf16_bits(rank_mul(a.mul, rr, j, a.R, s));
     }
   }
@@ -1119,9 +1136,10 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
                           float *out_a, bool transpose_a, uint16_t *bf16_a, int64_t ld_a,
                           const float *part_b, int64_t ks_b, int64_t rows_b, float *out_b,
                           bool transpose_b, uint16_t *bf16_b, int64_t ld_b, hipStream_t s,
-                         RankMul mul) {
-  ReduceArgs ra{part_a, ks_a, rows_a, R, out_a, transpose_a, bf16_a, ld_a, mul};
-  ReduceArgs rb{part_b, ks_b, rows_b, R, out_b, transpose_b, bf16_b, ld_b, RankMul()};
+                         RankMul mul,
+                          const AdamTarget &adam_a, const AdamTarget &adam_b) {
+  ReduceArgs ra{part_a, ks_a, rows_a, R, out_a, transpose_a, bf16_a, ld_a, mul, adam_a};
+  ReduceArgs rb{part_b, ks_b, rows_b, R, out_b, transpose_b, bf16_b, ld_b, RankMul(), adam_b};
   // one thread per 4 elements (vector form), else per element
   const int64_t per = R % 4 == 0 ? 4 : 1;
   const int64_t n_a = part_a ? grid_for(rows_a * (ld_a > R ? ld_a : R) / per) : 0;

@@ -41,6 +41,17 @@ class qlora_lora(ctypes.Structure):
                 ("keep", ctypes.c_void_p)]
 
 
+class qlora_adam_state(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("theta_bf16", ctypes.c_void_p)]
+
+
+class qlora_adam_hparams(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -65,6 +76,10 @@ def lib():
                                         plora, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd_lora.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32,
                                         ctypes.c_int, plora, vp, vp, vp, vp, vp, sz, vp]
+    pst, php = ctypes.POINTER(qlora_adam_state), ctypes.POINTER(qlora_adam_hparams)
+    L.qlora_linear_bwd_adam.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32,
+                                        ctypes.c_int, plora, vp, vp, pst, pst, php, vp, vp, vp,
+                                        sz, vp]
     L.qlora_merge.argtypes = [pnf4, vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
     f32 = ctypes.c_float
     L.qlora_adam_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
@@ -73,7 +88,7 @@ def lib():
     L.qlora_loftq_workspace_bytes.restype = sz
     for f in (L.qlora_quantize, L.qlora_linear_fwd, L.qlora_linear_bwd, L.qlora_merge,
               L.qlora_adam_step, L.qlora_loftq_init, L.qlora_linear_fwd_lora,
-              L.qlora_linear_bwd_lora):
+              L.qlora_linear_bwd_lora, L.qlora_linear_bwd_adam):
         f.restype = ctypes.c_int
     for f in (L.qlora_fwd_workspace_bytes, L.qlora_bwd_workspace_bytes):
         f.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -240,6 +255,27 @@ def qlora_linear_bwd_lora(wq, X, dY, M, act, A, B, r, adt, scale, dropout_p, kee
                                        _ptr(XA), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                        int(ws_bytes), _stream(stream)),
            "qlora_linear_bwd_lora")
+
+
+def qlora_linear_bwd_adam(wq, X, dY, M, act, A, B, r, adt, XA, dX, state_A, state_B, step, lr,
+                          ws, ws_bytes, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                          lora=None, dA=None, dB=None, stream=None):
+    """The backward with one Adam step of A and B fused into its last launch.
+    state_A / state_B: (theta, m, v, theta_bf16 or None) device tensors;
+    lora: None or (scale, dropout_p, keep)."""
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    sa = qlora_adam_state(*[_ptr(t) for t in state_A])
+    sb = qlora_adam_state(*[_ptr(t) for t in state_B])
+    hp = qlora_adam_hparams(int(step), float(lr), float(beta1), float(beta2), float(eps),
+                            float(weight_decay))
+    o = _lora(*lora) if lora is not None else None
+    _check(lib().qlora_linear_bwd_adam(ctypes.byref(s), _ptr(X), _ptr(dY), int(M), int(act),
+                                       _ptr(A), _ptr(B), int(r), int(adt),
+                                       ctypes.byref(o) if o is not None else None, _ptr(XA),
+                                       _ptr(dX), ctypes.byref(sa), ctypes.byref(sb),
+                                       ctypes.byref(hp), _ptr(dA), _ptr(dB), _ptr(ws),
+                                       int(ws_bytes), _stream(stream)),
+           "qlora_linear_bwd_adam")
 
 
 def qlora_levels():

@@ -217,6 +217,33 @@ def test_lora_validation(L):
     assert bwd(q.qlora_lora(2.0, 0.25, P)) == 1
 
 
+def test_bwd_adam_validation(L):
+    s = _nf4()
+    ws = q.qlora_bwd_workspace_bytes(64, 256, 256, 8, q.BF16)
+    st = q.qlora_adam_state(P, P, P, None)
+    good = q.qlora_adam_hparams(1, 1e-3, 0.9, 0.999, 1e-8, 0.0)
+    def call(M=64, sa=st, sb=st, hp=good, wsp=None, lora=None):
+        return L.qlora_linear_bwd_adam(ctypes.byref(s), P, P, M, q.BF16, P, P, 8, q.BF16,
+                                       ctypes.byref(lora) if lora is not None else None,
+                                       P, P, ctypes.byref(sa) if sa is not None else None,
+                                       ctypes.byref(sb) if sb is not None else None,
+                                       ctypes.byref(hp) if hp is not None else None,
+                                       None, None, wsp, ws, None)
+    assert call() == 1                                      # NULL workspace, after every check
+    assert call(hp=None) == 7
+    for bad in (q.qlora_adam_hparams(0, 1e-3, 0.9, 0.999, 1e-8, 0.0),
+                q.qlora_adam_hparams(1, 1e-3, 1.0, 0.999, 1e-8, 0.0),
+                q.qlora_adam_hparams(1, float("nan"), 0.9, 0.999, 1e-8, 0.0),
+                q.qlora_adam_hparams(1, 1e-3, 0.9, 0.999, -1.0, 0.0),
+                q.qlora_adam_hparams(1, 1e-3, 0.9, 0.999, 1e-8, -0.1)):
+        assert call(hp=bad) == 7
+    assert call(lora=q.qlora_lora(1.0, 0.5, None)) == 7
+    assert call(M=0) == 2
+    assert call(sa=None) == 1 and call(sb=q.qlora_adam_state(P, None, P, None)) == 1
+    assert call(sb=q.qlora_adam_state(P, P, U, None)) == 3
+    assert call(sa=q.qlora_adam_state(P, P, P, U)) == 3
+
+
 def test_merge_validation(L):
     s = _nf4()
     f = L.qlora_merge
