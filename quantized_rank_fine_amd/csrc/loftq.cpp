@@ -30,20 +30,28 @@ using Mat = std::vector<double>;   // row-major
 
 // Orthonormal columns of X (rows x k) by modified Gram-Schmidt, applied
 // twice; a column that vanishes becomes zero.
+// (The columns are copied out contiguously first, so every pass streams.)
 void orthonormalize(Mat &X, int64_t rows, int k) {
+  Mat C(X.size());
+  for (int64_t i = 0; i < rows; ++i)
+    for (int j = 0; j < k; ++j) C[j * rows + i] = X[i * k + j];
   for (int pass = 0; pass < 2; ++pass) {
     for (int j = 0; j < k; ++j) {
+      double *cj = C.data() + j * rows;
       for (int p = 0; p < j; ++p) {
+        const double *cp = C.data() + p * rows;
         double d = 0.0;
-        for (int64_t i = 0; i < rows; ++i) d += X[i * k + p] * X[i * k + j];
-        for (int64_t i = 0; i < rows; ++i) X[i * k + j] -= d * X[i * k + p];
+        for (int64_t i = 0; i < rows; ++i) d += cp[i] * cj[i];
+        for (int64_t i = 0; i < rows; ++i) cj[i] -= d * cp[i];
       }
       double n2 = 0.0;
-      for (int64_t i = 0; i < rows; ++i) n2 += X[i * k + j] * X[i * k + j];
+      for (int64_t i = 0; i < rows; ++i) n2 += cj[i] * cj[i];
       const double inv = n2 > 1e-300 ? 1.0 / std::sqrt(n2) : 0.0;
-      for (int64_t i = 0; i < rows; ++i) X[i * k + j] *= inv;
+      for (int64_t i = 0; i < rows; ++i) cj[i] *= inv;
     }
   }
+  for (int64_t i = 0; i < rows; ++i)
+    for (int j = 0; j < k; ++j) X[i * k + j] = C[j * rows + i];
 }
 
 // C (k x k) = Q^T X for Q, X (rows x k).
