@@ -39,6 +39,9 @@
 // each scale a per-scale table holds the 8 magnitudes bf16(|L|_m * scale) as
 // two v_perm byte planes (the level set is sign-symmetric), so a code becomes
 // its bf16 weight by table lookup and a sign bit.
+//
+// The dX GEMM can also form dB = XA^T . dY from the dY tiles it streams (see
+// DbFold below), so that the backward reads dY once.
 #include "device.h"
 
 namespace qlora {

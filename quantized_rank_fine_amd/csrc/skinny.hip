@@ -20,9 +20,12 @@
 // Launches are merged where the data allow it, each role on a contiguous
 // range of workgroup ids (the block-scale table for the GEMMs first).  At
 // M >= 1024 and r <= 32 the forward runs one launch (XA whole + scales) and
-// the backward one pass over dY (G whole, dB partials, scales), one pass over
-// X (dA partials) and one reduce of dA and dB; otherwise X.A and G come as
-// split-K partials with a reduce after each pass.
+// the backward one pass over dY (G whole, scales, and either dB partials or,
+// when the dX GEMM forms dB, the bf16 XA^T it needs), one pass over X (dA
+// partials) and one reduce of dA and dB; otherwise X.A and G come as split-K
+// partials with a reduce after each pass.  The bf16 copies of XA and G carry
+// the adapter options' multiplier (alpha/r, dropout; RankMul), and a reduce
+// can apply an Adam step to the sums it forms (AdamTarget).
 //
 // All matrix-core work is v_mfma_f32_16x16x32_bf16: operands rounded to bf16,
 // fp32 accumulation.
