@@ -42,6 +42,8 @@
 //
 // The dX GEMM can also form dB = XA^T . dY from the dY tiles it streams (see
 // DbFold below), so that the backward reads dY once.
+#include <type_traits>
+
 #include "device.h"
 
 namespace qlora {
@@ -440,7 +442,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   // ... and read back transposed as the two B fragments.
   auto read_b = [&](u32x4_t (&bb)[2]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32(scr, 32 * b);
+    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32(scr, 32 * (b ^ kh));   // see epilogue2
   };
   auto mfmas = [&](const u32x4_t (&a)[8], const u32x4_t (&bb)[2]) {
 #pragma unroll
@@ -767,6 +769,99 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem, cons
   }
 }
 
+// Forward epilogue.  The forward's K loop keeps column block b ^ kh in
+// accumulator b, so in every wavefront acc[0] is the column block it
+// finishes (kh) and acc[1] the one its partner (the other k half) finishes;
+// for kh = 0 that is the plain order, so the rank-r term is the same.  The k
+// halves then meet in two rounds of four row blocks: a wavefront writes
+// acc[1] of row blocks 4 h .. 4 h + 3 (16 KiB; 64 KiB in all), adds the
+// partner's copy of its own block to acc[0] (p0 + p1 either way round: fp32
+// addition commutes, so the bits are the four-round epilogue's), stages the
+// sums row-major and, after a barrier, stores half of the 128 staged rows.
+// Half the LDS traffic and five barriers instead of twelve.
+template <bool kOutBf16>
+__device__ __forceinline__ void epilogue2(f32x16_t (&acc)[2][8], char *smem, const RankOps &ro,
+                                          const uint16_t *__restrict__ P16, int ldp,
+                                          const AdapterRef q, int64_t M,
+                                          int64_t N, int64_t m0, int64_t n0, void *__restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ch = wave & 1, kh = wave >> 1;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int64_t nw = n0 + 64 * ch;
+
+  if (kh == 0 && q.r > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(ro.p[i], ro.qb[b], acc[b][i]);
+    for (int r0 = 16; r0 < q.r; r0 += 16) {
+      RankOps o;
+      load_rank_ops(o, P16, ldp, q, r0, M, N, m0, nw);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(o.p[i], o.qb[b], acc[b][i]);
+    }
+  }
+
+  constexpr int kOE = kOutBf16 ? 2 : 4;                       // output element bytes
+  constexpr int kOPitch = kOutBf16 ? 144 : 272;               // staging row pitch (bytes)
+  static_assert(65536 + 2 * 128 * kOPitch <= kLdsBytes, "epilogue LDS");
+  char *stg = smem + 65536 + ch * 128 * kOPitch;              // 128 rows x 64 columns per ch
+  char *wr = smem + (ch * 2 + kh) * 16384 + lane * 16;        // this wavefront's region
+  const char *rd = smem + (ch * 2 + (1 - kh)) * 16384 + lane * 16;   // the partner's
+  const bool ncol = nw < N;                                   // N % 64 == 0
+  auto round = [&](auto H) {
+    constexpr int h = decltype(H)::value;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const f32x16_t v = acc[1][4 * h + f];
+      char *w = wr + f * 4096;
+      *reinterpret_cast<f32x4_t *>(w) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+      *reinterpret_cast<f32x4_t *>(w + 1024) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+      *reinterpret_cast<f32x4_t *>(w + 2048) = __builtin_shufflevector(v, v, 8, 9, 10, 11);
+      *reinterpret_cast<f32x4_t *>(w + 3072) = __builtin_shufflevector(v, v, 12, 13, 14, 15);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(rd + f * 4096 + c * 1024);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[0][4 * h + f][4 * c + e] + x[e];
+          const int row = 32 * f + 8 * c + 4 * h2 + e;        // register 4c + e
+          char *d = stg + row * kOPitch + (32 * kh + l32) * kOE;
+          if constexpr (kOutBf16)
+            *reinterpret_cast<uint16_t *>(d) = bf16_bits(v);
+          else
+            *reinterpret_cast<float *>(d) = v;
+        }
+      }
+    }
+    __syncthreads();
+    // wavefront kh stores staged rows 64 kh .. 64 kh + 63 of these 128
+    constexpr int kChunks = 64 * kOE / 16;                    // 16-B chunks per row
+#pragma unroll
+    for (int qq = 0; qq < kChunks; ++qq) {
+      const int cid = lane + 64 * qq;
+      const int row = 64 * kh + cid / kChunks, c = cid % kChunks;
+      const int64_t m = m0 + 128 * h + row;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + row * kOPitch + 16 * c);
+      if (ncol && m < M)
+        *reinterpret_cast<u32x4_t *>(static_cast<char *>(Y) + (m * N + nw) * kOE + 16 * c) = v;
+    }
+  };
+  // Round 0 follows the K loop's last LDS reads; round 1's exchange writes
+  // follow round 0's exchange reads (two barriers back) and its staging
+  // writes follow round 0's stores (one barrier back).
+  __syncthreads();
+  round(std::integral_constant<int, 0>{});
+  round(std::integral_constant<int, 1>{});
+}
+
 // ================================================================ forward
 template <bool kOutBf16>
 __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
@@ -790,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc, DbFold{});
   // rank-r term: y += XA16 . B (B read as rows n of B^T)
-  epilogue<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
+  epilogue2<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
