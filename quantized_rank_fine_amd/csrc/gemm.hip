@@ -382,7 +382,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   } else {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int row = 64 * ch + 32 * b + l32;
+      const int row = 64 * ch + 32 * (b ^ kh) + l32;        // accumulator b = column block b ^ kh
       co[b] = uint32_t(((row >> 3) * 16 + h2 * 8 + (row & 7)) * 16 + 8 * kh);
     }
   }
@@ -410,8 +410,10 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       sc[0] = *reinterpret_cast<const float *>(sp);
       sc[1] = *reinterpret_cast<const float *>(sp + 32);     // k row kr(1) = kr(0) + 8
     } else {
-      sc[0] = *reinterpret_cast<const float *>(sp);
-      sc[1] = *reinterpret_cast<const float *>(sp + 128);
+      const float s0 = *reinterpret_cast<const float *>(sp);
+      const float s1 = *reinterpret_cast<const float *>(sp + 128);
+      sc[0] = kh ? s1 : s0;                                  // accumulator b = column block b ^ kh
+      sc[1] = kh ? s0 : s1;
     }
   };
   auto read_a = [&](const char *st, int j, u32x4_t (&a)[8]) {
@@ -442,7 +444,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   // ... and read back transposed as the two B fragments.
   auto read_b = [&](u32x4_t (&bb)[2]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32(scr, 32 * (b ^ kh));   // see epilogue2
+    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32(scr, 32 * (b ^ kh));   // see the epilogue
   };
   auto mfmas = [&](const u32x4_t (&a)[8], const u32x4_t (&bb)[2]) {
 #pragma unroll
@@ -675,112 +677,22 @@ __device__ __forceinline__ void load_rank_ops(RankOps &o, const uint16_t *__rest
 // Epilogue.  The rank-r term P16 . Q^T (P16 bf16 [M x ldp], zero-padded
 // columns r..ldp-1; Q the adapter factor, rows indexed by the output column)
 // is added by the k-half-0 wavefronts only, so it enters every output once
-// (ranks 0..15 from operands loaded at kernel start).
-// The two k halves of a column half are then summed through LDS in four
-// rounds of two row blocks: every wavefront writes its partials of row blocks
-// 2 rnd, 2 rnd + 1 (64 KiB in all), reads back both halves of column block
-// b = kh, sums them into a row-major staging tile, and after a barrier stores
-// half of the staged rows as whole row segments.  No register index depends
-// on kh, so the accumulators stay in their registers and are read straight
-// into the LDS writes.  LDS layout per fragment: 4 chunks of 1 KiB, chunk c =
-// registers 4c..4c+3 of every lane (16 B per lane, contiguous across lanes).
-template <bool kOutBf16>
-__device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem, const RankOps &ro,
-                                         const uint16_t *__restrict__ P16, int ldp,
-                                         const AdapterRef q, int64_t M,
-                                         int64_t N, int64_t m0, int64_t n0, void *__restrict__ Y) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ch = wave & 1, kh = wave >> 1;
-  const int l32 = lane & 31, h2 = lane >> 5;
-  const int64_t nw = n0 + 64 * ch;
-
-  if (kh == 0 && q.r > 0) {
-    // ranks 0..15 from the operands loaded at kernel start, the rest here
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(ro.p[i], ro.qb[b], acc[b][i]);
-    for (int r0 = 16; r0 < q.r; r0 += 16) {
-      RankOps o;
-      load_rank_ops(o, P16, ldp, q, r0, M, N, m0, nw);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[b][i] = mfma32x32x16(o.p[i], o.qb[b], acc[b][i]);
-    }
-  }
-
-  // Output staging after the 64-KiB exchange area: per column half ch, a
-  // 64-row x 64-column tile of the output dtype, so that the stores are whole
-  // 128-B (bf16) or 256-B (fp32) row segments written with 16-B stores.
-  constexpr int kOE = kOutBf16 ? 2 : 4;                       // output element bytes
-  constexpr int kOPitch = kOutBf16 ? 144 : 272;               // staging row pitch (bytes)
-  char *stg = smem + 65536 + ch * 64 * kOPitch;
-  char *wr = smem + (ch * 2 + kh) * 16384 + lane * 16;
-  const char *rd0 = smem + (ch * 2) * 16384 + kh * 4096 + lane * 16;   // k half 0, block b = kh
-  const char *rd1 = rd0 + 16384;                                         // k half 1
-  const bool ncol = nw < N;                                              // N % 64 == 0
-#pragma unroll
-  for (int rnd = 0; rnd < 4; ++rnd) {
-    __syncthreads();
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const f32x16_t v = acc[b][2 * rnd + ii];
-        char *w = wr + ii * 8192 + b * 4096;
-        *reinterpret_cast<f32x4_t *>(w) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
-        *reinterpret_cast<f32x4_t *>(w + 1024) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
-        *reinterpret_cast<f32x4_t *>(w + 2048) = __builtin_shufflevector(v, v, 8, 9, 10, 11);
-        *reinterpret_cast<f32x4_t *>(w + 3072) = __builtin_shufflevector(v, v, 12, 13, 14, 15);
-      }
-    __syncthreads();
-    // sum the two k halves of column block b = kh and stage them row-major
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(rd0 + ii * 8192 + c * 1024);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(rd1 + ii * 8192 + c * 1024);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 32 * ii + 8 * c + 4 * h2 + e;       // register 4c + e
-          char *d = stg + row * kOPitch + (32 * kh + l32) * kOE;
-          if constexpr (kOutBf16)
-            *reinterpret_cast<uint16_t *>(d) = bf16_bits(x0[e] + x1[e]);
-          else
-            *reinterpret_cast<float *>(d) = x0[e] + x1[e];
-        }
-      }
-    }
-    __syncthreads();
-    // wavefront kh stores staged rows 32 kh .. 32 kh + 31 of this 64-row block
-    constexpr int kChunks = 64 * kOE / 16;                    // 16-B chunks per row
-#pragma unroll
-    for (int q = 0; q < 32 * kChunks / 64; ++q) {
-      const int cid = lane + 64 * q;
-      const int row = 32 * kh + cid / kChunks, c = cid % kChunks;
-      const int64_t m = m0 + 64 * rnd + row;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + row * kOPitch + 16 * c);
-      if (ncol && m < M)
-        *reinterpret_cast<u32x4_t *>(static_cast<char *>(Y) + (m * N + nw) * kOE + 16 * c) = v;
-    }
-  }
-}
-
-// Forward epilogue.  The forward's K loop keeps column block b ^ kh in
-// accumulator b, so in every wavefront acc[0] is the column block it
-// finishes (kh) and acc[1] the one its partner (the other k half) finishes;
-// for kh = 0 that is the plain order, so the rank-r term is the same.  The k
-// halves then meet in two rounds of four row blocks: a wavefront writes
+// (ranks 0..15 from operands loaded at kernel start).  Both K loops keep
+// column block b ^ kh in accumulator b, so in every wavefront acc[0] is the
+// column block it finishes (kh) and acc[1] the one its partner (the other k
+// half) finishes; for kh = 0 that is the plain order, so the rank-r term
+// needs no change.  The k halves then meet in two rounds of four row blocks:
+// a wavefront writes
 // acc[1] of row blocks 4 h .. 4 h + 3 (16 KiB; 64 KiB in all), adds the
 // partner's copy of its own block to acc[0] (p0 + p1 either way round: fp32
 // addition commutes, so the bits are the four-round epilogue's), stages the
-// sums row-major and, after a barrier, stores half of the 128 staged rows.
-// Half the LDS traffic and five barriers instead of twelve.
+// sums row-major and, after a barrier, stores half of the 128 staged rows
+// as whole row segments.  LDS layout per fragment: 4 chunks of 1 KiB, chunk
+// c = registers 4c..4c+3 of every lane (16 B per lane, contiguous across
+// lanes).  (Exchanging both blocks in four rounds took twice the LDS
+// traffic and twelve barriers.)
 template <bool kOutBf16>
-__device__ __forceinline__ void epilogue2(f32x16_t (&acc)[2][8], char *smem, const RankOps &ro,
+__device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem, const RankOps &ro,
                                           const uint16_t *__restrict__ P16, int ldp,
                                           const AdapterRef q, int64_t M,
                                           int64_t N, int64_t m0, int64_t n0, void *__restrict__ Y) {
@@ -885,7 +797,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
   gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc, DbFold{});
   // rank-r term: y += XA16 . B (B read as rows n of B^T)
-  epilogue2<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
+  epilogue<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
