@@ -179,6 +179,11 @@ size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
  * into the workspace.  ws must hold qlora_bwd_workspace_bytes(M, in, out, r,
  * act) bytes of device memory.  r = 0 computes dX only (A, B, dA, dB, XA may
  * be NULL).  M = 0 writes zeros to dA and dB (ws may be NULL).
+ * With bf16 activations, M >= 1024, r <= 16 and r % 4 == 0, dB is formed
+ * inside the dX GEMM from a bf16 copy of XA (one partial per 256 tokens);
+ * without dX (dX == NULL) it comes from the pass over dY with XA in fp32, so
+ * the two calls may differ in the last bits of dB (both within the stated
+ * accuracy).  Same arguments always give the same bits.
  */
 qlora_status qlora_linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY,
                               int64_t M, qlora_dtype act, const void *A,
