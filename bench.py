@@ -221,13 +221,60 @@ def decode_report(sets, reps=5):
         nbytes = sets * sum(workloads.nf4_bytes(n_in, n_out) + M * n_in * 2 + (n_in * R + R * n_out) * 2
                             + M * n_out * 2 for (_, n_in, n_out) in lins)
         gbps = nbytes / (us * 1e-6) / 1e9
-        res[f"M{M}"] = {"us_per_layer_set": round(us / sets, 2), "GBps": round(gbps, 1),
-                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
         del graph
+
+        # The same sets with the projections that share an input grouped
+        # into one qlora_linear_fwd_group call each: q, k, v; o; gate, up;
+        # down (four launch pairs per set instead of seven).
+        names = [nm for (nm, _, _) in lins]
+        groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+        Yg = {nm: torch.empty(M, o, dtype=torch.bfloat16, device=dev) for (nm, _, o) in lins}
+        XAg = {nm: torch.empty(M, R, dtype=torch.float32, device=dev) for nm in names}
+        gws = max(q.qlora_fwd_group_workspace_bytes(M, [lins[names.index(nm)][1] for nm in grp],
+                                                    [lins[names.index(nm)][2] for nm in grp], R)
+                  for grp in groups)
+        wsg = torch.empty(gws, dtype=torch.uint8, device=dev)
+
+        def grouped():
+            for s in range(sets):
+                for grp in groups:
+                    idx = [names.index(nm) for nm in grp]
+                    q.qlora_linear_fwd_group([layers[s][i][0] for i in idx],
+                                             [X[lins[i][1]] for i in idx], M, q.BF16,
+                                             [layers[s][i][1] for i in idx],
+                                             [layers[s][i][2] for i in idx], R, q.BF16,
+                                             [Yg[nm] for nm in grp], [XAg[nm] for nm in grp],
+                                             wsg, gws)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            grouped()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            grouped()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        usg = e0.elapsed_time(e1) * 1e3 / reps
+        gbpsg = nbytes / (usg * 1e-6) / 1e9
+        del graph
+        res[f"M{M}"] = {"us_per_layer_set": round(us / sets, 2), "GBps": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                        "grouped": {"us_per_layer_set": round(usg / sets, 2),
+                                    "GBps": round(gbpsg, 1),
+                                    "frac_hbm_peak": round(gbpsg / PEAK_HBM_GBPS, 4)}}
     return {"workload": "7b-layer-decode-r16-bf16", "layer_sets": sets,
             "bytes_per_set_M1": sum(workloads.nf4_bytes(i, o) + i * 2 + (i * R + R * o) * 2 + o * 2
                                     for (_, i, o) in lins),
-            "timing": "HIP graph of the whole sequence, replayed", **res}
+            "timing": "HIP graph of the whole sequence, replayed; grouped: q/k/v and gate/up "
+                      "each one qlora_linear_fwd_group call", **res}
 
 
 def main():

@@ -276,6 +276,28 @@ qlora_status qlora_linear_bwd_adam(const qlora_nf4 *wq, const void *X, const voi
                                    hipStream_t stream);
 
 /*
+ * qlora_linear_fwd_group: the forward of up to 4 independent linears in one
+ * pair of launches, for decode (the q, k, v projections of a step share
+ * their input; gate and up too).  Only the few-token path: 1 <= M <= 16 and
+ * r <= 64, the same M, r, act, adt and codebook for all n; linear l has its
+ * own wq[l], X[l] [M, in_l], A[l], B[l], Y[l] [M, out_l] and XA[l] (as in
+ * qlora_linear_fwd; X[l] may be shared).  Each workgroup belongs to one
+ * linear, so every output is bit-identical to qlora_linear_fwd of that
+ * linear alone.  ws: qlora_fwd_group_workspace_bytes(n, M, in, out, r, act)
+ * bytes (in, out: host arrays of the n shapes).  Other shapes or n outside
+ * 1..4: QLORA_ERR_SHAPE; codebooks that differ: QLORA_ERR_DTYPE.
+ */
+qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq,
+                                    const void *const *X, int64_t M, qlora_dtype act,
+                                    const void *const *A, const void *const *B, int32_t r,
+                                    qlora_dtype adt, void *const *Y, float *const *XA,
+                                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of qlora_linear_fwd_group (host-only); 0 if invalid. */
+size_t qlora_fwd_group_workspace_bytes(int32_t n, int64_t M, const int64_t *in,
+                                       const int64_t *out, int32_t r, qlora_dtype act);
+
+/*
  * qlora_merge: the merged dense weight W = deq(Wq) + A.B
  *   ("How it works" step 5: fold the trained adapters into the base weight;
  *   "What the simulations show": the result is a dense float matrix, off the

@@ -435,6 +435,67 @@ qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M
 #undef QLORA_RUN
 }
 
+size_t qlora_fwd_group_workspace_bytes(int32_t n, int64_t M, const int64_t *in,
+                                       const int64_t *out, int32_t r, qlora_dtype act) {
+  if (n < 1 || n > kSmallMaxGroup || !in || !out || M < 1 || M > kSmallMaxM || r < 0 ||
+      r > kSmallMaxR || !dtype_ok(act))
+    return 0;
+  size_t total = 0;
+  for (int l = 0; l < n; ++l) {
+    if (!shape_ok(in[l], out[l])) return 0;
+    total += align_up(plan_fwd(M, in[l], out[l], r, act == QLORA_BF16).total);
+  }
+  return total;
+}
+
+qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq, const void *const *X,
+                                    int64_t M, qlora_dtype act, const void *const *A,
+                                    const void *const *B, int32_t r, qlora_dtype adt,
+                                    void *const *Y, float *const *XA, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (n < 1 || n > kSmallMaxGroup) return QLORA_ERR_SHAPE;
+  if (!wq || !X || !Y || (r > 0 && (!A || !B || !XA))) return QLORA_ERR_NULL;
+  if (M < 1 || M > kSmallMaxM || r < 0 || r > kSmallMaxR) return QLORA_ERR_SHAPE;
+  if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
+  SmallLinear lin[kSmallMaxGroup];
+  size_t off = 0;
+  for (int l = 0; l < n; ++l) {
+    qlora_status st = check_nf4(wq[l]);
+    if (st != QLORA_OK) return st;
+    if (wq[l]->codebook != wq[0]->codebook) return QLORA_ERR_DTYPE;
+    if (!X[l] || !Y[l]) return QLORA_ERR_NULL;
+    if (!aligned16(X[l]) || !aligned16(Y[l])) return QLORA_ERR_ALIGN;
+    if (r > 0) {
+      if (!A[l] || !B[l] || !XA[l]) return QLORA_ERR_NULL;
+      if (!aligned16(A[l]) || !aligned16(B[l]) || !aligned16(XA[l])) return QLORA_ERR_ALIGN;
+    }
+    const int64_t in = wq[l]->in, out = wq[l]->out;
+    const FwdPlan p = plan_fwd(M, in, out, r, act == QLORA_BF16);
+    SmallLinear &L = lin[l];
+    L.codes = wq[l]->codes;
+    L.qscale = wq[l]->qscale;
+    L.gscale = wq[l]->gscale;
+    L.K = in;
+    L.N = out;
+    L.X = X[l];
+    L.A = r > 0 ? A[l] : nullptr;
+    L.B = r > 0 ? B[l] : nullptr;
+    L.Kc = p.kc;
+    L.P = reinterpret_cast<float *>(static_cast<char *>(ws) + off + p.off_p);
+    L.PXA = r > 0 ? reinterpret_cast<float *>(static_cast<char *>(ws) + off + p.off_pxa) : nullptr;
+    L.XA = r > 0 ? XA[l] : nullptr;
+    L.Y = Y[l];
+    off += align_up(p.total);
+  }
+  if (!ws) return QLORA_ERR_NULL;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (ws_bytes < off) return QLORA_ERR_WORKSPACE;
+  return dev(timed(QLORA_KERNEL_FWD_SMALLM, stream, [&] {
+    return launch_fwd_small_group(n, lin, M, act == QLORA_BF16, adt == QLORA_BF16, r,
+                                  wq[0]->codebook, stream);
+  }));
+}
+
 qlora_status qlora_linear_bwd_lora(const qlora_nf4 *wq, const void *X, const void *dY,
                                    int64_t M, qlora_dtype act, const void *A, const void *B,
                                    int32_t r, qlora_dtype adt, const qlora_lora *lora,

@@ -187,6 +187,26 @@ hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS,
                                    void *Y, bool y_bf16, hipStream_t s,
                           RankMul mul = RankMul());
 
+// Up to kSmallMaxGroup independent few-token linears (same M, r and dtypes)
+// in the same two launches: each workgroup of the partial pass (and of the
+// reduction) is one of one linear's, so every linear's result is that of its
+// own launch pair.
+constexpr int kSmallMaxGroup = 4;
+struct SmallLinear {
+  const uint8_t *codes;
+  const int8_t *qscale;
+  const float *gscale;
+  int64_t K, N;                 // in, out
+  const void *X, *A, *B;
+  int64_t Kc;                   // small_fwd_chunk_rows(M, K, N)
+  float *P, *PXA;               // this linear's partials (workspace)
+  float *XA;
+  void *Y;
+  RankMul mul;
+};
+hipError_t launch_fwd_small_group(int n, const SmallLinear *lin, int64_t M, bool x_bf16,
+                                  bool a_bf16, int64_t r, int codebook, hipStream_t s);
+
 // W = deq(Wq) + A . B (W [in x out] fp32 or bf16; A [in x r], B [r x out]
 // in the adapter dtype), per element in fp32, one rounding at the end.
 hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2, int64_t in,

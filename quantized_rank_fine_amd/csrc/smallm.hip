@@ -122,7 +122,7 @@ __device__ __forceinline__ void store_x4(float (*xs)[kXPitchS], u32x4_t v, int64
 // The X . A workgroups (slice index == number of code slices): X[16 x kSub]
 // times A[kSub x r] for the chunk, wavefront w -> columns 16 w .. 16 w + 15.
 template <bool kX16, bool kA16>
-__device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int64_t kend,
+__device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int64_t kend, int by,
                                           float (*xs)[kXPitchS], uint16_t (*as)[kAPitch]) {
   const int t = threadIdx.x, lane = t & 63, g = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -185,7 +185,7 @@ __device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int6
   }
   const int j = 16 * wave + i;
   if (active && j < a.r) {
-    float *PX = a.PXA + int64_t(blockIdx.y) * a.M * a.r;
+    float *PX = a.PXA + int64_t(by) * a.M * a.r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = 4 * g + e;
@@ -194,8 +194,11 @@ __device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int6
   }
 }
 
+// One workgroup of the partial pass: column slice bx (bx == slices: the X . A
+// workgroup) of K chunk by.
 template <bool kX16, bool kA16>
-__global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, ExpandConsts16 t16) {
+__device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const ExpandConsts16 &t16,
+                                                int bx, int by) {
   __shared__ __attribute__((aligned(16))) float xs[16][kXPitchS];
   __shared__ __attribute__((aligned(16))) float cs[4][kSub];
   // codes of the 4 block columns, or (X . A workgroups) the adapter rows;
@@ -204,12 +207,12 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
   static_assert(kSub * kAPitch * 2 <= 4 * kRegion, "A tile fits the code tiles");
   static_assert(4 * 16 * 64 * 4 <= 4 * kRegion, "k-half sums fit the code tiles");
 
-  const int c = blockIdx.y;
+  const int c = by;
   const int64_t kbeg = int64_t(c) * a.Kc;
   const int64_t kend = min64(kbeg + a.Kc, a.K);
   const int64_t slices = (a.N + kSliceN - 1) / kSliceN;
-  if (blockIdx.x == slices) {
-    xa_worker<kX16, kA16>(a, kbeg, kend, xs, reinterpret_cast<uint16_t (*)[kAPitch]>(ct));
+  if (bx == slices) {
+    xa_worker<kX16, kA16>(a, kbeg, kend, by, xs, reinterpret_cast<uint16_t (*)[kAPitch]>(ct));
     return;
   }
 
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
   const int t = threadIdx.x, lane = t & 63, g = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: buffer descriptors
   const int bc = wave & 3, kh = wave >> 2;
-  const int64_t n0 = int64_t(blockIdx.x) * kSliceN;
+  const int64_t n0 = int64_t(bx) * kSliceN;
   const int64_t nblk = a.N / 64, blk = n0 / 64 + bc;
   const bool blk_ok = blk < nblk;
   const int64_t half_n = a.N / 2;
@@ -331,15 +334,58 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, Expan
   }
 }
 
+template <bool kX16, bool kA16>
+__global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, ExpandConsts16 t16) {
+  fwd_small_block<kX16, kA16>(a, t16, int(blockIdx.x), int(blockIdx.y));
+}
+
+// Several independent linears' partial passes in one launch: workgroups
+// base[g] .. base[g + 1] - 1 are linear g's grid, row-major over (slice,
+// chunk) with gx[g] slices per chunk.
+struct SmallGroup {
+  int n;
+  SmallArgs a[kSmallMaxGroup];
+  int base[kSmallMaxGroup + 1];
+  int gx[kSmallMaxGroup];
+};
+
+template <bool kX16, bool kA16>
+__global__ __launch_bounds__(kThreads1) void fwd_small_group_kernel(SmallGroup g,
+                                                                    ExpandConsts16 t16) {
+  const int bid = int(blockIdx.x);
+  int l = 0;
+#pragma unroll
+  for (int j = 1; j < kSmallMaxGroup; ++j)
+    if (j < g.n && bid >= g.base[j]) l = j;
+  const int local = bid - g.base[l];
+  fwd_small_block<kX16, kA16>(g.a[l], t16, local % g.gx[l], local / g.gx[l]);
+}
+
 // Pass 2: a workgroup covers `cols` = 256 / Mp columns of all M rows (Mp =
 // M rounded up to a power of two); thread -> (row, column).  The partials of
 // up to 32 chunks, 16 rows of B and the XA partials are all requested before
 // any is used (range-checked buffer loads: zero past the end), so the pass
 // waits for memory about once; sums run in chunk order.
+struct SmallReduceArgs {
+  const float *P, *PXA;
+  int64_t KS, M, N, r;
+  int cols;
+  const void *B;
+  float *XA;
+  void *Y;
+  RankMul mul;
+};
+
 template <bool kY16, bool kB16>
-__global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
-    const float *__restrict__ P, const float *__restrict__ PXA, int64_t KS, int64_t M, int64_t N,
-    int64_t r, int cols, const void *B, float *XA, void *Y, RankMul mul) {
+__device__ __forceinline__ void fwd_small_reduce_block(const SmallReduceArgs &ra, int bx) {
+  const float *__restrict__ P = ra.P;
+  const float *__restrict__ PXA = ra.PXA;
+  const int64_t KS = ra.KS, M = ra.M, N = ra.N, r = ra.r;
+  const int cols = ra.cols;
+  const void *B = ra.B;
+  float *XA = ra.XA;
+  void *Y = ra.Y;
+  const RankMul &mul = ra.mul;
   __shared__ float xa[16][kSmallMaxR];
   const int t = threadIdx.x;
   const int64_t ER = M * r;
@@ -351,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
       (void *)B, (short)0, clamp_records(r * N * esb), kBufFlags);
   const int m = t / cols;
-  const int64_t n = int64_t(blockIdx.x) * cols + (t % cols);
+  const int64_t n = int64_t(bx) * cols + (t % cols);
   const bool ok = m < M && n < N;
   auto load_b = [&](int j) -> float {
     const uint32_t off = uint32_t((int64_t(j) * N + n) * esb);
@@ -381,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
       for (int u = 0; u < 32; ++u) sx += xv[u];
     }
     xa[e / r][e % r] = rank_mul(mul, e / r, e % r, r, sx);
-    if (blockIdx.x == 0) XA[e] = sx;
+    if (bx == 0) XA[e] = sx;
   }
   __syncthreads();
   if (!ok) return;
@@ -414,6 +460,35 @@ __global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(
     static_cast<float *>(Y)[int64_t(m) * N + n] = y;
 }
 
+template <bool kY16, bool kB16>
+__global__ __launch_bounds__(kThreads) void fwd_small_reduce_kernel(SmallReduceArgs ra) {
+  fwd_small_reduce_block<kY16, kB16>(ra, int(blockIdx.x));
+}
+
+struct SmallReduceGroup {
+  int n;
+  SmallReduceArgs a[kSmallMaxGroup];
+  int base[kSmallMaxGroup + 1];
+};
+
+template <bool kY16, bool kB16>
+__global__ __launch_bounds__(kThreads) void fwd_small_reduce_group_kernel(SmallReduceGroup g) {
+  const int bid = int(blockIdx.x);
+  int l = 0;
+#pragma unroll
+  for (int j = 1; j < kSmallMaxGroup; ++j)
+    if (j < g.n && bid >= g.base[j]) l = j;
+  fwd_small_reduce_block<kY16, kB16>(g.a[l], bid - g.base[l]);
+}
+
+}  // namespace
+
+namespace {
+int reduce_cols(int64_t M) {
+  int mp = 1;
+  while (mp < M) mp *= 2;
+  return kThreads / mp;
+}
 }  // namespace
 
 int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N) {
@@ -449,16 +524,59 @@ hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
                                    void *Y, bool y_bf16, hipStream_t s,
                          RankMul mul) {
-  int mp = 1;
-  while (mp < M) mp *= 2;
-  const int cols = kThreads / mp;
+  const int cols = reduce_cols(M);
   const dim3 grid = dim3(unsigned((N + cols - 1) / cols));
+  const SmallReduceArgs ra{P, PXA, KS, M, N, r, cols, B, XA, Y, mul};
   if (y_bf16) {
-    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<true, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
-    else hipLaunchKernelGGL((fwd_small_reduce_kernel<true, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
+    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<true, true>), grid, dim3(kThreads), 0, s, ra);
+    else hipLaunchKernelGGL((fwd_small_reduce_kernel<true, false>), grid, dim3(kThreads), 0, s, ra);
   } else {
-    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<false, true>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
-    else hipLaunchKernelGGL((fwd_small_reduce_kernel<false, false>), grid, dim3(kThreads), 0, s, P, PXA, KS, M, N, r, cols, B, XA, Y, mul);
+    if (b_bf16) hipLaunchKernelGGL((fwd_small_reduce_kernel<false, true>), grid, dim3(kThreads), 0, s, ra);
+    else hipLaunchKernelGGL((fwd_small_reduce_kernel<false, false>), grid, dim3(kThreads), 0, s, ra);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_small_group(int n, const SmallLinear *lin, int64_t M, bool x_bf16,
+                                  bool a_bf16, int64_t r, int codebook, hipStream_t s) {
+  if (n < 1 || n > kSmallMaxGroup) return hipErrorInvalidValue;
+  if (!tables(codebook).symmetric) return hipErrorInvalidValue;
+  const ExpandConsts16 &t16 = tables(codebook).expand16;
+  SmallGroup g{};
+  SmallReduceGroup rg{};
+  g.n = rg.n = n;
+  int64_t nb = 0, nr = 0;
+  const int cols = reduce_cols(M);
+  for (int l = 0; l < n; ++l) {
+    const SmallLinear &L = lin[l];
+    const int64_t KS = (L.K + L.Kc - 1) / L.Kc;
+    const int64_t gx = (L.N + kSliceN - 1) / kSliceN + (r > 0 ? 1 : 0);
+    g.a[l] = SmallArgs{L.codes, L.qscale, L.gscale, L.K, L.N, L.X, L.A, M, r, L.Kc, L.P, L.PXA};
+    g.base[l] = int(nb);
+    g.gx[l] = int(gx);
+    nb += gx * KS;
+    rg.a[l] = SmallReduceArgs{L.P, L.PXA, KS, M, L.N, r, cols, L.B, L.XA, L.Y, L.mul};
+    rg.base[l] = int(nr);
+    nr += (L.N + cols - 1) / cols;
+  }
+  g.base[n] = int(nb);
+  rg.base[n] = int(nr);
+  if (x_bf16) {
+    if (a_bf16) hipLaunchKernelGGL((fwd_small_group_kernel<true, true>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
+    else hipLaunchKernelGGL((fwd_small_group_kernel<true, false>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
+  } else {
+    if (a_bf16) hipLaunchKernelGGL((fwd_small_group_kernel<false, true>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
+    else hipLaunchKernelGGL((fwd_small_group_kernel<false, false>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the reduction: y and B in the activation / adapter dtypes as the partial pass's X, A
+  if (x_bf16) {
+    if (a_bf16) hipLaunchKernelGGL((fwd_small_reduce_group_kernel<true, true>), dim3(unsigned(nr)), dim3(kThreads), 0, s, rg);
+    else hipLaunchKernelGGL((fwd_small_reduce_group_kernel<true, false>), dim3(unsigned(nr)), dim3(kThreads), 0, s, rg);
+  } else {
+    if (a_bf16) hipLaunchKernelGGL((fwd_small_reduce_group_kernel<false, true>), dim3(unsigned(nr)), dim3(kThreads), 0, s, rg);
+    else hipLaunchKernelGGL((fwd_small_reduce_group_kernel<false, false>), dim3(unsigned(nr)), dim3(kThreads), 0, s, rg);
   }
   return hipGetLastError();
 }

@@ -80,6 +80,14 @@ def lib():
     L.qlora_linear_bwd_adam.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32,
                                         ctypes.c_int, plora, vp, vp, pst, pst, php, vp, vp, vp,
                                         sz, vp]
+    L.qlora_linear_fwd_group.argtypes = [i32, ctypes.POINTER(pnf4), ctypes.POINTER(vp), i64,
+                                         ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                         i32, ctypes.c_int, ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), vp, sz, vp]
+    L.qlora_linear_fwd_group.restype = ctypes.c_int
+    L.qlora_fwd_group_workspace_bytes.argtypes = [i32, i64, ctypes.POINTER(i64),
+                                                  ctypes.POINTER(i64), i32, ctypes.c_int]
+    L.qlora_fwd_group_workspace_bytes.restype = sz
     L.qlora_merge.argtypes = [pnf4, vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
     f32 = ctypes.c_float
     L.qlora_adam_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
@@ -276,6 +284,27 @@ def qlora_linear_bwd_adam(wq, X, dY, M, act, A, B, r, adt, XA, dX, state_A, stat
                                        ctypes.byref(hp), _ptr(dA), _ptr(dB), _ptr(ws),
                                        int(ws_bytes), _stream(stream)),
            "qlora_linear_bwd_adam")
+
+
+def qlora_fwd_group_workspace_bytes(M, ins, outs, r, act=None):
+    n = len(ins)
+    act = BF16 if act is None else act
+    return int(lib().qlora_fwd_group_workspace_bytes(n, int(M), (ctypes.c_int64 * n)(*ins),
+                                                     (ctypes.c_int64 * n)(*outs), int(r),
+                                                     int(act)))
+
+
+def qlora_linear_fwd_group(wqs, Xs, M, act, As, Bs, r, adt, Ys, XAs, ws, ws_bytes, stream=None):
+    """Forward of up to 4 independent few-token linears in one pair of
+    launches (lists of the per-linear weights and tensors)."""
+    n = len(wqs)
+    structs = [w.struct() if isinstance(w, NF4Weight) else w for w in wqs]
+    pw = (ctypes.POINTER(qlora_nf4) * n)(*[ctypes.pointer(st) for st in structs])
+    arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
+    _check(lib().qlora_linear_fwd_group(n, pw, arr(Xs), int(M), int(act), arr(As), arr(Bs),
+                                        int(r), int(adt), arr(Ys), arr(XAs), _ptr(ws),
+                                        int(ws_bytes), _stream(stream)),
+           "qlora_linear_fwd_group")
 
 
 def qlora_levels():

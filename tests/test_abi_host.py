@@ -244,6 +244,28 @@ def test_bwd_adam_validation(L):
     assert call(sa=q.qlora_adam_state(P, P, P, U)) == 3
 
 
+def test_fwd_group_validation(L):
+    n = 2
+    ins, outs = [256, 320], [256, 192]
+    ws = q.qlora_fwd_group_workspace_bytes(4, ins, outs, 16)
+    assert ws > 0
+    assert q.qlora_fwd_group_workspace_bytes(17, ins, outs, 16) == 0      # not few-token
+    assert q.qlora_fwd_group_workspace_bytes(4, ins, outs, 65) == 0
+    assert q.qlora_fwd_group_workspace_bytes(4, [256, 100], outs, 16) == 0
+    s = [_nf4(256, 256), _nf4(320, 192)]
+    pw = lambda st: (ctypes.POINTER(q.qlora_nf4) * len(st))(*[ctypes.pointer(x) for x in st])
+    arr = lambda v, k=n: (ctypes.c_void_p * k)(*([v] * k))
+    def call(k=n, M=4, r=16, st=s, X=P, Y=P, wsp=P, wsb=ws):
+        return L.qlora_linear_fwd_group(k, pw(st), arr(X, len(st)), M, q.BF16, arr(P, len(st)),
+                                        arr(P, len(st)), r, q.BF16, arr(Y, len(st)),
+                                        arr(P, len(st)), wsp, wsb, None)
+    assert call(k=0) == 2 and call(k=5) == 2
+    assert call(M=0) == 2 and call(M=17) == 2 and call(r=65) == 2
+    assert call(st=[_nf4(256, 256), _nf4(320, 192, cb=1)]) == 4       # codebooks differ
+    assert call(X=None) == 1 and call(Y=U) == 3
+    assert call(wsp=None) == 1 and call(wsb=ws - 1) == 5
+
+
 def test_merge_validation(L):
     s = _nf4()
     f = L.qlora_merge

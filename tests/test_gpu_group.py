@@ -1,0 +1,41 @@
+"""qlora_linear_fwd_group: up to four independent few-token linears in one
+pair of launches give, for each linear, the bits of its own
+qlora_linear_fwd call (same kernels, one workgroup per linear's tile)."""
+
+import numpy as np
+import pytest
+
+from quantized_rank_fine_amd import qlora as q
+
+from gpu_harness import Layer, say, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("shapes,shared_x", [
+    ([(576, 448), (576, 448), (576, 448)], True),       # q, k, v: one input, three weights
+    ([(640, 704), (640, 704)], True),                   # gate, up
+    ([(576, 448), (640, 704), (320, 256), (1088, 192)], False),   # four unrelated shapes
+])
+def test_group_equals_single_calls(M, shapes, shared_x):
+    torch, dev = torch_dev()
+    say(f"[group] M={M} shapes={shapes} shared_x={shared_x}")
+    r = 16
+    layers = [Layer(61 + l, M, i, o, r) for l, (i, o) in enumerate(shapes)]
+    if shared_x:
+        for L in layers[1:]:
+            L.tX = layers[0].tX
+    ref = [L.fwd() for L in layers]
+    Ys = [torch.full((M, o), float("nan"), dtype=torch.bfloat16, device=dev) for (_, o) in shapes]
+    XAs = [torch.full((M, r), float("nan"), dtype=torch.float32, device=dev) for _ in shapes]
+    wsb = q.qlora_fwd_group_workspace_bytes(M, [i for i, _ in shapes], [o for _, o in shapes], r)
+    assert wsb > 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    q.qlora_linear_fwd_group([L.wq for L in layers], [L.tX for L in layers], M, q.BF16,
+                             [L.tA for L in layers], [L.tB for L in layers], r, q.BF16,
+                             Ys, XAs, ws, wsb)
+    torch.cuda.synchronize()
+    for l, ((Y0, XA0), Y, XA) in enumerate(zip(ref, Ys, XAs)):
+        assert np.array_equal(Y.float().cpu().numpy(), Y0.float().cpu().numpy()), l
+        assert np.array_equal(XA.cpu().numpy(), XA0.cpu().numpy()), l
