@@ -7,17 +7,34 @@
 //
 // Per element, in fp32: w = L[code] * (q_b * s2_g) (the two products the
 // fused GEMMs form before their bf16 rounding), plus sum_j A[k][j] * B[j][n]
-// accumulated in rank order with fp32 fused multiply-adds, then one rounding
-// to the output dtype.
+// in fp32, then one rounding to the output dtype.
 //
-// Workgroup: 256 threads, a 64-row x 128-column tile of W.  Thread t owns rows
+// Two kernels.  With bf16 adapters and r % 8 == 0 (and for r = 0) the rank-r
+// term is a dense contraction over r and runs on the matrix cores:
+// merge_mfma_kernel starts each 32 x 32 MFMA accumulator from the dequantized
+// fp32 weights and adds A.B in 16-rank steps (bf16 x bf16 products are exact
+// in fp32; only the order of the fp32 additions is the hardware's).  The FMA
+// kernel below serves fp32 adapters and other ranks, summing in rank order.
+//
+// merge_mfma_kernel: 256 threads, a 64-row x 128-column tile; wavefront w owns
+// rows 32 (w & 1) .. +31 and columns 64 (w >> 1) .. +63 as two 32 x 32 blocks.
+// Each block is computed transposed, D = B^T-block . A^T-block + C, so that
+// lane l holds W row l % 32 at columns 8 g + 4 (l / 32) + 0..3 (g = 0..3): the
+// 16-B code vector of that row segment gives its nibbles, one block scale
+// covers it, and A's 8 ranks per lane are one contiguous 16-B load (B's are
+// 8 strided 2-B loads, L2-resident).  The tile then goes through a per-wave
+// LDS buffer so that each store is a row-contiguous run (128 B of bf16, 256 B
+// of fp32 per row), written with
+// non-temporal stores (W is not read again by this launch).
+//
+// FMA kernel: 256 threads, a 64-row x 128-column tile of W.  Thread t owns rows
 // 4 (t >> 4) .. +3 and columns 8 (t & 15) .. +7: four 4-byte code words (one
 // 64-block each, so one scale per row) and a 4 x 8 fp32 accumulator of the
 // rank-r term.  The rank runs in chunks of 32: the A chunk is staged
 // transposed ([j][row], 68-float pitch) and the B chunk as is ([j][col]), so
 // a thread reads one 16-B A quad and two 16-B B quads per rank index for 32
 // multiply-adds.  The kernel is bound by HBM (the output write) for small r
-// and by the fp32 multiply-adds (8 r per weight) as r grows.
+// and by the fp32 multiply-adds (r per weight) as r grows.
 #include "device.h"
 
 namespace qlora {
@@ -120,6 +137,99 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, Levels lv) {
   }
 }
 
+// ---- matrix-core kernel ----
+constexpr int kMRows = 64, kMCols = 128, kMBlocks = 2;    // blocks of 32 columns per wave
+
+template <bool kWbf16>
+__global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv) {
+  constexpr int kES = kWbf16 ? 2 : 4;                      // output element bytes
+  constexpr int kRowB = 32 * kMBlocks * kES;               // staged bytes per row
+  constexpr int kPitch = kRowB + 16;
+  __shared__ float sL[4][16];
+  __shared__ __align__(16) uint8_t stage[4 * 32 * kPitch];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, l32 = l & 31, h = l >> 5;
+  const int64_t row0 = int64_t(blockIdx.y) * kMRows + 32 * (w & 1), row = row0 + l32;
+  const int64_t nw0 = int64_t(blockIdx.x) * kMCols + (w >> 1) * (32 * kMBlocks);
+  if (nw0 >= a.out) return;                                // whole wavefront; no block barrier
+  const int nb = int(min64(kMBlocks, (a.out - nw0) / 32));
+  if (l < 16) sL[w][l] = lv.L[l];
+  __builtin_amdgcn_wave_barrier();
+  const int64_t NB = a.out / 64;
+  const uint16_t *A = static_cast<const uint16_t *>(a.A);
+  const uint16_t *B = static_cast<const uint16_t *>(a.B);
+
+  u32x4_t cw[kMBlocks];
+  float sc[kMBlocks];
+#pragma unroll
+  for (int b = 0; b < kMBlocks; ++b) {
+    if (b < nb) {
+      const int64_t n = nw0 + 32 * b;
+      cw[b] = *reinterpret_cast<const u32x4_t *>(a.codes + (row * a.out + n) / 2);
+      const int64_t blk = row * NB + n / 64;
+      sc[b] = float(a.q8[blk]) * a.s2[blk >> 8];
+    }
+  }
+  f32x16_t acc[kMBlocks];
+#pragma unroll
+  for (int b = 0; b < kMBlocks; ++b) {
+    if (b < nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)                          // column 8 (i / 4) + 4 h + i % 4
+        acc[b][i] = sL[w][(cw[b][i >> 2] >> (4 * (4 * h + (i & 3)))) & 15u] * sc[b];
+    }
+  }
+  for (int j0 = 0; j0 < a.r; j0 += 16) {
+    const int jh = j0 + 8 * h;                              // this lane's 8 ranks
+    u32x4_t af = {0, 0, 0, 0};
+    if (jh < a.r) af = *reinterpret_cast<const u32x4_t *>(A + row * a.r + jh);
+#pragma unroll
+    for (int b = 0; b < kMBlocks; ++b) {
+      if (b < nb) {
+        const int64_t n = nw0 + 32 * b + l32;
+        u32x4_t bf = {0, 0, 0, 0};
+        if (jh < a.r) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bf[e] = uint32_t(B[int64_t(jh + 2 * e) * a.out + n]) |
+                    (uint32_t(B[int64_t(jh + 2 * e + 1) * a.out + n]) << 16);
+        }
+        acc[b] = mfma32x32x16(bf, af, acc[b]);
+      }
+    }
+  }
+  // Registers -> per-wave LDS rows -> row-contiguous stores.
+#pragma unroll
+  for (int b = 0; b < kMBlocks; ++b) {
+    if (b < nb) {
+      uint8_t *base = stage + (w * 32 + l32) * kPitch + 32 * kES * b;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint8_t *d = base + kES * (8 * g + 4 * h);
+        if constexpr (kWbf16)
+          *reinterpret_cast<u32x2_t *>(d) =
+              u32x2_t{pack_bf16x2(acc[b][4 * g], acc[b][4 * g + 1]),
+                      pack_bf16x2(acc[b][4 * g + 2], acc[b][4 * g + 3])};
+        else
+          *reinterpret_cast<f32x4_t *>(d) =
+              f32x4_t{acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  constexpr int kLanesRow = kRowB / 16, kRowsPer = 64 / kLanesRow;
+  const int pr = l / kLanesRow, pc = l % kLanesRow;
+  if (pc < nb * (kLanesRow / kMBlocks)) {
+    uint8_t *W = static_cast<uint8_t *>(a.W);
+#pragma unroll
+    for (int it = 0; it < 32 / kRowsPer; ++it) {
+      const int rr = it * kRowsPer + pr;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + (w * 32 + rr) * kPitch + 16 * pc);
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4_t *>(W + ((row0 + rr) * a.out + nw0) * kES + 16 * pc));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2, int64_t in,
@@ -129,6 +239,12 @@ hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2,
   Levels lv;
   const Tables &t = tables(codebook);
   for (int i = 0; i < 16; ++i) lv.L[i] = t.L[i];
+  if (r == 0 || (a_bf16 && r % 8 == 0)) {
+    const dim3 mgrid(unsigned((out + kMCols - 1) / kMCols), unsigned(in / kMRows));
+    if (w_bf16) hipLaunchKernelGGL((merge_mfma_kernel<true>), mgrid, dim3(256), 0, s, a, lv);
+    else hipLaunchKernelGGL((merge_mfma_kernel<false>), mgrid, dim3(256), 0, s, a, lv);
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned((out + kCols - 1) / kCols), unsigned(in / kRows));
   if (a_bf16) {
     if (w_bf16) hipLaunchKernelGGL((merge_kernel<true, true>), grid, dim3(256), 0, s, a, lv);
