@@ -417,7 +417,20 @@ def main():
              "GBps": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1),
              "frac_hbm_peak": round(merge_bytes / (merge_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
              "what": "W = deq(Wq) + A.B written as dense bf16, r = 16"}
-    del Wm
+    # The same from fp32 adapters (the optimizer's master copies).
+    A32, B32 = A.float().contiguous(), B.float().contiguous()
+    q.qlora_merge(wq, A32, B32, r, q.F32, Wm, q.BF16)
+    torch.cuda.synchronize()
+    em0.record()
+    for i in range(K):
+        q.qlora_merge(wq, A32, B32, r, q.F32, Wm, q.BF16)
+    em1.record()
+    torch.cuda.synchronize()
+    m32_us = em0.elapsed_time(em1) * 1e3 / K
+    m32_bytes = merge_bytes + 2 * r * (n_in + n_out)
+    merge["fp32_adapters"] = {"us": round(m32_us, 2), "algorithmic_bytes": m32_bytes,
+                              "GBps": round(m32_bytes / (m32_us * 1e-6) / 1e9, 1)}
+    del Wm, A32, B32
 
     # Adam step of both adapter matrices (fp32 master copies, bf16 copies for
     # the forward), K times.

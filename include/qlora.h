@@ -304,8 +304,8 @@ size_t qlora_fwd_group_workspace_bytes(int32_t n, int64_t M, const int64_t *in,
  *   quantization grid).
  *   A [in, r], B [r, out] in adt; W [in, out] in wdt (output, caller-owned).
  * Per element in fp32: L[code] * (q_b * s2_g), plus the rank-r sum, rounded
- * once to wdt.  With adt = QLORA_BF16 and r % 8 == 0 the sum runs on the
- * matrix cores (exact products, fp32 additions in the hardware's order);
+ * once to wdt.  With r % 8 == 0 the sum runs on the matrix cores (fp32
+ * additions in the hardware's order; bf16 adapters give exact products);
  * otherwise it is accumulated in rank order with fp32 fused multiply-adds.
  * r = 0 writes deq(Wq) (A, B may be NULL).  To store the merged weight
  * in 4 bits again, merge with wdt = QLORA_F32 and pass W to qlora_quantize

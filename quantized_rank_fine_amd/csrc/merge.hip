@@ -9,20 +9,21 @@
 // fused GEMMs form before their bf16 rounding), plus sum_j A[k][j] * B[j][n]
 // in fp32, then one rounding to the output dtype.
 //
-// Two kernels.  With bf16 adapters and r % 8 == 0 (and for r = 0) the rank-r
-// term is a dense contraction over r and runs on the matrix cores:
-// merge_mfma_kernel starts each 32 x 32 MFMA accumulator from the dequantized
-// fp32 weights and adds A.B in 16-rank steps (bf16 x bf16 products are exact
-// in fp32; only the order of the fp32 additions is the hardware's).  The FMA
-// kernel below serves fp32 adapters and other ranks, summing in rank order.
+// Two kernels.  For r % 8 == 0 (r = 0 included) the rank-r term is a dense
+// contraction over r and runs on the matrix cores: merge_mfma_kernel starts
+// each 32 x 32 MFMA accumulator from the dequantized fp32 weights and adds
+// A.B in 16-rank steps, as 32 x 32 x 16 bf16 MFMAs for bf16 adapters (the
+// products exact in fp32) or 32 x 32 x 2 fp32 MFMAs for fp32 adapters; the
+// order of the fp32 additions is the hardware's.  The FMA kernel below
+// serves the other ranks, summing in rank order.
 //
 // merge_mfma_kernel: 256 threads, a 64-row x 128-column tile; wavefront w owns
 // rows 32 (w & 1) .. +31 and columns 64 (w >> 1) .. +63 as two 32 x 32 blocks.
 // Each block is computed transposed, D = B^T-block . A^T-block + C, so that
 // lane l holds W row l % 32 at columns 8 g + 4 (l / 32) + 0..3 (g = 0..3): the
 // 16-B code vector of that row segment gives its nibbles, one block scale
-// covers it, and A's 8 ranks per lane are one contiguous 16-B load (B's are
-// 8 strided 2-B loads, L2-resident).  The tile then goes through a per-wave
+// covers it, and A's 8 ranks per lane are contiguous (B's are 8 strided
+// loads, L2-resident).  The tile then goes through a per-wave
 // LDS buffer so that each store is a row-contiguous run (128 B of bf16, 256 B
 // of fp32 per row), written with
 // non-temporal stores (W is not read again by this launch).
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, Levels lv) {
 // ---- matrix-core kernel ----
 constexpr int kMRows = 64, kMCols = 128, kMBlocks = 2;    // blocks of 32 columns per wave
 
-template <bool kWbf16>
+template <bool kAbf16, bool kWbf16>
 __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv) {
   constexpr int kES = kWbf16 ? 2 : 4;                      // output element bytes
   constexpr int kRowB = 32 * kMBlocks * kES;               // staged bytes per row
@@ -155,8 +156,6 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
   if (l < 16) sL[w][l] = lv.L[l];
   __builtin_amdgcn_wave_barrier();
   const int64_t NB = a.out / 64;
-  const uint16_t *A = static_cast<const uint16_t *>(a.A);
-  const uint16_t *B = static_cast<const uint16_t *>(a.B);
 
   u32x4_t cw[kMBlocks];
   float sc[kMBlocks];
@@ -178,6 +177,9 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
         acc[b][i] = sL[w][(cw[b][i >> 2] >> (4 * (4 * h + (i & 3)))) & 15u] * sc[b];
     }
   }
+  if constexpr (kAbf16) {
+  const uint16_t *A = static_cast<const uint16_t *>(a.A);
+  const uint16_t *B = static_cast<const uint16_t *>(a.B);
   for (int j0 = 0; j0 < a.r; j0 += 16) {
     const int jh = j0 + 8 * h;                              // this lane's 8 ranks
     u32x4_t af = {0, 0, 0, 0};
@@ -196,6 +198,34 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
         acc[b] = mfma32x32x16(bf, af, acc[b]);
       }
     }
+  }
+  } else {
+  // fp32 adapters: 32 x 32 x 2 fp32 MFMAs, lane half h taking ranks
+  // j0 + 8 h + s at step s (both operands alike, so each product pairs
+  // A[k][j] with B[j][n]).
+  const float *A = static_cast<const float *>(a.A);
+  const float *B = static_cast<const float *>(a.B);
+  for (int j0 = 0; j0 < a.r; j0 += 16) {
+    const int jh = j0 + 8 * h;
+    f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    if (jh < a.r) {
+      a0 = *reinterpret_cast<const f32x4_t *>(A + row * a.r + jh);
+      a1 = *reinterpret_cast<const f32x4_t *>(A + row * a.r + jh + 4);
+    }
+#pragma unroll
+    for (int b = 0; b < kMBlocks; ++b) {
+      if (b < nb) {
+        const int64_t n = nw0 + 32 * b + l32;
+        float bv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = jh < a.r ? B[int64_t(jh + e) * a.out + n] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[e], e < 4 ? a0[e] : a1[e - 4], acc[b],
+                                                        0, 0, 0);
+      }
+    }
+  }
   }
   // Registers -> per-wave LDS rows -> row-contiguous stores.
 #pragma unroll
@@ -239,10 +269,15 @@ hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2,
   Levels lv;
   const Tables &t = tables(codebook);
   for (int i = 0; i < 16; ++i) lv.L[i] = t.L[i];
-  if (r == 0 || (a_bf16 && r % 8 == 0)) {
+  if (r % 8 == 0) {                                        // r = 0 included
     const dim3 mgrid(unsigned((out + kMCols - 1) / kMCols), unsigned(in / kMRows));
-    if (w_bf16) hipLaunchKernelGGL((merge_mfma_kernel<true>), mgrid, dim3(256), 0, s, a, lv);
-    else hipLaunchKernelGGL((merge_mfma_kernel<false>), mgrid, dim3(256), 0, s, a, lv);
+    if (a_bf16) {
+      if (w_bf16) hipLaunchKernelGGL((merge_mfma_kernel<true, true>), mgrid, dim3(256), 0, s, a, lv);
+      else hipLaunchKernelGGL((merge_mfma_kernel<true, false>), mgrid, dim3(256), 0, s, a, lv);
+    } else {
+      if (w_bf16) hipLaunchKernelGGL((merge_mfma_kernel<false, true>), mgrid, dim3(256), 0, s, a, lv);
+      else hipLaunchKernelGGL((merge_mfma_kernel<false, false>), mgrid, dim3(256), 0, s, a, lv);
+    }
     return hipGetLastError();
   }
   const dim3 grid(unsigned((out + kCols - 1) / kCols), unsigned(in / kRows));
