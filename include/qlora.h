@@ -35,9 +35,14 @@
  *   - Outputs are overwritten, never accumulated.  Wq, X, A, B, dY and XA
  *     (in the backward) are only read.
  *   - The library keeps no state between calls except the constant tables
- *     it derives once from the level definition, and allocates no device
- *     memory: scratch space is the caller's `ws` buffer.  Calls are
- *     reentrant; calls on different streams may run concurrently.
+ *     it derives once from the level definition (and, only while switched
+ *     on, the kernel-timing records at the end of this header), and
+ *     allocates no device memory: scratch space is the caller's `ws`
+ *     buffer.  Calls are reentrant; calls on different streams may run
+ *     concurrently.
+ *   - Shapes: in and out are multiples of 64, at most 2^19 each, with
+ *     in*out < 2^32 weights; at most 2^24 tokens per call.  The kernels
+ *     address memory with 32-bit offsets; larger shapes give QLORA_ERR_SHAPE.
  *   - Same inputs give the same output bits (no order-dependent atomics).
  *   - Finite inputs are assumed; NaN/Inf inputs give unspecified outputs.
  */
@@ -56,8 +61,9 @@ extern "C" {
 typedef enum {
   QLORA_OK = 0,
   QLORA_ERR_NULL = 1,      /* a required pointer is NULL                    */
-  QLORA_ERR_SHAPE = 2,     /* in/out not positive multiples of 64, M < 0,
-                              r outside [0, QLORA_MAX_RANK]                 */
+  QLORA_ERR_SHAPE = 2,     /* in/out not positive multiples of 64 or past
+                              the limits above, M < 0 or M > 2^24, r
+                              outside [0, QLORA_MAX_RANK]                   */
   QLORA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned              */
   QLORA_ERR_DTYPE = 4,     /* unknown qlora_dtype or qlora_codebook         */
   QLORA_ERR_WORKSPACE = 5, /* ws too small (see qlora_bwd_workspace_bytes)  */
@@ -150,12 +156,13 @@ qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t st
  *   ("How it works" step 2; "Mathematical Formulation" forward pass).
  *   X   [M, in]  act dtype         Y  [M, out] act dtype (output)
  *   A   [in, r]  adt dtype         B  [r, out] adt dtype
- *   XA  [M, r]   fp32 (output; the saved activation the backward reads).
+ *   XA  [M, r]   fp32 (output, optional: the saved activation the backward
+ *                reads; NULL skips it, and the backward then recomputes it).
  * The base weight is expanded to bf16 in registers, w = bf16(L[code] *
  * (q_b * s2_g)) computed in fp32; X (and XA, B) enter the bf16 matrix cores
  * rounded to bf16; accumulation is fp32.  ws must hold
  * qlora_fwd_workspace_bytes(M, in, out, r, act) bytes of device memory.
- * r = 0 gives a plain NF4 linear (A, B, XA may be NULL).  M = 0 is a no-op
+ * r = 0 gives a plain NF4 linear (A, B may be NULL).  M = 0 is a no-op
  * (ws may be NULL).
  */
 qlora_status qlora_linear_fwd(const qlora_nf4 *wq, const void *X, int64_t M,
@@ -281,7 +288,7 @@ qlora_status qlora_linear_bwd_adam(const qlora_nf4 *wq, const void *X, const voi
  * their input; gate and up too).  Only the few-token path: 1 <= M <= 16 and
  * r <= 64, the same M, r, act, adt and codebook for all n; linear l has its
  * own wq[l], X[l] [M, in_l], A[l], B[l], Y[l] [M, out_l] and XA[l] (as in
- * qlora_linear_fwd; X[l] may be shared).  Each workgroup belongs to one
+ * qlora_linear_fwd; X[l] may be shared; XA itself or any XA[l] may be NULL).  Each workgroup belongs to one
  * linear, so every output is bit-identical to qlora_linear_fwd of that
  * linear alone.  ws: qlora_fwd_group_workspace_bytes(n, M, in, out, r, act)
  * bytes (in, out: host arrays of the n shapes).  Other shapes or n outside
@@ -379,7 +386,9 @@ int qlora_codebook_thresholds(int codebook, float out[15]);
  * launch of a selected kind is bracketed by a pair of HIP events recorded on
  * the call's stream (mask 0 turns timing off).  qlora_timing_read
  * synchronizes those events and returns the summed duration (ms) and the
- * number of launches of one kind since the last reset.  Not thread-safe.
+ * number of launches of one kind since the last reset.  The mask is read
+ * atomically and the records are guarded by a lock, so these calls may run
+ * on any thread while other threads launch; the records are process-wide.
  */
 typedef enum {
   QLORA_KERNEL_QUANTIZE = 0,

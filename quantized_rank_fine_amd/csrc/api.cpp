@@ -7,9 +7,11 @@
 // dA = X^T (dY B^T) and dB = (X A)^T dY, so dW is never formed).
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -27,14 +29,32 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool dtype_ok(qlora_dtype d) { return d == QLORA_F32 || d == QLORA_BF16; }
 
+// Shapes every kernel can address.  The kernels reach memory through 32-bit
+// offsets from a per-workgroup (or per-array) base, and a buffer descriptor
+// spans at most 2^31 - 1 bytes.  With in, out <= 2^19 and in*out < 2^32
+// weights the packed codes stay below 2^31 bytes, the block-scale tables
+// below 2^28, and any 256 activation rows below 2^29 bytes; with at most
+// 2^24 tokens the per-call token-major arrays (bf16 XA^T copies, few-token
+// partials) stay inside the same range.  Larger shapes are rejected with
+// QLORA_ERR_SHAPE rather than addressed wrongly.
+constexpr int64_t kMaxDim = int64_t(1) << 19;
+constexpr int64_t kMaxWeights = (int64_t(1) << 32) - 4096;
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+
 bool shape_ok(int64_t in, int64_t out) {
-  const int64_t lim = int64_t(1) << 24;  // keeps every index product in int64
-  return in > 0 && out > 0 && in % 64 == 0 && out % 64 == 0 && in <= lim && out <= lim;
+  return in > 0 && out > 0 && in % 64 == 0 && out % 64 == 0 && in <= kMaxDim &&
+         out <= kMaxDim && in * out <= kMaxWeights;
 }
 
+bool tokens_ok(int64_t M) { return M >= 0 && M <= kMaxTokens; }
+
 // ---------------------------------------------------------------- timing
+// Optional instrumentation (off by default): the mask is read atomically on
+// every launch, and the recorded event pairs are guarded by a mutex, so
+// calls on several threads may run while timing is switched on or off.
 struct TimingState {
-  int mask = 0;
+  std::atomic<int> mask{0};
+  std::mutex mu;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[QLORA_KERNEL_COUNT];
   double total_ms[QLORA_KERNEL_COUNT] = {};
   int64_t launches[QLORA_KERNEL_COUNT] = {};
@@ -43,12 +63,17 @@ TimingState g_timing;
 
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F &&launch) {
-  if (!(g_timing.mask & (1 << kind))) return launch();
+  if (!(g_timing.mask.load(std::memory_order_relaxed) & (1 << kind))) return launch();
   hipEvent_t a = nullptr, b = nullptr;
-  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
+  if (hipEventCreate(&a) != hipSuccess) return launch();
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return launch();
+  }
   (void)hipEventRecord(a, s);
   hipError_t e = launch();
   (void)hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   g_timing.pending[kind].emplace_back(a, b);
   return e;
 }
@@ -103,7 +128,7 @@ FwdPlan plan_fwd(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
 // are per 256-token block, and the dY pass writes XA^T in bf16.
 bool db_in_dx(int64_t M, int64_t in, int64_t out, int32_t r, bool act_bf16) {
   return act_bf16 && r > 0 && r <= 16 && r % 4 == 0 && g_complete(M, out, r) &&
-         dx_fold_fits(M, in, out);
+         dx_fold_fits(M, in, out) && (M + 255) / 256 * out * r * 4 <= 0x7fffffff;
 }
 
 struct BwdPlan {
@@ -183,7 +208,7 @@ qlora_status linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int6
   const bool adam = ta.theta != nullptr;
   qlora_status st = check_nf4(wq);
   if (st != QLORA_OK) return st;
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!tokens_ok(M) || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
   if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
   const int64_t in = wq->in, out = wq->out;
   if (r > 0) {
@@ -338,13 +363,13 @@ const char *qlora_status_string(qlora_status s) {
 
 size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
                                  qlora_dtype act) {
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out) || !dtype_ok(act)) return 0;
+  if (!tokens_ok(M) || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out) || !dtype_ok(act)) return 0;
   return plan_fwd(M, in, out, r, act == QLORA_BF16).total;
 }
 
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
                                  qlora_dtype act) {
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out) || !dtype_ok(act)) return 0;
+  if (!tokens_ok(M) || r < 0 || r > QLORA_MAX_RANK || !shape_ok(in, out) || !dtype_ok(act)) return 0;
   return plan_bwd(M, in, out, r, act == QLORA_BF16).total;
 }
 
@@ -382,14 +407,14 @@ qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M
   if (!lora_mul(lora, mul)) return QLORA_ERR_VALUE;
   qlora_status st = check_nf4(wq);
   if (st != QLORA_OK) return st;
-  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!tokens_ok(M) || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
   if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
   if (M == 0) return QLORA_OK;
   if (!X || !Y || !ws) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(Y) || !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (r > 0) {
-    if (!A || !B || !XA) return QLORA_ERR_NULL;
-    if (!aligned16(A) || !aligned16(B) || !aligned16(XA)) return QLORA_ERR_ALIGN;
+    if (!A || !B) return QLORA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || (XA && !aligned16(XA))) return QLORA_ERR_ALIGN;
   }
   const bool xb = act == QLORA_BF16, ab = adt == QLORA_BF16;
   const int64_t in = wq->in, out = wq->out;
@@ -454,7 +479,7 @@ qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq, const
                                     void *const *Y, float *const *XA, void *ws, size_t ws_bytes,
                                     hipStream_t stream) {
   if (n < 1 || n > kSmallMaxGroup) return QLORA_ERR_SHAPE;
-  if (!wq || !X || !Y || (r > 0 && (!A || !B || !XA))) return QLORA_ERR_NULL;
+  if (!wq || !X || !Y || (r > 0 && (!A || !B))) return QLORA_ERR_NULL;
   if (M < 1 || M > kSmallMaxM || r < 0 || r > kSmallMaxR) return QLORA_ERR_SHAPE;
   if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
   SmallLinear lin[kSmallMaxGroup];
@@ -466,8 +491,9 @@ qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq, const
     if (!X[l] || !Y[l]) return QLORA_ERR_NULL;
     if (!aligned16(X[l]) || !aligned16(Y[l])) return QLORA_ERR_ALIGN;
     if (r > 0) {
-      if (!A[l] || !B[l] || !XA[l]) return QLORA_ERR_NULL;
-      if (!aligned16(A[l]) || !aligned16(B[l]) || !aligned16(XA[l])) return QLORA_ERR_ALIGN;
+      if (!A[l] || !B[l]) return QLORA_ERR_NULL;
+      if (!aligned16(A[l]) || !aligned16(B[l]) || (XA && XA[l] && !aligned16(XA[l])))
+        return QLORA_ERR_ALIGN;
     }
     const int64_t in = wq[l]->in, out = wq[l]->out;
     const FwdPlan p = plan_fwd(M, in, out, r, act == QLORA_BF16);
@@ -483,7 +509,7 @@ qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq, const
     L.Kc = p.kc;
     L.P = reinterpret_cast<float *>(static_cast<char *>(ws) + off + p.off_p);
     L.PXA = r > 0 ? reinterpret_cast<float *>(static_cast<char *>(ws) + off + p.off_pxa) : nullptr;
-    L.XA = r > 0 ? XA[l] : nullptr;
+    L.XA = r > 0 && XA ? XA[l] : nullptr;
     L.Y = Y[l];
     off += align_up(p.total);
   }
@@ -561,12 +587,13 @@ qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v
 }
 
 int qlora_timing_enable(int kind_mask) {
-  g_timing.mask = kind_mask & ((1 << QLORA_KERNEL_COUNT) - 1);
+  g_timing.mask.store(kind_mask & ((1 << QLORA_KERNEL_COUNT) - 1), std::memory_order_relaxed);
   return 0;
 }
 
 int qlora_timing_read(int kind, double *total_ms, int64_t *launches) {
   if (kind < 0 || kind >= QLORA_KERNEL_COUNT) return -1;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   for (auto &pr : g_timing.pending[kind]) {
     float ms = 0.0f;
     if (hipEventSynchronize(pr.second) != hipSuccess) return -2;
@@ -583,6 +610,7 @@ int qlora_timing_read(int kind, double *total_ms, int64_t *launches) {
 }
 
 void qlora_timing_reset(void) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
   for (int k = 0; k < QLORA_KERNEL_COUNT; ++k) {
     for (auto &pr : g_timing.pending[k]) {
       (void)hipEventSynchronize(pr.second);

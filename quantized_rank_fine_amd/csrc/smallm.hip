@@ -427,7 +427,7 @@ __device__ __forceinline__ void fwd_small_reduce_block(const SmallReduceArgs &ra
       for (int u = 0; u < 32; ++u) sx += xv[u];
     }
     xa[e / r][e % r] = rank_mul(mul, e / r, e % r, r, sx);
-    if (bx == 0) XA[e] = sx;
+    if (bx == 0 && XA) XA[e] = sx;
   }
   __syncthreads();
   if (!ok) return;

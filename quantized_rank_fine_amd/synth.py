@@ -96,8 +96,10 @@ def adapters(n_in, n_out, rank, workload, dtype, b_zero=False, layer=0, linear=0
 
 
 def p2_sample():
-    """The 262,144-weight sample of the "LLMs · QLoRA" reconstruction
-    experiment: torch CPU generator seeded with 0, N(0, 1) * 0.02, fp32."""
+    """The weight sample of the reconstruction experiment on "LLMs · QLoRA"
+    (NormalFloat section): 262,144 standard-normal draws from torch's CPU
+    generator started at seed 0, scaled to a standard deviation of 0.02, fp32."""
     import torch
-    torch.manual_seed(0)
-    return (torch.randn(4096 * 64) * 0.02).numpy().astype(np.float32)
+    gen = torch.Generator().manual_seed(0)
+    draws = torch.randn(64 * 4096, generator=gen, dtype=torch.float32).numpy()
+    return draws * np.float32(W_STD)

@@ -83,6 +83,8 @@ class Layer:
         self.codebook = codebook
         self.act, self.adt = act, adt
         self.w0 = synth.weights(n_in, n_out, workload, layer, linear) if w0 is None else w0
+        self._okey = (workload, n_in, n_out, layer, linear, codebook) if w0 is None else None
+        self._oq = None
         self.X = synth.activations(M, n_in, workload, act, layer, linear)
         self.dY = synth.activations(M, n_out, workload, act, layer, linear, tensor=synth.T_DY)
         if r > 0:
@@ -108,14 +110,14 @@ class Layer:
         self.wq = quantize_gpu(self.w0, codebook)
 
     # ---------------------------------------------------------------- runs
-    def fwd(self, lora=None):
+    def fwd(self, lora=None, save_xa=True):
         """lora: None, or (scale, dropout_p, keep) with keep a device uint8
         [M, r] tensor or None -- then the call goes through the options entry
-        point."""
+        point.  save_xa=False passes a NULL XA (not saved)."""
         torch, dev = torch_dev()
         M, r = self.M, self.r
         Y = torch.empty(M, self.n_out, dtype=self.tdt, device=dev)
-        XA = torch.empty(M, max(r, 1), dtype=torch.float32, device=dev) if r else None
+        XA = torch.empty(M, max(r, 1), dtype=torch.float32, device=dev) if r and save_xa else None
         wsb = q.qlora_fwd_workspace_bytes(M, self.n_in, self.n_out, r, self.qact)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
         if lora is None:
@@ -145,16 +147,38 @@ class Layer:
         return dX, dA, dB
 
     # -------------------------------------------------------------- oracle
+    def oracle_q(self):
+        """The oracle's quantization of this layer's W0 (cached per seeded
+        weight): codes, q8 and s2 computed on the CPU from the same input."""
+        if self._oq is None:
+            key = self._okey
+            if key is not None and key in _ORACLE_Q:
+                self._oq = _ORACLE_Q[key]
+            else:
+                self._oq = oracle.quantize(self.w0, levels_of(self.codebook))
+                if key is not None:
+                    _ORACLE_Q.clear()          # keep one large weight at a time
+                    _ORACLE_Q[key] = self._oq
+        return self._oq
+
     def w_hat(self):
-        c = self.wq.codes.cpu().numpy()
-        q8 = self.wq.qscale.cpu().numpy()
-        s2 = self.wq.gscale.cpu().numpy()
-        return oracle.dequantize(c, q8, s2, self.n_in, self.n_out, levels_of(self.codebook))
+        """deq(Q(W0)) in float64, from the oracle's own quantization of W0
+        (nothing read back from the device)."""
+        oq = self.oracle_q()
+        return oracle.dequantize(oq["packed"], oq["q8"], oq["s2"], self.n_in, self.n_out,
+                                 levels_of(self.codebook))
+
+    def codes_match_oracle(self):
+        """The device's packed codes, q8 and s2 against the oracle's."""
+        oq = self.oracle_q()
+        assert np.array_equal(self.wq.codes.cpu().numpy(), oq["packed"])
+        assert np.array_equal(self.wq.qscale.cpu().numpy(), oq["q8"])
+        assert np.array_equal(self.wq.gscale.cpu().numpy().view(np.uint32),
+                              oq["s2"].view(np.uint32))
 
     def ref(self, rows=None):
-        """Oracle forward/backward (float64) on the GPU's own quantized
-        weight (its codes are checked bit-exactly elsewhere).  With `rows`,
-        y and dX only for those rows."""
+        """Oracle forward/backward (float64) on the oracle's quantized weight.
+        With `rows`, y and dX only for those rows."""
         W = self.w_hat()
         X = self.X.values.astype(np.float64)
         dY = self.dY.values.astype(np.float64)
@@ -174,3 +198,8 @@ class Layer:
             out["dA"] = X.T @ G
             out["dB"] = XA.T @ dY
         return out
+
+
+# The oracle's quantization of the most recent seeded weight, keyed by
+# (workload, in, out, layer, linear, codebook).
+_ORACLE_Q = {}

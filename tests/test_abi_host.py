@@ -113,6 +113,47 @@ def test_workspace_sizes(L):
     assert q.qlora_bwd_workspace_bytes(64, 256, 256, 8, 5) == 0          # invalid dtype
 
 
+def test_addressable_shape_limits(L):
+    """Shapes past the kernels' 32-bit addressing are rejected up front: in
+    and out at most 2^19, in*out below 2^32 weights, at most 2^24 tokens;
+    the largest accepted ones get a workspace size."""
+    ok = lambda M, i, o: (q.qlora_fwd_workspace_bytes(M, i, o, 16, q.BF16) > 0 and
+                          q.qlora_bwd_workspace_bytes(M, i, o, 16, q.BF16) > 0)
+    assert ok(4096, 1 << 19, 4096)
+    assert ok(4096, 4096, 1 << 19)
+    assert ok(2048, 1 << 19, 8128)             # in*out = 2^32 - 2^25
+    assert not ok(4096, (1 << 19) + 64, 64)
+    assert not ok(4096, 64, (1 << 19) + 64)
+    assert not ok(4096, 1 << 19, 8192)         # in*out = 2^32
+    assert not ok(4096, 131072, 131072)
+    assert ok(1 << 24, 4096, 4096)
+    assert not ok((1 << 24) + 1, 4096, 4096)
+    big = _nf4(1 << 19, 8192)
+    assert L.qlora_quantize(P, ctypes.byref(big), None) == 2
+    assert L.qlora_linear_fwd(ctypes.byref(big), P, 64, q.BF16, P, P, 8, q.BF16, P, P, P,
+                              1 << 30, None) == 2
+    s = _nf4()
+    assert L.qlora_linear_fwd(ctypes.byref(s), P, (1 << 24) + 1, q.BF16, P, P, 8, q.BF16, P, P,
+                              P, 1 << 30, None) == 2
+    assert L.qlora_linear_bwd(ctypes.byref(s), P, P, (1 << 24) + 1, q.BF16, P, P, 8, q.BF16, P,
+                              P, P, P, P, 1 << 30, None) == 2
+
+
+def test_db_fold_planned_before_launch(L):
+    """Where dB is formed inside the dX GEMM (bf16 activations, r <= 16) the
+    plan also holds the bf16 XA^T copy; at a token count whose per-block dB
+    partials would pass 2^31 bytes the plan falls back to dB in the dY pass,
+    so no launch can be refused after an earlier one was queued.  Seen
+    through the workspace: fp32 activations never fold and differ from bf16
+    only by the bf16 copy of dY."""
+    al = lambda b: (b + 255) // 256 * 256
+    for (M, i, o, r, fold) in [(2048, 4096, 4096, 16, True), (1 << 24, 4096, 32768, 16, False)]:
+        b16 = q.qlora_bwd_workspace_bytes(M, i, o, r, q.BF16)
+        b32 = q.qlora_bwd_workspace_bytes(M, i, o, r, q.F32)
+        assert b16 > 0 and b32 > 0
+        assert (b32 - b16 == al(M * o * 2)) == (not fold), (M, o)
+
+
 def test_status_strings(L):
     for s in range(8):
         assert q.qlora_status_string(s) == q.STATUS[s]
@@ -159,7 +200,10 @@ def test_fwd_validation(L):
     assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, 9, P, P, P, ws, None) == 4
     assert f(ctypes.byref(s), None, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 1
     assert f(ctypes.byref(s), P, 64, q.BF16, None, P, 8, q.BF16, P, P, P, ws, None) == 1
-    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, None, P, ws, None) == 1
+    # XA (the saved activation) is optional: a NULL XA passes the pointer
+    # checks and is stopped here by the workspace size, before any launch
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, None, P, ws - 1, None) == 5
+    assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, U, P, ws, None) == 3
     assert f(ctypes.byref(s), U, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws, None) == 3
     assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, U, P, P, ws, None) == 3
     assert f(ctypes.byref(s), P, 64, q.BF16, P, P, 8, q.BF16, P, P, P, ws - 1, None) == 5

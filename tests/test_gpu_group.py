@@ -7,7 +7,9 @@ import pytest
 
 from quantized_rank_fine_amd import qlora as q
 
-from gpu_harness import Layer, say, torch_dev
+from quantized_rank_fine_amd import workloads
+
+from gpu_harness import TOL, Layer, out_to_f64, rel_err, say, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -39,3 +41,34 @@ def test_group_equals_single_calls(M, shapes, shared_x):
     for l, ((Y0, XA0), Y, XA) in enumerate(zip(ref, Ys, XAs)):
         assert np.array_equal(Y.float().cpu().numpy(), Y0.float().cpu().numpy()), l
         assert np.array_equal(XA.cpu().numpy(), XA0.cpu().numpy()), l
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("group", [("q", "k", "v"), ("gate", "up")])
+def test_group_7b_shapes_against_oracle(M, group):
+    """The grouped calls the decode measurement makes (q/k/v share X, gate/up
+    share X) at the 7B shapes, r = 16, bf16: every output against the
+    float64 oracle on the oracle's own quantization of each weight."""
+    torch, dev = torch_dev()
+    names = [l[0] for l in workloads.LLAMA7B_LINEARS]
+    shapes = [workloads.LLAMA7B_LINEARS[names.index(nm)][1:] for nm in group]
+    say(f"[group] 7b {group} M={M}")
+    r = 16
+    layers = [Layer(2, M, i, o, r, linear=names.index(nm)) for nm, (i, o) in zip(group, shapes)]
+    for L in layers[1:]:
+        L.tX, L.X = layers[0].tX, layers[0].X
+    Ys = [torch.empty((M, o), dtype=torch.bfloat16, device=dev) for (_, o) in shapes]
+    XAs = [torch.empty((M, r), dtype=torch.float32, device=dev) for _ in shapes]
+    wsb = q.qlora_fwd_group_workspace_bytes(M, [i for i, _ in shapes], [o for _, o in shapes], r)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    q.qlora_linear_fwd_group([L.wq for L in layers], [L.tX for L in layers], M, q.BF16,
+                             [L.tA for L in layers], [L.tB for L in layers], r, q.BF16,
+                             Ys, XAs, ws, wsb)
+    torch.cuda.synchronize()
+    for nm, L, Y, XA in zip(group, layers, Ys, XAs):
+        L.codes_match_oracle()
+        ref = L.ref()
+        ey = rel_err(out_to_f64(Y, "bf16"), ref["y"])
+        exa = rel_err(XA.cpu().numpy(), ref["XA"])
+        say(f"    {nm}: y {ey:.3g} XA {exa:.3g}")
+        assert ey <= TOL and exa <= TOL, nm

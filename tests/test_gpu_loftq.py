@@ -8,18 +8,15 @@ import oracle
 from quantized_rank_fine_amd import qlora as q
 from quantized_rank_fine_amd import synth
 
-from gpu_harness import bf16_to_f64, quantize_gpu, say, torch_dev
+from gpu_harness import bf16_to_f64, levels_of, quantize_gpu, say, torch_dev
 
 pytestmark = pytest.mark.gpu
 
 
-def _w_hat32(wq):
-    """deq(Wq) in fp32 as the library forms it (merge with rank 0)."""
-    torch, dev = torch_dev()
-    W = torch.empty(wq.n_in, wq.n_out, dtype=torch.float32, device=dev)
-    q.qlora_merge(wq, None, None, 0, q.F32, W, q.F32)
-    torch.cuda.synchronize()
-    return W
+def _w_hat(w0, codebook=q.CB_NF4):
+    """deq(Q(W0)) in float64 from the oracle's own quantization of W0."""
+    oq = oracle.quantize(w0, levels_of(codebook))
+    return oracle.dequantize(oq["packed"], oq["q8"], oq["s2"], *w0.shape, levels_of(codebook))
 
 
 def _init(W0, wq, k, r, iters, adt="f32", seed=0):
@@ -37,16 +34,17 @@ def _init(W0, wq, k, r, iters, adt="f32", seed=0):
 
 
 def test_low_rank_residual_is_recovered():
-    """W0 = deq(Wq) + P with P of rank 4: the residual is P (to fp32
-    rounding) and A B recovers it."""
+    """W0 = fp32(deq(Wq)) + P with P of rank 4: the residual is P (up to
+    the fp32 rounding of the dequantized weight) and A B recovers it."""
     torch, dev = torch_dev()
-    wq = quantize_gpu(synth.weights(256, 384, workload=7))
-    W_hat = _w_hat32(wq)
+    w0 = synth.weights(256, 384, workload=7)
+    wq = quantize_gpu(w0)
+    W_hat = _w_hat(w0)
     g = np.random.default_rng(51)
     P = (g.standard_normal((256, 4)) @ g.standard_normal((4, 384)) * 0.01).astype(np.float32)
-    W0 = W_hat + torch.from_numpy(P).to(dev)
-    R = (W0 - W_hat).cpu().numpy().astype(np.float64)      # the exact fp32 residual
-    A, B = _init(W0, wq, 12, 4, 2)
+    W0 = (W_hat.astype(np.float32) + P).astype(np.float32)
+    R = W0.astype(np.float64) - W_hat
+    A, B = _init(torch.from_numpy(W0).to(dev), wq, 12, 4, 2)
     AB = A.cpu().numpy().astype(np.float64) @ B.cpu().numpy().astype(np.float64)
     assert np.abs(AB - R).max() <= 1e-4 * np.abs(R).max()
 
@@ -58,7 +56,7 @@ def test_quantization_residual_near_optimal(codebook):
     torch, dev = torch_dev()
     w0 = synth.weights(512, 768, workload=7)
     wq = quantize_gpu(w0, codebook)
-    W_hat = _w_hat32(wq).cpu().numpy().astype(np.float64)
+    W_hat = _w_hat(w0, codebook)
     R = oracle.residual(w0, W_hat)
     say(f"[loftq] 512x768 codebook={codebook}")
     A, B = _init(torch.from_numpy(w0).to(dev), wq, 24, 16, 3)

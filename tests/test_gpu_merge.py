@@ -56,6 +56,11 @@ def _ref(L):
     (256, 320, 0, "bf16", "f32"),         # rank 0: the dequantized weight
     (384, 576, 24, "bf16", "f32"),        # matrix cores: half-empty last 16-rank step, ragged tile
     (448, 640, 8, "bf16", "bf16"),        # matrix cores: one half-filled rank step
+    (384, 576, 16, "f32", "f32"),         # fp32 adapters on fp32 matrix cores: both lane halves
+    (384, 576, 16, "f32", "bf16"),        # the same, bf16 out, ragged last column tile
+    (384, 576, 24, "f32", "bf16"),        # fp32 adapters: a full and a half-filled rank step
+    (384, 576, 64, "f32", "f32"),         # fp32 adapters: four rank steps
+    (384, 576, 64, "f32", "bf16"),
 ])
 def test_merge_parity(n_in, n_out, r, adt, wdt):
     say(f"[merge] {n_in}x{n_out} r={r} adt={adt} wdt={wdt}")
@@ -105,22 +110,30 @@ def test_merged_weight_reproduces_the_forward():
 
 @pytest.mark.parametrize("codebook", [q.CB_NF4, q.CB_UNIFORM4])
 def test_requantize_merged_weight(codebook):
-    """The fp32 merged weight goes back through qlora_quantize: codes and
-    scales bit-exact against the oracle's quantizer on the same matrix; with
-    B = 0 the codes and block scales come back unchanged."""
+    """Merge, then quantize again.  The device's fp32 merged weight is within
+    fp32 rounding of the oracle's merge; the oracle's merged weight, rounded
+    to fp32, goes through qlora_quantize with codes and scales bit-exact
+    against the oracle's quantizer on the same matrix; with B = 0 the merged
+    weight is deq(Wq) and re-quantizing it gives back the oracle's original
+    codes and block scales."""
     torch, dev = torch_dev()
+    levels = levels_of(codebook)
     for b_zero in (False, True):
         L = Layer(21, 64, 256, 512, 16, b_zero=b_zero, codebook=codebook)
         W = _merge(L, "f32")
+        ref64 = _ref(L)
+        assert rel_err(W.cpu().numpy(), ref64) <= 1e-6
+        ref32 = ref64.astype(np.float32)
         wq2 = q.NF4Weight(256, 512, dev, codebook)
-        q.qlora_quantize(W, wq2)
+        q.qlora_quantize(torch.from_numpy(ref32).to(dev), wq2)
         torch.cuda.synchronize()
-        ref = oracle.quantize(W.cpu().numpy(), levels_of(codebook))
-        assert np.array_equal(wq2.codes.cpu().numpy(), ref["packed"])
-        assert np.array_equal(wq2.qscale.cpu().numpy(), ref["q8"])
+        oq = oracle.quantize(ref32, levels)
+        assert np.array_equal(wq2.codes.cpu().numpy(), oq["packed"])
+        assert np.array_equal(wq2.qscale.cpu().numpy(), oq["q8"])
         if b_zero:
-            assert np.array_equal(wq2.codes.cpu().numpy(), L.wq.codes.cpu().numpy())
-            assert np.array_equal(wq2.qscale.cpu().numpy(), L.wq.qscale.cpu().numpy())
+            o1 = L.oracle_q()
+            assert np.array_equal(oq["packed"], o1["packed"])
+            assert np.array_equal(oq["q8"], o1["q8"])
 
 
 def test_merge_uniform4():

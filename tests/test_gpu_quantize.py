@@ -91,8 +91,10 @@ def test_quantize_near_thresholds():
     """Weights whose quotient w / absmax lands within a few ulp of every
     decision threshold, for many random block scales: exercises the exact
     fp32 division of the kernel."""
-    from quantized_rank_fine_amd import qlora as q
-    T = np.array(q.qlora_thresholds(), np.float32)
+    # the decision points of the oracle's level table (its fp32 thresholds
+    # lie within an ulp of these midpoints)
+    L = oracle.nf4_levels().astype(np.float64)
+    T = (0.5 * (L[1:] + L[:-1])).astype(np.float32)
     g = np.random.default_rng(5)
     nblk = 4096
     c = (np.abs(g.standard_normal(nblk)) * 0.05 + 1e-3).astype(np.float32)
@@ -120,12 +122,14 @@ def test_quantize_7b_shapes(name, n_in, n_out):
     _check_full(synth.weights(n_in, n_out, workload=3, linear=5), f"7b {name}")
 
 
-@pytest.mark.parametrize("name,n_in,n_out", [("q", 8192, 8192), ("down", 22016, 8192)])
+@pytest.mark.parametrize("name,n_in,n_out", [("q", 8192, 8192), ("up", 8192, 22016),
+                                             ("down", 22016, 8192)])
 def test_quantize_65b_shapes_sampled(name, n_in, n_out):
     """Full-size 65B-style linears: compare 64 sampled double-quantization
     groups (each group depends on its own 16384 weights only)."""
     say(f"[quantize] 65b {name} {n_in}x{n_out}")
-    w0 = synth.weights(n_in, n_out, workload=4, layer=79, linear=6 if name == "down" else 0)
+    li = [l[0] for l in workloads.LLAMA65B_LINEARS].index(name)
+    w0 = synth.weights(n_in, n_out, workload=4, layer=79, linear=li)
     wq = quantize_gpu(w0)
     codes = wq.codes.cpu().numpy()
     q8 = wq.qscale.cpu().numpy()

@@ -80,6 +80,22 @@ def _backward_dB_from_A(X, dY, W, A=None, B=None, XA=None):
     return g
 
 
+def _quantize_against_dq_scale(w0, levels=None):
+    """Mistake: the codes taken against the double-quantized scale
+    q_b * s2_g instead of the block's exact absmax."""
+    w = np.ascontiguousarray(w0, np.float32).reshape(-1)
+    c = onf4.block_absmax(w)
+    q8, s2 = onf4.double_quantize(c)
+    c_hat = (q8.astype(np.float32) * np.repeat(s2, 256)[:q8.size]).astype(np.float32)
+    codes = onf4.encode(w, c_hat, levels)
+    return {"codes": codes, "packed": onf4.pack_codes(codes), "absmax": c, "q8": q8, "s2": s2}
+
+
+def test_codes_against_dq_scale_are_caught():
+    with pytest.raises(AssertionError):
+        pins.check_quantize_scale_rule(_quantize_against_dq_scale)
+
+
 def test_ties_high_is_caught():
     with pytest.raises(AssertionError):
         pins.check_encode_rules(_encode_ties_high)
