@@ -30,6 +30,12 @@ on X.A; `merge`
 times folding the adapters into a dense bf16 weight (HBM-bound); `adam`
 times one optimizer step of A and B; `loftq_init` times the start of A and B
 from the quantization residual.
+`cfg0` times the 256 x 256 fp32 step (no roofline claim); `cfg3` times the
+fwd+bwd of a 7B-style block's seven linears at r = 64, M = 4096 and their
+quantize; `cfg4` quantizes 80 layers of 65B-style linears streamed through a
+double-buffered fp32 source and times one such layer's fwd+bwd at r = 64,
+M = 8192.  Each carries the oracle's time on the host cores beside it
+(bounded samples, extrapolated where stated).
 """
 
 import argparse
@@ -67,6 +73,13 @@ def parse():
                    help="distinct 7B layer sets cycled by the decode measurement")
     p.add_argument("--copy-calibrate", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the 256^2, 7B-block and 65B-layer reports")
+    p.add_argument("--only", choices=["cfg1", "cfg3", "cfg4", "decode"],
+                   help="run only this workload's GPU steps (for profiler runs); prints its "
+                        "report without the oracle timings")
+    p.add_argument("--cfg4-layers", type=int, default=80,
+                   help="65B-style layers quantized in the cfg4 report")
     return p.parse_args()
 
 
@@ -113,23 +126,21 @@ def copy_calibrate():
 
 def cpu_baseline(w0, X, dY, A, B, min_seconds):
     """The oracle, as it stands, on the same workload: full quantize of W0
-    (fp32 numpy, one thread) and full forward+backward of all tokens
-    (dequantize + float64 BLAS matmuls), repeated until `min_seconds` of CPU
-    work have been timed (at most 50 repetitions)."""
+    (its fp32 NumPy quantizer, run on a pool of worker processes over whole
+    double-quantization groups) and full forward+backward of all tokens
+    (dequantize + float64 BLAS matmuls on all threads), repeated until
+    `min_seconds` of CPU work have been timed (at most 50 repetitions)."""
     import oracle
     from quantized_rank_fine_amd import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        blas = os.cpu_count()
+    blas = blas_threads()
+    procs = pool_workers()
     n_in, n_out = w0.shape
     M, r = X.shape[0], A.shape[1]
     tq = tf = 0.0
     reps = 0
     while (tq + tf) < min_seconds and reps < 50:
         t0 = time.perf_counter()
-        qd = oracle.quantize(w0)
+        qd, _ = pool_quantize(w0, procs)
         t1 = time.perf_counter()
         W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], n_in, n_out)
         XA, y = oracle.forward(X, W, A, B)
@@ -144,12 +155,15 @@ def cpu_baseline(w0, X, dY, A, B, min_seconds):
     return {
         "value": round(reps * flops / tf / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(blas),
+        "cores": int(max(blas, procs)),
         "kind": "oracle",
         "sample": (f"the full step {reps} time(s): quantize of the 4096x4096 W0 in fp32 numpy "
-                   f"(1 thread, {tq / reps:.2f} s each) and fwd+bwd of all {M} tokens "
-                   f"(dequantize + float64 BLAS on {blas} threads, {tf / reps:.2f} s each)"),
+                   f"({procs} processes over whole scale groups, {tq / reps:.2f} s each) and "
+                   f"fwd+bwd of all {M} tokens (dequantize + float64 BLAS on {blas} threads, "
+                   f"{tf / reps:.2f} s each)"),
         "quantize_GBps": round(reps * qbytes / tq / 1e9, 4),
+        "quantize_processes": procs,
+        "blas_threads": int(blas),
         "host_cpu_count": os.cpu_count(),
     }
 
@@ -277,6 +291,417 @@ def decode_report(sets, reps=5):
                       "each one qlora_linear_fwd_group call", **res}
 
 
+def pool_workers():
+    """Worker processes for the oracle's quantizer: the host's cores, at most
+    16 (the share of one GPU's host on the measurement boxes)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+_POOL_W = None
+
+
+def _pool_quantize_chunk(bounds):
+    import oracle
+    a, b = bounds
+    return oracle.quantize(_POOL_W[a:b])
+
+
+def pool_quantize(w0, procs):
+    """The oracle's quantize of w0, run on `procs` worker processes, each on
+    a run of whole double-quantization groups (16,384 consecutive weights:
+    every output of a group depends on that group alone), the parts
+    concatenated in order.  Returns (result dict, processes used)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    global _POOL_W
+    flat = np.ascontiguousarray(w0, np.float32).reshape(-1)
+    grp = 64 * 256
+    ng = (flat.size + grp - 1) // grp
+    procs = max(1, min(procs, ng))
+    cuts = [min(flat.size, (ng * i // procs) * grp) for i in range(procs + 1)]
+    _POOL_W = flat
+    try:
+        with mp.get_context("fork").Pool(procs) as pool:
+            parts = pool.map(_pool_quantize_chunk, list(zip(cuts[:-1], cuts[1:])))
+    finally:
+        _POOL_W = None
+    out = {k: np.concatenate([p_[k] for p_ in parts]) for k in parts[0]}
+    return out, procs
+
+
+def _dev_inputs(lins, R, M, dev, seed):
+    """Device-drawn inputs of a set of linears (torch generator, seeded per
+    linear): W0 ~ N(0, 0.02^2) fp32, A ~ N(0,1)/sqrt(in), B ~ N(0, 0.01^2)
+    (bf16), and one X [M, in] / dY [M, out] ~ N(0, 1) bf16 per distinct size."""
+    import math
+    import torch
+    g = torch.Generator(device=dev)
+    W0, A, B = [], [], []
+    for li, (_, n_in, n_out) in enumerate(lins):
+        g.manual_seed(seed * 1000 + li)
+        W0.append(torch.randn(n_in, n_out, device=dev, generator=g) * 0.02)
+        A.append((torch.randn(n_in, R, device=dev, generator=g) / math.sqrt(n_in)).to(torch.bfloat16))
+        B.append((torch.randn(R, n_out, device=dev, generator=g) * 0.01).to(torch.bfloat16))
+    X, dY = {}, {}
+    g.manual_seed(seed * 1000 + 999)
+    for (_, n_in, n_out) in lins:
+        if n_in not in X:
+            X[n_in] = torch.randn(M, n_in, device=dev, generator=g).to(torch.bfloat16)
+        if n_out not in dY:
+            dY[n_out] = torch.randn(M, n_out, device=dev, generator=g).to(torch.bfloat16)
+    return W0, A, B, X, dY
+
+
+def block_fwd_bwd(lins, wqs, A, B, X, dY, R, M, K, warmup, dev):
+    """Forward of every linear of a block, then the backward of every linear
+    in reverse order (each with its saved XA), K timed steps after `warmup`
+    untimed ones; then the same K steps once more with the library's
+    per-launch events on the two fused GEMMs.  Returns the step time and the
+    GEMM kernel totals."""
+    import torch
+    from quantized_rank_fine_amd import qlora as q, workloads
+    n = len(lins)
+    Y = {o: torch.empty(M, o, dtype=torch.bfloat16, device=dev) for (_, _, o) in lins}
+    dX = {i: torch.empty(M, i, dtype=torch.bfloat16, device=dev) for (_, i, _) in lins}
+    XA = [torch.empty(M, R, dtype=torch.float32, device=dev) for _ in range(n)]
+    dA = [torch.empty(i, R, dtype=torch.float32, device=dev) for (_, i, _) in lins]
+    dB = [torch.empty(R, o, dtype=torch.float32, device=dev) for (_, _, o) in lins]
+    fwb = max(q.qlora_fwd_workspace_bytes(M, i, o, R, q.BF16) for (_, i, o) in lins)
+    bwb = max(q.qlora_bwd_workspace_bytes(M, i, o, R, q.BF16) for (_, i, o) in lins)
+    wsf = torch.empty(fwb, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bwb, dtype=torch.uint8, device=dev)
+
+    def step():
+        for li, (_, i, o) in enumerate(lins):
+            q.qlora_linear_fwd(wqs[li], X[i], M, q.BF16, A[li], B[li], R, q.BF16, Y[o], XA[li],
+                               wsf, fwb)
+        for li in reversed(range(n)):
+            _, i, o = lins[li]
+            q.qlora_linear_bwd(wqs[li], X[i], dY[o], M, q.BF16, A[li], B[li], R, q.BF16, XA[li],
+                               dX[i], dA[li], dB[li], wsb, bwb)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    q.qlora_timing_reset()
+    q.qlora_timing_enable(["fwd_gemm", "dx_gemm"])
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    q.qlora_timing_disable()
+    flops = sum(workloads.fwd_flops(M, i, o, R) + workloads.bwd_flops(M, i, o, R)
+                for (_, i, o) in lins)
+    gemm = {}
+    for name in ("fwd_gemm", "dx_gemm"):
+        tot, cnt = q.qlora_timing_read(q.KERNELS.index(name))
+        if name == "fwd_gemm":
+            fl = sum(2 * M * o * (i + R) for (_, i, o) in lins)
+        else:
+            fl = sum(2 * M * i * (o + R) for (_, i, o) in lins)
+        gemm[name] = {"launches": cnt, "ms_per_step": round(tot / K, 4),
+                      "TFLOPs": round(K * fl / (tot * 1e-3) / 1e12, 2),
+                      "frac_bf16_peak": round(K * fl / (tot * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del wsf, wsb
+    return ms, flops, gemm
+
+
+def time_quantize_set(W0s, wqs, K):
+    """Quantize every weight of a set, K times (the set's fp32 source is
+    larger than the 256 MB Infinity Cache, so it streams from HBM)."""
+    import torch
+    from quantized_rank_fine_amd import qlora as q
+    for w, wq in zip(W0s, wqs):
+        q.qlora_quantize(w, wq)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        for w, wq in zip(W0s, wqs):
+            q.qlora_quantize(w, wq)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def cfg0_report(K):
+    """The 256 x 256, r = 8, M = 64 fp32 step (quantize, fwd, bwd, B drawn
+    N(0, 0.01^2)): time only, launch-bound, no roofline claim."""
+    import numpy as np
+    import torch
+    from quantized_rank_fine_amd import qlora as q, synth, workloads
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[0]
+    _, n_in, n_out = wl["linears"][0]
+    r, M = wl["rank"], wl["tokens"][0]
+    w0 = torch.from_numpy(synth.weights(n_in, n_out, 0)).to(dev)
+    X = torch.from_numpy(synth.activations(M, n_in, 0, "f32").raw).to(dev)
+    dY = torch.from_numpy(synth.activations(M, n_out, 0, "f32", tensor=synth.T_DY).raw).to(dev)
+    As, Bs = synth.adapters(n_in, n_out, r, 0, "f32")
+    A, B = torch.from_numpy(As.raw).to(dev), torch.from_numpy(Bs.raw).to(dev)
+    wq = q.NF4Weight(n_in, n_out, dev)
+    Y = torch.empty(M, n_out, device=dev)
+    XA = torch.empty(M, r, device=dev)
+    dX = torch.empty(M, n_in, device=dev)
+    dA = torch.empty(n_in, r, device=dev)
+    dB = torch.empty(r, n_out, device=dev)
+    fwb = q.qlora_fwd_workspace_bytes(M, n_in, n_out, r, q.F32)
+    bwb = q.qlora_bwd_workspace_bytes(M, n_in, n_out, r, q.F32)
+    wsf = torch.empty(fwb, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bwb, dtype=torch.uint8, device=dev)
+
+    def step():
+        q.qlora_quantize(w0, wq)
+        q.qlora_linear_fwd(wq, X, M, q.F32, A, B, r, q.F32, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd(wq, X, dY, M, q.F32, A, B, r, q.F32, XA, dX, dA, dB, wsb, bwb)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+    return {"workload": wl["name"], "step": "quantize+fwd+bwd, fp32",
+            "us_per_step_median": round(us[len(us) // 2], 2),
+            "us_per_step_p10": round(us[len(us) // 10], 2),
+            "us_per_step_p90": round(us[(9 * len(us)) // 10], 2),
+            "note": "correctness configuration: launch-bound, no roofline claim"}
+
+
+def cfg0_oracle():
+    import oracle
+    from quantized_rank_fine_amd import synth
+    w0 = synth.weights(256, 256, 0)
+    X = synth.activations(64, 256, 0, "f32").values
+    dY = synth.activations(64, 256, 0, "f32", tensor=synth.T_DY).values
+    As, Bs = synth.adapters(256, 256, 8, 0, "f32")
+    reps, t0 = 0, time.perf_counter()
+    while reps < 5 or time.perf_counter() - t0 < 0.5:
+        qd = oracle.quantize(w0)
+        W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], 256, 256)
+        XA, _ = oracle.forward(X, W, As.values, Bs.values)
+        oracle.backward(X, dY, W, As.values, Bs.values, XA)
+        reps += 1
+    return {"us_per_step": round((time.perf_counter() - t0) * 1e6 / reps, 1), "kind": "oracle",
+            "cores": 1, "sample": f"the full step, {reps} times"}
+
+
+def cfg3_report(K, warmup):
+    """A 7B-style block's seven linears (q, k, v, o 4096^2; gate, up 4096 x
+    11008; down 11008 x 4096) at r = 64, M = 4096 tokens, bf16: quantize of
+    the set (913.9 MB) and fwd+bwd of every linear."""
+    import torch
+    from quantized_rank_fine_amd import qlora as q, workloads
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[3]
+    lins, R, M = wl["linears"], wl["rank"], wl["tokens"][0]
+    W0, A, B, X, dY = _dev_inputs(lins, R, M, dev, seed=3)
+    wqs = [q.NF4Weight(i, o, dev) for (_, i, o) in lins]
+    q_ms = time_quantize_set(W0, wqs, K)
+    qbytes = sum(workloads.quantize_bytes(i, o) for (_, i, o) in lins)
+    del W0
+    ms, flops, gemm = block_fwd_bwd(lins, wqs, A, B, X, dY, R, M, K, warmup, dev)
+    tf = flops / (ms * 1e-3) / 1e12
+    qg = qbytes / (q_ms * 1e-3) / 1e9
+    return {"workload": wl["name"], "fwd_bwd_ms_per_step": round(ms, 4),
+            "fwd_bwd_flop": flops, "fwd_bwd_TFLOPs": round(tf, 2),
+            "fwd_bwd_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "gemm_kernels": gemm,
+            "quantize_ms": round(q_ms, 4), "quantize_bytes": qbytes,
+            "quantize_GBps": round(qg, 1), "quantize_frac_hbm": round(qg / PEAK_HBM_GBPS, 4)}
+
+
+def cfg4_report(layers, K, warmup):
+    """65B-style shapes (q, k, v, o 8192^2; gate, up 8192 x 22016; down
+    22016 x 8192): `layers` layers quantized from fp32 sources drawn on the
+    device one layer at a time into two alternating buffers (the 4-bit
+    weights of every layer stay resident: 33.4 GB at 80 layers); then the
+    fwd+bwd of one layer's seven linears at r = 64, M = 8192, bf16."""
+    import torch
+    from quantized_rank_fine_amd import qlora as q, workloads
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[4]
+    lins, R, M = wl["linears"], wl["rank"], wl["tokens"][0]
+    nf4 = [[q.NF4Weight(i, o, dev) for (_, i, o) in lins] for _ in range(layers)]
+    src = [[torch.empty(i, o, dtype=torch.float32, device=dev) for (_, i, o) in lins]
+           for _ in range(2)]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one untimed layer first (kernel load, clocks)
+    for li, w in enumerate(src[1]):
+        g.manual_seed(4_000_000 + li)
+        w.normal_(0.0, 0.02, generator=g)
+        q.qlora_quantize(w, nf4[0][li])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    q_ms = 0.0
+    for layer in range(layers):
+        buf = src[layer % 2]
+        for li, w in enumerate(buf):
+            g.manual_seed(4_000_000 + 1000 * layer + li)
+            w.normal_(0.0, 0.02, generator=g)
+        flush.fill_(layer & 0xFF)           # evict the fresh source from the Infinity Cache
+        e0.record()
+        for li, w in enumerate(buf):
+            q.qlora_quantize(w, nf4[layer][li])
+        e1.record()
+        torch.cuda.synchronize()
+        q_ms += e0.elapsed_time(e1)
+    wall = time.perf_counter() - t_wall
+    del src, flush
+    qbytes = layers * sum(workloads.quantize_bytes(i, o) for (_, i, o) in lins)
+    nf4_bytes = layers * sum(workloads.nf4_bytes(i, o) for (_, i, o) in lins)
+    qg = qbytes / (q_ms * 1e-3) / 1e9
+    # one layer's fwd+bwd (its own adapters and activations)
+    import math
+    gg = torch.Generator(device=dev)
+    A, B, X, dY = [], [], {}, {}
+    for li, (_, i, o) in enumerate(lins):
+        gg.manual_seed(4_100_000 + li)
+        A.append((torch.randn(i, R, device=dev, generator=gg) / math.sqrt(i)).to(torch.bfloat16))
+        B.append((torch.randn(R, o, device=dev, generator=gg) * 0.01).to(torch.bfloat16))
+        if i not in X:
+            X[i] = torch.randn(M, i, device=dev, generator=gg).to(torch.bfloat16)
+        if o not in dY:
+            dY[o] = torch.randn(M, o, device=dev, generator=gg).to(torch.bfloat16)
+    ms, flops, gemm = block_fwd_bwd(lins, nf4[0], A, B, X, dY, R, M, K, warmup, dev)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": wl["name"], "layers_quantized": layers,
+            "quantize_ms": round(q_ms, 3), "quantize_bytes": qbytes,
+            "quantize_GBps": round(qg, 1), "quantize_frac_hbm": round(qg / PEAK_HBM_GBPS, 4),
+            "nf4_resident_GB": round(nf4_bytes / 1e9, 3),
+            "quantize_wall_s_incl_source_generation": round(wall, 2),
+            "layer_fwd_bwd_ms": round(ms, 3), "layer_fwd_bwd_flop": flops,
+            "layer_fwd_bwd_TFLOPs": round(tf, 2),
+            "layer_fwd_bwd_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "gemm_kernels": gemm}
+
+
+def _oracle_linear_step(n_in, n_out, M, r, workload, li, procs, quantize=True, fwd_bwd=True):
+    """Seconds of the oracle's quantize (on `procs` processes) and of its
+    dequantize + float64 fwd+bwd for one linear."""
+    import oracle
+    from quantized_rank_fine_amd import synth
+    w0 = synth.weights(n_in, n_out, workload, linear=li)
+    t0 = time.perf_counter()
+    qd, _ = pool_quantize(w0, procs)
+    tq = time.perf_counter() - t0
+    tf = 0.0
+    if fwd_bwd:
+        X = synth.activations(M, n_in, workload, "bf16", linear=li).values
+        dY = synth.activations(M, n_out, workload, "bf16", linear=li, tensor=synth.T_DY).values
+        As, Bs = synth.adapters(n_in, n_out, r, workload, "bf16", linear=li)
+        t0 = time.perf_counter()
+        W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], n_in, n_out)
+        t1 = time.perf_counter()
+        XA, _ = oracle.forward(X, W, As.values, Bs.values)
+        oracle.backward(X, dY, W, As.values, Bs.values, XA)
+        tf = (t1 - t0, time.perf_counter() - t1)
+    return tq, tf, qd
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count()
+
+
+def cfg3_oracle():
+    """The oracle on the 7B block: one linear of each distinct shape (q for
+    the four 4096^2, gate for the two 4096 x 11008, down), counted with its
+    multiplicity: quantize on a process pool, fwd+bwd of all 4096 tokens in
+    float64 BLAS."""
+    from quantized_rank_fine_amd import workloads
+    procs = pool_workers()
+    shapes = [("q", 4096, 4096, 4), ("gate", 4096, 11008, 2), ("down", 11008, 4096, 1)]
+    tq = tf = 0.0
+    for name, i, o, mult in shapes:
+        li = [l[0] for l in workloads.LLAMA7B_LINEARS].index(name)
+        a, b, _ = _oracle_linear_step(i, o, 4096, 64, 3, li, procs)
+        tq += mult * a
+        tf += mult * sum(b)
+    flops = sum(workloads.fwd_flops(4096, i, o, 64) + workloads.bwd_flops(4096, i, o, 64)
+                for (_, i, o) in workloads.LLAMA7B_LINEARS)
+    qbytes = sum(workloads.quantize_bytes(i, o) for (_, i, o) in workloads.LLAMA7B_LINEARS)
+    return {"kind": "oracle", "cores": max(procs, blas_threads()),
+            "quantize_processes": procs, "blas_threads": blas_threads(),
+            "fwd_bwd_s": round(tf, 3), "fwd_bwd_TFLOPs": round(flops / tf / 1e12, 4),
+            "quantize_s": round(tq, 3), "quantize_GBps": round(qbytes / tq / 1e9, 4),
+            "sample": "one linear of each distinct shape (q, gate, down) timed once, counted "
+                      "4, 2 and 1 times"}
+
+
+def cfg2_oracle():
+    """The oracle's decode forward of one 7B layer set at M = 1: dequantize
+    each weight in float64 and multiply (one linear of each distinct shape,
+    counted with multiplicity)."""
+    import oracle
+    from quantized_rank_fine_amd import synth, workloads
+    procs = pool_workers()
+    shapes = [("q", 4096, 4096, 4), ("gate", 4096, 11008, 2), ("down", 11008, 4096, 1)]
+    t = 0.0
+    for name, i, o, mult in shapes:
+        li = [l[0] for l in workloads.LLAMA7B_LINEARS].index(name)
+        _, _, qd = _oracle_linear_step(i, o, 1, 16, 2, li, procs, fwd_bwd=False)
+        X = synth.activations(1, i, 2, "bf16", linear=li).values
+        As, Bs = synth.adapters(i, o, 16, 2, "bf16", linear=li)
+        t0 = time.perf_counter()
+        W = oracle.dequantize(qd["packed"], qd["q8"], qd["s2"], i, o)
+        oracle.forward(X, W, As.values, Bs.values)
+        t += mult * (time.perf_counter() - t0)
+    nbytes = sum(workloads.nf4_bytes(i, o) + i * 2 + (i * 16 + 16 * o) * 2 + o * 2
+                 for (_, i, o) in workloads.LLAMA7B_LINEARS)
+    return {"kind": "oracle", "cores": blas_threads(), "us_per_layer_set_M1": round(t * 1e6, 1),
+            "GBps": round(nbytes / t / 1e9, 4),
+            "sample": "dequantize + forward of one linear of each distinct shape at M = 1, "
+                      "counted 4, 2 and 1 times"}
+
+
+def cfg4_oracle():
+    """The oracle on 65B shapes, extrapolated from bounded samples: quantize
+    of 1024 rows of a q weight (8.4 M weights, process pool) scaled to the
+    80 layers' 64.76e9 weights; fwd+bwd of that 8192^2 linear at M = 256,
+    r = 64 scaled by flops to one layer at M = 8192."""
+    from quantized_rank_fine_amd import synth, workloads
+    import oracle
+    procs = pool_workers()
+    lins = workloads.LLAMA65B_LINEARS
+    w = synth.weights(1024, 8192, 4)
+    t0 = time.perf_counter()
+    pool_quantize(w, procs)
+    tq = time.perf_counter() - t0
+    weights = 80 * sum(i * o for (_, i, o) in lins)
+    qbytes = 80 * sum(workloads.quantize_bytes(i, o) for (_, i, o) in lins)
+    tq_all = tq * weights / w.size
+    _, (t_deq, t_mm), _ = _oracle_linear_step(8192, 8192, 256, 64, 4, 0, procs)
+    f_sample = workloads.fwd_flops(256, 8192, 8192, 64) + workloads.bwd_flops(256, 8192, 8192, 64)
+    f_layer = sum(workloads.fwd_flops(8192, i, o, 64) + workloads.bwd_flops(8192, i, o, 64)
+                  for (_, i, o) in lins)
+    layer_w = sum(i * o for (_, i, o) in lins)
+    t_layer = t_deq * layer_w / (8192 * 8192) + t_mm * f_layer / f_sample
+    return {"kind": "oracle", "cores": max(procs, blas_threads()), "extrapolated": True,
+            "quantize_80_layers_s": round(tq_all, 1), "quantize_GBps": round(qbytes / tq_all / 1e9, 4),
+            "layer_fwd_bwd_s": round(t_layer, 2),
+            "fwd_bwd_TFLOPs": round(f_layer / t_layer / 1e12, 4),
+            "sample": "quantize of 1024 x 8192 weights scaled by weight count to 80 layers; "
+                      "one 8192^2 linear at M = 256: its dequantization scaled by weight count "
+                      "and its float64 products by flops to one layer at M = 8192"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,6 +718,17 @@ def main():
 
     from quantized_rank_fine_amd import qlora as q
     from quantized_rank_fine_amd import synth, workloads
+
+    if args.only in ("cfg3", "cfg4", "decode"):
+        torch.cuda.set_device(0)
+        if args.only == "cfg3":
+            rep = cfg3_report(args.steps, args.warmup)
+        elif args.only == "cfg4":
+            rep = cfg4_report(args.cfg4_layers, args.steps, args.warmup)
+        else:
+            rep = decode_report(args.decode_sets)
+        print(json.dumps({"only": args.only, args.only: rep}))
+        return
 
     wl = workloads.WORKLOADS[1]
     _, n_in, n_out = wl["linears"][0]
@@ -352,6 +788,11 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    if args.only == "cfg1":
+        # profiler runs: the K timed steps only
+        print(json.dumps({"only": "cfg1", "ms_per_step": round((t1 - t0) * 1e3 / K, 4)}))
+        return
 
     # Per-launch kernel times for the roofline: the same K steps once more,
     # with the library's HIP events around each launch of the timed kernels
@@ -587,9 +1028,23 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = decode_report(args.decode_sets)
+    del W0s, wsf, wsb
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        out["cfg0"] = cfg0_report(max(K, 20))
+        out["cfg3"] = cfg3_report(max(3, K // 4), 2)
+        torch.cuda.empty_cache()
+        out["cfg4"] = cfg4_report(args.cfg4_layers, 3, 1)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w0_host[0], Xs.values, dYs.values, As.values,
                                            Bs.values, args.cpu_seconds)
+        if not args.no_configs:
+            out["cfg0"]["oracle"] = cfg0_oracle()
+            out["cfg3"]["oracle"] = cfg3_oracle()
+            out["cfg4"]["oracle"] = cfg4_oracle()
+        if not args.no_decode:
+            out["decode"]["oracle"] = cfg2_oracle()
     print(json.dumps(out))
 
 
