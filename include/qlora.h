@@ -176,6 +176,24 @@ size_t qlora_fwd_workspace_bytes(int64_t M, int64_t in, int64_t out, int32_t r,
                                  qlora_dtype act);
 
 /*
+ * qlora_linear_fwd_noalloc: qlora_linear_fwd without a workspace argument,
+ * for callers that cannot allocate device memory at the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and output bits as qlora_linear_fwd.  Its scratch
+ * is a device-resident array of QLORA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; the call allocates
+ * nothing.  A shape whose qlora_fwd_workspace_bytes exceeds that size is
+ * refused with QLORA_ERR_WORKSPACE before anything touches the device.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two threads) race and must be serialized by the caller.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4 *wq, const void *X, int64_t M,
+                                      qlora_dtype act, const void *A, const void *B,
+                                      int32_t r, qlora_dtype adt, void *Y, float *XA,
+                                      hipStream_t stream);
+
+/*
  * qlora_linear_bwd: with G = dY.B^T,
  *   dX = dY.deq(Wq)^T + G.A^T   (act dtype, [M, in]; NULL skips dX)
  *   dA = X^T.G                  (fp32, [in, r])

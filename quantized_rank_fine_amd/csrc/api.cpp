@@ -460,6 +460,24 @@ qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M
 #undef QLORA_RUN
 }
 
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4 *wq, const void *X, int64_t M,
+                                     qlora_dtype act, const void *A, const void *B, int32_t r,
+                                     qlora_dtype adt, void *Y, float *XA, hipStream_t stream) {
+  // The size check comes before the scratch lookup, so an oversized call
+  // touches nothing on the device.
+  qlora_status st = check_nf4(wq);
+  if (st != QLORA_OK) return st;
+  if (!tokens_ok(M) || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!dtype_ok(act) || !dtype_ok(adt)) return QLORA_ERR_DTYPE;
+  if (M == 0) return QLORA_OK;
+  if (plan_fwd(M, wq->in, wq->out, r, act == QLORA_BF16).total > kNoAllocScratchBytes)
+    return QLORA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return QLORA_ERR_DEVICE;
+  return qlora_linear_fwd_lora(wq, X, M, act, A, B, r, adt, nullptr, Y, XA, ws,
+                               kNoAllocScratchBytes, stream);
+}
+
 size_t qlora_fwd_group_workspace_bytes(int32_t n, int64_t M, const int64_t *in,
                                        const int64_t *out, int32_t r, qlora_dtype act) {
   if (n < 1 || n > kSmallMaxGroup || !in || !out || M < 1 || M > kSmallMaxM || r < 0 ||

@@ -236,4 +236,10 @@ inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 
+// Size of the device-resident scratch array of the forward that allocates
+// nothing, and the device address of the current device's copy (looked up
+// once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace qlora

@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "qlora.h")
 
 F32, BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20      # QLORA_NOALLOC_SCRATCH_BYTES
 CB_NF4, CB_UNIFORM4, CB_INT4, CB_INT3, CB_TERNARY = 0, 1, 2, 3, 4   # qlora_codebook
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "pointer not 16-byte aligned",
           4: "invalid dtype", 5: "workspace too small", 6: "HIP runtime error",
@@ -69,6 +70,9 @@ def lib():
     L.qlora_quantize.argtypes = [vp, pnf4, vp]
     L.qlora_linear_fwd.argtypes = [pnf4, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp, vp,
                                    vp, sz, vp]
+    L.qlora_linear_fwd_noalloc.argtypes = [pnf4, vp, i64, ctypes.c_int, vp, vp, i32,
+                                           ctypes.c_int, vp, vp, vp]
+    L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
     L.qlora_linear_bwd.argtypes = [pnf4, vp, vp, i64, ctypes.c_int, vp, vp, i32, ctypes.c_int, vp,
                                    vp, vp, vp, vp, sz, vp]
     plora = ctypes.POINTER(qlora_lora)
@@ -226,6 +230,15 @@ def qlora_linear_fwd(wq, X, M, act, A, B, r, adt, Y, XA, ws, ws_bytes, stream=No
     _check(lib().qlora_linear_fwd(ctypes.byref(s), _ptr(X), int(M), int(act), _ptr(A), _ptr(B),
                                   int(r), int(adt), _ptr(Y), _ptr(XA), _ptr(ws), int(ws_bytes),
                                   _stream(stream)), "qlora_linear_fwd")
+
+
+def qlora_linear_fwd_noalloc(wq, X, M, act, A, B, r, adt, Y, XA, stream=None):
+    """qlora_linear_fwd with the library's device-resident scratch (no
+    workspace argument; nothing is allocated)."""
+    s = wq.struct() if isinstance(wq, NF4Weight) else wq
+    _check(lib().qlora_linear_fwd_noalloc(ctypes.byref(s), _ptr(X), int(M), int(act), _ptr(A),
+                                          _ptr(B), int(r), int(adt), _ptr(Y), _ptr(XA),
+                                          _stream(stream)), "qlora_linear_fwd_noalloc")
 
 
 def qlora_linear_bwd(wq, X, dY, M, act, A, B, r, adt, XA, dX, dA, dB, ws, ws_bytes,

@@ -431,3 +431,21 @@ def test_fp64_reciprocal_product_rounds_like_fp32_division():
         y = 1.0 / c.astype(np.float64)
         mine = (ww.astype(np.float64) * y).astype(np.float32)
         assert np.array_equal(exact.view(np.uint32), mine.view(np.uint32))
+
+
+def test_noalloc_forward_validation(L):
+    """The forward that allocates nothing refuses a shape whose workspace
+    exceeds its device-resident array before any HIP call (so this runs
+    without a GPU), and validates like qlora_linear_fwd."""
+    import re
+    text = open(q.HEADER).read()
+    m = re.search(r"#define QLORA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == q.NOALLOC_SCRATCH_BYTES
+    f = L.qlora_linear_fwd_noalloc
+    s = _nf4(4096, 256)
+    assert q.qlora_fwd_workspace_bytes(8192, 4096, 256, 16, q.F32) > q.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(s), P, 8192, q.F32, P, P, 16, q.F32, P, P, None) == 5
+    assert f(ctypes.byref(s), P, 0, q.BF16, P, P, 16, q.BF16, P, P, None) == 0
+    assert f(ctypes.byref(s), P, -1, q.BF16, P, P, 16, q.BF16, P, P, None) == 2
+    assert f(ctypes.byref(_nf4(256, 100)), P, 64, q.BF16, P, P, 8, q.BF16, P, P, None) == 2
+    assert f(ctypes.byref(s), P, 64, 9, P, P, 8, q.BF16, P, P, None) == 4
