@@ -14,7 +14,9 @@ What it computes (plain, slow, obviously correct):
   the symmetric integer grids (4, 3 bits and ternary) of the QLoRA lab.
 * ``nf4``     -- blockwise absmax (64 weights per block), nearest-level
   encoding, two-codes-per-byte packing, double quantization of the block
-  scales to int8 with one fp32 scale per 256 blocks, and dequantization.
+  scales to int8 with one fp32 scale per 256 blocks, and dequantization;
+  the lab's variant with one fp32 scale per 16 entries and no double
+  quantization.
   The encoding runs in fp32 because its decision rule is an fp32 argmin;
   dequantization is exact in float64.
 * ``linear``  -- forward y = X.deq(Wq) + (X.A).B and the backward
@@ -43,6 +45,10 @@ from .nf4 import (
     quantize,
     dequantize,
     storage_bits_per_weight,
+    LAB_GROUP,
+    quantize_groups,
+    dequantize_groups,
+    group_storage_bits_per_weight,
 )
 from .linear import (
     forward,
@@ -73,6 +79,10 @@ __all__ = [
     "quantize",
     "dequantize",
     "storage_bits_per_weight",
+    "LAB_GROUP",
+    "quantize_groups",
+    "dequantize_groups",
+    "group_storage_bits_per_weight",
     "forward",
     "backward",
     "merge",

@@ -41,20 +41,21 @@ def block_absmax(w_flat):
     return np.abs(w).max(axis=1)
 
 
-def encode(w_flat, c, levels=None):
+def encode(w_flat, c, levels=None, block=BLOCK):
     """4-bit codes: argmin_i fp32(|fp32(w / c_b) - L_i|), first minimum wins.
 
-    ``w_flat`` fp32 [n], ``c`` fp32 [n/64]; returns uint8 [n] in 0..15.
+    ``w_flat`` fp32 [n], ``c`` fp32 [n/block] (one scale per ``block``
+    consecutive weights); returns uint8 [n] in 0..15.
     A table in sign-magnitude order (the integer grids) holds zero twice,
     -0 then +0, one value: there the tie goes by the sign of x (x > 0 takes
     +0), so that the codes rise with x.  The NF4 and uniform tables have no
     zero entry.
     """
     L = nf4_levels() if levels is None else np.asarray(levels, np.float32)
-    w = np.asarray(w_flat, dtype=np.float32).reshape(-1, BLOCK)
+    w = np.asarray(w_flat, dtype=np.float32).reshape(-1, block)
     c = np.asarray(c, dtype=np.float32).reshape(-1, 1)
     out = np.empty(w.shape, dtype=np.uint8)
-    rows_per_chunk = max(1, _CHUNK // BLOCK)
+    rows_per_chunk = max(1, _CHUNK // block)
     for r0 in range(0, w.shape[0], rows_per_chunk):
         wb = w[r0:r0 + rows_per_chunk]
         cb = c[r0:r0 + rows_per_chunk]
@@ -130,6 +131,45 @@ def dequantize(packed, q8, s2, n_in, n_out, levels=None):
     scale_block = q * np.repeat(s, GROUP)[:q.size]
     w = L[codes].reshape(-1, BLOCK) * scale_block[:, None]
     return w.reshape(n_in, n_out)
+
+
+# --------------------------------------------------------------------------
+# The lab's quantizer ("QLoRA (low-rank adapters on a quantized model)", "The
+# code, line by line" and its Simplifications paragraph): symmetric uniform
+# integers with one scale per 16 consecutive entries of the flattened
+# (in, out) matrix, and no double quantization.  Reading: the scale of a
+# group is its absmax c_g (fp32, exact), the level set is k/h for |k| <= h
+# (h = 7, 3, 1 for 4, 3 and 2 bits; "2-bit" is ternary), and a weight's
+# code is the nearest level of fp32(w / c_g) with the rule of ``encode``;
+# the dequantized weight is L[code] * c_g.  Any 16-entry level table works
+# the same way.
+
+LAB_GROUP = 16
+
+
+def quantize_groups(w0, levels, group=LAB_GROUP):
+    """Per-group quantize of an (in, out) fp32 matrix: returns ``codes``
+    (uint8 [n]), ``packed`` (uint8 [n/2]) and ``scales`` (fp32 [n/group],
+    group g = flat entries group*g .. group*g + group - 1)."""
+    w = np.ascontiguousarray(w0, dtype=np.float32).reshape(-1)
+    if w.size % group:
+        raise ValueError("number of weights must be a multiple of the group size")
+    c = np.abs(w.reshape(-1, group)).max(axis=1)
+    codes = encode(w, c, levels, block=group)
+    return {"codes": codes, "packed": pack_codes(codes), "scales": c}
+
+
+def dequantize_groups(packed, scales, n_in, n_out, levels, group=LAB_GROUP):
+    """w_hat = L[code] * c_g in float64, shape (in, out)."""
+    L = np.asarray(levels, np.float32).astype(np.float64)
+    codes = unpack_codes(packed)
+    c = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return (L[codes].reshape(-1, group) * c[:, None]).reshape(n_in, n_out)
+
+
+def group_storage_bits_per_weight(group=LAB_GROUP):
+    """4-bit code + one fp32 scale per group."""
+    return 4.0 + 32.0 / group
 
 
 def storage_bits_per_weight():

@@ -285,6 +285,59 @@ def test_quantize_scale_rule():
 
 
 # --------------------------------------------------------------------------
+# the lab's quantizer: symmetric integers, one scale per 16 flat entries
+
+
+def check_group_quantizer(quantize_groups):
+    """"QLoRA (low-rank adapters on a quantized model)", "The code, line by
+    line": symmetric uniform integers, one scale per 16 consecutive entries of
+    the flattened (in, out) matrix, no double quantization.
+
+    (i) Layout: a 16 x 16 matrix whose 16 flat groups (its rows) each hold multiples
+    m/h of their own power-of-two scale 2^(g - 8), one entry at +-scale: the
+    scales come back exactly, every code is its multiple's index, and the
+    dequantized matrix is the input.  (ii) Rounding: on random groups the
+    dequantized weight is rint(h * w / c_g) / h * c_g with c_g the group's
+    own absmax, computed here with a plain loop over the groups."""
+    for h in (7, 3, 1):
+        L = oracle.int_levels(h)
+        n_in, n_out = 16, 16
+        w = np.zeros(n_in * n_out, np.float32)
+        want_codes = np.zeros(w.size, np.int64)
+        g_rng = np.random.default_rng(h)
+        for g in range(w.size // 16):
+            sc = np.float32(2.0 ** (g - 8))
+            m = g_rng.integers(-h, h + 1, 16)
+            m[g % 16] = h if g % 2 == 0 else -h                     # the group's absmax
+            m[m == 0] = 1                                          # no zeros: unambiguous codes
+            w[16 * g:16 * g + 16] = (m / h * sc).astype(np.float32)
+            want_codes[16 * g:16 * g + 16] = np.where(m > 0, 8 + m, 7 + m)
+        qd = quantize_groups(w.reshape(n_in, n_out), L)
+        assert qd["scales"].dtype == np.float32 and qd["scales"].size == w.size // 16
+        assert np.array_equal(qd["scales"], np.float32(2.0) ** np.arange(-8, w.size // 16 - 8,
+                                                                          dtype=np.float32))
+        assert np.array_equal(qd["codes"].astype(np.int64), want_codes)
+        W = oracle.dequantize_groups(qd["packed"], qd["scales"], n_in, n_out, L)
+        assert np.array_equal(W, w.reshape(n_in, n_out).astype(np.float64))
+        # (ii) random groups against the closed form
+        x = g_rng.standard_normal(16 * 300).astype(np.float32) * np.float32(0.02)
+        qd = quantize_groups(x.reshape(-1, 64), L)
+        W = oracle.dequantize_groups(qd["packed"], qd["scales"], x.size // 64, 64, L).reshape(-1)
+        for g in range(x.size // 16):
+            grp = x[16 * g:16 * g + 16].astype(np.float64)
+            c = max(abs(v) for v in grp)
+            k = np.rint(h * grp / c)
+            keep = np.abs(np.abs(h * grp / c) - np.floor(np.abs(h * grp / c)) - 0.5) > 1e-4
+            got = W[16 * g:16 * g + 16]
+            assert np.allclose(got[keep], (k / h * c)[keep], rtol=1e-6, atol=0), (h, g)
+
+
+def test_group_quantizer():
+    check_group_quantizer(oracle.quantize_groups)
+    assert oracle.group_storage_bits_per_weight() == 6.0
+
+
+# --------------------------------------------------------------------------
 # double quantization and storage
 
 

@@ -91,6 +91,33 @@ def _quantize_against_dq_scale(w0, levels=None):
     return {"codes": codes, "packed": onf4.pack_codes(codes), "absmax": c, "q8": q8, "s2": s2}
 
 
+def _groups_of_64(w0, levels, group=16):
+    """Mistake: one scale per 64 entries (the NF4 block) instead of 16."""
+    q = onf4.quantize_groups(w0, levels, group=64)
+    return {**q, "scales": np.repeat(q["scales"], 4)}
+
+
+def _groups_down_columns(w0, levels, group=16):
+    """Mistake: groups of 16 consecutive rows of a column, not of the
+    flattened (in, out) matrix."""
+    w = np.ascontiguousarray(w0, np.float32)
+    q = onf4.quantize_groups(w.T.copy(), levels, group)
+    codes = q["codes"].reshape(w.shape[1], w.shape[0]).T.reshape(-1)
+    scales = np.repeat(q["scales"].reshape(w.shape[1], w.shape[0] // group), group, axis=1)
+    scales = scales.T.reshape(-1)[::group]
+    return {"codes": codes, "packed": onf4.pack_codes(codes), "scales": scales}
+
+
+def test_wrong_group_size_is_caught():
+    with pytest.raises(AssertionError):
+        pins.check_group_quantizer(_groups_of_64)
+
+
+def test_groups_down_columns_are_caught():
+    with pytest.raises(AssertionError):
+        pins.check_group_quantizer(_groups_down_columns)
+
+
 def test_codes_against_dq_scale_are_caught():
     with pytest.raises(AssertionError):
         pins.check_quantize_scale_rule(_quantize_against_dq_scale)
