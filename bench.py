@@ -820,6 +820,23 @@ def main():
         evu[i][2].record()
     torch.cuda.synchronize()
 
+    # The lab's 16-entry format (symmetric INT4 levels, one fp32 scale per 16
+    # entries, no double quantization): the same K steps.
+    wq_g = q.NF4Weight(n_in, n_out, dev, q.CB_INT4, q.LAB_GROUP)
+    for i in range(args.warmup):
+        q.qlora_quantize(W0s[i % N_W0], wq_g)
+        q.qlora_linear_fwd(wq_g, X, M, q.BF16, A, B, r, q.BF16, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd(wq_g, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
+    evg = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        evg[i][0].record()
+        q.qlora_quantize(W0s[i % N_W0], wq_g)
+        evg[i][1].record()
+        q.qlora_linear_fwd(wq_g, X, M, q.BF16, A, B, r, q.BF16, Y, XA, wsf, fwb)
+        q.qlora_linear_bwd(wq_g, X, dY, M, q.BF16, A, B, r, q.BF16, XA, dX, dA, dB, wsb, bwb)
+        evg[i][2].record()
+    torch.cuda.synchronize()
+
     # The adapter options (alpha/r = 2, dropout p = 0.05 on X.A with a fixed
     # seeded keep mask): the same K fwd+bwd steps through the options entry
     # points.
@@ -970,6 +987,18 @@ def main():
                 "fwd_bwd_ms_per_step": round(ufb_ms / K, 4),
                 "quantize_ms_per_step": round(uq_ms / K, 4)}
 
+    gq_ms = sum(e[0].elapsed_time(e[1]) for e in evg)
+    gfb_ms = sum(e[1].elapsed_time(e[2]) for e in evg)
+    nw_ = n_in * n_out
+    g16_bytes = 4 * nw_ + nw_ // 2 + 4 * (nw_ // 16)
+    group16 = {"format": "symmetric INT4 levels k/7, one fp32 absmax per 16 entries, "
+                         "no double quantization",
+               "fwd_bwd_TFLOPs": round(K * flops / (gfb_ms * 1e-3) / 1e12, 2),
+               "fwd_bwd_ms_per_step": round(gfb_ms / K, 4),
+               "quantize_bytes": g16_bytes,
+               "quantize_GBps": round(K * g16_bytes / (gq_ms * 1e-3) / 1e9, 1),
+               "quantize_ms_per_step": round(gq_ms / K, 4)}
+
     lora = {"what": "fwd+bwd with alpha/r = 2 and dropout p = 0.05 on X.A (keep mask given)",
             "fwd_bwd_TFLOPs": round(flops / (lora_ms * 1e-3) / 1e12, 2),
             "fwd_bwd_ms_per_step": round(lora_ms, 4)}
@@ -1021,6 +1050,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "uniform4": uniform4,
+        "group16": group16,
         "lora_options": lora,
         "merge": merge,
         "adam": adam,

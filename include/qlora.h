@@ -110,14 +110,28 @@ typedef enum {
  *   codes  [n/2]  uint8   byte j holds the 4-bit code of element 2j in its
  *                         low nibble and of element 2j+1 in its high nibble;
  *                         code i selects level L_i of the 16-entry table.
- *   qscale [n/64] int8    block b (elements 64b..64b+63) scale q_b in
- *                         [0, 127].
- *   gscale [ceil(n/64/256)] fp32  group g (blocks 256g..256g+255) scale s2_g.
  *   codebook              a qlora_codebook value: the level table L (zero,
  *                         as in a zero-initialised struct, is NF4).
- * Dequantized weight: w_hat = L[code] * (q_b * s2_g).
+ *   block                 the scale format:
+ *     0 or QLORA_BLOCK (64): absmax blocks of 64 weights, scales quantized
+ *       again ("What QLoRA adds"):
+ *         qscale [n/64] int8   block b (elements 64b..64b+63) scale q_b in
+ *                              [0, 127];
+ *         gscale [ceil(n/64/256)] fp32  group g (blocks 256g..256g+255)
+ *                              scale s2_g;
+ *       w_hat = L[code] * (q_b * s2_g).
+ *     QLORA_LAB_GROUP (16): the lab's quantizer ("QLoRA (low-rank adapters
+ *       on a quantized model)", "The code, line by line" and its
+ *       Simplifications: one scale per 16 consecutive entries of the
+ *       flattened (in, out) matrix, no double quantization):
+ *         gscale [n/16] fp32   group g (elements 16g..16g+15) absmax c_g;
+ *         qscale unused (may be NULL);
+ *       w_hat = L[code] * c_g.  With QLORA_CB_INT4 / INT3 / TERNARY this is
+ *       the lab's symmetric integer grid; any codebook may be used.
  * Requires in % 64 == 0 and out % 64 == 0, so blocks never straddle rows.
+ * qlora_loftq_init takes the 64-weight format only.
  */
+#define QLORA_LAB_GROUP 16
 typedef struct {
   int64_t in;
   int64_t out;
@@ -125,9 +139,12 @@ typedef struct {
   int8_t *qscale;
   float *gscale;
   int32_t codebook;
+  int32_t block;
 } qlora_nf4;
 
-/* Number of bytes of each part of a qlora_nf4 of shape (in, out). */
+/* Number of bytes of each part of a qlora_nf4 of shape (in, out) in the
+ * 64-weight format (the 16-entry format: codes as here, in*out/16 fp32
+ * scales in gscale, no qscale). */
 static inline size_t qlora_codes_bytes(int64_t in, int64_t out) {
   return (size_t)(in * out / 2);
 }
@@ -148,6 +165,9 @@ static inline size_t qlora_gscale_count(int64_t in, int64_t out) {
  * c_b = 0 encodes as x = 0 (code 7).  Double quantization ("What QLoRA
  * adds"): s2_g = fp32(max_b c_b) / 127, q_b = round_half_even(c_b / s2_g) in
  * fp32; an all-zero group has s2_g = 0 and q_b = 0.  Codes use the exact c_b.
+ * With wq->block == 16: c_g = max |w| over each 16 consecutive weights, the
+ * same encoding with c_g in place of c_b, and c_g stored in gscale (no
+ * double quantization).
  */
 qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t stream);
 

@@ -173,12 +173,18 @@ T *at(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
+// The 16-entry scale format (one fp32 absmax per 16 weights, no double
+// quantization); block 0 or 64 is the double-quantized 64-weight format.
+bool g16(const qlora_nf4 *wq) { return wq->block == QLORA_LAB_GROUP; }
+
 qlora_status check_nf4(const qlora_nf4 *wq) {
   if (!wq) return QLORA_ERR_NULL;
   if (!shape_ok(wq->in, wq->out)) return QLORA_ERR_SHAPE;
   if (wq->codebook < 0 || wq->codebook >= kCodebooks) return QLORA_ERR_DTYPE;
-  if (!wq->codes || !wq->qscale || !wq->gscale) return QLORA_ERR_NULL;
-  if (!aligned16(wq->codes) || !aligned16(wq->qscale) || !aligned16(wq->gscale))
+  if (wq->block != 0 && wq->block != QLORA_BLOCK && wq->block != QLORA_LAB_GROUP)
+    return QLORA_ERR_DTYPE;
+  if (!wq->codes || !wq->gscale || (!g16(wq) && !wq->qscale)) return QLORA_ERR_NULL;
+  if (!aligned16(wq->codes) || !aligned16(wq->gscale) || (!g16(wq) && !aligned16(wq->qscale)))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
@@ -278,10 +284,11 @@ qlora_status linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int6
   }
   QLORA_RUN(QLORA_KERNEL_DY_PASS, launch_bwd_dy(dY, xb, B, ab, XAd, M, out, r, gpart, G16, p.rp,
                                                 dbpart, xat, p.ldm, wq->qscale, wq->gscale, in,
-                                                cs, stream, mul));
+                                                g16(wq) ? nullptr : cs, stream, mul));
   auto dx_gemm = [&](const uint16_t *xt, float *dbp) {
-    return launch_dx_gemm(wq->codes, cs, in, out, dY16, M, G16, int32_t(p.rp), A, ab, r, dX, xb,
-                          wq->codebook, xt, p.ldm, dbp, stream);
+    return launch_dx_gemm(wq->codes, g16(wq) ? wq->gscale : cs, in, out, dY16, M, G16,
+                          int32_t(p.rp), A, ab, r, dX, xb, wq->codebook, g16(wq), xt, p.ldm,
+                          dbp, stream);
   };
   if (r == 0) {
     if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
@@ -380,7 +387,8 @@ qlora_status qlora_quantize(const float *W0, const qlora_nf4 *wq, hipStream_t st
   if (!aligned16(W0)) return QLORA_ERR_ALIGN;
   const int64_t nblocks = wq->in * wq->out / 64;
   return dev(timed(QLORA_KERNEL_QUANTIZE, stream, [&] {
-    return launch_quantize(W0, wq->codes, wq->qscale, wq->gscale, nblocks, wq->codebook, stream);
+    return launch_quantize(W0, wq->codes, wq->qscale, wq->gscale, nblocks, wq->codebook, g16(wq),
+                           stream);
   }));
 }
 
@@ -431,7 +439,7 @@ qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M
     float *PXA = r > 0 ? at<float>(ws, p.off_pxa) : nullptr;
     QLORA_RUN(QLORA_KERNEL_FWD_SMALLM,
               launch_fwd_small_partial(wq->codes, wq->qscale, wq->gscale, in, out, X, xb, M, A,
-                                       ab, r, p.kc, P, PXA, wq->codebook, stream));
+                                       ab, r, p.kc, P, PXA, wq->codebook, g16(wq), stream));
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_fwd_small_reduce(P, PXA, p.ks, M, out, r, B, ab, XA,
                                                            Y, xb, stream, mul));
     return QLORA_OK;
@@ -447,15 +455,16 @@ qlora_status qlora_linear_fwd_lora(const qlora_nf4 *wq, const void *X, int64_t M
   float *part = p.ks > 0 ? at<float>(ws, p.off_part) : nullptr;
   uint16_t *XA16 = r > 0 ? at<uint16_t>(ws, p.off_xa16) : nullptr;
   QLORA_RUN(QLORA_KERNEL_XA, launch_fwd_prep(X, xb, A, ab, M, in, r, part, XA, XA16, p.rp,
-                                             wq->qscale, wq->gscale, out, cs, stream, mul));
+                                             wq->qscale, wq->gscale, out,
+                                             g16(wq) ? nullptr : cs, stream, mul));
   if (p.ks > 0) {
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(part, p.ks, M, r, XA, false, XA16, p.rp,
                                                   nullptr, 0, 0, nullptr, false, nullptr, 0,
                                                   stream, mul));
   }
   QLORA_RUN(QLORA_KERNEL_FWD_GEMM,
-            launch_fwd_gemm(wq->codes, cs, in, out, X16, M, XA16, int32_t(p.rp), B, ab, r, Y, xb,
-                            wq->codebook, stream));
+            launch_fwd_gemm(wq->codes, g16(wq) ? wq->gscale : cs, in, out, X16, M, XA16,
+                            int32_t(p.rp), B, ab, r, Y, xb, wq->codebook, g16(wq), stream));
   return QLORA_OK;
 #undef QLORA_RUN
 }
@@ -505,7 +514,7 @@ qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq, const
   for (int l = 0; l < n; ++l) {
     qlora_status st = check_nf4(wq[l]);
     if (st != QLORA_OK) return st;
-    if (wq[l]->codebook != wq[0]->codebook) return QLORA_ERR_DTYPE;
+    if (wq[l]->codebook != wq[0]->codebook || g16(wq[l]) != g16(wq[0])) return QLORA_ERR_DTYPE;
     if (!X[l] || !Y[l]) return QLORA_ERR_NULL;
     if (!aligned16(X[l]) || !aligned16(Y[l])) return QLORA_ERR_ALIGN;
     if (r > 0) {
@@ -536,7 +545,7 @@ qlora_status qlora_linear_fwd_group(int32_t n, const qlora_nf4 *const *wq, const
   if (ws_bytes < off) return QLORA_ERR_WORKSPACE;
   return dev(timed(QLORA_KERNEL_FWD_SMALLM, stream, [&] {
     return launch_fwd_small_group(n, lin, M, act == QLORA_BF16, adt == QLORA_BF16, r,
-                                  wq[0]->codebook, stream);
+                                  wq[0]->codebook, g16(wq[0]), stream);
   }));
 }
 
@@ -584,7 +593,8 @@ qlora_status qlora_merge(const qlora_nf4 *wq, const void *A, const void *B, int3
     if (!aligned16(A) || !aligned16(B)) return QLORA_ERR_ALIGN;
   }
   return dev(launch_merge(wq->codes, wq->qscale, wq->gscale, wq->in, wq->out, A, B,
-                          adt == QLORA_BF16, r, W, wdt == QLORA_BF16, wq->codebook, stream));
+                          adt == QLORA_BF16, r, W, wdt == QLORA_BF16, wq->codebook, g16(wq),
+                          stream));
 }
 
 qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v, int64_t n,

@@ -58,19 +58,28 @@ constexpr int kThreads = 256;
 constexpr int kStages = 4;
 constexpr int kXBytes = BM * BK * 2;     // 32 KiB activation tile
 constexpr int kCBytes = 4096;            // code tile
-constexpr int kSBytes = 1024;            // scales (512 B used)
-constexpr int kStageBytes = kXBytes + kCBytes + kSBytes;
-constexpr int kRingBytes = kStages * kStageBytes;  // 148 KiB
-// Forward: per-wavefront expansion scratch after the ring, 16 k rows x 64
-// columns of bf16 with a 176-B (44-dword) row pitch: the expansion's 16-B
-// writes hit every LDS bank exactly 4 times per instruction (the minimum) and
-// the transposed reads at most 3 times (minimum 2).
-constexpr int kXPitch = 88;                          // elements
-constexpr int kScratchBytes = 16 * kXPitch * 2;      // 2816 B per wavefront
-constexpr int kLdsBytes = kRingBytes + 4 * kScratchBytes;   // 159 KiB
-static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 constexpr uint32_t kBufFlags = 0x00020000u;
-constexpr int kLoadsPerTile = 10;        // per wavefront: 8 X + 1 code + 1 scale
+
+// LDS geometry per scale format.  64-weight blocks (kG16 = false): one fp32
+// scale per (64-column block, row) -- 512 B of a 1-KiB slot per stage; the
+// forward's per-wavefront expansion scratch holds 16 k rows x 64 columns of
+// bf16 with a 176-B (44-dword) row pitch: the expansion's 16-B writes hit
+// every LDS bank exactly 4 times per instruction (the minimum) and the
+// transposed reads at most 3 times (minimum 2).  16-entry groups (kG16 =
+// true): one fp32 scale per (16-column group, row) -- 2 KiB per stage, paid
+// for with an unpadded scratch pitch, so the workgroup takes all 160 KiB.
+template <bool kG16>
+struct Geo {
+  static constexpr int kSBytes = kG16 ? 2048 : 1024;
+  static constexpr int kStageBytes = kXBytes + kCBytes + kSBytes;
+  static constexpr int kRingBytes = kStages * kStageBytes;
+  static constexpr int kXPitch = kG16 ? 64 : 88;                 // elements
+  static constexpr int kScratchBytes = 16 * kXPitch * 2;        // per wavefront
+  static constexpr int kLdsBytes = kRingBytes + 4 * kScratchBytes;
+  // loads per wavefront and tile: 8 X + 1 code + the scale loads
+  static constexpr int kLoadsPerTile = kG16 ? 11 : 10;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+};
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
@@ -174,6 +183,7 @@ __device__ __forceinline__ u32x4_t expand8_table(uint32_t d, const ScaledTable &
 // receives column cb + (l & 31), rows 8 (l >> 5) .. +7 -- one lane of a
 // v_mfma_f32_32x32x16 B operand -- from two ds_read_b64_tr_b16 (each: 16
 // lanes x 4 rows -> 4 columns).
+template <int kXPitch>
 __device__ __forceinline__ u32x4_t lds_col8_32(const char *T, int cb) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
   const int q = i16 & 3, tq = i16 >> 2;
@@ -287,12 +297,16 @@ __device__ __forceinline__ f32x4_t db_chain(const u32x4_t (&a)[8], const u32x4_t
   return d;
 }
 
-template <bool kFwd>
+template <bool kFwd, bool kG16>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, int64_t M, int64_t K,
                                               int64_t N, const uint8_t *__restrict__ codes,
                                               const float *__restrict__ cs, int64_t m0, int64_t n0,
                                               const ExpandConsts &tb, char *smem,
                                               f32x16_t (&acc)[2][8], const DbFold &dbf) {
+  using G = Geo<kG16>;
+  constexpr int kStageBytes = G::kStageBytes, kRingBytes = G::kRingBytes;
+  constexpr int kXPitch = G::kXPitch, kScratchBytes = G::kScratchBytes;
+  constexpr int kLoadsPerTile = G::kLoadsPerTile;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: LDS targets go to M0
   const int ch = wave & 1, kh = wave >> 1;
@@ -309,7 +323,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
     vx[j] = uint32_t(row) * uint32_t(K) * 2u + uint32_t(c) * 16u;
   }
   rsrc_t rC, rS;
-  uint32_t vc, vs;
+  uint32_t vc, vs, vs2 = 0;
   {
     const int s = 64 * wave + lane;               // 16-B slot of the code tile
     if constexpr (kFwd) {
@@ -323,19 +337,40 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       if (n0 / 2 + 16 * q + 16 > N / 2) q -= 2;
       rC = make_rsrc(codes + n0 / 2, K * (N / 2) - n0 / 2);
       vc = uint32_t(row) * uint32_t(N / 2) + 16u * q;
-      // scales: block column nb0 + (wave & 1), 64 k per tile
-      const int64_t nb = n0 / 64 + (wave & 1);
-      rS = make_rsrc(cs, (N / 64) * K * 4);
-      vs = uint32_t(nb * K + lane) * 4u;
+      if constexpr (kG16) {
+        // scales as stored, [k][N/16]: wavefront w gathers groups gg = 2 w
+        // and 2 w + 1 of the tile's eight (lane = k row; a group past N,
+        // in a ragged last tile, reads the last group: never stored)
+        const int64_t ng = N / 16;
+        rS = make_rsrc(cs, K * ng * 4);
+        const int64_t g0 = n0 / 16 + 2 * wave;
+        vs = uint32_t(int64_t(lane) * ng + (g0 < ng ? g0 : ng - 1)) * 4u;
+        vs2 = uint32_t(int64_t(lane) * ng + (g0 + 1 < ng ? g0 + 1 : ng - 1)) * 4u;
+      } else {
+        // scales: block column nb0 + (wave & 1), 64 k per tile
+        const int64_t nb = n0 / 64 + (wave & 1);
+        rS = make_rsrc(cs, (N / 64) * K * 4);
+        vs = uint32_t(nb * K + lane) * 4u;
+      }
     } else {
       // 128 W-rows x 2 pieces; slot s -> row 8*(s>>4) + (s&7), piece (s>>3)&1
       const int row = 8 * (s >> 4) + (s & 7), q = (s >> 3) & 1;
       rC = make_rsrc(codes + n0 * (K / 2), (N - n0) * (K / 2));
       vc = uint32_t(row) * uint32_t(K / 2) + 16u * q;
-      rS = make_rsrc(cs, (K / 64) * N * 4);
-      // the K offset is scalar (outside the range check): clamp the row
-      const int64_t srow = n0 + 64 * (wave & 1) + lane;
-      vs = uint32_t(srow < N ? srow : N - 1) * 4u;
+      if constexpr (kG16) {
+        // scales as stored, [W row][K/16]: wavefront w gathers group w of the
+        // tile's four for W rows 0..63 and 64..127 (rows past N clamped)
+        const int64_t ng = K / 16;
+        rS = make_rsrc(cs, N * ng * 4);
+        const int64_t r0 = n0 + lane, r1 = n0 + 64 + lane;
+        vs = uint32_t((r0 < N ? r0 : N - 1) * ng + wave) * 4u;
+        vs2 = uint32_t((r1 < N ? r1 : N - 1) * ng + wave) * 4u;
+      } else {
+        rS = make_rsrc(cs, (K / 64) * N * 4);
+        // the K offset is scalar (outside the range check): clamp the row
+        const int64_t srow = n0 + 64 * (wave & 1) + lane;
+        vs = uint32_t(srow < N ? srow : N - 1) * 4u;
+      }
     }
   }
 
@@ -350,13 +385,18 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
     uint32_t sc, ss;
     if constexpr (kFwd) {
       sc = uint32_t(kt) * BK * uint32_t(N / 2);
-      ss = uint32_t(kt) * BK * 4u;
+      ss = kG16 ? uint32_t(kt) * BK * uint32_t(N / 16) * 4u : uint32_t(kt) * BK * 4u;
     } else {
       sc = uint32_t(kt) * (BK / 2);
-      ss = uint32_t(kt) * uint32_t(N) * 4u;
+      ss = kG16 ? uint32_t(kt) * (BK / 16) * 4u : uint32_t(kt) * uint32_t(N) * 4u;
     }
     lds_load16(rC, base + kXBytes + wave * 1024, vc, sc);
-    lds_load4(rS, base + kXBytes + kCBytes + wave * 256, vs, ss);
+    if constexpr (kG16) {
+      lds_load4(rS, base + kXBytes + kCBytes + (2 * wave) * 256, vs, ss);
+      lds_load4(rS, base + kXBytes + kCBytes + (2 * wave + 1) * 256, vs2, ss);
+    } else {
+      lds_load4(rS, base + kXBytes + kCBytes + wave * 256, vs, ss);
+    }
   };
 
   // ---- per-lane LDS read offsets inside a stage
@@ -386,8 +426,18 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
       co[b] = uint32_t(((row >> 3) * 16 + h2 * 8 + (row & 7)) * 16 + 8 * kh);
     }
   }
-  // scale read offset (bytes into the scale area of a stage)
-  const uint32_t so = kFwd ? sco * 4u : uint32_t((ch * 64 + l32) * 4);
+  // scale read offset (bytes into the scale area of a stage).  16-entry
+  // groups: forward [group gg][k], the lane's 16 columns being group 4 ch +
+  // seg; dX [group gg][W row], the lane's k run (8 (2 kh + j) + 32 h2 ..
+  // + 7, both substeps) lying in group 2 h2 + kh.
+  uint32_t so;
+  if constexpr (kG16) {
+    const int kr0 = 32 * (er >> 3) + 16 * kh + (er & 7);      // k row kr(0)
+    so = kFwd ? uint32_t(((4 * ch + seg) * 64 + kr0) * 4)
+              : uint32_t(((2 * h2 + kh) * 128 + ch * 64 + l32) * 4);
+  } else {
+    so = kFwd ? sco * 4u : uint32_t((ch * 64 + l32) * 4);
+  }
   char *scr = smem + kRingBytes + wave * kScratchBytes;              // fwd expansion scratch
   const uint32_t swo = uint32_t((er * kXPitch + 16 * seg) * 2);      // this lane's scratch bytes
 
@@ -444,7 +494,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t *__restrict__ A16, 
   // ... and read back transposed as the two B fragments.
   auto read_b = [&](u32x4_t (&bb)[2]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32(scr, 32 * (b ^ kh));   // see the epilogue
+    for (int b = 0; b < 2; ++b) bb[b] = lds_col8_32<kXPitch>(scr, 32 * (b ^ kh));   // see the epilogue
   };
   auto mfmas = [&](const u32x4_t (&a)[8], const u32x4_t (&bb)[2]) {
 #pragma unroll
@@ -719,7 +769,7 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem, cons
 
   constexpr int kOE = kOutBf16 ? 2 : 4;                       // output element bytes
   constexpr int kOPitch = kOutBf16 ? 144 : 272;               // staging row pitch (bytes)
-  static_assert(65536 + 2 * 128 * kOPitch <= kLdsBytes, "epilogue LDS");
+  static_assert(65536 + 2 * 128 * kOPitch <= Geo<false>::kLdsBytes, "epilogue LDS");
   char *stg = smem + 65536 + ch * 128 * kOPitch;              // 128 rows x 64 columns per ch
   char *wr = smem + (ch * 2 + kh) * 16384 + lane * 16;        // this wavefront's region
   const char *rd = smem + (ch * 2 + (1 - kh)) * 16384 + lane * 16;   // the partner's
@@ -775,7 +825,7 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[2][8], char *smem, cons
 }
 
 // ================================================================ forward
-template <bool kOutBf16>
+template <bool kOutBf16, bool kG16>
 __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t K, int64_t N,
     const uint16_t *__restrict__ X16, int64_t M, const uint16_t *__restrict__ XA16,
@@ -795,13 +845,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
-  gemm_mainloop<true>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc, DbFold{});
+  gemm_mainloop<true, kG16>(X16, M, K, N, codes, cs, m0, n0, tb, smem, acc, DbFold{});
   // rank-r term: y += XA16 . B (B read as rows n of B^T)
   epilogue<kOutBf16>(acc, smem, ro, XA16, ldp, bq, M, N, m0, n0, Y);
 }
 
 // ================================================================ dX
-template <bool kOutBf16>
+template <bool kOutBf16, bool kG16>
 __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ cs, int64_t IN, int64_t OUT,
     const uint16_t *__restrict__ dY16, int64_t M, const uint16_t *__restrict__ G16,
@@ -821,13 +871,13 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
-  gemm_mainloop<false>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc, dbf);
+  gemm_mainloop<false, kG16>(dY16, M, OUT, IN, codes, cs, m0, i0, tb, smem, acc, dbf);
   // rank-r term: dX += G16 . A^T (A read as rows i of A)
   epilogue<kOutBf16>(acc, smem, ro, G16, ldp, aq, M, IN, m0, i0, dX);
 }
 
-bool set_lds(const void *fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) ==
+bool set_lds(const void *fn, int bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) ==
          hipSuccess;
 }
 
@@ -836,24 +886,28 @@ bool set_lds(const void *fn) {
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K, int64_t N,
                            const uint16_t *X16, int64_t M, const uint16_t *XA16, int32_t ldp,
                            const void *B, bool b_bf16, int32_t r, void *Y, bool y_bf16,
-                           int codebook, hipStream_t s) {
+                           int codebook, bool g16, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef bq{B, b_bf16, 1, N, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((N + BN - 1) / BN);
   dim3 grid(unsigned(mtc * ntc));
   if (!tables(codebook).symmetric) return hipErrorInvalidValue;
   const ExpandConsts tb = tables(codebook).expand;
-#define QLORA_FWD(OB)                                                                          \
-  do {                                                                                         \
-    static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB>));            \
-    if (!ok) return hipErrorInvalidValue;                                                      \
-    hipLaunchKernelGGL((fwd_gemm_kernel<OB>), grid, dim3(kThreads), kLdsBytes, s, codes, cs,  \
-                       K, N, X16, M, XA16, int(ldp), bq, Y, tb, ntc);                          \
+#define QLORA_FWD(OB, G)                                                                        \
+  do {                                                                                          \
+    constexpr int lds = Geo<G>::kLdsBytes;                                                      \
+    static bool ok = set_lds(reinterpret_cast<const void *>(&fwd_gemm_kernel<OB, G>), lds);     \
+    if (!ok) return hipErrorInvalidValue;                                                       \
+    hipLaunchKernelGGL((fwd_gemm_kernel<OB, G>), grid, dim3(kThreads), lds, s, codes, cs, K, N, \
+                       X16, M, XA16, int(ldp), bq, Y, tb, ntc);                                 \
   } while (0)
-  if (y_bf16)
-    QLORA_FWD(true);
-  else
-    QLORA_FWD(false);
+  if (g16) {
+    if (y_bf16) QLORA_FWD(true, true);
+    else QLORA_FWD(false, true);
+  } else {
+    if (y_bf16) QLORA_FWD(true, false);
+    else QLORA_FWD(false, false);
+  }
 #undef QLORA_FWD
   return hipGetLastError();
 }
@@ -866,8 +920,8 @@ bool dx_fold_fits(int64_t M, int64_t in, int64_t out) {
 hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int64_t out,
                           const uint16_t *dY16, int64_t M, const uint16_t *G16, int32_t ldp,
                           const void *A, bool a_bf16, int32_t r, void *dX, bool dx_bf16,
-                          int codebook, const uint16_t *xat, int64_t ldm, float *db_part,
-                          hipStream_t s) {
+                          int codebook, bool g16, const uint16_t *xat, int64_t ldm,
+                          float *db_part, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const AdapterRef aq{A, a_bf16, int64_t(r), 1, int(r)};
   const int mtc = int((M + BM - 1) / BM), ntc = int((in + BN - 1) / BN);
@@ -880,17 +934,21 @@ hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in, int
   dim3 grid(unsigned(mtc * ntc));
   if (!tables(codebook).symmetric) return hipErrorInvalidValue;
   const ExpandConsts tb = tables(codebook).expand;
-#define QLORA_DX(OB)                                                                           \
-  do {                                                                                         \
-    static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB>));             \
-    if (!ok) return hipErrorInvalidValue;                                                      \
-    hipLaunchKernelGGL((dx_gemm_kernel<OB>), grid, dim3(kThreads), kLdsBytes, s, codes, cs,   \
-                       in, out, dY16, M, G16, int(ldp), aq, dX, tb, ntc, dbf);                 \
+#define QLORA_DX(OB, G)                                                                         \
+  do {                                                                                          \
+    constexpr int lds = Geo<G>::kLdsBytes;                                                      \
+    static bool ok = set_lds(reinterpret_cast<const void *>(&dx_gemm_kernel<OB, G>), lds);      \
+    if (!ok) return hipErrorInvalidValue;                                                       \
+    hipLaunchKernelGGL((dx_gemm_kernel<OB, G>), grid, dim3(kThreads), lds, s, codes, cs, in,    \
+                       out, dY16, M, G16, int(ldp), aq, dX, tb, ntc, dbf);                      \
   } while (0)
-  if (dx_bf16)
-    QLORA_DX(true);
-  else
-    QLORA_DX(false);
+  if (g16) {
+    if (dx_bf16) QLORA_DX(true, true);
+    else QLORA_DX(false, true);
+  } else {
+    if (dx_bf16) QLORA_DX(true, false);
+    else QLORA_DX(false, false);
+  }
 #undef QLORA_DX
   return hipGetLastError();
 }

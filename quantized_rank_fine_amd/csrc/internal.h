@@ -84,8 +84,11 @@ const Tables &tables(int codebook);
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `s` and returns hipGetLastError() of the launch.
 
+// g16: the 16-entry format (one fp32 absmax per 16 weights into gscale, no
+// double quantization, qscale unused); nblocks counts 64-weight blocks.
 hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale,
-                           float *gscale, int64_t nblocks, int codebook, hipStream_t s);
+                           float *gscale, int64_t nblocks, int codebook, bool g16,
+                           hipStream_t s);
 
 // dst[n] (bf16) = src[n] (f32 or bf16)
 hipError_t launch_convert_to_bf16(const void *src, bool src_bf16, int64_t n,
@@ -149,12 +152,13 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
 
 // y = X16 . deq(Wq) + XA16 . B (K = in, N = out).  X16 [M x K] bf16; XA16
 // [M x ldp] bf16 with zero padding columns r..ldp-1; B [r x N] (f32 or bf16)
-// as given by the caller; cs from the prep pass (rows = K).
+// as given by the caller; cs from the prep pass (rows = K), or with g16 the
+// weight's own fp32 scales [K][N/16].
 hipError_t launch_fwd_gemm(const uint8_t *codes, const float *cs, int64_t K,
                            int64_t N, const uint16_t *X16, int64_t M,
                            const uint16_t *XA16, int32_t ldp, const void *B,
                            bool b_bf16, int32_t r, void *Y, bool y_bf16, int codebook,
-                           hipStream_t s);
+                           bool g16, hipStream_t s);
 
 // dX = dY16 . deq(Wq)^T + G16 . A^T.  dY16 [M x out] bf16; G16 [M x ldp] bf16
 // zero-padded; A [in x r] (f32 or bf16) as given; cs as in the forward.
@@ -166,7 +170,7 @@ hipError_t launch_dx_gemm(const uint8_t *codes, const float *cs, int64_t in,
                           int64_t out, const uint16_t *dY16, int64_t M,
                           const uint16_t *G16, int32_t ldp, const void *A,
                           bool a_bf16, int32_t r, void *dX, bool dx_bf16, int codebook,
-                          const uint16_t *xat, int64_t ldm, float *db_part,
+                          bool g16, const uint16_t *xat, int64_t ldm, float *db_part,
                           hipStream_t s);
 
 // Small-M forward (M <= kSmallMaxM tokens, r <= kSmallMaxR), two launches:
@@ -181,7 +185,8 @@ int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N);
 hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
                                     const float *gscale, int64_t K, int64_t N, const void *X,
                                     bool x_bf16, int64_t M, const void *A, bool a_bf16, int64_t r,
-                                    int64_t Kc, float *P, float *PXA, int codebook, hipStream_t s);
+                                    int64_t Kc, float *P, float *PXA, int codebook, bool g16,
+                                    hipStream_t s);
 hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS, int64_t M,
                                    int64_t N, int64_t r, const void *B, bool b_bf16, float *XA,
                                    void *Y, bool y_bf16, hipStream_t s,
@@ -205,13 +210,14 @@ struct SmallLinear {
   RankMul mul;
 };
 hipError_t launch_fwd_small_group(int n, const SmallLinear *lin, int64_t M, bool x_bf16,
-                                  bool a_bf16, int64_t r, int codebook, hipStream_t s);
+                                  bool a_bf16, int64_t r, int codebook, bool g16,
+                                  hipStream_t s);
 
 // W = deq(Wq) + A . B (W [in x out] fp32 or bf16; A [in x r], B [r x out]
 // in the adapter dtype), per element in fp32, one rounding at the end.
 hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2, int64_t in,
                         int64_t out, const void *A, const void *B, bool a_bf16, int32_t r,
-                        void *W, bool w_bf16, int codebook, hipStream_t s);
+                        void *W, bool w_bf16, int codebook, bool g16, hipStream_t s);
 
 // One Adam (AdamW) step over n fp32 elements in place (bias corrections for
 // step t >= 1); theta16, if not null, receives the updated theta as bf16.

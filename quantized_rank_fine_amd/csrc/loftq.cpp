@@ -151,6 +151,7 @@ extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, c
   if (!wq || !W0 || !omega || !A || !B || !ws) return QLORA_ERR_NULL;
   if (wq->in <= 0 || wq->out <= 0 || wq->in % 64 || wq->out % 64) return QLORA_ERR_SHAPE;
   if (wq->codebook < 0 || wq->codebook >= kCodebooks) return QLORA_ERR_DTYPE;
+  if (wq->block != 0 && wq->block != QLORA_BLOCK) return QLORA_ERR_DTYPE;   // 64-weight format only
   if (!wq->codes || !wq->qscale || !wq->gscale) return QLORA_ERR_NULL;
   if (adt != QLORA_F32 && adt != QLORA_BF16) return QLORA_ERR_DTYPE;
   if (k < 1 || k > 128 || r < 1 || r > k || k > wq->in || k > wq->out || iters < 0 || iters > 16)

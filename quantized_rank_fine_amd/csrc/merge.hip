@@ -5,7 +5,8 @@
 // is a dense float matrix, off the quantization grid ("What the simulations
 // show"), which qlora_quantize can take back to 4 bits at some loss.
 //
-// Per element, in fp32: w = L[code] * (q_b * s2_g) (the two products the
+// Per element, in fp32: w = L[code] * (q_b * s2_g), or L[code] * c_g in the
+// 16-entry format (the two products the
 // fused GEMMs form before their bf16 rounding), plus sum_j A[k][j] * B[j][n]
 // in fp32, then one rounding to the output dtype.
 //
@@ -52,6 +53,7 @@ struct MergeArgs {
   const void *B;      // [r x out]
   int r;
   void *W;            // [in x out]
+  int g16;            // 16-entry format: s2 holds one fp32 scale per 16 weights
 };
 
 struct Levels {
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, Levels lv) {
     const int64_t flat = row * a.out + col;
     const uint32_t word = *reinterpret_cast<const uint32_t *>(a.codes + flat / 2);
     const int64_t blk = row * NB + col / 64;
-    const float c = float(a.q8[blk]) * a.s2[blk >> 8];
+    const float c = a.g16 ? a.s2[flat / 16] : float(a.q8[blk]) * a.s2[blk >> 8];
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = sL[(word >> (4 * e)) & 15u] * c + acc[i][e];
@@ -157,15 +159,22 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
   __builtin_amdgcn_wave_barrier();
   const int64_t NB = a.out / 64;
 
+  // scales of columns n .. n + 15 and n + 16 .. n + 31 (one block scale, or
+  // two 16-entry group scales)
   u32x4_t cw[kMBlocks];
-  float sc[kMBlocks];
+  float sc[kMBlocks][2];
 #pragma unroll
   for (int b = 0; b < kMBlocks; ++b) {
     if (b < nb) {
       const int64_t n = nw0 + 32 * b;
       cw[b] = *reinterpret_cast<const u32x4_t *>(a.codes + (row * a.out + n) / 2);
-      const int64_t blk = row * NB + n / 64;
-      sc[b] = float(a.q8[blk]) * a.s2[blk >> 8];
+      if (a.g16) {
+        sc[b][0] = a.s2[(row * a.out + n) / 16];
+        sc[b][1] = a.s2[(row * a.out + n) / 16 + 1];
+      } else {
+        const int64_t blk = row * NB + n / 64;
+        sc[b][0] = sc[b][1] = float(a.q8[blk]) * a.s2[blk >> 8];
+      }
     }
   }
   f32x16_t acc[kMBlocks];
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
     if (b < nb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)                          // column 8 (i / 4) + 4 h + i % 4
-        acc[b][i] = sL[w][(cw[b][i >> 2] >> (4 * (4 * h + (i & 3)))) & 15u] * sc[b];
+        acc[b][i] = sL[w][(cw[b][i >> 2] >> (4 * (4 * h + (i & 3)))) & 15u] * sc[b][i >> 3];
     }
   }
   if constexpr (kAbf16) {
@@ -264,8 +273,8 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
 
 hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2, int64_t in,
                         int64_t out, const void *A, const void *B, bool a_bf16, int32_t r,
-                        void *W, bool w_bf16, int codebook, hipStream_t s) {
-  MergeArgs a{codes, q8, s2, in, out, A, B, int(r), W};
+                        void *W, bool w_bf16, int codebook, bool g16, hipStream_t s) {
+  MergeArgs a{codes, q8, s2, in, out, A, B, int(r), W, g16 ? 1 : 0};
   Levels lv;
   const Tables &t = tables(codebook);
   for (int i = 0; i < 16; ++i) lv.L[i] = t.L[i];

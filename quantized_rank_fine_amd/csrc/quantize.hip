@@ -33,6 +33,14 @@
 // nearest is 2^-10.7 away; the host checks this when it builds the table).
 // The table {T_bucket, base} is built on the host and copied into LDS by
 // each workgroup.
+//
+// The lab's 16-entry format ("QLoRA (low-rank adapters on a quantized
+// model)", "The code, line by line": one scale per 16 consecutive entries, no
+// double quantization) runs the same kernel with a 4-lane absmax: the 16
+// weights 16q .. 16q + 15 of a block are elements 4k .. 4k + 3 (q = 0, 1) or
+// 32 + 4k .. (q = 2, 3) of the four lanes k = 4 (q & 1) .. + 3, so each lane
+// reduces its two halves over its quad, encodes each against its own group's
+// absmax, and the quad's first lane stores the two fp32 group scales.
 #include "device.h"
 
 namespace qlora {
@@ -72,6 +80,24 @@ __device__ __forceinline__ uint32_t row8_max(uint32_t m) {
   return m;
 }
 
+// max over the 4 lanes of a DPP quad
+__device__ __forceinline__ uint32_t quad_max(uint32_t m) {
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
+  return m;
+}
+
+// max |w| over 4 weights (as absmax8)
+__device__ __forceinline__ float absmax4(f32x4_t a) {
+  float m;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\t"
+      "v_max_f32_e64 %0, %0, |%4|\n\t"
+      "s_nop 1"                     // VALU write -> DPP read of the result
+      : "=&v"(m)
+      : "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w));
+  return m;
+}
+
 // max |w| over the 8 weights of a lane (v_max3 with source modifiers; the
 // library's fmaxf would first canonicalize every operand)
 __device__ __forceinline__ float absmax8(f32x4_t a, f32x4_t b) {
@@ -88,11 +114,12 @@ __device__ __forceinline__ float absmax8(f32x4_t a, f32x4_t b) {
 
 struct GroupRefs {
   __amdgpu_buffer_rsrc_t w, c;   // this group's weights and codes, ending at the last block
+  __amdgpu_buffer_rsrc_t s;      // 16-entry format: its fp32 scales (4 per block)
   int nb;                        // blocks in this group
 };
 
-__device__ __forceinline__ GroupRefs group_refs(const float *W0, uint8_t *codes, int64_t nblocks,
-                                                int64_t g) {
+__device__ __forceinline__ GroupRefs group_refs(const float *W0, uint8_t *codes, float *scales,
+                                                int64_t nblocks, int64_t g) {
   const int64_t rem = nblocks - g * kBlocksPerGroup;
   GroupRefs r;
   r.nb = rem < kBlocksPerGroup ? int(rem) : kBlocksPerGroup;
@@ -100,6 +127,8 @@ __device__ __forceinline__ GroupRefs group_refs(const float *W0, uint8_t *codes,
                                           r.nb * 256, kBufFlags);
   r.c = __builtin_amdgcn_make_buffer_rsrc((void *)(codes + g * kBlocksPerGroup * 32), (short)0,
                                           r.nb * 32, kBufFlags);
+  r.s = __builtin_amdgcn_make_buffer_rsrc((void *)(scales + g * kBlocksPerGroup * 4), (short)0,
+                                          r.nb * 16, kBufFlags);
   return r;
 }
 
@@ -115,19 +144,35 @@ __device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t rW, uint32_t v
 // codes of this wavefront's 64 blocks: block absmax to sc_blk, the 16-bit
 // code groups to the wavefront's 2-KiB staging area, which then leaves in two
 // 1-KiB contiguous stores
+template <bool kG16>
 __device__ __forceinline__ void encode_group(const f32x4_t (&v)[kSteps][2], const BucketEntry *lut,
                                              float *sc_blk, uint16_t *stage, int bl0,
-                                             __amdgpu_buffer_rsrc_t rC) {
+                                             __amdgpu_buffer_rsrc_t rC, __amdgpu_buffer_rsrc_t rS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, k = lane & 7;
   uint16_t *st = stage + (lane >> 3) * 16 + k;   // block bl0 - 64 wave, halfword k
 #pragma unroll
   for (int j = 0; j < kSteps; ++j) {
     const f32x4_t a = v[j][0], b = v[j][1];
-    const float m = __uint_as_float(row8_max(__float_as_uint(absmax8(a, b))));
-    sc_blk[bl0 + 8 * j] = m;                    // the 8 lanes of the block agree
-    const double y = 1.0 / double(m == 0.0f ? 1.0f : m);
-    st[j * 128] = uint16_t(code4(a, y, lut));
-    st[j * 128 + 8] = uint16_t(code4(b, y, lut));
+    if constexpr (kG16) {
+      // groups 16 q: q = k >> 2 (elements of a) and 2 + (k >> 2) (of b)
+      const float ma = __uint_as_float(quad_max(__float_as_uint(absmax4(a))));
+      const float mb = __uint_as_float(quad_max(__float_as_uint(absmax4(b))));
+      const double ya = 1.0 / double(ma == 0.0f ? 1.0f : ma);
+      const double yb = 1.0 / double(mb == 0.0f ? 1.0f : mb);
+      st[j * 128] = uint16_t(code4(a, ya, lut));
+      st[j * 128 + 8] = uint16_t(code4(b, yb, lut));
+      if ((k & 3) == 0) {                        // one lane per quad stores its two scales
+        const uint32_t off = uint32_t((bl0 + 8 * j) * 16 + (k >> 2) * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ma), rS, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mb), rS, off + 8, 0, 0);
+      }
+    } else {
+      const float m = __uint_as_float(row8_max(__float_as_uint(absmax8(a, b))));
+      sc_blk[bl0 + 8 * j] = m;                  // the 8 lanes of the block agree
+      const double y = 1.0 / double(m == 0.0f ? 1.0f : m);
+      st[j * 128] = uint16_t(code4(a, y, lut));
+      st[j * 128 + 8] = uint16_t(code4(b, y, lut));
+    }
   }
   // LDS operations of one wavefront complete in order: the reads see all writes
   const u32x4_t *s4 = reinterpret_cast<const u32x4_t *>(stage);
@@ -160,6 +205,7 @@ __device__ __forceinline__ void double_quantize(const float *sc_blk, float *sred
   if (t == 0) gscale[g] = s2;
 }
 
+template <bool kG16>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const float *__restrict__ W0, uint8_t *__restrict__ codes, int8_t *__restrict__ qscale,
     float *__restrict__ gscale, int64_t nblocks, QuantConsts qc) {
@@ -175,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const uint32_t vw = uint32_t(bl0 * 256 + 16 * k);
 
   const int64_t g = blockIdx.x;
-  const GroupRefs cur = group_refs(W0, codes, nblocks, g);
+  const GroupRefs cur = group_refs(W0, codes, gscale, nblocks, g);
   BucketEntry own = {0.0f, 0u};
   if (t < kBuckets) own = qc.bucket[t];
   __builtin_amdgcn_sched_barrier(0);            // table read ahead of the weight loads
@@ -183,21 +229,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   load_group(cur.w, vw, v);
   if (t < kBuckets) lut[t] = own;
   __syncthreads();
-  encode_group(v, lut, sc_blk, stage[wave], bl0, cur.c);
-  __syncthreads();
-  double_quantize(sc_blk, sred, cur.nb, g, qscale, gscale);
+  encode_group<kG16>(v, lut, sc_blk, stage[wave], bl0, cur.c, cur.s);
+  if constexpr (!kG16) {
+    __syncthreads();
+    double_quantize(sc_blk, sred, cur.nb, g, qscale, gscale);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const float *W0, uint8_t *codes, int8_t *qscale, float *gscale,
-                           int64_t nblocks, int codebook, hipStream_t s) {
+                           int64_t nblocks, int codebook, bool g16, hipStream_t s) {
   const int64_t groups = (nblocks + kBlocksPerGroup - 1) / kBlocksPerGroup;
   if (groups == 0) return hipSuccess;
   const Tables &t = tables(codebook);
   if (!t.quant.ok) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, W0, codes,
-                     qscale, gscale, nblocks, t.quant);
+  if (g16)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)groups), dim3(kThreads), 0, s, W0,
+                       codes, qscale, gscale, nblocks, t.quant);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)groups), dim3(kThreads), 0, s, W0,
+                       codes, qscale, gscale, nblocks, t.quant);
   return hipGetLastError();
 }
 

@@ -22,6 +22,10 @@
 // workgroups accumulates each chunk's X . A (unscaled X, A staged in LDS and
 // read transposed).  Partials: P[chunk][m][n] and PXA[chunk][m][j], fp32.
 // Pass 2: XA = sum over chunks of PXA (written out), y = sum of P + XA . B.
+//
+// The lab's 16-entry format (one fp32 scale per 16 consecutive weights, no
+// double quantization) takes the same route with one scale per (k row,
+// 16-column MFMA tile q): the activation operand is scaled once per q.
 #include "device.h"
 
 namespace qlora {
@@ -90,6 +94,7 @@ struct Stage {
   u32x4_t xr;              // X[t >> 5][4 (t & 31) .. +3] (bf16: first 8 bytes)
   int qv;                  // int8 block scale of k row 64 (wave >> 2) + lane
   float s2;                // its group scale
+  f32x4_t s16;             // 16-entry format: the row's 4 group scales of the block column
 };
 
 // X[16 x kSub] of rows kb.. to registers: thread t -> row t >> 5, k run
@@ -196,11 +201,12 @@ __device__ __forceinline__ void xa_worker(const SmallArgs &a, int64_t kbeg, int6
 
 // One workgroup of the partial pass: column slice bx (bx == slices: the X . A
 // workgroup) of K chunk by.
-template <bool kX16, bool kA16>
+template <bool kX16, bool kA16, bool kG16>
 __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const ExpandConsts16 &t16,
                                                 int bx, int by) {
   __shared__ __attribute__((aligned(16))) float xs[16][kXPitchS];
-  __shared__ __attribute__((aligned(16))) float cs[4][kSub];
+  // scales per block column and k row; 16-entry format: per 16-column tile too
+  __shared__ __attribute__((aligned(16))) float cs[4][kG16 ? 4 : 1][kSub];
   // codes of the 4 block columns, or (X . A workgroups) the adapter rows;
   // after the K loop, the k-half partial sums
   __shared__ __attribute__((aligned(16))) uint8_t ct[4 * kRegion];
@@ -239,7 +245,8 @@ __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const Expand
   const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
       (void *)a.qscale, (short)0, clamp_records(a.K * nblk), kBufFlags);
   const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)a.gscale, (short)0, clamp_records((a.K * nblk + 255) / 256 * 4), kBufFlags);
+      (void *)a.gscale, (short)0,
+      clamp_records(kG16 ? a.K * nblk * 16 : (a.K * nblk + 255) / 256 * 4), kBufFlags);
 
   auto load_stage = [&](int64_t kb, Stage<kX16> &S) {
     // the workgroup's 128-B segment of 8 rows per load instruction (whole
@@ -252,8 +259,13 @@ __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const Expand
     }
     S.xr = load_x4<kX16>(rX, a.K, kb);
     const uint32_t b = uint32_t((kb + 64 * kh + lane) * nblk + blk);
-    S.qv = int(__builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0));
-    S.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, (b >> 8) * 4u, 0, 0));
+    if constexpr (kG16) {
+      // scales [K][N/16]: groups 4 blk .. 4 blk + 3 of k row kb + 64 kh + lane
+      S.s16 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rG, b * 16u, 0, 0));
+    } else {
+      S.qv = int(__builtin_amdgcn_raw_buffer_load_b8(rQ, b, 0, 0));
+      S.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rG, (b >> 8) * 4u, 0, 0));
+    }
   };
 
   f32x4_t acc[4];
@@ -273,7 +285,13 @@ __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const Expand
       *reinterpret_cast<u32x2_t *>(dst + 8) = u32x2_t{S.cv[it][2], S.cv[it][3]};
     }
     store_x4<kX16>(xs, S.xr, kb, kend);
-    cs[bc][64 * kh + lane] = (blk_ok && 64 * kh + lane < rows) ? float(int8_t(S.qv)) * S.s2 : 0.0f;
+    if constexpr (kG16) {
+      const bool in = blk_ok && 64 * kh + lane < rows;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cs[bc][q][64 * kh + lane] = in ? S.s16[q] : 0.0f;
+    } else {
+      cs[bc][0][64 * kh + lane] = (blk_ok && 64 * kh + lane < rows) ? float(int8_t(S.qv)) * S.s2 : 0.0f;
+    }
     __syncthreads();
     // ---- the next sub-chunk's loads fly while this one is multiplied
     if (kb + kSub < kend) load_stage(kb + kSub, S);
@@ -281,27 +299,36 @@ __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const Expand
     const int rb = 64 * kh;
     if (rb < rows) {
       // activation operand: X[m = i][rb + 16 g + 0..15] times the row scales
-      float xv[16], sv[16];
+      // (of the block column, or of 16-column tile sq in the 16-entry format)
+      float xv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4_t x4 = *reinterpret_cast<const f32x4_t *>(&xs[i][rb + 16 * g + 4 * q]);
-        const f32x4_t s4 = *reinterpret_cast<const f32x4_t *>(&cs[bc][rb + 16 * g + 4 * q]);
         xv[4 * q] = x4.x; xv[4 * q + 1] = x4.y; xv[4 * q + 2] = x4.z; xv[4 * q + 3] = x4.w;
-        sv[4 * q] = s4.x; sv[4 * q + 1] = s4.y; sv[4 * q + 2] = s4.z; sv[4 * q + 3] = s4.w;
       }
+      auto scaled_x = [&](int sq, u32x4_t &A1, u32x4_t &A2) {
+        float sv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t s4 = *reinterpret_cast<const f32x4_t *>(&cs[bc][sq][rb + 16 * g + 4 * q]);
+          sv[4 * q] = s4.x; sv[4 * q + 1] = s4.y; sv[4 * q + 2] = s4.z; sv[4 * q + 3] = s4.w;
+        }
+        A1[0] = pack_bf16x2(xv[0] * sv[0], xv[2] * sv[2]);
+        A1[1] = pack_bf16x2(xv[4] * sv[4], xv[6] * sv[6]);
+        A1[2] = pack_bf16x2(xv[1] * sv[1], xv[3] * sv[3]);
+        A1[3] = pack_bf16x2(xv[5] * sv[5], xv[7] * sv[7]);
+        A2[0] = pack_bf16x2(xv[8] * sv[8], xv[10] * sv[10]);
+        A2[1] = pack_bf16x2(xv[12] * sv[12], xv[14] * sv[14]);
+        A2[2] = pack_bf16x2(xv[9] * sv[9], xv[11] * sv[11]);
+        A2[3] = pack_bf16x2(xv[13] * sv[13], xv[15] * sv[15]);
+      };
       u32x4_t A1, A2;
-      A1[0] = pack_bf16x2(xv[0] * sv[0], xv[2] * sv[2]);
-      A1[1] = pack_bf16x2(xv[4] * sv[4], xv[6] * sv[6]);
-      A1[2] = pack_bf16x2(xv[1] * sv[1], xv[3] * sv[3]);
-      A1[3] = pack_bf16x2(xv[5] * sv[5], xv[7] * sv[7]);
-      A2[0] = pack_bf16x2(xv[8] * sv[8], xv[10] * sv[10]);
-      A2[1] = pack_bf16x2(xv[12] * sv[12], xv[14] * sv[14]);
-      A2[2] = pack_bf16x2(xv[9] * sv[9], xv[11] * sv[11]);
-      A2[3] = pack_bf16x2(xv[13] * sv[13], xv[15] * sv[15]);
+      if constexpr (!kG16) scaled_x(0, A1, A2);
       // weight operand: lane (g, i) <- column 16 q + i, rows rb + 16 g + 0..15
       const lds_char *crow = (const lds_char *)(myct + (rb + 16 * g + i) * kCodePitch);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if constexpr (kG16) scaled_x(q, A1, A2);
         const i32x2_t d = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(crow + 8 * q));
         acc[q] = mfma16x16x32(A1, expand_levels(uint32_t(d[0]), t16), acc[q]);
         acc[q] = mfma16x16x32(A2, expand_levels(uint32_t(d[1]), t16), acc[q]);
@@ -334,9 +361,9 @@ __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const Expand
   }
 }
 
-template <bool kX16, bool kA16>
+template <bool kX16, bool kA16, bool kG16>
 __global__ __launch_bounds__(kThreads1) void fwd_small_kernel(SmallArgs a, ExpandConsts16 t16) {
-  fwd_small_block<kX16, kA16>(a, t16, int(blockIdx.x), int(blockIdx.y));
+  fwd_small_block<kX16, kA16, kG16>(a, t16, int(blockIdx.x), int(blockIdx.y));
 }
 
 // Several independent linears' partial passes in one launch: workgroups
@@ -349,7 +376,7 @@ struct SmallGroup {
   int gx[kSmallMaxGroup];
 };
 
-template <bool kX16, bool kA16>
+template <bool kX16, bool kA16, bool kG16>
 __global__ __launch_bounds__(kThreads1) void fwd_small_group_kernel(SmallGroup g,
                                                                     ExpandConsts16 t16) {
   const int bid = int(blockIdx.x);
@@ -358,7 +385,7 @@ __global__ __launch_bounds__(kThreads1) void fwd_small_group_kernel(SmallGroup g
   for (int j = 1; j < kSmallMaxGroup; ++j)
     if (j < g.n && bid >= g.base[j]) l = j;
   const int local = bid - g.base[l];
-  fwd_small_block<kX16, kA16>(g.a[l], t16, local % g.gx[l], local / g.gx[l]);
+  fwd_small_block<kX16, kA16, kG16>(g.a[l], t16, local % g.gx[l], local / g.gx[l]);
 }
 
 // Pass 2: a workgroup covers `cols` = 256 / Mp columns of all M rows (Mp =
@@ -502,7 +529,8 @@ int64_t small_fwd_chunk_rows(int64_t M, int64_t K, int64_t N) {
 hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
                                     const float *gscale, int64_t K, int64_t N, const void *X,
                                     bool x_bf16, int64_t M, const void *A, bool a_bf16, int64_t r,
-                                    int64_t Kc, float *P, float *PXA, int codebook, hipStream_t s) {
+                                    int64_t Kc, float *P, float *PXA, int codebook, bool g16,
+                                    hipStream_t s) {
   const int64_t KS = (K + Kc - 1) / Kc;
   const int64_t slices = (N + kSliceN - 1) / kSliceN;
   SmallArgs a{codes, qscale, gscale, K, N, X, A, M, r, Kc, P, PXA};
@@ -510,13 +538,26 @@ hipError_t launch_fwd_small_partial(const uint8_t *codes, const int8_t *qscale,
   const ExpandConsts16 &t16 = tables(codebook).expand16;
   // one extra column of workgroups computes the X . A partials
   const dim3 grid = dim3(unsigned(slices + (r > 0 ? 1 : 0)), unsigned(KS));
-  if (x_bf16) {
-    if (a_bf16) hipLaunchKernelGGL((fwd_small_kernel<true, true>), grid, dim3(kThreads1), 0, s, a, t16);
-    else hipLaunchKernelGGL((fwd_small_kernel<true, false>), grid, dim3(kThreads1), 0, s, a, t16);
+#define QLORA_SMALL(XB, AB, G) \
+  hipLaunchKernelGGL((fwd_small_kernel<XB, AB, G>), grid, dim3(kThreads1), 0, s, a, t16)
+  if (g16) {
+    if (x_bf16) {
+      if (a_bf16) QLORA_SMALL(true, true, true);
+      else QLORA_SMALL(true, false, true);
+    } else {
+      if (a_bf16) QLORA_SMALL(false, true, true);
+      else QLORA_SMALL(false, false, true);
+    }
   } else {
-    if (a_bf16) hipLaunchKernelGGL((fwd_small_kernel<false, true>), grid, dim3(kThreads1), 0, s, a, t16);
-    else hipLaunchKernelGGL((fwd_small_kernel<false, false>), grid, dim3(kThreads1), 0, s, a, t16);
+    if (x_bf16) {
+      if (a_bf16) QLORA_SMALL(true, true, false);
+      else QLORA_SMALL(true, false, false);
+    } else {
+      if (a_bf16) QLORA_SMALL(false, true, false);
+      else QLORA_SMALL(false, false, false);
+    }
   }
+#undef QLORA_SMALL
   return hipGetLastError();
 }
 
@@ -538,7 +579,8 @@ hipError_t launch_fwd_small_reduce(const float *P, const float *PXA, int64_t KS,
 }
 
 hipError_t launch_fwd_small_group(int n, const SmallLinear *lin, int64_t M, bool x_bf16,
-                                  bool a_bf16, int64_t r, int codebook, hipStream_t s) {
+                                  bool a_bf16, int64_t r, int codebook, bool g16,
+                                  hipStream_t s) {
   if (n < 1 || n > kSmallMaxGroup) return hipErrorInvalidValue;
   if (!tables(codebook).symmetric) return hipErrorInvalidValue;
   const ExpandConsts16 &t16 = tables(codebook).expand16;
@@ -561,13 +603,27 @@ hipError_t launch_fwd_small_group(int n, const SmallLinear *lin, int64_t M, bool
   }
   g.base[n] = int(nb);
   rg.base[n] = int(nr);
-  if (x_bf16) {
-    if (a_bf16) hipLaunchKernelGGL((fwd_small_group_kernel<true, true>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
-    else hipLaunchKernelGGL((fwd_small_group_kernel<true, false>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
+#define QLORA_SMALLG(XB, AB, G) \
+  hipLaunchKernelGGL((fwd_small_group_kernel<XB, AB, G>), dim3(unsigned(nb)), dim3(kThreads1), 0, \
+                     s, g, t16)
+  if (g16) {
+    if (x_bf16) {
+      if (a_bf16) QLORA_SMALLG(true, true, true);
+      else QLORA_SMALLG(true, false, true);
+    } else {
+      if (a_bf16) QLORA_SMALLG(false, true, true);
+      else QLORA_SMALLG(false, false, true);
+    }
   } else {
-    if (a_bf16) hipLaunchKernelGGL((fwd_small_group_kernel<false, true>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
-    else hipLaunchKernelGGL((fwd_small_group_kernel<false, false>), dim3(unsigned(nb)), dim3(kThreads1), 0, s, g, t16);
+    if (x_bf16) {
+      if (a_bf16) QLORA_SMALLG(true, true, false);
+      else QLORA_SMALLG(true, false, false);
+    } else {
+      if (a_bf16) QLORA_SMALLG(false, true, false);
+      else QLORA_SMALLG(false, false, false);
+    }
   }
+#undef QLORA_SMALLG
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the reduction: y and B in the activation / adapter dtypes as the partial pass's X, A

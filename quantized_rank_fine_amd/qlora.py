@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "qlora.h")
 
 F32, BF16 = 0, 1
+LAB_GROUP = 16                        # QLORA_LAB_GROUP: 16-entry scale groups
 NOALLOC_SCRATCH_BYTES = 32 << 20      # QLORA_NOALLOC_SCRATCH_BYTES
 CB_NF4, CB_UNIFORM4, CB_INT4, CB_INT3, CB_TERNARY = 0, 1, 2, 3, 4   # qlora_codebook
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "pointer not 16-byte aligned",
@@ -34,7 +35,8 @@ class QloraError(RuntimeError):
 class qlora_nf4(ctypes.Structure):
     _fields_ = [("in_", ctypes.c_int64), ("out", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
-                ("gscale", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
+                ("gscale", ctypes.c_void_p), ("codebook", ctypes.c_int32),
+                ("block", ctypes.c_int32)]
 
 
 class qlora_lora(ctypes.Structure):
@@ -160,28 +162,34 @@ def _check(status, where):
         raise QloraError(status, where)
 
 
-def nf4_struct(n_in, n_out, codes, qscale, gscale, codebook=CB_NF4):
+def nf4_struct(n_in, n_out, codes, qscale, gscale, codebook=CB_NF4, block=0):
     """qlora_nf4 describing caller-owned buffers (tensors or raw pointers)."""
     return qlora_nf4(int(n_in), int(n_out), _ptr(codes), _ptr(qscale), _ptr(gscale),
-                     int(codebook))
+                     int(codebook), int(block))
 
 
 class NF4Weight:
-    """Caller-owned device buffers of one quantized (in, out) weight and the
-    codebook its codes index."""
+    """Caller-owned device buffers of one quantized (in, out) weight, the
+    codebook its codes index and its scale format: block 64 (int8 block
+    scales, double-quantized) or LAB_GROUP (one fp32 scale per 16 entries)."""
 
-    def __init__(self, n_in, n_out, device="cuda", codebook=CB_NF4):
+    def __init__(self, n_in, n_out, device="cuda", codebook=CB_NF4, block=64):
         import torch
         n = n_in * n_out
         self.n_in, self.n_out = n_in, n_out
         self.codebook = codebook
+        self.block = block
         self.codes = torch.empty(n // 2, dtype=torch.uint8, device=device)
-        self.qscale = torch.empty(n // 64, dtype=torch.int8, device=device)
-        self.gscale = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=device)
+        if block == LAB_GROUP:
+            self.qscale = None
+            self.gscale = torch.empty(n // LAB_GROUP, dtype=torch.float32, device=device)
+        else:
+            self.qscale = torch.empty(n // 64, dtype=torch.int8, device=device)
+            self.gscale = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=device)
 
     def struct(self):
         return nf4_struct(self.n_in, self.n_out, self.codes, self.qscale, self.gscale,
-                          self.codebook)
+                          self.codebook, 0 if self.block == 64 else self.block)
 
 
 # ------------------------------------------------------------- entry points

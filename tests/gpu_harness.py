@@ -60,12 +60,12 @@ def levels_of(codebook):
             q.CB_TERNARY: lambda: oracle.int_levels(1)}[codebook]()
 
 
-def quantize_gpu(w0, codebook=q.CB_NF4):
+def quantize_gpu(w0, codebook=q.CB_NF4, block=64):
     """Quantize an fp32 (in, out) numpy matrix on the GPU; returns the
-    NF4Weight (device buffers)."""
+    NF4Weight (device buffers).  block = 16: the lab's 16-entry format."""
     torch, dev = torch_dev()
     n_in, n_out = w0.shape
-    wq = q.NF4Weight(n_in, n_out, dev, codebook)
+    wq = q.NF4Weight(n_in, n_out, dev, codebook, block)
     tw = to_dev(w0)
     q.qlora_quantize(tw, wq)
     torch.cuda.synchronize()
@@ -77,13 +77,14 @@ class Layer:
     """Seeded inputs of one adapted linear, on host and device."""
 
     def __init__(self, workload, M, n_in, n_out, r, act="bf16", adt="bf16", b_zero=False,
-                 layer=0, linear=0, w0=None, codebook=q.CB_NF4):
+                 layer=0, linear=0, w0=None, codebook=q.CB_NF4, block=64):
         torch, dev = torch_dev()
         self.M, self.n_in, self.n_out, self.r = M, n_in, n_out, r
         self.codebook = codebook
+        self.block = block
         self.act, self.adt = act, adt
         self.w0 = synth.weights(n_in, n_out, workload, layer, linear) if w0 is None else w0
-        self._okey = (workload, n_in, n_out, layer, linear, codebook) if w0 is None else None
+        self._okey = (workload, n_in, n_out, layer, linear, codebook, block) if w0 is None else None
         self._oq = None
         self.X = synth.activations(M, n_in, workload, act, layer, linear)
         self.dY = synth.activations(M, n_out, workload, act, layer, linear, tensor=synth.T_DY)
@@ -107,7 +108,7 @@ class Layer:
         self.tdY = dv(self.dY, self.tdt)
         self.tA = dv(self.A, self.adt_t)
         self.tB = dv(self.B, self.adt_t)
-        self.wq = quantize_gpu(self.w0, codebook)
+        self.wq = quantize_gpu(self.w0, codebook, block)
 
     # ---------------------------------------------------------------- runs
     def fwd(self, lora=None, save_xa=True):
@@ -155,7 +156,10 @@ class Layer:
             if key is not None and key in _ORACLE_Q:
                 self._oq = _ORACLE_Q[key]
             else:
-                self._oq = oracle.quantize(self.w0, levels_of(self.codebook))
+                if self.block == 16:
+                    self._oq = oracle.quantize_groups(self.w0, levels_of(self.codebook))
+                else:
+                    self._oq = oracle.quantize(self.w0, levels_of(self.codebook))
                 if key is not None:
                     _ORACLE_Q.clear()          # keep one large weight at a time
                     _ORACLE_Q[key] = self._oq
@@ -165,6 +169,9 @@ class Layer:
         """deq(Q(W0)) in float64, from the oracle's own quantization of W0
         (nothing read back from the device)."""
         oq = self.oracle_q()
+        if self.block == 16:
+            return oracle.dequantize_groups(oq["packed"], oq["scales"], self.n_in, self.n_out,
+                                            levels_of(self.codebook))
         return oracle.dequantize(oq["packed"], oq["q8"], oq["s2"], self.n_in, self.n_out,
                                  levels_of(self.codebook))
 
@@ -172,6 +179,10 @@ class Layer:
         """The device's packed codes, q8 and s2 against the oracle's."""
         oq = self.oracle_q()
         assert np.array_equal(self.wq.codes.cpu().numpy(), oq["packed"])
+        if self.block == 16:
+            assert np.array_equal(self.wq.gscale.cpu().numpy().view(np.uint32),
+                                  oq["scales"].view(np.uint32))
+            return
         assert np.array_equal(self.wq.qscale.cpu().numpy(), oq["q8"])
         assert np.array_equal(self.wq.gscale.cpu().numpy().view(np.uint32),
                               oq["s2"].view(np.uint32))

@@ -449,3 +449,18 @@ def test_noalloc_forward_validation(L):
     assert f(ctypes.byref(s), P, -1, q.BF16, P, P, 16, q.BF16, P, P, None) == 2
     assert f(ctypes.byref(_nf4(256, 100)), P, 64, q.BF16, P, P, 8, q.BF16, P, P, None) == 2
     assert f(ctypes.byref(s), P, 64, 9, P, P, 8, q.BF16, P, P, None) == 4
+
+
+def test_scale_format_validation(L):
+    """qlora_nf4.block: 0 / 64 (double-quantized 64-weight blocks) or 16 (the
+    lab's 16-entry groups, qscale unused and may be NULL); anything else is
+    refused as a dtype error before any launch."""
+    for blk in (8, 32, 128, -16):
+        s = q.nf4_struct(256, 256, P, P, P, 0, blk)
+        assert L.qlora_quantize(P, ctypes.byref(s), None) == 4
+    s = q.nf4_struct(256, 256, P, None, P, q.CB_INT4, 16)     # no qscale: accepted
+    assert L.qlora_linear_fwd(ctypes.byref(s), P, 0, q.BF16, P, P, 8, q.BF16, P, P, P, 0, None) == 0
+    s = q.nf4_struct(256, 256, P, None, P, q.CB_INT4, 64)     # 64-weight format needs qscale
+    assert L.qlora_quantize(P, ctypes.byref(s), None) == 1
+    s = q.nf4_struct(256, 256, P, None, U, q.CB_INT4, 16)
+    assert L.qlora_quantize(P, ctypes.byref(s), None) == 3
