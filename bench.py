@@ -75,7 +75,7 @@ def parse():
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the 256^2, 7B-block and 65B-layer reports")
-    p.add_argument("--only", choices=["cfg1", "cfg3", "cfg4", "decode"],
+    p.add_argument("--only", choices=["cfg1", "cfg3", "cfg4", "decode", "loftq"],
                    help="run only this workload's GPU steps (for profiler runs); prints its "
                         "report without the oracle timings")
     p.add_argument("--cfg4-layers", type=int, default=80,
@@ -702,6 +702,34 @@ def cfg4_oracle():
                       "and its float64 products by flops to one layer at M = 8192"}
 
 
+def loftq_report(W0, wq, r, reps=3):
+    """LoftQ-style start of A and B (rank r, 24 probe columns, 2 power
+    iterations) of the quantized weight wq of W0: a synchronous call, timed
+    on the host clock."""
+    import torch
+
+    from quantized_rank_fine_amd import qlora as q
+
+    dev = W0.device
+    kq = 24
+    gq = torch.Generator(device="cpu").manual_seed(7)
+    omega = torch.randn(wq.n_out, kq, generator=gq).to(dev)
+    Aq = torch.empty(wq.n_in, r, dtype=torch.bfloat16, device=dev)
+    Bq = torch.empty(r, wq.n_out, dtype=torch.bfloat16, device=dev)
+    wsq_b = q.qlora_loftq_workspace_bytes(wq.n_in, wq.n_out, kq)
+    wsq = torch.empty(wsq_b, dtype=torch.uint8, device=dev)
+    q.qlora_quantize(W0, wq)
+    q.qlora_loftq_init(W0, wq, omega, kq, r, 2, Aq, Bq, q.BF16, wsq, wsq_b)
+    torch.cuda.synchronize()
+    tq0 = time.perf_counter()
+    for _ in range(reps):
+        q.qlora_loftq_init(W0, wq, omega, kq, r, 2, Aq, Bq, q.BF16, wsq, wsq_b)
+    return {"ms": round((time.perf_counter() - tq0) * 1e3 / reps, 3), "rank": r,
+            "probe_columns": kq, "power_iterations": 2,
+            "what": f"A, B from a rank-{r} SVD of W0 - deq(Wq) (6 GPU residual products, panels "
+                    "orthonormalised on the GPU, host k x k work)"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -719,9 +747,14 @@ def main():
     from quantized_rank_fine_amd import qlora as q
     from quantized_rank_fine_amd import synth, workloads
 
-    if args.only in ("cfg3", "cfg4", "decode"):
+    if args.only in ("cfg3", "cfg4", "decode", "loftq"):
         torch.cuda.set_device(0)
-        if args.only == "cfg3":
+        if args.only == "loftq":
+            wl = workloads.WORKLOADS[1]
+            _, n_in, n_out = wl["linears"][0]
+            W0 = torch.from_numpy(synth.weights(n_in, n_out, 1)).to("cuda:0")
+            rep = loftq_report(W0, q.NF4Weight(n_in, n_out, W0.device), wl["rank"], reps=10)
+        elif args.only == "cfg3":
             rep = cfg3_report(args.steps, args.warmup)
         elif args.only == "cfg4":
             rep = cfg4_report(args.cfg4_layers, args.steps, args.warmup)
@@ -952,25 +985,7 @@ def main():
             "fused_into_backward": adam_fused}
     del opt
 
-    # LoftQ-style start of A and B (rank 16, 24 probe columns, 2 power
-    # iterations): a synchronous call, timed on the host clock.
-    kq = 24
-    gq = torch.Generator(device="cpu").manual_seed(7)
-    omega = torch.randn(n_out, kq, generator=gq).to(dev)
-    Aq = torch.empty(n_in, r, dtype=torch.bfloat16, device=dev)
-    Bq = torch.empty(r, n_out, dtype=torch.bfloat16, device=dev)
-    wsq_b = q.qlora_loftq_workspace_bytes(n_in, n_out, kq)
-    wsq = torch.empty(wsq_b, dtype=torch.uint8, device=dev)
-    q.qlora_quantize(W0s[0], wq)
-    q.qlora_loftq_init(W0s[0], wq, omega, kq, r, 2, Aq, Bq, q.BF16, wsq, wsq_b)
-    torch.cuda.synchronize()
-    tq0 = time.perf_counter()
-    for _ in range(3):
-        q.qlora_loftq_init(W0s[0], wq, omega, kq, r, 2, Aq, Bq, q.BF16, wsq, wsq_b)
-    loftq = {"ms": round((time.perf_counter() - tq0) * 1e3 / 3, 2), "rank": r, "probe_columns": kq,
-             "power_iterations": 2,
-             "what": "A, B from a rank-16 SVD of W0 - deq(Wq) (6 GPU residual products + host k x k work)"}
-    del wsq
+    loftq = loftq_report(W0s[0], wq, r)
 
     ms_per_step = (t1 - t0) * 1e3 / K
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)

@@ -233,9 +233,25 @@ struct Levels16 {
 // Products with the quantization residual R = W0 - deq(Wq) (formed on the
 // fly in fp32): transpose = false: Y [in x k] = R . M (M [out x k]);
 // transpose = true: Y [out x k] = R^T . M (M [in x k]); 1 <= k <= 128.
+// `partial` holds the slices' partial products:
+// residual_mul_partial_bytes(in, out, k) bytes.
+size_t residual_mul_partial_bytes(int64_t in, int64_t out, int k);
 hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8_t *q8,
                                const float *s2, int64_t in, int64_t out, const float *M, int k,
-                               float *Y, bool transpose, int codebook, hipStream_t s);
+                               float *Y, bool transpose, int codebook, float *partial,
+                               hipStream_t s);
+
+// Thin-panel products for the orthonormalisation and the final factors, fp64
+// arithmetic on fp32 panels (ka, kb, k, m <= 128):
+// G [ka x kb] (fp64) = X^T . Y for X [rows x ka], Y [rows x kb] (`partial`:
+// panel_gram_partial_bytes(max(ka, kb)) bytes);
+// Out = X . T for X [rows x k] and T [k x m] fp64, rounded to fp32 (then to
+// bf16 when `bf16`), Out [rows x m] or, `transposed`, [m x rows].
+size_t panel_gram_partial_bytes(int k);
+hipError_t launch_panel_gram(const float *X, int ka, const float *Y, int kb, int64_t rows,
+                             double *G, double *partial, hipStream_t s);
+hipError_t launch_panel_apply(const float *X, int k, const double *T, int m, int64_t rows,
+                              void *Out, bool transposed, bool bf16, hipStream_t s);
 
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }

@@ -8,12 +8,18 @@
 // Martinsson & Tropp, "Finding structure with randomness": a range finder
 // from the caller's random test matrix, power iterations with
 // re-orthonormalisation, then the SVD of the small projected matrix):
-//   Q = orth(R . Omega);  repeat: Q = orth(R . orth(R^T . Q));
-//   Z = R^T . Q  (so R ~ Q Z^T);  Z = Qz Rz;  Rz^T = U~ S W~^T;
-//   R ~ (Q U~) S (Qz W~)^T;  A = (Q U~)_r sqrt(S_r),  B = sqrt(S_r) (Qz W~)_r^T.
-// The two large products run on the GPU (residual formed on the fly, fp32);
-// the k x k and (rows x k) orthonormalisations and the small SVD (one-sided
-// Jacobi rotations) run on the host in double.  The call is synchronous.
+//   Y = orth(R . Omega);  repeat: Z = orth(R^T . Y), Y = orth(R . Z);
+//   Z = R^T . Y  (so R ~ Y Z^T);  Qz = orth(Z), Rz = Qz^T Z;  Rz^T = U~ S W~^T;
+//   R ~ (Y U~) S (Qz W~)^T;  A = (Y U~)_r sqrt(S_r),  B = sqrt(S_r) (Qz W~)_r^T.
+// orth is Cholesky QR applied twice (Fukaya, Nakatsukasa, Yanagisawa &
+// Yamamoto, "CholeskyQR2: a simple and communication-avoiding algorithm for
+// computing a tall-skinny QR factorization"): G = X^T X, G = C^T C with C
+// upper triangular, X <- X C^-1; the second pass restores the orthogonality
+// the first loses to rounding.  The panels stay on the GPU in fp32; the GPU
+// forms the residual products, the Gram matrices and every panel update (in
+// fp64 arithmetic).  The host does O(k^3) work only: the k x k Cholesky
+// factor and its inverse, and the k x k SVD (one-sided Jacobi rotations), in
+// double.  The call is synchronous.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -28,41 +34,40 @@ namespace {
 
 using Mat = std::vector<double>;   // row-major
 
-// Orthonormal columns of X (rows x k) by modified Gram-Schmidt, applied
-// twice; a column that vanishes becomes zero.
-// (The columns are copied out contiguously first, so every pass streams.)
-void orthonormalize(Mat &X, int64_t rows, int k) {
-  Mat C(X.size());
-  for (int64_t i = 0; i < rows; ++i)
-    for (int j = 0; j < k; ++j) C[j * rows + i] = X[i * k + j];
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int j = 0; j < k; ++j) {
-      double *cj = C.data() + j * rows;
-      for (int p = 0; p < j; ++p) {
-        const double *cp = C.data() + p * rows;
-        double d = 0.0;
-        for (int64_t i = 0; i < rows; ++i) d += cp[i] * cj[i];
-        for (int64_t i = 0; i < rows; ++i) cj[i] -= d * cp[i];
-      }
-      double n2 = 0.0;
-      for (int64_t i = 0; i < rows; ++i) n2 += cj[i] * cj[i];
-      const double inv = n2 > 1e-300 ? 1.0 / std::sqrt(n2) : 0.0;
-      for (int64_t i = 0; i < rows; ++i) cj[i] *= inv;
+// T = C^-1 for the upper-triangular Cholesky factor C of the k x k Gram
+// matrix G (G = C^T C).  A column whose remaining squared length falls to
+// 1e-12 of its own (or to nothing) depends on the columns before it: its row
+// of C and its column of T are zero, so it leaves the panel as a zero
+// column, as it would from Gram-Schmidt.
+void cholesky_inverse(const Mat &G, int k, Mat &T) {
+  Mat C(size_t(k) * k, 0.0);
+  std::vector<char> live(k, 0);
+  for (int j = 0; j < k; ++j) {
+    double d = G[j * k + j];
+    for (int p = 0; p < j; ++p) d -= C[p * k + j] * C[p * k + j];
+    const double own = G[j * k + j];
+    if (!(own > 1e-300) || !(d > 1e-12 * own)) continue;
+    live[j] = 1;
+    const double cjj = std::sqrt(d);
+    C[j * k + j] = cjj;
+    for (int l = j + 1; l < k; ++l) {
+      double v = G[j * k + l];
+      for (int p = 0; p < j; ++p) v -= C[p * k + j] * C[p * k + l];
+      C[j * k + l] = v / cjj;
     }
   }
-  for (int64_t i = 0; i < rows; ++i)
-    for (int j = 0; j < k; ++j) X[i * k + j] = C[j * rows + i];
-}
-
-// C (k x k) = Q^T X for Q, X (rows x k).
-Mat gram(const Mat &Q, const Mat &X, int64_t rows, int k) {
-  Mat C(size_t(k) * k, 0.0);
-  for (int64_t i = 0; i < rows; ++i)
-    for (int a = 0; a < k; ++a) {
-      const double q = Q[i * k + a];
-      for (int b = 0; b < k; ++b) C[a * k + b] += q * X[i * k + b];
+  // back substitution, one column of T at a time: C T = I on the live set
+  T.assign(size_t(k) * k, 0.0);
+  for (int j = 0; j < k; ++j) {
+    if (!live[j]) continue;
+    T[j * k + j] = 1.0 / C[j * k + j];
+    for (int i = j - 1; i >= 0; --i) {
+      if (!live[i]) continue;
+      double v = 0.0;
+      for (int p = i + 1; p <= j; ++p) v += C[i * k + p] * T[p * k + j];
+      T[i * k + j] = -v / C[i * k + i];
     }
-  return C;
+  }
 }
 
 // One-sided Jacobi SVD of a square k x k matrix G: rotate column pairs until
@@ -105,33 +110,57 @@ void jacobi_svd(Mat &G, Mat &V, std::vector<double> &S, int k) {
   }
 }
 
-struct Residual {
+// Device panels and the small host buffers of one call.
+struct Ctx {
   const float *W0;
   const qlora_nf4 *wq;
-  float *dM, *dY;      // device [max(in, out) x k] each
-  int k;
+  double *dG, *dT;     // device [k x k] Gram matrix, [2 k x k] transforms
+  float *rpart;        // device partial products of the residual products
+  double *gpart;       // device partial Gram matrices
+  Mat hG, hT;
   hipStream_t s;
 };
 
-// Y = R . M (transpose = false; M rows = out, Y rows = in) or R^T . M.
-hipError_t residual_product(const Residual &r, const Mat &M, Mat &Y, bool transpose) {
-  const int64_t in = r.wq->in, out = r.wq->out;
-  const int64_t mrows = transpose ? in : out, yrows = transpose ? out : in;
-  std::vector<float> mf(M.begin(), M.end());
-  hipError_t e = hipMemcpyAsync(r.dM, mf.data(), sizeof(float) * mf.size(),
-                                hipMemcpyHostToDevice, r.s);
-  if (e != hipSuccess) return e;
-  e = launch_residual_mul(r.W0, r.wq->codes, r.wq->qscale, r.wq->gscale, in, out, r.dM, r.k,
-                          r.dY, transpose, r.wq->codebook, r.s);
-  if (e != hipSuccess) return e;
-  std::vector<float> yf(size_t(yrows) * r.k);
-  e = hipMemcpyAsync(yf.data(), r.dY, sizeof(float) * yf.size(), hipMemcpyDeviceToHost, r.s);
-  if (e != hipSuccess) return e;
-  e = hipStreamSynchronize(r.s);
-  (void)mrows;
-  Y.assign(yf.begin(), yf.end());
-  return e;
+// Y = R . M (M [out x k] -> Y [in x k]) or, transposed, R^T . M.
+hipError_t residual_product(const Ctx &c, const float *M, int k, float *Y, bool transpose) {
+  return launch_residual_mul(c.W0, c.wq->codes, c.wq->qscale, c.wq->gscale, c.wq->in, c.wq->out,
+                             M, k, Y, transpose, c.wq->codebook, c.rpart, c.s);
 }
+
+// H [ka x kb] on the host = X^T . Y (device panels [rows x ka], [rows x kb]).
+hipError_t gram_to_host(Ctx &c, const float *X, int ka, const float *Y, int kb, int64_t rows,
+                        Mat &H) {
+  hipError_t e = launch_panel_gram(X, ka, Y, kb, rows, c.dG, c.gpart, c.s);
+  if (e != hipSuccess) return e;
+  H.assign(size_t(ka) * kb, 0.0);
+  e = hipMemcpyAsync(H.data(), c.dG, sizeof(double) * H.size(), hipMemcpyDeviceToHost, c.s);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(c.s);
+}
+
+// Orthonormal columns of the device panel X [rows x k] (Cholesky QR, twice);
+// Xt is a panel of the same size used in between.  The result is in X.
+hipError_t orthonormalize(Ctx &c, float *X, float *Xt, int64_t rows, int k) {
+  float *src = X, *dst = Xt;
+  for (int pass = 0; pass < 2; ++pass) {
+    hipError_t e = gram_to_host(c, src, k, src, k, rows, c.hG);
+    if (e != hipSuccess) return e;
+    cholesky_inverse(c.hG, k, c.hT);
+    // (the host buffer is rewritten only after the next synchronisation,
+    // which follows this copy on the stream)
+    e = hipMemcpyAsync(c.dT, c.hT.data(), sizeof(double) * c.hT.size(), hipMemcpyHostToDevice,
+                       c.s);
+    if (e != hipSuccess) return e;
+    e = launch_panel_apply(src, k, c.dT, k, rows, dst, false, false, c.s);
+    if (e != hipSuccess) return e;
+    std::swap(src, dst);
+  }
+  return hipSuccess;
+}
+
+size_t panel_bytes(int64_t rows, int k) { return (size_t(rows) * size_t(k) * 4 + 255) / 256 * 256; }
+size_t small_bytes(int k) { return (size_t(k) * size_t(k) * 8 + 255) / 256 * 256; }
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 }  // namespace qlora
@@ -140,8 +169,10 @@ using namespace qlora;
 
 extern "C" size_t qlora_loftq_workspace_bytes(int64_t in, int64_t out, int32_t k) {
   if (in <= 0 || out <= 0 || k < 1 || k > 128) return 0;
-  const size_t rows = size_t(in > out ? in : out);
-  return 2 * ((rows * size_t(k) * 4 + 255) / 256 * 256);
+  // Y, Y' [in x k]; Z, Qz, Z' [out x k] fp32; G [k x k], T [2 k x k] fp64;
+  // the partial sums of the residual products and of the Gram matrices
+  return 2 * panel_bytes(in, k) + 3 * panel_bytes(out, k) + 3 * small_bytes(k) +
+         align256(residual_mul_partial_bytes(in, out, k)) + align256(panel_gram_partial_bytes(k));
 }
 
 extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, const float *omega,
@@ -165,77 +196,69 @@ extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, c
   if (al & 15u) return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora_loftq_workspace_bytes(wq->in, wq->out, k)) return QLORA_ERR_WORKSPACE;
   const int64_t in = wq->in, out = wq->out;
-  const size_t half = qlora_loftq_workspace_bytes(in, out, k) / 2;
-  Residual res{W0, wq, static_cast<float *>(ws),
-               reinterpret_cast<float *>(static_cast<char *>(ws) + half), k, stream};
-
-  // range finder from the caller's test matrix
-  std::vector<float> om(size_t(out) * k);
-  if (hipMemcpyAsync(om.data(), omega, sizeof(float) * om.size(), hipMemcpyDeviceToHost, stream) !=
-          hipSuccess ||
-      hipStreamSynchronize(stream) != hipSuccess)
-    return QLORA_ERR_DEVICE;
-  Mat M(om.begin(), om.end()), Y, Z;
-  if (residual_product(res, M, Y, false) != hipSuccess) return QLORA_ERR_DEVICE;
-  orthonormalize(Y, in, k);
-  for (int it = 0; it < iters; ++it) {
-    if (residual_product(res, Y, Z, true) != hipSuccess) return QLORA_ERR_DEVICE;
-    orthonormalize(Z, out, k);
-    if (residual_product(res, Z, Y, false) != hipSuccess) return QLORA_ERR_DEVICE;
-    orthonormalize(Y, in, k);
-  }
-  // R ~ Y Z^T with Z = R^T Y
-  if (residual_product(res, Y, Z, true) != hipSuccess) return QLORA_ERR_DEVICE;
-  Mat Qz = Z;
-  orthonormalize(Qz, out, k);
-  const Mat Rz = gram(Qz, Z, out, k);                  // Z = Qz Rz
-  Mat G(size_t(k) * k);                                 // G = Rz^T
-  for (int a = 0; a < k; ++a)
-    for (int b = 0; b < k; ++b) G[a * k + b] = Rz[b * k + a];
-  Mat W;
-  std::vector<double> S;
-  jacobi_svd(G, W, S, k);                               // G W = U~ S
-  std::vector<int> ord(k);
-  for (int j = 0; j < k; ++j) ord[j] = j;
-  std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return S[x] > S[y]; });
-
-  // A = (Y U~)_r sqrt(S_r), B = sqrt(S_r) (Qz W~)_r^T
-  std::vector<float> af(size_t(in) * r), bf(size_t(r) * out);
-  for (int c = 0; c < r; ++c) {
-    const int j = ord[c];
-    const double sj = S[j], sq = std::sqrt(sj);
-    for (int64_t i = 0; i < in; ++i) {
-      double u = 0.0;
-      if (sj > 0)
-        for (int a = 0; a < k; ++a) u += Y[i * k + a] * G[a * k + j] / sj;
-      af[i * r + c] = float(u * sq);
+  char *p = static_cast<char *>(ws);
+  auto take = [&](size_t bytes) {
+    char *q = p;
+    p += bytes;
+    return q;
+  };
+  float *Y = reinterpret_cast<float *>(take(panel_bytes(in, k)));
+  float *Yt = reinterpret_cast<float *>(take(panel_bytes(in, k)));
+  float *Z = reinterpret_cast<float *>(take(panel_bytes(out, k)));
+  float *Qz = reinterpret_cast<float *>(take(panel_bytes(out, k)));
+  float *Zt = reinterpret_cast<float *>(take(panel_bytes(out, k)));
+  double *dG = reinterpret_cast<double *>(take(small_bytes(k)));
+  double *dT = reinterpret_cast<double *>(take(2 * small_bytes(k)));
+  float *rpart = reinterpret_cast<float *>(take(align256(residual_mul_partial_bytes(in, out, k))));
+  double *gpart = reinterpret_cast<double *>(take(align256(panel_gram_partial_bytes(k))));
+  Ctx c{W0, wq, dG, dT, rpart, gpart, {}, {}, stream};
+  auto run = [&]() -> hipError_t {
+    hipError_t e;
+#define QLORA_TRY(x)              \
+  if ((e = (x)) != hipSuccess) return e
+    // range finder from the caller's test matrix, then the power iterations
+    QLORA_TRY(residual_product(c, omega, k, Y, false));
+    QLORA_TRY(orthonormalize(c, Y, Yt, in, k));
+    for (int it = 0; it < iters; ++it) {
+      QLORA_TRY(residual_product(c, Y, k, Z, true));
+      QLORA_TRY(orthonormalize(c, Z, Zt, out, k));
+      QLORA_TRY(residual_product(c, Z, k, Y, false));
+      QLORA_TRY(orthonormalize(c, Y, Yt, in, k));
     }
-    for (int64_t n = 0; n < out; ++n) {
-      double v = 0.0;
-      for (int a = 0; a < k; ++a) v += Qz[n * k + a] * W[a * k + j];
-      bf[size_t(c) * out + n] = float(v * sq);
+    // R ~ Y Z^T with Z = R^T Y;  Z = Qz Rz
+    QLORA_TRY(residual_product(c, Y, k, Z, true));
+    QLORA_TRY(hipMemcpyAsync(Qz, Z, sizeof(float) * size_t(out) * k, hipMemcpyDeviceToDevice,
+                             stream));
+    QLORA_TRY(orthonormalize(c, Qz, Zt, out, k));
+    Mat Rz;
+    QLORA_TRY(gram_to_host(c, Qz, k, Z, k, out, Rz));
+    Mat G(size_t(k) * k);                                 // G = Rz^T
+    for (int a = 0; a < k; ++a)
+      for (int b = 0; b < k; ++b) G[a * k + b] = Rz[b * k + a];
+    Mat W;
+    std::vector<double> S;
+    jacobi_svd(G, W, S, k);                               // G W = U~ S
+    std::vector<int> ord(k);
+    for (int j = 0; j < k; ++j) ord[j] = j;
+    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return S[x] > S[y]; });
+    // A = Y Pa, B^T = Qz Pb with Pa = (U~)_r sqrt(S_r), Pb = (W~)_r sqrt(S_r)
+    Mat P(size_t(2) * k * r, 0.0);
+    double *Pa = P.data(), *Pb = P.data() + size_t(k) * r;
+    for (int cc = 0; cc < r; ++cc) {
+      const int j = ord[cc];
+      const double sj = S[j], sq = std::sqrt(sj);
+      for (int a = 0; a < k; ++a) {
+        Pa[a * r + cc] = sj > 0 ? G[a * k + j] / sq : 0.0;
+        Pb[a * r + cc] = W[a * k + j] * sq;
+      }
     }
-  }
-  hipError_t e = hipSuccess;
-  if (adt == QLORA_F32) {
-    e = hipMemcpyAsync(A, af.data(), sizeof(float) * af.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(B, bf.data(), sizeof(float) * bf.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  } else {
-    auto to16 = [](float f) {
-      uint32_t u;
-      std::memcpy(&u, &f, 4);
-      u += 0x7fffu + ((u >> 16) & 1u);
-      return uint16_t(u >> 16);
-    };
-    std::vector<uint16_t> a16(af.size()), b16(bf.size());
-    for (size_t i = 0; i < af.size(); ++i) a16[i] = to16(af[i]);
-    for (size_t i = 0; i < bf.size(); ++i) b16[i] = to16(bf[i]);
-    e = hipMemcpyAsync(A, a16.data(), 2 * a16.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(B, b16.data(), 2 * b16.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  }
-  return e == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE;
+    QLORA_TRY(hipMemcpyAsync(c.dT, P.data(), sizeof(double) * P.size(), hipMemcpyHostToDevice,
+                             stream));
+    const bool b16 = adt == QLORA_BF16;
+    QLORA_TRY(launch_panel_apply(Y, k, c.dT, r, in, A, false, b16, stream));
+    QLORA_TRY(launch_panel_apply(Qz, k, c.dT + size_t(k) * r, r, out, B, true, b16, stream));
+    return hipStreamSynchronize(stream);   // (P is read by the copy above)
+#undef QLORA_TRY
+  };
+  return run() == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE;
 }

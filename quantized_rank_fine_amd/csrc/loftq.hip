@@ -8,13 +8,18 @@
 //   Y = R . M   (M [out x k], Y [in x k])   and   Z = R^T . Q   (Q [in x k]),
 // k <= 128 columns.  R is never stored: each tile of it is formed in fp32
 // (W0 minus L[code] * (q_b * s2_g), the value the fused GEMMs round to bf16)
-// and multiplied with fp32 multiply-adds.
+// and multiplied with fp32 multiply-adds.  The thin panels between the
+// products are orthonormalised here as well (Cholesky QR applied twice: the
+// k x k Gram matrix and the panel update run on the GPU in fp64 arithmetic),
+// and the final factors are formed from them.
 #include "device.h"
 
 namespace qlora {
 namespace {
 
 constexpr int kMaxK = 128;
+constexpr int64_t kMaxSlices = 16;   // slices of a residual product's summed axis
+constexpr int64_t kGramSlabs = 64;   // workgroups (partial sums) of a Gram matrix
 
 struct ResidualArgs {
   const float *W0;
@@ -24,7 +29,8 @@ struct ResidualArgs {
   int64_t in, out;
   const float *M;     // rmul: [out x k]; rtmul: [in x k]
   int k;
-  float *Y;           // rmul: [in x k]; rtmul: [out x k]
+  float *Y;           // rmul: [in x k]; rtmul: [out x k]; one such block per slice
+  int64_t span;       // length of a slice of the summed axis (a multiple of the chunk)
 };
 
 // 16 consecutive residual elements of row `row`, columns col .. col + 15
@@ -48,161 +54,422 @@ __device__ __forceinline__ void residual16(const ResidualArgs &a, const float *L
   }
 }
 
-// Y = R . M.  Workgroup = 16 rows of R; the out axis in chunks of 256
-// columns (fewer for wide k, to keep the M tile small).  A thread forms 16
-// consecutive residual elements of one row (row t / 16, columns 16 (t % 16)
-// ..) and loads its share of the chunk's rows of M; the next chunk's loads are issued into registers before
-// the current chunk is multiplied, so HBM streams while the FMAs run.
-// Thread t accumulates row t / 16, output columns t % 16 + 16 m, m < KB.
-template <int KB>
-__global__ __launch_bounds__(256) void rmul_kernel(ResidualArgs a, Levels16 lv) {
-  constexpr int CH = KB <= 2 ? 256 : (KB == 4 ? 128 : 64);   // columns of R per chunk
-  constexpr int KP = 16 * KB;                   // output columns held (k <= KP)
+// Y = R . M on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, products and
+// sums in fp32).  Workgroup = 4 wavefronts = 128 rows of R and one slice of
+// the out axis (blockIdx.y; its partial product goes to block blockIdx.y of
+// Y), walked in chunks of 64 columns.  Lane l of a wavefront forms the 32
+// residual elements of row l % 32, columns c0 + 32 (l / 32) .. + 31 (one
+// 128-B line of W0, one 64-block), and feeds them as the A operand, one per
+// step s: the two k slots of a step are columns c0 + s and c0 + 32 + s.  The
+// B operand (the matching rows of M, staged in LDS per chunk and shared by
+// the four wavefronts) gives output columns 32 t + l % 32 of tile t < KT.
+// The next chunk's loads are in flight while the current one is multiplied.
+template <int KT>
+__global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16 lv) {
+  constexpr int KP = 32 * KT;
   __shared__ float sL[16];
-  __shared__ __align__(16) float sR[16][CH + 4];
-  __shared__ __align__(16) float sM[CH][KP + 4];
-  const int t = threadIdx.x;
-  const int64_t r0 = int64_t(blockIdx.x) * 16;
+  __shared__ __align__(16) float sM[64][KP + 1];   // (+1: the two half-waves' rows on other banks)
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5;
+  const int64_t row = int64_t(blockIdx.x) * 128 + 32 * w + (l & 31);
+  const bool live = row < a.in;                 // in % 64 == 0: whole wavefronts
   if (t < 16) sL[t] = lv.L[t];
-  __syncthreads();
-  const int i = t >> 4, jl = t & 15;
-  float acc[KB];
+  const int64_t nb = int64_t(blockIdx.y) * a.span, ne = min64(a.out, nb + a.span);
+  // the chunk's M rows: thread t stages (row e / KP, column e % KP) for
+  // e = t + 256 u (columns >= k are zero)
+  constexpr int MPER = 64 * KP / 256;
+  float mv[MPER];
+  f32x4_t wv[8];
+  u32x4_t cv;
+  float cs = 0.0f;
+  auto load = [&](int64_t c0) {
+    if (live) {
+      const int64_t flat = row * a.out + c0 + 32 * h;
+      const f32x4_t *src = reinterpret_cast<const f32x4_t *>(a.W0 + flat);
 #pragma unroll
-  for (int m = 0; m < KB; ++m) acc[m] = 0.0f;
-  // M rows of a chunk: thread t loads element (n, j) = (t / KP' ...) in a
-  // strided loop (k may be below KP: columns j >= k are zero)
-  constexpr int MPER = CH * KP / 256;           // M elements per thread per chunk
-  float rv[16], mv[MPER];
-  // (the last chunk may run past out, a multiple of 64: those columns of R
-  // and rows of M are zero and nothing past out is read)
-  auto load = [&](int64_t n0) {
-    if (16 * jl < CH && n0 + 16 * jl < a.out) {
-      residual16(a, sL, r0 + i, n0 + 16 * jl, rv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) rv[e] = 0.0f;
+      for (int q = 0; q < 8; ++q) wv[q] = src[q];
+      cv = *reinterpret_cast<const u32x4_t *>(a.codes + flat / 2);
+      const int64_t blk = flat / 64;
+      cs = float(a.q8[blk]) * a.s2[blk >> 8];
     }
 #pragma unroll
     for (int u = 0; u < MPER; ++u) {
       const int e = t + 256 * u, n = e / KP, j = e - n * KP;
-      mv[u] = (j < a.k && n0 + n < a.out) ? a.M[(n0 + n) * a.k + j] : 0.0f;
+      mv[u] = (j < a.k && c0 + n < a.out) ? a.M[(c0 + n) * a.k + j] : 0.0f;
     }
   };
-  load(0);
-  for (int64_t n0 = 0; n0 < a.out; n0 += CH) {
-    __syncthreads();                            // the previous chunk's reads are done
-    if (16 * jl < CH) {
+  f32x16_t acc[KT];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sR[i][16 * jl + e] = rv[e];
-    }
+  for (int q = 0; q < KT; ++q)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[q][e] = 0.0f;
+  load(nb);
+  for (int64_t c0 = nb; c0 < ne; c0 += 64) {
+    __syncthreads();                            // the previous chunk's reads are done
 #pragma unroll
     for (int u = 0; u < MPER; ++u) {
       const int e = t + 256 * u, n = e / KP, j = e - n * KP;
       sM[n][j] = mv[u];
     }
-    __syncthreads();
-    if (n0 + CH < a.out) load(n0 + CH);         // in flight during the FMAs
-#pragma unroll 8
-    for (int n = 0; n < CH; ++n) {
-      const float r = sR[i][n];
+    float rv[32];
 #pragma unroll
-      for (int m = 0; m < KB; ++m) acc[m] = __builtin_fmaf(r, sM[n][16 * m + jl], acc[m]);
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t code = (cv[e >> 3] >> (4 * (e & 7))) & 15u;
+      rv[e] = wv[e >> 2][e & 3] - sL[code] * cs;
     }
-  }
+    __syncthreads();
+    if (c0 + 64 < ne) load(c0 + 64);            // in flight during the products
 #pragma unroll
-  for (int m = 0; m < KB; ++m)
-    if (16 * m + jl < a.k) a.Y[(r0 + i) * a.k + 16 * m + jl] = acc[m];
+    for (int st = 0; st < 32; ++st)
+#pragma unroll
+      for (int q = 0; q < KT; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(rv[st], sM[32 * h + st][32 * q + (l & 31)],
+                                                      acc[q], 0, 0, 0);
+  }
+  if (!live) return;
+  // register e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4 of the
+  // wavefront's 32, column 32 q + l % 32
+  float *Y = a.Y + int64_t(blockIdx.y) * a.in * a.k;
+  const int64_t rb = int64_t(blockIdx.x) * 128 + 32 * w;
+#pragma unroll
+  for (int q = 0; q < KT; ++q) {
+    const int j = 32 * q + (l & 31);
+    if (j >= a.k) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      Y[(rb + 8 * (e >> 2) + 4 * h + (e & 3)) * a.k + j] = acc[q][e];
+  }
 }
 
-// Z = R^T . Q.  Workgroup = 32 columns of R; the in axis in chunks of 128
-// rows.  Thread t forms 16 residual elements of row t / 2, columns
-// 16 (t % 2) .. (a whole 128-B line of W0 per thread pair) and loads its
-// share of the chunk's Q rows; the next chunk is loaded into registers while
-// the current one is multiplied.  Thread t accumulates column t % 32,
-// output ranks t / 32 + 8 m, m < KB.
-template <int KB>
-__global__ __launch_bounds__(256) void rtmul_kernel(ResidualArgs a, Levels16 lv) {
-  constexpr int CH = KB <= 8 ? 128 : 64;        // rows of R per chunk
-  constexpr int KP = 8 * KB;
+// Z = R^T . Q on the fp32 matrix cores.  Output rows are columns of R:
+// tile p < NQ of a wavefront holds the columns c0 + NQ m + p, m < 32, so a
+// lane loads NQ consecutive elements of a row of R at once; output columns
+// are 32 t + l % 32 for tiles t < KT.  Step s multiplies rows i0 + 2 s and
+// i0 + 2 s + 1 (lane l takes row i0 + 2 s + l / 32 as its k slot); the B
+// operand (the matching rows of Q) is the same for all NQ tiles.
+// Workgroup = 4 wavefronts on the same 32 NQ columns, each over a quarter of
+// the workgroup's slice of the in axis (blockIdx.y); their sums are added
+// in wavefront order through LDS, and the slice's partial product goes to
+// block blockIdx.y of Z.  Rows are walked 16 at a time, the next 16 loaded
+// while the current ones are multiplied.
+template <int KT, int NQ>
+__global__ __launch_bounds__(256) void rtmul_mfma_kernel(ResidualArgs a, Levels16 lv) {
   __shared__ float sL[16];
-  __shared__ __align__(16) float sR[CH][32 + 1];
-  __shared__ __align__(16) float sQ[CH][KP + 4];
-  const int t = threadIdx.x;
-  const int64_t c0 = int64_t(blockIdx.x) * 32;
+  __shared__ float sRed[3][KT * NQ * 16][64];
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, m = l & 31;
   if (t < 16) sL[t] = lv.L[t];
   __syncthreads();
-  const int c = t & 31, jg = t >> 5;
-  float acc[KB];
+  const int64_t c = int64_t(blockIdx.x) * 32 * NQ + NQ * m;   // first of the lane's columns
+  const bool live = c < a.out;                                // out % 64 == 0
+  const int64_t sb = int64_t(blockIdx.y) * a.span, se = min64(a.in, sb + a.span);
+  const int64_t q4 = (se - sb + 3) / 4;                        // this wavefront's quarter
+  const int64_t ib = min64(se, sb + w * q4), ie = min64(se, ib + q4);
+  f32x16_t acc[NQ][KT];
 #pragma unroll
-  for (int m = 0; m < KB; ++m) acc[m] = 0.0f;
-  constexpr int QPER = CH * KP / 256;
-  float rv[16], qv[QPER];
-  // (the last chunk may run past in, a multiple of 64: zero rows)
+  for (int p = 0; p < NQ; ++p)
+#pragma unroll
+    for (int q = 0; q < KT; ++q)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[p][q][e] = 0.0f;
+  float wv[8][NQ], bq[8][KT], cs[8];
+  uint32_t cd[8];
   auto load = [&](int64_t i0) {
-    if ((t >> 1) < CH && i0 + (t >> 1) < a.in) {
-      residual16(a, sL, i0 + (t >> 1), c0 + 16 * (t & 1), rv);
-    } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) rv[e] = 0.0f;
-    }
+    for (int st = 0; st < 8; ++st) {
+      const int64_t i = i0 + 2 * st + h;
+      const bool ok = live && i < ie;
+      if (ok) {
+        const int64_t flat = i * a.out + c;
+        if constexpr (NQ == 4) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t *>(a.W0 + flat);
 #pragma unroll
-    for (int u = 0; u < QPER; ++u) {
-      const int e = t + 256 * u, ii = e / KP, j = e - ii * KP;
-      qv[u] = (j < a.k && i0 + ii < a.in) ? a.M[(i0 + ii) * a.k + j] : 0.0f;
+          for (int p = 0; p < 4; ++p) wv[st][p] = v[p];
+          cd[st] = *reinterpret_cast<const uint16_t *>(a.codes + flat / 2);
+        } else if constexpr (NQ == 2) {
+          const float2 v = *reinterpret_cast<const float2 *>(a.W0 + flat);
+          wv[st][0] = v.x;
+          wv[st][1] = v.y;
+          cd[st] = a.codes[flat / 2];
+        } else {
+          wv[st][0] = a.W0[flat];
+          cd[st] = uint32_t(a.codes[flat / 2]) >> (4 * (flat & 1));
+        }
+        const int64_t blk = flat / 64;
+        cs[st] = float(a.q8[blk]) * a.s2[blk >> 8];
+      } else {
+#pragma unroll
+        for (int p = 0; p < NQ; ++p) wv[st][p] = 0.0f;
+        cd[st] = 0;
+        cs[st] = 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < KT; ++q) {
+        const int j = 32 * q + m;
+        bq[st][q] = (i < ie && j < a.k) ? a.M[i * a.k + j] : 0.0f;
+      }
     }
   };
-  load(0);
-  for (int64_t i0 = 0; i0 < a.in; i0 += CH) {
-    __syncthreads();
-    if ((t >> 1) < CH) {
+  if (ib < ie) load(ib);
+  for (int64_t i0 = ib; i0 < ie; i0 += 16) {
+    float rv[8][NQ], bv[8][KT];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sR[t >> 1][16 * (t & 1) + e] = rv[e];
-    }
+    for (int st = 0; st < 8; ++st) {
 #pragma unroll
-    for (int u = 0; u < QPER; ++u) {
-      const int e = t + 256 * u, ii = e / KP, j = e - ii * KP;
-      sQ[ii][j] = qv[u];
+      for (int p = 0; p < NQ; ++p)
+        rv[st][p] = wv[st][p] - sL[(cd[st] >> (4 * p)) & 15u] * cs[st];
+#pragma unroll
+      for (int q = 0; q < KT; ++q) bv[st][q] = bq[st][q];
+    }
+    if (i0 + 16 < ie) load(i0 + 16);            // in flight during the products
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int p = 0; p < NQ; ++p)
+#pragma unroll
+        for (int q = 0; q < KT; ++q)
+          acc[p][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(rv[st][p], bv[st][q], acc[p][q], 0, 0, 0);
+  }
+  // the four quarters, added in wavefront order
+  if (w > 0) {
+#pragma unroll
+    for (int p = 0; p < NQ; ++p)
+#pragma unroll
+      for (int q = 0; q < KT; ++q)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sRed[w - 1][(p * KT + q) * 16 + e][l] = acc[p][q][e];
+  }
+  __syncthreads();
+  if (w > 0) return;
+  // register e of lane l: output row 8 (e / 4) + 4 (l / 32) + e % 4 of the
+  // tile, i.e. column c0 + NQ (that row) + p of R (past out in a last,
+  // half-filled workgroup: not written)
+  float *Z = a.Y + int64_t(blockIdx.y) * a.out * a.k;
+  const int64_t c0 = int64_t(blockIdx.x) * 32 * NQ;
+#pragma unroll
+  for (int p = 0; p < NQ; ++p)
+#pragma unroll
+    for (int q = 0; q < KT; ++q) {
+      const int j = 32 * q + m;
+      if (j >= a.k) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t col = c0 + NQ * (8 * (e >> 2) + 4 * h + (e & 3)) + p;
+        if (col >= a.out) continue;
+        const int slot = (p * KT + q) * 16 + e;
+        const float v = ((acc[p][q][e] + sRed[0][slot][l]) + sRed[1][slot][l]) + sRed[2][slot][l];
+        Z[col * a.k + j] = v;
+      }
+    }
+}
+
+// Y[e] = sum over s of P[s n + e], s in order (the slices' partial products).
+__global__ __launch_bounds__(256) void slice_sum_kernel(const f32x4_t *P, int64_t n4, int S,
+                                                        f32x4_t *Y) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n4) return;
+  f32x4_t p[kMaxSlices];
+#pragma unroll
+  for (int sl = 0; sl < kMaxSlices; ++sl)
+    if (sl < S) p[sl] = P[sl * n4 + e];       // all loads first, then the sum in order
+  f32x4_t v = p[0];
+#pragma unroll
+  for (int sl = 1; sl < kMaxSlices; ++sl)
+    if (sl < S) v += p[sl];
+  Y[e] = v;
+}
+
+// ---- panel kernels of the orthonormalisation (CholeskyQR2) and the final
+// factors: fp32 panels [rows x k], fp64 arithmetic --------------------------
+
+// G [ka x kb] (fp64) = X^T . Y for X [rows x ka], Y [rows x kb] fp32, in
+// two passes.  Pass 1: workgroup w takes the 32-row slabs w, w + W, ... of
+// both panels through LDS; thread t owns the entries e = t + 256 u of G
+// (row-major) and sums their products over its slabs in fp64, in row order;
+// the W partial matrices go to P.  Pass 2 adds them in workgroup order, so the
+// result does not depend on timing.
+template <int NE>
+__global__ __launch_bounds__(256) void panel_gram_kernel(const float *X, int ka, const float *Y,
+                                                         int kb, int64_t rows, double *P) {
+  __shared__ float sX[32][kMaxK + 1], sY[32][kMaxK + 1];
+  const int t = threadIdx.x, n = ka * kb;
+  double acc[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) acc[u] = 0.0;
+  for (int64_t r0 = int64_t(blockIdx.x) * 32; r0 < rows; r0 += int64_t(gridDim.x) * 32) {
+    __syncthreads();                              // the previous slab's reads are done
+    for (int e = t; e < 32 * ka; e += 256) {
+      const int i = e / ka, a = e - i * ka;
+      sX[i][a] = r0 + i < rows ? X[(r0 + i) * ka + a] : 0.0f;
+    }
+    for (int e = t; e < 32 * kb; e += 256) {
+      const int i = e / kb, b = e - i * kb;
+      sY[i][b] = r0 + i < rows ? Y[(r0 + i) * kb + b] : 0.0f;
     }
     __syncthreads();
-    if (i0 + CH < a.in) load(i0 + CH);
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = t + 256 * u;
+      if (e < n) {
+        const int a = e / kb, b = e - a * kb;
+        double v = acc[u];
 #pragma unroll 8
-    for (int ii = 0; ii < CH; ++ii) {
-      const float r = sR[ii][c];
-#pragma unroll
-      for (int m = 0; m < KB; ++m) acc[m] = __builtin_fmaf(r, sQ[ii][jg + 8 * m], acc[m]);
+        for (int i = 0; i < 32; ++i) v = __builtin_fma(double(sX[i][a]), double(sY[i][b]), v);
+        acc[u] = v;
+      }
     }
   }
 #pragma unroll
-  for (int m = 0; m < KB; ++m)
-    if (jg + 8 * m < a.k) a.Y[(c0 + c) * a.k + jg + 8 * m] = acc[m];
+  for (int u = 0; u < NE; ++u) {
+    const int e = t + 256 * u;
+    if (e < n) P[int64_t(blockIdx.x) * n + e] = acc[u];
+  }
+}
+
+__global__ __launch_bounds__(256) void gram_sum_kernel(const double *P, int W, int n, double *G) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  double v = 0.0;
+  for (int w0 = 0; w0 < W; w0 += 16) {
+    double p[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (w0 + u < W) p[u] = P[int64_t(w0 + u) * n + e];   // loads first, then the sum in order
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (w0 + u < W) v = (w0 + u == 0) ? p[u] : v + p[u];
+  }
+  G[e] = v;
+}
+
+// Out = X . T for X [rows x k] fp32 and T [k x m] fp64 (m <= 128), products
+// summed in fp64 and rounded once to fp32 (and then, for bf16 output, from
+// that fp32 value to bf16, nearest even).  Out is [rows x m], or [m x rows]
+// when `transposed`.  Workgroup = 32 rows x 32 columns of Out, both operand
+// tiles staged in LDS; thread t computes column t % 32 of rows t / 32 + 8 j.
+__global__ __launch_bounds__(256) void panel_apply_kernel(const float *X, int k, const double *T,
+                                                          int m, int64_t rows, void *Out,
+                                                          bool transposed, bool bf16) {
+  __shared__ float sX[32][129];
+  __shared__ double sT[128][33];
+  const int t = threadIdx.x;
+  const int64_t i0 = int64_t(blockIdx.x) * 32;
+  const int c0 = 32 * blockIdx.y;
+  for (int e = t; e < 32 * k; e += 256) {
+    const int i = e / k, a = e - i * k;
+    sX[i][a] = i0 + i < rows ? X[(i0 + i) * k + a] : 0.0f;
+  }
+  for (int e = t; e < k * 32; e += 256) {
+    const int a = e >> 5, c = e & 31;
+    sT[a][c] = c0 + c < m ? T[a * m + c0 + c] : 0.0;
+  }
+  __syncthreads();
+  const int c = t & 31;
+  if (c0 + c >= m) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = (t >> 5) + 8 * j;
+    if (i0 + i >= rows) break;
+    double acc = 0.0;
+    for (int a = 0; a < k; ++a) acc = __builtin_fma(double(sX[i][a]), sT[a][c], acc);
+    const float v = float(acc);
+    const int64_t o = transposed ? int64_t(c0 + c) * rows + i0 + i : (i0 + i) * m + c0 + c;
+    if (bf16)
+      static_cast<__bf16 *>(Out)[o] = (__bf16)v;
+    else
+      static_cast<float *>(Out)[o] = v;
+  }
 }
 
 }  // namespace
 
+namespace {
+
+// Slices of the summed axis (each a whole number of chunks of `ch`) so that a
+// product with `base` workgroups launches about 1024.
+int64_t slice_span(int64_t base, int64_t len, int64_t ch) {
+  const int64_t chunks = (len + ch - 1) / ch;
+  int64_t S = (1024 + base - 1) / base;
+  if (S > chunks) S = chunks;
+  if (S > kMaxSlices) S = kMaxSlices;
+  if (S < 1) S = 1;
+  return (chunks + S - 1) / S * ch;
+}
+
+}  // namespace
+
+size_t residual_mul_partial_bytes(int64_t in, int64_t out, int k) {
+  const int64_t rows = in > out ? in : out;
+  return size_t(kMaxSlices) * size_t(rows) * size_t(k) * 4;
+}
+
 hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8_t *q8,
                                const float *s2, int64_t in, int64_t out, const float *M, int k,
-                               float *Y, bool transpose, int codebook, hipStream_t s) {
+                               float *Y, bool transpose, int codebook, float *partial,
+                               hipStream_t s) {
   if (k < 1 || k > kMaxK) return hipErrorInvalidValue;
-  ResidualArgs a{W0, codes, q8, s2, in, out, M, k, Y};
   Levels16 lv;
   const Tables &tb = tables(codebook);
   for (int i = 0; i < 16; ++i) lv.L[i] = tb.L[i];
   // in % 64 == 0 and out % 64 == 0 (checked by the caller): whole 16-row
   // and 32-column workgroups; the kernels zero what a last chunk has past
-  // the end.
+  // the end.  The summed axis is cut into slices whose partial products
+  // are added in slice order.
+  const int kt = k <= 32 ? 1 : (k <= 64 ? 2 : 4);   // 32-column output tiles
+  int64_t span, nrows, base, len;
   if (!transpose) {
-    const dim3 g(unsigned(in / 16));
-    if (k <= 16) hipLaunchKernelGGL(rmul_kernel<1>, g, dim3(256), 0, s, a, lv);
-    else if (k <= 32) hipLaunchKernelGGL(rmul_kernel<2>, g, dim3(256), 0, s, a, lv);
-    else if (k <= 64) hipLaunchKernelGGL(rmul_kernel<4>, g, dim3(256), 0, s, a, lv);
-    else hipLaunchKernelGGL(rmul_kernel<8>, g, dim3(256), 0, s, a, lv);
+    base = (in + 127) / 128, len = out, nrows = in;
+    span = slice_span(4 * base, len, 64);
   } else {
-    const dim3 g(unsigned(out / 32));
-    if (k <= 16) hipLaunchKernelGGL(rtmul_kernel<2>, g, dim3(256), 0, s, a, lv);
-    else if (k <= 32) hipLaunchKernelGGL(rtmul_kernel<4>, g, dim3(256), 0, s, a, lv);
-    else if (k <= 64) hipLaunchKernelGGL(rtmul_kernel<8>, g, dim3(256), 0, s, a, lv);
-    else hipLaunchKernelGGL(rtmul_kernel<16>, g, dim3(256), 0, s, a, lv);
+    const int nq = 4 / kt;                         // columns of R per lane
+    base = (out + 32 * nq - 1) / (32 * nq), len = in, nrows = out;
+    span = slice_span(4 * base, len, 64);
   }
+  const int64_t S = (len + span - 1) / span;
+  ResidualArgs a{W0, codes, q8, s2, in, out, M, k, S > 1 ? partial : Y, span};
+  const dim3 g = dim3(unsigned(base), unsigned(S));
+  if (!transpose) {
+    if (kt == 1) hipLaunchKernelGGL(rmul_mfma_kernel<1>, g, dim3(256), 0, s, a, lv);
+    else if (kt == 2) hipLaunchKernelGGL(rmul_mfma_kernel<2>, g, dim3(256), 0, s, a, lv);
+    else hipLaunchKernelGGL(rmul_mfma_kernel<4>, g, dim3(256), 0, s, a, lv);
+  } else {
+    if (kt == 1) hipLaunchKernelGGL((rtmul_mfma_kernel<1, 4>), g, dim3(256), 0, s, a, lv);
+    else if (kt == 2) hipLaunchKernelGGL((rtmul_mfma_kernel<2, 2>), g, dim3(256), 0, s, a, lv);
+    else hipLaunchKernelGGL((rtmul_mfma_kernel<4, 1>), g, dim3(256), 0, s, a, lv);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t n4 = nrows * k / 4;                // nrows % 64 == 0
+  hipLaunchKernelGGL(slice_sum_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const f32x4_t *>(partial), n4, int(S),
+                     reinterpret_cast<f32x4_t *>(Y));
+  return hipGetLastError();
+}
+
+size_t panel_gram_partial_bytes(int k) { return size_t(kGramSlabs) * size_t(k) * size_t(k) * 8; }
+
+hipError_t launch_panel_gram(const float *X, int ka, const float *Y, int kb, int64_t rows,
+                             double *G, double *partial, hipStream_t s) {
+  if (ka < 1 || kb < 1 || ka > kMaxK || kb > kMaxK || rows < 1) return hipErrorInvalidValue;
+  const int n = ka * kb;
+  int64_t W = (rows + 31) / 32;
+  if (W > kGramSlabs) W = kGramSlabs;
+  const dim3 g = dim3(unsigned(W));
+  if (n <= 256) hipLaunchKernelGGL(panel_gram_kernel<1>, g, dim3(256), 0, s, X, ka, Y, kb, rows, partial);
+  else if (n <= 1024) hipLaunchKernelGGL(panel_gram_kernel<4>, g, dim3(256), 0, s, X, ka, Y, kb, rows, partial);
+  else if (n <= 4096) hipLaunchKernelGGL(panel_gram_kernel<16>, g, dim3(256), 0, s, X, ka, Y, kb, rows, partial);
+  else hipLaunchKernelGGL(panel_gram_kernel<64>, g, dim3(256), 0, s, X, ka, Y, kb, rows, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gram_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, partial,
+                     int(W), n, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_panel_apply(const float *X, int k, const double *T, int m, int64_t rows,
+                              void *Out, bool transposed, bool bf16, hipStream_t s) {
+  if (k < 1 || m < 1 || k > kMaxK || m > kMaxK || rows < 1) return hipErrorInvalidValue;
+  const dim3 g(unsigned((rows + 31) / 32), unsigned((m + 31) / 32));
+  hipLaunchKernelGGL(panel_apply_kernel, g, dim3(256), 0, s, X, k, T, m, rows, Out, transposed,
+                     bf16);
   return hipGetLastError();
 }
 

@@ -33,15 +33,18 @@ def _init(W0, wq, k, r, iters, adt="f32", seed=0):
     return A, B
 
 
-def test_low_rank_residual_is_recovered():
+@pytest.mark.parametrize("n_in,n_out", [(256, 384), (192, 320)])
+def test_low_rank_residual_is_recovered(n_in, n_out):
     """W0 = fp32(deq(Wq)) + P with P of rank 4: the residual is P (up to
-    the fp32 rounding of the dequantized weight) and A B recovers it."""
+    the fp32 rounding of the dequantized weight) and A B recovers it
+    (192 x 320: half-filled last workgroups of both residual products)."""
     torch, dev = torch_dev()
-    w0 = synth.weights(256, 384, workload=7)
+    say(f"[loftq] rank-4 residual {n_in}x{n_out}")
+    w0 = synth.weights(n_in, n_out, workload=7)
     wq = quantize_gpu(w0)
     W_hat = _w_hat(w0)
     g = np.random.default_rng(51)
-    P = (g.standard_normal((256, 4)) @ g.standard_normal((4, 384)) * 0.01).astype(np.float32)
+    P = (g.standard_normal((n_in, 4)) @ g.standard_normal((4, n_out)) * 0.01).astype(np.float32)
     W0 = (W_hat.astype(np.float32) + P).astype(np.float32)
     R = W0.astype(np.float64) - W_hat
     A, B = _init(torch.from_numpy(W0).to(dev), wq, 12, 4, 2)
@@ -49,19 +52,21 @@ def test_low_rank_residual_is_recovered():
     assert np.abs(AB - R).max() <= 1e-4 * np.abs(R).max()
 
 
-@pytest.mark.parametrize("codebook", [q.CB_NF4, q.CB_UNIFORM4])
-def test_quantization_residual_near_optimal(codebook):
-    """On a real quantization residual the rank-16 start removes at least 90 %
-    of what the exact truncated SVD removes, and its factors are balanced."""
+@pytest.mark.parametrize("codebook,k,r,iters", [(q.CB_NF4, 24, 16, 3), (q.CB_UNIFORM4, 24, 16, 3),
+                                                (q.CB_NF4, 96, 64, 4)])
+def test_quantization_residual_near_optimal(codebook, k, r, iters):
+    """On a real quantization residual the rank-r start removes at least 90 %
+    of what the exact truncated SVD removes, and its factors are balanced
+    (k = 96 takes the wide-panel kernels)."""
     torch, dev = torch_dev()
     w0 = synth.weights(512, 768, workload=7)
     wq = quantize_gpu(w0, codebook)
     W_hat = _w_hat(w0, codebook)
     R = oracle.residual(w0, W_hat)
-    say(f"[loftq] 512x768 codebook={codebook}")
-    A, B = _init(torch.from_numpy(w0).to(dev), wq, 24, 16, 3)
+    say(f"[loftq] 512x768 codebook={codebook} k={k} r={r}")
+    A, B = _init(torch.from_numpy(w0).to(dev), wq, k, r, iters)
     An, Bn = A.cpu().numpy().astype(np.float64), B.cpu().numpy().astype(np.float64)
-    Ao, Bo = oracle.loftq_init(w0, W_hat, 16)
+    Ao, Bo = oracle.loftq_init(w0, W_hat, r)
     full = np.sum(R ** 2)
     e_opt = np.sum((R - Ao @ Bo) ** 2)
     e_gpu = np.sum((R - An @ Bn) ** 2)
