@@ -437,7 +437,7 @@ typedef enum {
   QLORA_KERNEL_FWD_GEMM = 2,    /* fused y = X.deq(Wq) + XA.B             */
   QLORA_KERNEL_DY_PASS = 3,     /* G = dY.B^T and dB partials             */
   QLORA_KERNEL_DX_GEMM = 4,     /* fused dX = dY.deq(Wq)^T + G.A^T        */
-  QLORA_KERNEL_DA_PASS = 5,     /* dA partials = X^T.G                    */
+  QLORA_KERNEL_DA_PASS = 5,     /* dA = X^T.G (partials, or whole with dB) */
   QLORA_KERNEL_REDUCE = 6,      /* deterministic reduction of partials    */
   QLORA_KERNEL_FWD_SMALLM = 7,  /* small-M forward                        */
   QLORA_KERNEL_COUNT = 8

@@ -295,14 +295,17 @@ qlora_status linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int6
     return QLORA_OK;
   }
   float *dapart = at<float>(ws, p.off_dapart);
+  // r <= 16: dA is formed whole after the dX GEMM (the last reader of A), in
+  // one launch with the reduction of dB's partials where those are pending;
+  // the bits of dA then do not depend on whether dX is asked for.
+  const bool whole = da_whole(r);
+  auto tail = [&](const float *dbp, int64_t ks) {
+    return launch_bwd_tail(X, xb, G16, p.rp, M, in, r, dA, ta, dbp, ks, out, dB, tb, stream);
+  };
   if (fold) {
-    // dA = X^T . G; dX and the dB partials in the GEMM; dA and dB (stored
-    // [r x out]) in one reduction launch
-    QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
+    // dX and the dB partials in the GEMM; then dA and dB
     QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(xat, dbpart));
-    QLORA_RUN(QLORA_KERNEL_REDUCE,
-              launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0, dbpart, p.ks_bx, out,
-                             dB, true, nullptr, 0, stream, RankMul(), ta, tb));
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, tail(dbpart, p.ks_bx));
     return QLORA_OK;
   }
   if (p.ks_g > 0) {
@@ -311,12 +314,21 @@ qlora_status linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int6
     QLORA_RUN(QLORA_KERNEL_REDUCE,
               launch_reduce2(gpart, p.ks_g, M, r, nullptr, false, G16, p.rp, dbpart, p.ks_b, out,
                              dB, true, nullptr, 0, stream, mul, AdamTarget(), tb));
+    if (whole) {
+      if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
+      QLORA_RUN(QLORA_KERNEL_DA_PASS, tail(nullptr, 0));
+      return QLORA_OK;
+    }
     // dA = X^T . G; dX (the last reader of A); dA
     QLORA_RUN(QLORA_KERNEL_DA_PASS, launch_bwd_x(X, xb, G16, p.rp, M, in, r, dapart, stream));
     if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
     QLORA_RUN(QLORA_KERNEL_REDUCE, launch_reduce2(dapart, p.ks_a, in, r, dA, false, nullptr, 0,
                                                   nullptr, 0, 0, nullptr, false, nullptr, 0,
                                                   stream, RankMul(), ta));
+  } else if (whole) {
+    // G is complete: dX, then dA and dB (stored [r x out]) in one launch
+    if (dX) QLORA_RUN(QLORA_KERNEL_DX_GEMM, dx_gemm(nullptr, nullptr));
+    QLORA_RUN(QLORA_KERNEL_DA_PASS, tail(dbpart, p.ks_b));
   } else {
     // G is complete: dA = X^T . G, dX, then dA and dB (stored [r x out]) in
     // one launch

@@ -585,8 +585,13 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
 #pragma unroll
     for (int s = 0; s < kMaxRT; ++s) acc[c4][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t mm = mb; mm < me; mm += 64) {
-    u32x4_t pv[kNP];
+  // P tile of tokens mm..mm+63 (and, kQFastC, the Q rows mm..mm+63 as 16-B
+  // chunks) into registers; the next slice's loads are issued as soon as the
+  // current slice is in LDS, so they are in flight during its products.
+  constexpr int kNQ = kQFastC ? (64 * (16 * kMaxRT) / 8 + 255) / 256 : 1;
+  const int C8 = RP / 8;
+  u32x4_t pv[kNP], qv[kNQ];
+  auto load_slice = [&](int64_t mm) {
 #pragma unroll
     for (int q = 0; q < kNP; ++q) {
       const int cid = t + 256 * q;
@@ -595,6 +600,19 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
       pv[q] = (m < me && col < K) ? load8_bf16<kPbf16>(P + (m * K + col) * esz)
                                   : u32x4_t{0u, 0u, 0u, 0u};
     }
+    if constexpr (kQFastC) {
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        const int cid = t + 256 * q, mi = cid / C8, c = cid - mi * C8;
+        const int64_t m = mm + mi;
+        qv[q] = (cid < 64 * C8 && m < me && 8 * c < a.ldq)
+                    ? load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (m * a.ldq + 8 * c) * (kQbf16 ? 2 : 4))
+                    : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  if (mb < me) load_slice(mb);
+  for (int64_t mm = mb; mm < me; mm += 64) {
     __syncthreads();                         // previous slice's readers are done
 #pragma unroll
     for (int q = 0; q < kNP; ++q) {
@@ -604,14 +622,10 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
     }
     if constexpr (kQFastC) {
       // Q rows mm..mm+63, columns 0..RP-1, as 16-B chunks into [64][RP]
-      const int C8 = RP / 8;
-      for (int cid = t; cid < 64 * C8; cid += 256) {
-        const int mi = cid / C8, c = cid - mi * C8;
-        const int64_t m = mm + mi;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (m < me && 8 * c < a.ldq)
-          v = load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (m * a.ldq + 8 * c) * (kQbf16 ? 2 : 4));
-        *reinterpret_cast<u32x4_t *>(sQ + mi * RP + 8 * c) = v;
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        const int cid = t + 256 * q, mi = cid / C8, c = cid - mi * C8;
+        if (cid < 64 * C8) *reinterpret_cast<u32x4_t *>(sQ + mi * RP + 8 * c) = qv[q];
       }
     } else {
       // Q^T for tokens mm..mm+63: coalesced element reads of Q rows,
@@ -635,6 +649,7 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
       }
     }
     __syncthreads();
+    if (mm + 64 < me) load_slice(mm + 64);   // in flight during the products
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -787,6 +802,118 @@ __device__ __forceinline__ void reduce_role(const ReduceArgs &a, int64_t wg, int
   }
 }
 
+// ------------------------------------------------------------ dA whole
+//
+// dA [K x R] = P[M x K]^T . Q[M x R] for R <= 16 without token partials (P =
+// X, Q = G16 bf16 [M x ldq], zero beyond R): a workgroup owns 16 columns of P
+// and every token.  The tokens go in 64-token slabs, slab s to wavefront
+// s % 4; a wavefront stages a slab of P (64 x 16) and of Q (64 x 16) in its
+// own LDS area, row-major as loaded, and reads both back transposed as the
+// A and B operands of two v_mfma_f32_16x16x32_bf16.  It keeps the loads of
+// its next kDaGroup slabs in flight while it multiplies the current ones.
+// The four wavefronts' products are summed in wavefront order; every sum is
+// therefore fixed by the shapes alone.  Optionally one Adam step of A from
+// the sums (as in the reduce pass).
+constexpr int kDaPitch = 24;                    // LDS row pitch of a staged slab (elements)
+
+struct DaFullArgs {
+  const void *P;
+  const uint16_t *Q;
+  int64_t ldq, M, K;
+  int R;
+  float *out;          // [K x R] fp32
+  AdamTarget adam;
+};
+
+template <bool kPbf16>
+__device__ __forceinline__ void da_full_role(const DaFullArgs &a, int64_t wg, unsigned char *smem) {
+  constexpr int kG = kPbf16 ? 4 : 2;            // slabs per load group
+  constexpr int kPL = kPbf16 ? 2 : 4;           // 16-B P loads per lane and slab
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t c0 = wg * 16;
+  const int64_t slabs = (a.M + 63) / 64;
+  const int64_t mine = slabs > wave ? (slabs - wave + 3) / 4 : 0;   // slabs of this wavefront
+  uint16_t *sP = reinterpret_cast<uint16_t *>(smem) + wave * (2 * 64 * kDaPitch);
+  uint16_t *sQ = sP + 64 * kDaPitch;
+  const size_t pes = kPbf16 ? 2 : 4;
+  const char *P = static_cast<const char *>(a.P);
+
+  // lane = token row of the slab: its 16 columns of P and its 16 of Q
+  u32x4_t pv[2][kG][kPL], qv[2][kG][2];
+  auto load_group = [&](int64_t grp, u32x4_t (&pg)[kG][kPL], u32x4_t (&qg)[kG][2]) {
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      const int64_t ls = grp * kG + u;                       // this wavefront's slab index
+      const int64_t m = (wave + 4 * ls) * 64 + lane;
+      const bool ok = ls < mine && m < a.M;
+#pragma unroll
+      for (int c = 0; c < kPL; ++c)
+        pg[u][c] = ok ? *reinterpret_cast<const u32x4_t *>(P + (m * a.K + c0) * pes + 16 * c)
+                      : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        qg[u][c] = ok ? *reinterpret_cast<const u32x4_t *>(a.Q + m * a.ldq + 8 * c)
+                      : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute_group = [&](const u32x4_t (&pg)[kG][kPL], const u32x4_t (&qg)[kG][2], int64_t grp) {
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      if (grp * kG + u >= mine) break;
+      // (LDS operations of one wavefront complete in order: these writes
+      // follow the previous slab's reads and precede this slab's)
+      u32x4_t p16[2];
+      if constexpr (kPbf16) {
+        p16[0] = pg[u][0];
+        p16[1] = pg[u][1];
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const f32x4_t x = __builtin_bit_cast(f32x4_t, pg[u][2 * c]);
+          const f32x4_t y = __builtin_bit_cast(f32x4_t, pg[u][2 * c + 1]);
+          p16[c] = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                           pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+      }
+      *reinterpret_cast<u32x4_t *>(sP + lane * kDaPitch) = p16[0];
+      *reinterpret_cast<u32x4_t *>(sP + lane * kDaPitch + 8) = p16[1];
+      *reinterpret_cast<u32x4_t *>(sQ + lane * kDaPitch) = qg[u][0];
+      *reinterpret_cast<u32x4_t *>(sQ + lane * kDaPitch + 8) = qg[u][1];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        acc = mfma16x16x32(lds_col8(sP, kDaPitch, 32 * k, 0), lds_col8(sQ, kDaPitch, 32 * k, 0), acc);
+    }
+  };
+  const int64_t groups = (mine + kG - 1) / kG;
+  if (groups > 0) load_group(0, pv[0], qv[0]);
+  for (int64_t grp = 0; grp < groups; grp += 2) {
+    if (grp + 1 < groups) load_group(grp + 1, pv[1], qv[1]);
+    compute_group(pv[0], qv[0], grp);
+    if (grp + 1 >= groups) break;
+    if (grp + 2 < groups) load_group(grp + 2, pv[0], qv[0]);
+    compute_group(pv[1], qv[1], grp + 1);
+  }
+
+  // C layout: lane holds rows 4 h .. 4 h + 3 (columns of P), column i16 (rank)
+  float *red = reinterpret_cast<float *>(smem + 4 * 2 * 64 * kDaPitch * 2);   // [4][16][16]
+  const int i16 = lane & 15, h = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[(wave * 16 + 4 * h + e) * 16 + i16] = acc[e];
+  __syncthreads();
+  const int row = t >> 4, j = t & 15;
+  if (j < a.R && c0 + row < a.K) {
+    const float v = ((red[row * 16 + j] + red[(16 + row) * 16 + j]) + red[(32 + row) * 16 + j]) +
+                    red[(48 + row) * 16 + j];
+    const int64_t i = (c0 + row) * a.R + j;
+    if (a.out) a.out[i] = v;
+    if (a.adam.theta) reduce_adam(a.adam, i, v);
+  }
+}
+
+constexpr size_t kDaLdsBytes = size_t(4) * 2 * 64 * kDaPitch * 2 + size_t(4) * 16 * 16 * 4;
+
 // ------------------------------------------------------------------ kernels
 
 // Block scales on workgroups [0, n_sc), XA partials (rowdot with Q = A
@@ -861,6 +988,23 @@ template <bool kXbf16, bool kWide>
 __global__ __launch_bounds__(256) void bwd_x_kernel(ColdotArgs ca) {
   extern __shared__ __align__(16) unsigned char smem[];
   coldot_role<kXbf16, true, kWide, true>(ca, blockIdx.x, smem);
+}
+
+// After the dX GEMM: dA whole (da_full_role) on workgroups [0, n_da) and
+// the reduction of dB's partials (reduce_role) on the rest.
+template <bool kXbf16>
+__global__ __launch_bounds__(256) void bwd_tail_kernel(DaFullArgs da, int64_t n_da, ReduceArgs rb) {
+  __shared__ __align__(16) unsigned char smem[kDaLdsBytes];
+  const int64_t wg = blockIdx.x;
+  if (wg < n_da) {
+    // Workgroups are dealt to the 8 XCDs round-robin: give each XCD a
+    // contiguous run of column groups, so that the four groups sharing a
+    // 128-B line of P read it through one L2.
+    const int64_t c = n_da % 8 == 0 ? (wg % 8) * (n_da / 8) + wg / 8 : wg;
+    da_full_role<kXbf16>(da, c, smem);
+  } else {
+    reduce_role(rb, wg - n_da, int64_t(gridDim.x) - n_da);
+  }
 }
 
 // U = mul(XA), element by element.
@@ -1149,6 +1293,25 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
   const int64_t n_b = part_b ? grid_for(rows_b * (ld_b > R ? ld_b : R) / per) : 0;
   if (n_a + n_b == 0) return hipSuccess;
   hipLaunchKernelGGL(reduce2_kernel, dim3(unsigned(n_a + n_b)), dim3(256), 0, s, ra, n_a, rb);
+  return hipGetLastError();
+}
+
+bool da_whole(int64_t r) { return r > 0 && r <= 16; }
+
+hipError_t launch_bwd_tail(const void *X, bool x_bf16, const uint16_t *G16, int64_t ldg,
+                           int64_t M, int64_t in, int64_t r, float *dA, const AdamTarget &adam_a,
+                           const float *part_b, int64_t ks_b, int64_t out, float *dB,
+                           const AdamTarget &adam_b, hipStream_t s) {
+  if (!da_whole(r) || in % 16 != 0 || ldg < 16 || ldg % 8 != 0) return hipErrorInvalidValue;
+  DaFullArgs da{X, G16, ldg, M, in, int(r), dA, adam_a};
+  const int64_t n_da = in / 16;
+  ReduceArgs rb{part_b, ks_b, out, r, dB, true, nullptr, 0, RankMul(), adam_b};
+  const int64_t n_b = part_b ? grid_for(out * r / (r % 4 == 0 ? 4 : 1)) : 0;
+  const dim3 grid = dim3(unsigned(n_da + n_b));
+  if (x_bf16)
+    hipLaunchKernelGGL((bwd_tail_kernel<true>), grid, dim3(256), 0, s, da, n_da, rb);
+  else
+    hipLaunchKernelGGL((bwd_tail_kernel<false>), grid, dim3(256), 0, s, da, n_da, rb);
   return hipGetLastError();
 }
 
