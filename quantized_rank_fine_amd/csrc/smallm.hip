@@ -257,6 +257,11 @@ __device__ __forceinline__ void fwd_small_block(const SmallArgs &a, const Expand
       const uint32_t off = uint32_t((kb - kbeg + row) * half_n) + 16u * uint32_t(t & 7);
       S.cv[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 2));
     }
+    // The code loads go out first: scheduled after the scale loads, their
+    // address arithmetic (a 64-bit multiply-add whose unused high half the
+    // compiler may take from any register) could name the register of an
+    // in-flight load and wait for it.
+    __builtin_amdgcn_sched_barrier(0);
     S.xr = load_x4<kX16>(rX, a.K, kb);
     const uint32_t b = uint32_t((kb + 64 * kh + lane) * nblk + blk);
     if constexpr (kG16) {
