@@ -298,7 +298,7 @@ qlora_status linear_bwd(const qlora_nf4 *wq, const void *X, const void *dY, int6
   // r <= 16: dA is formed whole after the dX GEMM (the last reader of A), in
   // one launch with the reduction of dB's partials where those are pending;
   // the bits of dA then do not depend on whether dX is asked for.
-  const bool whole = da_whole(r);
+  const bool whole = da_whole(M, in, r, xb);
   auto tail = [&](const float *dbp, int64_t ks) {
     return launch_bwd_tail(X, xb, G16, p.rp, M, in, r, dA, ta, dbp, ks, out, dB, tb, stream);
   };

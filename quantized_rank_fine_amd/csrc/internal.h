@@ -143,12 +143,12 @@ hipError_t launch_rank_mul(const float *XA, int64_t M, int64_t R, RankMul mul, f
                            hipStream_t s);
 
 // dA = X^T . G whole, for 0 < r <= 16 (da_whole): G16 bf16 [M x ldg] (ldg a
-// multiple of 8, >= 16, zero beyond r), dA fp32 [in x r] (in % 16 == 0),
+// multiple of 8, 16 <= ldg <= 64, zero beyond r), dA fp32 [in x r] (in % 16 == 0),
 // optionally with one Adam step of A (adam_a.theta != nullptr); in the same
 // launch, if part_b != nullptr, dB[r x out] = the sum of ks_b partials
 // part_b[ks][out][r] (optionally with Adam, adam_b) as launch_reduce2 forms it.
 // The sums depend on the shapes only, not on which other outputs a call asks for.
-bool da_whole(int64_t r);
+bool da_whole(int64_t M, int64_t in, int64_t r, bool x_bf16);
 hipError_t launch_bwd_tail(const void *X, bool x_bf16, const uint16_t *G16, int64_t ldg,
                            int64_t M, int64_t in, int64_t r, float *dA, const AdamTarget &adam_a,
                            const float *part_b, int64_t ks_b, int64_t out, float *dB,

@@ -839,22 +839,30 @@ __device__ __forceinline__ void da_full_role(const DaFullArgs &a, int64_t wg, un
   const size_t pes = kPbf16 ? 2 : 4;
   const char *P = static_cast<const char *>(a.P);
 
-  // lane = token row of the slab: its 16 columns of P and its 16 of Q
+  // lane = token row of the slab: its 16 columns of P and its 16 of Q.  The
+  // loads go through buffer descriptors that end at row M (rows past it,
+  // including every row of a slab past this wavefront's last, read zero), so
+  // none is conditional and the waits before each group's products leave
+  // the next group's loads in flight.  (The host keeps every offset below
+  // 2^31.)
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(a.P), (short)0, clamp_records(a.M * a.K * int64_t(pes)), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.Q), (short)0, clamp_records(a.M * a.ldq * 2), kBufFlags);
   u32x4_t pv[2][kG][kPL], qv[2][kG][2];
   auto load_group = [&](int64_t grp, u32x4_t (&pg)[kG][kPL], u32x4_t (&qg)[kG][2]) {
 #pragma unroll
     for (int u = 0; u < kG; ++u) {
       const int64_t ls = grp * kG + u;                       // this wavefront's slab index
-      const int64_t m = (wave + 4 * ls) * 64 + lane;
-      const bool ok = ls < mine && m < a.M;
+      const int64_t m = (wave + 4 * ls) * 64 + lane;         // >= M past the last slab
+      const uint32_t po = uint32_t((m * a.K + c0) * int64_t(pes));
+      const uint32_t qo = uint32_t(m * a.ldq * 2);
 #pragma unroll
       for (int c = 0; c < kPL; ++c)
-        pg[u][c] = ok ? *reinterpret_cast<const u32x4_t *>(P + (m * a.K + c0) * pes + 16 * c)
-                      : u32x4_t{0u, 0u, 0u, 0u};
+        pg[u][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, po + 16 * c, 0, 0));
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        qg[u][c] = ok ? *reinterpret_cast<const u32x4_t *>(a.Q + m * a.ldq + 8 * c)
-                      : u32x4_t{0u, 0u, 0u, 0u};
+        qg[u][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo + 16 * c, 0, 0));
     }
   };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -887,13 +895,23 @@ __device__ __forceinline__ void da_full_role(const DaFullArgs &a, int64_t wg, un
     }
   };
   const int64_t groups = (mine + kG - 1) / kG;
+  // The first two groups' loads go out before any product, outside the
+  // loop (whose waits, merged over its back edge, would otherwise make the
+  // first iteration wait for group 0 before issuing group 1); the scheduling
+  // barriers keep each group's loads ahead of the previous group's products.
   if (groups > 0) load_group(0, pv[0], qv[0]);
-  for (int64_t grp = 0; grp < groups; grp += 2) {
-    if (grp + 1 < groups) load_group(grp + 1, pv[1], qv[1]);
-    compute_group(pv[0], qv[0], grp);
+  if (groups > 1) load_group(1, pv[1], qv[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (groups > 0) compute_group(pv[0], qv[0], 0);
+  for (int64_t grp = 1; grp < groups; grp += 2) {
+    // pv[1] holds group grp
+    if (grp + 1 < groups) load_group(grp + 1, pv[0], qv[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group(pv[1], qv[1], grp);
     if (grp + 1 >= groups) break;
-    if (grp + 2 < groups) load_group(grp + 2, pv[0], qv[0]);
-    compute_group(pv[1], qv[1], grp + 1);
+    if (grp + 2 < groups) load_group(grp + 2, pv[1], qv[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group(pv[0], qv[0], grp + 1);
   }
 
   // C layout: lane holds rows 4 h .. 4 h + 3 (columns of P), column i16 (rank)
@@ -1296,13 +1314,19 @@ hipError_t launch_reduce2(const float *part_a, int64_t ks_a, int64_t rows_a, int
   return hipGetLastError();
 }
 
-bool da_whole(int64_t r) { return r > 0 && r <= 16; }
+bool da_whole(int64_t M, int64_t in, int64_t r, bool x_bf16) {
+  // every offset of the whole-dA loads below 2^31 (a slab past the last can
+  // reach 4 * 64 rows past M)
+  const int64_t rows = M + 4 * 64 * 2;
+  return r > 0 && r <= 16 && rows * in * (x_bf16 ? 2 : 4) <= 0x7fffffff && rows * 64 * 2 <= 0x7fffffff;
+}
 
 hipError_t launch_bwd_tail(const void *X, bool x_bf16, const uint16_t *G16, int64_t ldg,
                            int64_t M, int64_t in, int64_t r, float *dA, const AdamTarget &adam_a,
                            const float *part_b, int64_t ks_b, int64_t out, float *dB,
                            const AdamTarget &adam_b, hipStream_t s) {
-  if (!da_whole(r) || in % 16 != 0 || ldg < 16 || ldg % 8 != 0) return hipErrorInvalidValue;
+  if (!da_whole(M, in, r, x_bf16) || in % 16 != 0 || ldg < 16 || ldg % 8 != 0 || ldg > 64)
+    return hipErrorInvalidValue;
   DaFullArgs da{X, G16, ldg, M, in, int(r), dA, adam_a};
   const int64_t n_da = in / 16;
   ReduceArgs rb{part_b, ks_b, out, r, dB, true, nullptr, 0, RankMul(), adam_b};
