@@ -129,7 +129,7 @@ typedef enum {
  *       w_hat = L[code] * c_g.  With QLORA_CB_INT4 / INT3 / TERNARY this is
  *       the lab's symmetric integer grid; any codebook may be used.
  * Requires in % 64 == 0 and out % 64 == 0, so blocks never straddle rows.
- * qlora_loftq_init takes the 64-weight format only.
+ * qlora_loftq_init takes either format.
  */
 #define QLORA_LAB_GROUP 16
 typedef struct {

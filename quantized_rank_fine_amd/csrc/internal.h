@@ -243,14 +243,15 @@ struct Levels16 {
 };
 
 // Products with the quantization residual R = W0 - deq(Wq) (formed on the
-// fly in fp32): transpose = false: Y [in x k] = R . M (M [out x k]);
+// fly in fp32; g16: the 16-entry format, s2 = the fp32 scale per 16
+// weights): transpose = false: Y [in x k] = R . M (M [out x k]);
 // transpose = true: Y [out x k] = R^T . M (M [in x k]); 1 <= k <= 128.
 // `partial` holds the slices' partial products:
 // residual_mul_partial_bytes(in, out, k) bytes.
 size_t residual_mul_partial_bytes(int64_t in, int64_t out, int k);
 hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8_t *q8,
-                               const float *s2, int64_t in, int64_t out, const float *M, int k,
-                               float *Y, bool transpose, int codebook, float *partial,
+                               const float *s2, bool g16, int64_t in, int64_t out, const float *M,
+                               int k, float *Y, bool transpose, int codebook, float *partial,
                                hipStream_t s);
 
 // Thin-panel products for the orthonormalisation and the final factors, fp64

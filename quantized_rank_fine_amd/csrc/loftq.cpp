@@ -123,8 +123,9 @@ struct Ctx {
 
 // Y = R . M (M [out x k] -> Y [in x k]) or, transposed, R^T . M.
 hipError_t residual_product(const Ctx &c, const float *M, int k, float *Y, bool transpose) {
-  return launch_residual_mul(c.W0, c.wq->codes, c.wq->qscale, c.wq->gscale, c.wq->in, c.wq->out,
-                             M, k, Y, transpose, c.wq->codebook, c.rpart, c.s);
+  return launch_residual_mul(c.W0, c.wq->codes, c.wq->qscale, c.wq->gscale,
+                             c.wq->block == QLORA_LAB_GROUP, c.wq->in, c.wq->out, M, k, Y,
+                             transpose, c.wq->codebook, c.rpart, c.s);
 }
 
 // H [ka x kb] on the host = X^T . Y (device panels [rows x ka], [rows x kb]).
@@ -182,8 +183,10 @@ extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, c
   if (!wq || !W0 || !omega || !A || !B || !ws) return QLORA_ERR_NULL;
   if (wq->in <= 0 || wq->out <= 0 || wq->in % 64 || wq->out % 64) return QLORA_ERR_SHAPE;
   if (wq->codebook < 0 || wq->codebook >= kCodebooks) return QLORA_ERR_DTYPE;
-  if (wq->block != 0 && wq->block != QLORA_BLOCK) return QLORA_ERR_DTYPE;   // 64-weight format only
-  if (!wq->codes || !wq->qscale || !wq->gscale) return QLORA_ERR_NULL;
+  if (wq->block != 0 && wq->block != QLORA_BLOCK && wq->block != QLORA_LAB_GROUP)
+    return QLORA_ERR_DTYPE;
+  const bool g16 = wq->block == QLORA_LAB_GROUP;
+  if (!wq->codes || !wq->gscale || (!g16 && !wq->qscale)) return QLORA_ERR_NULL;
   if (adt != QLORA_F32 && adt != QLORA_BF16) return QLORA_ERR_DTYPE;
   if (k < 1 || k > 128 || r < 1 || r > k || k > wq->in || k > wq->out || iters < 0 || iters > 16)
     return QLORA_ERR_SHAPE;
@@ -191,7 +194,7 @@ extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, c
                        reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
                        reinterpret_cast<uintptr_t>(ws) |
                        reinterpret_cast<uintptr_t>(wq->codes) |
-                       reinterpret_cast<uintptr_t>(wq->qscale) |
+                       (g16 ? 0 : reinterpret_cast<uintptr_t>(wq->qscale)) |
                        reinterpret_cast<uintptr_t>(wq->gscale);
   if (al & 15u) return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora_loftq_workspace_bytes(wq->in, wq->out, k)) return QLORA_ERR_WORKSPACE;

@@ -7,7 +7,8 @@
 // subspace iteration, which touches R only through the products
 //   Y = R . M   (M [out x k], Y [in x k])   and   Z = R^T . Q   (Q [in x k]),
 // k <= 128 columns.  R is never stored: each tile of it is formed in fp32
-// (W0 minus L[code] * (q_b * s2_g), the value the fused GEMMs round to bf16)
+// (W0 minus L[code] * (q_b * s2_g), or L[code] * c_g in the 16-entry format:
+// the value the fused GEMMs round to bf16)
 // and multiplied with fp32 multiply-adds.  The thin panels between the
 // products are orthonormalised here as well (Cholesky QR applied twice: the
 // k x k Gram matrix and the panel update run on the GPU in fp64 arithmetic),
@@ -25,33 +26,22 @@ struct ResidualArgs {
   const float *W0;
   const uint8_t *codes;
   const int8_t *q8;
-  const float *s2;
+  const float *s2;    // 64-weight blocks: one fp32 scale per 256 blocks; g16: one per 16 weights
   int64_t in, out;
   const float *M;     // rmul: [out x k]; rtmul: [in x k]
   int k;
   float *Y;           // rmul: [in x k]; rtmul: [out x k]; one such block per slice
   int64_t span;       // length of a slice of the summed axis (a multiple of the chunk)
+  int g16;            // the 16-entry format: scale of weight f = s2[f / 16], no q8
 };
 
-// 16 consecutive residual elements of row `row`, columns col .. col + 15
-// (col % 16 == 0: one 64-block, one scale).
-__device__ __forceinline__ void residual16(const ResidualArgs &a, const float *L, int64_t row,
-                                           int64_t col, float (&v)[16]) {
-  const int64_t flat = row * a.out + col;
-  const int64_t blk = flat / 64;
-  const float c = float(a.q8[blk]) * a.s2[blk >> 8];
-  const u32x2_t cw = *reinterpret_cast<const u32x2_t *>(a.codes + flat / 2);
-  const f32x4_t *w = reinterpret_cast<const f32x4_t *>(a.W0 + flat);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4_t x = w[q];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * q + e;
-      const uint32_t code = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
-      v[i] = x[e] - L[code] * c;
-    }
-  }
+// The dequantization scale of flat weight f (the product the fused GEMMs
+// form: q_b * s2_g for 64-weight blocks, the group's fp32 absmax for the
+// 16-entry format).
+__device__ __forceinline__ float scale_of(const ResidualArgs &a, int64_t f) {
+  if (a.g16) return a.s2[f / 16];
+  const int64_t blk = f / 64;
+  return float(a.q8[blk]) * a.s2[blk >> 8];
 }
 
 // Y = R . M on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, products and
@@ -80,7 +70,7 @@ __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16
   float mv[MPER];
   f32x4_t wv[8];
   u32x4_t cv;
-  float cs = 0.0f;
+  float cs = 0.0f, cs2 = 0.0f;
   auto load = [&](int64_t c0) {
     if (live) {
       const int64_t flat = row * a.out + c0 + 32 * h;
@@ -88,8 +78,8 @@ __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16
 #pragma unroll
       for (int q = 0; q < 8; ++q) wv[q] = src[q];
       cv = *reinterpret_cast<const u32x4_t *>(a.codes + flat / 2);
-      const int64_t blk = flat / 64;
-      cs = float(a.q8[blk]) * a.s2[blk >> 8];
+      cs = scale_of(a, flat);
+      cs2 = a.g16 ? scale_of(a, flat + 16) : cs;   // elements 16..31 (another group)
     }
 #pragma unroll
     for (int u = 0; u < MPER; ++u) {
@@ -114,7 +104,7 @@ __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const uint32_t code = (cv[e >> 3] >> (4 * (e & 7))) & 15u;
-      rv[e] = wv[e >> 2][e & 3] - sL[code] * cs;
+      rv[e] = wv[e >> 2][e & 3] - sL[code] * (e < 16 ? cs : cs2);
     }
     __syncthreads();
     if (c0 + 64 < ne) load(c0 + 64);            // in flight during the products
@@ -193,8 +183,7 @@ __global__ __launch_bounds__(256) void rtmul_mfma_kernel(ResidualArgs a, Levels1
           wv[st][0] = a.W0[flat];
           cd[st] = uint32_t(a.codes[flat / 2]) >> (4 * (flat & 1));
         }
-        const int64_t blk = flat / 64;
-        cs[st] = float(a.q8[blk]) * a.s2[blk >> 8];
+        cs[st] = scale_of(a, flat);           // the lane's NQ columns lie in one group
       } else {
 #pragma unroll
         for (int p = 0; p < NQ; ++p) wv[st][p] = 0.0f;
@@ -402,8 +391,8 @@ size_t residual_mul_partial_bytes(int64_t in, int64_t out, int k) {
 }
 
 hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8_t *q8,
-                               const float *s2, int64_t in, int64_t out, const float *M, int k,
-                               float *Y, bool transpose, int codebook, float *partial,
+                               const float *s2, bool g16, int64_t in, int64_t out, const float *M,
+                               int k, float *Y, bool transpose, int codebook, float *partial,
                                hipStream_t s) {
   if (k < 1 || k > kMaxK) return hipErrorInvalidValue;
   Levels16 lv;
@@ -424,7 +413,7 @@ hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8
     span = slice_span(4 * base, len, 64);
   }
   const int64_t S = (len + span - 1) / span;
-  ResidualArgs a{W0, codes, q8, s2, in, out, M, k, S > 1 ? partial : Y, span};
+  ResidualArgs a{W0, codes, q8, s2, in, out, M, k, S > 1 ? partial : Y, span, g16 ? 1 : 0};
   const dim3 g = dim3(unsigned(base), unsigned(S));
   if (!transpose) {
     if (kt == 1) hipLaunchKernelGGL(rmul_mfma_kernel<1>, g, dim3(256), 0, s, a, lv);

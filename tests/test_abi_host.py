@@ -360,6 +360,18 @@ def test_loftq_validation(L):
     assert call(6, U) == 3
     assert call(10, ws - 1) == 5
     assert call(1, ctypes.byref(_nf4(256, 100))) == 2
+    bad = _nf4(256, 256)
+    bad.block = 32                      # neither the 64-weight nor the 16-entry format
+    assert call(1, ctypes.byref(bad)) == 4
+    # the 16-entry format has no int8 scales: a NULL qscale passes the null
+    # check and the call stops at the (too small) workspace, before any
+    # device work
+    g16 = _nf4(256, 256)
+    g16.block = 16
+    g16.qscale = None
+    a = list(ok)
+    a[1], a[10] = ctypes.byref(g16), ws - 1
+    assert f(*a) == 5
 
 
 def test_algorithmic_work_formulas():

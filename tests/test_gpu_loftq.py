@@ -13,8 +13,12 @@ from gpu_harness import bf16_to_f64, levels_of, quantize_gpu, say, torch_dev
 pytestmark = pytest.mark.gpu
 
 
-def _w_hat(w0, codebook=q.CB_NF4):
-    """deq(Q(W0)) in float64 from the oracle's own quantization of W0."""
+def _w_hat(w0, codebook=q.CB_NF4, block=64):
+    """deq(Q(W0)) in float64 from the oracle's own quantization of W0 (block
+    16: the lab's 16-entry format)."""
+    if block == 16:
+        og = oracle.quantize_groups(w0, levels_of(codebook))
+        return oracle.dequantize_groups(og["packed"], og["scales"], *w0.shape, levels_of(codebook))
     oq = oracle.quantize(w0, levels_of(codebook))
     return oracle.dequantize(oq["packed"], oq["q8"], oq["s2"], *w0.shape, levels_of(codebook))
 
@@ -85,3 +89,38 @@ def test_bf16_output_is_the_rounded_fp32_output():
     A32, B32 = _init(W0, wq, 16, 8, 2)
     A16, B16 = _init(W0, wq, 16, 8, 2, adt="bf16")
     assert torch.equal(A32.to(torch.bfloat16), A16) and torch.equal(B32.to(torch.bfloat16), B16)
+
+
+@pytest.mark.parametrize("n_in,n_out", [(256, 384), (192, 320)])
+def test_group16_low_rank_residual_is_recovered(n_in, n_out):
+    """The lab's 16-entry format (INT4 levels k/7, one fp32 absmax per 16
+    entries): W0 = fp32(deq(Wq)) + P with P of rank 4 is recovered."""
+    torch, dev = torch_dev()
+    say(f"[loftq] 16-entry format, rank-4 residual {n_in}x{n_out}")
+    w0 = synth.weights(n_in, n_out, workload=7)
+    wq = quantize_gpu(w0, q.CB_INT4, block=16)
+    W_hat = _w_hat(w0, q.CB_INT4, block=16)
+    g = np.random.default_rng(52)
+    P = (g.standard_normal((n_in, 4)) @ g.standard_normal((4, n_out)) * 0.01).astype(np.float32)
+    W0 = (W_hat.astype(np.float32) + P).astype(np.float32)
+    R = W0.astype(np.float64) - W_hat
+    A, B = _init(torch.from_numpy(W0).to(dev), wq, 12, 4, 2)
+    AB = A.cpu().numpy().astype(np.float64) @ B.cpu().numpy().astype(np.float64)
+    assert np.abs(AB - R).max() <= 1e-4 * np.abs(R).max()
+
+
+def test_group16_quantization_residual_near_optimal():
+    """On the 16-entry format's real quantization residual the rank-16 start
+    removes at least 90 % of what the exact truncated SVD removes."""
+    torch, dev = torch_dev()
+    w0 = synth.weights(512, 768, workload=7)
+    wq = quantize_gpu(w0, q.CB_INT4, block=16)
+    W_hat = _w_hat(w0, q.CB_INT4, block=16)
+    R = oracle.residual(w0, W_hat)
+    A, B = _init(torch.from_numpy(w0).to(dev), wq, 24, 16, 3)
+    An, Bn = A.cpu().numpy().astype(np.float64), B.cpu().numpy().astype(np.float64)
+    Ao, Bo = oracle.loftq_init(w0, W_hat, 16)
+    full = np.sum(R ** 2)
+    e_opt = np.sum((R - Ao @ Bo) ** 2)
+    e_gpu = np.sum((R - An @ Bn) ** 2)
+    assert e_gpu <= e_opt + 0.1 * (full - e_opt), (full, e_opt, e_gpu)
