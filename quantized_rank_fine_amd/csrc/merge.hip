@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, Levels lv) {
 // ---- matrix-core kernel ----
 constexpr int kMRows = 64, kMCols = 128, kMBlocks = 2;    // blocks of 32 columns per wave
 
-template <bool kAbf16, bool kWbf16>
+template <bool kAbf16, bool kWbf16, bool kG16>
 __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv) {
   constexpr int kES = kWbf16 ? 2 : 4;                      // output element bytes
   constexpr int kRowB = 32 * kMBlocks * kES;               // staged bytes per row
@@ -155,58 +155,75 @@ __global__ __launch_bounds__(256) void merge_mfma_kernel(MergeArgs a, Levels lv)
   const int64_t nw0 = int64_t(blockIdx.x) * kMCols + (w >> 1) * (32 * kMBlocks);
   if (nw0 >= a.out) return;                                // whole wavefront; no block barrier
   const int nb = int(min64(kMBlocks, (a.out - nw0) / 32));
-  if (l < 16) sL[w][l] = lv.L[l];
-  __builtin_amdgcn_wave_barrier();
   const int64_t NB = a.out / 64;
 
-  // scales of columns n .. n + 15 and n + 16 .. n + 31 (one block scale, or
-  // two 16-entry group scales)
+  // Every load of the tile goes out first, with no condition around it (a
+  // block past `nb` or a rank past r reads a valid element and is zeroed
+  // or dropped), so a workgroup waits for memory once: the codes and scales
+  // of columns n .. n + 31 (one block scale, or two 16-entry group scales)
+  // and, for bf16 adapters, the operands of ranks 0..15.
   u32x4_t cw[kMBlocks];
   float sc[kMBlocks][2];
 #pragma unroll
   for (int b = 0; b < kMBlocks; ++b) {
-    if (b < nb) {
-      const int64_t n = nw0 + 32 * b;
-      cw[b] = *reinterpret_cast<const u32x4_t *>(a.codes + (row * a.out + n) / 2);
-      if (a.g16) {
-        sc[b][0] = a.s2[(row * a.out + n) / 16];
-        sc[b][1] = a.s2[(row * a.out + n) / 16 + 1];
-      } else {
-        const int64_t blk = row * NB + n / 64;
-        sc[b][0] = sc[b][1] = float(a.q8[blk]) * a.s2[blk >> 8];
-      }
+    const int64_t n = nw0 + 32 * (b < nb ? b : 0);
+    cw[b] = *reinterpret_cast<const u32x4_t *>(a.codes + (row * a.out + n) / 2);
+    if constexpr (kG16) {
+      sc[b][0] = a.s2[(row * a.out + n) / 16];
+      sc[b][1] = a.s2[(row * a.out + n) / 16 + 1];
+    } else {
+      const int64_t blk = row * NB + n / 64;
+      sc[b][0] = float(a.q8[blk]) * a.s2[blk >> 8];
+      sc[b][1] = sc[b][0];
     }
   }
+  // bf16 adapters, ranks j0 .. j0 + 15: af = A[row][jh .. jh + 7] (jh = j0 +
+  // 8 h), bf[b] = B[jh .. jh + 7][n] paired as the MFMA operand
+  auto load_ab = [&](int j0, u32x4_t &af, u32x4_t (&bf)[kMBlocks]) {
+    const uint16_t *A = static_cast<const uint16_t *>(a.A);
+    const uint16_t *B = static_cast<const uint16_t *>(a.B);
+    const int jh = j0 + 8 * h;
+    const bool ok = jh < a.r;                               // r % 8 == 0: all 8 or none
+    const u32x4_t av = *reinterpret_cast<const u32x4_t *>(A + row * a.r + (ok ? jh : 0));
+    uint16_t raw[kMBlocks][8];
+#pragma unroll
+    for (int b = 0; b < kMBlocks; ++b) {
+      const int64_t n = nw0 + 32 * (b < nb ? b : 0) + l32;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) raw[b][e] = B[(ok ? jh + e : 0) * int64_t(a.out) + n];
+    }
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    af = ok ? av : zero;
+#pragma unroll
+    for (int b = 0; b < kMBlocks; ++b) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        bf[b][e] = ok ? uint32_t(raw[b][2 * e]) | (uint32_t(raw[b][2 * e + 1]) << 16) : 0u;
+    }
+  };
+  u32x4_t af0 = {0u, 0u, 0u, 0u}, bf0[kMBlocks];
+  if constexpr (kAbf16) {
+    if (a.r > 0) load_ab(0, af0, bf0);
+  }
+  // the level table (read from the kernel arguments) after the tile's loads
+  if (l < 16) sL[w][l] = lv.L[l];
+  __builtin_amdgcn_wave_barrier();
   f32x16_t acc[kMBlocks];
 #pragma unroll
   for (int b = 0; b < kMBlocks; ++b) {
-    if (b < nb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)                          // column 8 (i / 4) + 4 h + i % 4
-        acc[b][i] = sL[w][(cw[b][i >> 2] >> (4 * (4 * h + (i & 3)))) & 15u] * sc[b][i >> 3];
-    }
+    for (int i = 0; i < 16; ++i)                            // column 8 (i / 4) + 4 h + i % 4
+      acc[b][i] = sL[w][(cw[b][i >> 2] >> (4 * (4 * h + (i & 3)))) & 15u] * sc[b][i >> 3];
   }
   if constexpr (kAbf16) {
-  const uint16_t *A = static_cast<const uint16_t *>(a.A);
-  const uint16_t *B = static_cast<const uint16_t *>(a.B);
   for (int j0 = 0; j0 < a.r; j0 += 16) {
-    const int jh = j0 + 8 * h;                              // this lane's 8 ranks
-    u32x4_t af = {0, 0, 0, 0};
-    if (jh < a.r) af = *reinterpret_cast<const u32x4_t *>(A + row * a.r + jh);
+    u32x4_t af = af0, bf[kMBlocks];
 #pragma unroll
-    for (int b = 0; b < kMBlocks; ++b) {
-      if (b < nb) {
-        const int64_t n = nw0 + 32 * b + l32;
-        u32x4_t bf = {0, 0, 0, 0};
-        if (jh < a.r) {
+    for (int b = 0; b < kMBlocks; ++b) bf[b] = bf0[b];
+    if (j0 > 0) load_ab(j0, af, bf);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bf[e] = uint32_t(B[int64_t(jh + 2 * e) * a.out + n]) |
-                    (uint32_t(B[int64_t(jh + 2 * e + 1) * a.out + n]) << 16);
-        }
-        acc[b] = mfma32x32x16(bf, af, acc[b]);
-      }
-    }
+    for (int b = 0; b < kMBlocks; ++b)
+      if (b < nb) acc[b] = mfma32x32x16(bf[b], af, acc[b]);
   }
   } else {
   // fp32 adapters: 32 x 32 x 2 fp32 MFMAs, lane half h taking ranks
@@ -280,13 +297,17 @@ hipError_t launch_merge(const uint8_t *codes, const int8_t *q8, const float *s2,
   for (int i = 0; i < 16; ++i) lv.L[i] = t.L[i];
   if (r % 8 == 0) {                                        // r = 0 included
     const dim3 mgrid(unsigned((out + kMCols - 1) / kMCols), unsigned(in / kMRows));
+#define QLORA_MERGE(AB, WB)                                                                     \
+  do {                                                                                          \
+    if (g16) hipLaunchKernelGGL((merge_mfma_kernel<AB, WB, true>), mgrid, dim3(256), 0, s, a, lv);  \
+    else hipLaunchKernelGGL((merge_mfma_kernel<AB, WB, false>), mgrid, dim3(256), 0, s, a, lv);     \
+  } while (0)
     if (a_bf16) {
-      if (w_bf16) hipLaunchKernelGGL((merge_mfma_kernel<true, true>), mgrid, dim3(256), 0, s, a, lv);
-      else hipLaunchKernelGGL((merge_mfma_kernel<true, false>), mgrid, dim3(256), 0, s, a, lv);
+      if (w_bf16) QLORA_MERGE(true, true); else QLORA_MERGE(true, false);
     } else {
-      if (w_bf16) hipLaunchKernelGGL((merge_mfma_kernel<false, true>), mgrid, dim3(256), 0, s, a, lv);
-      else hipLaunchKernelGGL((merge_mfma_kernel<false, false>), mgrid, dim3(256), 0, s, a, lv);
+      if (w_bf16) QLORA_MERGE(false, true); else QLORA_MERGE(false, false);
     }
+#undef QLORA_MERGE
     return hipGetLastError();
   }
   const dim3 grid(unsigned((out + kCols - 1) / kCols), unsigned(in / kRows));
