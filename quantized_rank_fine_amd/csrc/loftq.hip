@@ -32,16 +32,34 @@ struct ResidualArgs {
   int k;
   float *Y;           // rmul: [in x k]; rtmul: [out x k]; one such block per slice
   int64_t span;       // length of a slice of the summed axis (a multiple of the chunk)
-  int g16;            // the 16-entry format: scale of weight f = s2[f / 16], no q8
 };
 
-// The dequantization scale of flat weight f (the product the fused GEMMs
-// form: q_b * s2_g for 64-weight blocks, the group's fp32 absmax for the
-// 16-entry format).
-__device__ __forceinline__ float scale_of(const ResidualArgs &a, int64_t f) {
-  if (a.g16) return a.s2[f / 16];
+// The dequantization scale of flat weight f, as loaded (int8 q_b and the
+// fp32 s2_g for 64-weight blocks; the group's fp32 absmax for the 16-entry
+// format, with q = 1), and its value q * s -- the product the fused GEMMs
+// form.  The kernels load it with the rest of a chunk and form the value
+// only when the chunk is used, so that no wait follows the loads.
+struct RawScale {
+  int q;
+  float s;
+};
+
+template <bool kG16>
+__device__ __forceinline__ RawScale load_scale(const ResidualArgs &a, int64_t f) {
+  if constexpr (kG16) return RawScale{1, a.s2[f / 16]};
   const int64_t blk = f / 64;
-  return float(a.q8[blk]) * a.s2[blk >> 8];
+  return RawScale{int(a.q8[blk]), a.s2[blk >> 8]};
+}
+
+__device__ __forceinline__ float scale_value(RawScale r) { return float(r.q) * r.s; }
+
+// The level table into LDS from one lane: the kernel argument's values come
+// through scalar registers, so that staging them waits on no vector load.
+__device__ __forceinline__ void stage_levels(float *sL, const Levels16 &lv, int t) {
+  if (t == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sL[i] = lv.L[i];
+  }
 }
 
 // Y = R . M on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, products and
@@ -54,7 +72,7 @@ __device__ __forceinline__ float scale_of(const ResidualArgs &a, int64_t f) {
 // B operand (the matching rows of M, staged in LDS per chunk and shared by
 // the four wavefronts) gives output columns 32 t + l % 32 of tile t < KT.
 // The next chunk's loads are in flight while the current one is multiplied.
-template <int KT>
+template <int KT, bool kG16>
 __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16 lv) {
   constexpr int KP = 32 * KT;
   __shared__ float sL[16];
@@ -62,29 +80,33 @@ __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16
   const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5;
   const int64_t row = int64_t(blockIdx.x) * 128 + 32 * w + (l & 31);
   const bool live = row < a.in;                 // in % 64 == 0: whole wavefronts
-  if (t < 16) sL[t] = lv.L[t];
   const int64_t nb = int64_t(blockIdx.y) * a.span, ne = min64(a.out, nb + a.span);
   // the chunk's M rows: thread t stages (row e / KP, column e % KP) for
   // e = t + 256 u (columns >= k are zero)
   constexpr int MPER = 64 * KP / 256;
   float mv[MPER];
+  uint32_t mok = 0;                             // bit u: mv[u] is a row of M (else it stages 0)
   f32x4_t wv[8];
   u32x4_t cv;
-  float cs = 0.0f, cs2 = 0.0f;
+  RawScale cs{0, 0.0f}, cs2{0, 0.0f};
+  // Every load is unconditional, so that no wait follows it: a row past
+  // `in` reads row 0 (its wavefront writes nothing) and a staging slot
+  // past k or out reads M[0] and is masked when it is stored.
   auto load = [&](int64_t c0) {
-    if (live) {
-      const int64_t flat = row * a.out + c0 + 32 * h;
-      const f32x4_t *src = reinterpret_cast<const f32x4_t *>(a.W0 + flat);
+    const int64_t flat = live ? row * a.out + c0 + 32 * h : 0;
+    const f32x4_t *src = reinterpret_cast<const f32x4_t *>(a.W0 + flat);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) wv[q] = src[q];
-      cv = *reinterpret_cast<const u32x4_t *>(a.codes + flat / 2);
-      cs = scale_of(a, flat);
-      cs2 = a.g16 ? scale_of(a, flat + 16) : cs;   // elements 16..31 (another group)
-    }
+    for (int q = 0; q < 8; ++q) wv[q] = src[q];
+    cv = *reinterpret_cast<const u32x4_t *>(a.codes + flat / 2);
+    cs = load_scale<kG16>(a, flat);
+    cs2 = kG16 ? load_scale<kG16>(a, flat + 16) : cs;   // elements 16..31 (another group)
+    mok = 0;
 #pragma unroll
     for (int u = 0; u < MPER; ++u) {
       const int e = t + 256 * u, n = e / KP, j = e - n * KP;
-      mv[u] = (j < a.k && c0 + n < a.out) ? a.M[(c0 + n) * a.k + j] : 0.0f;
+      const bool ok = j < a.k && c0 + n < a.out;
+      mv[u] = a.M[ok ? (c0 + n) * a.k + j : 0];
+      mok |= uint32_t(ok) << u;
     }
   };
   f32x16_t acc[KT];
@@ -93,18 +115,20 @@ __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[q][e] = 0.0f;
   load(nb);
+  stage_levels(sL, lv, t);                      // (visible at the loop's first barrier)
   for (int64_t c0 = nb; c0 < ne; c0 += 64) {
     __syncthreads();                            // the previous chunk's reads are done
 #pragma unroll
     for (int u = 0; u < MPER; ++u) {
       const int e = t + 256 * u, n = e / KP, j = e - n * KP;
-      sM[n][j] = mv[u];
+      sM[n][j] = (mok >> u) & 1u ? mv[u] : 0.0f;
     }
     float rv[32];
+    const float c1 = scale_value(cs), c2 = scale_value(cs2);
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const uint32_t code = (cv[e >> 3] >> (4 * (e & 7))) & 15u;
-      rv[e] = wv[e >> 2][e & 3] - sL[code] * (e < 16 ? cs : cs2);
+      rv[e] = wv[e >> 2][e & 3] - sL[code] * (e < 16 ? c1 : c2);
     }
     __syncthreads();
     if (c0 + 64 < ne) load(c0 + 64);            // in flight during the products
@@ -141,13 +165,11 @@ __global__ __launch_bounds__(256) void rmul_mfma_kernel(ResidualArgs a, Levels16
 // in wavefront order through LDS, and the slice's partial product goes to
 // block blockIdx.y of Z.  Rows are walked 16 at a time, the next 16 loaded
 // while the current ones are multiplied.
-template <int KT, int NQ>
+template <int KT, int NQ, bool kG16>
 __global__ __launch_bounds__(256) void rtmul_mfma_kernel(ResidualArgs a, Levels16 lv) {
   __shared__ float sL[16];
   __shared__ float sRed[3][KT * NQ * 16][64];
   const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, m = l & 31;
-  if (t < 16) sL[t] = lv.L[t];
-  __syncthreads();
   const int64_t c = int64_t(blockIdx.x) * 32 * NQ + NQ * m;   // first of the lane's columns
   const bool live = c < a.out;                                // out % 64 == 0
   const int64_t sb = int64_t(blockIdx.y) * a.span, se = min64(a.in, sb + a.span);
@@ -160,53 +182,58 @@ __global__ __launch_bounds__(256) void rtmul_mfma_kernel(ResidualArgs a, Levels1
     for (int q = 0; q < KT; ++q)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[p][q][e] = 0.0f;
-  float wv[8][NQ], bq[8][KT], cs[8];
+  float wv[8][NQ], bq[8][KT];
+  RawScale cs[8];
   uint32_t cd[8];
+  uint32_t rok = 0, bok = 0;   // bit st: step st's row is in the slice; bit st KT + q: its M entry is
+  // Every load is unconditional, so that no wait follows it: a row past the
+  // quarter or a column past out reads element 0 and is masked at use.
   auto load = [&](int64_t i0) {
+    rok = 0;
+    bok = 0;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int64_t i = i0 + 2 * st + h;
       const bool ok = live && i < ie;
-      if (ok) {
-        const int64_t flat = i * a.out + c;
-        if constexpr (NQ == 4) {
-          const f32x4_t v = *reinterpret_cast<const f32x4_t *>(a.W0 + flat);
+      const int64_t flat = ok ? i * a.out + c : 0;
+      if constexpr (NQ == 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(a.W0 + flat);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) wv[st][p] = v[p];
-          cd[st] = *reinterpret_cast<const uint16_t *>(a.codes + flat / 2);
-        } else if constexpr (NQ == 2) {
-          const float2 v = *reinterpret_cast<const float2 *>(a.W0 + flat);
-          wv[st][0] = v.x;
-          wv[st][1] = v.y;
-          cd[st] = a.codes[flat / 2];
-        } else {
-          wv[st][0] = a.W0[flat];
-          cd[st] = uint32_t(a.codes[flat / 2]) >> (4 * (flat & 1));
-        }
-        cs[st] = scale_of(a, flat);           // the lane's NQ columns lie in one group
+        for (int p = 0; p < 4; ++p) wv[st][p] = v[p];
+        cd[st] = *reinterpret_cast<const uint16_t *>(a.codes + flat / 2);
+      } else if constexpr (NQ == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(a.W0 + flat);
+        wv[st][0] = v.x;
+        wv[st][1] = v.y;
+        cd[st] = a.codes[flat / 2];
       } else {
-#pragma unroll
-        for (int p = 0; p < NQ; ++p) wv[st][p] = 0.0f;
-        cd[st] = 0;
-        cs[st] = 0.0f;
+        wv[st][0] = a.W0[flat];
+        cd[st] = uint32_t(a.codes[flat / 2]) >> (4 * (flat & 1));
       }
+      cs[st] = load_scale<kG16>(a, flat);     // the lane's NQ columns lie in one group
+      rok |= uint32_t(ok) << st;
 #pragma unroll
       for (int q = 0; q < KT; ++q) {
         const int j = 32 * q + m;
-        bq[st][q] = (i < ie && j < a.k) ? a.M[i * a.k + j] : 0.0f;
+        const bool okb = i < ie && j < a.k;
+        bq[st][q] = a.M[okb ? i * a.k + j : 0];
+        bok |= uint32_t(okb) << (st * KT + q);
       }
     }
   };
-  if (ib < ie) load(ib);
+  load(ib);                                     // (an empty quarter: all masked)
+  stage_levels(sL, lv, t);
+  __syncthreads();
   for (int64_t i0 = ib; i0 < ie; i0 += 16) {
     float rv[8][NQ], bv[8][KT];
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
+      const bool okr = (rok >> st) & 1u;
 #pragma unroll
       for (int p = 0; p < NQ; ++p)
-        rv[st][p] = wv[st][p] - sL[(cd[st] >> (4 * p)) & 15u] * cs[st];
+        rv[st][p] = okr ? wv[st][p] - sL[(cd[st] >> (4 * p)) & 15u] * scale_value(cs[st]) : 0.0f;
 #pragma unroll
-      for (int q = 0; q < KT; ++q) bv[st][q] = bq[st][q];
+      for (int q = 0; q < KT; ++q) bv[st][q] = (bok >> (st * KT + q)) & 1u ? bq[st][q] : 0.0f;
     }
     if (i0 + 16 < ie) load(i0 + 16);            // in flight during the products
 #pragma unroll
@@ -413,17 +440,22 @@ hipError_t launch_residual_mul(const float *W0, const uint8_t *codes, const int8
     span = slice_span(4 * base, len, 64);
   }
   const int64_t S = (len + span - 1) / span;
-  ResidualArgs a{W0, codes, q8, s2, in, out, M, k, S > 1 ? partial : Y, span, g16 ? 1 : 0};
+  ResidualArgs a{W0, codes, q8, s2, in, out, M, k, S > 1 ? partial : Y, span};
   const dim3 g = dim3(unsigned(base), unsigned(S));
-  if (!transpose) {
-    if (kt == 1) hipLaunchKernelGGL(rmul_mfma_kernel<1>, g, dim3(256), 0, s, a, lv);
-    else if (kt == 2) hipLaunchKernelGGL(rmul_mfma_kernel<2>, g, dim3(256), 0, s, a, lv);
-    else hipLaunchKernelGGL(rmul_mfma_kernel<4>, g, dim3(256), 0, s, a, lv);
-  } else {
-    if (kt == 1) hipLaunchKernelGGL((rtmul_mfma_kernel<1, 4>), g, dim3(256), 0, s, a, lv);
-    else if (kt == 2) hipLaunchKernelGGL((rtmul_mfma_kernel<2, 2>), g, dim3(256), 0, s, a, lv);
-    else hipLaunchKernelGGL((rtmul_mfma_kernel<4, 1>), g, dim3(256), 0, s, a, lv);
-  }
+#define QLORA_RES(G)                                                                             \
+  do {                                                                                           \
+    if (!transpose) {                                                                            \
+      if (kt == 1) hipLaunchKernelGGL((rmul_mfma_kernel<1, G>), g, dim3(256), 0, s, a, lv);      \
+      else if (kt == 2) hipLaunchKernelGGL((rmul_mfma_kernel<2, G>), g, dim3(256), 0, s, a, lv); \
+      else hipLaunchKernelGGL((rmul_mfma_kernel<4, G>), g, dim3(256), 0, s, a, lv);              \
+    } else {                                                                                     \
+      if (kt == 1) hipLaunchKernelGGL((rtmul_mfma_kernel<1, 4, G>), g, dim3(256), 0, s, a, lv);  \
+      else if (kt == 2) hipLaunchKernelGGL((rtmul_mfma_kernel<2, 2, G>), g, dim3(256), 0, s, a, lv); \
+      else hipLaunchKernelGGL((rtmul_mfma_kernel<4, 1, G>), g, dim3(256), 0, s, a, lv);          \
+    }                                                                                            \
+  } while (0)
+  if (g16) QLORA_RES(true); else QLORA_RES(false);
+#undef QLORA_RES
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t n4 = nrows * k / 4;                // nrows % 64 == 0
