@@ -389,13 +389,14 @@ qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v
  *   U_r S_r V_r^T of R = W0 - deq(Wq), split as A = U_r sqrt(S_r),
  *   B = sqrt(S_r) V_r^T, found by randomized subspace iteration with
  *   `iters` power iterations (0..16; 2 is usual).  R is formed on the fly in
- *   fp32 by the GPU products R.M and R^T.M.  The thin panels stay on the GPU
- *   (fp32) and are orthonormalised there by Cholesky QR applied twice (Gram
- *   matrices and panel updates in fp64 arithmetic); the host does only the
- *   k x k work in double (each Cholesky factor and its inverse, the final
- *   SVD).  ws: qlora_loftq_workspace_bytes(in, out, k) bytes of device
- *   memory.  The call is synchronous (it waits for the stream after every
- *   Gram matrix) and cannot be captured in a graph.
+ *   fp32 by the GPU products R.M and R^T.M.  The thin panels (fp32) are
+ *   orthonormalised by Cholesky QR applied twice (Gram matrices and panel
+ *   updates in fp64 arithmetic); the k x k steps (each Cholesky factor's
+ *   inverse, the final SVD by one-sided Jacobi rotations) run in fp64 on the
+ *   GPU as well.  ws: qlora_loftq_workspace_bytes(in, out, k) bytes of device
+ *   memory.  Asynchronous like the other calls: the work is enqueued on
+ *   `stream` and the call never waits for the device, so it can be captured
+ *   in a graph; A, B and ws must stay untouched until it has run.
  */
 qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, const float *omega,
                               int32_t k, int32_t r, int32_t iters, void *A, void *B,

@@ -265,6 +265,13 @@ hipError_t launch_panel_gram(const float *X, int ka, const float *Y, int kb, int
                              double *G, double *partial, hipStream_t s);
 hipError_t launch_panel_apply(const float *X, int k, const double *T, int m, int64_t rows,
                               void *Out, bool transposed, bool bf16, hipStream_t s);
+// k x k steps on the GPU (one workgroup, fp64): T [k x k] = C^-1 for the
+// Cholesky factor of the Gram matrix G (dependent columns leave as zero
+// columns); P = [Pa | Pb'] ([k x r] each) from the SVD Rz^T = U S V^T, Rz
+// [k x k] row-major: Pa = U_r S_r^(1/2), Pb' = U_r S_r^(-1/2) (so that
+// Z Pb' = Qz V_r S_r^(1/2) when Rz = Qz^T Z).  k <= 128, r <= k.
+hipError_t launch_chol_inv(const double *G, int k, double *T, hipStream_t s);
+hipError_t launch_small_svd(const double *Rz, int k, int r, double *P, hipStream_t s);
 
 inline int64_t rank_pad32(int64_t r) { return (r + 31) / 32 * 32; }
 inline int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }

@@ -15,16 +15,14 @@
 // Yamamoto, "CholeskyQR2: a simple and communication-avoiding algorithm for
 // computing a tall-skinny QR factorization"): G = X^T X, G = C^T C with C
 // upper triangular, X <- X C^-1; the second pass restores the orthogonality
-// the first loses to rounding.  The panels stay on the GPU in fp32; the GPU
-// forms the residual products, the Gram matrices and every panel update (in
-// fp64 arithmetic).  The host does O(k^3) work only: the k x k Cholesky
-// factor and its inverse, and the k x k SVD (one-sided Jacobi rotations), in
-// double.  The call is synchronous.
-#include <algorithm>
-#include <cmath>
+// the first loses to rounding.  Every step runs on the GPU, in order on the
+// caller's stream: the residual products, the Gram matrices and the panel
+// updates (fp64 arithmetic on fp32 panels), and the k x k steps (each
+// Cholesky factor's inverse, and the final SVD by one-sided Jacobi
+// rotations) in fp64 by one workgroup each.  The call only enqueues work:
+// it never waits for the device, so it can be captured in a graph.
 #include <cstdint>
-#include <cstring>
-#include <vector>
+#include <utility>
 
 #include "internal.h"
 #include "qlora.h"
@@ -32,92 +30,13 @@
 namespace qlora {
 namespace {
 
-using Mat = std::vector<double>;   // row-major
-
-// T = C^-1 for the upper-triangular Cholesky factor C of the k x k Gram
-// matrix G (G = C^T C).  A column whose remaining squared length falls to
-// 1e-12 of its own (or to nothing) depends on the columns before it: its row
-// of C and its column of T are zero, so it leaves the panel as a zero
-// column, as it would from Gram-Schmidt.
-void cholesky_inverse(const Mat &G, int k, Mat &T) {
-  Mat C(size_t(k) * k, 0.0);
-  std::vector<char> live(k, 0);
-  for (int j = 0; j < k; ++j) {
-    double d = G[j * k + j];
-    for (int p = 0; p < j; ++p) d -= C[p * k + j] * C[p * k + j];
-    const double own = G[j * k + j];
-    if (!(own > 1e-300) || !(d > 1e-12 * own)) continue;
-    live[j] = 1;
-    const double cjj = std::sqrt(d);
-    C[j * k + j] = cjj;
-    for (int l = j + 1; l < k; ++l) {
-      double v = G[j * k + l];
-      for (int p = 0; p < j; ++p) v -= C[p * k + j] * C[p * k + l];
-      C[j * k + l] = v / cjj;
-    }
-  }
-  // back substitution, one column of T at a time: C T = I on the live set
-  T.assign(size_t(k) * k, 0.0);
-  for (int j = 0; j < k; ++j) {
-    if (!live[j]) continue;
-    T[j * k + j] = 1.0 / C[j * k + j];
-    for (int i = j - 1; i >= 0; --i) {
-      if (!live[i]) continue;
-      double v = 0.0;
-      for (int p = i + 1; p <= j; ++p) v += C[i * k + p] * T[p * k + j];
-      T[i * k + j] = -v / C[i * k + i];
-    }
-  }
-}
-
-// One-sided Jacobi SVD of a square k x k matrix G: rotate column pairs until
-// all are orthogonal; then G V = U S with V the accumulated rotations, S the
-// column norms.  G is overwritten by U S.
-void jacobi_svd(Mat &G, Mat &V, std::vector<double> &S, int k) {
-  V.assign(size_t(k) * k, 0.0);
-  for (int i = 0; i < k; ++i) V[i * k + i] = 1.0;
-  for (int sweep = 0; sweep < 80; ++sweep) {
-    bool rotated = false;
-    for (int p = 0; p < k - 1; ++p)
-      for (int q = p + 1; q < k; ++q) {
-        double a = 0.0, b = 0.0, g = 0.0;
-        for (int i = 0; i < k; ++i) {
-          a += G[i * k + p] * G[i * k + p];
-          b += G[i * k + q] * G[i * k + q];
-          g += G[i * k + p] * G[i * k + q];
-        }
-        if (std::fabs(g) <= 1e-15 * std::sqrt(a * b) || g == 0.0) continue;
-        rotated = true;
-        const double zeta = (b - a) / (2.0 * g);
-        const double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
-        const double c = 1.0 / std::sqrt(1.0 + t * t), s = c * t;
-        for (int i = 0; i < k; ++i) {
-          const double gp = G[i * k + p], gq = G[i * k + q];
-          G[i * k + p] = c * gp - s * gq;
-          G[i * k + q] = s * gp + c * gq;
-          const double vp = V[i * k + p], vq = V[i * k + q];
-          V[i * k + p] = c * vp - s * vq;
-          V[i * k + q] = s * vp + c * vq;
-        }
-      }
-    if (!rotated) break;
-  }
-  S.assign(k, 0.0);
-  for (int j = 0; j < k; ++j) {
-    double n2 = 0.0;
-    for (int i = 0; i < k; ++i) n2 += G[i * k + j] * G[i * k + j];
-    S[j] = std::sqrt(n2);
-  }
-}
-
-// Device panels and the small host buffers of one call.
+// The device buffers of one call.
 struct Ctx {
   const float *W0;
   const qlora_nf4 *wq;
-  double *dG, *dT;     // device [k x k] Gram matrix, [2 k x k] transforms
-  float *rpart;        // device partial products of the residual products
-  double *gpart;       // device partial Gram matrices
-  Mat hG, hT;
+  double *dG, *dT;     // [k x k] Gram matrix; [k x k] transform or the [2 k x r] factors
+  float *rpart;        // partial products of the residual products
+  double *gpart;       // partial Gram matrices
   hipStream_t s;
 };
 
@@ -128,29 +47,14 @@ hipError_t residual_product(const Ctx &c, const float *M, int k, float *Y, bool 
                              transpose, c.wq->codebook, c.rpart, c.s);
 }
 
-// H [ka x kb] on the host = X^T . Y (device panels [rows x ka], [rows x kb]).
-hipError_t gram_to_host(Ctx &c, const float *X, int ka, const float *Y, int kb, int64_t rows,
-                        Mat &H) {
-  hipError_t e = launch_panel_gram(X, ka, Y, kb, rows, c.dG, c.gpart, c.s);
-  if (e != hipSuccess) return e;
-  H.assign(size_t(ka) * kb, 0.0);
-  e = hipMemcpyAsync(H.data(), c.dG, sizeof(double) * H.size(), hipMemcpyDeviceToHost, c.s);
-  if (e != hipSuccess) return e;
-  return hipStreamSynchronize(c.s);
-}
-
 // Orthonormal columns of the device panel X [rows x k] (Cholesky QR, twice);
 // Xt is a panel of the same size used in between.  The result is in X.
 hipError_t orthonormalize(Ctx &c, float *X, float *Xt, int64_t rows, int k) {
   float *src = X, *dst = Xt;
   for (int pass = 0; pass < 2; ++pass) {
-    hipError_t e = gram_to_host(c, src, k, src, k, rows, c.hG);
+    hipError_t e = launch_panel_gram(src, k, src, k, rows, c.dG, c.gpart, c.s);
     if (e != hipSuccess) return e;
-    cholesky_inverse(c.hG, k, c.hT);
-    // (the host buffer is rewritten only after the next synchronisation,
-    // which follows this copy on the stream)
-    e = hipMemcpyAsync(c.dT, c.hT.data(), sizeof(double) * c.hT.size(), hipMemcpyHostToDevice,
-                       c.s);
+    e = launch_chol_inv(c.dG, k, c.dT, c.s);
     if (e != hipSuccess) return e;
     e = launch_panel_apply(src, k, c.dT, k, rows, dst, false, false, c.s);
     if (e != hipSuccess) return e;
@@ -214,7 +118,7 @@ extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, c
   double *dT = reinterpret_cast<double *>(take(2 * small_bytes(k)));
   float *rpart = reinterpret_cast<float *>(take(align256(residual_mul_partial_bytes(in, out, k))));
   double *gpart = reinterpret_cast<double *>(take(align256(panel_gram_partial_bytes(k))));
-  Ctx c{W0, wq, dG, dT, rpart, gpart, {}, {}, stream};
+  Ctx c{W0, wq, dG, dT, rpart, gpart, stream};
   auto run = [&]() -> hipError_t {
     hipError_t e;
 #define QLORA_TRY(x)              \
@@ -228,39 +132,19 @@ extern "C" qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, c
       QLORA_TRY(residual_product(c, Z, k, Y, false));
       QLORA_TRY(orthonormalize(c, Y, Yt, in, k));
     }
-    // R ~ Y Z^T with Z = R^T Y;  Z = Qz Rz
+    // R ~ Y Z^T with Z = R^T Y;  Z = Qz Rz, Rz = Qz^T Z;  from the SVD of
+    // Rz^T = U~ S W~^T:  A = Y U~_r S_r^(1/2),
+    // B^T = Qz W~_r S_r^(1/2) = Z U~_r S_r^(-1/2)  (Qz W~ = Qz Rz U~ S^-1)
     QLORA_TRY(residual_product(c, Y, k, Z, true));
     QLORA_TRY(hipMemcpyAsync(Qz, Z, sizeof(float) * size_t(out) * k, hipMemcpyDeviceToDevice,
                              stream));
     QLORA_TRY(orthonormalize(c, Qz, Zt, out, k));
-    Mat Rz;
-    QLORA_TRY(gram_to_host(c, Qz, k, Z, k, out, Rz));
-    Mat G(size_t(k) * k);                                 // G = Rz^T
-    for (int a = 0; a < k; ++a)
-      for (int b = 0; b < k; ++b) G[a * k + b] = Rz[b * k + a];
-    Mat W;
-    std::vector<double> S;
-    jacobi_svd(G, W, S, k);                               // G W = U~ S
-    std::vector<int> ord(k);
-    for (int j = 0; j < k; ++j) ord[j] = j;
-    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return S[x] > S[y]; });
-    // A = Y Pa, B^T = Qz Pb with Pa = (U~)_r sqrt(S_r), Pb = (W~)_r sqrt(S_r)
-    Mat P(size_t(2) * k * r, 0.0);
-    double *Pa = P.data(), *Pb = P.data() + size_t(k) * r;
-    for (int cc = 0; cc < r; ++cc) {
-      const int j = ord[cc];
-      const double sj = S[j], sq = std::sqrt(sj);
-      for (int a = 0; a < k; ++a) {
-        Pa[a * r + cc] = sj > 0 ? G[a * k + j] / sq : 0.0;
-        Pb[a * r + cc] = W[a * k + j] * sq;
-      }
-    }
-    QLORA_TRY(hipMemcpyAsync(c.dT, P.data(), sizeof(double) * P.size(), hipMemcpyHostToDevice,
-                             stream));
+    QLORA_TRY(launch_panel_gram(Qz, k, Z, k, out, c.dG, c.gpart, stream));
+    QLORA_TRY(launch_small_svd(c.dG, k, r, c.dT, stream));
     const bool b16 = adt == QLORA_BF16;
     QLORA_TRY(launch_panel_apply(Y, k, c.dT, r, in, A, false, b16, stream));
-    QLORA_TRY(launch_panel_apply(Qz, k, c.dT + size_t(k) * r, r, out, B, true, b16, stream));
-    return hipStreamSynchronize(stream);   // (P is read by the copy above)
+    QLORA_TRY(launch_panel_apply(Z, k, c.dT + size_t(k) * r, r, out, B, true, b16, stream));
+    return hipSuccess;
 #undef QLORA_TRY
   };
   return run() == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE;

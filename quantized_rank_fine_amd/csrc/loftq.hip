@@ -13,6 +13,8 @@
 // products are orthonormalised here as well (Cholesky QR applied twice: the
 // k x k Gram matrix and the panel update run on the GPU in fp64 arithmetic),
 // and the final factors are formed from them.
+#include <type_traits>
+
 #include "device.h"
 
 namespace qlora {
@@ -395,15 +397,257 @@ __global__ __launch_bounds__(256) void panel_apply_kernel(const float *X, int k,
   }
 }
 
+// ---- k x k steps of the orthonormalisation and of the final SVD, one
+// workgroup each, in fp64, so that the call never waits for the host.
+
+// T = C^-1 for the upper-triangular Cholesky factor C of the k x k Gram
+// matrix G = C^T C (Cholesky QR, Fukaya et al.).  A column whose remaining
+// squared length falls to 1e-12 of its own (or to nothing) depends on the
+// columns before it: its row of C and its column of T are zero, so it leaves
+// the panel as a zero column, as it would from Gram-Schmidt.  One wavefront:
+// G is factored in place in LDS (right-looking: row j of C is finished at
+// step j and the trailing upper triangle updated, so entry (j, l) receives
+// the subtractions of rows 0 .. j-1 in that order); then lane t forms
+// columns t, t + 64 of T by back substitution, each column stored in the
+// free lower triangle (T[i][j], i < j, at row j, column i; the diagonal
+// apart), so the lanes need no barrier between rows.
+constexpr int kCholThreads = 64;
+
+// The k x k row-major src (global fp64) into LDS with row pitch P, by nt
+// threads, 16 loads per thread in flight before any is stored.
+__device__ __forceinline__ void load_small(double *dst, const double *src, int k, int P, int t,
+                                           int nt) {
+  const int n = k * k;
+  for (int base = 0; base < n; base += 16 * nt) {
+    double v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = base + u * nt + t;
+      v[u] = src[e < n ? e : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = base + u * nt + t;
+      if (e < n) dst[(e / k) * P + e % k] = v[u];
+    }
+  }
+}
+
+constexpr int kSmallLds = kMaxK * (kMaxK + 1);
+
+__global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const double *G, int k, double *T) {
+  __shared__ double sA[kMaxK * (kMaxK + 8)];
+  __shared__ double sDiag[kMaxK], sTd[kMaxK];
+  __shared__ int sLive[kMaxK];
+  const int t = threadIdx.x, P = (k + 7) | 1;       // odd pitch, >= 7 zero columns past k
+  for (int e = t; e < k * P; e += kCholThreads) sA[e] = 0.0;
+  __syncthreads();
+  load_small(sA, G, k, P, t, kCholThreads);
+  __syncthreads();
+  for (int j = t; j < k; j += kCholThreads) sDiag[j] = sA[j * P + j];
+  __syncthreads();
+  for (int j = 0; j < k; ++j) {
+    const double d = sA[j * P + j], own = sDiag[j];
+    const bool live = own > 1e-300 && d > 1e-12 * own;
+    double inv = 0.0;
+    if (live) {                                      // 1 / sqrt(d): rsq and one Newton step
+      inv = __builtin_amdgcn_rsq(d);
+      inv = inv * __builtin_fma(-0.5 * d * inv, inv, 1.5);
+    }
+    const double cjj = d * inv;
+    __syncthreads();                                 // every lane has read d
+    for (int l = j + t; l < k; l += kCholThreads)
+      sA[j * P + l] = live ? (l == j ? cjj : sA[j * P + l] * inv) : 0.0;
+    if (t == 0) {
+      sLive[j] = live;
+      sTd[j] = inv;                                  // T[j][j] = 1 / C[j][j]
+    }
+    __syncthreads();                                 // row j of C is final
+    // trailing update, one row l per lane: A[l][m] -= C[j][l] C[j][m], m >= l
+    // (8 columns at a time; the zero columns past k absorb the overshoot)
+    for (int l = j + 1 + t; l < k; l += kCholThreads) {
+      const double cl = sA[j * P + l];
+      for (int m0 = l; m0 < k; m0 += 8) {
+        double cm[8], am[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          cm[u] = sA[j * P + m0 + u];
+          am[u] = sA[l * P + m0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sA[l * P + m0 + u] = __builtin_fma(-cl, cm[u], am[u]);
+      }
+    }
+    __syncthreads();
+  }
+  for (int j = t; j < k; j += kCholThreads) {
+    const double tjj = sTd[j];
+    for (int i = j - 1; i >= 0; --i) {
+      double v = 0.0;
+      if (sLive[i]) {
+        double acc = sA[i * P + j] * tjj;            // p = j
+#pragma unroll 8
+        for (int p = j - 1; p > i; --p) acc = __builtin_fma(sA[i * P + p], sA[j * P + p], acc);
+        v = -acc * sTd[i];
+      }
+      sA[j * P + i] = v;                             // T[i][j]
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < k * k; e += kCholThreads) {
+    const int i = e / k, j = e - i * k;
+    T[e] = i < j ? sA[j * P + i] : (i == j ? sTd[j] : 0.0);
+  }
+}
+
+// v summed over the four lanes of its quad (DPP quad permutations).
+__device__ __forceinline__ double quad_sum(double v) {
+  auto perm = [](double x, auto ctrl) {
+    constexpr int c = decltype(ctrl)::value;
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), c, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), c, 0xF, 0xF, true);
+    return __hiloint2double(hi, lo);
+  };
+  v += perm(v, std::integral_constant<int, 0xB1>{});   // lanes ^ 1
+  v += perm(v, std::integral_constant<int, 0x4E>{});   // lanes ^ 2
+  return v;
+}
+
+// The rank-r factors of the k x k matrix Rz^T (Rz = Qz^T Z, row-major):
+// one-sided Jacobi SVD (Hestenes) of G = Rz^T -- column pairs are rotated
+// until every pair is orthogonal, so that G V = U S with orthonormal V and
+// the rotated columns g_j = u_j s_j -- and then P = [Pa | Pb'] [k x r each]
+// for the r largest singular values in descending order (ties: lower index
+// first): Pa = U_r S_r^(1/2), column j of Pb' = g_j / s_j^(3/2).  V is not
+// formed: Qz V_r S_r^(1/2) = Qz Rz U_r S_r^(-1/2) = Z Pb', so B^T = Z Pb'
+// (Z = Qz Rz, Qz an orthonormal basis of Z's columns).  A sweep visits every pair once in the round-robin order (k/2
+// disjoint pairs per step, one quad of lanes each); sweeps repeat until one
+// rotates nothing (|g_p . g_q| <= 1e-10 |g_p| |g_q|: singular vectors far
+// beyond the fp32 accuracy of the factors), at most 80.  The
+// workgroup has 4 lanes per pair (one wavefront up to k = 32); a lane keeps
+// its rows of the pair's two columns in registers for the step.
+constexpr int kSvdMaxThreads = 4 * (kMaxK / 2);
+
+template <int RPL>   // rows of G per lane: k <= 4 RPL
+__global__ __launch_bounds__(kSvdMaxThreads) void small_svd_kernel(const double *Rz, int k, int r,
+                                                                   double *P) {
+  // column j of G at sG[j LP ..] (row j of Rz), rows k .. 4 RPL - 1 and the
+  // round robin's padding column k (odd k) zero, so that every access of a
+  // step is unconditional: zero rows and columns stay zero under rotation
+  __shared__ double sG[kSmallLds];
+  __shared__ double sS[kMaxK];
+  __shared__ int sOrd[kMaxK];
+  __shared__ int sRot;
+  constexpr int LP = 4 * RPL + 1;
+  const int t = threadIdx.x, nt = blockDim.x, g = t >> 2, li = t & 3;
+  const int kp = (k + 1) & ~1;                       // players of the round robin
+  for (int e = t; e < kp * LP; e += nt) sG[e] = 0.0;
+  __syncthreads();
+  load_small(sG, Rz, k, LP, t, nt);
+  const int n1 = kp - 1;
+  // round-robin positions: pair g holds the players at positions g and
+  // kp - 1 - g; position 0 keeps player 0, position m >= 1 holds player
+  // (m - 1 + step) mod (kp - 1) + 1
+  auto player = [&](int m, int step) {
+    if (m == 0) return 0;
+    int v = m - 1 + step;
+    if (v >= n1) v -= n1;
+    return v + 1;
+  };
+  for (int sweep = 0; sweep < 80; ++sweep) {
+    if (t == 0) sRot = 0;
+    __syncthreads();
+    for (int step = 0; step < n1; ++step) {
+      if (g < kp / 2) {
+        double *gp = sG + player(g, step) * LP + li, *gq = sG + player(kp - 1 - g, step) * LP + li;
+        double x[RPL], y[RPL];
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+          x[u] = gp[4 * u];
+          y[u] = gq[4 * u];
+        }
+        double a = 0.0, b = 0.0, c = 0.0;
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+          a = __builtin_fma(x[u], x[u], a);
+          b = __builtin_fma(y[u], y[u], b);
+          c = __builtin_fma(x[u], y[u], c);
+        }
+        a = quad_sum(a);
+        b = quad_sum(b);
+        c = quad_sum(c);
+        if (c != 0.0 && c * c > 1e-20 * (a * b)) {
+          // tan of the rotation angle, t = sign(z) / (|z| + sqrt(1 + z^2)) for
+          // z = (b - a) / 2c, in fp32 (1 / 2z where |z| > 1e15): an angle
+          // good to fp32 leaves the pair's product at a 1e-7 fraction, taken
+          // up by the next sweep; cos and sin from t in fp64, so the rotation
+          // is orthogonal to fp64 rounding
+          const double zeta = (b - a) / (2.0 * c);
+          double tt;
+          if (fabs(zeta) > 1e15) {
+            tt = 0.5 / zeta;
+          } else {
+            const float zf = float(zeta);
+            tt = double(copysignf(1.0f, zf) / (fabsf(zf) + sqrtf(fmaf(zf, zf, 1.0f))));
+          }
+          const double w = __builtin_fma(tt, tt, 1.0);
+          double cs = __builtin_amdgcn_rsq(w);
+          cs = cs * __builtin_fma(-0.5 * w * cs, cs, 1.5);          // one Newton step
+          const double sn = cs * tt;
+#pragma unroll
+          for (int u = 0; u < RPL; ++u) {
+            gp[4 * u] = cs * x[u] - sn * y[u];
+            gq[4 * u] = sn * x[u] + cs * y[u];
+          }
+          if (li == 0) sRot = 1;
+        }
+      }
+      __syncthreads();
+    }
+    const int rot = sRot;
+    __syncthreads();                                 // every thread has read the flag
+    if (!rot) break;
+  }
+  for (int j = t; j < kMaxK; j += nt) sOrd[j] = 0;   // (no gaps even if S holds NaN)
+  for (int j = t; j < k; j += nt) {
+    double n2 = 0.0;
+    for (int i = 0; i < k; ++i) n2 = __builtin_fma(sG[j * LP + i], sG[j * LP + i], n2);
+    sS[j] = sqrt(n2);
+  }
+  __syncthreads();
+  for (int j = t; j < k; j += nt) {
+    int rank = 0;
+    for (int i = 0; i < k; ++i) rank += (sS[i] > sS[j]) || (sS[i] == sS[j] && i < j);
+    sOrd[rank] = j;
+  }
+  __syncthreads();
+  double *Pa = P, *Pb = P + k * r;
+  for (int e = t; e < k * r; e += nt) {
+    const int a = e / r, cc = e - a * r, j = sOrd[cc];
+    const double sj = sS[j];
+    double pa = 0.0, pb = 0.0;
+    if (sj > 0.0) {
+      const double sq = sqrt(sj), gj = sG[j * LP + a];
+      pa = gj / sq;
+      pb = gj / (sj * sq);
+    }
+    Pa[e] = pa;
+    Pb[e] = pb;
+  }
+}
+
 }  // namespace
 
 namespace {
 
 // Slices of the summed axis (each a whole number of chunks of `ch`) so that a
-// product with `base` workgroups launches about 1024.
+// product of `base` wavefronts launches about 2048, two per SIMD, so that one
+// wavefront's loads are in flight while the other multiplies (1024: one per
+// SIMD took 34 and 41 us for the two products at 4096^2, 2048: 28 and 33 us;
+// 4096 gained nothing more).
 int64_t slice_span(int64_t base, int64_t len, int64_t ch) {
   const int64_t chunks = (len + ch - 1) / ch;
-  int64_t S = (1024 + base - 1) / base;
+  int64_t S = (2048 + base - 1) / base;
   if (S > chunks) S = chunks;
   if (S > kMaxSlices) S = kMaxSlices;
   if (S < 1) S = 1;
@@ -491,6 +735,25 @@ hipError_t launch_panel_apply(const float *X, int k, const double *T, int m, int
   const dim3 g(unsigned((rows + 31) / 32), unsigned((m + 31) / 32));
   hipLaunchKernelGGL(panel_apply_kernel, g, dim3(256), 0, s, X, k, T, m, rows, Out, transposed,
                      bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_chol_inv(const double *G, int k, double *T, hipStream_t s) {
+  if (k < 1 || k > kMaxK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kCholThreads), 0, s, G, k, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_svd(const double *Rz, int k, int r, double *P, hipStream_t s) {
+  if (k < 1 || k > kMaxK || r < 1 || r > k) return hipErrorInvalidValue;
+  const int pairs = (k + 1) / 2;
+  const unsigned threads = unsigned((4 * pairs + 63) / 64 * 64);   // whole wavefronts
+  if (k <= 32)
+    hipLaunchKernelGGL(small_svd_kernel<8>, dim3(1), dim3(threads), 0, s, Rz, k, r, P);
+  else if (k <= 64)
+    hipLaunchKernelGGL(small_svd_kernel<16>, dim3(1), dim3(threads), 0, s, Rz, k, r, P);
+  else
+    hipLaunchKernelGGL(small_svd_kernel<32>, dim3(1), dim3(threads), 0, s, Rz, k, r, P);
   return hipGetLastError();
 }
 

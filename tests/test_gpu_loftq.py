@@ -37,13 +37,17 @@ def _init(W0, wq, k, r, iters, adt="f32", seed=0):
     return A, B
 
 
-@pytest.mark.parametrize("n_in,n_out", [(256, 384), (192, 320)])
-def test_low_rank_residual_is_recovered(n_in, n_out):
+@pytest.mark.parametrize("n_in,n_out,k", [(256, 384, 12), (192, 320, 12), (256, 384, 13),
+                                          (256, 384, 4)])
+def test_low_rank_residual_is_recovered(n_in, n_out, k):
     """W0 = fp32(deq(Wq)) + P with P of rank 4: the residual is P (up to
     the fp32 rounding of the dequantized weight) and A B recovers it
-    (192 x 320: half-filled last workgroups of both residual products)."""
+    (192 x 320: half-filled last workgroups of both residual products; k =
+    13: an odd number of columns for the pairwise rotations of the small
+    SVD; the columns past rank 4 are dependent and leave the Cholesky QR as
+    zero columns; k = 4 = r: no oversampling)."""
     torch, dev = torch_dev()
-    say(f"[loftq] rank-4 residual {n_in}x{n_out}")
+    say(f"[loftq] rank-4 residual {n_in}x{n_out} k={k}")
     w0 = synth.weights(n_in, n_out, workload=7)
     wq = quantize_gpu(w0)
     W_hat = _w_hat(w0)
@@ -51,17 +55,17 @@ def test_low_rank_residual_is_recovered(n_in, n_out):
     P = (g.standard_normal((n_in, 4)) @ g.standard_normal((4, n_out)) * 0.01).astype(np.float32)
     W0 = (W_hat.astype(np.float32) + P).astype(np.float32)
     R = W0.astype(np.float64) - W_hat
-    A, B = _init(torch.from_numpy(W0).to(dev), wq, 12, 4, 2)
+    A, B = _init(torch.from_numpy(W0).to(dev), wq, k, 4, 2)
     AB = A.cpu().numpy().astype(np.float64) @ B.cpu().numpy().astype(np.float64)
     assert np.abs(AB - R).max() <= 1e-4 * np.abs(R).max()
 
 
 @pytest.mark.parametrize("codebook,k,r,iters", [(q.CB_NF4, 24, 16, 3), (q.CB_UNIFORM4, 24, 16, 3),
-                                                (q.CB_NF4, 96, 64, 4)])
+                                                (q.CB_NF4, 96, 64, 4), (q.CB_NF4, 128, 64, 2)])
 def test_quantization_residual_near_optimal(codebook, k, r, iters):
     """On a real quantization residual the rank-r start removes at least 90 %
     of what the exact truncated SVD removes, and its factors are balanced
-    (k = 96 takes the wide-panel kernels)."""
+    (k = 96 takes the wide-panel kernels; k = 128 is the largest panel)."""
     torch, dev = torch_dev()
     w0 = synth.weights(512, 768, workload=7)
     wq = quantize_gpu(w0, codebook)
@@ -124,3 +128,50 @@ def test_group16_quantization_residual_near_optimal():
     e_opt = np.sum((R - Ao @ Bo) ** 2)
     e_gpu = np.sum((R - An @ Bn) ** 2)
     assert e_gpu <= e_opt + 0.1 * (full - e_opt), (full, e_opt, e_gpu)
+
+
+def test_graph_replays_match_eager():
+    """The whole start (products, Cholesky QR steps, the small SVD) is
+    enqueued on the stream without waiting for the device, so it can be
+    captured in a graph: every replay, with eager work between replays, gives
+    the bits of the eager call, and two eager calls agree bit for bit."""
+    torch, dev = torch_dev()
+    say("[loftq] graph capture 256x384 k=24 r=16")
+    w0 = synth.weights(256, 384, workload=7)
+    wq = quantize_gpu(w0)
+    W0 = torch.from_numpy(w0).to(dev)
+    g = torch.Generator(device="cpu").manual_seed(3)
+    k, r = 24, 16
+    omega = torch.randn(wq.n_out, k, generator=g).to(dev)
+    A = torch.empty(wq.n_in, r, dtype=torch.float32, device=dev)
+    B = torch.empty(r, wq.n_out, dtype=torch.float32, device=dev)
+    wsb = q.qlora_loftq_workspace_bytes(wq.n_in, wq.n_out, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def call():
+        q.qlora_loftq_init(W0, wq, omega, k, r, 2, A, B, q.F32, ws, wsb)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (A.cpu().numpy().copy(), B.cpu().numpy().copy())
+    call()
+    torch.cuda.synchronize()
+    assert np.array_equal(A.cpu().numpy(), ref[0]) and np.array_equal(B.cpu().numpy(), ref[1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        A.fill_(float("nan"))                # eager work between replays
+        B.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(A.cpu().numpy(), ref[0]), rep
+        assert np.array_equal(B.cpu().numpy(), ref[1]), rep
