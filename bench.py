@@ -841,6 +841,16 @@ def main():
     torch.cuda.synchronize()
     q.qlora_timing_disable()
 
+    # Quantize alone: K launches back to back over the cycled W0 buffers
+    # between one event pair (no per-launch event in between).
+    eq0, eq1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eq0.record()
+    for i in range(K):
+        q.qlora_quantize(W0s[i % N_W0], wq)
+    eq1.record()
+    torch.cuda.synchronize()
+    qbb_us = eq0.elapsed_time(eq1) * 1e3 / K
+
     # The uniform 4-bit codebook on the same kernels: the same K steps with a
     # weight quantized to that grid (quantize GB/s and fwd+bwd TFLOP/s).
     wq_u = q.NF4Weight(n_in, n_out, dev, q.CB_UNIFORM4)
@@ -993,6 +1003,8 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / K
     q_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
     fb_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
+    fb_us = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
+    q_us = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
     flops = workloads.fwd_flops(M, n_in, n_out, r) + workloads.bwd_flops(M, n_in, n_out, r)
     qbytes = workloads.quantize_bytes(n_in, n_out)
     value = K * flops / (fb_ms * 1e-3) / 1e12
@@ -1064,6 +1076,16 @@ def main():
         "quantize_frac_hbm": round(q_gbps / PEAK_HBM_GBPS, 4),
         "fwd_bwd_ms_per_step": round(fb_ms / K, 4),
         "quantize_ms_per_step": round(q_ms / K, 4),
+        "fwd_bwd_us_per_step_p10_median_p90": [round(fb_us[len(fb_us) // 10], 2),
+                                               round(fb_us[len(fb_us) // 2], 2),
+                                               round(fb_us[(9 * len(fb_us)) // 10], 2)],
+        "quantize_back_to_back": {"us": round(qbb_us, 2),
+                                  "GBps": round(qbytes / (qbb_us * 1e-6) / 1e9, 1),
+                                  "frac_hbm_peak": round(qbytes / (qbb_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                                  "what": f"{K} quantize launches over the {N_W0} cycled W0 buffers between one event pair"},
+        "quantize_us_per_step_p10_median_p90": [round(q_us[len(q_us) // 10], 2),
+                                                round(q_us[len(q_us) // 2], 2),
+                                                round(q_us[(9 * len(q_us)) // 10], 2)],
         "fwd_bwd_frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "kernels": kernels,
