@@ -246,6 +246,28 @@ def test_65b_layer_r64_M8192_sampled(name, n_in, n_out, li):
     _check(L, rows=rows, tag=f"65b {name} r64 M8192")
 
 
+def test_zero_tokens():
+    """M = 0 (an empty token batch): the forward is a no-op that needs no
+    workspace, and the backward writes dA = dB = 0, the sums over no tokens
+    (the NaN the buffers held is gone)."""
+    import torch
+    L = Layer(31, 8, 256, 384, 16)
+    dev = torch.device("cuda:0")
+    X = torch.empty(0, L.n_in, dtype=L.tdt, device=dev)
+    dY = torch.empty(0, L.n_out, dtype=L.tdt, device=dev)
+    Y = torch.empty(0, L.n_out, dtype=L.tdt, device=dev)
+    XA = torch.empty(0, L.r, dtype=torch.float32, device=dev)
+    dX = torch.empty(0, L.n_in, dtype=L.tdt, device=dev)
+    dA = torch.full((L.n_in, L.r), float("nan"), device=dev)
+    dB = torch.full((L.r, L.n_out), float("nan"), device=dev)
+    assert q.qlora_fwd_workspace_bytes(0, L.n_in, L.n_out, L.r, L.qact) == 0
+    assert q.qlora_bwd_workspace_bytes(0, L.n_in, L.n_out, L.r, L.qact) == 0
+    q.qlora_linear_fwd(L.wq, X, 0, L.qact, L.tA, L.tB, L.r, L.qadt, Y, XA, None, 0)
+    q.qlora_linear_bwd(L.wq, X, dY, 0, L.qact, L.tA, L.tB, L.r, L.qadt, XA, dX, dA, dB, None, 0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA).item() == 0 and torch.count_nonzero(dB).item() == 0
+
+
 def test_two_streams_concurrently():
     """Two layers on two non-default streams at once, each with its own
     workspace: every output equals the same call alone on the default stream
