@@ -396,7 +396,8 @@ qlora_status qlora_adam_step(float *theta, const float *grad, float *m, float *v
  *   GPU as well.  ws: qlora_loftq_workspace_bytes(in, out, k) bytes of device
  *   memory.  Asynchronous like the other calls: the work is enqueued on
  *   `stream` and the call never waits for the device, so it can be captured
- *   in a graph; A, B and ws must stay untouched until it has run.
+ *   in a graph; W0, omega, wq's arrays, A, B and ws must stay valid (and A,
+ *   B, ws untouched by other work) until the stream has run it.
  */
 qlora_status qlora_loftq_init(const float *W0, const qlora_nf4 *wq, const float *omega,
                               int32_t k, int32_t r, int32_t iters, void *A, void *B,
