@@ -175,3 +175,22 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert np.array_equal(A.cpu().numpy(), ref[0]), rep
         assert np.array_equal(B.cpu().numpy(), ref[1]), rep
+
+
+def test_square_panel_is_the_exact_svd():
+    """k = in = out = 64: the probe panel spans the whole space, so the start
+    is the exact truncated SVD of the residual (up to fp32 rounding): the
+    residual energy left matches the oracle's within 1e-4 of the total."""
+    torch, dev = torch_dev()
+    say("[loftq] 64x64 k=64 r=8")
+    w0 = synth.weights(64, 64, workload=7)
+    wq = quantize_gpu(w0)
+    W_hat = _w_hat(w0)
+    R = oracle.residual(w0, W_hat)
+    A, B = _init(torch.from_numpy(w0).to(dev), wq, 64, 8, 1)
+    An, Bn = A.cpu().numpy().astype(np.float64), B.cpu().numpy().astype(np.float64)
+    Ao, Bo = oracle.loftq_init(w0, W_hat, 8)
+    full = np.sum(R ** 2)
+    e_opt = np.sum((R - Ao @ Bo) ** 2)
+    e_gpu = np.sum((R - An @ Bn) ** 2)
+    assert abs(e_gpu - e_opt) <= 1e-4 * full, (full, e_opt, e_gpu)
