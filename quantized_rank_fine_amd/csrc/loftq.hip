@@ -578,18 +578,14 @@ __global__ __launch_bounds__(kSvdMaxThreads) void small_svd_kernel(const double 
         c = quad_sum(c);
         if (c != 0.0 && c * c > 1e-20 * (a * b)) {
           // tan of the rotation angle, t = sign(z) / (|z| + sqrt(1 + z^2)) for
-          // z = (b - a) / 2c, in fp32 (1 / 2z where |z| > 1e15): an angle
-          // good to fp32 leaves the pair's product at a 1e-7 fraction, taken
-          // up by the next sweep; cos and sin from t in fp64, so the rotation
-          // is orthogonal to fp64 rounding
+          // z = (b - a) / 2c (1 / 2z for |z| > 1e15: the same to fp64 rounding,
+          // and z^2 never overflows); cos and sin from t with one Newton step on rsq, so the
+          // rotation is orthogonal to fp64 rounding.  (An fp32 tangent took
+          // as many sweeps and was 4 % slower.)
           const double zeta = (b - a) / (2.0 * c);
-          double tt;
-          if (fabs(zeta) > 1e15) {
-            tt = 0.5 / zeta;
-          } else {
-            const float zf = float(zeta);
-            tt = double(copysignf(1.0f, zf) / (fabsf(zf) + sqrtf(fmaf(zf, zf, 1.0f))));
-          }
+          const double tt = fabs(zeta) > 1e15
+                                ? 0.5 / zeta
+                                : (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(__builtin_fma(zeta, zeta, 1.0)));
           const double w = __builtin_fma(tt, tt, 1.0);
           double cs = __builtin_amdgcn_rsq(w);
           cs = cs * __builtin_fma(-0.5 * w * cs, cs, 1.5);          // one Newton step
