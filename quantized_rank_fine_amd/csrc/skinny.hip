@@ -69,6 +69,43 @@ __device__ __forceinline__ uint32_t load1_bf16(const void *p, int64_t i) {
     return f32_to_bf16_bits(static_cast<const float *>(p)[i]);
 }
 
+// 8 consecutive elements as loaded (bf16: one 16-B piece; fp32: two), and
+// their conversion to the bf16x8 MFMA operand at the point of use.
+template <bool kBf16>
+struct Raw8 {
+  u32x4_t v[kBf16 ? 1 : 2];
+};
+
+template <bool kBf16>
+__device__ __forceinline__ Raw8<kBf16> buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  Raw8<kBf16> x;
+  x.v[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  if constexpr (!kBf16)
+    x.v[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+  return x;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ u32x4_t as_bf16x8_op(const Raw8<kBf16> &x) {
+  if constexpr (kBf16) {
+    return x.v[0];
+  } else {
+    const f32x4_t a = __builtin_bit_cast(f32x4_t, x.v[0]), b = __builtin_bit_cast(f32x4_t, x.v[1]);
+    return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                   pack_bf16x2(b[2], b[3])};
+  }
+}
+
+// The same 8 elements from a flat address.
+template <bool kBf16>
+__device__ __forceinline__ Raw8<kBf16> raw_load8(const void *p) {
+  Raw8<kBf16> x;
+  const u32x4_t *q = static_cast<const u32x4_t *>(p);
+  x.v[0] = q[0];
+  if constexpr (!kBf16) x.v[1] = q[1];
+  return x;
+}
+
 // Transposed read of a row-major bf16 LDS tile T (pitch PP elements): lane
 // (i16 = lane & 15, h = (lane >> 4) & 3) receives column cb + i16, rows
 // rb + 8h .. rb + 8h + 7 -- the k-run of one MFMA 16x16x32 operand lane --
@@ -215,66 +252,92 @@ struct RowdotArgs {
 // transposed element by element.
 constexpr int kQRows = 0, kQFast = 1, kQGeneric = 2;
 
-template <bool kPbf16, int kQMode, bool kQbf16, bool kWide>
-__device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, unsigned char *smem) {
-  constexpr int kTK = kWide ? 256 : 64;      // slice width
-  constexpr int kCPR = kTK / 8;              // 16-B chunks per staged Q row
+// One workgroup of rowdot with kRT 16-wide rank tiles (kGuard: at most kRT,
+// the actual count R / 16 rounded up read at run time).  Every global load of
+// a slice -- the Q chunks to stage and the P pieces of every substep -- is
+// issued before the first of them is used: out-of-range pieces load from an
+// in-range address (row 0, column 0, k0) and are replaced by zero at use, so
+// no load sits behind a branch and the waits count down the loads in order.
+template <bool kPbf16, int kQMode, bool kQbf16, int kTK, int kRT, bool kGuard>
+__device__ __forceinline__ void rowdot_body(const RowdotArgs &a, int64_t wg, unsigned char *smem) {
+  constexpr int kCPR = kTK / 8;              // 16-B chunks per staged Qt row
   constexpr int kNS = kTK / 32;              // MFMA k substeps per slice
-  constexpr int kMaxRT = kWide ? 4 : 16;     // 16-wide column tiles of R
   constexpr int kMask = (kCPR < 16 ? kCPR : 16) - 1;
+  constexpr int kNQ = (16 * kRT * kTK / 8 + 255) / 256;   // 16-B Q chunks per thread
+  constexpr int pes = kPbf16 ? 2 : 4, qes = kQbf16 ? 2 : 4;
   uint16_t *sQ = reinterpret_cast<uint16_t *>(smem);   // [RP][kTK], or [kTK][RP] (kQFast)
   const int R = a.R;
-  const int RT = (R + 15) / 16;
+  const int RT = kGuard ? (R + 15) / 16 : kRT;
   const int RP = RT * 16;
+  const int nq = RP * kTK / 8;               // 16-B Q chunks per slice
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i16 = lane & 15, h = lane >> 4;
+  const int64_t K = a.K;
   const int64_t m0 = (wg % a.mt) * kRowdotRows;
   const int ks = int(wg / a.mt);
   const int64_t kb = int64_t(ks) * a.kchunk;
-  const int64_t ke = min64(a.K, kb + a.kchunk);
+  const int64_t ke = min64(K, kb + a.kchunk);
   const int64_t row = m0 + wave * 16 + i16;
   const bool row_ok = row < a.M;
-  const size_t esz = kPbf16 ? 2 : 4;
-  const char *prow = static_cast<const char *>(a.P) + (row_ok ? row : 0) * a.K * esz;
+  const char *prow = static_cast<const char *>(a.P) + (row_ok ? row : 0) * K * pes;
+  const char *qbase = static_cast<const char *>(a.Q);
 
-  f32x4_t acc[kMaxRT];
+  f32x4_t acc[kRT];
 #pragma unroll
-  for (int s = 0; s < kMaxRT; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kRT; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t k0 = kb; k0 < ke; k0 += kTK) {
+    // Q chunks of this slice (kQRows: 8 k of one row j of Qt; kQFast: 8
+    // columns of one row k of Q), with their LDS places
+    Raw8<kQbf16> qv[kNQ];
+    bool qok[kNQ];
+    int qdst[kNQ];
+    if constexpr (kQMode != kQGeneric) {
+#pragma unroll
+      for (int u = 0; u < kNQ; ++u) {
+        if (kGuard && 256 * u >= nq) break;
+        const int cid = t + 256 * u;
+        int64_t off;
+        if constexpr (kQMode == kQRows) {
+          const int j = cid / kCPR, ch = cid % kCPR;
+          const int64_t k = k0 + 8 * ch;
+          qok[u] = j < R && k < ke;
+          off = qok[u] ? int64_t(j) * K + k : k0;
+          qdst[u] = j * kTK + ((ch ^ (j & kMask)) * 8);
+        } else {
+          const int C8 = RP / 8;
+          const int kk = cid / C8, c = cid - kk * C8;
+          const int64_t k = k0 + kk;
+          qok[u] = 8 * c < R && k < ke;
+          off = qok[u] ? k * R + 8 * c : k0 * R;
+          qdst[u] = kk * RP + 8 * c;
+        }
+        qv[u] = raw_load8<kQbf16>(qbase + off * qes);
+      }
+    }
     // A operands of this slice: substep s covers k0 + 32 s + 8 h .. +8
-    u32x4_t pv[kNS];
+    Raw8<kPbf16> pv[kNS];
+    bool pok[kNS];
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
       const int64_t k = k0 + 32 * s + 8 * h;
-      pv[s] = (row_ok && k < ke) ? load8_bf16<kPbf16>(prow + k * esz) : u32x4_t{0u, 0u, 0u, 0u};
+      pok[s] = row_ok && k < ke;
+      pv[s] = raw_load8<kPbf16>(prow + (pok[s] ? k : k0) * pes);
     }
     __syncthreads();                         // previous slice's readers are done
-    if constexpr (kQMode == kQRows) {
-      // rows of Qt are contiguous along k: one 16-B chunk = 8 k of one j
-      for (int cid = t; cid < RP * kCPR; cid += 256) {
-        const int j = cid / kCPR, ch = cid % kCPR;
-        const int64_t k = k0 + 8 * ch;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (j < R && k < ke)
-          v = load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (int64_t(j) * a.K + k) * (kQbf16 ? 2 : 4));
-        *reinterpret_cast<u32x4_t *>(sQ + j * kTK + ((ch ^ (j & kMask)) * 8)) = v;
-      }
-    } else if constexpr (kQMode == kQFast) {
-      // Q [K x R], R % 8 == 0: rows k0..k0+kTK-1 copied as 16-B chunks into
-      // [kTK][RP] (columns R..RP-1 zero)
-      const int C8 = RP / 8, R8 = R / 8;
-      for (int cid = t; cid < kTK * C8; cid += 256) {
-        const int kk = cid / C8, c = cid - kk * C8;
-        const int64_t k = k0 + kk;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (c < R8 && k < ke)
-          v = load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (k * R + 8 * c) * (kQbf16 ? 2 : 4));
-        *reinterpret_cast<u32x4_t *>(sQ + kk * RP + 8 * c) = v;
+    if constexpr (kQMode != kQGeneric) {
+      // columns R..RP-1 (kQFast) or rows R..RP-1 (kQRows) and k past ke are zero
+#pragma unroll
+      for (int u = 0; u < kNQ; ++u) {
+        if (kGuard && 256 * u >= nq) break;
+        const u32x4_t v = as_bf16x8_op<kQbf16>(qv[u]);
+        if (!kGuard || t + 256 * u < nq)
+          *reinterpret_cast<u32x4_t *>(sQ + qdst[u]) = qok[u] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     } else {
       // Q [K x R] row-major: coalesced element reads (16 in flight per
       // thread), transposed LDS writes
+#pragma unroll 1
       for (int e0 = 0; e0 < kTK * RP; e0 += 256 * 16) {
         uint16_t v[16];
 #pragma unroll
@@ -282,8 +345,9 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
           const int e = e0 + 256 * u + t;
           const int kk = e / RP, j = e - kk * RP;
           const int64_t k = k0 + kk;
-          v[u] = (e < kTK * RP && j < R && k < ke) ? uint16_t(load1_bf16<kQbf16>(a.Q, k * R + j))
-                                                   : uint16_t(0);
+          const bool ok = e < kTK * RP && j < R && k < ke;
+          const uint16_t x = uint16_t(load1_bf16<kQbf16>(a.Q, ok ? k * R + j : int64_t(0)));
+          v[u] = ok ? x : uint16_t(0);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -296,9 +360,11 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
+      const u32x4_t av0 = as_bf16x8_op<kPbf16>(pv[s]);
+      const u32x4_t av = pok[s] ? av0 : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int st = 0; st < kMaxRT; ++st) {
-        if (st < RT) {
+      for (int st = 0; st < kRT; ++st) {
+        if (!kGuard || st < RT) {
           u32x4_t b;
           if constexpr (kQMode == kQFast) {
             b = lds_col8(sQ, RP, 32 * s, 16 * st);
@@ -307,7 +373,7 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
             const int c = 4 * s + h;
             b = *reinterpret_cast<const u32x4_t *>(sQ + j * kTK + ((c ^ (j & kMask)) * 8));
           }
-          acc[st] = mfma16x16x32(pv[s], b, acc[st]);
+          acc[st] = mfma16x16x32(av, b, acc[st]);
         }
       }
     }
@@ -315,8 +381,8 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
   // C layout: lane holds rows 4h..4h+3 of the wave's 16, column i16 of subtile st
   float *out = a.part + int64_t(ks) * a.M * R;
 #pragma unroll
-  for (int st = 0; st < kMaxRT; ++st) {
-    if (st < RT) {
+  for (int st = 0; st < kRT; ++st) {
+    if (!kGuard || st < RT) {
       const int j = 16 * st + i16;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -324,6 +390,22 @@ __device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, uns
         if (m < a.M && j < R) out[m * R + j] = acc[st][q];
       }
     }
+  }
+}
+
+// R <= 64: 256-wide slices with the rank tile count fixed at compile time
+// (one body per count); larger R: 64-wide slices, up to 16 tiles.
+template <bool kPbf16, int kQMode, bool kQbf16, bool kWide>
+__device__ __forceinline__ void rowdot_role(const RowdotArgs &a, int64_t wg, unsigned char *smem) {
+  if constexpr (kWide) {
+    switch ((a.R + 15) / 16) {
+      case 1: rowdot_body<kPbf16, kQMode, kQbf16, 256, 1, false>(a, wg, smem); break;
+      case 2: rowdot_body<kPbf16, kQMode, kQbf16, 256, 2, false>(a, wg, smem); break;
+      case 3: rowdot_body<kPbf16, kQMode, kQbf16, 256, 3, false>(a, wg, smem); break;
+      default: rowdot_body<kPbf16, kQMode, kQbf16, 256, 4, false>(a, wg, smem); break;
+    }
+  } else {
+    rowdot_body<kPbf16, kQMode, kQbf16, 64, 16, true>(a, wg, smem);
   }
 }
 
@@ -358,33 +440,6 @@ struct RowfullArgs {
 
 __host__ __device__ inline int32_t clamp_records(int64_t bytes) {
   return bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : int32_t(bytes));
-}
-
-// 8 consecutive elements as loaded (bf16: one 16-B piece; fp32: two), and
-// their conversion to the bf16x8 MFMA operand at the point of use.
-template <bool kBf16>
-struct Raw8 {
-  u32x4_t v[kBf16 ? 1 : 2];
-};
-
-template <bool kBf16>
-__device__ __forceinline__ Raw8<kBf16> buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  Raw8<kBf16> x;
-  x.v[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  if constexpr (!kBf16)
-    x.v[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
-  return x;
-}
-
-template <bool kBf16>
-__device__ __forceinline__ u32x4_t as_bf16x8_op(const Raw8<kBf16> &x) {
-  if constexpr (kBf16) {
-    return x.v[0];
-  } else {
-    const f32x4_t a = __builtin_bit_cast(f32x4_t, x.v[0]), b = __builtin_bit_cast(f32x4_t, x.v[1]);
-    return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                   pack_bf16x2(b[2], b[3])};
-  }
 }
 
 // Per-wavefront Q staging of one batch (kQFast only): [kFullSteps * 32][RP],
