@@ -554,9 +554,11 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
   load_batch(0, xb[0], qb[0]);
   for (int b = 0; b < nb; b += 2) {
     load_batch(b + 1, xb[1], qb[1]);
+    __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the products
     compute_batch(xb[0], qb[0]);
     if (b + 1 >= nb) break;
     load_batch(b + 2, xb[0], qb[0]);
+    __builtin_amdgcn_sched_barrier(0);
     compute_batch(xb[1], qb[1]);
   }
 
@@ -610,17 +612,19 @@ struct ColdotArgs {
 // kQFastC: Q rows hold a multiple of 8 columns and are 16-B aligned (R % 8
 // == 0 or a zero-padded bf16 Q), so Q[mm..mm+63][0..RP) is copied row-major
 // with 16-B chunks and read transposed; otherwise Q^T is staged element by
-// element.
-template <bool kPbf16, bool kQbf16, bool kWide, bool kQFastC>
-__device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, unsigned char *smem) {
-  constexpr int kTN = kWide ? 256 : 64;
+// element.  kRT 16-wide rank tiles (kGuard: at most kRT, the actual count
+// read at run time).  Out-of-range P and Q pieces load from an in-range
+// address (token mb, column c0 or 0) and are stored to LDS as zero, so no
+// load sits behind a branch.
+template <bool kPbf16, bool kQbf16, int kTN, bool kQFastC, int kRT, bool kGuard>
+__device__ __forceinline__ void coldot_body(const ColdotArgs &a, int64_t wg, unsigned char *smem) {
   constexpr int kPP = kTN == 256 ? 272 : 80;  // LDS row pitch of the P tile (elements)
   constexpr int kCPR = kTN / 8;               // 16-B chunks per P row
   constexpr int kNP = 64 * kCPR / 256;        // P chunks per thread: 8 or 2
   constexpr int kNCT = kTN / 64;              // 16-wide column tiles per wavefront
-  constexpr int kMaxRT = kWide ? 4 : 16;
+  constexpr int pes = kPbf16 ? 2 : 4, qes = kQbf16 ? 2 : 4;
   const int R = a.R;
-  const int RT = (R + 15) / 16;
+  const int RT = kGuard ? (R + 15) / 16 : kRT;
   const int RP = RT * 16;
   uint16_t *sP = reinterpret_cast<uint16_t *>(smem);               // [64][kPP]
   uint16_t *sQ = sP + 64 * kPP;                        // [RP][64], or [64][RP] (kQFastC)
@@ -631,38 +635,53 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
   const int64_t mb = int64_t(ks) * a.mchunk;
   const int64_t me = min64(a.M, mb + a.mchunk);
   const int64_t K = a.K;
-  const size_t esz = kPbf16 ? 2 : 4;
   const char *P = static_cast<const char *>(a.P);
+  const char *Qb = static_cast<const char *>(a.Q);
 
-  f32x4_t acc[kNCT][kMaxRT];
+  f32x4_t acc[kNCT][kRT];
 #pragma unroll
   for (int c4 = 0; c4 < kNCT; ++c4)
 #pragma unroll
-    for (int s = 0; s < kMaxRT; ++s) acc[c4][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < kRT; ++s) acc[c4][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // P tile of tokens mm..mm+63 (and, kQFastC, the Q rows mm..mm+63 as 16-B
   // chunks) into registers; the next slice's loads are issued as soon as the
   // current slice is in LDS, so they are in flight during its products.
-  constexpr int kNQ = kQFastC ? (64 * (16 * kMaxRT) / 8 + 255) / 256 : 1;
+  constexpr int kNQ = kQFastC ? (64 * (16 * kRT) / 8 + 255) / 256 : 1;
   const int C8 = RP / 8;
-  u32x4_t pv[kNP], qv[kNQ];
+  Raw8<kPbf16> pv[kNP];
+  Raw8<kQbf16> qv[kNQ];
+  auto p_ok = [&](int64_t mm, int q, int64_t &m, int64_t &col, int &rr, int &ch) {
+    const int cid = t + 256 * q;
+    rr = cid / kCPR;
+    ch = cid % kCPR;
+    m = mm + rr;
+    col = c0 + 8 * ch;
+    return m < me && col < K;
+  };
+  auto q_ok = [&](int64_t mm, int q, int64_t &m, int &mi, int &c) {
+    const int cid = t + 256 * q;
+    mi = cid / C8;
+    c = cid - mi * C8;
+    m = mm + mi;
+    return cid < 64 * C8 && m < me && 8 * c < a.ldq;
+  };
   auto load_slice = [&](int64_t mm) {
 #pragma unroll
     for (int q = 0; q < kNP; ++q) {
-      const int cid = t + 256 * q;
-      const int rr = cid / kCPR, ch = cid % kCPR;
-      const int64_t m = mm + rr, col = c0 + 8 * ch;
-      pv[q] = (m < me && col < K) ? load8_bf16<kPbf16>(P + (m * K + col) * esz)
-                                  : u32x4_t{0u, 0u, 0u, 0u};
+      int64_t m, col;
+      int rr, ch;
+      const bool ok = p_ok(mm, q, m, col, rr, ch);
+      pv[q] = raw_load8<kPbf16>(P + (ok ? m * K + col : mb * K + c0) * pes);
     }
     if constexpr (kQFastC) {
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) {
-        const int cid = t + 256 * q, mi = cid / C8, c = cid - mi * C8;
-        const int64_t m = mm + mi;
-        qv[q] = (cid < 64 * C8 && m < me && 8 * c < a.ldq)
-                    ? load8_bf16<kQbf16>(static_cast<const char *>(a.Q) + (m * a.ldq + 8 * c) * (kQbf16 ? 2 : 4))
-                    : u32x4_t{0u, 0u, 0u, 0u};
+        if (kGuard && 256 * q >= 64 * C8) break;
+        int64_t m;
+        int mi, c;
+        const bool ok = q_ok(mm, q, m, mi, c);
+        qv[q] = raw_load8<kQbf16>(Qb + (ok ? m * a.ldq + 8 * c : mb * a.ldq) * qes);
       }
     }
   };
@@ -671,20 +690,28 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
     __syncthreads();                         // previous slice's readers are done
 #pragma unroll
     for (int q = 0; q < kNP; ++q) {
-      const int cid = t + 256 * q;
-      const int rr = cid / kCPR, ch = cid % kCPR;
-      *reinterpret_cast<u32x4_t *>(sP + rr * kPP + 8 * ch) = pv[q];
+      int64_t m, col;
+      int rr, ch;
+      const bool ok = p_ok(mm, q, m, col, rr, ch);
+      const u32x4_t v = as_bf16x8_op<kPbf16>(pv[q]);
+      *reinterpret_cast<u32x4_t *>(sP + rr * kPP + 8 * ch) = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
     if constexpr (kQFastC) {
       // Q rows mm..mm+63, columns 0..RP-1, as 16-B chunks into [64][RP]
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) {
-        const int cid = t + 256 * q, mi = cid / C8, c = cid - mi * C8;
-        if (cid < 64 * C8) *reinterpret_cast<u32x4_t *>(sQ + mi * RP + 8 * c) = qv[q];
+        if (kGuard && 256 * q >= 64 * C8) break;
+        int64_t m;
+        int mi, c;
+        const bool ok = q_ok(mm, q, m, mi, c);
+        const u32x4_t v = as_bf16x8_op<kQbf16>(qv[q]);
+        if (t + 256 * q < 64 * C8)
+          *reinterpret_cast<u32x4_t *>(sQ + mi * RP + 8 * c) = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     } else {
       // Q^T for tokens mm..mm+63: coalesced element reads of Q rows,
       // transposed LDS writes (16-B chunks of 8 tokens, swizzled by j)
+#pragma unroll 1
       for (int e0 = 0; e0 < 64 * RP; e0 += 256 * 16) {
         uint16_t v[16];
 #pragma unroll
@@ -692,8 +719,9 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
           const int e = e0 + 256 * u + t;
           const int mi = e / RP, j = e - mi * RP;
           const int64_t m = mm + mi;
-          v[u] = (e < 64 * RP && j < R && m < me) ? uint16_t(load1_bf16<kQbf16>(a.Q, m * a.ldq + j))
-                                                  : uint16_t(0);
+          const bool ok = e < 64 * RP && j < R && m < me;
+          const uint16_t x = uint16_t(load1_bf16<kQbf16>(a.Q, ok ? m * a.ldq + j : int64_t(0)));
+          v[u] = ok ? x : uint16_t(0);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -705,6 +733,7 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
     }
     __syncthreads();
     if (mm + 64 < me) load_slice(mm + 64);   // in flight during the products
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -725,8 +754,8 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
           av = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
         }
 #pragma unroll
-        for (int st = 0; st < kMaxRT; ++st) {
-          if (st < RT) {
+        for (int st = 0; st < kRT; ++st) {
+          if (!kGuard || st < RT) {
             u32x4_t b;
             if constexpr (kQFastC) {
               b = lds_col8(sQ, RP, 32 * u, 16 * st);
@@ -745,8 +774,8 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
 #pragma unroll
   for (int c4 = 0; c4 < kNCT; ++c4) {
 #pragma unroll
-    for (int st = 0; st < kMaxRT; ++st) {
-      if (st < RT) {
+    for (int st = 0; st < kRT; ++st) {
+      if (!kGuard || st < RT) {
         const int j = 16 * st + i16;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -755,6 +784,22 @@ __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, uns
         }
       }
     }
+  }
+}
+
+// R <= 64: 256 columns per workgroup with the rank tile count fixed at
+// compile time (one body per count); larger R: 64 columns, up to 16 tiles.
+template <bool kPbf16, bool kQbf16, bool kWide, bool kQFastC>
+__device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, unsigned char *smem) {
+  if constexpr (kWide) {
+    switch ((a.R + 15) / 16) {
+      case 1: coldot_body<kPbf16, kQbf16, 256, kQFastC, 1, false>(a, wg, smem); break;
+      case 2: coldot_body<kPbf16, kQbf16, 256, kQFastC, 2, false>(a, wg, smem); break;
+      case 3: coldot_body<kPbf16, kQbf16, 256, kQFastC, 3, false>(a, wg, smem); break;
+      default: coldot_body<kPbf16, kQbf16, 256, kQFastC, 4, false>(a, wg, smem); break;
+    }
+  } else {
+    coldot_body<kPbf16, kQbf16, 64, kQFastC, 16, true>(a, wg, smem);
   }
 }
 
