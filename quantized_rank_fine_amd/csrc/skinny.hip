@@ -253,19 +253,26 @@ struct RowdotArgs {
 constexpr int kQRows = 0, kQFast = 1, kQGeneric = 2;
 
 // One workgroup of rowdot with kRT 16-wide rank tiles (kGuard: at most kRT,
-// the actual count R / 16 rounded up read at run time).  Every global load of
-// a slice -- the Q chunks to stage and the P pieces of every substep -- is
-// issued before the first of them is used: out-of-range pieces load from an
-// in-range address (row 0, column 0, k0) and are replaced by zero at use, so
-// no load sits behind a branch and the waits count down the loads in order.
+// the actual count R / 16 rounded up read at run time).  A slice's P rows
+// (64 x kTK) and Q chunks are loaded with coalesced 16-B loads into
+// registers, stored to LDS, and the next slice's loads are issued before the
+// products of the current one, which read both operands from LDS.
+// Out-of-range pieces load from an in-range address (row m0 or 0, column
+// 0, k kb) and are stored as zero, so no load sits behind a branch.
+template <int kTK>
+__host__ __device__ constexpr int rowdot_ppitch() { return kTK + 8; }
+
 template <bool kPbf16, int kQMode, bool kQbf16, int kTK, int kRT, bool kGuard>
 __device__ __forceinline__ void rowdot_body(const RowdotArgs &a, int64_t wg, unsigned char *smem) {
-  constexpr int kCPR = kTK / 8;              // 16-B chunks per staged Qt row
+  constexpr int kCPR = kTK / 8;              // 16-B chunks per staged row
   constexpr int kNS = kTK / 32;              // MFMA k substeps per slice
   constexpr int kMask = (kCPR < 16 ? kCPR : 16) - 1;
   constexpr int kNQ = (16 * kRT * kTK / 8 + 255) / 256;   // 16-B Q chunks per thread
+  constexpr int kNP = kRowdotRows * kCPR / 256;            // 16-B P chunks per thread
+  constexpr int kPP = rowdot_ppitch<kTK>();
   constexpr int pes = kPbf16 ? 2 : 4, qes = kQbf16 ? 2 : 4;
-  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem);   // [RP][kTK], or [kTK][RP] (kQFast)
+  uint16_t *sP = reinterpret_cast<uint16_t *>(smem);   // [64][kPP]
+  uint16_t *sQ = sP + kRowdotRows * kPP;               // [RP][kTK], or [kTK][RP] (kQFast)
   const int R = a.R;
   const int RT = kGuard ? (R + 15) / 16 : kRT;
   const int RP = RT * 16;
@@ -277,62 +284,86 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs &a, int64_t wg, uns
   const int ks = int(wg / a.mt);
   const int64_t kb = int64_t(ks) * a.kchunk;
   const int64_t ke = min64(K, kb + a.kchunk);
-  const int64_t row = m0 + wave * 16 + i16;
-  const bool row_ok = row < a.M;
-  const char *prow = static_cast<const char *>(a.P) + (row_ok ? row : 0) * K * pes;
+  const char *Pb = static_cast<const char *>(a.P);
   const char *qbase = static_cast<const char *>(a.Q);
 
   f32x4_t acc[kRT];
 #pragma unroll
   for (int s = 0; s < kRT; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = kb; k0 < ke; k0 += kTK) {
-    // Q chunks of this slice (kQRows: 8 k of one row j of Qt; kQFast: 8
-    // columns of one row k of Q), with their LDS places
-    Raw8<kQbf16> qv[kNQ];
-    bool qok[kNQ];
-    int qdst[kNQ];
+  // P chunk q of slice k0: 8 k of row m0 + rr
+  auto p_chunk = [&](int64_t k0, int q, int64_t &off, int &dst) {
+    const int cid = t + 256 * q, rr = cid / kCPR, ch = cid % kCPR;
+    const int64_t m = m0 + rr, k = k0 + 8 * ch;
+    const bool ok = m < a.M && k < ke;
+    off = ok ? m * K + k : m0 * K + kb;
+    dst = rr * kPP + 8 * ch;
+    return ok;
+  };
+  // Q chunk cid of slice k0 (kQRows: 8 k of row j of Qt; kQFast: 8 columns
+  // of row k of Q)
+  auto q_chunk = [&](int64_t k0, int cid, int64_t &off, int &dst) {
+    bool ok;
+    if constexpr (kQMode == kQRows) {
+      const int j = cid / kCPR, ch = cid % kCPR;
+      const int64_t k = k0 + 8 * ch;
+      ok = j < R && k < ke;
+      off = ok ? int64_t(j) * K + k : kb;
+      dst = j * kTK + ((ch ^ (j & kMask)) * 8);
+    } else {
+      const int C8 = RP / 8;
+      const int kk = cid / C8, c = cid - kk * C8;
+      const int64_t k = k0 + kk;
+      ok = 8 * c < R && k < ke;
+      off = ok ? k * R + 8 * c : kb * R;
+      dst = kk * RP + 8 * c;
+    }
+    return ok;
+  };
+  Raw8<kPbf16> pv[kNP];
+  Raw8<kQbf16> qv[kNQ];
+  auto load_slice = [&](int64_t k0) {
     if constexpr (kQMode != kQGeneric) {
 #pragma unroll
       for (int u = 0; u < kNQ; ++u) {
         if (kGuard && 256 * u >= nq) break;
-        const int cid = t + 256 * u;
         int64_t off;
-        if constexpr (kQMode == kQRows) {
-          const int j = cid / kCPR, ch = cid % kCPR;
-          const int64_t k = k0 + 8 * ch;
-          qok[u] = j < R && k < ke;
-          off = qok[u] ? int64_t(j) * K + k : k0;
-          qdst[u] = j * kTK + ((ch ^ (j & kMask)) * 8);
-        } else {
-          const int C8 = RP / 8;
-          const int kk = cid / C8, c = cid - kk * C8;
-          const int64_t k = k0 + kk;
-          qok[u] = 8 * c < R && k < ke;
-          off = qok[u] ? k * R + 8 * c : k0 * R;
-          qdst[u] = kk * RP + 8 * c;
-        }
+        int dst;
+        q_chunk(k0, t + 256 * u, off, dst);
         qv[u] = raw_load8<kQbf16>(qbase + off * qes);
       }
     }
-    // A operands of this slice: substep s covers k0 + 32 s + 8 h .. +8
-    Raw8<kPbf16> pv[kNS];
-    bool pok[kNS];
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) {
-      const int64_t k = k0 + 32 * s + 8 * h;
-      pok[s] = row_ok && k < ke;
-      pv[s] = raw_load8<kPbf16>(prow + (pok[s] ? k : k0) * pes);
+    for (int q = 0; q < kNP; ++q) {
+      int64_t off;
+      int dst;
+      p_chunk(k0, q, off, dst);
+      pv[q] = raw_load8<kPbf16>(Pb + off * pes);
     }
+  };
+
+  load_slice(kb);
+  for (int64_t k0 = kb; k0 < ke; k0 += kTK) {
     __syncthreads();                         // previous slice's readers are done
+#pragma unroll
+    for (int q = 0; q < kNP; ++q) {
+      int64_t off;
+      int dst;
+      const bool ok = p_chunk(k0, q, off, dst);
+      const u32x4_t v = as_bf16x8_op<kPbf16>(pv[q]);
+      *reinterpret_cast<u32x4_t *>(sP + dst) = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
     if constexpr (kQMode != kQGeneric) {
       // columns R..RP-1 (kQFast) or rows R..RP-1 (kQRows) and k past ke are zero
 #pragma unroll
       for (int u = 0; u < kNQ; ++u) {
         if (kGuard && 256 * u >= nq) break;
+        int64_t off;
+        int dst;
+        const bool ok = q_chunk(k0, t + 256 * u, off, dst);
         const u32x4_t v = as_bf16x8_op<kQbf16>(qv[u]);
         if (!kGuard || t + 256 * u < nq)
-          *reinterpret_cast<u32x4_t *>(sQ + qdst[u]) = qok[u] ? v : u32x4_t{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4_t *>(sQ + dst) = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     } else {
       // Q [K x R] row-major: coalesced element reads (16 in flight per
@@ -358,10 +389,13 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs &a, int64_t wg, uns
       }
     }
     __syncthreads();
+    if (k0 + kTK < ke) load_slice(k0 + kTK);   // in flight during the products
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
-      const u32x4_t av0 = as_bf16x8_op<kPbf16>(pv[s]);
-      const u32x4_t av = pok[s] ? av0 : u32x4_t{0u, 0u, 0u, 0u};
+      // A operand: row wave * 16 + i16, k 32 s + 8 h .. +8
+      const u32x4_t av =
+          *reinterpret_cast<const u32x4_t *>(sP + (wave * 16 + i16) * kPP + 32 * s + 8 * h);
 #pragma unroll
       for (int st = 0; st < kRT; ++st) {
         if (!kGuard || st < RT) {
@@ -1153,7 +1187,13 @@ int64_t rowdot_chunk(int64_t M, int64_t K, int64_t R) {
   const int64_t TK = skinny_wide(int(R)) ? 256 : 64;
   const int64_t rt = (M + kRowdotRows - 1) / kRowdotRows;
   const int64_t slices = (K + TK - 1) / TK;
+  // about two workgroups per CU (512), but at least 4 slices per workgroup
+  // while that keeps 256 or more: the next slice's loads fly during the
+  // current products, so fewer, longer splits cost little and write fewer
+  // partials
   int64_t ks = (512 + rt - 1) / rt;
+  if (ks > slices / 4) ks = slices / 4;
+  if (ks < (256 + rt - 1) / rt) ks = (256 + rt - 1) / rt;
   if (ks < 1) ks = 1;
   if (ks > slices) ks = slices;
   const int64_t per = (slices + ks - 1) / ks;   // slices per split
@@ -1192,7 +1232,11 @@ ColdotArgs coldot_args(const void *P, const void *Q, int64_t ldq, int64_t M, int
   return a;
 }
 
-size_t rowdot_lds(int64_t R) { return size_t(rank_pad16(int(R))) * (skinny_wide(int(R)) ? 256 : 64) * 2; }
+size_t rowdot_lds(int64_t R) {
+  const bool wide = skinny_wide(int(R));
+  const size_t p = size_t(kRowdotRows) * (wide ? rowdot_ppitch<256>() : rowdot_ppitch<64>()) * 2;
+  return p + size_t(rank_pad16(int(R))) * (wide ? 256 : 64) * 2;
+}
 size_t coldot_lds(int64_t R) {
   return size_t(64) * coldot_pitch(coldot_tn(int(R))) * 2 + size_t(rank_pad16(int(R))) * 64 * 2;
 }
