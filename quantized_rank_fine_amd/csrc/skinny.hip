@@ -225,11 +225,9 @@ __device__ __forceinline__ void xat_role(const XatArgs &a, int64_t wg) {
 //
 // Workgroup: 4 wavefronts x 16 rows = 64 rows of P, all R columns, one
 // contiguous K range walked in slices of kTK (256 for R <= 64, else 64).  Per
-// slice, Q is staged in LDS as [RP][kTK] (16-B chunks XOR-swizzled by row) and
-// shared by the 4 wavefronts; P rows go straight from global memory into the
-// MFMA A operand.  Small register and LDS footprints keep several workgroups
-// resident per CU, which hides the load latency of a slice; at the usual
-// shapes one slice is the whole K range of a workgroup.
+// slice, the P rows (64 x kTK) and Q go to LDS, Q as [RP][kTK] (16-B chunks
+// XOR-swizzled by row) or [kTK][RP], shared by the 4 wavefronts, and the next
+// slice's loads fly while the current one is multiplied.
 
 constexpr int kRowdotRows = 64;
 
@@ -623,14 +621,14 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
 
 // ------------------------------------------------------------------ coldot
 //
-// Workgroup: 4 wavefronts, kTN columns of P (256 for R <= 64, else 64; a
+// Workgroup: 4 wavefronts, kTN columns of P (128 for R <= 64, else 64; a
 // wavefront owns kTN/4 of them as 16-wide MFMA tiles), all R, one contiguous
 // token range walked in 64-token slices.  Per slice the P tile (64 x kTN
 // bf16) is stored row-major in LDS with a row pitch that keeps the transposed
 // reads conflict-free, and Q^T (R x 64) with swizzled 16-B chunks.
 
-__host__ __device__ inline int coldot_tn(int R) { return skinny_wide(R) ? 256 : 64; }
-__host__ __device__ inline int coldot_pitch(int TN) { return TN == 256 ? 272 : 80; }
+__host__ __device__ inline int coldot_tn(int R) { return skinny_wide(R) ? 128 : 64; }
+__host__ __device__ inline int coldot_pitch(int TN) { return TN == 128 ? 144 : 80; }
 
 struct ColdotArgs {
   const void *P;      // [M x K]
@@ -652,7 +650,7 @@ struct ColdotArgs {
 // load sits behind a branch.
 template <bool kPbf16, bool kQbf16, int kTN, bool kQFastC, int kRT, bool kGuard>
 __device__ __forceinline__ void coldot_body(const ColdotArgs &a, int64_t wg, unsigned char *smem) {
-  constexpr int kPP = kTN == 256 ? 272 : 80;  // LDS row pitch of the P tile (elements)
+  constexpr int kPP = kTN == 128 ? 144 : 80;  // LDS row pitch of the P tile (elements)
   constexpr int kCPR = kTN / 8;               // 16-B chunks per P row
   constexpr int kNP = 64 * kCPR / 256;        // P chunks per thread: 8 or 2
   constexpr int kNCT = kTN / 64;              // 16-wide column tiles per wavefront
@@ -821,16 +819,16 @@ __device__ __forceinline__ void coldot_body(const ColdotArgs &a, int64_t wg, uns
   }
 }
 
-// R <= 64: 256 columns per workgroup with the rank tile count fixed at
+// R <= 64: 128 columns per workgroup with the rank tile count fixed at
 // compile time (one body per count); larger R: 64 columns, up to 16 tiles.
 template <bool kPbf16, bool kQbf16, bool kWide, bool kQFastC>
 __device__ __forceinline__ void coldot_role(const ColdotArgs &a, int64_t wg, unsigned char *smem) {
   if constexpr (kWide) {
     switch ((a.R + 15) / 16) {
-      case 1: coldot_body<kPbf16, kQbf16, 256, kQFastC, 1, false>(a, wg, smem); break;
-      case 2: coldot_body<kPbf16, kQbf16, 256, kQFastC, 2, false>(a, wg, smem); break;
-      case 3: coldot_body<kPbf16, kQbf16, 256, kQFastC, 3, false>(a, wg, smem); break;
-      default: coldot_body<kPbf16, kQbf16, 256, kQFastC, 4, false>(a, wg, smem); break;
+      case 1: coldot_body<kPbf16, kQbf16, 128, kQFastC, 1, false>(a, wg, smem); break;
+      case 2: coldot_body<kPbf16, kQbf16, 128, kQFastC, 2, false>(a, wg, smem); break;
+      case 3: coldot_body<kPbf16, kQbf16, 128, kQFastC, 3, false>(a, wg, smem); break;
+      default: coldot_body<kPbf16, kQbf16, 128, kQFastC, 4, false>(a, wg, smem); break;
     }
   } else {
     coldot_body<kPbf16, kQbf16, 64, kQFastC, 16, true>(a, wg, smem);
@@ -1203,7 +1201,11 @@ int64_t rowdot_chunk(int64_t M, int64_t K, int64_t R) {
 int64_t coldot_chunk(int64_t M, int64_t K, int64_t R) {
   const int64_t ct = (K + coldot_tn(int(R)) - 1) / coldot_tn(int(R));
   const int64_t mt = (M + 63) / 64;
-  int64_t ks = (256 + ct - 1) / ct;
+  // splits of about 8 slices while that keeps the grid within two
+  // workgroups per CU (512), and at least 256 workgroups
+  int64_t ks = (mt + 7) / 8;
+  if (ks > 512 / ct) ks = 512 / ct;
+  if (ks < (256 + ct - 1) / ct) ks = (256 + ct - 1) / ct;
   if (ks < 1) ks = 1;
   if (ks > mt) ks = mt;
   const int64_t per = (mt + ks - 1) / ks;
