@@ -8,8 +8,9 @@
 //
 // rowfull: C[M x R] = P[M x K] . Q whole, R <= 32 and M >= 1024: a
 //          workgroup owns a few rows of P and all of K (no partials).
-// rowdot:  the same product split over K (any shape): a slice of Q is staged
-//          in LDS in the form the MFMA B operand reads; fp32 partials.
+// rowdot:  the same product split over K (any shape): a slice of P and of Q
+//          is staged in LDS, Q in the form the MFMA B operand reads; fp32
+//          partials.
 // coldot:  C[K x R] = P[M x K]^T . Q[M x R], contraction over the token axis
 //          (P = X or dY, Q = G or XA given row-major).  P tiles are staged
 //          row-major in LDS and read transposed with ds_read_b64_tr_b16
