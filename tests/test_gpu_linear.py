@@ -59,6 +59,7 @@ def test_small_config_fp32(b_zero):
     (130, 320, 448, 12, "bf16", "f32"),     # r % 8 != 0: element-wise staging of A, XA
     (70, 256, 320, 5, "f32", "bf16"),       # r % 8 != 0, fp32 activations
     (96, 576, 320, 80, "bf16", "bf16"),     # r > 64: narrow skinny tiles
+    (520, 1088, 704, 24, "bf16", "bf16"),   # two rank tiles in the split-K passes, ragged slices
     (65, 384, 256, 100, "bf16", "f32"),     # r > 64 and r % 8 != 0
     (130, 256, 320, 256, "bf16", "bf16"),   # the largest rank accepted
     (8, 192, 256, 256, "f32", "f32"),       # few tokens at the largest rank: GEMM path
