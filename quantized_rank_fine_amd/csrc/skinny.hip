@@ -482,12 +482,21 @@ __host__ __device__ constexpr size_t rowfull_stage_bytes() {
   return kQMode == kQFast ? size_t(kFullSteps) * 32 * (16 * kRT) * 2 : 0;
 }
 
-template <int kQMode, int kRT>
-__host__ __device__ constexpr size_t rowfull_lds_bytes() {
-  return 4 * rowfull_stage_bytes<kQMode, kRT>() + size_t(4) * kRT * 16 * 16 * 4;
+// Per-wavefront P staging of one batch: kRows rows x kFullSteps * 32 k, rows
+// padded by 16 B.
+constexpr int kFullPPitch = kFullSteps * 32 + 8;
+template <int kRows>
+__host__ __device__ constexpr size_t rowfull_pstage_bytes() {
+  return size_t(kRows) * kFullPPitch * 2;
 }
 
-template <bool kPbf16, int kQMode, bool kQbf16, int kRT>
+template <int kQMode, int kRT, int kRows>
+__host__ __device__ constexpr size_t rowfull_lds_bytes() {
+  return 4 * (rowfull_stage_bytes<kQMode, kRT>() + rowfull_pstage_bytes<kRows>()) +
+         size_t(4) * kRT * 16 * 16 * 4;
+}
+
+template <bool kPbf16, int kQMode, bool kQbf16, int kRT, int kRows>
 __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, unsigned char *smem) {
   constexpr int kRP = 16 * kRT;
   constexpr int pes = kPbf16 ? 2 : 4, qes = kQbf16 ? 2 : 4;
@@ -496,21 +505,25 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
   // the B operands of every step and rank tile
   constexpr int kQN = kQMode == kQFast ? kFullSteps * 32 * kCPR / 64 : kFullSteps * kRT;
   constexpr size_t kStageBytes = rowfull_stage_bytes<kQMode, kRT>();   // per wavefront
+  constexpr size_t kPStageBytes = rowfull_pstage_bytes<kRows>();      // per wavefront
+  // 16-B P chunks per lane and batch: kRows rows x kFullSteps * 32 k
+  constexpr int kNP = kRows * kFullSteps * 32 / 8 / 64;
+  constexpr int kPCR = kFullSteps * 32 / 8;                      // 16-B chunks per P row and batch
   static_assert(kQMode == kQRows || kQMode == kQFast, "rowfull Q form");
+  static_assert(kRows == 8 || kRows == 16, "rows per workgroup");
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int i16 = lane & 15, h = lane >> 4;
   const int64_t K = a.K;
   const int R = a.R;
-  const int64_t m0 = wg * a.rows;
-  const int nrows = int(min64(a.rows, a.M - m0));
+  const int64_t m0 = wg * kRows;
+  const int nrows = int(min64(kRows, a.M - m0));
 
   // P rows m0 .. m0 + nrows - 1; lanes past them address the first byte
   // past the range (every later k offset stays out of range too)
   const uint32_t p_rec = uint32_t(clamp_records(int64_t(nrows) * K * pes));
   const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(static_cast<const char *>(a.P) + m0 * K * pes), (short)0, int32_t(p_rec), kBufFlags);
-  const uint32_t prow = i16 < nrows ? uint32_t(i16 * K * pes) : p_rec;
   const uint32_t q_rec = uint32_t(clamp_records(int64_t(R) * K * qes));
   const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void *)a.Q, (short)0,
                                                                       int32_t(q_rec), kBufFlags);
@@ -524,16 +537,25 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
   const int ns = int(K / 32);
   const int s0 = wave * ns / 4, s1 = (wave + 1) * ns / 4;
   const int nb = (s1 - s0 + kFullSteps - 1) / kFullSteps;
-  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + wave * kStageBytes);
+  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + wave * (kStageBytes + kPStageBytes));
+  uint16_t *sPw = reinterpret_cast<uint16_t *>(smem + wave * (kStageBytes + kPStageBytes) + kStageBytes);
 
-  Raw8<kPbf16> xb[2][kFullSteps];
+  Raw8<kPbf16> xb[2][kNP];
   Raw8<kQbf16> qb[2][kQN];
-  auto load_batch = [&](int b, Raw8<kPbf16> (&xv)[kFullSteps], Raw8<kQbf16> (&qv)[kQN]) {
+  auto load_batch = [&](int b, Raw8<kPbf16> (&xv)[kNP], Raw8<kQbf16> (&qv)[kQN]) {
+    // P: whole 512-B row runs (32 lanes per row), rows past nrows and steps
+    // past the run read zero
+#pragma unroll
+    for (int u = 0; u < kNP; ++u) {
+      const int cid = lane + 64 * u, row = cid / kPCR, kc = cid % kPCR;
+      const int st = s0 + kFullSteps * b + kc / 4;
+      xv[u] = buf_load8<kPbf16>(
+          rP, (row < nrows && st < s1) ? uint32_t((row * K + 32 * st + 8 * (kc % 4)) * pes) : p_rec);
+    }
 #pragma unroll
     for (int u = 0; u < kFullSteps; ++u) {
       const int st = s0 + kFullSteps * b + u;
       const bool in = st < s1;
-      xv[u] = buf_load8<kPbf16>(rP, in ? prow + uint32_t((32 * st + 8 * h) * pes) : p_rec);
       if constexpr (kQMode == kQRows) {
         // the B operand straight from the rows of Qt
 #pragma unroll
@@ -556,7 +578,15 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
   f32x4_t acc[kRT];
 #pragma unroll
   for (int r = 0; r < kRT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute_batch = [&](const Raw8<kPbf16> (&xv)[kFullSteps], const Raw8<kQbf16> (&qv)[kQN]) {
+  auto compute_batch = [&](const Raw8<kPbf16> (&xv)[kNP], const Raw8<kQbf16> (&qv)[kQN]) {
+    // P rows to this wavefront's area (LDS operations of one wavefront
+    // complete in order, so the reads below see these writes, and the next
+    // batch's writes follow this batch's reads)
+#pragma unroll
+    for (int u = 0; u < kNP; ++u) {
+      const int cid = lane + 64 * u, row = cid / kPCR, kc = cid % kPCR;
+      *reinterpret_cast<u32x4_t *>(sPw + row * kFullPPitch + 8 * kc) = as_bf16x8_op<kPbf16>(xv[u]);
+    }
     if constexpr (kQMode == kQFast) {
       // stage Q rows [kFullSteps * 32][kRP] in this wavefront's area (LDS
       // operations of one wavefront complete in order, so the transposed
@@ -569,7 +599,10 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
     }
 #pragma unroll
     for (int u = 0; u < kFullSteps; ++u) {
-      const u32x4_t av = as_bf16x8_op<kPbf16>(xv[u]);
+      // A operand: row i16 (zero past kRows), k 32 u + 8 h .. +8
+      const u32x4_t a8 =
+          *reinterpret_cast<const u32x4_t *>(sPw + (i16 & (kRows - 1)) * kFullPPitch + 32 * u + 8 * h);
+      const u32x4_t av = i16 < kRows ? a8 : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int r = 0; r < kRT; ++r) {
         u32x4_t bv;
@@ -596,7 +629,7 @@ __device__ __forceinline__ void rowfull_role(const RowfullArgs &a, int64_t wg, u
   }
 
   // fixed-order sum of the four wavefronts' products
-  float *red = reinterpret_cast<float *>(smem + 4 * kStageBytes);
+  float *red = reinterpret_cast<float *>(smem + 4 * (kStageBytes + kPStageBytes));
 #pragma unroll
   for (int r = 0; r < kRT; ++r)
 #pragma unroll
@@ -1088,8 +1121,10 @@ __global__ __launch_bounds__(256) void fwd_full_kernel(RowfullArgs ra, int64_t n
   const int64_t wg = blockIdx.x;
   if (wg < n_sc)
     scales_role(sa, wg);
+  else if (ra.rows == 8)
+    rowfull_role<kXbf16, kQFast, kAbf16, kRT, 8>(ra, wg - n_sc, smem);
   else
-    rowfull_role<kXbf16, kQFast, kAbf16, kRT>(ra, wg - n_sc, smem);
+    rowfull_role<kXbf16, kQFast, kAbf16, kRT, 16>(ra, wg - n_sc, smem);
 }
 
 // One pass over dY with G complete: block scales on [0, n_sc), XA^T bf16 on
@@ -1112,9 +1147,12 @@ __global__ __launch_bounds__(256) void dy_full_kernel(RowfullArgs ra, int64_t n_
     return;
   }
   wg -= n_xat;
-  if (wg < n_row)
-    rowfull_role<kDYbf16, kQRows, kBbf16, kRT>(ra, wg, smem);
-  else
+  if (wg < n_row) {
+    if (ra.rows == 8)
+      rowfull_role<kDYbf16, kQRows, kBbf16, kRT, 8>(ra, wg, smem);
+    else
+      rowfull_role<kDYbf16, kQRows, kBbf16, kRT, 16>(ra, wg, smem);
+  } else
     coldot_role<kDYbf16, false, true, kQFastC>(ca, wg - n_row, smem);
 }
 
@@ -1306,7 +1344,9 @@ hipError_t launch_fwd_prep(const void *X, bool x_bf16, const void *A, bool a_bf1
     RowfullArgs fa = rowfull_args(X, A, M, in, r, XA, XA16, ld16, n_full);
     fa.mul = mul;
     const dim3 grid = dim3(unsigned(n_full + n_sc));
-    const size_t lds1 = rowfull_lds_bytes<kQFast, 1>(), lds2 = rowfull_lds_bytes<kQFast, 2>();
+    const bool r8 = fa.rows == 8;
+    const size_t lds1 = r8 ? rowfull_lds_bytes<kQFast, 1, 8>() : rowfull_lds_bytes<kQFast, 1, 16>();
+    const size_t lds2 = r8 ? rowfull_lds_bytes<kQFast, 2, 8>() : rowfull_lds_bytes<kQFast, 2, 16>();
 #define QLORA_FULL(XB, AB)                                                                      \
   do {                                                                                          \
     if (r <= 16)                                                                                \
@@ -1368,7 +1408,8 @@ hipError_t launch_bwd_dy(const void *dY, bool dy_bf16, const void *B, bool b_bf1
     const int64_t n_xat = xat ? xat_workgroups(ldm) : 0;
     if (xat) n_col = 0;    // dB is formed by the dX GEMM
     const dim3 grid = dim3(unsigned(n_sc + n_xat + n_full + n_col));
-    const size_t lds_full = rowfull_lds_bytes<kQRows, 2>();
+    const size_t lds_full =
+        fa.rows == 8 ? rowfull_lds_bytes<kQRows, 2, 8>() : rowfull_lds_bytes<kQRows, 2, 16>();
     const size_t lds = coldot_lds(r) > lds_full ? coldot_lds(r) : lds_full;
 #define QLORA_DYF2(DB, BB, RT)                                                                  \
   do {                                                                                          \
