@@ -1020,15 +1020,21 @@ __device__ __forceinline__ void da_full_role(const DaFullArgs &a, int64_t wg, un
 #pragma unroll
     for (int u = 0; u < kG; ++u) {
       const int64_t ls = grp * kG + u;                       // this wavefront's slab index
-      const int64_t m = (wave + 4 * ls) * 64 + lane;         // >= M past the last slab
-      const uint32_t po = uint32_t((m * a.K + c0) * int64_t(pes));
-      const uint32_t qo = uint32_t(m * a.ldq * 2);
+      // load c covers rows 32 (c / (kPL / 2)) .. +31 of the slab, two lanes
+      // per row (lane & 1: the row's first or second 8 columns)
 #pragma unroll
-      for (int c = 0; c < kPL; ++c)
-        pg[u][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, po + 16 * c, 0, 0));
+      for (int c = 0; c < kPL; ++c) {
+        const int half = c / (kPL / 2), part = c % (kPL / 2);
+        const int64_t m = (wave + 4 * ls) * 64 + 32 * half + (lane >> 1);   // >= M past the last slab
+        const uint32_t po = uint32_t((m * a.K + c0) * int64_t(pes)) + 16u * uint32_t((lane & 1) * (kPL / 2) + part);
+        pg[u][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, po, 0, 0));
+      }
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        qg[u][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo + 16 * c, 0, 0));
+      for (int c = 0; c < 2; ++c) {
+        const int64_t m = (wave + 4 * ls) * 64 + 32 * c + (lane >> 1);
+        const uint32_t qo = uint32_t(m * a.ldq * 2) + 16u * uint32_t(lane & 1);
+        qg[u][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rQ, qo, 0, 0));
+      }
     }
   };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -1038,6 +1044,7 @@ __device__ __forceinline__ void da_full_role(const DaFullArgs &a, int64_t wg, un
       if (grp * kG + u >= mine) break;
       // (LDS operations of one wavefront complete in order: these writes
       // follow the previous slab's reads and precede this slab's)
+      // p16[h]: 8 columns (lane & 1) of row 32 h + (lane >> 1)
       u32x4_t p16[2];
       if constexpr (kPbf16) {
         p16[0] = pg[u][0];
@@ -1045,16 +1052,18 @@ __device__ __forceinline__ void da_full_role(const DaFullArgs &a, int64_t wg, un
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
+          // fp32: loads 2c, 2c + 1 are the two 16-B halves of the lane's 32 B
           const f32x4_t x = __builtin_bit_cast(f32x4_t, pg[u][2 * c]);
           const f32x4_t y = __builtin_bit_cast(f32x4_t, pg[u][2 * c + 1]);
           p16[c] = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                            pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         }
       }
-      *reinterpret_cast<u32x4_t *>(sP + lane * kDaPitch) = p16[0];
-      *reinterpret_cast<u32x4_t *>(sP + lane * kDaPitch + 8) = p16[1];
-      *reinterpret_cast<u32x4_t *>(sQ + lane * kDaPitch) = qg[u][0];
-      *reinterpret_cast<u32x4_t *>(sQ + lane * kDaPitch + 8) = qg[u][1];
+      const int rw = lane >> 1, cw = 8 * (lane & 1);
+      *reinterpret_cast<u32x4_t *>(sP + rw * kDaPitch + cw) = p16[0];
+      *reinterpret_cast<u32x4_t *>(sP + (32 + rw) * kDaPitch + cw) = p16[1];
+      *reinterpret_cast<u32x4_t *>(sQ + rw * kDaPitch + cw) = qg[u][0];
+      *reinterpret_cast<u32x4_t *>(sQ + (32 + rw) * kDaPitch + cw) = qg[u][1];
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         acc = mfma16x16x32(lds_col8(sP, kDaPitch, 32 * k, 0), lds_col8(sQ, kDaPitch, 32 * k, 0), acc);
