@@ -124,6 +124,51 @@ def copy_calibrate():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
+def context_report(reps=20):
+    """Machine context beside the roofline fractions, measured on the same
+    box: a plain 1 GiB device copy (GB/s of bytes read + written) and the
+    vendor library's dense bf16 GEMM (torch.matmul, weights already bf16
+    and contiguous, so no dequantization) at the forward GEMM's shape and at
+    8192^3.  Neither is part of the measured path."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    out["device_copy_1GiB"] = {"us": round(us, 1), "GBps_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)}
+    del src, dst
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for (m, k, nn) in ((2048, 4096, 4096), (8192, 8192, 8192)):
+        x = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        w = torch.randn(k, nn, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(5):
+            torch.matmul(x, w)
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            torch.matmul(x, w)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        tf = 2.0 * m * k * nn / (us * 1e-6) / 1e12
+        out[f"library_bf16_gemm_{m}x{k}x{nn}"] = {"us": round(us, 2), "TFLOPs": round(tf, 1),
+                                                   "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del x, w
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w0, X, dY, A, B, min_seconds):
     """The oracle, as it stands, on the same workload: full quantize of W0
     (its fp32 NumPy quantizer, run on a pool of worker processes over whole
@@ -1102,6 +1147,9 @@ def main():
     if not args.no_decode:
         out["decode"] = decode_report(args.decode_sets)
     del W0s, wsf, wsb
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        out["context"] = context_report()
     torch.cuda.empty_cache()
     if not args.no_configs:
         out["cfg0"] = cfg0_report(max(K, 20))
