@@ -324,11 +324,51 @@ def decode_report(sets, reps=5):
         usg = e0.elapsed_time(e1) * 1e3 / reps
         gbpsg = nbytes / (usg * 1e-6) / 1e9
         del graph
+
+        # Per shape: the linears of one shape from every set, back to back
+        # in their own graph (the first linear of that shape in each set).
+        per_shape = {}
+        for (_, n_in, n_out) in lins:
+            key = f"{n_in}x{n_out}"
+            if key in per_shape:
+                continue
+            li = next(i for i, (_, a, b) in enumerate(lins) if (a, b) == (n_in, n_out))
+
+            def one_shape():
+                for s in range(sets):
+                    wq, A, B = layers[s][li]
+                    q.qlora_linear_fwd(wq, X[n_in], M, q.BF16, A, B, R, q.BF16, Y[n_out], None,
+                                       ws, wsb)
+
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                one_shape()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                one_shape()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us1 = e0.elapsed_time(e1) * 1e3 / reps / sets
+            b1 = (workloads.nf4_bytes(n_in, n_out) + M * n_in * 2 + (n_in * R + R * n_out) * 2
+                  + M * n_out * 2)
+            per_shape[key] = {"us_per_linear": round(us1, 2),
+                              "GBps": round(b1 / (us1 * 1e-6) / 1e9, 1),
+                              "frac_hbm_peak": round(b1 / (us1 * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+            del graph
         res[f"M{M}"] = {"us_per_layer_set": round(us / sets, 2), "GBps": round(gbps, 1),
                         "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "grouped": {"us_per_layer_set": round(usg / sets, 2),
                                     "GBps": round(gbpsg, 1),
-                                    "frac_hbm_peak": round(gbpsg / PEAK_HBM_GBPS, 4)}}
+                                    "frac_hbm_peak": round(gbpsg / PEAK_HBM_GBPS, 4)},
+                        "per_shape": per_shape}
     return {"workload": "7b-layer-decode-r16-bf16", "layer_sets": sets,
             "bytes_per_set_M1": sum(workloads.nf4_bytes(i, o) + i * 2 + (i * R + R * o) * 2 + o * 2
                                     for (_, i, o) in lins),
