@@ -16,9 +16,9 @@
 // zeros and drops its stores without a branch.
 //
 // The quotient x = w / c_b is the fp32 rounding of w * y in fp64, where
-// y = 1/c_b is the correctly rounded fp64 reciprocal (one fp64 division per
-// lane and block).  That equals the IEEE fp32 quotient: the fp64 product is
-// within 2^-52 (relative) of w / c_b, while a quotient of two fp32 numbers in
+// y = 1/c_b is the fp64 reciprocal to within a few ulps (one per lane and
+// block, see recip64).  That equals the IEEE fp32 quotient: the fp64 product
+// is within 2^-50 (relative) of w / c_b, while a quotient of two fp32 numbers in
 // the fp32 normal range is never an fp32 rounding midpoint and never within
 // 2^-49 (relative) of one, so both round to the same fp32 value.  (Below the
 // normal range x may differ, but every |x| < 2^-9 gets the same code.)
@@ -64,6 +64,19 @@ __device__ __forceinline__ uint32_t bucket_of(float x) {
 __device__ __forceinline__ uint32_t code_of(float x, const BucketEntry *lut) {
   const BucketEntry e = lut[bucket_of(x)];
   return e.base + ((x >= e.T) ? 1u : 0u);
+}
+
+// y = 1/c in fp64 to within a few ulps: the hardware reciprocal refined by
+// two Newton steps (y <- y + y (1 - c y), fused), a shorter dependent chain
+// than the correctly rounded division.  The argument above needs the product
+// w y within 2^-49 (relative) of w / c; with y a few fp64 ulps from 1/c it
+// stays within 2^-50.  An infinite c gives y = 0, as the division would.
+__device__ __forceinline__ double recip64(float c) {
+  const double d = double(c);
+  double y = __builtin_amdgcn_rcp(d);
+  y = __builtin_fma(y, __builtin_fma(-d, y, 1.0), y);
+  y = __builtin_fma(y, __builtin_fma(-d, y, 1.0), y);
+  return __builtin_isinf(c) ? 0.0 : y;
 }
 
 // x = w / c as described above; y = 1/c in fp64 (y = 1 for a zero block, x = 0)
@@ -163,8 +176,8 @@ __device__ __forceinline__ void encode_group(const f32x4_t (&v)[kSteps][2], cons
       // groups 16 q: q = k >> 2 (elements of a) and 2 + (k >> 2) (of b)
       const float ma = __uint_as_float(quad_max(__float_as_uint(absmax4(a))));
       const float mb = __uint_as_float(quad_max(__float_as_uint(absmax4(b))));
-      const double ya = 1.0 / double(ma == 0.0f ? 1.0f : ma);
-      const double yb = 1.0 / double(mb == 0.0f ? 1.0f : mb);
+      const double ya = recip64(ma == 0.0f ? 1.0f : ma);
+      const double yb = recip64(mb == 0.0f ? 1.0f : mb);
       st[j * 128] = uint16_t(code4(a, ya, lut));
       st[j * 128 + 8] = uint16_t(code4(b, yb, lut));
       if ((k & 3) == 0) {                        // one lane per quad stores its two scales
@@ -175,7 +188,7 @@ __device__ __forceinline__ void encode_group(const f32x4_t (&v)[kSteps][2], cons
     } else {
       const float m = __uint_as_float(row8_max(__float_as_uint(absmax8(a, b))));
       sc_blk[bl0 + 8 * j] = m;                  // the 8 lanes of the block agree
-      const double y = 1.0 / double(m == 0.0f ? 1.0f : m);
+      const double y = recip64(m == 0.0f ? 1.0f : m);
       st[j * 128] = uint16_t(code4(a, y, lut));
       st[j * 128 + 8] = uint16_t(code4(b, y, lut));
     }
